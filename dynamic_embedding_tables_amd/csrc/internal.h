@@ -1,0 +1,279 @@
+// internal.h -- shared declarations of the recis HIP library (not installed).
+//
+// Memory layout in HBM (one table):
+//   IDMap        Slot[slot_cap]      16 B per slot: key, row, count; linear
+//                                    probing from a multiplicative hash.
+//   EmbeddingBlocks  block_rows rows per block; row r lives in block r >> lb at
+//                    byte (r & mb) * stride; a row is [dim params in the storage
+//                    dtype | slots * dim float32 optimizer state].
+//   free list    int32 rows released by eviction.
+//   DevCounters  bump pointer, free-list top, key count, error word.
+//   scratch      per-step dedup table and per-occurrence / per-key arrays.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "recis.h"
+
+namespace recis {
+
+constexpr long long kEmptyKey = -1;  // free slot
+constexpr long long kBadKey = -2;    // an occurrence whose transform failed
+constexpr long long kGoneKey = -3;   // evicted, awaiting rebuild
+
+constexpr unsigned kErrInvalid = 1u << RECIS_ERR_INVALID_ARG;
+constexpr unsigned kErrCapacity = 1u << RECIS_ERR_CAPACITY;
+constexpr unsigned kErrKeyRange = 1u << RECIS_ERR_KEY_RANGE;
+
+// Occurrence tiling of the per-occurrence kernels.
+constexpr int kThreads = 256;
+constexpr int kOccPerThread = 8;
+constexpr int kOccTile = kThreads * kOccPerThread;  // 2048
+constexpr int kLdsTab = 2 * kOccTile;               // block-local aggregation table
+// Distinct-key tiling of the per-key kernels (same 2048 per block).
+constexpr int kKeyPerThread = 8;
+constexpr int kKeyTile = kThreads * kKeyPerThread;
+// Backward: keys with more occurrences than kShortMax are split into chunks.
+constexpr int kShortMax = 64;
+constexpr int kChunk = 256;
+
+struct __align__(16) Slot {
+  long long key;
+  int row;
+  unsigned count;
+};
+
+struct __align__(16) DedupSlot {
+  long long key;
+  int count;  // occurrences in this call (writeback: last occurrence index)
+  int uidx;   // index of the key among the call's distinct keys
+};
+
+struct DevCounters {
+  unsigned long long next_row;  // bump pointer over EmbeddingBlocks
+  long long free_top;           // entries in the free list
+  unsigned long long num_keys;  // keys in the IDMap
+  unsigned int error;           // sticky error bits (kErr*)
+  unsigned int pad0;
+  // written by the scan kernel for the finalize kernel of the same call
+  long long take_free;
+  long long free_top_old;
+  long long bump_base;
+  unsigned long long scratch_count;  // writeback distinct keys / export count / evicted
+};
+
+// Device view of one feature of a call.
+struct FeatDev {
+  const long long* values;
+  const int* offs;
+  long long n;
+  long long base;       // global index of its first occurrence
+  long long tile_base;  // first occurrence tile of this feature
+  unsigned long long mod;
+  unsigned slot;
+  unsigned ops;
+  int bnd_off;
+  int nb;
+};
+
+// Backward work plan header (in recis_lookup_result.plan).
+struct PlanLayout {
+  long long max_long, max_chunks;
+  // word offsets
+  long long o_long_u, o_long_base, o_long_nch, o_long_done, o_chunk_owner;
+  long long words;
+};
+
+__host__ __device__ inline PlanLayout plan_layout(long long cap) {
+  PlanLayout p;
+  p.max_long = cap / kShortMax + 1;
+  p.max_chunks = cap / kChunk + p.max_long + 1;
+  p.o_long_u = 4;
+  p.o_long_base = p.o_long_u + p.max_long;
+  p.o_long_nch = p.o_long_base + p.max_long;
+  p.o_long_done = p.o_long_nch + p.max_long;
+  p.o_chunk_owner = p.o_long_done + p.max_long;
+  p.words = p.o_chunk_owner + p.max_chunks;
+  return p;
+}
+
+struct RowSpace {
+  char* const* blocks;  // device array of block base pointers
+  int lb;               // log2(block_rows)
+  long long mb;         // block_rows - 1
+  long long stride;     // bytes per row
+};
+
+__device__ __forceinline__ char* row_ptr(const RowSpace& rs, long long r) {
+  return rs.blocks[r >> rs.lb] + (size_t)(r & rs.mb) * (size_t)rs.stride;
+}
+
+// Multiplicative (Fibonacci) hash of a key to a slot of a 2^k table; shift = 64 - k.
+__device__ __forceinline__ unsigned long long slot_of(long long key, int shift) {
+  return ((unsigned long long)key * 0x9E3779B97F4A7C15ull) >> shift;
+}
+
+// ----------------------------------------------------------------- values
+// bfloat16 <-> float; float -> bfloat16 rounds to nearest, ties to even.
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
+  return __uint_as_float((unsigned)b << 16);
+}
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))  // NaN stays NaN
+    return (unsigned short)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// MurmurHash3's 64-bit finalizer (the Hash transform).
+__device__ __forceinline__ unsigned long long fmix64(unsigned long long k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdull;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ull;
+  k ^= k >> 33;
+  return k;
+}
+
+// Philox4x32-10 block (Salmon et al., SC'11).
+__device__ __forceinline__ uint4 philox10(uint4 c, uint2 k) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const unsigned lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k.x, lo1, hi0 ^ c.w ^ k.y, lo0);
+    k.x += 0x9E3779B9u;
+    k.y += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Four initial values of elements 4g..4g+3 of the row of `key`: the top 24
+// bits of each Philox word, centred, times bound * 2^-23 (one rounding).
+__device__ __forceinline__ float4 init4(unsigned long long seed, long long key, unsigned g,
+                                        float scale) {
+  const uint4 w = philox10(make_uint4(g, 0u, (unsigned)key, (unsigned)((unsigned long long)key >> 32)),
+                           make_uint2((unsigned)seed, (unsigned)(seed >> 32)));
+  float4 v;
+  v.x = __fmul_rn((float)((int)(w.x >> 8) - (1 << 23)), scale);
+  v.y = __fmul_rn((float)((int)(w.y >> 8) - (1 << 23)), scale);
+  v.z = __fmul_rn((float)((int)(w.z >> 8) - (1 << 23)), scale);
+  v.w = __fmul_rn((float)((int)(w.w >> 8) - (1 << 23)), scale);
+  return v;
+}
+
+// ------------------------------------------------------------ the table
+struct TableDev {
+  Slot* slots;
+  unsigned long long slot_mask;
+  int slot_shift;
+  DevCounters* ctr;
+  int* free_list;
+  RowSpace rs;
+  int dim, dtype, optim, state_words;  // state_words = slots per element (0, 1, 2)
+  unsigned admit;
+  unsigned long long seed;
+  float init_scale;                    // bound * 2^-23
+  long long rows_limit;                // rows covered by blocks
+};
+
+}  // namespace recis
+
+struct recis_table {
+  recis_table_config cfg;
+  recis_allocator alloc;
+  bool own_alloc;
+  int device;
+  int state_words;
+  long long row_bytes;
+  int lb;
+
+  recis::Slot* slots = nullptr;
+  long long slot_cap = 0;
+  recis::DevCounters* ctr = nullptr;
+  std::vector<char*> blocks;
+  char** d_blocks = nullptr;
+  long long d_blocks_cap = 0;
+  long long rows_alloc = 0;
+  int* free_list = nullptr;
+  long long free_cap = 0;
+
+  // host-side upper bounds (exact after a sync)
+  long long rows_hi = 0;
+  long long keys_hi = 0;
+  long long adam_step = 0;
+  long long bytes = 0;
+
+  // per-step scratch, sized for scr_cap occurrences
+  long long scr_cap = 0;
+  recis::DedupSlot* dd = nullptr;
+  long long dd_cap = 0;
+  int* occ_slot = nullptr;
+  int* occ_rank = nullptr;
+  int* uslot = nullptr;
+  unsigned* idslot = nullptr;
+  unsigned long long* blk_sums = nullptr;
+  long long* wb_keys = nullptr;
+  double* partials = nullptr;
+
+  // pinned staging ring for per-call descriptors
+  static constexpr int kRing = 4;
+  char* stage_host[kRing] = {};
+  char* stage_dev[kRing] = {};
+  size_t stage_cap[kRing] = {};
+  hipEvent_t stage_ev[kRing] = {};
+  int ring_pos = 0;
+
+  recis::TableDev dev() const;
+};
+
+namespace recis {
+
+// Launchers (defined in the .hip files; all enqueue on `s`).
+void launch_fill_slots(Slot* slots, long long cap, hipStream_t s);
+void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s);
+void launch_rehash(const Slot* old_slots, long long old_cap, const TableDev& t, hipStream_t s);
+
+struct LookupLaunch {
+  const FeatDev* feats;
+  const long long* bnd_pool;
+  int F, B;
+  long long N;
+  long long occ_tiles;
+  unsigned flags;
+  recis_lookup_result res;
+  DedupSlot* dd;
+  unsigned long long dd_mask;
+  int dd_shift;
+  int* occ_slot;
+  int* occ_rank;
+  int* uslot;
+  unsigned* idslot;
+  unsigned long long* blk_sums;
+  long long key_tiles;
+};
+void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);
+
+void launch_forward(const recis_lookup_result& res, const TableDev& t, int pool, void* out,
+                    hipStream_t s);
+struct OptConsts {
+  float lr, b1, omb1, b2, omb2, eps, step_size;  // omb = 1 - beta, formed in double
+};
+recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, int pool,
+                             const void* grad, int grad_dtype, const OptConsts& oc,
+                             double* partials, hipStream_t s);
+
+void launch_evict(const TableDev& t, unsigned min_count, long long* num_evicted, hipStream_t s);
+void launch_writeback(const TableDev& t, const long long* keys, long long n, const float* rows,
+                      DedupSlot* dd, unsigned long long dd_mask, int dd_shift, long long* wb_keys,
+                      int* uslot, hipStream_t s);
+void launch_export(const TableDev& t, long long cap, long long* keys, long long* rows,
+                   unsigned* counts, hipStream_t s);
+void launch_export_rows(const TableDev& t, long long n, const long long* rows, void* params,
+                        float* state, hipStream_t s);
+
+}  // namespace recis

@@ -1,0 +1,344 @@
+// maint.hip -- table maintenance kernels: slot fills, IDMap rebuild (growth
+// and after eviction), the eviction pass, the cache writeback, and export.
+//
+// Pages: "RecIS (Recommendation Intelligence System)" README --
+//   Core architecture > Embedding Engine (eviction and admission);
+//   Key optimisations > Efficient dynamic Embedding (blocks grow on demand);
+// "Memory Layer: Train the In-Model Cache for Recommendation Models" --
+//   What carries the argument / Referee Report > Summary (Writeback: the
+//   item tower's output is assigned exactly into the cache row).
+#include "internal.h"
+
+namespace recis {
+
+namespace {
+
+__global__ void k_fill_slots(Slot* slots, long long cap) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < cap;
+       i += (long long)gridDim.x * blockDim.x) {
+    Slot s;
+    s.key = kEmptyKey;
+    s.row = -1;
+    s.count = 0;
+    slots[i] = s;
+  }
+}
+
+__global__ void k_fill_dedup(DedupSlot* dd, long long cap) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < cap;
+       i += (long long)gridDim.x * blockDim.x) {
+    DedupSlot s;
+    s.key = kEmptyKey;
+    s.count = 0;
+    s.uidx = -1;
+    dd[i] = s;
+  }
+}
+
+// Insert `key` (absent, unique among concurrent inserters) into t's IDMap.
+__device__ __forceinline__ long long claim_slot(const TableDev& t, long long key) {
+  unsigned long long p = slot_of(key, t.slot_shift);
+  for (unsigned long long n = 0; n <= t.slot_mask; ++n) {
+    const long long cur = t.slots[p].key;
+    if (cur == kEmptyKey) {
+      const long long old = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
+                                                 (unsigned long long)kEmptyKey, (unsigned long long)key);
+      if (old == kEmptyKey) return (long long)p;
+    }
+    p = (p + 1) & t.slot_mask;
+  }
+  return -1;
+}
+
+__global__ void k_rehash(const Slot* old_slots, long long old_cap, TableDev t) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < old_cap;
+       i += (long long)gridDim.x * blockDim.x) {
+    const Slot s = old_slots[i];
+    if (s.key < 0) continue;
+    const long long p = claim_slot(t, s.key);
+    if (p < 0) {
+      atomicOr(&t.ctr->error, kErrCapacity);
+      continue;
+    }
+    t.slots[p].row = s.row;
+    t.slots[p].count = s.count;
+  }
+}
+
+__device__ __forceinline__ long long wave_add(unsigned long long* ctr, bool take) {
+  const unsigned long long m = __ballot(take);
+  if (!m) return -1;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  unsigned long long base = 0;
+  if (lane == leader) base = atomicAdd(ctr, (unsigned long long)__popcll(m));
+  base = (unsigned long long)__shfl((long long)base, leader);
+  const unsigned long long below = m & ((1ull << lane) - 1ull);
+  return take ? (long long)(base + __popcll(below)) : -1;
+}
+
+__global__ void k_set_scratch(DevCounters* c) { c->scratch_count = 0; }
+
+// Eviction: keys whose window count is below min_count leave (their slot is
+// marked gone and the IDMap is rebuilt afterwards); their rows go to the free
+// list; survivors restart their count at 0.
+__global__ void k_evict_mark(TableDev t, unsigned min_count) {
+  for (long long i0 = (long long)blockIdx.x * blockDim.x; i0 <= (long long)t.slot_mask;
+       i0 += (long long)gridDim.x * blockDim.x) {
+    const long long i = i0 + threadIdx.x;
+    bool gone = false, frees = false;
+    int row = -1;
+    if (i <= (long long)t.slot_mask) {
+      Slot s = t.slots[i];
+      if (s.key >= 0) {
+        if (s.count < min_count) {
+          gone = true;
+          row = s.row;
+          frees = row >= 0;
+          t.slots[i].key = kGoneKey;
+        } else {
+          t.slots[i].count = 0;
+        }
+      }
+    }
+    const long long at = wave_add((unsigned long long*)&t.ctr->free_top, frees);
+    if (frees) t.free_list[at] = row;
+    wave_add(&t.ctr->scratch_count, gone);
+  }
+}
+
+__global__ void k_evict_done(DevCounters* c, long long* num_evicted) {
+  c->num_keys -= c->scratch_count;
+  if (num_evicted) *num_evicted = (long long)c->scratch_count;
+}
+
+// Writeback, step 1: dedup the keys; the slot keeps the last occurrence index.
+__global__ __launch_bounds__(256) void k_wb_dedup(TableDev t, const long long* keys, long long n,
+                                                  DedupSlot* dd, unsigned long long mask, int shift,
+                                                  long long* wb_keys, int* uslot) {
+  __shared__ int s_new;
+  __shared__ long long s_base;
+  if (threadIdx.x == 0) s_new = 0;
+  __syncthreads();
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  int p = -1, nidx = -1;
+  long long key = 0;
+  if (i < n) {
+    key = keys[i];
+    if (key < 0) {
+      atomicOr(&t.ctr->error, kErrKeyRange);
+    } else {
+      unsigned long long q = ((unsigned long long)key * 0x9E3779B97F4A7C15ull) >> shift;
+      bool won = false;
+      while (true) {
+        const long long cur = dd[q].key;
+        if (cur == key) break;
+        if (cur == kEmptyKey) {
+          const long long old = (long long)atomicCAS((unsigned long long*)&dd[q].key,
+                                                     (unsigned long long)kEmptyKey, (unsigned long long)key);
+          if (old == kEmptyKey) {
+            won = true;
+            break;
+          }
+          if (old == key) break;
+        }
+        q = (q + 1) & mask;
+      }
+      p = (int)q;
+      atomicMax(&dd[p].count, (int)i);
+      if (won) nidx = atomicAdd(&s_new, 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && s_new > 0)
+    s_base = (long long)atomicAdd(&t.ctr->scratch_count, (unsigned long long)s_new);
+  __syncthreads();
+  if (nidx >= 0) {
+    const long long u = s_base + nidx;
+    wb_keys[u] = key;
+    uslot[u] = p;
+    dd[p].uidx = (int)u;
+  }
+}
+
+__device__ long long alloc_one_row(const TableDev& t) {
+  long long top = t.ctr->free_top;
+  while (top > 0) {
+    const long long seen = (long long)atomicCAS((unsigned long long*)&t.ctr->free_top,
+                                                (unsigned long long)top, (unsigned long long)(top - 1));
+    if (seen == top) return t.free_list[top - 1];
+    top = seen;
+  }
+  const long long r = (long long)atomicAdd(&t.ctr->next_row, 1ull);
+  if (r >= t.rows_limit) {
+    atomicAdd(&t.ctr->next_row, ~0ull);  // give the number back
+    return -1;
+  }
+  return r;
+}
+
+// Writeback, step 2: one wave per distinct key: find or insert it, give it a
+// row if it has none, and store the last occurrence's values.
+template <typename TP>
+__global__ __launch_bounds__(256) void k_wb_apply(TableDev t, const float* rows, DedupSlot* dd,
+                                                  const long long* wb_keys, const int* uslot) {
+  const long long U = (long long)t.ctr->scratch_count;
+  const int lane = threadIdx.x & 63;
+  for (long long u = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); u < U; u += (long long)gridDim.x * 4) {
+    const long long key = wb_keys[u];
+    DedupSlot* d = &dd[uslot[u]];
+    const int last = d->count;
+    long long row = -1;
+    int fresh = 0;
+    if (lane == 0) {
+      unsigned long long p = slot_of(key, t.slot_shift);
+      long long at = -1;
+      bool inserted = false;
+      for (unsigned long long n = 0; n <= t.slot_mask; ++n) {
+        const long long cur = t.slots[p].key;
+        if (cur == key) {
+          at = (long long)p;
+          break;
+        }
+        if (cur == kEmptyKey) {
+          const long long old = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
+                                                     (unsigned long long)kEmptyKey, (unsigned long long)key);
+          if (old == kEmptyKey) {
+            at = (long long)p;
+            inserted = true;
+            break;
+          }
+          if (old == key) {
+            at = (long long)p;
+            break;
+          }
+        }
+        p = (p + 1) & t.slot_mask;
+      }
+      if (at < 0) {
+        atomicOr(&t.ctr->error, kErrCapacity);
+      } else {
+        if (inserted) atomicAdd(&t.ctr->num_keys, 1ull);
+        row = inserted ? -1 : t.slots[at].row;
+        if (row < 0) {
+          row = alloc_one_row(t);
+          if (row < 0) atomicOr(&t.ctr->error, kErrCapacity);
+          else {
+            t.slots[at].row = (int)row;
+            fresh = 1;
+          }
+        }
+      }
+    }
+    row = __shfl(row, 0);
+    fresh = __shfl(fresh, 0);
+    if (row >= 0) {
+      char* rp = row_ptr(t.rs, row);
+      const float* src = rows + (long long)last * t.dim;
+      for (int e = lane; e < t.dim; e += 64) {
+        if (sizeof(TP) == 2) reinterpret_cast<unsigned short*>(rp)[e] = f32_to_bf16(src[e]);
+        else reinterpret_cast<float*>(rp)[e] = src[e];
+      }
+      if (fresh) {
+        float* st = reinterpret_cast<float*>(rp + (long long)t.dim * (long long)sizeof(TP));
+        for (int e = lane; e < t.state_words * t.dim; e += 64) st[e] = 0.f;
+      }
+    }
+    if (lane == 0) {
+      d->key = kEmptyKey;
+      d->count = 0;
+    }
+  }
+}
+
+// Export step 1: compact the occupied slots.
+__global__ void k_export(TableDev t, long long cap, long long* keys, long long* rows, unsigned* counts) {
+  for (long long i0 = (long long)blockIdx.x * blockDim.x; i0 <= (long long)t.slot_mask;
+       i0 += (long long)gridDim.x * blockDim.x) {
+    const long long i = i0 + threadIdx.x;
+    Slot s;
+    s.key = kEmptyKey;
+    if (i <= (long long)t.slot_mask) s = t.slots[i];
+    const long long at = wave_add(&t.ctr->scratch_count, s.key >= 0);
+    if (at >= 0 && at < cap) {
+      keys[at] = s.key;
+      rows[at] = s.row;
+      counts[at] = s.count;
+    }
+  }
+}
+
+// Export step 2: one wave per exported key copies params and state.
+__global__ void k_export_rows(TableDev t, long long n, const long long* rows, char* params, float* state) {
+  const int lane = threadIdx.x & 63;
+  const int es = t.dtype == RECIS_DTYPE_BF16 ? 2 : 4;
+  const long long pbytes = (long long)t.dim * es;
+  const int sw = t.state_words * t.dim;
+  for (long long k = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); k < n; k += (long long)gridDim.x * 4) {
+    const long long r = rows[k];
+    const char* rp = r >= 0 ? row_ptr(t.rs, r) : nullptr;
+    for (long long b = lane; b < pbytes; b += 64) params[k * pbytes + b] = rp ? rp[b] : 0;
+    if (state) {
+      const float* st = rp ? reinterpret_cast<const float*>(rp + pbytes) : nullptr;
+      for (int e = lane; e < sw; e += 64) state[k * sw + e] = st ? st[e] : 0.f;
+    }
+  }
+}
+
+unsigned grid_for(long long n, int threads) {
+  long long g = (n + threads - 1) / threads;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+void launch_fill_slots(Slot* slots, long long cap, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_slots, dim3(grid_for(cap, 256)), dim3(256), 0, s, slots, cap);
+}
+
+void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_dedup, dim3(grid_for(cap, 256)), dim3(256), 0, s, dd, cap);
+}
+
+void launch_rehash(const Slot* old_slots, long long old_cap, const TableDev& t, hipStream_t s) {
+  hipLaunchKernelGGL(k_rehash, dim3(grid_for(old_cap, 256)), dim3(256), 0, s, old_slots, old_cap, t);
+}
+
+void launch_evict(const TableDev& t, unsigned min_count, long long* num_evicted, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_scratch, dim3(1), dim3(1), 0, s, t.ctr);
+  hipLaunchKernelGGL(k_evict_mark, dim3(grid_for((long long)t.slot_mask + 1, 256)), dim3(256), 0, s, t,
+                     min_count);
+  hipLaunchKernelGGL(k_evict_done, dim3(1), dim3(1), 0, s, t.ctr, num_evicted);
+}
+
+void launch_writeback(const TableDev& t, const long long* keys, long long n, const float* rows,
+                      DedupSlot* dd, unsigned long long dd_mask, int dd_shift, long long* wb_keys,
+                      int* uslot, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_scratch, dim3(1), dim3(1), 0, s, t.ctr);
+  if (n == 0) return;
+  hipLaunchKernelGGL(k_wb_dedup, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, t, keys, n, dd,
+                     dd_mask, dd_shift, wb_keys, uslot);
+  const unsigned g = grid_for(n, 4);
+  if (t.dtype == RECIS_DTYPE_BF16)
+    hipLaunchKernelGGL(k_wb_apply<unsigned short>, dim3(g), dim3(256), 0, s, t, rows, dd, wb_keys, uslot);
+  else
+    hipLaunchKernelGGL(k_wb_apply<float>, dim3(g), dim3(256), 0, s, t, rows, dd, wb_keys, uslot);
+}
+
+void launch_export(const TableDev& t, long long cap, long long* keys, long long* rows, unsigned* counts,
+                   hipStream_t s) {
+  hipLaunchKernelGGL(k_set_scratch, dim3(1), dim3(1), 0, s, t.ctr);
+  hipLaunchKernelGGL(k_export, dim3(grid_for((long long)t.slot_mask + 1, 256)), dim3(256), 0, s, t, cap,
+                     keys, rows, counts);
+}
+
+void launch_export_rows(const TableDev& t, long long n, const long long* rows, void* params, float* state,
+                        hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_export_rows, dim3(grid_for(n, 4)), dim3(256), 0, s, t, n, rows,
+                     static_cast<char*>(params), state);
+}
+
+}  // namespace recis

@@ -1,0 +1,607 @@
+// table.hip -- host side of the recis C ABI: argument checks, table memory
+// (IDMap, EmbeddingBlocks, free list, scratch), growth, descriptor staging and
+// the launches of each call.
+//
+// Pages: "RecIS (Recommendation Intelligence System)" README --
+//   Key optimisations > Efficient dynamic Embedding: a two-level store whose
+//   second level is made of blocks that are added as the table grows;
+//   Core architecture > Embedding Engine: collision-free, extensible KV table.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+using namespace recis;
+
+namespace {
+
+struct ScopedDevice {
+  int prev = -1;
+  explicit ScopedDevice(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) (void)hipSetDevice(dev);
+  }
+  ~ScopedDevice() {
+    int cur;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+void* default_alloc(void*, size_t bytes, hipStream_t) {
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return p;
+}
+
+void default_free(void*, void* p, hipStream_t) {
+  if (p) (void)hipFree(p);
+}
+
+long long next_pow2(long long x) {
+  long long p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+int log2_exact(long long x) {
+  int k = 0;
+  while ((1ll << k) < x) ++k;
+  return k;
+}
+
+bool valid_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+void* tab_alloc(recis_table* t, size_t bytes, hipStream_t s) {
+  if (bytes == 0) bytes = 256;
+  void* p = t->alloc.alloc(t->alloc.ctx, bytes, s);
+  if (p) t->bytes += (long long)bytes;
+  return p;
+}
+
+void tab_free(recis_table* t, void* p, size_t bytes, hipStream_t s) {
+  if (!p) return;
+  t->alloc.free(t->alloc.ctx, p, s);
+  t->bytes -= (long long)(bytes == 0 ? 256 : bytes);
+}
+
+#define HIP_TRY(x)                              \
+  do {                                          \
+    if ((x) != hipSuccess) {                    \
+      (void)hipGetLastError();                  \
+      return RECIS_ERR_HIP;                     \
+    }                                           \
+  } while (0)
+
+recis_status check_launch() {
+  if (hipPeekAtLastError() != hipSuccess) {
+    (void)hipGetLastError();
+    return RECIS_ERR_HIP;
+  }
+  return RECIS_OK;
+}
+
+// Adds blocks until at least `rows` rows are covered (capped at max_rows).
+recis_status grow_rows(recis_table* t, long long rows, hipStream_t s) {
+  rows = std::min<long long>(rows, t->cfg.max_rows);
+  if (rows <= t->rows_alloc) return RECIS_OK;
+  const long long br = t->cfg.block_rows;
+  const long long nblocks = (rows + br - 1) / br;
+  HIP_TRY(hipStreamSynchronize(s));
+  // block pointer table
+  if (nblocks > t->d_blocks_cap) {
+    long long cap = std::max<long long>(16, t->d_blocks_cap);
+    while (cap < nblocks) cap *= 2;
+    char** nb = static_cast<char**>(tab_alloc(t, cap * sizeof(char*), s));
+    if (!nb) return RECIS_ERR_OUT_OF_MEMORY;
+    if (t->d_blocks) tab_free(t, t->d_blocks, t->d_blocks_cap * sizeof(char*), s);
+    t->d_blocks = nb;
+    t->d_blocks_cap = cap;
+  }
+  while ((long long)t->blocks.size() < nblocks) {
+    char* b = static_cast<char*>(tab_alloc(t, (size_t)(br * t->row_bytes), s));
+    if (!b) return RECIS_ERR_OUT_OF_MEMORY;
+    t->blocks.push_back(b);
+  }
+  HIP_TRY(hipMemcpyAsync(t->d_blocks, t->blocks.data(), t->blocks.size() * sizeof(char*),
+                         hipMemcpyHostToDevice, s));
+  const long long new_rows = (long long)t->blocks.size() * br;
+  // free list must hold every row
+  if (new_rows > t->free_cap) {
+    int* nf = static_cast<int*>(tab_alloc(t, (size_t)new_rows * sizeof(int), s));
+    if (!nf) return RECIS_ERR_OUT_OF_MEMORY;
+    if (t->free_list) {
+      HIP_TRY(hipMemcpyAsync(nf, t->free_list, (size_t)t->free_cap * sizeof(int), hipMemcpyDeviceToDevice, s));
+      HIP_TRY(hipStreamSynchronize(s));
+      tab_free(t, t->free_list, (size_t)t->free_cap * sizeof(int), s);
+    }
+    t->free_list = nf;
+    t->free_cap = new_rows;
+  }
+  HIP_TRY(hipStreamSynchronize(s));
+  t->rows_alloc = std::min<long long>(new_rows, t->cfg.max_rows);
+  return RECIS_OK;
+}
+
+// Rebuilds the IDMap into `new_cap` slots (growth or after eviction).
+recis_status rebuild_idmap(recis_table* t, long long new_cap, hipStream_t s) {
+  Slot* old = t->slots;
+  const long long old_cap = t->slot_cap;
+  Slot* ns = static_cast<Slot*>(tab_alloc(t, (size_t)new_cap * sizeof(Slot), s));
+  if (!ns) return RECIS_ERR_OUT_OF_MEMORY;
+  launch_fill_slots(ns, new_cap, s);
+  t->slots = ns;
+  t->slot_cap = new_cap;
+  launch_rehash(old, old_cap, t->dev(), s);
+  recis_status st = check_launch();
+  HIP_TRY(hipStreamSynchronize(s));
+  tab_free(t, old, (size_t)old_cap * sizeof(Slot), s);
+  return st;
+}
+
+recis_status read_counters(recis_table* t, DevCounters* c, hipStream_t s) {
+  HIP_TRY(hipStreamSynchronize(s));
+  HIP_TRY(hipMemcpy(c, t->ctr, sizeof(DevCounters), hipMemcpyDeviceToHost));
+  return RECIS_OK;
+}
+
+// Makes room for a call that may add up to n keys and n rows.
+recis_status ensure_capacity(recis_table* t, long long n, hipStream_t s) {
+  const long long max_keys = (long long)(t->cfg.max_load * (double)t->slot_cap);
+  const bool rows_tight = t->rows_hi + n > t->rows_alloc && t->rows_alloc < t->cfg.max_rows;
+  const bool keys_tight = t->keys_hi + n > max_keys;
+  if (rows_tight || keys_tight) {
+    DevCounters c;
+    recis_status st = read_counters(t, &c, s);
+    if (st != RECIS_OK) return st;
+    t->rows_hi = (long long)c.next_row;
+    t->keys_hi = (long long)c.num_keys;
+    const long long free_rows = c.free_top > 0 ? c.free_top : 0;
+    const long long need_rows = t->rows_hi + std::max<long long>(0, n - free_rows);
+    if (need_rows > t->rows_alloc) {
+      st = grow_rows(t, need_rows + t->cfg.block_rows, s);
+      if (st != RECIS_OK) return st;
+    }
+    long long cap = t->slot_cap;
+    while ((long long)(t->cfg.max_load * (double)cap) < t->keys_hi + n) cap *= 2;
+    if (cap != t->slot_cap) {
+      if (cap > (1ll << 32)) return RECIS_ERR_CAPACITY;
+      st = rebuild_idmap(t, cap, s);
+      if (st != RECIS_OK) return st;
+    }
+  }
+  t->rows_hi += n;
+  t->keys_hi += n;
+  return RECIS_OK;
+}
+
+// Per-step scratch sized for n occurrences.
+recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
+  if (n <= t->scr_cap && t->dd) return RECIS_OK;
+  const long long cap = std::max<long long>(next_pow2(std::max<long long>(n, 1)), 4096);
+  HIP_TRY(hipStreamSynchronize(s));
+  const long long old = t->scr_cap;
+  const long long old_dd = t->dd_cap;
+  const PlanLayout opl = plan_layout(old);
+  tab_free(t, t->dd, (size_t)old_dd * sizeof(DedupSlot), s);
+  tab_free(t, t->occ_slot, (size_t)old * 4, s);
+  tab_free(t, t->occ_rank, (size_t)old * 4, s);
+  tab_free(t, t->uslot, (size_t)old * 4, s);
+  tab_free(t, t->idslot, (size_t)old * 4, s);
+  tab_free(t, t->blk_sums, (size_t)(old / kKeyTile + 2) * 8, s);
+  tab_free(t, t->wb_keys, (size_t)old * 8, s);
+  tab_free(t, t->partials, (size_t)opl.max_chunks * t->cfg.dim * 8, s);
+  t->dd = nullptr;
+  t->scr_cap = 0;
+  const PlanLayout pl = plan_layout(cap);
+  t->dd_cap = 2 * cap;
+  t->dd = static_cast<DedupSlot*>(tab_alloc(t, (size_t)t->dd_cap * sizeof(DedupSlot), s));
+  t->occ_slot = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
+  t->occ_rank = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
+  t->uslot = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
+  t->idslot = static_cast<unsigned*>(tab_alloc(t, (size_t)cap * 4, s));
+  t->blk_sums = static_cast<unsigned long long*>(tab_alloc(t, (size_t)(cap / kKeyTile + 2) * 8, s));
+  t->wb_keys = static_cast<long long*>(tab_alloc(t, (size_t)cap * 8, s));
+  t->partials = static_cast<double*>(tab_alloc(t, (size_t)pl.max_chunks * t->cfg.dim * 8, s));
+  if (!t->dd || !t->occ_slot || !t->occ_rank || !t->uslot || !t->idslot || !t->blk_sums || !t->wb_keys ||
+      !t->partials)
+    return RECIS_ERR_OUT_OF_MEMORY;
+  launch_fill_dedup(t->dd, t->dd_cap, s);
+  recis_status st = check_launch();
+  if (st != RECIS_OK) return st;
+  t->scr_cap = cap;
+  return RECIS_OK;
+}
+
+// Copies `bytes` of host data to device memory through the pinned ring.
+recis_status stage(recis_table* t, const void* src, size_t bytes, hipStream_t s, void** dev_out) {
+  const int k = t->ring_pos;
+  t->ring_pos = (t->ring_pos + 1) % recis_table::kRing;
+  if (t->stage_ev[k]) HIP_TRY(hipEventSynchronize(t->stage_ev[k]));
+  if (bytes > t->stage_cap[k]) {
+    size_t cap = std::max<size_t>(bytes, 4096);
+    if (t->stage_host[k]) (void)hipHostFree(t->stage_host[k]);
+    if (t->stage_dev[k]) tab_free(t, t->stage_dev[k], t->stage_cap[k], s);
+    t->stage_host[k] = nullptr;
+    t->stage_dev[k] = nullptr;
+    t->stage_cap[k] = 0;
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&t->stage_host[k]), cap, hipHostMallocDefault));
+    t->stage_dev[k] = static_cast<char*>(tab_alloc(t, cap, s));
+    if (!t->stage_dev[k]) return RECIS_ERR_OUT_OF_MEMORY;
+    t->stage_cap[k] = cap;
+  }
+  if (!t->stage_ev[k]) HIP_TRY(hipEventCreateWithFlags(&t->stage_ev[k], hipEventDisableTiming));
+  std::memcpy(t->stage_host[k], src, bytes);
+  HIP_TRY(hipMemcpyAsync(t->stage_dev[k], t->stage_host[k], bytes, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipEventRecord(t->stage_ev[k], s));
+  *dev_out = t->stage_dev[k];
+  return RECIS_OK;
+}
+
+}  // namespace
+
+TableDev recis_table::dev() const {
+  TableDev d;
+  d.slots = slots;
+  d.slot_mask = (unsigned long long)(slot_cap - 1);
+  d.slot_shift = 64 - log2_exact(slot_cap);
+  d.ctr = ctr;
+  d.free_list = free_list;
+  d.rs.blocks = d_blocks;
+  d.rs.lb = lb;
+  d.rs.mb = cfg.block_rows - 1;
+  d.rs.stride = row_bytes;
+  d.dim = cfg.dim;
+  d.dtype = cfg.dtype;
+  d.optim = cfg.optim;
+  d.state_words = state_words;
+  d.admit = cfg.admit_threshold == 0 ? 1u : cfg.admit_threshold;
+  d.seed = cfg.seed;
+  d.init_scale = std::ldexp(cfg.init_bound, -23);
+  d.rows_limit = rows_alloc;
+  return d;
+}
+
+extern "C" {
+
+void recis_table_config_default(recis_table_config* c) {
+  if (!c) return;
+  std::memset(c, 0, sizeof(*c));
+  c->dim = 64;
+  c->dtype = RECIS_DTYPE_F32;
+  c->optim = RECIS_OPTIM_ADAGRAD;
+  c->admit_threshold = 1;
+  c->seed = 20250925ull;
+  c->init_bound = 0.05f;
+  c->max_load = 0.5f;
+  c->slot_capacity = 1ll << 20;
+  c->block_rows = 1ll << 20;
+  c->max_rows = (1ll << 31) - 1;
+  c->reserve_rows = 0;
+}
+
+int64_t recis_plan_words(int64_t capacity) {
+  if (capacity < 0) return -1;
+  return plan_layout(capacity).words;
+}
+
+recis_status recis_idmap_create(const recis_table_config* cfg, const recis_allocator* alloc, hipStream_t s,
+                                recis_table** out) {
+  if (!cfg || !out) return RECIS_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (cfg->dtype != RECIS_DTYPE_F32 && cfg->dtype != RECIS_DTYPE_BF16) return RECIS_ERR_INVALID_ARG;
+  if (cfg->optim < RECIS_OPTIM_NONE || cfg->optim > RECIS_OPTIM_ADAM) return RECIS_ERR_INVALID_ARG;
+  if (!(cfg->max_load > 0.f && cfg->max_load <= 0.9f)) return RECIS_ERR_INVALID_ARG;
+  if (!std::isfinite(cfg->init_bound) || cfg->init_bound < 0.f) return RECIS_ERR_INVALID_ARG;
+  if (cfg->slot_capacity < 1 || cfg->slot_capacity > (1ll << 32)) return RECIS_ERR_INVALID_ARG;
+  if (cfg->block_rows < 1 || cfg->block_rows > (1ll << 30)) return RECIS_ERR_INVALID_ARG;
+  if (cfg->max_rows < 1 || cfg->max_rows > (1ll << 31) - 1) return RECIS_ERR_INVALID_ARG;
+  if (cfg->reserve_rows < 0) return RECIS_ERR_INVALID_ARG;
+  if (alloc && (!alloc->alloc || !alloc->free)) return RECIS_ERR_INVALID_ARG;
+  if (!valid_dim(cfg->dim)) return RECIS_ERR_UNSUPPORTED;
+
+  recis_table* t = new (std::nothrow) recis_table();
+  if (!t) return RECIS_ERR_OUT_OF_MEMORY;
+  t->cfg = *cfg;
+  t->cfg.block_rows = std::max<long long>(next_pow2(cfg->block_rows), 64);
+  t->lb = log2_exact(t->cfg.block_rows);
+  t->own_alloc = alloc == nullptr;
+  if (alloc) t->alloc = *alloc;
+  else t->alloc = recis_allocator{nullptr, default_alloc, default_free};
+  t->state_words = cfg->optim == RECIS_OPTIM_ADAM ? 2 : (cfg->optim == RECIS_OPTIM_ADAGRAD ? 1 : 0);
+  t->row_bytes = (long long)cfg->dim * (cfg->dtype == RECIS_DTYPE_BF16 ? 2 : 4) +
+                 (long long)t->state_words * cfg->dim * 4;
+
+  auto fail = [&](recis_status st) {
+    recis_idmap_destroy(t);
+    return st;
+  };
+  t->ctr = static_cast<DevCounters*>(tab_alloc(t, sizeof(DevCounters), s));
+  if (!t->ctr) return fail(RECIS_ERR_OUT_OF_MEMORY);
+  if (hipGetDevice(&t->device) != hipSuccess) return fail(RECIS_ERR_HIP);
+  DevCounters zero;
+  std::memset(&zero, 0, sizeof(zero));
+  if (hipMemcpyAsync(t->ctr, &zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess) return fail(RECIS_ERR_HIP);
+  t->slot_cap = std::max<long long>(next_pow2(cfg->slot_capacity), 64);
+  t->slots = static_cast<Slot*>(tab_alloc(t, (size_t)t->slot_cap * sizeof(Slot), s));
+  if (!t->slots) return fail(RECIS_ERR_OUT_OF_MEMORY);
+  launch_fill_slots(t->slots, t->slot_cap, s);
+  if (check_launch() != RECIS_OK) return fail(RECIS_ERR_HIP);
+  recis_status st = grow_rows(t, std::max<long long>(cfg->reserve_rows, 1), s);
+  if (st != RECIS_OK) return fail(st);
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(RECIS_ERR_HIP);
+  *out = t;
+  return RECIS_OK;
+}
+
+recis_status recis_idmap_destroy(recis_table* t) {
+  if (!t) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  hipStream_t s = nullptr;
+  (void)hipDeviceSynchronize();
+  for (char* b : t->blocks) tab_free(t, b, (size_t)(t->cfg.block_rows * t->row_bytes), s);
+  tab_free(t, t->d_blocks, t->d_blocks_cap * sizeof(char*), s);
+  tab_free(t, t->free_list, (size_t)t->free_cap * 4, s);
+  tab_free(t, t->slots, (size_t)t->slot_cap * sizeof(Slot), s);
+  tab_free(t, t->ctr, sizeof(DevCounters), s);
+  const long long old = t->scr_cap;
+  if (t->dd) {
+    tab_free(t, t->dd, (size_t)t->dd_cap * sizeof(DedupSlot), s);
+    tab_free(t, t->occ_slot, (size_t)old * 4, s);
+    tab_free(t, t->occ_rank, (size_t)old * 4, s);
+    tab_free(t, t->uslot, (size_t)old * 4, s);
+    tab_free(t, t->idslot, (size_t)old * 4, s);
+    tab_free(t, t->blk_sums, (size_t)(old / kKeyTile + 2) * 8, s);
+    tab_free(t, t->wb_keys, (size_t)old * 8, s);
+    tab_free(t, t->partials, (size_t)plan_layout(old).max_chunks * t->cfg.dim * 8, s);
+  }
+  for (int k = 0; k < recis_table::kRing; ++k) {
+    if (t->stage_host[k]) (void)hipHostFree(t->stage_host[k]);
+    if (t->stage_dev[k]) tab_free(t, t->stage_dev[k], t->stage_cap[k], s);
+    if (t->stage_ev[k]) (void)hipEventDestroy(t->stage_ev[k]);
+  }
+  delete t;
+  return RECIS_OK;
+}
+
+recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* feats, int32_t num_feats,
+                                     int32_t batch, uint32_t flags, recis_lookup_result* res, hipStream_t s) {
+  if (!t || !res || num_feats < 0 || batch < 0) return RECIS_ERR_INVALID_ARG;
+  if (num_feats > 0 && !feats) return RECIS_ERR_INVALID_ARG;
+  if (flags & ~(RECIS_FIND_ONLY | RECIS_GROUP_BY_OCCURRENCE)) return RECIS_ERR_INVALID_ARG;
+  if ((long long)num_feats * batch >= (1ll << 31) - 1) return RECIS_ERR_INVALID_ARG;
+  long long N = 0, nbounds = 0;
+  for (int f = 0; f < num_feats; ++f) {
+    const recis_feature_desc& d = feats[f];
+    if (d.n < 0 || (d.n > 0 && !d.values) || !d.bag_offsets) return RECIS_ERR_INVALID_ARG;
+    if (batch == 0 && d.n != 0) return RECIS_ERR_INVALID_ARG;
+    if (d.slot >= (1u << 15)) return RECIS_ERR_INVALID_ARG;
+    if (d.ops & ~(RECIS_OP_HASH | RECIS_OP_MOD | RECIS_OP_BUCKETIZE)) return RECIS_ERR_INVALID_ARG;
+    if ((d.ops & RECIS_OP_BUCKETIZE) && (d.ops & (RECIS_OP_HASH | RECIS_OP_MOD))) return RECIS_ERR_INVALID_ARG;
+    if ((d.ops & RECIS_OP_MOD) && d.mod == 0) return RECIS_ERR_INVALID_ARG;
+    if ((d.ops & RECIS_OP_MOD) && !(d.ops & RECIS_OP_HASH) && d.mod > (uint64_t)INT64_MAX)
+      return RECIS_ERR_INVALID_ARG;
+    if (d.ops & RECIS_OP_BUCKETIZE) {
+      if (d.nb < 0 || (d.nb > 0 && !d.boundaries) || d.nb > (1 << 30)) return RECIS_ERR_INVALID_ARG;
+      for (long long i = 1; i < d.nb; ++i)
+        if (!(d.boundaries[i - 1] < d.boundaries[i])) return RECIS_ERR_INVALID_ARG;
+      nbounds += d.nb;
+    }
+    N += d.n;
+  }
+  if (N > (1ll << 30) || N > res->capacity) return RECIS_ERR_INVALID_ARG;
+  if (!res->bag_offsets || !res->num_unique || !res->unique_offsets || !res->plan) return RECIS_ERR_INVALID_ARG;
+  if (N > 0 && (!res->unique_keys || !res->unique_rows || !res->inverse || !res->counts || !res->grouped))
+    return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+
+  recis_status st = ensure_scratch(t, N, s);
+  if (st != RECIS_OK) return st;
+  if (!(flags & RECIS_FIND_ONLY)) {
+    st = ensure_capacity(t, N, s);
+    if (st != RECIS_OK) return st;
+  }
+
+  // descriptors + boundary pool, staged in one copy
+  std::vector<char> host(sizeof(FeatDev) * (size_t)std::max(num_feats, 1) + 8 * (size_t)nbounds + 16);
+  FeatDev* fd = reinterpret_cast<FeatDev*>(host.data());
+  long long* pool = reinterpret_cast<long long*>(host.data() + sizeof(FeatDev) * (size_t)std::max(num_feats, 1));
+  long long base = 0, tiles = 0, boff = 0;
+  for (int f = 0; f < num_feats; ++f) {
+    const recis_feature_desc& d = feats[f];
+    fd[f].values = reinterpret_cast<const long long*>(d.values);
+    fd[f].offs = d.bag_offsets;
+    fd[f].n = d.n;
+    fd[f].base = base;
+    fd[f].tile_base = tiles;
+    fd[f].mod = d.mod;
+    fd[f].slot = d.slot;
+    fd[f].ops = d.ops;
+    fd[f].bnd_off = (int)boff;
+    fd[f].nb = (d.ops & RECIS_OP_BUCKETIZE) ? (int)d.nb : 0;
+    if (d.ops & RECIS_OP_BUCKETIZE) {
+      std::memcpy(pool + boff, d.boundaries, (size_t)d.nb * 8);
+      boff += d.nb;
+    }
+    base += d.n;
+    tiles += (d.n + kOccTile - 1) / kOccTile;
+  }
+  void* dev = nullptr;
+  st = stage(t, host.data(), host.size(), s, &dev);
+  if (st != RECIS_OK) return st;
+
+  res->n = N;
+  res->num_feats = num_feats;
+  res->batch = batch;
+  res->flags = flags;
+
+  LookupLaunch L;
+  L.feats = static_cast<const FeatDev*>(dev);
+  L.bnd_pool = reinterpret_cast<const long long*>(static_cast<char*>(dev) + sizeof(FeatDev) * (size_t)std::max(num_feats, 1));
+  L.F = num_feats;
+  L.B = batch;
+  L.N = N;
+  L.occ_tiles = tiles;
+  L.flags = flags;
+  L.res = *res;
+  L.dd = t->dd;
+  L.dd_mask = (unsigned long long)(t->dd_cap - 1);
+  L.dd_shift = 64 - log2_exact(t->dd_cap);
+  L.occ_slot = t->occ_slot;
+  L.occ_rank = t->occ_rank;
+  L.uslot = t->uslot;
+  L.idslot = t->idslot;
+  L.blk_sums = t->blk_sums;
+  L.key_tiles = (N + kKeyTile - 1) / kKeyTile;
+  launch_lookup(L, t->dev(), s);
+  return check_launch();
+}
+
+recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted, hipStream_t s) {
+  if (!t) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  launch_evict(t->dev(), min_count, reinterpret_cast<long long*>(num_evicted), s);
+  recis_status st = check_launch();
+  if (st != RECIS_OK) return st;
+  st = rebuild_idmap(t, t->slot_cap, s);
+  if (st != RECIS_OK) return st;
+  DevCounters c;
+  st = read_counters(t, &c, s);
+  if (st != RECIS_OK) return st;
+  t->rows_hi = (long long)c.next_row;
+  t->keys_hi = (long long)c.num_keys;
+  return RECIS_OK;
+}
+
+recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_result* res, int32_t pool, void* out,
+                                   hipStream_t s) {
+  if (!t || !res) return RECIS_ERR_INVALID_ARG;
+  if (pool != RECIS_POOL_SUM && pool != RECIS_POOL_MEAN && pool != RECIS_POOL_NONE) return RECIS_ERR_INVALID_ARG;
+  const long long outn = pool == RECIS_POOL_NONE ? res->n : (long long)res->num_feats * res->batch;
+  if (outn > 0 && !out) return RECIS_ERR_INVALID_ARG;
+  if (res->n > res->capacity || res->n < 0) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  launch_forward(*res, t->dev(), pool, out, s);
+  return check_launch();
+}
+
+recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* res, int32_t pool,
+                                   const void* grad_out, int32_t grad_dtype, const recis_optim_params* opt,
+                                   hipStream_t s) {
+  if (!t || !res || !opt) return RECIS_ERR_INVALID_ARG;
+  if (pool != RECIS_POOL_SUM && pool != RECIS_POOL_MEAN && pool != RECIS_POOL_NONE) return RECIS_ERR_INVALID_ARG;
+  if (grad_dtype != RECIS_DTYPE_F32 && grad_dtype != RECIS_DTYPE_BF16) return RECIS_ERR_INVALID_ARG;
+  const bool by_occ = (res->flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
+  if ((pool == RECIS_POOL_NONE) != by_occ) return RECIS_ERR_INVALID_ARG;
+  if (res->n > 0 && !grad_out) return RECIS_ERR_INVALID_ARG;
+  if (t->cfg.optim == RECIS_OPTIM_NONE) return RECIS_ERR_UNSUPPORTED;
+  if (!(opt->lr >= 0.0) || !(opt->eps >= 0.0)) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  OptConsts oc;
+  oc.lr = (float)opt->lr;
+  oc.eps = (float)opt->eps;
+  oc.b1 = (float)opt->beta1;
+  oc.b2 = (float)opt->beta2;
+  oc.omb1 = (float)(1.0 - opt->beta1);
+  oc.omb2 = (float)(1.0 - opt->beta2);
+  oc.step_size = 0.f;
+  if (t->cfg.optim == RECIS_OPTIM_ADAM) {
+    if (!(opt->beta1 >= 0.0 && opt->beta1 < 1.0 && opt->beta2 >= 0.0 && opt->beta2 < 1.0))
+      return RECIS_ERR_INVALID_ARG;
+    t->adam_step += 1;
+    const double n = (double)t->adam_step;
+    oc.step_size = (float)(opt->lr * std::sqrt(1.0 - std::pow(opt->beta2, n)) / (1.0 - std::pow(opt->beta1, n)));
+  }
+  if (res->n > t->scr_cap) {
+    recis_status st = ensure_scratch(t, res->n, s);
+    if (st != RECIS_OK) return st;
+  }
+  recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, t->partials, s);
+  if (st != RECIS_OK) return st;
+  return check_launch();
+}
+
+recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, const float* rows, hipStream_t s) {
+  if (!t || n < 0 || (n > 0 && (!keys || !rows)) || n > (1ll << 30)) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  recis_status st = ensure_scratch(t, n, s);
+  if (st != RECIS_OK) return st;
+  st = ensure_capacity(t, n, s);
+  if (st != RECIS_OK) return st;
+  launch_writeback(t->dev(), reinterpret_cast<const long long*>(keys), n, rows, t->dd,
+                   (unsigned long long)(t->dd_cap - 1), 64 - log2_exact(t->dd_cap), t->wb_keys, t->uslot, s);
+  return check_launch();
+}
+
+recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int64_t* rows, uint32_t* counts,
+                                void* params, float* state, int64_t* n, hipStream_t s) {
+  if (!t || !n || cap < 0) return RECIS_ERR_INVALID_ARG;
+  if (cap > 0 && (!keys || !rows || !counts || !params)) return RECIS_ERR_INVALID_ARG;
+  if (cap > 0 && t->state_words > 0 && !state) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  launch_export(t->dev(), cap, reinterpret_cast<long long*>(keys), reinterpret_cast<long long*>(rows), counts, s);
+  recis_status st = check_launch();
+  if (st != RECIS_OK) return st;
+  DevCounters c;
+  st = read_counters(t, &c, s);
+  if (st != RECIS_OK) return st;
+  *n = (int64_t)c.scratch_count;
+  const long long m = std::min<long long>(cap, (long long)c.scratch_count);
+  launch_export_rows(t->dev(), m, reinterpret_cast<const long long*>(rows), params,
+                     t->state_words > 0 ? state : nullptr, s);
+  st = check_launch();
+  if (st != RECIS_OK) return st;
+  HIP_TRY(hipStreamSynchronize(s));
+  return RECIS_OK;
+}
+
+recis_status recis_idmap_stats(recis_table* t, recis_table_stats* out, hipStream_t s) {
+  if (!t || !out) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  DevCounters c;
+  recis_status st = read_counters(t, &c, s);
+  if (st != RECIS_OK) return st;
+  out->keys = (int64_t)c.num_keys;
+  out->rows_in_use = (int64_t)c.next_row - (c.free_top > 0 ? c.free_top : 0);
+  out->rows_allocated = t->rows_alloc;
+  out->blocks = (int64_t)t->blocks.size();
+  out->slot_capacity = t->slot_cap;
+  out->adam_step = t->adam_step;
+  out->bytes = t->bytes;
+  return RECIS_OK;
+}
+
+recis_status recis_get_error(recis_table* t, hipStream_t s) {
+  if (!t) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  HIP_TRY(hipStreamSynchronize(s));
+  unsigned err = 0;
+  HIP_TRY(hipMemcpy(&err, &t->ctr->error, sizeof(err), hipMemcpyDeviceToHost));
+  if (err) {
+    unsigned zero = 0;
+    HIP_TRY(hipMemcpy(&t->ctr->error, &zero, sizeof(zero), hipMemcpyHostToDevice));
+  }
+  if (err & kErrCapacity) return RECIS_ERR_CAPACITY;
+  if (err & kErrKeyRange) return RECIS_ERR_KEY_RANGE;
+  if (err & kErrInvalid) return RECIS_ERR_INVALID_ARG;
+  return RECIS_OK;
+}
+
+const char* recis_status_string(recis_status st) {
+  switch (st) {
+    case RECIS_OK: return "ok";
+    case RECIS_ERR_INVALID_ARG: return "invalid argument";
+    case RECIS_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case RECIS_ERR_CAPACITY: return "table capacity exceeded";
+    case RECIS_ERR_KEY_RANGE: return "key outside the 48-bit id / 15-bit slot range";
+    case RECIS_ERR_HIP: return "HIP runtime error";
+    case RECIS_ERR_UNSUPPORTED: return "unsupported combination";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+/* recis.h -- C ABI of the dynamic-embedding hot path on one MI355X (gfx950).
+ *
+ * The library implements the embedding engine that the RecIS pages describe
+ * (page: "RecIS (Recommendation Intelligence System)" README, mirror of
+ * alibaba/RecIS v1.1.0) for one GPU:
+ *   - a two-level table: IDMap (feature ID -> Offset) over EmbeddingBlocks that
+ *     hold parameters and optimizer state, growing block by block
+ *     (section "Key optimisations > Efficient dynamic Embedding");
+ *   - collision-free keys, merged same-attribute tables, eviction/admission
+ *     (section "Core architecture > Embedding Engine");
+ *   - Hash / Mod / Bucketize ID transforms fused into the lookup
+ *     (sections "Core architecture > Feature Engine" and "Key optimisations >
+ *     GPU concurrency");
+ *   - merged, deduplicated requests (section "Key optimisations > Distributed
+ *     optimisation > request merge and split");
+ *   - duplicate-gradient reduction without hot atomics (section "Key
+ *     optimisations > Operator implementation");
+ * plus the exact-assignment cache write of the in-model item cache (page:
+ * "Memory Layer: Train the In-Model Cache for Recommendation Models", sections
+ * "What carries the argument" and "Referee Report > Summary").
+ *
+ * Conventions shared by every call:
+ *   - Every pointer named "device" is GPU memory of the current HIP device;
+ *     "host" pointers are CPU memory.  The caller owns every buffer it passes
+ *     and keeps it alive until the stream work of the call has completed.  No
+ *     call keeps a caller pointer after that.
+ *   - The table owns its IDMap, EmbeddingBlocks and per-step scratch, obtained
+ *     from the allocator given at creation (hipMalloc / hipFree when NULL).
+ *   - All calls are asynchronous and ordered on the stream `s`, except those
+ *     documented as synchronising.  A table is used from one stream at a time;
+ *     separate tables are independent.
+ *   - Argument errors are returned at once and nothing is enqueued.  Errors
+ *     found on the GPU (capacity, key range, malformed bag offsets) are
+ *     recorded in the table's sticky device error word and returned by
+ *     recis_get_error(); the data they concern is then unspecified, but no
+ *     kernel reads or writes out of bounds.
+ */
+#ifndef RECIS_H
+#define RECIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t recis_status;
+#define RECIS_OK 0
+#define RECIS_ERR_INVALID_ARG 1   /* bad pointer, size, enum, unsorted boundaries, small buffer */
+#define RECIS_ERR_OUT_OF_MEMORY 2 /* the allocator returned NULL */
+#define RECIS_ERR_CAPACITY 3      /* max_rows / IDMap probe space exhausted (device, sticky) */
+#define RECIS_ERR_KEY_RANGE 4     /* transformed id outside [0, 2^48) or slot >= 2^15 (device) */
+#define RECIS_ERR_HIP 5           /* a HIP runtime call failed */
+#define RECIS_ERR_UNSUPPORTED 6   /* a valid but unimplemented combination */
+
+/* Parameter storage type; optimizer state is always float32. */
+#define RECIS_DTYPE_F32 0
+#define RECIS_DTYPE_BF16 1
+
+#define RECIS_OPTIM_NONE 0    /* no state; rows change only by writeback */
+#define RECIS_OPTIM_ADAGRAD 1 /* 1 state word per element: accumulated G^2 */
+#define RECIS_OPTIM_ADAM 2    /* 2 state words per element: m, v */
+
+#define RECIS_POOL_SUM 0
+#define RECIS_POOL_MEAN 1
+#define RECIS_POOL_NONE 2 /* gather only: one output row per occurrence */
+
+/* Per-feature ID transforms (Feature Engine).  HASH is MurmurHash3's 64-bit
+ * finalizer of the value's bit pattern; MOD is an unsigned remainder after
+ * HASH and a floor remainder in [0, mod) on a raw signed value; BUCKETIZE
+ * gives the number of boundaries <= value and excludes HASH and MOD. */
+#define RECIS_OP_HASH 1u
+#define RECIS_OP_MOD 2u
+#define RECIS_OP_BUCKETIZE 4u
+
+/* insert_find flags */
+#define RECIS_FIND_ONLY 1u          /* eval: no insert, no count; absent -> row -1 */
+#define RECIS_GROUP_BY_OCCURRENCE 2u /* group occurrences for POOL_NONE backward */
+
+typedef struct recis_table recis_table; /* opaque */
+
+typedef struct {
+  int32_t dim;              /* elements per row: 8, 16, 32, 64, 128 or 256 */
+  int32_t dtype;            /* RECIS_DTYPE_* */
+  int32_t optim;            /* RECIS_OPTIM_* */
+  uint32_t admit_threshold; /* a key gets a row once its count reaches this (0 or 1: at once) */
+  uint64_t seed;            /* initializer seed */
+  float init_bound;         /* rows start uniform on [-init_bound, init_bound) */
+  float max_load;           /* IDMap occupancy that triggers growth, in (0, 0.9] */
+  int64_t slot_capacity;    /* initial IDMap slots (rounded up to a power of two) */
+  int64_t block_rows;       /* rows per EmbeddingBlock (rounded up to a power of two) */
+  int64_t max_rows;         /* hard row limit (<= 2^31 - 1) */
+  int64_t reserve_rows;     /* rows allocated at creation (rounded up to whole blocks) */
+} recis_table_config;
+
+/* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
+ * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^31-1, reserve 0). */
+void recis_table_config_default(recis_table_config* cfg);
+
+/* Device-memory provider.  alloc returns `bytes` of device memory (256-byte
+ * aligned) or NULL; free releases it.  Both may be called with the stream of
+ * the call that needs the memory. */
+typedef struct {
+  void* ctx;
+  void* (*alloc)(void* ctx, size_t bytes, hipStream_t s);
+  void (*free)(void* ctx, void* p, hipStream_t s);
+} recis_allocator;
+
+/* One sparse feature of a batch, CSR over `batch` samples. */
+typedef struct {
+  const int64_t* values;      /* device [n] raw values */
+  const int32_t* bag_offsets; /* device [batch + 1]: 0 = o[0] <= ... <= o[batch] = n */
+  int64_t n;
+  uint32_t slot;              /* feature tag, < 2^15; key = (slot << 48) | id */
+  uint32_t ops;               /* RECIS_OP_* */
+  uint64_t mod;               /* > 0 when RECIS_OP_MOD */
+  const int64_t* boundaries;  /* host [nb], strictly increasing, for RECIS_OP_BUCKETIZE */
+  int64_t nb;
+} recis_feature_desc;
+
+/* Result of one insert_find; all arrays are caller-allocated device memory
+ * sized for `capacity` occurrences (N <= capacity) and are filled on the
+ * stream.  unique order is unspecified.  Fields after `capacity` are written
+ * by insert_find on the host and read by the forward / backward calls. */
+typedef struct {
+  int64_t* unique_keys;    /* [capacity] distinct keys, first num_unique valid */
+  int64_t* unique_rows;    /* [capacity] row of each distinct key, -1 = none */
+  int32_t* inverse;        /* [capacity] occurrence -> index into unique_* */
+  int32_t* counts;         /* [capacity] occurrences of each distinct key */
+  int32_t* bag_offsets;    /* [num_feats * batch + 1] merged CSR, bag f*batch + i */
+  int64_t* num_unique;     /* [1] */
+  int32_t* unique_offsets; /* [capacity + 1] start of each key's group in `grouped` */
+  int32_t* grouped;        /* [capacity] bag ids (or occurrence ids) grouped by key */
+  int32_t* plan;           /* [recis_plan_words(capacity)] backward work plan */
+  int64_t capacity;
+  int64_t n;               /* occurrences of the last insert_find */
+  int32_t num_feats;
+  int32_t batch;
+  uint32_t flags;
+} recis_lookup_result;
+
+/* int32 words needed by recis_lookup_result.plan for `capacity` occurrences. */
+int64_t recis_plan_words(int64_t capacity);
+
+/* Hyper-parameters in double: the library derives 1 - beta1 and 1 - beta2 in
+ * double before rounding them once to the float the kernels use. */
+typedef struct {
+  double lr, beta1, beta2, eps; /* Adam uses all four; Adagrad lr and eps */
+} recis_optim_params;
+
+typedef struct {
+  int64_t keys;           /* keys in the IDMap (with or without a row) */
+  int64_t rows_in_use;    /* rows held by keys */
+  int64_t rows_allocated; /* rows covered by EmbeddingBlocks */
+  int64_t blocks;
+  int64_t slot_capacity;
+  int64_t adam_step;
+  int64_t bytes;          /* device bytes owned by the table */
+} recis_table_stats;
+
+/* Creates a table.  Allocates the IDMap and `reserve_rows` worth of blocks
+ * (synchronises `s` once).  Errors: INVALID_ARG (bad config, NULL out),
+ * UNSUPPORTED (dim/dtype), OUT_OF_MEMORY, HIP. */
+recis_status recis_idmap_create(const recis_table_config* cfg, const recis_allocator* alloc,
+                                hipStream_t s, recis_table** out);
+
+/* Releases everything the table owns.  No work on `t` may be pending. */
+recis_status recis_idmap_destroy(recis_table* t);
+
+/* Lookup of one batch: transform + tag every value, merge the features
+ * feature-major (bag f*batch + i), dedup, then per distinct key probe the
+ * IDMap, insert on a miss (unless RECIS_FIND_ONLY), add its occurrences to
+ * its count, give it a row initialised from (seed, key) with zero optimizer
+ * state once the count reaches admit_threshold, and group the occurrences of
+ * each key for the backward.  Grows the IDMap or the blocks first when the
+ * batch could exceed them (may synchronise `s` then).
+ * feats: host array [num_feats].  Errors: INVALID_ARG, OUT_OF_MEMORY, HIP,
+ * CAPACITY (max_rows reached, host-detected); device: CAPACITY, KEY_RANGE,
+ * INVALID_ARG (bag offsets). */
+recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* feats,
+                                     int32_t num_feats, int32_t batch, uint32_t flags,
+                                     recis_lookup_result* res, hipStream_t s);
+
+/* Eviction pass: removes every key whose count since the last pass is below
+ * min_count (with or without a row), returns its row to the free list, and
+ * restarts the surviving counts at 0.  num_evicted: device [1] (may be NULL). */
+recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted,
+                               hipStream_t s);
+
+/* Forward: SUM / MEAN write float32 out [batch, num_feats * dim] with
+ * out[i, f*dim + d] = pooled element d of bag (f, i) (mean divides by the bag
+ * length; an empty bag gives 0; a key without a row adds zeros); NONE writes
+ * out [N, dim] in the storage dtype, one row per occurrence. */
+recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_result* res,
+                                   int32_t pool, void* out, hipStream_t s);
+
+/* Backward + update: G[u] = sum of the upstream gradients of u's occurrences
+ * (grad_out [batch, num_feats*dim] for SUM / MEAN, divided by the bag length
+ * for MEAN; grad_out [N, dim] for NONE, which needs RECIS_GROUP_BY_OCCURRENCE
+ * at insert_find), summed in double, then one optimizer step on every
+ * distinct key that has a row.  Adam's step counter is the table's and grows
+ * by one per call.  grad_dtype: RECIS_DTYPE_F32 or RECIS_DTYPE_BF16. */
+recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* res, int32_t pool,
+                                   const void* grad_out, int32_t grad_dtype,
+                                   const recis_optim_params* opt, hipStream_t s);
+
+/* Exact-assignment writeback: for i in order, row(keys[i]) <- rows[i] rounded
+ * to the storage dtype, so the last occurrence of a repeated key wins.  An
+ * absent key is inserted and given a row at once; counts are not touched.
+ * keys: device [n] (>= 0); rows: device float32 [n, dim]. */
+recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, const float* rows,
+                             hipStream_t s);
+
+/* Copies the table out (synchronises `s`): keys device [cap], rows device
+ * [cap] (-1 = no row), counts device [cap], params device [cap, dim] in the
+ * storage dtype, state device float32 [cap, slots*dim] (may be NULL when the
+ * optimizer has none).  *n receives the number of keys (host); when it
+ * exceeds cap only cap entries are written.  Order unspecified. */
+recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int64_t* rows,
+                                uint32_t* counts, void* params, float* state, int64_t* n,
+                                hipStream_t s);
+
+/* Table statistics (synchronises `s`); st: host. */
+recis_status recis_idmap_stats(recis_table* t, recis_table_stats* st, hipStream_t s);
+
+/* Synchronises `s` and returns the first error recorded on the device since
+ * the last call, clearing it. */
+recis_status recis_get_error(recis_table* t, hipStream_t s);
+
+const char* recis_status_string(recis_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RECIS_H */

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element, on seeded inputs shaped like the five workloads (scaled so the
+oracle finishes in seconds while still spanning many tiles, ragged tails,
+long duplicate runs and the backward's multi-chunk path).
+
+Bar: bit-exact for keys, inverse, counts, bag segments, row presence, the
+initial rows and bf16 gather / writeback values; pooled outputs within
+1e-5 of the sum of |terms|; updated fp32 parameters within 1e-5 and bf16
+parameters within 1e-2 of max(|w|, lr); optimizer state within 1e-5
+relative."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from harness import (canon_export, canon_lookup, check_export, check_forward, check_lookup,
+                     device_features, forward_out, gpu_step, lookup_flags, make_table, oracle_step)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dynamic_embedding_tables_amd import recis
+    recis.load_library()  # raises when the HIP library is missing
+    print(f"\n[gpu] {torch.cuda.get_device_name(0)}", flush=True)
+
+
+def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopulate=None,
+               export_every=1):
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    table = make_table(spec, **(table_kw or {}))
+    otab = oracle.OracleTable(spec)
+    if prepopulate is not None:
+        cap = max(prepopulate.n, 1)
+        res = recis.LookupResult(cap, prepopulate.num_feats * prepopulate.batch)
+        table.insert_find(device_features(prepopulate), prepopulate.batch, res,
+                          flags=lookup_flags(spec))
+        r = otab.insert_find(prepopulate.features, prepopulate.batch)
+        assert r.status == 0
+    for step, b in enumerate(batches):
+        print(f"[parity] step {step} N={b.n}", flush=True)
+        res = recis.LookupResult(max(b.n, 1), b.num_feats * b.batch)
+        out, _ = gpu_step(table, spec, b, res)
+        r, oout, oab = oracle_step(otab, spec, b)
+        torch.cuda.synchronize()
+        assert table.get_error() == 0
+        check_lookup(canon_lookup(res), r)
+        check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+        if evict_every and (step + 1) % evict_every == 0:
+            ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+            table.evict(evict_min, ne)
+            assert int(ne.item()) == otab.evict(evict_min)
+        if (step + 1) % export_every == 0 or step == len(batches) - 1:
+            check_export(canon_export(table), otab.export(), spec)
+    st = table.stats()
+    assert st.keys == otab.size()
+    assert st.rows_in_use == otab.rows_in_use()
+    table.close()
+
+
+def test_tiny_config_all_ten_steps():
+    run_parity(W.spec_tiny(), [W.tiny_batch(s) for s in range(10)])
+
+
+def test_ctr_config_scaled():
+    run_parity(W.spec_ctr(), [W.ctr_batch(s, batch=256) for s in range(3)])
+
+
+def test_sequence_config_scaled_bf16_long_keys():
+    run_parity(W.spec_seq(), [W.seq_batch(s, batch=12, seq_len=1000) for s in range(3)])
+
+
+def test_capacity_config_scaled_prepopulated():
+    spec = W.spec_capacity()
+    feats = []
+    for f, ids in W.capacity_resident_keys(num_feats=5, per_feature=20000):
+        feats.append(W.FeatureInput(values=ids, bag_offsets=np.array([0, ids.size], np.int32), slot=f))
+    pre = W.Batch(feats, 1, np.zeros((1, 5 * spec.dim), np.float32))
+    batches = [W.capacity_batch(s, batch=1024, num_feats=5, resident_per_feature=20000) for s in range(3)]
+    run_parity(spec, batches, prepopulate=pre)
+
+
+@pytest.mark.parametrize("table", range(5))
+def test_multi_table_config_scaled_with_eviction(table):
+    spec = W.spec_multi(table)
+    batches = [W.multi_batch(s, table, batch=128, num_feats=6) for s in range(6)]
+    run_parity(spec, batches, evict_every=2)
+
+
+def test_growth_of_idmap_and_blocks():
+    spec = W.spec_ctr()
+    run_parity(spec, [W.ctr_batch(s, batch=64, num_feats=8) for s in range(3)],
+               table_kw=dict(slot_capacity=64, block_rows=64))
+
+
+def test_initial_rows_bit_exact():
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    for spec in (W.spec_tiny(), W.spec_seq(), W.spec_multi(0)):
+        spec.admit_threshold = 1
+        b = W.tiny_batch(3, id_space=5000)
+        table = make_table(spec)
+        otab = oracle.OracleTable(spec)
+        res = recis.LookupResult(b.n, b.batch)
+        table.insert_find(device_features(b), b.batch, res, flags=lookup_flags(spec))
+        otab.insert_find(b.features, b.batch)
+        torch.cuda.synchronize()
+        g, o = canon_export(table), otab.export()
+        np.testing.assert_array_equal(g["keys"], o["keys"])
+        np.testing.assert_array_equal(g["params"], o["params"])   # exact, including bf16 rounding
+        assert not g["state"].any()
+        table.close()
+
+
+def test_transforms_hash_mod_bucketize_and_find_only():
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.TableSpec(dim=32, dtype="f32", optim="adagrad", pool="sum", lr=0.01, eps=1e-10)
+    rng = W.rng_for(42)
+    B = 300
+    f0 = W.FeatureInput(values=rng.integers(-2**62, 2**62, 900, dtype=np.int64),
+                        bag_offsets=W.offsets_from_lengths(rng.poisson(3, B)[:B] * 0 + 3), slot=0,
+                        ops=W.OP_HASH | W.OP_MOD, mod=1000)
+    lens = rng.poisson(2.0, B)
+    off = W.offsets_from_lengths(lens)
+    f1 = W.FeatureInput(values=rng.integers(-5000, 5000, int(off[-1]), dtype=np.int64), bag_offsets=off,
+                        slot=7, ops=W.OP_MOD, mod=97)
+    f2 = W.bucketize_feature(rng, B, 50, slot=9)
+    f3 = W.FeatureInput(values=rng.integers(0, 1 << 47, 500, dtype=np.int64),
+                        bag_offsets=W.offsets_from_lengths(np.full(B, 0, np.int64) + np.r_[np.full(250, 2), np.zeros(50, np.int64)]),
+                        slot=(1 << 15) - 1)
+    batches = []
+    for step in range(2):
+        g = W.rng_for(43, step).standard_normal((B, 4 * 32), dtype=np.float32)
+        batches.append(W.Batch([f0, f1, f2, f3], B, g))
+    run_parity(spec, batches)
+    # FIND_ONLY: absent keys report no row and nothing is inserted or counted
+    table = make_table(spec)
+    otab = oracle.OracleTable(spec)
+    b = batches[0]
+    half = W.Batch([f1], B, b.grad[:, :32].copy())
+    res = recis.LookupResult(b.n, b.num_feats * B)
+    gpu_step(table, spec, half, recis.LookupResult(half.n, B))
+    oracle_step(otab, spec, half)
+    out, _ = gpu_step(table, spec, b, res, find_only=True, with_backward=False)
+    r, oout, oab = oracle_step(otab, spec, b, find_only=True, with_backward=False)
+    torch.cuda.synchronize()
+    check_lookup(canon_lookup(res), r)
+    check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+    check_export(canon_export(table), otab.export(), spec)
+
+
+def test_empty_batches_and_empty_bags():
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.TableSpec(dim=16, dtype="f32", optim="adam", pool="mean", lr=1e-3, eps=1e-8)
+    table = make_table(spec)
+    otab = oracle.OracleTable(spec)
+    # all bags empty
+    B = 37
+    f = W.FeatureInput(values=np.zeros(0, np.int64), bag_offsets=np.zeros(B + 1, np.int32), slot=0)
+    b = W.Batch([f, f], B, np.ones((B, 32), np.float32))
+    res = recis.LookupResult(1, 2 * B)
+    out, _ = gpu_step(table, spec, b, res)
+    r, oout, oab = oracle_step(otab, spec, b)
+    torch.cuda.synchronize()
+    assert res.U() == 0 and not out.cpu().numpy().any()
+    check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+    # mostly-empty bags with a few long ones
+    lens = np.zeros(B, np.int64)
+    lens[[3, 17, 36]] = [40, 1, 300]
+    off = W.offsets_from_lengths(lens)
+    vals = W.rng_for(5).integers(0, 50, int(off[-1]), dtype=np.int64)
+    b = W.Batch([W.FeatureInput(values=vals, bag_offsets=off, slot=2)], B,
+                W.rng_for(6).standard_normal((B, 16), dtype=np.float32))
+    res = recis.LookupResult(b.n, B)
+    out, _ = gpu_step(table, spec, b, res)
+    r, oout, oab = oracle_step(otab, spec, b)
+    torch.cuda.synchronize()
+    check_lookup(canon_lookup(res), r)
+    check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+    check_export(canon_export(table), otab.export(), spec)
+    # zero features
+    res = recis.LookupResult(1, 0)
+    table.insert_find([], 5, res)
+    torch.cuda.synchronize()
+    assert res.U() == 0 and table.get_error() == 0
+
+
+def test_one_key_dominates():
+    """A single key with 20k occurrences (80 backward chunks) plus a tail."""
+    spec = W.TableSpec(dim=64, dtype="f32", optim="adagrad", pool="sum", lr=0.01, eps=1e-10)
+    rng = W.rng_for(77)
+    B = 2000
+    lens = rng.poisson(12, B)
+    off = W.offsets_from_lengths(lens)
+    vals = np.where(rng.random(int(off[-1])) < 0.8, 123456789, rng.integers(0, 3000, int(off[-1])))
+    b = W.Batch([W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=1)], B,
+                rng.standard_normal((B, 64), dtype=np.float32))
+    run_parity(spec, [b, b])
+
+
+def test_writeback_cache_last_writer_wins():
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_cache()
+    table = make_table(spec)
+    otab = oracle.OracleTable(spec)
+    keys = W.cache_keys(5000)
+    # pre-insert the cache keys, then write batches with repeated keys
+    table.writeback(torch.from_numpy(keys).cuda(), torch.zeros(keys.size, 256, device="cuda"))
+    otab.writeback(keys, np.zeros((keys.size, 256), np.float32))
+    for step in range(3):
+        k, e = W.cache_writes(step, keys, n=3000)
+        k = np.concatenate([k, np.array([1 << 45, 1 << 45], np.int64)])   # a miss, written twice
+        e = np.concatenate([e, W.rng_for(step, 99).standard_normal((2, 256), dtype=np.float32)])
+        table.writeback(torch.from_numpy(k).cuda(), torch.from_numpy(e).cuda())
+        assert otab.writeback(k, e) == 0
+        torch.cuda.synchronize()
+        assert table.get_error() == 0
+        g, o = canon_export(table), otab.export()
+        np.testing.assert_array_equal(g["keys"], o["keys"])
+        np.testing.assert_array_equal(g["params"], o["params"])   # bit-exact RNE of the last write
+    table.close()
+
+
+def test_device_errors_are_reported():
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_tiny()
+    # raw negative id -> KEY_RANGE
+    table = make_table(spec)
+    b = W.Batch([W.FeatureInput(values=np.array([5, -3, 7], np.int64), bag_offsets=np.array([0, 2, 3], np.int32),
+                                slot=0)], 2, np.ones((2, 16), np.float32))
+    res = recis.LookupResult(3, 2)
+    gpu_step(table, spec, b, res)
+    assert table.get_error() == recis.RECIS_ERR_KEY_RANGE
+    assert table.get_error() == 0   # read-and-clear
+    # malformed bag offsets -> INVALID_ARG, no fault
+    bad = W.Batch([W.FeatureInput(values=np.array([1, 2, 3, 4], np.int64),
+                                  bag_offsets=np.array([0, 3, 1, 4], np.int32), slot=0)], 3,
+                  np.ones((3, 16), np.float32))
+    res = recis.LookupResult(4, 3)
+    gpu_step(table, spec, bad, res)
+    assert table.get_error() == recis.RECIS_ERR_INVALID_ARG
+    table.close()
+    # row capacity -> CAPACITY, keys past the limit get no row
+    table = make_table(spec, max_rows=100, block_rows=64)
+    b = W.tiny_batch(0, id_space=100000)
+    res = recis.LookupResult(b.n, b.batch)
+    table.insert_find(device_features(b), b.batch, res)
+    torch.cuda.synchronize()
+    assert table.get_error() == recis.RECIS_ERR_CAPACITY
+    rows = res.unique_rows[:res.U()].cpu().numpy()
+    assert (rows >= 0).sum() == 100 and rows.max() < 100
+    table.close()
+    # argument errors surface as exceptions
+    with pytest.raises(recis.RecisError):
+        recis.Table(dim=48)
