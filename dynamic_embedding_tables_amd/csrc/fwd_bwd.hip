@@ -10,29 +10,28 @@
 // Work layout: a row is split into 16-byte chunks (4 fp32 or 8 bf16
 // elements); a "group" of C = row_bytes / 16 lanes of one 64-lane wavefront
 // owns one bag (forward) or one distinct key (backward), so a wave moves
-// 64 / C rows per instruction with full 16-byte loads.
+// 64 / C rows per instruction with full 16-byte loads.  A group first fetches
+// the indices of up to C occurrences at once (one lane each), then walks them
+// with cross-lane broadcasts, so up to C row loads are in flight per group.
+//
+// Rows allocated by insert_find stay pending until their first update: their
+// values are the initializer's, recomputed here from (seed, key) instead of
+// being read, and the update writes the row once (parameters and state).
+//
 // Backward, no atomics on data: each key's occurrences were grouped by
-// insert_find.  Keys with <= kShortMax occurrences are reduced by one group
-// and updated at once; longer keys are cut into kChunk-occurrence chunks, one
-// wave per chunk sums its share across its groups with cross-lane shuffles,
-// writes a double-precision partial, and the last chunk to finish (one
-// counter per key) sums the partials in chunk order and applies the update.
+// insert_find.  Keys with more than kShortMax occurrences take two launches:
+// one wave per kChunk-occurrence chunk writes a double-precision partial sum,
+// then one wave per key sums its partials in a fixed order and applies the
+// update (a launch boundary instead of fences and completion counters, which
+// serialise on the per-XCD L2 writeback).  The other keys take a third
+// launch: a block stages the metadata and gradient references of 256
+// consecutive keys in LDS, then each group of KL lanes reduces and updates
+// one key at a time with all of the key's loads in flight together.
 #include "internal.h"
 
 namespace recis {
 
 namespace {
-
-struct FwdArgs {
-  const int* off;
-  const int* inverse;
-  const long long* urows;
-  long long N;
-  long long nbags;
-  int F, B, pool;
-  void* out;
-  RowSpace rs;
-};
 
 template <typename TP>
 struct Vec;
@@ -42,6 +41,10 @@ struct Vec<float> {
   __device__ static void load(const void* p, float (&v)[4]) {
     const float4 x = *reinterpret_cast<const float4*>(p);
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+  __device__ static void unpack(uint4 x, float (&v)[4]) {
+    v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y);
+    v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
   }
   __device__ static void store(void* p, const float (&v)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -53,8 +56,7 @@ struct bf16_t {
 template <>
 struct Vec<bf16_t> {
   static constexpr int E = 8;
-  __device__ static void load(const void* p, float (&v)[8]) {
-    const uint4 x = *reinterpret_cast<const uint4*>(p);
+  __device__ static void unpack(uint4 x, float (&v)[8]) {
     const unsigned w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -62,6 +64,7 @@ struct Vec<bf16_t> {
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
+  __device__ static void load(const void* p, float (&v)[8]) { unpack(*reinterpret_cast<const uint4*>(p), v); }
   __device__ static void store(void* p, const float (&v)[8]) {
     uint4 x;
     x.x = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
@@ -71,6 +74,20 @@ struct Vec<bf16_t> {
     *reinterpret_cast<uint4*>(p) = x;
   }
 };
+
+__device__ __forceinline__ long long shfl64(long long v, int src) {
+  const int lo = __shfl((int)(unsigned long long)v, src);
+  const int hi = __shfl((int)((unsigned long long)v >> 32), src);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double shfl_d(double v, int src) {
+  return __longlong_as_double(shfl64(__double_as_longlong(v), src));
+}
+__device__ __forceinline__ double shfl_xor_d(double v, int m) {
+  const unsigned long long b = __double_as_longlong(v);
+  const int lo = __shfl_xor((int)(unsigned)b, m), hi = __shfl_xor((int)(unsigned)(b >> 32), m);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
 
 // Gradient loads of E consecutive elements (E = 4 or 8) in either dtype.
 template <int E>
@@ -95,13 +112,74 @@ __device__ __forceinline__ void load_grad(const void* base, long long elem, int 
   }
 }
 
+// Where the values of distinct key u live: >= 0 a written row, -1 no row,
+// -2 a pending row (values = initializer of `key`).
+__device__ __forceinline__ long long resolve_row(const TableDev& t, const long long* urows,
+                                                 const long long* ukeys, const unsigned* idslot,
+                                                 long long u, long long& key) {
+  long long r = urows[u];
+  if (r < 0) return -1;
+  if (r & kFreshRow) {
+    r &= ~kFreshRow;
+    if (t.slots[idslot[u]].row & kPendingRow) {
+      key = ukeys[u];
+      return -2;
+    }
+  }
+  return r;
+}
+
 // ------------------------------------------------------------- forward
+struct FwdArgs {
+  const int* off;
+  const int* inverse;
+  const long long* urows;
+  const long long* ukeys;
+  const unsigned* idslot;
+  const long long* occref;
+  long long N;
+  long long nbags;
+  int F, B, pool, current;
+  void* out;
+  TableDev t;
+};
+
+// Row of occurrence j, as resolve_row encodes it.  While the lookup is
+// current its per-occurrence reference is used directly (one load);
+// otherwise the distinct key's row and the IDMap slot are read.
+__device__ __forceinline__ long long occurrence_row(const FwdArgs& a, long long j, long long& key) {
+  if (a.current) {
+    const long long v = a.occref[j];
+    if (v == kOccNoRow) return -1;
+    if (v < 0) {
+      key = (long long)((unsigned long long)v & ~kOccPendingBit);
+      return -2;
+    }
+    return v;
+  }
+  return resolve_row(a.t, a.urows, a.ukeys, a.idslot, a.inverse[j], key);
+}
+
+template <typename TP, int E>
+__device__ __forceinline__ void fetch_values(const TableDev& t, long long r, long long key, int lane,
+                                             float (&v)[E]) {
+  if (r >= 0) {
+    Vec<TP>::load(row_ptr(t.rs, r) + lane * 16, v);
+  } else if (r == -2) {
+    Vec<TP>::unpack(init_chunk(t, key, lane), v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = 0.f;
+  }
+}
+
 template <int D, typename TP>
 __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
   constexpr int E = Vec<TP>::E;
   constexpr int C = D / E;  // lanes per bag
   constexpr int GPB = 256 / C;
-  const int lane = threadIdx.x % C;
+  const int wl = threadIdx.x & 63;
+  const int lane = wl % C, gbase = wl - lane;
   const long long bag = (long long)blockIdx.x * GPB + threadIdx.x / C;
   if (bag >= a.nbags) return;
   long long lo = a.off[bag], hi = a.off[bag + 1];
@@ -110,29 +188,29 @@ __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  long long j = lo;
-  for (; j + 4 <= hi; j += 4) {
-    long long r[4];
+  for (long long base = lo; base < hi; base += C) {
+    const int cnt = (int)(hi - base < C ? hi - base : C);
+    long long enc = -1, key = 0;
+    if (lane < cnt) enc = occurrence_row(a, base + lane, key);
+    int q = 0;
+    for (; q + 4 <= cnt; q += 4) {
+      float v[4][E];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = a.urows[a.inverse[j + q]];
-    float v[4][E];
+      for (int x = 0; x < 4; ++x) {
+        const long long r = shfl64(enc, gbase + q + x);
+        const long long k = r == -2 ? shfl64(key, gbase + q + x) : 0;
+        fetch_values<TP, E>(a.t, r, k, lane, v[x]);
+      }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (r[q] >= 0) Vec<TP>::load(row_ptr(a.rs, r[q]) + lane * 16, v[q]);
-      else
+      for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[q][e] = 0.f;
+        for (int e = 0; e < E; ++e) acc[e] += v[x][e];
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += v[q][e];
-  }
-  for (; j < hi; ++j) {
-    const long long r = a.urows[a.inverse[j]];
-    if (r >= 0) {
+    for (; q < cnt; ++q) {
       float v[E];
-      Vec<TP>::load(row_ptr(a.rs, r) + lane * 16, v);
+      const long long r = shfl64(enc, gbase + q);
+      const long long k = r == -2 ? shfl64(key, gbase + q) : 0;
+      fetch_values<TP, E>(a.t, r, k, lane, v);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] += v[e];
     }
@@ -157,9 +235,11 @@ __global__ __launch_bounds__(256) void k_fwd_gather(FwdArgs a) {
   const int lane = threadIdx.x % C;
   const long long j = (long long)blockIdx.x * GPB + threadIdx.x / C;
   if (j >= a.N) return;
-  const long long r = a.urows[a.inverse[j]];
+  long long key = 0;
+  const long long r = occurrence_row(a, j, key);
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (r >= 0) v = *reinterpret_cast<const uint4*>(row_ptr(a.rs, r) + lane * 16);
+  if (r >= 0) v = *reinterpret_cast<const uint4*>(row_ptr(a.t.rs, r) + lane * 16);
+  else if (r == -2) v = init_chunk(a.t, key, lane);
   reinterpret_cast<uint4*>(static_cast<char*>(a.out) + (j * D * (long long)sizeof(TP)))[lane] = v;
 }
 
@@ -169,177 +249,414 @@ struct BwdArgs {
   const int* grouped;
   const int* uoff;
   const int* counts;
-  const long long* urows;
+  long long* urows;
+  const long long* ukeys;
   const long long* num_unique;
   const int* plan;
+  const unsigned* idslot;
   PlanLayout pl;
   int F, B, pool, gdt;
   const void* grad;
   OptConsts oc;
-  RowSpace rs;
+  TableDev t;
   double* partials;
+  int current;  // no update since the lookup: a fresh row is still pending
 };
 
-// Adds the upstream gradient of one grouped entry (a bag, or an occurrence
-// for POOL_NONE) to acc, element chunk `lane`.
-template <int D, int E>
-__device__ __forceinline__ void add_grad(const BwdArgs& a, int gval, int lane, double (&acc)[E]) {
-  float g[E];
+constexpr int kBwdKeys = kThreads;  // distinct keys per block tile (short path)
+constexpr int kBwdStage = 1024;     // gradient entries staged in LDS per tile
+#ifndef RECIS_BWD_LANES
+#define RECIS_BWD_LANES 16
+#endif
+constexpr int kBwdLanes = RECIS_BWD_LANES;  // lanes per key in the short path (at most)
+#ifndef RECIS_BWD_BATCH
+#define RECIS_BWD_BATCH 16
+#endif
+constexpr int kBwdBatchElems = RECIS_BWD_BATCH;  // gradient elements per lane in flight (short path)
+
+// Upstream-gradient row of grouped entry gval (a bag, or an occurrence for
+// POOL_NONE) and the scale it enters with (1 / bag length for mean pooling).
+template <int D>
+__device__ __forceinline__ void grad_ref(const BwdArgs& a, int gval, int& grow, double& scale) {
+  scale = 1.0;
   if (a.pool == RECIS_POOL_NONE) {
-    load_grad<E>(a.grad, (long long)gval * D + lane * E, a.gdt, g);
+    grow = gval;
+    return;
+  }
+  const int f = gval / a.B, i = gval - f * a.B;
+  grow = i * a.F + f;
+  if (a.pool == RECIS_POOL_MEAN) {
+    const int len = a.off[gval + 1] - a.off[gval];
+    scale = 1.0 / (double)(len > 0 ? len : 1);
+  }
+}
+
+// A row is split into NCH 16-byte chunks of E elements; with KL lanes per key
+// each lane owns CH = NCH / KL chunks, chunk ch * KL + lane, so that every
+// load instruction of a group covers KL * 16 contiguous bytes.
+template <int D, typename TP, int KL>
+struct RowMap {
+  static constexpr int E = Vec<TP>::E;
+  static constexpr int NCH = D / E;
+  static constexpr int CH = NCH / KL;
+  static_assert(CH >= 1 && CH * KL == NCH, "lanes per key must divide the row's chunks");
+};
+
+// Row state of this lane's chunks: the stored values, or for a pending row
+// the initializer's values and zero optimizer state.
+template <int D, typename TP, int OPT, int KL>
+__device__ __forceinline__ void load_row(const BwdArgs& a, long long row, bool pending, long long key, int lane,
+                                         float (&w)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
+                                         float (&s0)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
+                                         float (&s1)[RowMap<D, TP, KL>::CH][Vec<TP>::E]) {
+  constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
+  if (pending) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += (double)g[e];
-  } else {
-    const int f = gval / a.B, i = gval - f * a.B;
-    load_grad<E>(a.grad, ((long long)i * a.F + f) * D + lane * E, a.gdt, g);
-    if (a.pool == RECIS_POOL_MEAN) {
-      const int len = a.off[gval + 1] - a.off[gval];
-      const double inv = 1.0 / (double)(len > 0 ? len : 1);
+    for (int ch = 0; ch < CH; ++ch) {
+      Vec<TP>::unpack(init_chunk(a.t, key, ch * KL + lane), w[ch]);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += (double)g[e] * inv;
+      for (int e = 0; e < E; ++e) s0[ch][e] = s1[ch][e] = 0.f;
+    }
+    return;
+  }
+  const char* rp = row_ptr(a.t.rs, row);
+  const float* st = reinterpret_cast<const float*>(rp + D * (int)sizeof(TP));
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = ch * KL + lane;
+    Vec<TP>::load(rp + c * 16, w[ch]);
+    Vec<float>::load(st + c * E, *reinterpret_cast<float(*)[4]>(s0[ch]));
+    if constexpr (E == 8) Vec<float>::load(st + c * E + 4, *reinterpret_cast<float(*)[4]>(s0[ch] + 4));
+    if constexpr (OPT == RECIS_OPTIM_ADAM) {
+      Vec<float>::load(st + D + c * E, *reinterpret_cast<float(*)[4]>(s1[ch]));
+      if constexpr (E == 8) Vec<float>::load(st + D + c * E + 4, *reinterpret_cast<float(*)[4]>(s1[ch] + 4));
+    }
+  }
+}
+
+// One optimizer step on this lane's chunks, then their stores.  The square
+// root and reciprocal are the hardware's (about 1 ulp each).
+template <int D, typename TP, int OPT, int KL>
+__device__ __forceinline__ void update_store(const BwdArgs& a, long long row, int lane,
+                                             const double (&G)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
+                                             float (&w)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
+                                             float (&s0)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
+                                             float (&s1)[RowMap<D, TP, KL>::CH][Vec<TP>::E]) {
+  constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
+  char* rp = row_ptr(a.t.rs, row);
+  float* st = reinterpret_cast<float*>(rp + D * (int)sizeof(TP));
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = ch * KL + lane;
+    if constexpr (OPT == RECIS_OPTIM_ADAGRAD) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float g = (float)G[ch][e];
+        s0[ch][e] = s0[ch][e] + g * g;
+        w[ch][e] = w[ch][e] - a.oc.lr * g * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(s0[ch][e]) + a.oc.eps);
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += (double)g[e];
+      for (int e = 0; e < E; ++e) {
+        const float g = (float)G[ch][e];
+        s0[ch][e] = a.oc.b1 * s0[ch][e] + a.oc.omb1 * g;
+        s1[ch][e] = a.oc.b2 * s1[ch][e] + a.oc.omb2 * (g * g);
+        w[ch][e] = w[ch][e] - a.oc.step_size * s0[ch][e] *
+                                  __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(s1[ch][e]) + a.oc.eps);
+      }
+      Vec<float>::store(st + D + c * E, *reinterpret_cast<float(*)[4]>(s1[ch]));
+      if constexpr (E == 8) Vec<float>::store(st + D + c * E + 4, *reinterpret_cast<float(*)[4]>(s1[ch] + 4));
     }
+    Vec<float>::store(st + c * E, *reinterpret_cast<float(*)[4]>(s0[ch]));
+    if constexpr (E == 8) Vec<float>::store(st + c * E + 4, *reinterpret_cast<float(*)[4]>(s0[ch] + 4));
+    Vec<TP>::store(rp + c * 16, w[ch]);
   }
 }
 
-// One optimizer step on element chunk `lane` of row r.
-template <int D, typename TP, int OPT>
-__device__ __forceinline__ void apply_update(const BwdArgs& a, long long r, int lane,
-                                             const double (&G)[Vec<TP>::E]) {
-  constexpr int E = Vec<TP>::E;
-  char* rp = row_ptr(a.rs, r);
-  void* wp = rp + lane * 16;
-  float* st = reinterpret_cast<float*>(rp + D * (int)sizeof(TP)) + lane * E;
-  float w[E], s0[E];
-  Vec<TP>::load(wp, w);
-  Vec<float>::load(st, *reinterpret_cast<float(*)[4]>(s0));
-  if constexpr (E == 8) Vec<float>::load(st + 4, *reinterpret_cast<float(*)[4]>(s0 + 4));
-  if constexpr (OPT == RECIS_OPTIM_ADAGRAD) {
+// acc += scale * (upstream-gradient row grow), this lane's chunks.
+template <int D, typename TP, int KL>
+__device__ __forceinline__ void add_grad_row(const BwdArgs& a, int grow, double scale, int lane,
+                                             double (&acc)[RowMap<D, TP, KL>::CH][Vec<TP>::E]) {
+  constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
+  float g[CH][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float g = (float)G[e];
-      s0[e] = s0[e] + g * g;
-      w[e] = w[e] - a.oc.lr * g / (sqrtf(s0[e]) + a.oc.eps);
-    }
-  } else {
-    float s1[E];
-    Vec<float>::load(st + D, *reinterpret_cast<float(*)[4]>(s1));
-    if constexpr (E == 8) Vec<float>::load(st + D + 4, *reinterpret_cast<float(*)[4]>(s1 + 4));
+  for (int ch = 0; ch < CH; ++ch) load_grad<E>(a.grad, (long long)grow * D + (ch * KL + lane) * E, a.gdt, g[ch]);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float g = (float)G[e];
-      s0[e] = a.oc.b1 * s0[e] + a.oc.omb1 * g;
-      s1[e] = a.oc.b2 * s1[e] + a.oc.omb2 * (g * g);
-      w[e] = w[e] - a.oc.step_size * s0[e] / (sqrtf(s1[e]) + a.oc.eps);
-    }
-    Vec<float>::store(st + D, *reinterpret_cast<float(*)[4]>(s1));
-    if constexpr (E == 8) Vec<float>::store(st + D + 4, *reinterpret_cast<float(*)[4]>(s1 + 4));
+  for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[ch][e] += (double)g[ch][e] * scale;
+}
+
+// Block-wide exclusive scan of one int per thread (kThreads = 256).
+__device__ __forceinline__ int block_scan_int(int v, int* total) {
+  __shared__ int s_w[kThreads / 64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl(x, lane >= d ? lane - d : lane);
+    if (lane >= d) x += y;
   }
-  Vec<float>::store(st, *reinterpret_cast<float(*)[4]>(s0));
-  if constexpr (E == 8) Vec<float>::store(st + 4, *reinterpret_cast<float(*)[4]>(s0 + 4));
-  Vec<TP>::store(wp, w);
-}
-
-template <int D, typename TP, int OPT>
-__global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
-  constexpr int E = Vec<TP>::E;
-  constexpr int C = D / E;
-  constexpr int GPB = 256 / C;
-  const int lane = threadIdx.x % C;
-  const long long U = *a.num_unique;
-  const long long step = (long long)gridDim.x * GPB;
-  for (long long u = (long long)blockIdx.x * GPB + threadIdx.x / C; u < U; u += step) {
-    const int c = a.counts[u];
-    if (c > kShortMax) continue;
-    const long long r = a.urows[u];
-    if (r < 0) continue;
-    const int o = a.uoff[u];
-    double acc[E];
+  if (lane == 63) s_w[wid] = x;
+  __syncthreads();
+  int before = 0, all = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0;
-    int k = 0;
-    for (; k + 4 <= c; k += 4) {
-      const int g0 = a.grouped[o + k], g1 = a.grouped[o + k + 1];
-      const int g2 = a.grouped[o + k + 2], g3 = a.grouped[o + k + 3];
-      add_grad<D, E>(a, g0, lane, acc);
-      add_grad<D, E>(a, g1, lane, acc);
-      add_grad<D, E>(a, g2, lane, acc);
-      add_grad<D, E>(a, g3, lane, acc);
-    }
-    for (; k < c; ++k) add_grad<D, E>(a, a.grouped[o + k], lane, acc);
-    apply_update<D, TP, OPT>(a, r, lane, acc);
+  for (int w = 0; w < kThreads / 64; ++w) {
+    before += w < wid ? s_w[w] : 0;
+    all += s_w[w];
   }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
 }
 
-__device__ __forceinline__ double shfl_xor_d(double v, int m) {
-  const unsigned long long b = __double_as_longlong(v);
-  const int lo = __shfl_xor((int)(unsigned)b, m), hi = __shfl_xor((int)(unsigned)(b >> 32), m);
-  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
-}
-
-__device__ __forceinline__ double load_coherent(const double* p) {
-  const unsigned long long v =
-      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
-                        __HIP_MEMORY_SCOPE_AGENT);
-  return __longlong_as_double((long long)v);
-}
-
-template <int D, typename TP, int OPT>
-__global__ __launch_bounds__(256) void k_bwd_long(BwdArgs a) {
+// Long keys, pass 1: one wave per kChunk-entry chunk.  The chunk's entries
+// sit one per lane; each group of C = D / E lanes sums a contiguous share of
+// them (kLongBatch rows in flight), a butterfly across the groups merges the
+// shares, and the chunk's double-precision partial is stored.  No atomics and
+// no cross-block waits: the finishing pass runs as the next launch.
+template <int D, typename TP>
+__global__ __launch_bounds__(256) void k_bwd_long_partial(BwdArgs a) {
   constexpr int E = Vec<TP>::E;
   constexpr int C = D / E;
-  constexpr int GPW = 64 / C;  // groups per wave
+  constexpr int GPW = 64 / C;           // groups per wave
+  constexpr int PER = kChunk / GPW;     // entries per group
+  constexpr int GF = PER < 8 ? PER : 8;  // gradient rows in flight per group
   const int wl = threadIdx.x & 63;
   const int lane = wl % C, g = wl / C;
   const int nchunks = a.plan[1];
-  const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long long nwaves = (long long)gridDim.x * 4;
   const int* long_u = a.plan + a.pl.o_long_u;
   const int* long_base = a.plan + a.pl.o_long_base;
-  const int* long_nch = a.plan + a.pl.o_long_nch;
-  int* long_done = const_cast<int*>(a.plan) + a.pl.o_long_done;
   const int* owner = a.plan + a.pl.o_chunk_owner;
-  for (long long q = wave; q < nchunks; q += nwaves) {
+  for (long long q = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); q < nchunks; q += nwaves) {
     const int idx = owner[q];
-    const int u = long_u[idx], cb = long_base[idx], nch = long_nch[idx];
-    const long long r = a.urows[u];
+    const int u = long_u[idx], cb = long_base[idx];
     const int o = a.uoff[u], c = a.counts[u];
     const int k0 = (int)(q - cb) * kChunk;
-    const int k1 = k0 + kChunk < c ? k0 + kChunk : c;
-    double acc[E];
+    const int cnt = c - k0 < kChunk ? c - k0 : kChunk;
+    int gr = 0;
+    double scale = 0.0;
+    if (wl < cnt) grad_ref<D>(a, a.grouped[o + k0 + wl], gr, scale);
+    double acc[1][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0;
-    for (int k = k0 + g; k < k1; k += GPW) add_grad<D, E>(a, a.grouped[o + k], lane, acc);
+    for (int e = 0; e < E; ++e) acc[0][e] = 0.0;
+    // All 64 lanes take part in every shuffle: the trip counts are constants
+    // and each group masks its own loads.
+#pragma unroll 1
+    for (int x0 = 0; x0 < PER; x0 += GF) {
+      float gv[GF][E];
+      double sv[GF];
+#pragma unroll
+      for (int x = 0; x < GF; ++x) {
+        const int src = g * PER + x0 + x;
+        const int s = src < cnt ? src : 0;
+        const int gi = __shfl(gr, s);
+        sv[x] = shfl_d(scale, s);
+        if (src < cnt) {
+          load_grad<E>(a.grad, (long long)gi * D + lane * E, a.gdt, gv[x]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) gv[x][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < GF; ++x)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[0][e] += (double)gv[x][e] * sv[x];
+    }
 #pragma unroll
     for (int m = C; m < 64; m <<= 1)
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += shfl_xor_d(acc[e], m);
+      for (int e = 0; e < E; ++e) acc[0][e] += shfl_xor_d(acc[0][e], m);
     if (g == 0) {
       double* pp = a.partials + q * D + lane * E;
 #pragma unroll
-      for (int e = 0; e < E; ++e) pp[e] = acc[e];
+      for (int e = 0; e < E; ++e) pp[e] = acc[0][e];
     }
-    __threadfence();
-    int last = 0;
-    if (wl == 0) last = atomicAdd(&long_done[idx], 1) == nch - 1;
-    last = __shfl(last, 0);
-    if (last) {
-      __threadfence();
-      if (g == 0) {
-        double G[E];
+  }
+}
+
+// Long keys, pass 2: one wave per long key sums its chunk partials (every
+// group loads kMergeBatch partials at a time, then a butterfly across the
+// groups; a fixed order, so runs repeat exactly) and applies the update.
+template <int D, typename TP, int OPT>
+__global__ __launch_bounds__(256) void k_bwd_long_final(BwdArgs a) {
+  constexpr int E = Vec<TP>::E;
+  constexpr int C = D / E;
+  constexpr int GPW = 64 / C;
+  constexpr int kMergeBatch = 4;
+  const int wl = threadIdx.x & 63;
+  const int lane = wl % C, g = wl / C;
+  const int nlong = a.plan[0];
+  const long long nwaves = (long long)gridDim.x * 4;
+  for (long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); idx < nlong; idx += nwaves) {
+    const int u = a.plan[a.pl.o_long_u + idx];
+    const int cb = a.plan[a.pl.o_long_base + idx], nch = a.plan[a.pl.o_long_nch + idx];
+    long long r = a.urows[u];
+    if (r < 0) continue;  // no row (FIND_ONLY miss): nothing to update
+    const bool fresh = (r & kFreshRow) != 0;
+    r &= ~kFreshRow;
+    unsigned sl = 0;
+    bool pending = false;
+    if (fresh) {
+      sl = a.idslot[u];
+      pending = a.current ? true : (a.t.slots[sl].row & kPendingRow) != 0;
+    }
+    double G[1][E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) G[e] = 0.0;
-        for (int p = 0; p < nch; ++p) {
-          const double* pp = a.partials + (long long)(cb + p) * D + lane * E;
+    for (int e = 0; e < E; ++e) G[0][e] = 0.0;
+    for (int p0 = 0; p0 < nch; p0 += GPW * kMergeBatch) {
+      double part[kMergeBatch][E];
 #pragma unroll
-          for (int e = 0; e < E; ++e) G[e] += load_coherent(pp + e);
-        }
-        if (r >= 0) apply_update<D, TP, OPT>(a, r, lane, G);
+      for (int m = 0; m < kMergeBatch; ++m) {
+        const int p = p0 + m * GPW + g;
+        const double* pp = a.partials + (long long)(cb + (p < nch ? p : 0)) * D + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) part[m][e] = p < nch ? pp[e] : 0.0;
       }
-      if (wl == 0) long_done[idx] = 0;
+#pragma unroll
+      for (int m = 0; m < kMergeBatch; ++m)
+#pragma unroll
+        for (int e = 0; e < E; ++e) G[0][e] += part[m][e];
     }
+#pragma unroll
+    for (int m = C; m < 64; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e) G[0][e] += shfl_xor_d(G[0][e], m);
+    if (g == 0) {
+      float w[1][E], s0[1][E], s1[1][E];
+      load_row<D, TP, OPT, C>(a, r, pending, pending ? a.ukeys[u] : 0, lane, w, s0, s1);
+      update_store<D, TP, OPT, C>(a, r, lane, G, w, s0, s1);
+    }
+    if (wl == 0 && fresh) {
+      if (pending) a.t.slots[sl].row = (int)r;
+      a.urows[u] = r;
+    }
+  }
+}
+
+// Short keys (<= kShortMax entries).  A block takes kBwdKeys consecutive keys,
+// stages their metadata and (when they fit) their gradient references in LDS
+// in two coalesced passes, then each group of KL lanes updates its keys one
+// at a time with the row and gradient loads of a key in flight together.
+template <int D, typename TP, int OPT, int KL>
+__global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
+  constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
+  constexpr int GPB = 256 / KL;
+  constexpr int GB = CH * E >= kBwdBatchElems ? 1 : kBwdBatchElems / (CH * E);  // gradient rows per batch
+  const int wl = threadIdx.x & 63;
+  const int lane = wl % KL, gbase = wl - lane;
+  const int tid = threadIdx.x;
+  __shared__ int s_o[kBwdKeys], s_c[kBwdKeys], s_eo[kBwdKeys + 1], s_st[kBwdKeys];
+  __shared__ long long s_r[kBwdKeys], s_key[kBwdKeys];
+  __shared__ unsigned s_sl[kBwdKeys];
+  __shared__ int s_grow[kBwdStage];
+  __shared__ double s_sc[kBwdStage];
+  const long long U = *a.num_unique;
+  for (long long t0 = (long long)blockIdx.x * kBwdKeys; t0 < U; t0 += (long long)gridDim.x * kBwdKeys) {
+    const long long u = t0 + tid;
+    int c = 0, o = 0, st = 0;  // st: 0 written row, 1 fresh but written, 2 pending
+    long long r = -1, key = 0;
+    unsigned sl = 0;
+    if (u < U) {
+      c = a.counts[u];
+      o = a.uoff[u];
+      r = a.urows[u];
+      if (r >= 0 && (r & kFreshRow)) {
+        r &= ~kFreshRow;
+        sl = a.idslot[u];
+        key = a.ukeys[u];
+        st = a.current ? 2 : ((a.t.slots[sl].row & kPendingRow) ? 2 : 1);
+      }
+      if (c > kShortMax) r = -1;  // the long-key kernel updates it
+    }
+    const int ce = r >= 0 ? c : 0;
+    int tot;
+    const int eo = block_scan_int(ce, &tot);
+    s_o[tid] = o;
+    s_c[tid] = ce;
+    s_eo[tid] = eo;
+    s_st[tid] = st;
+    s_r[tid] = r;
+    s_key[tid] = key;
+    s_sl[tid] = sl;
+    if (tid == 0) s_eo[kBwdKeys] = tot;
+    __syncthreads();
+    const bool staged = tot <= kBwdStage;
+    if (staged) {
+      for (int i = tid; i < tot; i += kThreads) {
+        int lo = 0, hi = kBwdKeys;  // the key whose staged range holds i
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_eo[mid] <= i) lo = mid;
+          else hi = mid;
+        }
+        int go;
+        double sc;
+        grad_ref<D>(a, a.grouped[s_o[lo] + (i - s_eo[lo])], go, sc);
+        s_grow[i] = go;
+        s_sc[i] = sc;
+      }
+      __syncthreads();
+    }
+    for (int k = tid / KL; k < kBwdKeys; k += GPB) {
+      const long long row = s_r[k];
+      if (row < 0) continue;
+      const int kst = s_st[k], kc = s_c[k];
+      float w[CH][E], s0[CH][E], s1[CH][E];
+      load_row<D, TP, OPT, KL>(a, row, kst == 2, s_key[k], lane, w, s0, s1);
+      double acc[CH][E];
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[ch][e] = 0.0;
+      if (staged) {
+        // up to GB gradient rows of the key in flight together
+        const int base = s_eo[k];
+        for (int x0 = 0; x0 < kc; x0 += GB) {
+          float gv[GB][CH][E];
+#pragma unroll
+          for (int i = 0; i < GB; ++i) {
+            const int go = x0 + i < kc ? s_grow[base + x0 + i] : 0;
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) {
+              if (x0 + i < kc) {
+                load_grad<E>(a.grad, (long long)go * D + (ch * KL + lane) * E, a.gdt, gv[i][ch]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) gv[i][ch][e] = 0.f;
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < GB; ++i) {
+            const double sc = x0 + i < kc ? s_sc[base + x0 + i] : 0.0;
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+              for (int e = 0; e < E; ++e) acc[ch][e] += (double)gv[i][ch][e] * sc;
+          }
+        }
+      } else {
+        // entries straight from global memory, KL at a time (one per lane)
+        const int ko = s_o[k];
+        for (int b0 = 0; b0 < kc; b0 += KL) {
+          const int cnt = kc - b0 < KL ? kc - b0 : KL;
+          int grow = 0;
+          double scale = 0.0;
+          if (lane < cnt) grad_ref<D>(a, a.grouped[ko + b0 + lane], grow, scale);
+          for (int x = 0; x < cnt; ++x)
+            add_grad_row<D, TP, KL>(a, __shfl(grow, gbase + x), shfl_d(scale, gbase + x), lane, acc);
+        }
+      }
+      update_store<D, TP, OPT, KL>(a, row, lane, acc, w, s0, s1);
+      if (lane == 0 && kst != 0) {
+        if (kst == 2) a.t.slots[s_sl[k]].row = (int)row;
+        a.urows[t0 + k] = row;
+      }
+    }
+    __syncthreads();  // the tile's LDS is reused by the next tile
   }
 }
 
@@ -357,28 +674,29 @@ void fwd_dispatch(const FwdArgs& a, int pool, hipStream_t s) {
 }
 
 template <int D, typename TP, int OPT>
-void bwd_dispatch(const BwdArgs& a, long long cap, hipStream_t s) {
-  constexpr int C = D / Vec<TP>::E;
-  constexpr int GPB = 256 / C;
-  long long blocks = (cap + GPB - 1) / GPB;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((k_bwd_short<D, TP, OPT>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  long long lb = (cap / kChunk + 4) / 4;
-  if (lb > 4096) lb = 4096;
-  if (lb < 1) lb = 1;
-  hipLaunchKernelGGL((k_bwd_long<D, TP, OPT>), dim3((unsigned)lb), dim3(256), 0, s, a);
+void bwd_dispatch(BwdArgs a, long long n, hipStream_t s) {
+  constexpr int NCH = D / Vec<TP>::E;
+  constexpr int KL = NCH < kBwdLanes ? NCH : kBwdLanes;
+  long long lb = (n / kChunk + 4) / 4;
+  lb = lb > 2048 ? 2048 : (lb < 1 ? 1 : lb);
+  hipLaunchKernelGGL((k_bwd_long_partial<D, TP>), dim3((unsigned)lb), dim3(256), 0, s, a);
+  long long fb = (n / kShortMax + 4) / 4;  // long keys <= n / (kShortMax + 1)
+  fb = fb > 1024 ? 1024 : (fb < 1 ? 1 : fb);
+  hipLaunchKernelGGL((k_bwd_long_final<D, TP, OPT>), dim3((unsigned)fb), dim3(256), 0, s, a);
+  long long sb = (n + kBwdKeys - 1) / kBwdKeys;
+  sb = sb > 4096 ? 4096 : (sb < 1 ? 1 : sb);
+  hipLaunchKernelGGL((k_bwd_short<D, TP, OPT, KL>), dim3((unsigned)sb), dim3(256), 0, s, a);
 }
 
 template <typename TP, int OPT>
-void bwd_dim(const BwdArgs& a, int dim, long long cap, hipStream_t s) {
+void bwd_dim(const BwdArgs& a, int dim, long long n, hipStream_t s) {
   switch (dim) {
-    case 8: bwd_dispatch<8, TP, OPT>(a, cap, s); break;
-    case 16: bwd_dispatch<16, TP, OPT>(a, cap, s); break;
-    case 32: bwd_dispatch<32, TP, OPT>(a, cap, s); break;
-    case 64: bwd_dispatch<64, TP, OPT>(a, cap, s); break;
-    case 128: bwd_dispatch<128, TP, OPT>(a, cap, s); break;
-    case 256: bwd_dispatch<256, TP, OPT>(a, cap, s); break;
+    case 8: bwd_dispatch<8, TP, OPT>(a, n, s); break;
+    case 16: bwd_dispatch<16, TP, OPT>(a, n, s); break;
+    case 32: bwd_dispatch<32, TP, OPT>(a, n, s); break;
+    case 64: bwd_dispatch<64, TP, OPT>(a, n, s); break;
+    case 128: bwd_dispatch<128, TP, OPT>(a, n, s); break;
+    case 256: bwd_dispatch<256, TP, OPT>(a, n, s); break;
   }
 }
 
@@ -397,50 +715,57 @@ void fwd_dim(const FwdArgs& a, int dim, int pool, hipStream_t s) {
 }  // namespace
 
 void launch_forward(const recis_lookup_result& res, const TableDev& t, int pool, void* out,
-                    hipStream_t s) {
+                    bool current, hipStream_t s) {
   FwdArgs a;
+  const PlanLayout pl = plan_layout(res.capacity);
   a.off = res.bag_offsets;
   a.inverse = res.inverse;
   a.urows = reinterpret_cast<const long long*>(res.unique_rows);
+  a.ukeys = reinterpret_cast<const long long*>(res.unique_keys);
+  a.idslot = reinterpret_cast<const unsigned*>(res.plan + pl.o_idslot);
+  a.occref = reinterpret_cast<const long long*>(res.plan + pl.o_occref);
+  a.current = current ? 1 : 0;
   a.N = res.n;
   a.nbags = (long long)res.num_feats * res.batch;
   a.F = res.num_feats;
   a.B = res.batch;
   a.pool = pool;
   a.out = out;
-  a.rs = t.rs;
+  a.t = t;
   if (t.dtype == RECIS_DTYPE_BF16) fwd_dim<bf16_t>(a, t.dim, pool, s);
   else fwd_dim<float>(a, t.dim, pool, s);
 }
 
 recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, int pool,
                              const void* grad, int grad_dtype, const OptConsts& oc,
-                             double* partials, hipStream_t s) {
+                             double* partials, bool current, hipStream_t s) {
+  if (res.n == 0) return RECIS_OK;
   BwdArgs a;
+  a.current = current ? 1 : 0;
   a.off = res.bag_offsets;
   a.grouped = res.grouped;
   a.uoff = res.unique_offsets;
   a.counts = res.counts;
-  a.urows = reinterpret_cast<const long long*>(res.unique_rows);
+  a.urows = reinterpret_cast<long long*>(res.unique_rows);
+  a.ukeys = reinterpret_cast<const long long*>(res.unique_keys);
   a.num_unique = reinterpret_cast<const long long*>(res.num_unique);
   a.plan = res.plan;
   a.pl = plan_layout(res.capacity);
+  a.idslot = reinterpret_cast<const unsigned*>(res.plan + a.pl.o_idslot);
   a.F = res.num_feats;
   a.B = res.batch;
   a.pool = pool;
   a.gdt = grad_dtype;
   a.grad = grad;
   a.oc = oc;
-  a.rs = t.rs;
+  a.t = t;
   a.partials = partials;
-  if (res.n == 0) return RECIS_OK;
-  const long long cap = res.n;
   if (t.dtype == RECIS_DTYPE_BF16) {
-    if (t.optim == RECIS_OPTIM_ADAGRAD) bwd_dim<bf16_t, RECIS_OPTIM_ADAGRAD>(a, t.dim, cap, s);
-    else bwd_dim<bf16_t, RECIS_OPTIM_ADAM>(a, t.dim, cap, s);
+    if (t.optim == RECIS_OPTIM_ADAGRAD) bwd_dim<bf16_t, RECIS_OPTIM_ADAGRAD>(a, t.dim, res.n, s);
+    else bwd_dim<bf16_t, RECIS_OPTIM_ADAM>(a, t.dim, res.n, s);
   } else {
-    if (t.optim == RECIS_OPTIM_ADAGRAD) bwd_dim<float, RECIS_OPTIM_ADAGRAD>(a, t.dim, cap, s);
-    else bwd_dim<float, RECIS_OPTIM_ADAM>(a, t.dim, cap, s);
+    if (t.optim == RECIS_OPTIM_ADAGRAD) bwd_dim<float, RECIS_OPTIM_ADAGRAD>(a, t.dim, res.n, s);
+    else bwd_dim<float, RECIS_OPTIM_ADAM>(a, t.dim, res.n, s);
   }
   return RECIS_OK;
 }

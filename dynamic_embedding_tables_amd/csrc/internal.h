@@ -24,6 +24,13 @@ constexpr long long kEmptyKey = -1;  // free slot
 constexpr long long kBadKey = -2;    // an occurrence whose transform failed
 constexpr long long kGoneKey = -3;   // evicted, awaiting rebuild
 
+// A row is materialised lazily: insert_find allocates it and marks it
+// pending; until its first update (or writeback) its values are the
+// initializer's, recomputed from (seed, key) wherever they are read.
+constexpr int kPendingRow = 1 << 30;               // in Slot.row
+constexpr long long kFreshRow = 1ll << 62;         // in unique_rows: row may be pending
+constexpr long long kMaxRows = (1ll << 30) - 1;
+
 constexpr unsigned kErrInvalid = 1u << RECIS_ERR_INVALID_ARG;
 constexpr unsigned kErrCapacity = 1u << RECIS_ERR_CAPACITY;
 constexpr unsigned kErrKeyRange = 1u << RECIS_ERR_KEY_RANGE;
@@ -33,12 +40,12 @@ constexpr int kThreads = 256;
 constexpr int kOccPerThread = 8;
 constexpr int kOccTile = kThreads * kOccPerThread;  // 2048
 constexpr int kLdsTab = 2 * kOccTile;               // block-local aggregation table
-// Distinct-key tiling of the per-key kernels (same 2048 per block).
-constexpr int kKeyPerThread = 8;
-constexpr int kKeyTile = kThreads * kKeyPerThread;
+// Distinct-key tiling of the per-key kernels: one key per thread, so that the
+// dependent probe chains of different keys overlap instead of queueing.
+constexpr int kKeyTile = kThreads;
 // Backward: keys with more occurrences than kShortMax are split into chunks.
 constexpr int kShortMax = 64;
-constexpr int kChunk = 256;
+constexpr int kChunk = 64;  // one grouped entry per lane of a wave
 
 struct __align__(16) Slot {
   long long key;
@@ -83,7 +90,7 @@ struct FeatDev {
 struct PlanLayout {
   long long max_long, max_chunks;
   // word offsets
-  long long o_long_u, o_long_base, o_long_nch, o_long_done, o_chunk_owner;
+  long long o_long_u, o_long_base, o_long_nch, o_chunk_owner, o_idslot, o_occref;
   long long words;
 };
 
@@ -94,11 +101,18 @@ __host__ __device__ inline PlanLayout plan_layout(long long cap) {
   p.o_long_u = 4;
   p.o_long_base = p.o_long_u + p.max_long;
   p.o_long_nch = p.o_long_base + p.max_long;
-  p.o_long_done = p.o_long_nch + p.max_long;
-  p.o_chunk_owner = p.o_long_done + p.max_long;
-  p.words = p.o_chunk_owner + p.max_chunks;
+  p.o_chunk_owner = p.o_long_nch + p.max_long;
+  p.o_idslot = p.o_chunk_owner + p.max_chunks;  // IDMap slot of each distinct key
+  p.o_occref = (p.o_idslot + cap + 2) & ~1ll;   // 8-byte aligned: int64 per occurrence
+  p.words = p.o_occref + 2 * cap + 2;
   return p;
 }
+
+// Per-occurrence row reference written by insert_find for the forward:
+// a row offset (>= 0), kOccNoRow, or kOccPendingBit | key for a row that was
+// pending at the lookup (its values are the initializer's of `key`).
+constexpr long long kOccNoRow = 1ll << 62;
+constexpr unsigned long long kOccPendingBit = 1ull << 63;
 
 struct RowSpace {
   char* const* blocks;  // device array of block base pointers
@@ -107,8 +121,11 @@ struct RowSpace {
   long long stride;     // bytes per row
 };
 
+// Rows are below 2^30, so the block index and the in-block product fit 32-bit
+// operands (one 32x32->64 multiply-add).
 __device__ __forceinline__ char* row_ptr(const RowSpace& rs, long long r) {
-  return rs.blocks[r >> rs.lb] + (size_t)(r & rs.mb) * (size_t)rs.stride;
+  const unsigned ri = (unsigned)r;
+  return rs.blocks[ri >> rs.lb] + (unsigned long long)(ri & (unsigned)rs.mb) * (unsigned)rs.stride;
 }
 
 // Multiplicative (Fibonacci) hash of a key to a slot of a 2^k table; shift = 64 - k.
@@ -181,6 +198,21 @@ struct TableDev {
   long long rows_limit;                // rows covered by blocks
 };
 
+// Initial values of 16-byte parameter chunk c of the row of `key`, in the
+// storage format (4 fp32 or 8 bf16 elements).
+__device__ __forceinline__ uint4 init_chunk(const TableDev& t, long long key, int c) {
+  if (t.dtype == RECIS_DTYPE_BF16) {
+    const float4 a = init4(t.seed, key, 2u * c, t.init_scale);
+    const float4 b = init4(t.seed, key, 2u * c + 1u, t.init_scale);
+    return make_uint4((unsigned)f32_to_bf16(a.x) | ((unsigned)f32_to_bf16(a.y) << 16),
+                      (unsigned)f32_to_bf16(a.z) | ((unsigned)f32_to_bf16(a.w) << 16),
+                      (unsigned)f32_to_bf16(b.x) | ((unsigned)f32_to_bf16(b.y) << 16),
+                      (unsigned)f32_to_bf16(b.z) | ((unsigned)f32_to_bf16(b.w) << 16));
+  }
+  const float4 a = init4(t.seed, key, (unsigned)c, t.init_scale);
+  return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
+}
+
 }  // namespace recis
 
 struct recis_table {
@@ -207,6 +239,9 @@ struct recis_table {
   long long keys_hi = 0;
   long long adam_step = 0;
   long long bytes = 0;
+  // bumped by every call that writes rows or frees them (update, writeback,
+  // eviction); a lookup result records the value it was made at
+  unsigned long long update_epoch = 1;
 
   // per-step scratch, sized for scr_cap occurrences
   long long scr_cap = 0;
@@ -215,7 +250,6 @@ struct recis_table {
   int* occ_slot = nullptr;
   int* occ_rank = nullptr;
   int* uslot = nullptr;
-  unsigned* idslot = nullptr;
   unsigned long long* blk_sums = nullptr;
   long long* wb_keys = nullptr;
   double* partials = nullptr;
@@ -252,20 +286,22 @@ struct LookupLaunch {
   int* occ_slot;
   int* occ_rank;
   int* uslot;
-  unsigned* idslot;
   unsigned long long* blk_sums;
   long long key_tiles;
 };
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);
 
+// `current`: no update, writeback or eviction ran on the table since the
+// lookup, so its fresh marks and per-occurrence row references still hold
+// and the IDMap need not be read again.
 void launch_forward(const recis_lookup_result& res, const TableDev& t, int pool, void* out,
-                    hipStream_t s);
+                    bool current, hipStream_t s);
 struct OptConsts {
   float lr, b1, omb1, b2, omb2, eps, step_size;  // omb = 1 - beta, formed in double
 };
 recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, int pool,
                              const void* grad, int grad_dtype, const OptConsts& oc,
-                             double* partials, hipStream_t s);
+                             double* partials, bool current, hipStream_t s);
 
 void launch_evict(const TableDev& t, unsigned min_count, long long* num_evicted, hipStream_t s);
 void launch_writeback(const TableDev& t, const long long* keys, long long n, const float* rows,
@@ -273,7 +309,7 @@ void launch_writeback(const TableDev& t, const long long* keys, long long n, con
                       int* uslot, hipStream_t s);
 void launch_export(const TableDev& t, long long cap, long long* keys, long long* rows,
                    unsigned* counts, hipStream_t s);
-void launch_export_rows(const TableDev& t, long long n, const long long* rows, void* params,
+void launch_export_rows(const TableDev& t, long long n, const long long* keys, long long* rows, void* params,
                         float* state, hipStream_t s);
 
 }  // namespace recis

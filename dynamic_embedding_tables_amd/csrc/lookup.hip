@@ -1,5 +1,5 @@
 // lookup.hip -- insert_find: fused transform + dedup, IDMap probe / insert,
-// row allocation and initialisation, and the per-key grouping of occurrences.
+// row allocation, and the per-key grouping of occurrences.
 //
 // Pages: "RecIS (Recommendation Intelligence System)" README --
 //   Core architecture > Feature Engine (Hash / Mod / Bucketize, fused);
@@ -19,11 +19,16 @@
 //   k_key_scan  one block: exclusive scan of the block sums; rows come from
 //               the free list first, then from the bump pointer -- by prefix
 //               sum, not by atomics
-//   k_key_finalize  per distinct key: group offsets, row assignment, backward
-//               plan for long keys, row initialisation (wave-cooperative),
-//               dedup-table reset
-//   k_group     per occurrence: inverse index and the grouped bag / occurrence
-//               list used by the backward reduction
+//   k_key_finalize  per distinct key: group offsets, row assignment (the new
+//               row is marked pending, not written: its values are the
+//               initializer's until its first update), backward plan for
+//               long keys, dedup-table reset
+//   k_group     per occurrence: inverse index, the grouped bag / occurrence
+//               list used by the backward reduction, and the occurrence's row
+//               reference used by the forward
+// Memory accesses that do not depend on each other are issued as one batch
+// per thread (all loads of a phase before any use), so that each thread
+// waits once per phase rather than once per item.
 #include "internal.h"
 
 namespace recis {
@@ -149,56 +154,88 @@ __global__ __launch_bounds__(kThreads) void k_dedup(LookupLaunch L, TableDev t) 
     s_new = 0;
     s_err = 0;
   }
-  __syncthreads();
-
-  int pos[kOccPerThread], ent[kOccPerThread], rank[kOccPerThread], nidx[kOccPerThread];
-  long long keyv[kOccPerThread];
+  long long keyv[kOccPerThread], cur[kOccPerThread];
+  unsigned long long p[kOccPerThread];
+  bool valid[kOccPerThread];
   unsigned err = 0;
+  // phase 1: values, all loads issued together
 #pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
     const long long j = j0 + tid + (long long)k * kThreads;
-    pos[k] = -1;
-    nidx[k] = -1;
-    keyv[k] = 0;
+    valid[k] = j < fd.n;
+    keyv[k] = valid[k] ? fd.values[j] : 0;
+  }
+  // phase 2: transform, first probe of each key
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) {
+    if (!valid[k]) continue;
+    keyv[k] = transform_value(keyv[k], fd, L.bnd_pool, err);
+    p[k] = ((unsigned long long)keyv[k] * 0x9E3779B97F4A7C15ull) >> L.dd_shift;
+    cur[k] = L.dd[p[k]].key;  // a stale empty is settled by the CAS
+  }
+  // phase 3: claim empty first slots, all CAS issued together
+  long long old[kOccPerThread];
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) {
+    old[k] = 0;
+    if (valid[k] && cur[k] == kEmptyKey)
+      old[k] = (long long)atomicCAS((unsigned long long*)&L.dd[p[k]].key, (unsigned long long)kEmptyKey,
+                                    (unsigned long long)keyv[k]);
+  }
+  // phase 4: resolve; a key whose first slot holds another key keeps probing
+  bool won[kOccPerThread];
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) {
+    won[k] = false;
+    if (!valid[k]) continue;
+    if (cur[k] == keyv[k]) continue;
+    if (cur[k] == kEmptyKey) {
+      if (old[k] == kEmptyKey) {
+        won[k] = true;
+        continue;
+      }
+      if (old[k] == keyv[k]) continue;
+    }
+    unsigned long long q = (p[k] + 1) & L.dd_mask;
+    while (true) {
+      const long long c = L.dd[q].key;
+      if (c == keyv[k]) break;
+      if (c == kEmptyKey) {
+        const long long o = (long long)atomicCAS((unsigned long long*)&L.dd[q].key,
+                                                 (unsigned long long)kEmptyKey, (unsigned long long)keyv[k]);
+        if (o == kEmptyKey) {
+          won[k] = true;
+          break;
+        }
+        if (o == keyv[k]) break;
+      }
+      q = (q + 1) & L.dd_mask;
+    }
+    p[k] = q;
+  }
+  __syncthreads();  // LDS table initialised
+  int ent[kOccPerThread], rank[kOccPerThread], nidx[kOccPerThread];
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) {
     ent[k] = 0;
     rank[k] = 0;
-    if (j < fd.n) {
-      const long long key = transform_value(fd.values[j], fd, L.bnd_pool, err);
-      keyv[k] = key;
-      unsigned long long p = ((unsigned long long)key * 0x9E3779B97F4A7C15ull) >> L.dd_shift;
-      bool won = false;
-      while (true) {
-        const long long cur = L.dd[p].key;  // a stale empty is settled by the CAS
-        if (cur == key) break;
-        if (cur == kEmptyKey) {
-          const long long old = (long long)atomicCAS((unsigned long long*)&L.dd[p].key,
-                                                     (unsigned long long)kEmptyKey,
-                                                     (unsigned long long)key);
-          if (old == kEmptyKey) {
-            won = true;
-            break;
-          }
-          if (old == key) break;
-        }
-        p = (p + 1) & L.dd_mask;
-      }
-      pos[k] = (int)p;
-      unsigned h = ((unsigned)p * 2654435761u) >> 20;  // 12 bits: kLdsTab = 4096
-      while (true) {
-        const int old = atomicCAS(&s_pos[h], -1, (int)p);
-        if (old == -1 || old == (int)p) break;
-        h = (h + 1) & (kLdsTab - 1);
-      }
-      ent[k] = (int)h;
-      rank[k] = atomicAdd(&s_cnt[h], 1);
-      if (won) nidx[k] = atomicAdd(&s_new, 1);
+    nidx[k] = -1;
+    if (!valid[k]) continue;
+    unsigned h = ((unsigned)p[k] * 2654435761u) >> 20;  // 12 bits: kLdsTab = 4096
+    while (true) {
+      const int o = atomicCAS(&s_pos[h], -1, (int)p[k]);
+      if (o == -1 || o == (int)p[k]) break;
+      h = (h + 1) & (kLdsTab - 1);
     }
+    ent[k] = (int)h;
+    rank[k] = atomicAdd(&s_cnt[h], 1);
+    if (won[k]) nidx[k] = atomicAdd(&s_new, 1);
   }
   if (err) atomicOr(&s_err, err);
   __syncthreads();
   for (int i = tid; i < kLdsTab; i += kThreads) {
-    const int p = s_pos[i];
-    if (p >= 0) s_cnt[i] = atomicAdd(&L.dd[p].count, s_cnt[i]);  // base of this block's ranks
+    const int q = s_pos[i];
+    if (q >= 0) s_cnt[i] = atomicAdd(&L.dd[q].count, s_cnt[i]);  // base of this block's ranks
   }
   if (tid == 0) {
     if (s_new > 0)
@@ -208,20 +245,22 @@ __global__ __launch_bounds__(kThreads) void k_dedup(LookupLaunch L, TableDev t) 
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
-    if (pos[k] < 0) continue;
+    if (!valid[k]) continue;
     const long long gj = fd.base + j0 + tid + (long long)k * kThreads;
-    L.occ_slot[gj] = pos[k];
+    L.occ_slot[gj] = (int)p[k];
     L.occ_rank[gj] = s_cnt[ent[k]] + rank[k];
     if (nidx[k] >= 0) {
       const long long u = s_ubase + nidx[k];
-      L.dd[pos[k]].uidx = (int)u;
+      L.dd[p[k]].uidx = (int)u;
       L.res.unique_keys[u] = keyv[k];
-      L.uslot[u] = pos[k];
+      L.uslot[u] = (int)p[k];
     }
   }
 }
 
 // ---------------------------------------------------------- k_key_probe
+// One distinct key per thread.  The first probe loads the whole 16-byte slot,
+// so a hit costs one dependent access after the key itself.
 __global__ __launch_bounds__(kThreads) void k_key_probe(LookupLaunch L, TableDev t) {
   __shared__ unsigned s_ins;
   __shared__ unsigned s_err;
@@ -237,36 +276,38 @@ __global__ __launch_bounds__(kThreads) void k_key_probe(LookupLaunch L, TableDev
   }
   __syncthreads();
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
+  unsigned* idslot = reinterpret_cast<unsigned*>(L.res.plan + plan_layout(L.res.capacity).o_idslot);
   unsigned long long acc = 0;
   unsigned ins = 0, err = 0;
-  for (int k = 0; k < kKeyPerThread; ++k) {
-    const long long u = t0 + (long long)threadIdx.x * kKeyPerThread + k;
-    if (u >= U) break;
+  const long long u = t0 + threadIdx.x;
+  if (u < U) {
     const long long key = L.res.unique_keys[u];
-    const int c = L.dd[L.uslot[u]].count;
+    const int us = L.uslot[u];
+    const int c = L.dd[us].count;
     L.res.counts[u] = c;
     long long row = -1;
     unsigned sl = 0xFFFFFFFFu;
     int need = 0;
     if (key >= 0) {
       unsigned long long p = slot_of(key, t.slot_shift);
+      Slot s = t.slots[p];
       bool found = false, inserted = false;
       for (unsigned long long n = 0; n <= t.slot_mask; ++n) {
-        const long long cur = t.slots[p].key;
-        if (cur == key) {
+        if (n > 0) s = t.slots[p];
+        if (s.key == key) {
           found = true;
           break;
         }
-        if (cur == kEmptyKey) {
+        if (s.key == kEmptyKey) {
           if (find_only) break;
-          const long long old = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
-                                                     (unsigned long long)kEmptyKey,
-                                                     (unsigned long long)key);
-          if (old == kEmptyKey) {
+          const long long o = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
+                                                   (unsigned long long)kEmptyKey, (unsigned long long)key);
+          if (o == kEmptyKey) {
             inserted = true;
             break;
           }
-          if (old == key) {
+          if (o == key) {  // not expected: keys are distinct within a call
+            s = t.slots[p];
             found = true;
             break;
           }
@@ -276,22 +317,26 @@ __global__ __launch_bounds__(kThreads) void k_key_probe(LookupLaunch L, TableDev
       if (!found && !inserted) {
         if (!find_only) err |= kErrCapacity;
       } else if (find_only) {
-        row = t.slots[p].row;
+        row = s.row;
+        sl = (unsigned)p;
       } else {
-        const unsigned c0 = inserted ? 0u : t.slots[p].count;
+        const unsigned c0 = inserted ? 0u : s.count;
         const unsigned long long cs = (unsigned long long)c0 + (unsigned)c;
         const unsigned cnt = cs > 0xFFFFFFFFull ? 0xFFFFFFFFu : (unsigned)cs;
         t.slots[p].count = cnt;
-        const int r = inserted ? -1 : t.slots[p].row;
+        const int r = inserted ? -1 : s.row;
         if (r < 0 && cnt >= t.admit) need = 1;
         else row = r;
         sl = (unsigned)p;
-        ins += inserted ? 1u : 0u;
+        ins = inserted ? 1u : 0u;
       }
     }
+    // a pending row is reported with the fresh mark (its values may still be
+    // the initializer's); -2 marks a key that needs a row from this call
+    if (row >= 0 && (row & kPendingRow)) row = (row & ~(long long)kPendingRow) | kFreshRow;
     L.res.unique_rows[u] = need ? -2 : row;
-    L.idslot[u] = sl;
-    acc += ((unsigned long long)need << 32) | (unsigned)c;
+    idslot[u] = sl;
+    acc = ((unsigned long long)need << 32) | (unsigned)c;
   }
   if (ins) atomicAdd(&s_ins, ins);
   if (err) atomicOr(&s_err, err);
@@ -350,106 +395,59 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
 }
 
 // ------------------------------------------------------- k_key_finalize
-__device__ void init_row(const TableDev& t, long long r, long long key, int lane) {
-  char* rp = row_ptr(t.rs, r);
-  const int pbytes = t.dim * (t.dtype == RECIS_DTYPE_BF16 ? 2 : 4);
-  const int chunks = (int)(t.rs.stride >> 4);
-  for (int c = lane; c < chunks; c += 64) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (c * 16 < pbytes) {
-      if (t.dtype == RECIS_DTYPE_BF16) {
-        const float4 a = init4(t.seed, key, 2u * c, t.init_scale);
-        const float4 b = init4(t.seed, key, 2u * c + 1u, t.init_scale);
-        v.x = (unsigned)f32_to_bf16(a.x) | ((unsigned)f32_to_bf16(a.y) << 16);
-        v.y = (unsigned)f32_to_bf16(a.z) | ((unsigned)f32_to_bf16(a.w) << 16);
-        v.z = (unsigned)f32_to_bf16(b.x) | ((unsigned)f32_to_bf16(b.y) << 16);
-        v.w = (unsigned)f32_to_bf16(b.z) | ((unsigned)f32_to_bf16(b.w) << 16);
-      } else {
-        const float4 a = init4(t.seed, key, (unsigned)c, t.init_scale);
-        v = make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
-                       __float_as_uint(a.w));
-      }
-    }
-    reinterpret_cast<uint4*>(rp)[c] = v;
-  }
-}
-
 __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, TableDev t) {
   __shared__ unsigned s_err;
   const long long U = *L.res.num_unique;
   const long long t0 = (long long)blockIdx.x * kKeyTile;
   if (t0 >= U) return;
   if (threadIdx.x == 0) s_err = 0;
-  const int lane = threadIdx.x & 63;
-  int cnt[kKeyPerThread];
-  long long mark[kKeyPerThread];
-  unsigned long long acc = 0;
-  for (int k = 0; k < kKeyPerThread; ++k) {
-    const long long u = t0 + (long long)threadIdx.x * kKeyPerThread + k;
-    cnt[k] = 0;
-    mark[k] = -1;
-    if (u < U) {
-      cnt[k] = L.res.counts[u];
-      mark[k] = L.res.unique_rows[u];
-      acc += ((unsigned long long)(mark[k] == -2) << 32) | (unsigned)cnt[k];
-    }
+  const long long u = t0 + threadIdx.x;
+  const bool valid = u < U;
+  int cnt = 0, us = 0;
+  long long mark = -1;
+  if (valid) {
+    cnt = L.res.counts[u];
+    mark = L.res.unique_rows[u];
+    us = L.uslot[u];
   }
+  const unsigned long long acc = valid ? (((unsigned long long)(mark == -2) << 32) | (unsigned)cnt) : 0ull;
   unsigned long long total;
-  unsigned long long run = block_exclusive_scan(acc, &total) + L.blk_sums[blockIdx.x];
-  const long long take = t.ctr->take_free, ftop = t.ctr->free_top_old, base = t.ctr->bump_base;
-  const PlanLayout pl = plan_layout(L.res.capacity);
-  int* plan = L.res.plan;
+  const unsigned long long run = block_exclusive_scan(acc, &total) + L.blk_sums[blockIdx.x];
   unsigned err = 0;
-  long long newrow[kKeyPerThread], keyv[kKeyPerThread];
-  for (int k = 0; k < kKeyPerThread; ++k) {
-    const long long u = t0 + (long long)threadIdx.x * kKeyPerThread + k;
-    newrow[k] = -1;
-    keyv[k] = 0;
-    if (u >= U) continue;
+  if (valid) {
+    const PlanLayout pl = plan_layout(L.res.capacity);
+    int* plan = L.res.plan;
+    const unsigned* idslot = reinterpret_cast<const unsigned*>(plan + pl.o_idslot);
+    const long long take = t.ctr->take_free, ftop = t.ctr->free_top_old, base = t.ctr->bump_base;
     L.res.unique_offsets[u] = (int)(run & 0xFFFFFFFFull);
-    long long row = mark[k];
+    long long row = mark;
     if (row == -2) {
       const long long i = (long long)(run >> 32);
       row = i < take ? (long long)t.free_list[ftop - 1 - i] : base + (i - take);
       if (row >= t.rows_limit) {
         row = -1;
         err |= kErrCapacity;
+        L.res.unique_rows[u] = -1;
       } else {
-        t.slots[L.idslot[u]].row = (int)row;
-        newrow[k] = row;
-        keyv[k] = L.res.unique_keys[u];
+        // allocated but not written: its first update materialises it
+        t.slots[idslot[u]].row = (int)row | kPendingRow;
+        L.res.unique_rows[u] = row | kFreshRow;
       }
-      L.res.unique_rows[u] = row;
     }
-    run += ((unsigned long long)(mark[k] == -2) << 32) | (unsigned)cnt[k];
-    if (cnt[k] > kShortMax && row >= 0) {
+    if (cnt > kShortMax && row >= 0) {
       const int idx = atomicAdd(&plan[0], 1);
-      const int nch = (cnt[k] + kChunk - 1) / kChunk;
+      const int nch = (cnt + kChunk - 1) / kChunk;
       const int cb = atomicAdd(&plan[1], nch);
       plan[pl.o_long_u + idx] = (int)u;
       plan[pl.o_long_base + idx] = cb;
       plan[pl.o_long_nch + idx] = nch;
-      plan[pl.o_long_done + idx] = 0;
       for (int q = 0; q < nch; ++q) plan[pl.o_chunk_owner + cb + q] = idx;
     }
-    DedupSlot* d = &L.dd[L.uslot[u]];
+    DedupSlot* d = &L.dd[us];
     d->key = kEmptyKey;
     d->count = 0;
   }
-  // initialise the new rows, one row per pass of the whole wave
-  for (int k = 0; k < kKeyPerThread; ++k) {
-    unsigned long long m = __ballot(newrow[k] >= 0);
-    while (m) {
-      const int src = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const long long r = shfl64(newrow[k], src);
-      const long long key = shfl64(keyv[k], src);
-      init_row(t, r, key, lane);
-    }
-  }
-  if (err) {
-    atomicOr(&s_err, err);
-  }
+  if (err) atomicOr(&s_err, err);
   __syncthreads();
   if (threadIdx.x == 0 && s_err) atomicOr(&t.ctr->error, s_err);
 }
@@ -466,6 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_group(LookupLaunch L, TableDev t) 
   const long long j0 = (blk - fd.tile_base) * kOccTile;
   const bool by_occ = (L.flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
   const int B = L.B;
+  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
   if (!by_occ) {
     if (tid < 2) {
       // bag containing occurrence j: the last i with offs[i] <= j, clamped to [0, B)
@@ -487,13 +486,37 @@ __global__ __launch_bounds__(kThreads) void k_group(LookupLaunch L, TableDev t) 
       for (int i = tid; i < cnt; i += kThreads) s_off[i] = fd.offs[s_blo + i];
     __syncthreads();
   }
+  // phase 1: this thread's occurrences (coalesced)
+  int p[kOccPerThread], rk[kOccPerThread];
+#pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
     const long long j = j0 + tid + (long long)k * kThreads;
-    if (j >= fd.n) break;
+    p[k] = -1;
+    if (j < fd.n) {
+      p[k] = L.occ_slot[fd.base + j];
+      rk[k] = L.occ_rank[fd.base + j];
+    }
+  }
+  // phase 2: distinct-key index of each
+  int u[kOccPerThread];
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) u[k] = p[k] >= 0 ? L.dd[p[k]].uidx : 0;
+  // phase 3: group offset, row and key of each distinct key
+  int uo[kOccPerThread];
+  long long r[kOccPerThread], key[kOccPerThread];
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) {
+    if (p[k] < 0) continue;
+    uo[k] = L.res.unique_offsets[u[k]];
+    r[k] = L.res.unique_rows[u[k]];
+    key[k] = L.res.unique_keys[u[k]];
+  }
+  // phase 4: outputs
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) {
+    if (p[k] < 0) continue;
+    const long long j = j0 + tid + (long long)k * kThreads;
     const long long gj = fd.base + j;
-    const int p = L.occ_slot[gj];
-    const int u = L.dd[p].uidx;
-    L.res.inverse[gj] = u;
     int gval;
     if (by_occ) {
       gval = (int)gj;
@@ -522,7 +545,10 @@ __global__ __launch_bounds__(kThreads) void k_group(LookupLaunch L, TableDev t) 
       i = i < 0 ? 0 : (i > B - 1 ? B - 1 : i);
       gval = f * B + i;
     }
-    L.res.grouped[L.res.unique_offsets[u] + L.occ_rank[gj]] = gval;
+    L.res.inverse[gj] = u[k];
+    L.res.grouped[uo[k] + rk[k]] = gval;
+    occref[gj] = r[k] < 0 ? kOccNoRow
+                          : ((r[k] & kFreshRow) ? (long long)(kOccPendingBit | (unsigned long long)key[k]) : r[k]);
   }
 }
 

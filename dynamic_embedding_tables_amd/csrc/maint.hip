@@ -93,7 +93,7 @@ __global__ void k_evict_mark(TableDev t, unsigned min_count) {
       if (s.key >= 0) {
         if (s.count < min_count) {
           gone = true;
-          row = s.row;
+          row = s.row < 0 ? -1 : (s.row & ~kPendingRow);
           frees = row >= 0;
           t.slots[i].key = kGoneKey;
         } else {
@@ -220,7 +220,11 @@ __global__ __launch_bounds__(256) void k_wb_apply(TableDev t, const float* rows,
       } else {
         if (inserted) atomicAdd(&t.ctr->num_keys, 1ull);
         row = inserted ? -1 : t.slots[at].row;
-        if (row < 0) {
+        if (row >= 0 && (row & kPendingRow)) {  // allocated, never written: written now
+          row &= ~(long long)kPendingRow;
+          t.slots[at].row = (int)row;
+          fresh = 1;
+        } else if (row < 0) {
           row = alloc_one_row(t);
           if (row < 0) atomicOr(&t.ctr->error, kErrCapacity);
           else {
@@ -268,20 +272,31 @@ __global__ void k_export(TableDev t, long long cap, long long* keys, long long* 
   }
 }
 
-// Export step 2: one wave per exported key copies params and state.
-__global__ void k_export_rows(TableDev t, long long n, const long long* rows, char* params, float* state) {
+// Export step 2: one wave per exported key copies params and state; a pending
+// row reports its initial values and zero state.  rows[] is left without the
+// pending mark.
+__global__ void k_export_rows(TableDev t, long long n, const long long* keys, long long* rows, char* params,
+                              float* state) {
   const int lane = threadIdx.x & 63;
   const int es = t.dtype == RECIS_DTYPE_BF16 ? 2 : 4;
   const long long pbytes = (long long)t.dim * es;
   const int sw = t.state_words * t.dim;
   for (long long k = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); k < n; k += (long long)gridDim.x * 4) {
-    const long long r = rows[k];
-    const char* rp = r >= 0 ? row_ptr(t.rs, r) : nullptr;
-    for (long long b = lane; b < pbytes; b += 64) params[k * pbytes + b] = rp ? rp[b] : 0;
+    long long r = rows[k];
+    const bool pending = r >= 0 && (r & kPendingRow);
+    if (pending) r &= ~(long long)kPendingRow;
+    const char* rp = r >= 0 && !pending ? row_ptr(t.rs, r) : nullptr;
+    if (pending) {
+      for (int c = lane; c < (int)(pbytes >> 4); c += 64)
+        reinterpret_cast<uint4*>(params + k * pbytes)[c] = init_chunk(t, keys[k], c);
+    } else {
+      for (long long b = lane; b < pbytes; b += 64) params[k * pbytes + b] = rp ? rp[b] : 0;
+    }
     if (state) {
       const float* st = rp ? reinterpret_cast<const float*>(rp + pbytes) : nullptr;
       for (int e = lane; e < sw; e += 64) state[k * sw + e] = st ? st[e] : 0.f;
     }
+    if (lane == 0) rows[k] = r;
   }
 }
 
@@ -334,10 +349,10 @@ void launch_export(const TableDev& t, long long cap, long long* keys, long long*
                      keys, rows, counts);
 }
 
-void launch_export_rows(const TableDev& t, long long n, const long long* rows, void* params, float* state,
-                        hipStream_t s) {
+void launch_export_rows(const TableDev& t, long long n, const long long* keys, long long* rows, void* params,
+                        float* state, hipStream_t s) {
   if (n <= 0) return;
-  hipLaunchKernelGGL(k_export_rows, dim3(grid_for(n, 4)), dim3(256), 0, s, t, n, rows,
+  hipLaunchKernelGGL(k_export_rows, dim3(grid_for(n, 4)), dim3(256), 0, s, t, n, keys, rows,
                      static_cast<char*>(params), state);
 }
 

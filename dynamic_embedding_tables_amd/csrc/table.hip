@@ -191,7 +191,6 @@ recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
   tab_free(t, t->occ_slot, (size_t)old * 4, s);
   tab_free(t, t->occ_rank, (size_t)old * 4, s);
   tab_free(t, t->uslot, (size_t)old * 4, s);
-  tab_free(t, t->idslot, (size_t)old * 4, s);
   tab_free(t, t->blk_sums, (size_t)(old / kKeyTile + 2) * 8, s);
   tab_free(t, t->wb_keys, (size_t)old * 8, s);
   tab_free(t, t->partials, (size_t)opl.max_chunks * t->cfg.dim * 8, s);
@@ -203,11 +202,10 @@ recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
   t->occ_slot = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
   t->occ_rank = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
   t->uslot = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
-  t->idslot = static_cast<unsigned*>(tab_alloc(t, (size_t)cap * 4, s));
   t->blk_sums = static_cast<unsigned long long*>(tab_alloc(t, (size_t)(cap / kKeyTile + 2) * 8, s));
   t->wb_keys = static_cast<long long*>(tab_alloc(t, (size_t)cap * 8, s));
   t->partials = static_cast<double*>(tab_alloc(t, (size_t)pl.max_chunks * t->cfg.dim * 8, s));
-  if (!t->dd || !t->occ_slot || !t->occ_rank || !t->uslot || !t->idslot || !t->blk_sums || !t->wb_keys ||
+  if (!t->dd || !t->occ_slot || !t->occ_rank || !t->uslot || !t->blk_sums || !t->wb_keys ||
       !t->partials)
     return RECIS_ERR_OUT_OF_MEMORY;
   launch_fill_dedup(t->dd, t->dd_cap, s);
@@ -280,7 +278,7 @@ void recis_table_config_default(recis_table_config* c) {
   c->max_load = 0.5f;
   c->slot_capacity = 1ll << 20;
   c->block_rows = 1ll << 20;
-  c->max_rows = (1ll << 31) - 1;
+  c->max_rows = kMaxRows;
   c->reserve_rows = 0;
 }
 
@@ -299,7 +297,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   if (!std::isfinite(cfg->init_bound) || cfg->init_bound < 0.f) return RECIS_ERR_INVALID_ARG;
   if (cfg->slot_capacity < 1 || cfg->slot_capacity > (1ll << 32)) return RECIS_ERR_INVALID_ARG;
   if (cfg->block_rows < 1 || cfg->block_rows > (1ll << 30)) return RECIS_ERR_INVALID_ARG;
-  if (cfg->max_rows < 1 || cfg->max_rows > (1ll << 31) - 1) return RECIS_ERR_INVALID_ARG;
+  if (cfg->max_rows < 1 || cfg->max_rows > kMaxRows) return RECIS_ERR_INVALID_ARG;
   if (cfg->reserve_rows < 0) return RECIS_ERR_INVALID_ARG;
   if (alloc && (!alloc->alloc || !alloc->free)) return RECIS_ERR_INVALID_ARG;
   if (!valid_dim(cfg->dim)) return RECIS_ERR_UNSUPPORTED;
@@ -354,8 +352,7 @@ recis_status recis_idmap_destroy(recis_table* t) {
     tab_free(t, t->occ_slot, (size_t)old * 4, s);
     tab_free(t, t->occ_rank, (size_t)old * 4, s);
     tab_free(t, t->uslot, (size_t)old * 4, s);
-    tab_free(t, t->idslot, (size_t)old * 4, s);
-    tab_free(t, t->blk_sums, (size_t)(old / kKeyTile + 2) * 8, s);
+      tab_free(t, t->blk_sums, (size_t)(old / kKeyTile + 2) * 8, s);
     tab_free(t, t->wb_keys, (size_t)old * 8, s);
     tab_free(t, t->partials, (size_t)plan_layout(old).max_chunks * t->cfg.dim * 8, s);
   }
@@ -438,6 +435,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   res->num_feats = num_feats;
   res->batch = batch;
   res->flags = flags;
+  res->epoch = t->update_epoch;
 
   LookupLaunch L;
   L.feats = static_cast<const FeatDev*>(dev);
@@ -454,7 +452,6 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.occ_slot = t->occ_slot;
   L.occ_rank = t->occ_rank;
   L.uslot = t->uslot;
-  L.idslot = t->idslot;
   L.blk_sums = t->blk_sums;
   L.key_tiles = (N + kKeyTile - 1) / kKeyTile;
   launch_lookup(L, t->dev(), s);
@@ -464,6 +461,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
 recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted, hipStream_t s) {
   if (!t) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  t->update_epoch += 1;
   launch_evict(t->dev(), min_count, reinterpret_cast<long long*>(num_evicted), s);
   recis_status st = check_launch();
   if (st != RECIS_OK) return st;
@@ -485,7 +483,7 @@ recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_resu
   if (outn > 0 && !out) return RECIS_ERR_INVALID_ARG;
   if (res->n > res->capacity || res->n < 0) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
-  launch_forward(*res, t->dev(), pool, out, s);
+  launch_forward(*res, t->dev(), pool, out, res->epoch == t->update_epoch, s);
   return check_launch();
 }
 
@@ -520,7 +518,9 @@ recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* re
     recis_status st = ensure_scratch(t, res->n, s);
     if (st != RECIS_OK) return st;
   }
-  recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, t->partials, s);
+  const bool current = res->epoch == t->update_epoch;
+  t->update_epoch += 1;
+  recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, t->partials, current, s);
   if (st != RECIS_OK) return st;
   return check_launch();
 }
@@ -532,6 +532,7 @@ recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, con
   if (st != RECIS_OK) return st;
   st = ensure_capacity(t, n, s);
   if (st != RECIS_OK) return st;
+  t->update_epoch += 1;
   launch_writeback(t->dev(), reinterpret_cast<const long long*>(keys), n, rows, t->dd,
                    (unsigned long long)(t->dd_cap - 1), 64 - log2_exact(t->dd_cap), t->wb_keys, t->uslot, s);
   return check_launch();
@@ -551,7 +552,7 @@ recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int6
   if (st != RECIS_OK) return st;
   *n = (int64_t)c.scratch_count;
   const long long m = std::min<long long>(cap, (long long)c.scratch_count);
-  launch_export_rows(t->dev(), m, reinterpret_cast<const long long*>(rows), params,
+  launch_export_rows(t->dev(), m, reinterpret_cast<const long long*>(keys), reinterpret_cast<long long*>(rows), params,
                      t->state_words > 0 ? state : nullptr, s);
   st = check_launch();
   if (st != RECIS_OK) return st;

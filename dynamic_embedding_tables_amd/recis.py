@@ -74,7 +74,7 @@ class recis_lookup_result(C.Structure):
                 ("counts", C.c_void_p), ("bag_offsets", C.c_void_p), ("num_unique", C.c_void_p),
                 ("unique_offsets", C.c_void_p), ("grouped", C.c_void_p), ("plan", C.c_void_p),
                 ("capacity", C.c_int64), ("n", C.c_int64), ("num_feats", C.c_int32),
-                ("batch", C.c_int32), ("flags", C.c_uint32)]
+                ("batch", C.c_int32), ("flags", C.c_uint32), ("epoch", C.c_uint64)]
 
 
 class recis_optim_params(C.Structure):
@@ -237,7 +237,7 @@ class LookupResult:
             self.unique_keys.data_ptr(), self.unique_rows.data_ptr(), self.inverse.data_ptr(),
             self.counts.data_ptr(), self.bag_offsets.data_ptr(), self.num_unique.data_ptr(),
             self.unique_offsets.data_ptr(), self.grouped.data_ptr(), self.plan.data_ptr(),
-            cap, 0, 0, 0, 0)
+            cap, 0, 0, 0, 0, 0)
         self.capacity = cap
         self.nbags = nbags
 
@@ -279,7 +279,7 @@ class Table:
 
     def __init__(self, dim: int, dtype: str = "f32", optim: str = "adagrad", seed: int = 20250925,
                  init_bound: float = 0.05, admit_threshold: int = 1, slot_capacity: int = 1 << 20,
-                 block_rows: int = 1 << 20, max_rows: int = (1 << 31) - 1, reserve_rows: int = 0,
+                 block_rows: int = 1 << 20, max_rows: int = (1 << 30) - 1, reserve_rows: int = 0,
                  max_load: float = 0.5, stream=None):
         cfg = recis_table_config_default()
         cfg.dim, cfg.dtype, cfg.optim = dim, DTYPES[dtype], OPTIMS[optim]

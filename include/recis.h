@@ -92,12 +92,12 @@ typedef struct {
   float max_load;           /* IDMap occupancy that triggers growth, in (0, 0.9] */
   int64_t slot_capacity;    /* initial IDMap slots (rounded up to a power of two) */
   int64_t block_rows;       /* rows per EmbeddingBlock (rounded up to a power of two) */
-  int64_t max_rows;         /* hard row limit (<= 2^31 - 1) */
+  int64_t max_rows;         /* hard row limit (<= 2^30 - 1) */
   int64_t reserve_rows;     /* rows allocated at creation (rounded up to whole blocks) */
 } recis_table_config;
 
 /* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
- * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^31-1, reserve 0). */
+ * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0). */
 void recis_table_config_default(recis_table_config* cfg);
 
 /* Device-memory provider.  alloc returns `bytes` of device memory (256-byte
@@ -127,19 +127,28 @@ typedef struct {
  * by insert_find on the host and read by the forward / backward calls. */
 typedef struct {
   int64_t* unique_keys;    /* [capacity] distinct keys, first num_unique valid */
-  int64_t* unique_rows;    /* [capacity] row of each distinct key, -1 = none */
+  int64_t* unique_rows;    /* [capacity] row of each distinct key, -1 = none; bit 62 set:
+                              the row may still hold only its initial values, which
+                              the library recomputes from (seed, key) until the
+                              row's first update writes it (the backward clears
+                              the bit) -- the row offset is the value without it */
   int32_t* inverse;        /* [capacity] occurrence -> index into unique_* */
   int32_t* counts;         /* [capacity] occurrences of each distinct key */
   int32_t* bag_offsets;    /* [num_feats * batch + 1] merged CSR, bag f*batch + i */
   int64_t* num_unique;     /* [1] */
   int32_t* unique_offsets; /* [capacity + 1] start of each key's group in `grouped` */
   int32_t* grouped;        /* [capacity] bag ids (or occurrence ids) grouped by key */
-  int32_t* plan;           /* [recis_plan_words(capacity)] backward work plan */
+  int32_t* plan;           /* [recis_plan_words(capacity)] opaque: backward work plan,
+                              per-key IDMap slots, per-occurrence row references */
   int64_t capacity;
   int64_t n;               /* occurrences of the last insert_find */
   int32_t num_feats;
   int32_t batch;
   uint32_t flags;
+  uint64_t epoch;          /* the table's update count at the lookup: while no update,
+                              writeback or eviction has run since, forward and
+                              backward use the lookup's row references directly;
+                              otherwise they re-read the IDMap */
 } recis_lookup_result;
 
 /* int32 words needed by recis_lookup_result.plan for `capacity` occurrences. */

@@ -118,17 +118,27 @@ def check_export(g, o, spec, rtol_state=1e-5):
         assert not sb.any(), f"{sb.sum()} state elements off; worst {np.max(se / np.maximum(sc, 1e-30))}"
 
 
-def check_forward(out_gpu, spec, oracle_out, oracle_abs, merged_offsets=None, num_feats=1):
-    """gather: bit-exact.  pooled: |y - y_ref| <= 1e-5 * (sum |terms| + terms * lr),
-    the summation-order bound of fp32 plus the parameter tolerance that earlier
-    updates may already have used (terms = bag length for sum, 1 for mean)."""
+def check_forward(out_gpu, spec, oracle_out, oracle_abs, merged_offsets=None, num_feats=1, exact=None):
+    """gather: a copy of the stored rows -- bit-exact while every row still holds
+    its initial values (exact=True, the first step), afterwards within the
+    parameter tolerance (rows updated on both sides may differ by an ulp).
+    pooled: |y - y_ref| <= 1e-5 * (sum |terms| + terms * lr), the summation-order
+    bound of fp32 plus the parameter tolerance that earlier updates may already
+    have used (terms = bag length for sum, 1 for mean)."""
     if spec.pool == "none":
         import torch
         if spec.dtype == "bf16":
             g = out_gpu.view(torch.int16).cpu().numpy().view(np.uint16)
         else:
             g = out_gpu.cpu().numpy()
-        np.testing.assert_array_equal(g, oracle_out)
+        if exact or spec.optim == "none":
+            np.testing.assert_array_equal(g, oracle_out)
+            return
+        to_f = (lambda b: (b.astype(np.uint32) << 16).view(np.float32)) if spec.dtype == "bf16" else (lambda x: x)
+        gv, ov = to_f(g).astype(np.float64), to_f(oracle_out).astype(np.float64)
+        tol = 1e-2 if spec.dtype == "bf16" else 1e-5
+        bad = np.abs(gv - ov) > tol * np.maximum(np.abs(ov), spec.lr)
+        assert not bad.any(), f"{bad.sum()} gathered elements off"
         return
     g = out_gpu.cpu().numpy()
     err = np.abs(g.astype(np.float64) - oracle_out.astype(np.float64))

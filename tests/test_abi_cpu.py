@@ -71,7 +71,7 @@ def test_struct_layouts_match_header(lib, tmp_path):
 def test_config_defaults_and_plan_words(lib):
     c = lib.recis_table_config_default()
     assert c.dim == 64 and c.dtype == lib.RECIS_DTYPE_F32 and c.optim == lib.RECIS_OPTIM_ADAGRAD
-    assert abs(c.init_bound - 0.05) < 1e-9 and c.max_load == 0.5 and c.max_rows == 2**31 - 1
+    assert abs(c.init_bound - 0.05) < 1e-9 and c.max_load == 0.5 and c.max_rows == 2**30 - 1
     assert lib.recis_plan_words(0) > 0
     assert lib.recis_plan_words(1 << 20) > lib.recis_plan_words(1 << 10)
     assert lib.recis_plan_words(-1) == -1
@@ -90,7 +90,7 @@ def test_invalid_arguments_return_synchronously(lib):
     c = lib.recis_table_config_default()
     assert L.recis_idmap_create(C.byref(c), None, None, None) == lib.RECIS_ERR_INVALID_ARG
     for field, bad in [("dtype", 7), ("optim", 9), ("max_load", 0.0), ("max_load", 0.95),
-                       ("slot_capacity", 0), ("block_rows", 0), ("max_rows", 0), ("max_rows", 2**31),
+                       ("slot_capacity", 0), ("block_rows", 0), ("max_rows", 0), ("max_rows", 2**30),
                        ("reserve_rows", -1), ("init_bound", -1.0)]:
         c = lib.recis_table_config_default()
         setattr(c, field, bad)
