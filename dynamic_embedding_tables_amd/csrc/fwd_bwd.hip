@@ -270,9 +270,13 @@ constexpr int kBwdStage = 1024;     // gradient entries staged in LDS per tile
 #endif
 constexpr int kBwdLanes = RECIS_BWD_LANES;  // lanes per key in the short path (at most)
 #ifndef RECIS_BWD_BATCH
-#define RECIS_BWD_BATCH 16
+#define RECIS_BWD_BATCH 8
 #endif
 constexpr int kBwdBatchElems = RECIS_BWD_BATCH;  // gradient elements per lane in flight (short path)
+#ifndef RECIS_BWD_P
+#define RECIS_BWD_P 1
+#endif
+constexpr int kBwdKeysPerGroup = RECIS_BWD_P;  // keys a group of the short path works on together
 
 // Upstream-gradient row of grouped entry gval (a bag, or an occurrence for
 // POOL_NONE) and the scale it enters with (1 / bag length for mean pooling).
@@ -305,7 +309,7 @@ struct RowMap {
 // Row state of this lane's chunks: the stored values, or for a pending row
 // the initializer's values and zero optimizer state.
 template <int D, typename TP, int OPT, int KL>
-__device__ __forceinline__ void load_row(const BwdArgs& a, long long row, bool pending, long long key, int lane,
+__device__ __forceinline__ void load_row(const BwdArgs& a, const char* rp, bool pending, long long key, int lane,
                                          float (&w)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
                                          float (&s0)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
                                          float (&s1)[RowMap<D, TP, KL>::CH][Vec<TP>::E]) {
@@ -319,7 +323,6 @@ __device__ __forceinline__ void load_row(const BwdArgs& a, long long row, bool p
     }
     return;
   }
-  const char* rp = row_ptr(a.t.rs, row);
   const float* st = reinterpret_cast<const float*>(rp + D * (int)sizeof(TP));
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) {
@@ -337,13 +340,12 @@ __device__ __forceinline__ void load_row(const BwdArgs& a, long long row, bool p
 // One optimizer step on this lane's chunks, then their stores.  The square
 // root and reciprocal are the hardware's (about 1 ulp each).
 template <int D, typename TP, int OPT, int KL>
-__device__ __forceinline__ void update_store(const BwdArgs& a, long long row, int lane,
+__device__ __forceinline__ void update_store(const BwdArgs& a, char* rp, int lane,
                                              const double (&G)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
                                              float (&w)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
                                              float (&s0)[RowMap<D, TP, KL>::CH][Vec<TP>::E],
                                              float (&s1)[RowMap<D, TP, KL>::CH][Vec<TP>::E]) {
   constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
-  char* rp = row_ptr(a.t.rs, row);
   float* st = reinterpret_cast<float*>(rp + D * (int)sizeof(TP));
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) {
@@ -387,19 +389,19 @@ __device__ __forceinline__ void add_grad_row(const BwdArgs& a, int grow, double 
     for (int e = 0; e < E; ++e) acc[ch][e] += (double)g[ch][e] * scale;
 }
 
-// Block-wide exclusive scan of one int per thread (kThreads = 256).
-__device__ __forceinline__ int block_scan_int(int v, int* total) {
-  __shared__ int s_w[kThreads / 64];
+// Block-wide exclusive scan of one 64-bit value per thread (kThreads = 256).
+__device__ __forceinline__ long long block_scan_ll(long long v, long long* total) {
+  __shared__ long long s_w[kThreads / 64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
+  long long x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl(x, lane >= d ? lane - d : lane);
+    const long long y = shfl64(x, lane >= d ? lane - d : lane);
     if (lane >= d) x += y;
   }
   if (lane == 63) s_w[wid] = x;
   __syncthreads();
-  int before = 0, all = 0;
+  long long before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) {
     before += w < wid ? s_w[w] : 0;
@@ -412,7 +414,7 @@ __device__ __forceinline__ int block_scan_int(int v, int* total) {
 
 // Long keys, pass 1: one wave per kChunk-entry chunk.  The chunk's entries
 // sit one per lane; each group of C = D / E lanes sums a contiguous share of
-// them (kLongBatch rows in flight), a butterfly across the groups merges the
+// them (up to 8 rows in flight), a butterfly across the groups merges the
 // shares, and the chunk's double-precision partial is stored.  No atomics and
 // no cross-block waits: the finishing pass runs as the next launch.
 template <int D, typename TP>
@@ -526,8 +528,9 @@ __global__ __launch_bounds__(256) void k_bwd_long_final(BwdArgs a) {
       for (int e = 0; e < E; ++e) G[0][e] += shfl_xor_d(G[0][e], m);
     if (g == 0) {
       float w[1][E], s0[1][E], s1[1][E];
-      load_row<D, TP, OPT, C>(a, r, pending, pending ? a.ukeys[u] : 0, lane, w, s0, s1);
-      update_store<D, TP, OPT, C>(a, r, lane, G, w, s0, s1);
+      char* rp = row_ptr(a.t.rs, r);
+      load_row<D, TP, OPT, C>(a, rp, pending, pending ? a.ukeys[u] : 0, lane, w, s0, s1);
+      update_store<D, TP, OPT, C>(a, rp, lane, G, w, s0, s1);
     }
     if (wl == 0 && fresh) {
       if (pending) a.t.slots[sl].row = (int)r;
@@ -536,11 +539,15 @@ __global__ __launch_bounds__(256) void k_bwd_long_final(BwdArgs a) {
   }
 }
 
-// Short keys (<= kShortMax entries).  A block takes kBwdKeys consecutive keys,
-// stages their metadata and (when they fit) their gradient references in LDS
-// in two coalesced passes, then each group of KL lanes updates its keys one
-// at a time with the row and gradient loads of a key in flight together.
-template <int D, typename TP, int OPT, int KL>
+// Short keys (<= kShortMax entries).  A block takes kBwdKeys consecutive keys.
+// Phase 1, one thread per key: metadata and the row's address (the block
+// table is read here once, not per update), and one packed block scan that
+// gives each key its staged-entry base and its place in an order with the
+// pending rows first, so the groups of a wave mostly agree on whether to run
+// the initializer.  Phase 2: the keys' gradient references, staged in LDS
+// when they fit.  Phase 3: each group of KL lanes takes P keys at a time,
+// issues the row and gradient loads of all of them, then updates and stores.
+template <int D, typename TP, int OPT, int KL, int P>
 __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
   constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
   constexpr int GPB = 256 / KL;
@@ -548,11 +555,16 @@ __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
   const int wl = threadIdx.x & 63;
   const int lane = wl % KL, gbase = wl - lane;
   const int tid = threadIdx.x;
-  __shared__ int s_o[kBwdKeys], s_c[kBwdKeys], s_eo[kBwdKeys + 1], s_st[kBwdKeys];
-  __shared__ long long s_r[kBwdKeys], s_key[kBwdKeys];
+  __shared__ int s_o[kBwdKeys], s_c[kBwdKeys], s_eo[kBwdKeys + 1];
+  __shared__ char* s_ptr[kBwdKeys];
+  __shared__ int s_r[kBwdKeys];
+  __shared__ long long s_key[kBwdKeys];
   __shared__ unsigned s_sl[kBwdKeys];
+  __shared__ unsigned char s_st[kBwdKeys];
+  __shared__ unsigned char s_perm[kBwdKeys];
   __shared__ int s_grow[kBwdStage];
   __shared__ double s_sc[kBwdStage];
+  __shared__ int s_nact;
   const long long U = *a.num_unique;
   for (long long t0 = (long long)blockIdx.x * kBwdKeys; t0 < U; t0 += (long long)gridDim.x * kBwdKeys) {
     const long long u = t0 + tid;
@@ -569,19 +581,32 @@ __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
         key = a.ukeys[u];
         st = a.current ? 2 : ((a.t.slots[sl].row & kPendingRow) ? 2 : 1);
       }
-      if (c > kShortMax) r = -1;  // the long-key kernel updates it
+      if (c > kShortMax) r = -1;  // the long-key kernels update it
     }
-    const int ce = r >= 0 ? c : 0;
-    int tot;
-    const int eo = block_scan_int(ce, &tot);
+    const bool act = r >= 0;
+    char* rp = act ? row_ptr(a.t.rs, r) : nullptr;
+    // fields: entries (bits 0..19), pending keys (20..39), active keys (40..59)
+    const long long packed = (act ? (long long)c : 0) | ((long long)(act && st == 2) << 20) | ((long long)act << 40);
+    long long all;
+    const long long pre = block_scan_ll(packed, &all);
+    const int eo = (int)(pre & 0xFFFFF), tot = (int)(all & 0xFFFFF);
+    const int npend = (int)((all >> 20) & 0xFFFFF);
+    if (act) {
+      const int pb = (int)((pre >> 20) & 0xFFFFF), ab = (int)((pre >> 40) & 0xFFFFF);
+      s_perm[st == 2 ? pb : npend + (ab - pb)] = (unsigned char)tid;
+    }
     s_o[tid] = o;
-    s_c[tid] = ce;
+    s_c[tid] = act ? c : 0;
     s_eo[tid] = eo;
-    s_st[tid] = st;
-    s_r[tid] = r;
+    s_st[tid] = (unsigned char)st;
+    s_ptr[tid] = rp;
+    s_r[tid] = (int)r;
     s_key[tid] = key;
     s_sl[tid] = sl;
-    if (tid == 0) s_eo[kBwdKeys] = tot;
+    if (tid == 0) {
+      s_eo[kBwdKeys] = tot;
+      s_nact = (int)((all >> 40) & 0xFFFFF);
+    }
     __syncthreads();
     const bool staged = tot <= kBwdStage;
     if (staged) {
@@ -592,68 +617,95 @@ __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
           if (s_eo[mid] <= i) lo = mid;
           else hi = mid;
         }
-        int go;
+        int gr;
         double sc;
-        grad_ref<D>(a, a.grouped[s_o[lo] + (i - s_eo[lo])], go, sc);
-        s_grow[i] = go;
+        grad_ref<D>(a, a.grouped[s_o[lo] + (i - s_eo[lo])], gr, sc);
+        s_grow[i] = gr;
         s_sc[i] = sc;
       }
       __syncthreads();
     }
-    for (int k = tid / KL; k < kBwdKeys; k += GPB) {
-      const long long row = s_r[k];
-      if (row < 0) continue;
-      const int kst = s_st[k], kc = s_c[k];
-      float w[CH][E], s0[CH][E], s1[CH][E];
-      load_row<D, TP, OPT, KL>(a, row, kst == 2, s_key[k], lane, w, s0, s1);
-      double acc[CH][E];
+    const int nact = s_nact;
+    for (int q0 = tid / KL; q0 < nact; q0 += GPB * P) {
+      int kk[P], kc[P], kst[P];
+      char* prow[P];
+      float w[P][CH][E], s0[P][CH][E], s1[P][CH][E];
+      double acc[P][CH][E];
 #pragma unroll
-      for (int ch = 0; ch < CH; ++ch)
+      for (int j = 0; j < P; ++j) {
+        const int q = q0 + j * GPB;
+        kk[j] = q < nact ? s_perm[q] : -1;
+        kc[j] = kk[j] >= 0 ? s_c[kk[j]] : 0;
+        kst[j] = kk[j] >= 0 ? s_st[kk[j]] : 0;
+        prow[j] = kk[j] >= 0 ? s_ptr[kk[j]] : nullptr;
+        if (kk[j] >= 0) load_row<D, TP, OPT, KL>(a, prow[j], kst[j] == 2, s_key[kk[j]], lane, w[j], s0[j], s1[j]);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[ch][e] = 0.0;
+        for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[j][ch][e] = 0.0;
+      }
       if (staged) {
-        // up to GB gradient rows of the key in flight together
-        const int base = s_eo[k];
-        for (int x0 = 0; x0 < kc; x0 += GB) {
-          float gv[GB][CH][E];
+        int kmax = 0;
 #pragma unroll
-          for (int i = 0; i < GB; ++i) {
-            const int go = x0 + i < kc ? s_grow[base + x0 + i] : 0;
+        for (int j = 0; j < P; ++j) kmax = kc[j] > kmax ? kc[j] : kmax;
+        // GB gradient rows of each of the P keys in flight together
+        for (int x0 = 0; x0 < kmax; x0 += GB) {
+          float gv[P][GB][CH][E];
 #pragma unroll
-            for (int ch = 0; ch < CH; ++ch) {
-              if (x0 + i < kc) {
-                load_grad<E>(a.grad, (long long)go * D + (ch * KL + lane) * E, a.gdt, gv[i][ch]);
-              } else {
+          for (int j = 0; j < P; ++j) {
+            const int base = kk[j] >= 0 ? s_eo[kk[j]] : 0;
 #pragma unroll
-                for (int e = 0; e < E; ++e) gv[i][ch][e] = 0.f;
+            for (int i = 0; i < GB; ++i) {
+              const bool in = x0 + i < kc[j];
+              const int gr = in ? s_grow[base + x0 + i] : 0;
+#pragma unroll
+              for (int ch = 0; ch < CH; ++ch) {
+                if (in) {
+                  load_grad<E>(a.grad, (long long)gr * D + (ch * KL + lane) * E, a.gdt, gv[j][i][ch]);
+                } else {
+#pragma unroll
+                  for (int e = 0; e < E; ++e) gv[j][i][ch][e] = 0.f;
+                }
               }
             }
           }
 #pragma unroll
-          for (int i = 0; i < GB; ++i) {
-            const double sc = x0 + i < kc ? s_sc[base + x0 + i] : 0.0;
+          for (int j = 0; j < P; ++j) {
+            const int base = kk[j] >= 0 ? s_eo[kk[j]] : 0;
 #pragma unroll
-            for (int ch = 0; ch < CH; ++ch)
+            for (int i = 0; i < GB; ++i) {
+              const double sc = x0 + i < kc[j] ? s_sc[base + x0 + i] : 0.0;
 #pragma unroll
-              for (int e = 0; e < E; ++e) acc[ch][e] += (double)gv[i][ch][e] * sc;
+              for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[j][ch][e] += (double)gv[j][i][ch][e] * sc;
+            }
           }
         }
       } else {
         // entries straight from global memory, KL at a time (one per lane)
-        const int ko = s_o[k];
-        for (int b0 = 0; b0 < kc; b0 += KL) {
-          const int cnt = kc - b0 < KL ? kc - b0 : KL;
-          int grow = 0;
-          double scale = 0.0;
-          if (lane < cnt) grad_ref<D>(a, a.grouped[ko + b0 + lane], grow, scale);
-          for (int x = 0; x < cnt; ++x)
-            add_grad_row<D, TP, KL>(a, __shfl(grow, gbase + x), shfl_d(scale, gbase + x), lane, acc);
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const int ko = kk[j] >= 0 ? s_o[kk[j]] : 0;
+          for (int b0 = 0; b0 < kc[j]; b0 += KL) {
+            const int cnt = kc[j] - b0 < KL ? kc[j] - b0 : KL;
+            int gr = 0;
+            double scale = 0.0;
+            if (lane < cnt) grad_ref<D>(a, a.grouped[ko + b0 + lane], gr, scale);
+            for (int x = 0; x < cnt; ++x)
+              add_grad_row<D, TP, KL>(a, __shfl(gr, gbase + x), shfl_d(scale, gbase + x), lane, acc[j]);
+          }
         }
       }
-      update_store<D, TP, OPT, KL>(a, row, lane, acc, w, s0, s1);
-      if (lane == 0 && kst != 0) {
-        if (kst == 2) a.t.slots[s_sl[k]].row = (int)row;
-        a.urows[t0 + k] = row;
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        if (kk[j] < 0) continue;
+        update_store<D, TP, OPT, KL>(a, prow[j], lane, acc[j], w[j], s0[j], s1[j]);
+        if (lane == 0 && kst[j] != 0) {
+          const int row = s_r[kk[j]];
+          if (kst[j] == 2) a.t.slots[s_sl[kk[j]]].row = row;
+          a.urows[t0 + kk[j]] = row;
+        }
       }
     }
     __syncthreads();  // the tile's LDS is reused by the next tile
@@ -685,7 +737,7 @@ void bwd_dispatch(BwdArgs a, long long n, hipStream_t s) {
   hipLaunchKernelGGL((k_bwd_long_final<D, TP, OPT>), dim3((unsigned)fb), dim3(256), 0, s, a);
   long long sb = (n + kBwdKeys - 1) / kBwdKeys;
   sb = sb > 4096 ? 4096 : (sb < 1 ? 1 : sb);
-  hipLaunchKernelGGL((k_bwd_short<D, TP, OPT, KL>), dim3((unsigned)sb), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_bwd_short<D, TP, OPT, KL, kBwdKeysPerGroup>), dim3((unsigned)sb), dim3(256), 0, s, a);
 }
 
 template <typename TP, int OPT>

@@ -39,7 +39,9 @@ constexpr unsigned kErrKeyRange = 1u << RECIS_ERR_KEY_RANGE;
 constexpr int kThreads = 256;
 constexpr int kOccPerThread = 8;
 constexpr int kOccTile = kThreads * kOccPerThread;  // 2048
-constexpr int kLdsTab = 2 * kOccTile;               // block-local aggregation table
+constexpr int kLdsTabBits = 12;
+constexpr int kLdsTab = 1 << kLdsTabBits;            // block-local dedup table (2 x kOccTile)
+static_assert(kLdsTab == 2 * kOccTile, "block-local dedup table at most half full");
 // Distinct-key tiling of the per-key kernels: one key per thread, so that the
 // dependent probe chains of different keys overlap instead of queueing.
 constexpr int kKeyTile = kThreads;
@@ -160,9 +162,10 @@ __device__ __forceinline__ unsigned long long fmix64(unsigned long long k) {
 __device__ __forceinline__ uint4 philox10(uint4 c, uint2 k) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const unsigned lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-    const unsigned lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-    c = make_uint4(hi1 ^ c.y ^ k.x, lo1, hi0 ^ c.w ^ k.y, lo0);
+    // one 32x32->64 multiply each (v_mad_u64_u32), not separate lo/hi
+    const unsigned long long p0 = (unsigned long long)c.x * 0xD2511F53u;
+    const unsigned long long p1 = (unsigned long long)c.z * 0xCD9E8D57u;
+    c = make_uint4((unsigned)(p1 >> 32) ^ c.y ^ k.x, (unsigned)p1, (unsigned)(p0 >> 32) ^ c.w ^ k.y, (unsigned)p0);
     k.x += 0x9E3779B9u;
     k.y += 0xBB67AE85u;
   }

@@ -10,10 +10,10 @@
 //
 // Kernel sequence of one call (all on one stream, no host read-back):
 //   k_prep      merged bag offsets, offset validation, per-call counters
-//   k_dedup     per occurrence: transform + tag, insert into the call's dedup
-//               table; per-block LDS aggregation gives each occurrence its rank
-//               among equal keys with one global atomic per distinct key per
-//               block (hot keys never serialise on one address)
+//   k_dedup     per occurrence: transform + tag, dedup within the block in
+//               LDS (rank among equal keys), then one insert into the call's
+//               dedup table and one count atomic per distinct key per block
+//               (hot keys never serialise on one address)
 //   k_key_probe per distinct key: IDMap probe / CAS insert, count, admission
 //               decision; block sums of (occurrences, rows to allocate)
 //   k_key_scan  one block: exclusive scan of the block sums; rows come from
@@ -136,10 +136,21 @@ __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
 }
 
 // -------------------------------------------------------------- k_dedup
+// A block takes kOccTile occurrences of one feature.  Their keys are first
+// deduplicated in an LDS table (64-bit CAS in LDS), which also gives each
+// occurrence its rank among the block's equal keys; only then does each
+// distinct key of the block touch the call's global dedup table -- one probe,
+// at most one CAS and one count atomic per block, instead of one per
+// occurrence, so the hot keys of a Zipf feature do not serialise thousands
+// of atomics on one address.  Each thread issues the global accesses of all
+// its entries together, so a phase costs one round trip.
+constexpr int kDistPerThread = kOccTile / kThreads;  // list entries a thread resolves
+
 __global__ __launch_bounds__(kThreads) void k_dedup(LookupLaunch L, TableDev t) {
-  __shared__ int s_pos[kLdsTab];
-  __shared__ int s_cnt[kLdsTab];
-  __shared__ int s_new;
+  __shared__ unsigned long long s_key[kLdsTab];  // block's distinct keys; then their dedup slots
+  __shared__ int s_cnt[kLdsTab];                 // occurrences in the block; then the rank base
+  __shared__ unsigned short s_list[kOccTile];    // entries of s_key in use
+  __shared__ int s_nd, s_new;
   __shared__ long long s_ubase;
   __shared__ unsigned s_err;
   const int tid = threadIdx.x;
@@ -147,96 +158,115 @@ __global__ __launch_bounds__(kThreads) void k_dedup(LookupLaunch L, TableDev t) 
   const FeatDev fd = L.feats[find_feature(L.feats, L.F, blk)];
   const long long j0 = (blk - fd.tile_base) * kOccTile;
   for (int i = tid; i < kLdsTab; i += kThreads) {
-    s_pos[i] = -1;
+    s_key[i] = (unsigned long long)kEmptyKey;
     s_cnt[i] = 0;
   }
   if (tid == 0) {
+    s_nd = 0;
     s_new = 0;
     s_err = 0;
   }
-  long long keyv[kOccPerThread], cur[kOccPerThread];
-  unsigned long long p[kOccPerThread];
+  long long keyv[kOccPerThread];
   bool valid[kOccPerThread];
   unsigned err = 0;
-  // phase 1: values, all loads issued together
+  // values, all loads issued together; then the transform
 #pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
     const long long j = j0 + tid + (long long)k * kThreads;
     valid[k] = j < fd.n;
     keyv[k] = valid[k] ? fd.values[j] : 0;
   }
-  // phase 2: transform, first probe of each key
 #pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    if (!valid[k]) continue;
-    keyv[k] = transform_value(keyv[k], fd, L.bnd_pool, err);
-    p[k] = ((unsigned long long)keyv[k] * 0x9E3779B97F4A7C15ull) >> L.dd_shift;
-    cur[k] = L.dd[p[k]].key;  // a stale empty is settled by the CAS
-  }
-  // phase 3: claim empty first slots, all CAS issued together
-  long long old[kOccPerThread];
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    old[k] = 0;
-    if (valid[k] && cur[k] == kEmptyKey)
-      old[k] = (long long)atomicCAS((unsigned long long*)&L.dd[p[k]].key, (unsigned long long)kEmptyKey,
-                                    (unsigned long long)keyv[k]);
-  }
-  // phase 4: resolve; a key whose first slot holds another key keeps probing
-  bool won[kOccPerThread];
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    won[k] = false;
-    if (!valid[k]) continue;
-    if (cur[k] == keyv[k]) continue;
-    if (cur[k] == kEmptyKey) {
-      if (old[k] == kEmptyKey) {
-        won[k] = true;
-        continue;
-      }
-      if (old[k] == keyv[k]) continue;
-    }
-    unsigned long long q = (p[k] + 1) & L.dd_mask;
-    while (true) {
-      const long long c = L.dd[q].key;
-      if (c == keyv[k]) break;
-      if (c == kEmptyKey) {
-        const long long o = (long long)atomicCAS((unsigned long long*)&L.dd[q].key,
-                                                 (unsigned long long)kEmptyKey, (unsigned long long)keyv[k]);
-        if (o == kEmptyKey) {
-          won[k] = true;
-          break;
-        }
-        if (o == keyv[k]) break;
-      }
-      q = (q + 1) & L.dd_mask;
-    }
-    p[k] = q;
-  }
+  for (int k = 0; k < kOccPerThread; ++k)
+    if (valid[k]) keyv[k] = transform_value(keyv[k], fd, L.bnd_pool, err);
+  if (err) atomicOr(&s_err, err);
   __syncthreads();  // LDS table initialised
-  int ent[kOccPerThread], rank[kOccPerThread], nidx[kOccPerThread];
+  // block-local dedup: entry and rank of each occurrence
+  unsigned short ent[kOccPerThread];
+  int rank[kOccPerThread];
 #pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
     ent[k] = 0;
     rank[k] = 0;
-    nidx[k] = -1;
     if (!valid[k]) continue;
-    unsigned h = ((unsigned)p[k] * 2654435761u) >> 20;  // 12 bits: kLdsTab = 4096
+    const unsigned long long key = (unsigned long long)keyv[k];
+    unsigned h = (unsigned)((key * 0x9E3779B97F4A7C15ull) >> (64 - kLdsTabBits));
     while (true) {
-      const int o = atomicCAS(&s_pos[h], -1, (int)p[k]);
-      if (o == -1 || o == (int)p[k]) break;
+      const unsigned long long o = atomicCAS(&s_key[h], (unsigned long long)kEmptyKey, key);
+      if (o == (unsigned long long)kEmptyKey) {
+        s_list[atomicAdd(&s_nd, 1)] = (unsigned short)h;
+        break;
+      }
+      if (o == key) break;
       h = (h + 1) & (kLdsTab - 1);
     }
-    ent[k] = (int)h;
+    ent[k] = (unsigned short)h;
     rank[k] = atomicAdd(&s_cnt[h], 1);
-    if (won[k]) nidx[k] = atomicAdd(&s_new, 1);
   }
-  if (err) atomicOr(&s_err, err);
   __syncthreads();
-  for (int i = tid; i < kLdsTab; i += kThreads) {
-    const int q = s_pos[i];
-    if (q >= 0) s_cnt[i] = atomicAdd(&L.dd[q].count, s_cnt[i]);  // base of this block's ranks
+  // the block's distinct keys against the global dedup table
+  const int nd = s_nd;
+  int hh[kDistPerThread];
+  unsigned long long key[kDistPerThread], p[kDistPerThread];
+  long long cur[kDistPerThread];
+#pragma unroll
+  for (int m = 0; m < kDistPerThread; ++m) {
+    const int i = tid + m * kThreads;
+    hh[m] = i < nd ? (int)s_list[i] : -1;
+    key[m] = hh[m] >= 0 ? s_key[hh[m]] : 0;
+    p[m] = (key[m] * 0x9E3779B97F4A7C15ull) >> L.dd_shift;
+    cur[m] = hh[m] >= 0 ? L.dd[p[m]].key : 0;  // a stale empty is settled by the CAS
   }
+  long long old[kDistPerThread];
+#pragma unroll
+  for (int m = 0; m < kDistPerThread; ++m) {
+    old[m] = 0;
+    if (hh[m] >= 0 && cur[m] == kEmptyKey)
+      old[m] = (long long)atomicCAS((unsigned long long*)&L.dd[p[m]].key, (unsigned long long)kEmptyKey, key[m]);
+  }
+  bool won[kDistPerThread];
+#pragma unroll
+  for (int m = 0; m < kDistPerThread; ++m) {
+    won[m] = false;
+    if (hh[m] < 0) continue;
+    const long long kv = (long long)key[m];
+    if (cur[m] == kv) continue;
+    if (cur[m] == kEmptyKey) {
+      if (old[m] == kEmptyKey) {
+        won[m] = true;
+        continue;
+      }
+      if (old[m] == kv) continue;
+    }
+    // the first slot holds another key: linear probing (the table has twice
+    // as many slots as the call has occurrences, so this is uncommon)
+    unsigned long long q = (p[m] + 1) & L.dd_mask;
+    while (true) {
+      const long long c = L.dd[q].key;
+      if (c == kv) break;
+      if (c == kEmptyKey) {
+        const long long o = (long long)atomicCAS((unsigned long long*)&L.dd[q].key,
+                                                 (unsigned long long)kEmptyKey, (unsigned long long)kv);
+        if (o == kEmptyKey) {
+          won[m] = true;
+          break;
+        }
+        if (o == kv) break;
+      }
+      q = (q + 1) & L.dd_mask;
+    }
+    p[m] = q;
+  }
+  int base[kDistPerThread], nidx[kDistPerThread];
+#pragma unroll
+  for (int m = 0; m < kDistPerThread; ++m) {
+    base[m] = 0;
+    nidx[m] = -1;
+    if (hh[m] < 0) continue;
+    base[m] = atomicAdd(&L.dd[p[m]].count, s_cnt[hh[m]]);  // base of this block's ranks
+    if (won[m]) nidx[m] = atomicAdd(&s_new, 1);
+  }
+  __syncthreads();
   if (tid == 0) {
     if (s_new > 0)
       s_ubase = (long long)atomicAdd((unsigned long long*)L.res.num_unique, (unsigned long long)s_new);
@@ -244,17 +274,24 @@ __global__ __launch_bounds__(kThreads) void k_dedup(LookupLaunch L, TableDev t) 
   }
   __syncthreads();
 #pragma unroll
+  for (int m = 0; m < kDistPerThread; ++m) {
+    if (hh[m] < 0) continue;
+    if (nidx[m] >= 0) {
+      const long long u = s_ubase + nidx[m];
+      L.dd[p[m]].uidx = (int)u;
+      L.res.unique_keys[u] = (long long)key[m];
+      L.uslot[u] = (int)p[m];
+    }
+    s_key[hh[m]] = p[m];
+    s_cnt[hh[m]] = base[m];
+  }
+  __syncthreads();
+#pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
     if (!valid[k]) continue;
     const long long gj = fd.base + j0 + tid + (long long)k * kThreads;
-    L.occ_slot[gj] = (int)p[k];
+    L.occ_slot[gj] = (int)s_key[ent[k]];
     L.occ_rank[gj] = s_cnt[ent[k]] + rank[k];
-    if (nidx[k] >= 0) {
-      const long long u = s_ubase + nidx[k];
-      L.dd[p[k]].uidx = (int)u;
-      L.res.unique_keys[u] = keyv[k];
-      L.uslot[u] = (int)p[k];
-    }
   }
 }
 
