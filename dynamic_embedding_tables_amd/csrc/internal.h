@@ -61,6 +61,14 @@ struct __align__(16) DedupSlot {
   int uidx;   // index of the key among the call's distinct keys
 };
 
+// One occurrence in its hash bucket: key, merged occurrence index, and its
+// grouped-list value (bag or occurrence).
+struct __align__(16) PartEntry {
+  long long key;
+  int occ;
+  int g;
+};
+
 struct DevCounters {
   unsigned long long next_row;  // bump pointer over EmbeddingBlocks
   long long free_top;           // entries in the free list
@@ -80,7 +88,6 @@ struct FeatDev {
   const int* offs;
   long long n;
   long long base;       // global index of its first occurrence
-  long long tile_base;  // first occurrence tile of this feature
   unsigned long long mod;
   unsigned slot;
   unsigned ops;
@@ -250,8 +257,11 @@ struct recis_table {
   long long scr_cap = 0;
   recis::DedupSlot* dd = nullptr;
   long long dd_cap = 0;
-  int* occ_slot = nullptr;
-  int* occ_rank = nullptr;
+  recis::PartEntry* part = nullptr;
+  int* hist = nullptr;
+  int* bbase = nullptr;
+  int* ubase = nullptr;
+  int* ovf = nullptr;
   int* uslot = nullptr;
   unsigned long long* blk_sums = nullptr;
   long long* wb_keys = nullptr;
@@ -275,21 +285,36 @@ void launch_fill_slots(Slot* slots, long long cap, hipStream_t s);
 void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s);
 void launch_rehash(const Slot* old_slots, long long old_cap, const TableDev& t, hipStream_t s);
 
+// Hash partition of a lookup call.
+constexpr int kPartThreads = 1024;   // partition kernels' block size
+constexpr int kPartPer = 8;          // occurrences per thread per pass
+constexpr int kPartOcc = kPartThreads * kPartPer;
+constexpr int kMaxPartBlocks = 1024;
+constexpr int kBucketOcc = 384;      // target occurrences per bucket
+constexpr int kMaxBucketBits = 13;
+constexpr int kMaxBuckets = 1 << kMaxBucketBits;
+constexpr int kBagWin = 4096;        // merged bag offsets a partition block keeps in LDS
+constexpr int kBucketPer = 4;        // occurrences per thread per pass of k_bucket
+
 struct LookupLaunch {
   const FeatDev* feats;
   const long long* bnd_pool;
   int F, B;
   long long N;
-  long long occ_tiles;
   unsigned flags;
   recis_lookup_result res;
-  DedupSlot* dd;
-  unsigned long long dd_mask;
-  int dd_shift;
-  int* occ_slot;
-  int* occ_rank;
-  int* uslot;
-  unsigned long long* blk_sums;
+  DedupSlot* dd;  // empty between calls; regions of it back overflowed buckets
+  int nbits, nbk;             // hash buckets: nbk = 2^nbits
+  int part_blocks;            // partition blocks
+  long long part_range;       // occurrences per partition block
+  int big_tab;                // buckets average more than kBucketOcc occurrences
+  int* hist;                  // [part_blocks][nbk]
+  int* bbase;                 // nbk + 1: first position of each bucket
+  int* ubase;                 // nbk + 1: distinct keys per bucket, then their first index
+  PartEntry* part;            // N
+  int* ovf;                   // 1 + nbk: count, overflowed buckets
+  unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
+  unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
   long long key_tiles;
 };
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);

@@ -10,22 +10,22 @@
 //
 // Kernel sequence of one call (all on one stream, no host read-back):
 //   k_prep      merged bag offsets, offset validation, per-call counters
-//   k_dedup     per occurrence: transform + tag, dedup within the block in
-//               LDS (rank among equal keys), then one insert into the call's
-//               dedup table and one count atomic per distinct key per block
-//               (hot keys never serialise on one address)
+//   k_part_hist / k_part_colscan / k_part_bscan / k_part_scatter
+//               transform + tag every occurrence and partition the call by
+//               the top bits of the key's hash (one radix-sort pass)
+//   k_bucket    one bucket per block: dedup in LDS, counts, distinct-key
+//               indices, group offsets, inverse index and the grouped bag /
+//               occurrence list used by the backward; k_bucket_big takes the
+//               (adversarial) buckets that overflow the LDS table
 //   k_key_probe per distinct key: IDMap probe / CAS insert, count, admission
-//               decision; block sums of (occurrences, rows to allocate)
+//               decision; block sums of the rows to allocate
 //   k_key_scan  one block: exclusive scan of the block sums; rows come from
 //               the free list first, then from the bump pointer -- by prefix
 //               sum, not by atomics
-//   k_key_finalize  per distinct key: group offsets, row assignment (the new
-//               row is marked pending, not written: its values are the
-//               initializer's until its first update), backward plan for
-//               long keys, dedup-table reset
-//   k_group     per occurrence: inverse index, the grouped bag / occurrence
-//               list used by the backward reduction, and the occurrence's row
-//               reference used by the forward
+//   k_key_finalize  per distinct key: row assignment (the new row is marked
+//               pending, not written: its values are the initializer's until
+//               its first update), backward plan for long keys
+//   k_occref    per occurrence: the row reference used by the forward
 // Memory accesses that do not depend on each other are issued as one batch
 // per thread (all loads of a phase before any use), so that each thread
 // waits once per phase rather than once per item.
@@ -63,16 +63,6 @@ __device__ unsigned long long block_exclusive_scan(unsigned long long v, unsigne
   __syncthreads();
   *total = all;
   return before + x - v;
-}
-
-__device__ __forceinline__ int find_feature(const FeatDev* feats, int F, long long blk) {
-  int lo = 0, hi = F - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (feats[mid].tile_base <= blk) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
 }
 
 // Hash -> Mod, or Bucketize, then the feature tag.
@@ -118,6 +108,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
     *L.res.num_unique = 0;
     L.res.plan[0] = 0;  // long keys
     L.res.plan[1] = 0;  // chunks
+    L.ovf[0] = 0;       // overflowed buckets
   }
   if (idx > nb) return;
   if (idx == nb) {
@@ -135,163 +126,432 @@ __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
   L.res.bag_offsets[idx] = (int)(fd.base + oc);
 }
 
-// -------------------------------------------------------------- k_dedup
-// A block takes kOccTile occurrences of one feature.  Their keys are first
-// deduplicated in an LDS table (64-bit CAS in LDS), which also gives each
-// occurrence its rank among the block's equal keys; only then does each
-// distinct key of the block touch the call's global dedup table -- one probe,
-// at most one CAS and one count atomic per block, instead of one per
-// occurrence, so the hot keys of a Zipf feature do not serialise thousands
-// of atomics on one address.  Each thread issues the global accesses of all
-// its entries together, so a phase costs one round trip.
-constexpr int kDistPerThread = kOccTile / kThreads;  // list entries a thread resolves
+// ------------------------------------------------------ hash partition
+// The call's occurrences are partitioned by the top bits of their key's
+// Fibonacci hash into nbk buckets (about kBucketOcc occurrences each), like
+// one pass of a radix sort: k_part_hist counts per (partition block,
+// bucket), two scans turn the counts into positions, and k_part_scatter
+// writes every occurrence to its bucket's range.  Each bucket is then
+// deduplicated by one block entirely in LDS (k_bucket), so the dedup needs
+// no global atomics at all: on this GPU those are performed at the memory
+// side and would bound the step.
+__device__ __forceinline__ unsigned long long fib_mix(long long key) {
+  return (unsigned long long)key * 0x9E3779B97F4A7C15ull;
+}
+__device__ __forceinline__ int bucket_of(long long key, int bits) {
+  return bits == 0 ? 0 : (int)(fib_mix(key) >> (64 - bits));
+}
 
-__global__ __launch_bounds__(kThreads) void k_dedup(LookupLaunch L, TableDev t) {
-  __shared__ unsigned long long s_key[kLdsTab];  // block's distinct keys; then their dedup slots
-  __shared__ int s_cnt[kLdsTab];                 // occurrences in the block; then the rank base
-  __shared__ unsigned short s_list[kOccTile];    // entries of s_key in use
-  __shared__ int s_nd, s_new;
-  __shared__ long long s_ubase;
+// Feature of merged occurrence j (F small: a scan of the bases).
+__device__ __forceinline__ int feature_of(const FeatDev* feats, int F, long long j) {
+  int lo = 0, hi = F - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (feats[mid].base <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Key of merged occurrence j; the feature descriptor is cached across calls
+// of one thread (its occurrences rarely change feature).
+struct FeatCursor {
+  FeatDev fd;
+  long long lo = 1, hi = 0;  // [lo, hi) of the cached feature
+};
+__device__ __forceinline__ long long key_of(const LookupLaunch& L, FeatCursor& c, long long j, unsigned& err) {
+  if (j < c.lo || j >= c.hi) {
+    c.fd = L.feats[feature_of(L.feats, L.F, j)];
+    c.lo = c.fd.base;
+    c.hi = c.fd.base + c.fd.n;
+  }
+  return transform_value(c.fd.values[j - c.fd.base], c.fd, L.bnd_pool, err);
+}
+
+__global__ __launch_bounds__(kPartThreads) void k_part_hist(LookupLaunch L, TableDev t) {
+  __shared__ int s_h[kMaxBuckets];
   __shared__ unsigned s_err;
   const int tid = threadIdx.x;
-  const long long blk = blockIdx.x;
-  const FeatDev fd = L.feats[find_feature(L.feats, L.F, blk)];
-  const long long j0 = (blk - fd.tile_base) * kOccTile;
-  for (int i = tid; i < kLdsTab; i += kThreads) {
-    s_key[i] = (unsigned long long)kEmptyKey;
+  const long long j0 = (long long)blockIdx.x * L.part_range;
+  const long long j1 = j0 + L.part_range < L.N ? j0 + L.part_range : L.N;
+  for (int b = tid; b < L.nbk; b += kPartThreads) s_h[b] = 0;
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+  FeatCursor fc;
+  unsigned err = 0;
+  for (long long c0 = j0; c0 < j1; c0 += (long long)kPartThreads * kPartPer) {
+    long long key[kPartPer];
+#pragma unroll
+    for (int k = 0; k < kPartPer; ++k) {
+      const long long j = c0 + tid + (long long)k * kPartThreads;
+      key[k] = j < j1 ? key_of(L, fc, j, err) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPartPer; ++k) {
+      const long long j = c0 + tid + (long long)k * kPartThreads;
+      if (j < j1) atomicAdd(&s_h[bucket_of(key[k], L.nbits)], 1);
+    }
+  }
+  if (err) atomicOr(&s_err, err);
+  __syncthreads();
+  int* row = L.hist + (long long)blockIdx.x * L.nbk;
+  for (int b = tid; b < L.nbk; b += kPartThreads) row[b] = s_h[b];
+  if (tid == 0 && s_err) atomicOr(&t.ctr->error, s_err);
+}
+
+// Per bucket, the exclusive prefix of its counts over the partition blocks
+// (in place) and its total.  A block takes 64 buckets (one per lane); its 16
+// waves split the partition blocks.
+__global__ __launch_bounds__(kPartThreads) void k_part_colscan(LookupLaunch L) {
+  __shared__ int s_part[kPartThreads / 64][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int W = kPartThreads / 64;
+  const int b = blockIdx.x * 64 + lane;
+  const int G = L.part_blocks;
+  const int per = (G + W - 1) / W;
+  const int g0 = w * per, g1 = g0 + per < G ? g0 + per : G;
+  int sum = 0;
+  if (b < L.nbk)
+    for (int g = g0; g < g1; ++g) sum += L.hist[(long long)g * L.nbk + b];
+  s_part[w][lane] = sum;
+  __syncthreads();
+  int run = 0, all = 0;
+#pragma unroll
+  for (int x = 0; x < W; ++x) {
+    run += x < w ? s_part[x][lane] : 0;
+    all += s_part[x][lane];
+  }
+  if (b < L.nbk) {
+    for (int g = g0; g < g1; ++g) {
+      int* p = L.hist + (long long)g * L.nbk + b;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    if (w == 0) L.bbase[b] = all;  // total, scanned by k_part_bscan
+  }
+}
+
+// In-place exclusive scan of a[0..n) (n <= kMaxBuckets), a[n] = total, and
+// the total also to *total_ll when given.  Bucket positions (bbase) and the
+// distinct-key bases of the buckets (ubase).
+__global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long long* total_ll) {
+  __shared__ int s_w[kPartThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (n + kPartThreads - 1) / kPartThreads;
+  const int b0 = tid * per;
+  int sum = 0;
+  for (int b = b0; b < b0 + per && b < n; ++b) sum += a[b];
+  int x = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl(x, lane >= d ? lane - d : lane);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_w[w] = x;
+  __syncthreads();
+  int run = x - sum, all = 0;
+#pragma unroll
+  for (int v = 0; v < kPartThreads / 64; ++v) {
+    run += v < w ? s_w[v] : 0;
+    all += s_w[v];
+  }
+  for (int b = b0; b < b0 + per && b < n; ++b) {
+    const int c = a[b];
+    a[b] = run;
+    run += c;
+  }
+  if (tid == 0) {
+    a[n] = all;
+    if (total_ll) *total_ll = all;
+  }
+}
+
+// Grouped-list value of merged occurrence j: its bag (f * B + i), found by a
+// binary search over the block's window of merged bag offsets (kept in LDS
+// when it fits), or j itself when grouping by occurrence.
+__global__ __launch_bounds__(kPartThreads) void k_part_scatter(LookupLaunch L) {
+  __shared__ int s_h[kMaxBuckets];
+  __shared__ int s_off[kBagWin];
+  __shared__ int s_blo, s_bhi;
+  const int tid = threadIdx.x;
+  const long long j0 = (long long)blockIdx.x * L.part_range;
+  const long long j1 = j0 + L.part_range < L.N ? j0 + L.part_range : L.N;
+  const bool by_occ = (L.flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
+  const int* off = L.res.bag_offsets;  // merged, F * B + 1 entries
+  const int nbags = L.F * L.B;
+  const int* row = L.hist + (long long)blockIdx.x * L.nbk;
+  for (int b = tid; b < L.nbk; b += kPartThreads) s_h[b] = L.bbase[b] + row[b];
+  if (!by_occ && tid < 2) {
+    // bag of occurrence j: the last i with off[i] <= j (empty bags skipped)
+    const long long j = tid == 0 ? j0 : j1 - 1;
+    int lo = 0, hi = nbags;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((long long)off[mid] <= j) lo = mid + 1;
+      else hi = mid;
+    }
+    const int b = lo - 1 < 0 ? 0 : lo - 1;
+    if (tid == 0) s_blo = b;
+    else s_bhi = b;
+  }
+  __syncthreads();
+  const int blo = by_occ ? 0 : s_blo, wn = by_occ ? 0 : s_bhi - s_blo + 2;
+  const bool win = wn > 0 && wn <= kBagWin;
+  if (win)
+    for (int i = tid; i < wn; i += kPartThreads) s_off[i] = off[blo + i];
+  __syncthreads();
+  FeatCursor fc;
+  unsigned err = 0;
+  for (long long c0 = j0; c0 < j1; c0 += (long long)kPartThreads * kPartPer) {
+    long long key[kPartPer];
+#pragma unroll
+    for (int k = 0; k < kPartPer; ++k) {
+      const long long j = c0 + tid + (long long)k * kPartThreads;
+      key[k] = j < j1 ? key_of(L, fc, j, err) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPartPer; ++k) {
+      const long long j = c0 + tid + (long long)k * kPartThreads;
+      if (j >= j1) continue;
+      int g;
+      if (by_occ) {
+        g = (int)j;
+      } else {
+        int lo, hi;
+        if (win) {
+          lo = 0;
+          hi = wn - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((long long)s_off[mid] <= j) lo = mid + 1;
+            else hi = mid;
+          }
+          lo += blo;
+        } else {
+          lo = 0;
+          hi = nbags;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((long long)off[mid] <= j) lo = mid + 1;
+            else hi = mid;
+          }
+        }
+        g = lo - 1;
+        g = g < 0 ? 0 : (g > nbags - 1 ? nbags - 1 : g);
+      }
+      const int pos = atomicAdd(&s_h[bucket_of(key[k], L.nbits)], 1);
+      PartEntry e;
+      e.key = key[k];
+      e.occ = (int)j;
+      e.g = g;
+      L.part[pos] = e;
+    }
+  }
+}
+
+// One bucket per block, in two launches around a scan of the per-bucket
+// distinct counts (so the distinct keys get dense indices without a global
+// counter, which thousands of blocks would serialise on).  Both launches
+// deduplicate the bucket in an LDS table of TAB entries (at most 3/4 full; a
+// bucket with more distinct keys is marked -1 and handed to k_bucket_big).
+// COUNT writes the bucket's distinct count; EMIT writes the distinct keys
+// (index ubase[b] + their order in the table), counts and group offsets
+// inside the bucket's range, then every occurrence's inverse index and
+// grouped-list entry.
+template <int TAB, bool EMIT>
+__global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L) {
+  constexpr int kMaxDistinct = TAB / 4 * 3;
+  constexpr int kTabBits = TAB == 1024 ? 10 : (TAB == 2048 ? 11 : 0);
+  static_assert(kTabBits > 0, "TAB is 1024 or 2048");
+  __shared__ long long s_key[TAB];
+  __shared__ int s_cnt[TAB];
+  __shared__ int s_u[EMIT ? TAB : 1];
+  __shared__ unsigned short s_list[kMaxDistinct];
+  __shared__ int s_nd, s_over, s_cursor;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int s = L.bbase[b], m = L.bbase[b + 1] - s;
+  if (m == 0) {
+    if (!EMIT && tid == 0) L.ubase[b] = 0;
+    return;
+  }
+  for (int i = tid; i < TAB; i += kThreads) {
+    s_key[i] = kEmptyKey;
     s_cnt[i] = 0;
   }
   if (tid == 0) {
     s_nd = 0;
-    s_new = 0;
-    s_err = 0;
-  }
-  long long keyv[kOccPerThread];
-  bool valid[kOccPerThread];
-  unsigned err = 0;
-  // values, all loads issued together; then the transform
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    const long long j = j0 + tid + (long long)k * kThreads;
-    valid[k] = j < fd.n;
-    keyv[k] = valid[k] ? fd.values[j] : 0;
-  }
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k)
-    if (valid[k]) keyv[k] = transform_value(keyv[k], fd, L.bnd_pool, err);
-  if (err) atomicOr(&s_err, err);
-  __syncthreads();  // LDS table initialised
-  // block-local dedup: entry and rank of each occurrence
-  unsigned short ent[kOccPerThread];
-  int rank[kOccPerThread];
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    ent[k] = 0;
-    rank[k] = 0;
-    if (!valid[k]) continue;
-    const unsigned long long key = (unsigned long long)keyv[k];
-    unsigned h = (unsigned)((key * 0x9E3779B97F4A7C15ull) >> (64 - kLdsTabBits));
-    while (true) {
-      const unsigned long long o = atomicCAS(&s_key[h], (unsigned long long)kEmptyKey, key);
-      if (o == (unsigned long long)kEmptyKey) {
-        s_list[atomicAdd(&s_nd, 1)] = (unsigned short)h;
-        break;
-      }
-      if (o == key) break;
-      h = (h + 1) & (kLdsTab - 1);
-    }
-    ent[k] = (unsigned short)h;
-    rank[k] = atomicAdd(&s_cnt[h], 1);
+    s_over = 0;
+    s_cursor = 0;
   }
   __syncthreads();
-  // the block's distinct keys against the global dedup table
-  const int nd = s_nd;
-  int hh[kDistPerThread];
-  unsigned long long key[kDistPerThread], p[kDistPerThread];
-  long long cur[kDistPerThread];
+  // the bits below the bucket bits index the table
+  const int hs = 64 - L.nbits - kTabBits;
+  for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
+    long long key[kBucketPer];
 #pragma unroll
-  for (int m = 0; m < kDistPerThread; ++m) {
-    const int i = tid + m * kThreads;
-    hh[m] = i < nd ? (int)s_list[i] : -1;
-    key[m] = hh[m] >= 0 ? s_key[hh[m]] : 0;
-    p[m] = (key[m] * 0x9E3779B97F4A7C15ull) >> L.dd_shift;
-    cur[m] = hh[m] >= 0 ? L.dd[p[m]].key : 0;  // a stale empty is settled by the CAS
-  }
-  long long old[kDistPerThread];
-#pragma unroll
-  for (int m = 0; m < kDistPerThread; ++m) {
-    old[m] = 0;
-    if (hh[m] >= 0 && cur[m] == kEmptyKey)
-      old[m] = (long long)atomicCAS((unsigned long long*)&L.dd[p[m]].key, (unsigned long long)kEmptyKey, key[m]);
-  }
-  bool won[kDistPerThread];
-#pragma unroll
-  for (int m = 0; m < kDistPerThread; ++m) {
-    won[m] = false;
-    if (hh[m] < 0) continue;
-    const long long kv = (long long)key[m];
-    if (cur[m] == kv) continue;
-    if (cur[m] == kEmptyKey) {
-      if (old[m] == kEmptyKey) {
-        won[m] = true;
-        continue;
-      }
-      if (old[m] == kv) continue;
+    for (int k = 0; k < kBucketPer; ++k) {
+      const int i = i0 + tid + k * kThreads;
+      key[k] = i < m ? L.part[s + i].key : 0;
     }
-    // the first slot holds another key: linear probing (the table has twice
-    // as many slots as the call has occurrences, so this is uncommon)
-    unsigned long long q = (p[m] + 1) & L.dd_mask;
-    while (true) {
-      const long long c = L.dd[q].key;
-      if (c == kv) break;
-      if (c == kEmptyKey) {
-        const long long o = (long long)atomicCAS((unsigned long long*)&L.dd[q].key,
-                                                 (unsigned long long)kEmptyKey, (unsigned long long)kv);
+#pragma unroll
+    for (int k = 0; k < kBucketPer; ++k) {
+      if (i0 + tid + k * kThreads >= m) continue;
+      unsigned h = (unsigned)(fib_mix(key[k]) >> hs) & (TAB - 1);
+      int steps = 0;
+      while (true) {
+        const long long o = (long long)atomicCAS((unsigned long long*)&s_key[h], (unsigned long long)kEmptyKey,
+                                                 (unsigned long long)key[k]);
         if (o == kEmptyKey) {
-          won[m] = true;
+          const int idx = atomicAdd(&s_nd, 1);
+          if (idx < kMaxDistinct) s_list[idx] = (unsigned short)h;
+          else s_over = 1;
           break;
         }
-        if (o == kv) break;
+        if (o == key[k]) break;
+        h = (h + 1) & (TAB - 1);
+        if (++steps == TAB) {  // full: only after the distinct limit was passed
+          s_over = 1;
+          break;
+        }
       }
-      q = (q + 1) & L.dd_mask;
+      if (steps < TAB) atomicAdd(&s_cnt[h], 1);
     }
-    p[m] = q;
-  }
-  int base[kDistPerThread], nidx[kDistPerThread];
-#pragma unroll
-  for (int m = 0; m < kDistPerThread; ++m) {
-    base[m] = 0;
-    nidx[m] = -1;
-    if (hh[m] < 0) continue;
-    base[m] = atomicAdd(&L.dd[p[m]].count, s_cnt[hh[m]]);  // base of this block's ranks
-    if (won[m]) nidx[m] = atomicAdd(&s_new, 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    if (s_new > 0)
-      s_ubase = (long long)atomicAdd((unsigned long long*)L.res.num_unique, (unsigned long long)s_new);
-    if (s_err) atomicOr(&t.ctr->error, s_err);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < kDistPerThread; ++m) {
-    if (hh[m] < 0) continue;
-    if (nidx[m] >= 0) {
-      const long long u = s_ubase + nidx[m];
-      L.dd[p[m]].uidx = (int)u;
-      L.res.unique_keys[u] = (long long)key[m];
-      L.uslot[u] = (int)p[m];
+  if (EMIT && s_over) return;  // k_bucket_big's
+  if (!EMIT) {
+    if (tid == 0) {
+      if (s_over) {
+        const int k = atomicAdd(&L.ovf[0], 1);  // rare: colliding inputs only
+        L.ovf[1 + k] = b;
+        L.ubase[b] = 0;  // counted by k_bucket_big
+      } else {
+        L.ubase[b] = s_nd;
+      }
     }
-    s_key[hh[m]] = p[m];
-    s_cnt[hh[m]] = base[m];
+    return;
+  }
+  const int nd = s_nd;
+  const long long ub = L.ubase[b];
+  for (int idx = tid; idx < nd; idx += kThreads) {
+    const int h = s_list[idx];
+    const long long u = ub + idx;
+    const int c = s_cnt[h];
+    const int o = atomicAdd(&s_cursor, c);
+    L.res.unique_keys[u] = s_key[h];
+    L.res.counts[u] = c;
+    L.res.unique_offsets[u] = s + o;
+    s_u[h] = (int)u;
+    s_cnt[h] = o;  // from here on: the next free position of the key's group
   }
   __syncthreads();
+  for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
+    PartEntry e[kBucketPer];
 #pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    if (!valid[k]) continue;
-    const long long gj = fd.base + j0 + tid + (long long)k * kThreads;
-    L.occ_slot[gj] = (int)s_key[ent[k]];
-    L.occ_rank[gj] = s_cnt[ent[k]] + rank[k];
+    for (int k = 0; k < kBucketPer; ++k) {
+      const int i = i0 + tid + k * kThreads;
+      if (i < m) e[k] = L.part[s + i];
+    }
+#pragma unroll
+    for (int k = 0; k < kBucketPer; ++k) {
+      if (i0 + tid + k * kThreads >= m) continue;
+      unsigned h = (unsigned)(fib_mix(e[k].key) >> hs) & (TAB - 1);
+      while (s_key[h] != e[k].key) h = (h + 1) & (TAB - 1);
+      const int pos = atomicAdd(&s_cnt[h], 1);
+      L.res.grouped[s + pos] = e[k].g;
+      L.res.inverse[e[k].occ] = s_u[h];
+    }
+  }
+}
+
+// Buckets whose distinct keys overflowed the LDS table (only inputs built to
+// collide in the hash's top bits get here): the same steps with an open-
+// addressing table in global memory, the bucket's own region of the dedup
+// table (2 slots per occurrence), and atomics.  Slow but bounded; the region
+// is left empty again.
+__device__ __forceinline__ long long ld_key(const DedupSlot* d) {
+  return (long long)__hip_atomic_load(reinterpret_cast<const unsigned long long*>(&d->key), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_int(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_int(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// COUNT: insert the bucket's keys into its region and count them; its
+// distinct count goes to ubase[b].  EMIT (after the scan): the distinct keys'
+// outputs, the occurrences' inverse and grouped entries, then the region is
+// emptied again.
+template <bool EMIT>
+__global__ __launch_bounds__(kThreads) void k_bucket_big(LookupLaunch L) {
+  __shared__ int s_nd, s_cursor;
+  const int tid = threadIdx.x;
+  for (int q = blockIdx.x; q < ld_int(&L.ovf[0]); q += gridDim.x) {
+    const int b = L.ovf[1 + q];
+    const int s = L.bbase[b], m = L.bbase[b + 1] - s;
+    DedupSlot* R = L.dd + 2ll * s;
+    const unsigned long long cap = 2ull * (unsigned long long)m;
+    if (tid == 0) {
+      s_nd = 0;
+      s_cursor = 0;
+    }
+    if (!EMIT) {
+      for (int i = tid; i < m; i += kThreads) {
+        const long long key = L.part[s + i].key;
+        unsigned long long h = (fib_mix(key) >> 20) % cap;
+        while (true) {
+          const long long c = ld_key(&R[h]);
+          if (c == key) break;
+          if (c == kEmptyKey) {
+            const long long o = (long long)atomicCAS((unsigned long long*)&R[h].key,
+                                                     (unsigned long long)kEmptyKey, (unsigned long long)key);
+            if (o == kEmptyKey || o == key) break;
+          }
+          h = h + 1 == cap ? 0 : h + 1;
+        }
+        atomicAdd(&R[h].count, 1);
+      }
+      __syncthreads();
+      for (unsigned long long h = tid; h < cap; h += kThreads)
+        if (ld_key(&R[h]) != kEmptyKey) atomicAdd(&s_nd, 1);
+      __syncthreads();
+      if (tid == 0) L.ubase[b] = s_nd;
+      __syncthreads();
+      continue;
+    }
+    __syncthreads();
+    const long long ub = L.ubase[b];
+    for (unsigned long long h = tid; h < cap; h += kThreads) {
+      const long long key = ld_key(&R[h]);
+      if (key == kEmptyKey) continue;
+      const long long u = ub + atomicAdd(&s_nd, 1);
+      const int c = ld_int(&R[h].count);
+      const int o = atomicAdd(&s_cursor, c);
+      L.res.unique_keys[u] = key;
+      L.res.counts[u] = c;
+      st_int(&L.res.unique_offsets[u], s + o);
+      st_int(&R[h].uidx, (int)u);
+    }
+    __syncthreads();
+    for (int i = tid; i < m; i += kThreads) {
+      const PartEntry e = L.part[s + i];
+      unsigned long long h = (fib_mix(e.key) >> 20) % cap;
+      while (ld_key(&R[h]) != e.key) h = h + 1 == cap ? 0 : h + 1;
+      const int u = ld_int(&R[h].uidx);
+      const int pos = atomicSub(&R[h].count, 1) - 1;  // the group is filled from its end
+      L.res.grouped[ld_int(&L.res.unique_offsets[u]) + pos] = e.g;
+      L.res.inverse[e.occ] = u;
+    }
+    __syncthreads();
+    for (unsigned long long h = tid; h < cap; h += kThreads) {
+      R[h].key = kEmptyKey;
+      R[h].count = 0;
+    }
+    __syncthreads();
   }
 }
 
@@ -299,29 +559,26 @@ __global__ __launch_bounds__(kThreads) void k_dedup(LookupLaunch L, TableDev t) 
 // One distinct key per thread.  The first probe loads the whole 16-byte slot,
 // so a hit costs one dependent access after the key itself.
 __global__ __launch_bounds__(kThreads) void k_key_probe(LookupLaunch L, TableDev t) {
-  __shared__ unsigned s_ins;
   __shared__ unsigned s_err;
   const long long U = *L.res.num_unique;
   const long long t0 = (long long)blockIdx.x * kKeyTile;
   if (t0 >= U) {
-    if (threadIdx.x == 0) L.blk_sums[blockIdx.x] = 0;
+    if (threadIdx.x == 0) {
+      L.blk_sums[blockIdx.x] = 0;
+      L.blk_long[blockIdx.x] = 0;
+    }
     return;
   }
-  if (threadIdx.x == 0) {
-    s_ins = 0;
-    s_err = 0;
-  }
+  if (threadIdx.x == 0) s_err = 0;
   __syncthreads();
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
   unsigned* idslot = reinterpret_cast<unsigned*>(L.res.plan + plan_layout(L.res.capacity).o_idslot);
-  unsigned long long acc = 0;
+  unsigned long long acc = 0, acc_long = 0;
   unsigned ins = 0, err = 0;
   const long long u = t0 + threadIdx.x;
   if (u < U) {
     const long long key = L.res.unique_keys[u];
-    const int us = L.uslot[u];
-    const int c = L.dd[us].count;
-    L.res.counts[u] = c;
+    const int c = L.res.counts[u];
     long long row = -1;
     unsigned sl = 0xFFFFFFFFu;
     int need = 0;
@@ -373,29 +630,32 @@ __global__ __launch_bounds__(kThreads) void k_key_probe(LookupLaunch L, TableDev
     if (row >= 0 && (row & kPendingRow)) row = (row & ~(long long)kPendingRow) | kFreshRow;
     L.res.unique_rows[u] = need ? -2 : row;
     idslot[u] = sl;
-    acc = ((unsigned long long)need << 32) | (unsigned)c;
+    acc = ((unsigned long long)need << 32) | ins;
+    // a key that will have a row and more than kShortMax occurrences is
+    // reduced in chunks by the backward
+    if (c > kShortMax && (need || row >= 0))
+      acc_long = (1ull << 32) | (unsigned long long)((c + kChunk - 1) / kChunk);
   }
-  if (ins) atomicAdd(&s_ins, ins);
   if (err) atomicOr(&s_err, err);
-  unsigned long long total;
+  unsigned long long total, total_long;
   block_exclusive_scan(acc, &total);
+  block_exclusive_scan(acc_long, &total_long);
   if (threadIdx.x == 0) {
     L.blk_sums[blockIdx.x] = total;
-    if (s_ins) atomicAdd(&t.ctr->num_keys, (unsigned long long)s_ins);
+    L.blk_long[blockIdx.x] = total_long;
     if (s_err) atomicOr(&t.ctr->error, s_err);
   }
 }
 
 // ----------------------------------------------------------- k_key_scan
 constexpr int kScanThreads = 1024;
-__global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, TableDev t) {
+// In-place exclusive scan of a[0..n) by one block; returns the total.
+__device__ unsigned long long scan_tiles(unsigned long long* a, long long n) {
   __shared__ unsigned long long s_w[kScanThreads / 64];
-  const long long U = *L.res.num_unique;
-  const long long nblk = (U + kKeyTile - 1) / kKeyTile;
-  const long long per = (nblk + kScanThreads - 1) / kScanThreads;
+  const long long per = (n + kScanThreads - 1) / kScanThreads;
   const long long b0 = (long long)threadIdx.x * per;
   unsigned long long sum = 0;
-  for (long long b = b0; b < b0 + per && b < nblk; ++b) sum += L.blk_sums[b];
+  for (long long b = b0; b < b0 + per && b < n; ++b) sum += a[b];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   unsigned long long x = sum;
   for (int d = 1; d < 64; d <<= 1) {
@@ -409,12 +669,24 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
     if (w < wid) before += s_w[w];
     all += s_w[w];
   }
+  __syncthreads();
   unsigned long long run = before + x - sum;
-  for (long long b = b0; b < b0 + per && b < nblk; ++b) {
-    const unsigned long long v = L.blk_sums[b];
-    L.blk_sums[b] = run;
+  for (long long b = b0; b < b0 + per && b < n; ++b) {
+    const unsigned long long v = a[b];
+    a[b] = run;
     run += v;
   }
+  return all;
+}
+
+// One block: prefix sums of the key tiles' (rows to allocate, keys inserted)
+// and (long keys, chunks); the row sources of this call; the key and chunk
+// counts of the backward plan.
+__global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, TableDev t) {
+  const long long U = *L.res.num_unique;
+  const long long nblk = (U + kKeyTile - 1) / kKeyTile;
+  const unsigned long long all = scan_tiles(L.blk_sums, nblk);
+  const unsigned long long all_long = scan_tiles(L.blk_long, nblk);
   if (threadIdx.x == 0) {
     const long long R = (long long)(all >> 32);
     const long long Fr = t.ctr->free_top > 0 ? t.ctr->free_top : 0;
@@ -427,7 +699,10 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
     t.ctr->bump_base = base;
     t.ctr->free_top = Fr - take;
     t.ctr->next_row = (unsigned long long)next;
-    L.res.unique_offsets[U] = (int)(all & 0xFFFFFFFFull);
+    t.ctr->num_keys += all & 0xFFFFFFFFull;
+    L.res.unique_offsets[U] = (int)L.N;
+    L.res.plan[0] = (int)(all_long >> 32);
+    L.res.plan[1] = (int)(all_long & 0xFFFFFFFFull);
   }
 }
 
@@ -440,23 +715,25 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
   if (threadIdx.x == 0) s_err = 0;
   const long long u = t0 + threadIdx.x;
   const bool valid = u < U;
-  int cnt = 0, us = 0;
+  int cnt = 0;
   long long mark = -1;
   if (valid) {
     cnt = L.res.counts[u];
     mark = L.res.unique_rows[u];
-    us = L.uslot[u];
   }
-  const unsigned long long acc = valid ? (((unsigned long long)(mark == -2) << 32) | (unsigned)cnt) : 0ull;
+  const unsigned long long acc = valid ? ((unsigned long long)(mark == -2) << 32) : 0ull;
+  const bool is_long = valid && cnt > kShortMax && mark != -1;  // as k_key_probe counted it
+  const int nch = (cnt + kChunk - 1) / kChunk;
+  const unsigned long long acc_long = is_long ? ((1ull << 32) | (unsigned long long)nch) : 0ull;
   unsigned long long total;
   const unsigned long long run = block_exclusive_scan(acc, &total) + L.blk_sums[blockIdx.x];
+  const unsigned long long run_long = block_exclusive_scan(acc_long, &total) + L.blk_long[blockIdx.x];
   unsigned err = 0;
   if (valid) {
     const PlanLayout pl = plan_layout(L.res.capacity);
     int* plan = L.res.plan;
     const unsigned* idslot = reinterpret_cast<const unsigned*>(plan + pl.o_idslot);
     const long long take = t.ctr->take_free, ftop = t.ctr->free_top_old, base = t.ctr->bump_base;
-    L.res.unique_offsets[u] = (int)(run & 0xFFFFFFFFull);
     long long row = mark;
     if (row == -2) {
       const long long i = (long long)(run >> 32);
@@ -471,121 +748,42 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
         L.res.unique_rows[u] = row | kFreshRow;
       }
     }
-    if (cnt > kShortMax && row >= 0) {
-      const int idx = atomicAdd(&plan[0], 1);
-      const int nch = (cnt + kChunk - 1) / kChunk;
-      const int cb = atomicAdd(&plan[1], nch);
+    if (is_long) {  // a failed allocation (row -1) is skipped by the backward
+      const int idx = (int)(run_long >> 32);
+      const int cb = (int)(run_long & 0xFFFFFFFFull);
       plan[pl.o_long_u + idx] = (int)u;
       plan[pl.o_long_base + idx] = cb;
       plan[pl.o_long_nch + idx] = nch;
       for (int q = 0; q < nch; ++q) plan[pl.o_chunk_owner + cb + q] = idx;
     }
-    DedupSlot* d = &L.dd[us];
-    d->key = kEmptyKey;
-    d->count = 0;
   }
   if (err) atomicOr(&s_err, err);
   __syncthreads();
   if (threadIdx.x == 0 && s_err) atomicOr(&t.ctr->error, s_err);
 }
 
-// -------------------------------------------------------------- k_group
-__global__ __launch_bounds__(kThreads) void k_group(LookupLaunch L, TableDev t) {
-  constexpr int kLdsOff = 4096;
-  __shared__ int s_off[kLdsOff];
-  __shared__ int s_blo, s_bhi;
-  const int tid = threadIdx.x;
-  const long long blk = blockIdx.x;
-  const int f = find_feature(L.feats, L.F, blk);
-  const FeatDev fd = L.feats[f];
-  const long long j0 = (blk - fd.tile_base) * kOccTile;
-  const bool by_occ = (L.flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
-  const int B = L.B;
+// ------------------------------------------------------------- k_occref
+// Per occurrence: the row reference the forward reads while the lookup is
+// current (a row, the pending key, or no row).
+__global__ __launch_bounds__(kThreads) void k_occref(LookupLaunch L) {
   long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
-  if (!by_occ) {
-    if (tid < 2) {
-      // bag containing occurrence j: the last i with offs[i] <= j, clamped to [0, B)
-      const long long j = tid == 0 ? j0 : ((j0 + kOccTile < fd.n ? j0 + kOccTile : fd.n) - 1);
-      int lo = 0, hi = B;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((long long)fd.offs[mid] <= j) lo = mid + 1;
-        else hi = mid;
-      }
-      int b = lo - 1;
-      b = b < 0 ? 0 : (b > B - 1 ? B - 1 : b);
-      if (tid == 0) s_blo = b;
-      else s_bhi = b;
-    }
-    __syncthreads();
-    const int cnt = s_bhi - s_blo + 2;
-    if (cnt <= kLdsOff && cnt > 0)
-      for (int i = tid; i < cnt; i += kThreads) s_off[i] = fd.offs[s_blo + i];
-    __syncthreads();
-  }
-  // phase 1: this thread's occurrences (coalesced)
-  int p[kOccPerThread], rk[kOccPerThread];
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    const long long j = j0 + tid + (long long)k * kThreads;
-    p[k] = -1;
-    if (j < fd.n) {
-      p[k] = L.occ_slot[fd.base + j];
-      rk[k] = L.occ_rank[fd.base + j];
-    }
-  }
-  // phase 2: distinct-key index of each
+  const long long j0 = (long long)blockIdx.x * kOccTile + threadIdx.x;
   int u[kOccPerThread];
 #pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) u[k] = p[k] >= 0 ? L.dd[p[k]].uidx : 0;
-  // phase 3: group offset, row and key of each distinct key
-  int uo[kOccPerThread];
-  long long r[kOccPerThread], key[kOccPerThread];
-#pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
-    if (p[k] < 0) continue;
-    uo[k] = L.res.unique_offsets[u[k]];
-    r[k] = L.res.unique_rows[u[k]];
-    key[k] = L.res.unique_keys[u[k]];
+    const long long j = j0 + (long long)k * kThreads;
+    u[k] = j < L.N ? L.res.inverse[j] : -1;
   }
-  // phase 4: outputs
+  long long r[kOccPerThread];
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k) r[k] = u[k] >= 0 ? L.res.unique_rows[u[k]] : -1;
 #pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
-    if (p[k] < 0) continue;
-    const long long j = j0 + tid + (long long)k * kThreads;
-    const long long gj = fd.base + j;
-    int gval;
-    if (by_occ) {
-      gval = (int)gj;
-    } else {
-      const int blo = s_blo, cnt = s_bhi - s_blo + 2;
-      int lo, hi;
-      if (cnt <= kLdsOff && cnt > 0) {
-        lo = 0;
-        hi = cnt - 1;  // search offsets[blo .. bhi]
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if ((long long)s_off[mid] <= j) lo = mid + 1;
-          else hi = mid;
-        }
-        lo += blo;
-      } else {
-        lo = 0;
-        hi = B;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if ((long long)fd.offs[mid] <= j) lo = mid + 1;
-          else hi = mid;
-        }
-      }
-      int i = lo - 1;
-      i = i < 0 ? 0 : (i > B - 1 ? B - 1 : i);
-      gval = f * B + i;
-    }
-    L.res.inverse[gj] = u[k];
-    L.res.grouped[uo[k] + rk[k]] = gval;
-    occref[gj] = r[k] < 0 ? kOccNoRow
-                          : ((r[k] & kFreshRow) ? (long long)(kOccPendingBit | (unsigned long long)key[k]) : r[k]);
+    if (u[k] < 0) continue;
+    long long v = r[k];
+    if (v < 0) v = kOccNoRow;
+    else if (v & kFreshRow) v = (long long)(kOccPendingBit | (unsigned long long)L.res.unique_keys[u[k]]);
+    occref[j0 + (long long)k * kThreads] = v;
   }
 }
 
@@ -596,13 +794,30 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
   hipLaunchKernelGGL(k_prep, dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
                      L, t);
   if (L.N > 0) {
-    hipLaunchKernelGGL(k_dedup, dim3((unsigned)L.occ_tiles), dim3(kThreads), 0, s, L, t);
+    const unsigned G = (unsigned)L.part_blocks;
+    hipLaunchKernelGGL(k_part_hist, dim3(G), dim3(kPartThreads), 0, s, L, t);
+    hipLaunchKernelGGL(k_part_colscan, dim3((unsigned)((L.nbk + 63) / 64)), dim3(kPartThreads), 0, s, L);
+    hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kPartThreads), 0, s, L.bbase, L.nbk, (long long*)nullptr);
+    hipLaunchKernelGGL(k_part_scatter, dim3(G), dim3(kPartThreads), 0, s, L);
+    const dim3 nb_grid((unsigned)L.nbk);
+    if (L.big_tab)
+      hipLaunchKernelGGL((k_bucket<2048, false>), nb_grid, dim3(kThreads), 0, s, L);
+    else
+      hipLaunchKernelGGL((k_bucket<1024, false>), nb_grid, dim3(kThreads), 0, s, L);
+    hipLaunchKernelGGL(k_bucket_big<false>, dim3(64), dim3(kThreads), 0, s, L);
+    hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kPartThreads), 0, s, L.ubase, L.nbk,
+                       reinterpret_cast<long long*>(L.res.num_unique));
+    if (L.big_tab)
+      hipLaunchKernelGGL((k_bucket<2048, true>), nb_grid, dim3(kThreads), 0, s, L);
+    else
+      hipLaunchKernelGGL((k_bucket<1024, true>), nb_grid, dim3(kThreads), 0, s, L);
+    hipLaunchKernelGGL(k_bucket_big<true>, dim3(64), dim3(kThreads), 0, s, L);
     hipLaunchKernelGGL(k_key_probe, dim3((unsigned)L.key_tiles), dim3(kThreads), 0, s, L, t);
   }
   hipLaunchKernelGGL(k_key_scan, dim3(1), dim3(kScanThreads), 0, s, L, t);
   if (L.N > 0) {
     hipLaunchKernelGGL(k_key_finalize, dim3((unsigned)L.key_tiles), dim3(kThreads), 0, s, L, t);
-    hipLaunchKernelGGL(k_group, dim3((unsigned)L.occ_tiles), dim3(kThreads), 0, s, L, t);
+    hipLaunchKernelGGL(k_occref, dim3((unsigned)((L.N + kOccTile - 1) / kOccTile)), dim3(kThreads), 0, s, L);
   }
 }
 

@@ -179,40 +179,91 @@ recis_status ensure_capacity(recis_table* t, long long n, hipStream_t s) {
   return RECIS_OK;
 }
 
+// Hash-partition geometry of a call with n occurrences: buckets of about
+// kBucketOcc occurrences (a power of two, at most kMaxBuckets), partition
+// blocks of about kPartOcc occurrences (at most kMaxPartBlocks).
+struct PartGeom {
+  int nbits, nbk, blocks, big;
+  long long range;
+};
+PartGeom part_geom(long long n) {
+  PartGeom g;
+  const long long want = std::max<long long>(1, (n + kBucketOcc - 1) / kBucketOcc);
+  g.nbk = (int)std::min<long long>(next_pow2(want), kMaxBuckets);
+  g.nbits = log2_exact(g.nbk);
+  g.blocks = (int)std::min<long long>(std::max<long long>(1, (n + kPartOcc - 1) / kPartOcc), kMaxPartBlocks);
+  g.range = std::max<long long>(1, (n + g.blocks - 1) / g.blocks);
+  g.big = n > (long long)g.nbk * kBucketOcc ? 1 : 0;
+  return g;
+}
+
+// Bytes of each per-step scratch array for cap occurrences.
+struct ScratchSizes {
+  size_t dd, part, hist, bbase, ovf, uslot, blk, wb, partials;
+};
+ScratchSizes scratch_sizes(long long cap, int dim) {
+  ScratchSizes z;
+  const PartGeom g = part_geom(cap);
+  z.dd = (size_t)(2 * cap) * sizeof(DedupSlot);
+  z.part = (size_t)cap * sizeof(PartEntry);
+  z.hist = (size_t)g.blocks * (size_t)g.nbk * 4;
+  z.bbase = (size_t)(kMaxBuckets + 1) * 4 * 2;  // bbase, then ubase
+  z.ovf = (size_t)(kMaxBuckets + 1) * 4;
+  z.uslot = (size_t)cap * 4;
+  z.blk = (size_t)(cap / kKeyTile + 2) * 8 * 2;  // blk_sums, then blk_long
+  z.wb = (size_t)cap * 8;
+  z.partials = (size_t)plan_layout(cap).max_chunks * (size_t)dim * 8;
+  return z;
+}
+
+void free_scratch(recis_table* t, hipStream_t s) {
+  if (!t->scr_cap) return;
+  const ScratchSizes z = scratch_sizes(t->scr_cap, t->cfg.dim);
+  tab_free(t, t->dd, z.dd, s);
+  tab_free(t, t->part, z.part, s);
+  tab_free(t, t->hist, z.hist, s);
+  tab_free(t, t->bbase, z.bbase, s);
+  tab_free(t, t->ovf, z.ovf, s);
+  tab_free(t, t->uslot, z.uslot, s);
+  tab_free(t, t->blk_sums, z.blk, s);
+  tab_free(t, t->wb_keys, z.wb, s);
+  tab_free(t, t->partials, z.partials, s);
+  t->dd = nullptr;
+  t->part = nullptr;
+  t->hist = t->bbase = t->ubase = t->ovf = t->uslot = nullptr;
+  t->blk_sums = nullptr;
+  t->wb_keys = nullptr;
+  t->partials = nullptr;
+  t->scr_cap = 0;
+  t->dd_cap = 0;
+}
+
 // Per-step scratch sized for n occurrences.
 recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
   if (n <= t->scr_cap && t->dd) return RECIS_OK;
   const long long cap = std::max<long long>(next_pow2(std::max<long long>(n, 1)), 4096);
   HIP_TRY(hipStreamSynchronize(s));
-  const long long old = t->scr_cap;
-  const long long old_dd = t->dd_cap;
-  const PlanLayout opl = plan_layout(old);
-  tab_free(t, t->dd, (size_t)old_dd * sizeof(DedupSlot), s);
-  tab_free(t, t->occ_slot, (size_t)old * 4, s);
-  tab_free(t, t->occ_rank, (size_t)old * 4, s);
-  tab_free(t, t->uslot, (size_t)old * 4, s);
-  tab_free(t, t->blk_sums, (size_t)(old / kKeyTile + 2) * 8, s);
-  tab_free(t, t->wb_keys, (size_t)old * 8, s);
-  tab_free(t, t->partials, (size_t)opl.max_chunks * t->cfg.dim * 8, s);
-  t->dd = nullptr;
-  t->scr_cap = 0;
-  const PlanLayout pl = plan_layout(cap);
+  free_scratch(t, s);
+  const ScratchSizes z = scratch_sizes(cap, t->cfg.dim);
+  t->scr_cap = cap;  // sizes of whatever is allocated below, for free_scratch
   t->dd_cap = 2 * cap;
-  t->dd = static_cast<DedupSlot*>(tab_alloc(t, (size_t)t->dd_cap * sizeof(DedupSlot), s));
-  t->occ_slot = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
-  t->occ_rank = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
-  t->uslot = static_cast<int*>(tab_alloc(t, (size_t)cap * 4, s));
-  t->blk_sums = static_cast<unsigned long long*>(tab_alloc(t, (size_t)(cap / kKeyTile + 2) * 8, s));
-  t->wb_keys = static_cast<long long*>(tab_alloc(t, (size_t)cap * 8, s));
-  t->partials = static_cast<double*>(tab_alloc(t, (size_t)pl.max_chunks * t->cfg.dim * 8, s));
-  if (!t->dd || !t->occ_slot || !t->occ_rank || !t->uslot || !t->blk_sums || !t->wb_keys ||
-      !t->partials)
+  t->dd = static_cast<DedupSlot*>(tab_alloc(t, z.dd, s));
+  t->part = static_cast<PartEntry*>(tab_alloc(t, z.part, s));
+  t->hist = static_cast<int*>(tab_alloc(t, z.hist, s));
+  t->bbase = static_cast<int*>(tab_alloc(t, z.bbase, s));
+  t->ubase = t->bbase ? t->bbase + (kMaxBuckets + 1) : nullptr;
+  t->ovf = static_cast<int*>(tab_alloc(t, z.ovf, s));
+  t->uslot = static_cast<int*>(tab_alloc(t, z.uslot, s));
+  t->blk_sums = static_cast<unsigned long long*>(tab_alloc(t, z.blk, s));
+  t->wb_keys = static_cast<long long*>(tab_alloc(t, z.wb, s));
+  t->partials = static_cast<double*>(tab_alloc(t, z.partials, s));
+  if (!t->dd || !t->part || !t->hist || !t->bbase || !t->ovf || !t->uslot || !t->blk_sums || !t->wb_keys ||
+      !t->partials) {
+    free_scratch(t, s);
     return RECIS_ERR_OUT_OF_MEMORY;
+  }
   launch_fill_dedup(t->dd, t->dd_cap, s);
-  recis_status st = check_launch();
-  if (st != RECIS_OK) return st;
-  t->scr_cap = cap;
-  return RECIS_OK;
+  return check_launch();
 }
 
 // Copies `bytes` of host data to device memory through the pinned ring.
@@ -346,16 +397,7 @@ recis_status recis_idmap_destroy(recis_table* t) {
   tab_free(t, t->free_list, (size_t)t->free_cap * 4, s);
   tab_free(t, t->slots, (size_t)t->slot_cap * sizeof(Slot), s);
   tab_free(t, t->ctr, sizeof(DevCounters), s);
-  const long long old = t->scr_cap;
-  if (t->dd) {
-    tab_free(t, t->dd, (size_t)t->dd_cap * sizeof(DedupSlot), s);
-    tab_free(t, t->occ_slot, (size_t)old * 4, s);
-    tab_free(t, t->occ_rank, (size_t)old * 4, s);
-    tab_free(t, t->uslot, (size_t)old * 4, s);
-      tab_free(t, t->blk_sums, (size_t)(old / kKeyTile + 2) * 8, s);
-    tab_free(t, t->wb_keys, (size_t)old * 8, s);
-    tab_free(t, t->partials, (size_t)plan_layout(old).max_chunks * t->cfg.dim * 8, s);
-  }
+  free_scratch(t, s);
   for (int k = 0; k < recis_table::kRing; ++k) {
     if (t->stage_host[k]) (void)hipHostFree(t->stage_host[k]);
     if (t->stage_dev[k]) tab_free(t, t->stage_dev[k], t->stage_cap[k], s);
@@ -407,14 +449,13 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   std::vector<char> host(sizeof(FeatDev) * (size_t)std::max(num_feats, 1) + 8 * (size_t)nbounds + 16);
   FeatDev* fd = reinterpret_cast<FeatDev*>(host.data());
   long long* pool = reinterpret_cast<long long*>(host.data() + sizeof(FeatDev) * (size_t)std::max(num_feats, 1));
-  long long base = 0, tiles = 0, boff = 0;
+  long long base = 0, boff = 0;
   for (int f = 0; f < num_feats; ++f) {
     const recis_feature_desc& d = feats[f];
     fd[f].values = reinterpret_cast<const long long*>(d.values);
     fd[f].offs = d.bag_offsets;
     fd[f].n = d.n;
     fd[f].base = base;
-    fd[f].tile_base = tiles;
     fd[f].mod = d.mod;
     fd[f].slot = d.slot;
     fd[f].ops = d.ops;
@@ -425,7 +466,6 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
       boff += d.nb;
     }
     base += d.n;
-    tiles += (d.n + kOccTile - 1) / kOccTile;
   }
   void* dev = nullptr;
   st = stage(t, host.data(), host.size(), s, &dev);
@@ -443,16 +483,22 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.F = num_feats;
   L.B = batch;
   L.N = N;
-  L.occ_tiles = tiles;
   L.flags = flags;
   L.res = *res;
   L.dd = t->dd;
-  L.dd_mask = (unsigned long long)(t->dd_cap - 1);
-  L.dd_shift = 64 - log2_exact(t->dd_cap);
-  L.occ_slot = t->occ_slot;
-  L.occ_rank = t->occ_rank;
-  L.uslot = t->uslot;
+  const PartGeom g = part_geom(N);
+  L.nbits = g.nbits;
+  L.nbk = g.nbk;
+  L.part_blocks = g.blocks;
+  L.part_range = g.range;
+  L.big_tab = g.big;
+  L.hist = t->hist;
+  L.bbase = t->bbase;
+  L.ubase = t->ubase;
+  L.part = t->part;
+  L.ovf = t->ovf;
   L.blk_sums = t->blk_sums;
+  L.blk_long = t->blk_sums + (t->scr_cap / kKeyTile + 2);
   L.key_tiles = (N + kKeyTile - 1) / kKeyTile;
   launch_lookup(L, t->dev(), s);
   return check_launch();

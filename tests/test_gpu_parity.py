@@ -241,6 +241,35 @@ def test_one_key_dominates():
     run_parity(spec, [b, b])
 
 
+def _ids_in_first_hash_bucket(count, bits, rng):
+    """Ids (slot 0, no transform: key == id) whose Fibonacci hash has `bits`
+    leading zero bits, i.e. that all land in the first hash bucket of the
+    lookup's partition."""
+    out = []
+    while sum(len(x) for x in out) < count:
+        c = rng.integers(1, 1 << 47, 200000, dtype=np.int64)
+        h = c.astype(np.uint64) * np.uint64(0x9E3779B97F4A7C15)   # wraps mod 2^64
+        out.append(c[(h >> np.uint64(64 - bits)) == 0])
+    return np.unique(np.concatenate(out))[:count]
+
+
+def test_bucket_overflow_path():
+    """2000 distinct keys that collide in the top bits of the partition hash:
+    3000 occurrences make 8 buckets (bits = 3), so all of them land in one
+    bucket and overflow its LDS table; the global-table path must give the
+    same lookup, forward and update as the oracle."""
+    spec = W.TableSpec(dim=16, dtype="f32", optim="adagrad", pool="sum", lr=0.05)
+    rng = W.rng_for(91)
+    ids = _ids_in_first_hash_bucket(2000, 3, rng)
+    vals = np.concatenate([ids, rng.choice(ids, 1000)])
+    rng.shuffle(vals)
+    B = 300
+    off = (np.arange(B + 1) * (vals.size // B)).astype(np.int32)
+    b = W.Batch([W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=0)], B,
+                rng.standard_normal((B, 16), dtype=np.float32))
+    run_parity(spec, [b, b])
+
+
 def test_writeback_cache_last_writer_wins():
     import torch
     from dynamic_embedding_tables_amd import recis
