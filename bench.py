@@ -87,6 +87,169 @@ def cpu_baseline(seconds_budget=20.0):
                       f"{t_total:.1f} s"}
 
 
+# kernels the warm-up steps time, one per step, to pick the dominant one
+CANDIDATE_KERNELS = ("k_bwd_short", "k_fwd_pool", "k_key_probe", "k_bucket_emit", "k_part_scatter")
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch, dev):
+    """Three plain device-to-device copies of COPY_BYTES (reads COPY_BYTES,
+    writes COPY_BYTES each): the reference for scaling FETCH_SIZE/WRITE_SIZE."""
+    x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+
+
+def step_shapes(results, U, resident0):
+    """Per timed step: distinct keys with a row and count <= SHORT_MAX (short)
+    or more (long), how many short ones got their row in that step, and the
+    occurrences of short keys; averaged over the steps."""
+    per = []
+    for r, u in zip(results, U):
+        counts = r.counts[:u].cpu().numpy().astype(np.int64)
+        raw = r.unique_rows[:u].cpu().numpy()
+        per.append((counts, raw >= 0, raw & ((1 << 62) - 1)))
+    # a row allocated in the timed steps is new in the first step that uses it
+    cand = [np.nonzero(h & (rw >= resident0))[0] for (_, h, rw) in per]
+    allrows = np.concatenate([per[k][2][c] for k, c in enumerate(cand)]) if cand else np.zeros(0, np.int64)
+    _, first = np.unique(allrows, return_index=True)
+    is_first = np.zeros(allrows.size, bool)
+    is_first[first] = True
+    out, pos = [], 0
+    for (counts, has, _), c in zip(per, cand):
+        new = np.zeros(counts.size, bool)
+        new[c[is_first[pos:pos + c.size]]] = True
+        pos += c.size
+        short = counts <= SHORT_MAX
+        out.append({"U_s": int((short & has).sum()), "U_s_new": int((short & new).sum()),
+                    "E_s": int(counts[short & has].sum()), "U_l": int((~short & has).sum()),
+                    "E_l": int(counts[~short & has].sum())})
+    return {k: float(np.mean([o[k] for o in out])) for k in out[0]}
+
+
+SHORT_MAX = 64   # occurrences up to which the backward treats a key as short
+
+
+def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D):
+    """Bytes the method must move, per launch / per step (fp32 params s = 4,
+    Adam S = 2 state words per element; P = D s + S D 4 = 768 B per row).
+      k_bwd_short: per short key 16 (count, group offset, row) + its grouped
+        entries 4 each; resident rows read and written 2P, new rows written P;
+        the upstream gradient Bg D 4 once.
+      k_fwd_pool: per occurrence its row reference 8; offsets 4 (Bg + 1);
+        resident rows' params D s; the output Bg D 4.
+      k_key_probe: per distinct key its key and count 12, the IDMap slot 16,
+        its row and slot index 12; per new key the slot written 16.
+      step: insert_find 12 N + 4 (Bg + 1) + 32 U + 16 U_new, forward
+        4 N + 8 U + U_hit D s + Bg D 4, backward 4 N + 8 U + U_hit 2P + U_new P
+        + Bg D 4."""
+    s, S = 4, 2
+    P = D * s + S * D * 4
+    Us, Usn = shape["U_s"], shape["U_s_new"]
+    bwd_short = 16 * Us + 4 * shape["E_s"] + (Us - Usn) * 2 * P + Usn * P + Bg * D * 4
+    fwd = 8 * N + 4 * (Bg + 1) + Uhit * D * s + Bg * D * 4
+    probe = 40 * Um + 16 * Unew
+    ins = 12 * N + 4 * (Bg + 1) + 32 * Um + 16 * Unew
+    fwd_call = 4 * N + 8 * Um + Uhit * D * s + Bg * D * 4
+    bwd_call = 4 * N + 8 * Um + Uhit * 2 * P + Unew * P + Bg * D * 4
+    return {"k_bwd_short": bwd_short, "k_fwd_pool": fwd, "k_key_probe": probe,
+            "step": ins + fwd_call + bwd_call}
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dynamic_embedding_tables_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<kernel>_ctr_counters.txt: FETCH_SIZE / WRITE_SIZE in KiB per
+    dispatch, scaled by the copy-kernel factors), or None when there is none or
+    the kernel sources changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_ctr_counters.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _kernel_label(name):
+    import re
+    m = re.search(r"(k_[a-z_]+)", name)
+    if m:
+        return m.group(1)
+    if "copy" in name:
+        return "copy"
+    return name[:60]
+
+
+def summarize(prof_dir, kernel, command, out_path):
+    """Writes the committed summary of a profiled bench run: per-kernel mean
+    durations (rocprofv3 --kernel-trace --stats, csv) from prof_dir/trace, and
+    for `kernel` the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch, from
+    prof_dir/fetch and prof_dir/write) scaled by the same counters of the
+    plain copies of COPY_BYTES that --copy-calibration runs."""
+    import csv
+    stats = list(csv.DictReader(open(os.path.join(prof_dir, "trace", "p_kernel_stats.csv"))))
+    lines = [f"# rocprofv3 summary: {kernel} on the CTR workload (26 features merged, batch 8192,",
+             "# dim 64 fp32, Hash+Mod, mean pooling, sparse Adam, ~20M resident rows)",
+             f"# command: {command}", f"kernel={kernel}", f"source_hash={kernel_source_hash()}"]
+    dur = {}
+    for r in stats:
+        lab = _kernel_label(r["Name"])
+        dur.setdefault(lab, []).append((float(r["AverageNs"]), int(r["Calls"]), float(r["Percentage"])))
+    for lab, v in sorted(dur.items(), key=lambda kv: -sum(x[2] for x in kv[1])):
+        avg = sum(a * c for a, c, _ in v) / sum(c for _, c, _ in v)
+        lines.append(f"kernel_avg_us[{lab}]={avg / 1e3:.2f}  calls={sum(c for _, c, _ in v)}  "
+                     f"pct={sum(p for *_, p in v):.2f}")
+    lines.append(f"avg_duration_us={sum(a * c for a, c, _ in dur[kernel]) / sum(c for _, c, _ in dur[kernel]) / 1e3:.2f}")
+
+    def counter(sub, cname):
+        rows = list(csv.DictReader(open(os.path.join(prof_dir, sub, "p_counter_collection.csv"))))
+        per = {}
+        for r in rows:
+            if r["Counter_Name"] != cname:
+                continue
+            lab = _kernel_label(r["Kernel_Name"])
+            v = float(r["Counter_Value"])
+            # the calibration copies are the copy dispatches that move COPY_BYTES
+            # (a counter that reads 1/4 or more of it); other copies are small
+            if lab == "copy" and v * 1024 < COPY_BYTES / 4:
+                continue
+            per.setdefault(lab, []).append(v)
+        return per
+    fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
+    cf, cw = fetch.get("copy", [])[-3:], write.get("copy", [])[-3:]
+    kf, kw = fetch.get(kernel, []), write.get(kernel, [])
+    if cf and cw and kf and kw:
+        fs = COPY_BYTES / (np.mean(cf) * 1024.0)
+        ws = COPY_BYTES / (np.mean(cw) * 1024.0)
+        # the timed steps are the last dispatches of the run
+        f_kib, w_kib = float(np.mean(kf[-5:])), float(np.mean(kw[-5:]))
+        lines += [f"copy_bytes={COPY_BYTES}", f"copy_fetch_kib={np.mean(cf):.1f}", f"copy_write_kib={np.mean(cw):.1f}",
+                  f"fetch_scale={fs:.4f}", f"write_scale={ws:.4f}",
+                  f"fetch_kib_per_dispatch={f_kib:.1f}", f"write_kib_per_dispatch={w_kib:.1f}",
+                  f"traffic_bytes_per_launch={f_kib * 1024 * fs + w_kib * 1024 * ws:.0f}"]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,7 +258,18 @@ def main():
     ap.add_argument("--resident", type=int, default=RESIDENT_TARGET)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workers", type=int, default=8)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run plain device copies of known size (for HBM counter scaling)")
+    ap.add_argument("--summarize", metavar="PROF_DIR",
+                    help="write the profiles/ summary of a profiled run (see summarize()) and exit")
+    ap.add_argument("--kernel", default="k_bwd_short")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--out", default=None)
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.kernel, args.command,
+                  args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_ctr_counters.txt"))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
@@ -154,20 +328,39 @@ def main():
     # ---- stage warm-up + timed inputs in HBM
     staged = [upload(batches[j]) for j in range(i, i + Wm + K)]
     timed_res = [recis.LookupResult(cap, F * B) for _ in range(K)]
+    stream = torch.cuda.current_stream()
+
+    def event_pair():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)  # creates the HIP events, so the library can record them
+        b.record(stream)
+        return a, b
+
+    # warm-up; each warm-up step also times one candidate kernel, to find the
+    # dominant one (the kernel with the longest launch)
+    probe_ms = {}
     for w in range(Wm):
         dfs, descs, n, grad = staged[w]
+        name = CANDIDATE_KERNELS[w % len(CANDIDATE_KERNELS)]
+        a, b = event_pair()
+        table.profile_kernel(name, a, b)
         step(dfs, descs, grad, res_pool[w % 2])
+        torch.cuda.synchronize()
+        probe_ms.setdefault(name, []).append(a.elapsed_time(b))
+    table.profile_kernel(None)
+    dom = max(probe_ms, key=lambda k: np.mean(probe_ms[k])) if probe_ms else "k_bwd_short"
     table.check()
     st0 = table.stats()
 
-    stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    kev = [event_pair() for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
         dfs, descs, n, grad = staged[Wm + k]
         res = timed_res[k]
         e = ev[k]
+        table.profile_kernel(dom, *kev[k])
         e[0].record(stream)
         table.insert_find(dfs, B, res, descs=descs)
         e[1].record(stream)
@@ -178,8 +371,12 @@ def main():
         e[3].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    table.profile_kernel(None)
     table.check()
     st1 = table.stats()
+    t_dom = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e-3
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
 
     ids = sum(staged[Wm + k][2] for k in range(K))
     U = [int(r.num_unique.item()) for r in timed_res]
@@ -188,30 +385,21 @@ def main():
     t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
 
-    # Algorithmic bytes of one step, from measured counts, split by call:
-    #   A = 20 N + 4 (Bg + 1) + 48 U + 16 U_new + U_hit (3 D s + 2 S D 4)
-    #       + U_new (D s + S D 4) + 2 Bg D 4
-    # insert_find: IDs 8N, inverse write 4N, offsets 4(Bg+1), per distinct key
-    #   unique-key write 8 + slot probe 16 + row write 8, slot insert 16 per new key;
-    # forward: inverse 4N, row index 8U, params of resident rows, output Bg D 4;
-    # backward: inverse 4N, row index 8U, resident rows read+written (params and
-    #   state), new rows written once, upstream gradient Bg D 4.
+    # Measured shape of each timed step: N, U, and per distinct key its count and
+    # whether its row is new (allocated in this step: no eviction runs here, so a
+    # row >= the resident count before the timed steps that no earlier timed
+    # step used).
     N = ids / K
     Um = float(np.mean(U))
     Unew = new_rows / K
     Uhit = Um - Unew
     Bg = F * B
-    s, S = 4, 2                      # fp32 params, Adam: 2 state words per element
-    row_p, row_s = D * s, S * D * 4
-    ins_bytes = 12 * N + 4 * (Bg + 1) + 32 * Um + 16 * Unew
-    fwd_bytes = 4 * N + 8 * Um + Uhit * row_p + Bg * D * 4
-    bwd_bytes = 4 * N + 8 * Um + Uhit * 2 * (row_p + row_s) + Unew * (row_p + row_s) + Bg * D * 4
-    kernels = {"pool_bwd_update": (bwd_bytes, t_bwd), "lookup_pool_fwd": (fwd_bytes, t_fwd),
-               "idmap_insert_find": (ins_bytes, t_ins)}
-    dom = max(kernels, key=lambda k: kernels[k][1])
-    a_bytes, a_t = kernels[dom]
-    achieved = a_bytes / a_t / 1e9
-    step_bytes = fwd_bytes + bwd_bytes + ins_bytes
+    shape = step_shapes(timed_res, U, int(st0.rows_in_use))
+    alg = algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D)
+    a_bytes = alg[dom] if dom in alg else None
+    achieved = a_bytes / t_dom / 1e9 if a_bytes else None
+    step_bytes = alg["step"]
+    traffic = read_traffic(dom)
 
     result = {
         "metric": "lookup+pool+update IDs/sec and achieved HBM GB/s vs peak, 1xMI355X",
@@ -239,8 +427,12 @@ def main():
                               "pool_bwd_update": t_bwd * 1e3},
         "step_algorithmic_bytes": step_bytes,
         "step_achieved_GBps": step_bytes / (elapsed / K) / 1e9,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dom, "kernel_ms": t_dom * 1e3,
+                     "algorithmic_bytes": a_bytes, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
+                     "traffic": traffic},
+        "warmup_kernel_ms": {k: float(np.mean(v)) for k, v in probe_ms.items()},
+        "backward_key_split": shape,
     }
     if not args.no_cpu_baseline:
         table.close()

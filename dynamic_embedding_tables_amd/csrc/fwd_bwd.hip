@@ -718,10 +718,10 @@ void fwd_dispatch(const FwdArgs& a, int pool, hipStream_t s) {
   constexpr int GPB = 256 / C;
   if (pool == RECIS_POOL_NONE) {
     if (a.N == 0) return;
-    hipLaunchKernelGGL((k_fwd_gather<D, TP>), dim3((unsigned)((a.N + GPB - 1) / GPB)), dim3(256), 0, s, a);
+    RECIS_LAUNCH("k_fwd_gather", (k_fwd_gather<D, TP>), dim3((unsigned)((a.N + GPB - 1) / GPB)), dim3(256), s, a);
   } else {
     if (a.nbags == 0) return;
-    hipLaunchKernelGGL((k_fwd_pool<D, TP>), dim3((unsigned)((a.nbags + GPB - 1) / GPB)), dim3(256), 0, s, a);
+    RECIS_LAUNCH("k_fwd_pool", (k_fwd_pool<D, TP>), dim3((unsigned)((a.nbags + GPB - 1) / GPB)), dim3(256), s, a);
   }
 }
 
@@ -731,13 +731,13 @@ void bwd_dispatch(BwdArgs a, long long n, hipStream_t s) {
   constexpr int KL = NCH < kBwdLanes ? NCH : kBwdLanes;
   long long lb = (n / kChunk + 4) / 4;
   lb = lb > 2048 ? 2048 : (lb < 1 ? 1 : lb);
-  hipLaunchKernelGGL((k_bwd_long_partial<D, TP>), dim3((unsigned)lb), dim3(256), 0, s, a);
+  RECIS_LAUNCH("k_bwd_long_partial", (k_bwd_long_partial<D, TP>), dim3((unsigned)lb), dim3(256), s, a);
   long long fb = (n / kShortMax + 4) / 4;  // long keys <= n / (kShortMax + 1)
   fb = fb > 1024 ? 1024 : (fb < 1 ? 1 : fb);
-  hipLaunchKernelGGL((k_bwd_long_final<D, TP, OPT>), dim3((unsigned)fb), dim3(256), 0, s, a);
+  RECIS_LAUNCH("k_bwd_long_final", (k_bwd_long_final<D, TP, OPT>), dim3((unsigned)fb), dim3(256), s, a);
   long long sb = (n + kBwdKeys - 1) / kBwdKeys;
   sb = sb > 4096 ? 4096 : (sb < 1 ? 1 : sb);
-  hipLaunchKernelGGL((k_bwd_short<D, TP, OPT, KL, kBwdKeysPerGroup>), dim3((unsigned)sb), dim3(256), 0, s, a);
+  RECIS_LAUNCH("k_bwd_short", (k_bwd_short<D, TP, OPT, KL, kBwdKeysPerGroup>), dim3((unsigned)sb), dim3(256), s, a);
 }
 
 template <typename TP, int OPT>

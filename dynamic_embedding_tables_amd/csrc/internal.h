@@ -223,6 +223,25 @@ __device__ __forceinline__ uint4 init_chunk(const TableDev& t, long long key, in
   return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
 }
 
+// Instrumentation: launches of the kernel named `name` are bracketed by the
+// two events (see recis_profile_kernel).  The table's probe is made current
+// for the duration of each of its calls.
+struct KernelProbe {
+  char name[64] = {};
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local const KernelProbe* tl_probe;
+inline bool probe_on(const char* name) {
+  return tl_probe && tl_probe->start && __builtin_strcmp(tl_probe->name, name) == 0;
+}
+#define RECIS_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...)                 \
+  do {                                                                       \
+    const bool probe_ = probe_on(NAME);                                      \
+    if (probe_) (void)hipEventRecord(tl_probe->start, STREAM);               \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);         \
+    if (probe_) (void)hipEventRecord(tl_probe->stop, STREAM);                \
+  } while (0)
+
 }  // namespace recis
 
 struct recis_table {
@@ -252,6 +271,8 @@ struct recis_table {
   // bumped by every call that writes rows or frees them (update, writeback,
   // eviction); a lookup result records the value it was made at
   unsigned long long update_epoch = 1;
+
+  recis::KernelProbe probe;
 
   // per-step scratch, sized for scr_cap occurrences
   long long scr_cap = 0;

@@ -791,33 +791,33 @@ __global__ __launch_bounds__(kThreads) void k_occref(LookupLaunch L) {
 
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
   const long long nb = (long long)L.F * L.B + 1;
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+  RECIS_LAUNCH("k_prep", k_prep, dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), s,
                      L, t);
   if (L.N > 0) {
     const unsigned G = (unsigned)L.part_blocks;
-    hipLaunchKernelGGL(k_part_hist, dim3(G), dim3(kPartThreads), 0, s, L, t);
-    hipLaunchKernelGGL(k_part_colscan, dim3((unsigned)((L.nbk + 63) / 64)), dim3(kPartThreads), 0, s, L);
-    hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kPartThreads), 0, s, L.bbase, L.nbk, (long long*)nullptr);
-    hipLaunchKernelGGL(k_part_scatter, dim3(G), dim3(kPartThreads), 0, s, L);
+    RECIS_LAUNCH("k_part_hist", k_part_hist, dim3(G), dim3(kPartThreads), s, L, t);
+    RECIS_LAUNCH("k_part_colscan", k_part_colscan, dim3((unsigned)((L.nbk + 63) / 64)), dim3(kPartThreads), s, L);
+    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.bbase, L.nbk, (long long*)nullptr);
+    RECIS_LAUNCH("k_part_scatter", k_part_scatter, dim3(G), dim3(kPartThreads), s, L);
     const dim3 nb_grid((unsigned)L.nbk);
     if (L.big_tab)
-      hipLaunchKernelGGL((k_bucket<2048, false>), nb_grid, dim3(kThreads), 0, s, L);
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), nb_grid, dim3(kThreads), s, L);
     else
-      hipLaunchKernelGGL((k_bucket<1024, false>), nb_grid, dim3(kThreads), 0, s, L);
-    hipLaunchKernelGGL(k_bucket_big<false>, dim3(64), dim3(kThreads), 0, s, L);
-    hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kPartThreads), 0, s, L.ubase, L.nbk,
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), nb_grid, dim3(kThreads), s, L);
+    RECIS_LAUNCH("k_bucket_big_count", k_bucket_big<false>, dim3(64), dim3(kThreads), s, L);
+    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.ubase, L.nbk,
                        reinterpret_cast<long long*>(L.res.num_unique));
     if (L.big_tab)
-      hipLaunchKernelGGL((k_bucket<2048, true>), nb_grid, dim3(kThreads), 0, s, L);
+      RECIS_LAUNCH("k_bucket_emit", (k_bucket<2048, true>), nb_grid, dim3(kThreads), s, L);
     else
-      hipLaunchKernelGGL((k_bucket<1024, true>), nb_grid, dim3(kThreads), 0, s, L);
-    hipLaunchKernelGGL(k_bucket_big<true>, dim3(64), dim3(kThreads), 0, s, L);
-    hipLaunchKernelGGL(k_key_probe, dim3((unsigned)L.key_tiles), dim3(kThreads), 0, s, L, t);
+      RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true>), nb_grid, dim3(kThreads), s, L);
+    RECIS_LAUNCH("k_bucket_big_emit", k_bucket_big<true>, dim3(64), dim3(kThreads), s, L);
+    RECIS_LAUNCH("k_key_probe", k_key_probe, dim3((unsigned)L.key_tiles), dim3(kThreads), s, L, t);
   }
-  hipLaunchKernelGGL(k_key_scan, dim3(1), dim3(kScanThreads), 0, s, L, t);
+  RECIS_LAUNCH("k_key_scan", k_key_scan, dim3(1), dim3(kScanThreads), s, L, t);
   if (L.N > 0) {
-    hipLaunchKernelGGL(k_key_finalize, dim3((unsigned)L.key_tiles), dim3(kThreads), 0, s, L, t);
-    hipLaunchKernelGGL(k_occref, dim3((unsigned)((L.N + kOccTile - 1) / kOccTile)), dim3(kThreads), 0, s, L);
+    RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.key_tiles), dim3(kThreads), s, L, t);
+    RECIS_LAUNCH("k_occref", k_occref, dim3((unsigned)((L.N + kOccTile - 1) / kOccTile)), dim3(kThreads), s, L);
   }
 }
 

@@ -16,7 +16,18 @@
 
 using namespace recis;
 
+namespace recis {
+thread_local const KernelProbe* tl_probe = nullptr;
+}
+
 namespace {
+
+// Makes a table's kernel probe current for one call.
+struct ScopedProbe {
+  const KernelProbe* prev;
+  explicit ScopedProbe(const recis_table* t) : prev(tl_probe) { tl_probe = &t->probe; }
+  ~ScopedProbe() { tl_probe = prev; }
+};
 
 struct ScopedDevice {
   int prev = -1;
@@ -390,6 +401,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
 recis_status recis_idmap_destroy(recis_table* t) {
   if (!t) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   hipStream_t s = nullptr;
   (void)hipDeviceSynchronize();
   for (char* b : t->blocks) tab_free(t, b, (size_t)(t->cfg.block_rows * t->row_bytes), s);
@@ -437,6 +449,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   if (N > 0 && (!res->unique_keys || !res->unique_rows || !res->inverse || !res->counts || !res->grouped))
     return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
 
   recis_status st = ensure_scratch(t, N, s);
   if (st != RECIS_OK) return st;
@@ -507,6 +520,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
 recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted, hipStream_t s) {
   if (!t) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   t->update_epoch += 1;
   launch_evict(t->dev(), min_count, reinterpret_cast<long long*>(num_evicted), s);
   recis_status st = check_launch();
@@ -529,6 +543,7 @@ recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_resu
   if (outn > 0 && !out) return RECIS_ERR_INVALID_ARG;
   if (res->n > res->capacity || res->n < 0) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   launch_forward(*res, t->dev(), pool, out, res->epoch == t->update_epoch, s);
   return check_launch();
 }
@@ -545,6 +560,7 @@ recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* re
   if (t->cfg.optim == RECIS_OPTIM_NONE) return RECIS_ERR_UNSUPPORTED;
   if (!(opt->lr >= 0.0) || !(opt->eps >= 0.0)) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   OptConsts oc;
   oc.lr = (float)opt->lr;
   oc.eps = (float)opt->eps;
@@ -574,6 +590,7 @@ recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* re
 recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, const float* rows, hipStream_t s) {
   if (!t || n < 0 || (n > 0 && (!keys || !rows)) || n > (1ll << 30)) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   recis_status st = ensure_scratch(t, n, s);
   if (st != RECIS_OK) return st;
   st = ensure_capacity(t, n, s);
@@ -590,6 +607,7 @@ recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int6
   if (cap > 0 && (!keys || !rows || !counts || !params)) return RECIS_ERR_INVALID_ARG;
   if (cap > 0 && t->state_words > 0 && !state) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   launch_export(t->dev(), cap, reinterpret_cast<long long*>(keys), reinterpret_cast<long long*>(rows), counts, s);
   recis_status st = check_launch();
   if (st != RECIS_OK) return st;
@@ -609,6 +627,7 @@ recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int6
 recis_status recis_idmap_stats(recis_table* t, recis_table_stats* out, hipStream_t s) {
   if (!t || !out) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   DevCounters c;
   recis_status st = read_counters(t, &c, s);
   if (st != RECIS_OK) return st;
@@ -625,6 +644,7 @@ recis_status recis_idmap_stats(recis_table* t, recis_table_stats* out, hipStream
 recis_status recis_get_error(recis_table* t, hipStream_t s) {
   if (!t) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
   HIP_TRY(hipStreamSynchronize(s));
   unsigned err = 0;
   HIP_TRY(hipMemcpy(&err, &t->ctr->error, sizeof(err), hipMemcpyDeviceToHost));
@@ -635,6 +655,20 @@ recis_status recis_get_error(recis_table* t, hipStream_t s) {
   if (err & kErrCapacity) return RECIS_ERR_CAPACITY;
   if (err & kErrKeyRange) return RECIS_ERR_KEY_RANGE;
   if (err & kErrInvalid) return RECIS_ERR_INVALID_ARG;
+  return RECIS_OK;
+}
+
+recis_status recis_profile_kernel(recis_table* t, const char* kernel, hipEvent_t start, hipEvent_t stop) {
+  if (!t) return RECIS_ERR_INVALID_ARG;
+  if (!kernel) {
+    t->probe = KernelProbe();
+    return RECIS_OK;
+  }
+  if (!start || !stop || std::strlen(kernel) >= sizeof(t->probe.name)) return RECIS_ERR_INVALID_ARG;
+  std::memset(t->probe.name, 0, sizeof(t->probe.name));
+  std::memcpy(t->probe.name, kernel, std::strlen(kernel));
+  t->probe.start = start;
+  t->probe.stop = stop;
   return RECIS_OK;
 }
 

@@ -48,7 +48,7 @@ EXPORTED_SYMBOLS = (
     "recis_table_config_default", "recis_plan_words", "recis_idmap_create", "recis_idmap_destroy",
     "recis_idmap_insert_find", "recis_idmap_evict", "recis_lookup_pool_fwd", "recis_pool_bwd_update",
     "recis_writeback", "recis_idmap_export", "recis_idmap_stats", "recis_get_error",
-    "recis_status_string",
+    "recis_status_string", "recis_profile_kernel",
 )
 
 
@@ -121,6 +121,7 @@ def load_library() -> C.CDLL:
     L.recis_idmap_export.argtypes = [p, i64, p, p, p, p, p, C.POINTER(i64), p]
     L.recis_idmap_stats.argtypes = [p, C.POINTER(recis_table_stats), p]
     L.recis_get_error.argtypes = [p, p]
+    L.recis_profile_kernel.argtypes = [p, C.c_char_p, p, p]
     L.recis_status_string.argtypes = [i32]
     L.recis_status_string.restype = C.c_char_p
     for name in ("recis_idmap_create", "recis_idmap_destroy", "recis_idmap_insert_find",
@@ -192,6 +193,15 @@ def recis_pool_bwd_update(h, res: recis_lookup_result, pool: int, grad, grad_dty
                           opt: recis_optim_params, stream=None):
     _check(load_library().recis_pool_bwd_update(h, C.byref(res), pool, _ptr(grad), grad_dtype,
                                                 C.byref(opt), _stream(stream)), "recis_pool_bwd_update")
+
+
+def recis_profile_kernel(h, kernel: Optional[str], start=None, stop=None):
+    """Bracket launches of library kernel `kernel` with two torch.cuda.Event
+    objects (already recorded once, so their HIP events exist); None clears."""
+    name = None if kernel is None else kernel.encode()
+    a = None if start is None else C.c_void_p(start.cuda_event)
+    b = None if stop is None else C.c_void_p(stop.cuda_event)
+    _check(load_library().recis_profile_kernel(h, name, a, b), "recis_profile_kernel")
 
 
 def recis_writeback(h, keys, n: int, rows, stream=None):
@@ -324,6 +334,9 @@ class Table:
 
     def stats(self, stream=None) -> recis_table_stats:
         return recis_idmap_stats(self.h, stream)
+
+    def profile_kernel(self, kernel, start=None, stop=None):
+        recis_profile_kernel(self.h, kernel, start, stop)
 
     def get_error(self, stream=None) -> int:
         return recis_get_error(self.h, stream)

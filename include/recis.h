@@ -241,6 +241,16 @@ recis_status recis_get_error(recis_table* t, hipStream_t s);
 
 const char* recis_status_string(recis_status st);
 
+/* Instrumentation (not part of the method): while set, every launch of the
+ * library kernel named `kernel` (e.g. "k_bwd_short", "k_fwd_pool",
+ * "k_bucket_emit") made by a call on `t` is bracketed by
+ * hipEventRecord(start) / hipEventRecord(stop) on the call's stream, so
+ * hipEventElapsedTime(start, stop) is that launch's duration (the last one,
+ * when a call launches it twice).  The events are the caller's and must stay
+ * valid while set; kernel == NULL clears.  The name is copied.  Errors:
+ * INVALID_ARG for a NULL table, or a name with NULL events. */
+recis_status recis_profile_kernel(recis_table* t, const char* kernel, hipEvent_t start, hipEvent_t stop);
+
 #ifdef __cplusplus
 }
 #endif
