@@ -92,6 +92,32 @@ def test_multi_table_config_scaled_with_eviction(table):
     run_parity(spec, batches, evict_every=2)
 
 
+# ---- full sizes: the bench's workload and table configuration, and the
+# largest per-table shape of the multi-table config (which takes the lookup's
+# large-bucket path)
+@pytest.mark.timeout(900)
+def test_ctr_full_size_bench_configuration():
+    """Two full CTR steps (8192 x 26 features, 2.2M IDs each) on a table laid
+    out as the benchmark's (2^27 IDMap slots, 2^20-row blocks)."""
+    run_parity(W.spec_ctr(), [W.ctr_batch(s) for s in range(2)],
+               table_kw=dict(slot_capacity=1 << 27, block_rows=1 << 20, reserve_rows=1 << 22))
+
+
+@pytest.mark.timeout(900)
+def test_sequence_full_size():
+    """Two full sequence steps (2048 x 1000 positions, bf16 gather + Adagrad)."""
+    run_parity(W.spec_seq(), [W.seq_batch(s) for s in range(2)])
+
+
+@pytest.mark.timeout(900)
+def test_multi_table_full_size_with_eviction():
+    """One merged table of the multi-table config at full size (32768 x 60
+    features, 7.9M IDs per step, admission threshold 2), with an eviction
+    pass after the second step."""
+    spec = W.spec_multi(0)
+    run_parity(spec, [W.multi_batch(s, 0) for s in range(3)], evict_every=2, export_every=2)
+
+
 def test_growth_of_idmap_and_blocks():
     spec = W.spec_ctr()
     run_parity(spec, [W.ctr_batch(s, batch=64, num_feats=8) for s in range(3)],
