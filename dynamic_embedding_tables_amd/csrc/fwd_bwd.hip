@@ -144,40 +144,44 @@ struct FwdArgs {
   TableDev t;
 };
 
-// Row of occurrence j, as resolve_row encodes it.  While the lookup is
-// current its per-occurrence reference is used directly (one load);
-// otherwise the distinct key's row and the IDMap slot are read.
-__device__ __forceinline__ long long occurrence_row(const FwdArgs& a, long long j, long long& key) {
-  if (a.current) {
-    const long long v = a.occref[j];
-    if (v == kOccNoRow) return -1;
-    if (v < 0) {
-      key = (long long)((unsigned long long)v & ~kOccPendingBit);
-      return -2;
-    }
-    return v;
-  }
-  return resolve_row(a.t, a.urows, a.ukeys, a.idslot, a.inverse[j], key);
+// Reference to the values of occurrence j: the device address of its row
+// (>= 0), kOccNoRow (zeros), or kOccPendingBit | key for a row that still
+// holds its initial values.  While the lookup is current this is the
+// occurrence's reference written by insert_find (one load); otherwise the
+// distinct key's row and IDMap slot are read.
+__device__ __forceinline__ long long occurrence_ref(const FwdArgs& a, long long j) {
+  if (a.current) return a.occref[j];
+  long long key = 0;
+  const long long r = resolve_row(a.t, a.urows, a.ukeys, a.idslot, a.inverse[j], key);
+  if (r == -1) return kOccNoRow;
+  if (r == -2) return (long long)(kOccPendingBit | (unsigned long long)key);
+  return (long long)row_ptr(a.t.rs, r);
 }
 
 template <typename TP, int E>
-__device__ __forceinline__ void fetch_values(const TableDev& t, long long r, long long key, int lane,
-                                             float (&v)[E]) {
-  if (r >= 0) {
-    Vec<TP>::load(row_ptr(t.rs, r) + lane * 16, v);
-  } else if (r == -2) {
-    Vec<TP>::unpack(init_chunk(t, key, lane), v);
-  } else {
+__device__ __forceinline__ void fetch_values(const TableDev& t, long long ref, int lane, float (&v)[E]) {
+  if (ref == kOccNoRow) {
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] = 0.f;
+  } else if (ref >= 0) {
+    Vec<TP>::load(reinterpret_cast<const char*>(ref) + lane * 16, v);
+  } else {
+    Vec<TP>::unpack(init_chunk(t, (long long)((unsigned long long)ref & ~kOccPendingBit), lane), v);
   }
 }
+
+// Pooling: a group of C = D / E lanes per bag.  The group reads the
+// references of up to C occurrences at once (one per lane), then broadcasts
+// them kFwdBatch at a time and keeps those rows' loads in flight together;
+// the sum runs in occurrence order.
+constexpr int kFwdBatch = 4;
 
 template <int D, typename TP>
 __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
   constexpr int E = Vec<TP>::E;
   constexpr int C = D / E;  // lanes per bag
   constexpr int GPB = 256 / C;
+  constexpr int BF = kFwdBatch < C ? kFwdBatch : C;
   const int wl = threadIdx.x & 63;
   const int lane = wl % C, gbase = wl - lane;
   const long long bag = (long long)blockIdx.x * GPB + threadIdx.x / C;
@@ -190,29 +194,20 @@ __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (long long base = lo; base < hi; base += C) {
     const int cnt = (int)(hi - base < C ? hi - base : C);
-    long long enc = -1, key = 0;
-    if (lane < cnt) enc = occurrence_row(a, base + lane, key);
-    int q = 0;
-    for (; q + 4 <= cnt; q += 4) {
-      float v[4][E];
+    const long long ref = lane < cnt ? occurrence_ref(a, base + lane) : kOccNoRow;
+    // the group's lanes run the same trip counts, so every shuffle source
+    // (a lane of the same group) is active
+    for (int q = 0; q < cnt; q += BF) {
+      float v[BF][E];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const long long r = shfl64(enc, gbase + q + x);
-        const long long k = r == -2 ? shfl64(key, gbase + q + x) : 0;
-        fetch_values<TP, E>(a.t, r, k, lane, v[x]);
+      for (int x = 0; x < BF; ++x) {
+        const long long r = shfl64(ref, gbase + (q + x < cnt ? q + x : 0));
+        fetch_values<TP, E>(a.t, q + x < cnt ? r : kOccNoRow, lane, v[x]);
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < BF; ++x)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] += v[x][e];
-    }
-    for (; q < cnt; ++q) {
-      float v[E];
-      const long long r = shfl64(enc, gbase + q);
-      const long long k = r == -2 ? shfl64(key, gbase + q) : 0;
-      fetch_values<TP, E>(a.t, r, k, lane, v);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += v[e];
     }
   }
   if (a.pool == RECIS_POOL_MEAN && hi > lo) {
@@ -235,11 +230,14 @@ __global__ __launch_bounds__(256) void k_fwd_gather(FwdArgs a) {
   const int lane = threadIdx.x % C;
   const long long j = (long long)blockIdx.x * GPB + threadIdx.x / C;
   if (j >= a.N) return;
-  long long key = 0;
-  const long long r = occurrence_row(a, j, key);
+  const long long r = occurrence_ref(a, j);
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (r >= 0) v = *reinterpret_cast<const uint4*>(row_ptr(a.t.rs, r) + lane * 16);
-  else if (r == -2) v = init_chunk(a.t, key, lane);
+  if (r == kOccNoRow) {
+  } else if (r >= 0) {
+    v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(r) + lane * 16);
+  } else {
+    v = init_chunk(a.t, (long long)((unsigned long long)r & ~kOccPendingBit), lane);
+  }
   reinterpret_cast<uint4*>(static_cast<char*>(a.out) + (j * D * (long long)sizeof(TP)))[lane] = v;
 }
 
@@ -273,10 +271,6 @@ constexpr int kBwdLanes = RECIS_BWD_LANES;  // lanes per key in the short path (
 #define RECIS_BWD_BATCH 8
 #endif
 constexpr int kBwdBatchElems = RECIS_BWD_BATCH;  // gradient elements per lane in flight (short path)
-#ifndef RECIS_BWD_P
-#define RECIS_BWD_P 1
-#endif
-constexpr int kBwdKeysPerGroup = RECIS_BWD_P;  // keys a group of the short path works on together
 
 // Upstream-gradient row of grouped entry gval (a bag, or an occurrence for
 // POOL_NONE) and the scale it enters with (1 / bag length for mean pooling).
@@ -539,15 +533,58 @@ __global__ __launch_bounds__(256) void k_bwd_long_final(BwdArgs a) {
   }
 }
 
+// One key of the short path in flight: its LDS metadata, row state (loaded or
+// initial) and its first GB gradient rows.
+template <int D, typename TP, int KL, int GB>
+struct KeyStage {
+  static constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
+  int k = -1, c = 0, st = 0, base = 0;
+  char* prow = nullptr;
+  float w[CH][E], s0[CH][E], s1[CH][E];
+  float g[GB][CH][E];
+};
+
+template <int D, typename TP, int OPT, int KL, int GB>
+__device__ __forceinline__ void stage_key(const BwdArgs& a, int q, int nact, int lane, const unsigned char* s_perm,
+                                          const int* s_c, const unsigned char* s_st, const int* s_eo,
+                                          char* const* s_ptr, const long long* s_key, const int* s_grow,
+                                          KeyStage<D, TP, KL, GB>& S) {
+  constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
+  S.k = q < nact ? (int)s_perm[q] : -1;
+  if (S.k < 0) {
+    S.c = 0;
+    return;
+  }
+  S.c = s_c[S.k];
+  S.st = s_st[S.k];
+  S.base = s_eo[S.k];
+  S.prow = s_ptr[S.k];
+  load_row<D, TP, OPT, KL>(a, S.prow, S.st == 2, s_key[S.k], lane, S.w, S.s0, S.s1);
+#pragma unroll
+  for (int i = 0; i < GB; ++i) {
+    const bool in = i < S.c;
+    const int gr = in ? s_grow[S.base + i] : 0;
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+      if (in) {
+        load_grad<E>(a.grad, (long long)gr * D + (ch * KL + lane) * E, a.gdt, S.g[i][ch]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) S.g[i][ch][e] = 0.f;
+      }
+    }
+  }
+}
+
 // Short keys (<= kShortMax entries).  A block takes kBwdKeys consecutive keys.
 // Phase 1, one thread per key: metadata and the row's address (the block
 // table is read here once, not per update), and one packed block scan that
 // gives each key its staged-entry base and its place in an order with the
 // pending rows first, so the groups of a wave mostly agree on whether to run
 // the initializer.  Phase 2: the keys' gradient references, staged in LDS
-// when they fit.  Phase 3: each group of KL lanes takes P keys at a time,
-// issues the row and gradient loads of all of them, then updates and stores.
-template <int D, typename TP, int OPT, int KL, int P>
+// when they fit.  Phase 3: each group of KL lanes walks its keys, with the
+// next key's loads issued before the current key's update and stores.
+template <int D, typename TP, int OPT, int KL>
 __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
   constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
   constexpr int GPB = 256 / KL;
@@ -626,85 +663,90 @@ __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
       __syncthreads();
     }
     const int nact = s_nact;
-    for (int q0 = tid / KL; q0 < nact; q0 += GPB * P) {
-      int kk[P], kc[P], kst[P];
-      char* prow[P];
-      float w[P][CH][E], s0[P][CH][E], s1[P][CH][E];
-      double acc[P][CH][E];
-#pragma unroll
-      for (int j = 0; j < P; ++j) {
-        const int q = q0 + j * GPB;
-        kk[j] = q < nact ? s_perm[q] : -1;
-        kc[j] = kk[j] >= 0 ? s_c[kk[j]] : 0;
-        kst[j] = kk[j] >= 0 ? s_st[kk[j]] : 0;
-        prow[j] = kk[j] >= 0 ? s_ptr[kk[j]] : nullptr;
-        if (kk[j] >= 0) load_row<D, TP, OPT, KL>(a, prow[j], kst[j] == 2, s_key[kk[j]], lane, w[j], s0[j], s1[j]);
+    if (staged) {
+      // Software-pipelined over the group's keys: the loads of the next key
+      // (row, first GB gradient rows) are issued before the current key's
+      // update and stores.  The vector-memory counter retires in issue order,
+      // so waiting for those loads then does not wait for the stores too.
+      KeyStage<D, TP, KL, GB> cur, nxt;
+      int q = tid / KL;
+      stage_key<D, TP, OPT, KL, GB>(a, q, nact, lane, s_perm, s_c, s_st, s_eo, s_ptr, s_key, s_grow, cur);
+      while (q < nact) {
+        stage_key<D, TP, OPT, KL, GB>(a, q + GPB, nact, lane, s_perm, s_c, s_st, s_eo, s_ptr, s_key, s_grow, nxt);
+        double acc[CH][E];
 #pragma unroll
         for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[j][ch][e] = 0.0;
-      }
-      if (staged) {
-        int kmax = 0;
+          for (int e = 0; e < E; ++e) acc[ch][e] = 0.0;
 #pragma unroll
-        for (int j = 0; j < P; ++j) kmax = kc[j] > kmax ? kc[j] : kmax;
-        // GB gradient rows of each of the P keys in flight together
-        for (int x0 = 0; x0 < kmax; x0 += GB) {
-          float gv[P][GB][CH][E];
+        for (int i = 0; i < GB; ++i) {
+          const double sc = i < cur.c ? s_sc[cur.base + i] : 0.0;
 #pragma unroll
-          for (int j = 0; j < P; ++j) {
-            const int base = kk[j] >= 0 ? s_eo[kk[j]] : 0;
+          for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
-            for (int i = 0; i < GB; ++i) {
-              const bool in = x0 + i < kc[j];
-              const int gr = in ? s_grow[base + x0 + i] : 0;
+            for (int e = 0; e < E; ++e) acc[ch][e] += (double)cur.g[i][ch][e] * sc;
+        }
+        for (int x0 = GB; x0 < cur.c; x0 += GB) {  // keys with more than GB entries
+          float gv[GB][CH][E];
 #pragma unroll
-              for (int ch = 0; ch < CH; ++ch) {
-                if (in) {
-                  load_grad<E>(a.grad, (long long)gr * D + (ch * KL + lane) * E, a.gdt, gv[j][i][ch]);
-                } else {
+          for (int i = 0; i < GB; ++i) {
+            const bool in = x0 + i < cur.c;
+            const int gr = in ? s_grow[cur.base + x0 + i] : 0;
 #pragma unroll
-                  for (int e = 0; e < E; ++e) gv[j][i][ch][e] = 0.f;
-                }
+            for (int ch = 0; ch < CH; ++ch) {
+              if (in) {
+                load_grad<E>(a.grad, (long long)gr * D + (ch * KL + lane) * E, a.gdt, gv[i][ch]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) gv[i][ch][e] = 0.f;
               }
             }
           }
 #pragma unroll
-          for (int j = 0; j < P; ++j) {
-            const int base = kk[j] >= 0 ? s_eo[kk[j]] : 0;
+          for (int i = 0; i < GB; ++i) {
+            const double sc = x0 + i < cur.c ? s_sc[cur.base + x0 + i] : 0.0;
 #pragma unroll
-            for (int i = 0; i < GB; ++i) {
-              const double sc = x0 + i < kc[j] ? s_sc[base + x0 + i] : 0.0;
+            for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
-              for (int ch = 0; ch < CH; ++ch)
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[j][ch][e] += (double)gv[j][i][ch][e] * sc;
-            }
+              for (int e = 0; e < E; ++e) acc[ch][e] += (double)gv[i][ch][e] * sc;
           }
         }
-      } else {
-        // entries straight from global memory, KL at a time (one per lane)
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-          const int ko = kk[j] >= 0 ? s_o[kk[j]] : 0;
-          for (int b0 = 0; b0 < kc[j]; b0 += KL) {
-            const int cnt = kc[j] - b0 < KL ? kc[j] - b0 : KL;
-            int gr = 0;
-            double scale = 0.0;
-            if (lane < cnt) grad_ref<D>(a, a.grouped[ko + b0 + lane], gr, scale);
-            for (int x = 0; x < cnt; ++x)
-              add_grad_row<D, TP, KL>(a, __shfl(gr, gbase + x), shfl_d(scale, gbase + x), lane, acc[j]);
-          }
+        update_store<D, TP, OPT, KL>(a, cur.prow, lane, acc, cur.w, cur.s0, cur.s1);
+        if (lane == 0 && cur.st != 0) {
+          const int row = s_r[cur.k];
+          if (cur.st == 2) a.t.slots[s_sl[cur.k]].row = row;
+          a.urows[t0 + cur.k] = row;
         }
+        cur = nxt;
+        q += GPB;
       }
+    } else {
+      // more entries than the stage holds: one key at a time, the entries
+      // straight from global memory, KL at a time (one per lane)
+      for (int q = tid / KL; q < nact; q += GPB) {
+        const int k = s_perm[q], c = s_c[k], st = s_st[k];
+        char* prow = s_ptr[k];
+        float w[CH][E], s0[CH][E], s1[CH][E];
+        load_row<D, TP, OPT, KL>(a, prow, st == 2, s_key[k], lane, w, s0, s1);
+        double acc[CH][E];
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        if (kk[j] < 0) continue;
-        update_store<D, TP, OPT, KL>(a, prow[j], lane, acc[j], w[j], s0[j], s1[j]);
-        if (lane == 0 && kst[j] != 0) {
-          const int row = s_r[kk[j]];
-          if (kst[j] == 2) a.t.slots[s_sl[kk[j]]].row = row;
-          a.urows[t0 + kk[j]] = row;
+        for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[ch][e] = 0.0;
+        const int ko = s_o[k];
+        for (int b0 = 0; b0 < c; b0 += KL) {
+          const int cnt = c - b0 < KL ? c - b0 : KL;
+          int gr = 0;
+          double scale = 0.0;
+          if (lane < cnt) grad_ref<D>(a, a.grouped[ko + b0 + lane], gr, scale);
+          for (int x = 0; x < cnt; ++x)
+            add_grad_row<D, TP, KL>(a, __shfl(gr, gbase + x), shfl_d(scale, gbase + x), lane, acc);
+        }
+        update_store<D, TP, OPT, KL>(a, prow, lane, acc, w, s0, s1);
+        if (lane == 0 && st != 0) {
+          const int row = s_r[k];
+          if (st == 2) a.t.slots[s_sl[k]].row = row;
+          a.urows[t0 + k] = row;
         }
       }
     }
@@ -737,7 +779,7 @@ void bwd_dispatch(BwdArgs a, long long n, hipStream_t s) {
   RECIS_LAUNCH("k_bwd_long_final", (k_bwd_long_final<D, TP, OPT>), dim3((unsigned)fb), dim3(256), s, a);
   long long sb = (n + kBwdKeys - 1) / kBwdKeys;
   sb = sb > 4096 ? 4096 : (sb < 1 ? 1 : sb);
-  RECIS_LAUNCH("k_bwd_short", (k_bwd_short<D, TP, OPT, KL, kBwdKeysPerGroup>), dim3((unsigned)sb), dim3(256), s, a);
+  RECIS_LAUNCH("k_bwd_short", (k_bwd_short<D, TP, OPT, KL>), dim3((unsigned)sb), dim3(256), s, a);
 }
 
 template <typename TP, int OPT>

@@ -117,8 +117,9 @@ __host__ __device__ inline PlanLayout plan_layout(long long cap) {
   return p;
 }
 
-// Per-occurrence row reference written by insert_find for the forward:
-// a row offset (>= 0), kOccNoRow, or kOccPendingBit | key for a row that was
+// Per-occurrence row reference written by insert_find for the forward: the
+// row's device address (>= 0; blocks never move, so it stays valid while
+// the table lives), kOccNoRow, or kOccPendingBit | key for a row that was
 // pending at the lookup (its values are the initializer's of `key`).
 constexpr long long kOccNoRow = 1ll << 62;
 constexpr unsigned long long kOccPendingBit = 1ull << 63;

@@ -763,9 +763,9 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
 }
 
 // ------------------------------------------------------------- k_occref
-// Per occurrence: the row reference the forward reads while the lookup is
-// current (a row, the pending key, or no row).
-__global__ __launch_bounds__(kThreads) void k_occref(LookupLaunch L) {
+// Per occurrence: the reference the forward reads while the lookup is
+// current -- the row's device address, the pending key, or no row.
+__global__ __launch_bounds__(kThreads) void k_occref(LookupLaunch L, TableDev t) {
   long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
   const long long j0 = (long long)blockIdx.x * kOccTile + threadIdx.x;
   int u[kOccPerThread];
@@ -783,6 +783,7 @@ __global__ __launch_bounds__(kThreads) void k_occref(LookupLaunch L) {
     long long v = r[k];
     if (v < 0) v = kOccNoRow;
     else if (v & kFreshRow) v = (long long)(kOccPendingBit | (unsigned long long)L.res.unique_keys[u[k]]);
+    else v = (long long)row_ptr(t.rs, v);
     occref[j0 + (long long)k * kThreads] = v;
   }
 }
@@ -817,7 +818,7 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
   RECIS_LAUNCH("k_key_scan", k_key_scan, dim3(1), dim3(kScanThreads), s, L, t);
   if (L.N > 0) {
     RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.key_tiles), dim3(kThreads), s, L, t);
-    RECIS_LAUNCH("k_occref", k_occref, dim3((unsigned)((L.N + kOccTile - 1) / kOccTile)), dim3(kThreads), s, L);
+    RECIS_LAUNCH("k_occref", k_occref, dim3((unsigned)((L.N + kOccTile - 1) / kOccTile)), dim3(kThreads), s, L, t);
   }
 }
 
