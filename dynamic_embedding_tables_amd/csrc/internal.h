@@ -283,7 +283,6 @@ struct recis_table {
   int* hist = nullptr;
   int* bbase = nullptr;
   int* ubase = nullptr;
-  int* ovf = nullptr;
   int* uslot = nullptr;
   unsigned long long* blk_sums = nullptr;
   long long* wb_keys = nullptr;
@@ -334,7 +333,6 @@ struct LookupLaunch {
   int* bbase;                 // nbk + 1: first position of each bucket
   int* ubase;                 // nbk + 1: distinct keys per bucket, then their first index
   PartEntry* part;            // N
-  int* ovf;                   // 1 + nbk: count, overflowed buckets
   unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
   unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
   long long key_tiles;

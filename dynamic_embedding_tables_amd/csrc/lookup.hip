@@ -10,13 +10,14 @@
 //
 // Kernel sequence of one call (all on one stream, no host read-back):
 //   k_prep      merged bag offsets, offset validation, per-call counters
-//   k_part_hist / k_part_colscan / k_part_bscan / k_part_scatter
+//   k_part_hist / k_part_colscan / k_scan_small / k_part_scatter
 //               transform + tag every occurrence and partition the call by
 //               the top bits of the key's hash (one radix-sort pass)
-//   k_bucket    one bucket per block: dedup in LDS, counts, distinct-key
-//               indices, group offsets, inverse index and the grouped bag /
-//               occurrence list used by the backward; k_bucket_big takes the
-//               (adversarial) buckets that overflow the LDS table
+//   k_bucket    one bucket per block, twice around a scan of the per-bucket
+//               distinct counts: dedup in LDS, counts, distinct-key indices,
+//               group offsets, inverse index and the grouped bag / occurrence
+//               list used by the backward (a bucket that overflows the LDS
+//               table, from colliding inputs, uses a global one)
 //   k_key_probe per distinct key: IDMap probe / CAS insert, count, admission
 //               decision; block sums of the rows to allocate
 //   k_key_scan  one block: exclusive scan of the block sums; rows come from
@@ -108,7 +109,6 @@ __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
     *L.res.num_unique = 0;
     L.res.plan[0] = 0;  // long keys
     L.res.plan[1] = 0;  // chunks
-    L.ovf[0] = 0;       // overflowed buckets
   }
   if (idx > nb) return;
   if (idx == nb) {
@@ -236,12 +236,16 @@ __global__ __launch_bounds__(kPartThreads) void k_part_colscan(LookupLaunch L) {
 // the total also to *total_ll when given.  Bucket positions (bbase) and the
 // distinct-key bases of the buckets (ubase).
 __global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long long* total_ll) {
+  constexpr int kPer = kMaxBuckets / kPartThreads;  // n <= kMaxBuckets
   __shared__ int s_w[kPartThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (n + kPartThreads - 1) / kPartThreads;
-  const int b0 = tid * per;
+  const int b0 = tid * kPer;
+  int v[kPer];
   int sum = 0;
-  for (int b = b0; b < b0 + per && b < n; ++b) sum += a[b];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = b0 + k < n ? a[b0 + k] : 0;  // all loads in flight
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) sum += v[k];
   int x = sum;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -252,14 +256,14 @@ __global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long
   __syncthreads();
   int run = x - sum, all = 0;
 #pragma unroll
-  for (int v = 0; v < kPartThreads / 64; ++v) {
-    run += v < w ? s_w[v] : 0;
-    all += s_w[v];
+  for (int q = 0; q < kPartThreads / 64; ++q) {
+    run += q < w ? s_w[q] : 0;
+    all += s_w[q];
   }
-  for (int b = b0; b < b0 + per && b < n; ++b) {
-    const int c = a[b];
-    a[b] = run;
-    run += c;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (b0 + k < n) a[b0 + k] = run;
+    run += v[k];
   }
   if (tid == 0) {
     a[n] = all;
@@ -350,11 +354,93 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(LookupLaunch L) {
   }
 }
 
+// A bucket whose distinct keys overflow the LDS table (only inputs built to
+// collide in the hash's top bits get here) is done by its block with an
+// open-addressing table in global memory -- the bucket's own region of the
+// dedup table, 2 slots per occurrence -- and atomics.  Slow but bounded.
+// COUNT inserts the bucket's keys and counts them (the distinct count goes to
+// ubase[b]); EMIT (after the scan) writes the distinct keys' outputs and the
+// occurrences' inverse and grouped entries, then empties the region again.
+__device__ __forceinline__ long long ld_key(const DedupSlot* d) {
+  return (long long)__hip_atomic_load(reinterpret_cast<const unsigned long long*>(&d->key), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_int(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_int(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool EMIT>
+__device__ void bucket_global(const LookupLaunch& L, int b, int& s_nd, int& s_cursor) {
+  const int tid = threadIdx.x;
+  const int s = L.bbase[b], m = L.bbase[b + 1] - s;
+  DedupSlot* R = L.dd + 2ll * s;
+  const unsigned long long cap = 2ull * (unsigned long long)m;
+  __syncthreads();
+  if (tid == 0) {
+    s_nd = 0;
+    s_cursor = 0;
+  }
+  __syncthreads();
+  if (!EMIT) {
+    for (int i = tid; i < m; i += kThreads) {
+      const long long key = L.part[s + i].key;
+      unsigned long long h = (fib_mix(key) >> 20) % cap;
+      while (true) {
+        const long long c = ld_key(&R[h]);
+        if (c == key) break;
+        if (c == kEmptyKey) {
+          const long long o = (long long)atomicCAS((unsigned long long*)&R[h].key, (unsigned long long)kEmptyKey,
+                                                   (unsigned long long)key);
+          if (o == kEmptyKey || o == key) break;
+        }
+        h = h + 1 == cap ? 0 : h + 1;
+      }
+      atomicAdd(&R[h].count, 1);
+    }
+    __syncthreads();
+    for (unsigned long long h = tid; h < cap; h += kThreads)
+      if (ld_key(&R[h]) != kEmptyKey) atomicAdd(&s_nd, 1);
+    __syncthreads();
+    if (tid == 0) L.ubase[b] = s_nd;
+    return;
+  }
+  const long long ub = L.ubase[b];
+  for (unsigned long long h = tid; h < cap; h += kThreads) {
+    const long long key = ld_key(&R[h]);
+    if (key == kEmptyKey) continue;
+    const long long u = ub + atomicAdd(&s_nd, 1);
+    const int c = ld_int(&R[h].count);
+    const int o = atomicAdd(&s_cursor, c);
+    L.res.unique_keys[u] = key;
+    L.res.counts[u] = c;
+    st_int(&L.res.unique_offsets[u], s + o);
+    st_int(&R[h].uidx, (int)u);
+  }
+  __syncthreads();
+  for (int i = tid; i < m; i += kThreads) {
+    const PartEntry e = L.part[s + i];
+    unsigned long long h = (fib_mix(e.key) >> 20) % cap;
+    while (ld_key(&R[h]) != e.key) h = h + 1 == cap ? 0 : h + 1;
+    const int u = ld_int(&R[h].uidx);
+    const int pos = atomicSub(&R[h].count, 1) - 1;  // the group is filled from its end
+    L.res.grouped[ld_int(&L.res.unique_offsets[u]) + pos] = e.g;
+    L.res.inverse[e.occ] = u;
+  }
+  __syncthreads();
+  for (unsigned long long h = tid; h < cap; h += kThreads) {
+    R[h].key = kEmptyKey;
+    R[h].count = 0;
+  }
+}
+
 // One bucket per block, in two launches around a scan of the per-bucket
 // distinct counts (so the distinct keys get dense indices without a global
 // counter, which thousands of blocks would serialise on).  Both launches
 // deduplicate the bucket in an LDS table of TAB entries (at most 3/4 full; a
-// bucket with more distinct keys is marked -1 and handed to k_bucket_big).
+// bucket with more distinct keys takes bucket_global instead).
 // COUNT writes the bucket's distinct count; EMIT writes the distinct keys
 // (index ubase[b] + their order in the table), counts and group offsets
 // inside the bucket's range, then every occurrence's inverse index and
@@ -420,17 +506,12 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L) {
     }
   }
   __syncthreads();
-  if (EMIT && s_over) return;  // k_bucket_big's
+  if (s_over) {  // rare: colliding inputs only
+    bucket_global<EMIT>(L, b, s_nd, s_cursor);
+    return;
+  }
   if (!EMIT) {
-    if (tid == 0) {
-      if (s_over) {
-        const int k = atomicAdd(&L.ovf[0], 1);  // rare: colliding inputs only
-        L.ovf[1 + k] = b;
-        L.ubase[b] = 0;  // counted by k_bucket_big
-      } else {
-        L.ubase[b] = s_nd;
-      }
-    }
+    if (tid == 0) L.ubase[b] = s_nd;
     return;
   }
   const int nd = s_nd;
@@ -463,95 +544,6 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L) {
       L.res.grouped[s + pos] = e[k].g;
       L.res.inverse[e[k].occ] = s_u[h];
     }
-  }
-}
-
-// Buckets whose distinct keys overflowed the LDS table (only inputs built to
-// collide in the hash's top bits get here): the same steps with an open-
-// addressing table in global memory, the bucket's own region of the dedup
-// table (2 slots per occurrence), and atomics.  Slow but bounded; the region
-// is left empty again.
-__device__ __forceinline__ long long ld_key(const DedupSlot* d) {
-  return (long long)__hip_atomic_load(reinterpret_cast<const unsigned long long*>(&d->key), __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_int(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_int(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// COUNT: insert the bucket's keys into its region and count them; its
-// distinct count goes to ubase[b].  EMIT (after the scan): the distinct keys'
-// outputs, the occurrences' inverse and grouped entries, then the region is
-// emptied again.
-template <bool EMIT>
-__global__ __launch_bounds__(kThreads) void k_bucket_big(LookupLaunch L) {
-  __shared__ int s_nd, s_cursor;
-  const int tid = threadIdx.x;
-  for (int q = blockIdx.x; q < ld_int(&L.ovf[0]); q += gridDim.x) {
-    const int b = L.ovf[1 + q];
-    const int s = L.bbase[b], m = L.bbase[b + 1] - s;
-    DedupSlot* R = L.dd + 2ll * s;
-    const unsigned long long cap = 2ull * (unsigned long long)m;
-    if (tid == 0) {
-      s_nd = 0;
-      s_cursor = 0;
-    }
-    if (!EMIT) {
-      for (int i = tid; i < m; i += kThreads) {
-        const long long key = L.part[s + i].key;
-        unsigned long long h = (fib_mix(key) >> 20) % cap;
-        while (true) {
-          const long long c = ld_key(&R[h]);
-          if (c == key) break;
-          if (c == kEmptyKey) {
-            const long long o = (long long)atomicCAS((unsigned long long*)&R[h].key,
-                                                     (unsigned long long)kEmptyKey, (unsigned long long)key);
-            if (o == kEmptyKey || o == key) break;
-          }
-          h = h + 1 == cap ? 0 : h + 1;
-        }
-        atomicAdd(&R[h].count, 1);
-      }
-      __syncthreads();
-      for (unsigned long long h = tid; h < cap; h += kThreads)
-        if (ld_key(&R[h]) != kEmptyKey) atomicAdd(&s_nd, 1);
-      __syncthreads();
-      if (tid == 0) L.ubase[b] = s_nd;
-      __syncthreads();
-      continue;
-    }
-    __syncthreads();
-    const long long ub = L.ubase[b];
-    for (unsigned long long h = tid; h < cap; h += kThreads) {
-      const long long key = ld_key(&R[h]);
-      if (key == kEmptyKey) continue;
-      const long long u = ub + atomicAdd(&s_nd, 1);
-      const int c = ld_int(&R[h].count);
-      const int o = atomicAdd(&s_cursor, c);
-      L.res.unique_keys[u] = key;
-      L.res.counts[u] = c;
-      st_int(&L.res.unique_offsets[u], s + o);
-      st_int(&R[h].uidx, (int)u);
-    }
-    __syncthreads();
-    for (int i = tid; i < m; i += kThreads) {
-      const PartEntry e = L.part[s + i];
-      unsigned long long h = (fib_mix(e.key) >> 20) % cap;
-      while (ld_key(&R[h]) != e.key) h = h + 1 == cap ? 0 : h + 1;
-      const int u = ld_int(&R[h].uidx);
-      const int pos = atomicSub(&R[h].count, 1) - 1;  // the group is filled from its end
-      L.res.grouped[ld_int(&L.res.unique_offsets[u]) + pos] = e.g;
-      L.res.inverse[e.occ] = u;
-    }
-    __syncthreads();
-    for (unsigned long long h = tid; h < cap; h += kThreads) {
-      R[h].key = kEmptyKey;
-      R[h].count = 0;
-    }
-    __syncthreads();
   }
 }
 
@@ -651,11 +643,19 @@ __global__ __launch_bounds__(kThreads) void k_key_probe(LookupLaunch L, TableDev
 constexpr int kScanThreads = 1024;
 // In-place exclusive scan of a[0..n) by one block; returns the total.
 __device__ unsigned long long scan_tiles(unsigned long long* a, long long n) {
+  constexpr int kPer = 8;  // loads a thread keeps in flight
   __shared__ unsigned long long s_w[kScanThreads / 64];
   const long long per = (n + kScanThreads - 1) / kScanThreads;
   const long long b0 = (long long)threadIdx.x * per;
+  const long long b1 = b0 + per < n ? b0 + per : n;
   unsigned long long sum = 0;
-  for (long long b = b0; b < b0 + per && b < n; ++b) sum += a[b];
+  for (long long c = b0; c < b1; c += kPer) {
+    unsigned long long v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) v[k] = c + k < b1 ? a[c + k] : 0ull;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) sum += v[k];
+  }
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   unsigned long long x = sum;
   for (int d = 1; d < 64; d <<= 1) {
@@ -671,10 +671,15 @@ __device__ unsigned long long scan_tiles(unsigned long long* a, long long n) {
   }
   __syncthreads();
   unsigned long long run = before + x - sum;
-  for (long long b = b0; b < b0 + per && b < n; ++b) {
-    const unsigned long long v = a[b];
-    a[b] = run;
-    run += v;
+  for (long long c = b0; c < b1; c += kPer) {
+    unsigned long long v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) v[k] = c + k < b1 ? a[c + k] : 0ull;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      if (c + k < b1) a[c + k] = run;
+      run += v[k];
+    }
   }
   return all;
 }
@@ -777,15 +782,17 @@ __global__ __launch_bounds__(kThreads) void k_occref(LookupLaunch L, TableDev t)
   long long r[kOccPerThread];
 #pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) r[k] = u[k] >= 0 ? L.res.unique_rows[u[k]] : -1;
+  // second dependent batch: the pending key, or the row's block base
+  long long v[kOccPerThread];
 #pragma unroll
   for (int k = 0; k < kOccPerThread; ++k) {
-    if (u[k] < 0) continue;
-    long long v = r[k];
-    if (v < 0) v = kOccNoRow;
-    else if (v & kFreshRow) v = (long long)(kOccPendingBit | (unsigned long long)L.res.unique_keys[u[k]]);
-    else v = (long long)row_ptr(t.rs, v);
-    occref[j0 + (long long)k * kThreads] = v;
+    if (r[k] < 0) v[k] = kOccNoRow;
+    else if (r[k] & kFreshRow) v[k] = (long long)(kOccPendingBit | (unsigned long long)L.res.unique_keys[u[k]]);
+    else v[k] = (long long)row_ptr(t.rs, r[k]);
   }
+#pragma unroll
+  for (int k = 0; k < kOccPerThread; ++k)
+    if (u[k] >= 0) occref[j0 + (long long)k * kThreads] = v[k];
 }
 
 }  // namespace
@@ -805,14 +812,12 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
       RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), nb_grid, dim3(kThreads), s, L);
     else
       RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), nb_grid, dim3(kThreads), s, L);
-    RECIS_LAUNCH("k_bucket_big_count", k_bucket_big<false>, dim3(64), dim3(kThreads), s, L);
     RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.ubase, L.nbk,
                        reinterpret_cast<long long*>(L.res.num_unique));
     if (L.big_tab)
       RECIS_LAUNCH("k_bucket_emit", (k_bucket<2048, true>), nb_grid, dim3(kThreads), s, L);
     else
       RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true>), nb_grid, dim3(kThreads), s, L);
-    RECIS_LAUNCH("k_bucket_big_emit", k_bucket_big<true>, dim3(64), dim3(kThreads), s, L);
     RECIS_LAUNCH("k_key_probe", k_key_probe, dim3((unsigned)L.key_tiles), dim3(kThreads), s, L, t);
   }
   RECIS_LAUNCH("k_key_scan", k_key_scan, dim3(1), dim3(kScanThreads), s, L, t);
