@@ -88,7 +88,7 @@ def cpu_baseline(seconds_budget=20.0):
 
 
 # kernels the warm-up steps time, one per step, to pick the dominant one
-CANDIDATE_KERNELS = ("k_bwd_short", "k_fwd_pool", "k_key_probe", "k_bucket_emit", "k_part_scatter")
+CANDIDATE_KERNELS = ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bucket_count")
 COPY_BYTES = 1 << 30
 
 

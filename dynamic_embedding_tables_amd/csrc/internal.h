@@ -44,7 +44,6 @@ constexpr int kLdsTab = 1 << kLdsTabBits;            // block-local dedup table 
 static_assert(kLdsTab == 2 * kOccTile, "block-local dedup table at most half full");
 // Distinct-key tiling of the per-key kernels: one key per thread, so that the
 // dependent probe chains of different keys overlap instead of queueing.
-constexpr int kKeyTile = kThreads;
 // Backward: keys with more occurrences than kShortMax are split into chunks.
 constexpr int kShortMax = 64;
 constexpr int kChunk = 64;  // one grouped entry per lane of a wave
@@ -195,10 +194,20 @@ __device__ __forceinline__ float4 init4(unsigned long long seed, long long key, 
 }
 
 // ------------------------------------------------------------ the table
+// The IDMap is open addressing with linear probing, split into 2^region_bits
+// regions by the top bits of the key's hash: a key's home slot is the top
+// bits of its hash (as for one undivided table) and its probe wraps inside
+// the home slot's region.  The lookup partitions a call by the same top bits,
+// so one block owns every region its bucket maps to and inserts without
+// global atomics.
+constexpr int kMinRegionSlotBits = 10;  // regions hold at least 1024 slots
+
 struct TableDev {
   Slot* slots;
   unsigned long long slot_mask;
   int slot_shift;
+  int region_bits;
+  unsigned long long region_mask;  // slots per region - 1
   DevCounters* ctr;
   int* free_list;
   RowSpace rs;
@@ -208,6 +217,10 @@ struct TableDev {
   float init_scale;                    // bound * 2^-23
   long long rows_limit;                // rows covered by blocks
 };
+
+__device__ __forceinline__ unsigned long long next_slot(const TableDev& t, unsigned long long p) {
+  return (p & ~t.region_mask) | ((p + 1) & t.region_mask);
+}
 
 // Initial values of 16-byte parameter chunk c of the row of `key`, in the
 // storage format (4 fp32 or 8 bf16 elements).
@@ -335,7 +348,6 @@ struct LookupLaunch {
   PartEntry* part;            // N
   unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
   unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
-  long long key_tiles;
 };
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);
 

@@ -15,18 +15,19 @@
 //               the top bits of the key's hash (one radix-sort pass)
 //   k_bucket    one bucket per block, twice around a scan of the per-bucket
 //               distinct counts: dedup in LDS, counts, distinct-key indices,
-//               group offsets, inverse index and the grouped bag / occurrence
-//               list used by the backward (a bucket that overflows the LDS
-//               table, from colliding inputs, uses a global one)
-//   k_key_probe per distinct key: IDMap probe / CAS insert, count, admission
-//               decision; block sums of the rows to allocate
-//   k_key_scan  one block: exclusive scan of the block sums; rows come from
-//               the free list first, then from the bump pointer -- by prefix
-//               sum, not by atomics
-//   k_key_finalize  per distinct key: row assignment (the new row is marked
+//               group offsets; in the second launch also the IDMap probe /
+//               insert of every distinct key (count, admission decision,
+//               without global atomics: the block owns the bucket's IDMap
+//               regions), then each occurrence's inverse index, grouped bag /
+//               occurrence entry and forward reference (a bucket that
+//               overflows the LDS table, from colliding inputs, uses a global
+//               one)
+//   k_key_scan  one block: exclusive scan of the per-bucket sums; rows come
+//               from the free list first, then from the bump pointer -- by
+//               prefix sum, not by atomics
+//   k_key_finalize  per bucket: row assignment (the new row is marked
 //               pending, not written: its values are the initializer's until
 //               its first update), backward plan for long keys
-//   k_occref    per occurrence: the row reference used by the forward
 // Memory accesses that do not depend on each other are issued as one batch
 // per thread (all loads of a phase before any use), so that each thread
 // waits once per phase rather than once per item.
@@ -354,6 +355,93 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(LookupLaunch L) {
   }
 }
 
+// ------------------------------------------------ IDMap probe / insert
+struct ProbeOut {
+  long long row = -1;   // the key's row (pending rows with kFreshRow), or -1
+  unsigned sl = 0xFFFFFFFFu;
+  int need = 0;         // no row yet and the count reached the admission threshold
+  int ins = 0;          // inserted by this call
+  unsigned err = 0;
+};
+
+// One distinct key with `c` occurrences in this call: probe its region of the
+// IDMap; on a miss (unless find_only) take an empty slot that claim(p) grants
+// this thread, and write the slot whole; add c to its count (saturating).  The
+// caller's block owns the key's region, so the slot stores need no atomics.
+template <typename Claim>
+__device__ __forceinline__ ProbeOut idmap_probe(const TableDev& t, long long key, int c, bool find_only,
+                                                Claim claim) {
+  ProbeOut o;
+  if (key < 0) return o;  // a failed transform
+  unsigned long long p = slot_of(key, t.slot_shift);
+  bool found = false, inserted = false;
+  Slot sv;
+  for (unsigned long long n = 0; n <= t.region_mask; ++n) {
+    sv = t.slots[p];
+    if (sv.key == key) {
+      found = true;
+      break;
+    }
+    if (sv.key == kEmptyKey) {
+      if (find_only) break;
+      if (claim(p)) {
+        inserted = true;
+        break;
+      }
+    }
+    p = next_slot(t, p);
+  }
+  if (!found && !inserted) {
+    if (!find_only) o.err = kErrCapacity;  // the key's region is full
+    return o;
+  }
+  o.sl = (unsigned)p;
+  if (find_only) {
+    o.row = sv.row;
+  } else {
+    const unsigned c0 = inserted ? 0u : sv.count;
+    const unsigned long long cs = (unsigned long long)c0 + (unsigned)c;
+    const unsigned cnt = cs > 0xFFFFFFFFull ? 0xFFFFFFFFu : (unsigned)cs;
+    if (inserted) {
+      Slot ns;
+      ns.key = key;
+      ns.row = -1;
+      ns.count = cnt;
+      t.slots[p] = ns;
+    } else {
+      t.slots[p].count = cnt;
+    }
+    const int r = inserted ? -1 : sv.row;
+    if (r < 0 && cnt >= t.admit) o.need = 1;
+    else o.row = r;
+    o.ins = inserted ? 1 : 0;
+  }
+  // a pending row is reported with the fresh mark (its values may still be
+  // the initializer's)
+  if (o.row >= 0 && (o.row & kPendingRow)) o.row = (o.row & ~(long long)kPendingRow) | kFreshRow;
+  return o;
+}
+
+// The forward's reference for the occurrences of a key (see kOccNoRow).
+__device__ __forceinline__ long long occ_ref(const TableDev& t, const ProbeOut& o, long long key) {
+  if (o.need || (o.row >= 0 && (o.row & kFreshRow))) return (long long)(kOccPendingBit | (unsigned long long)key);
+  if (o.row < 0) return kOccNoRow;
+  return (long long)row_ptr(t.rs, o.row);
+}
+
+// Per-key outputs of the probe, and its share of the bucket's sums: rows to
+// allocate << 32 | keys inserted, and long keys << 32 | their chunks.
+__device__ __forceinline__ void key_outputs(const LookupLaunch& L, long long u, int c, const ProbeOut& o,
+                                            unsigned long long& sum, unsigned long long& sum_long) {
+  unsigned* idslot = reinterpret_cast<unsigned*>(L.res.plan + plan_layout(L.res.capacity).o_idslot);
+  L.res.unique_rows[u] = o.need ? -2 : o.row;  // -2: needs a row from this call
+  idslot[u] = o.sl;
+  sum += ((unsigned long long)o.need << 32) | (unsigned)o.ins;
+  // a key that will have a row and more than kShortMax occurrences is reduced
+  // in chunks by the backward
+  if (c > kShortMax && (o.need || o.row >= 0)) sum_long += (1ull << 32) | (unsigned)((c + kChunk - 1) / kChunk);
+}
+
 // A bucket whose distinct keys overflow the LDS table (only inputs built to
 // collide in the hash's top bits get here) is done by its block with an
 // open-addressing table in global memory -- the bucket's own region of the
@@ -372,8 +460,16 @@ __device__ __forceinline__ void st_int(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Reference of an occurrence of distinct key u from its final row entry.
+__device__ __forceinline__ long long ref_of_row(const TableDev& t, long long v, long long key) {
+  if (v == -2 || (v >= 0 && (v & kFreshRow))) return (long long)(kOccPendingBit | (unsigned long long)key);
+  if (v < 0) return kOccNoRow;
+  return (long long)row_ptr(t.rs, v);
+}
+
 template <bool EMIT>
-__device__ void bucket_global(const LookupLaunch& L, int b, int& s_nd, int& s_cursor) {
+__device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, int& s_nd, int& s_cursor,
+                              unsigned long long& s_sum, unsigned long long& s_sum_long) {
   const int tid = threadIdx.x;
   const int s = L.bbase[b], m = L.bbase[b + 1] - s;
   DedupSlot* R = L.dd + 2ll * s;
@@ -382,6 +478,8 @@ __device__ void bucket_global(const LookupLaunch& L, int b, int& s_nd, int& s_cu
   if (tid == 0) {
     s_nd = 0;
     s_cursor = 0;
+    s_sum = 0;
+    s_sum_long = 0;
   }
   __syncthreads();
   if (!EMIT) {
@@ -408,6 +506,10 @@ __device__ void bucket_global(const LookupLaunch& L, int b, int& s_nd, int& s_cu
     return;
   }
   const long long ub = L.ubase[b];
+  const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
+  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
+  unsigned long long sum = 0, sum_long = 0;
+  unsigned err = 0;
   for (unsigned long long h = tid; h < cap; h += kThreads) {
     const long long key = ld_key(&R[h]);
     if (key == kEmptyKey) continue;
@@ -418,8 +520,23 @@ __device__ void bucket_global(const LookupLaunch& L, int b, int& s_nd, int& s_cu
     L.res.counts[u] = c;
     st_int(&L.res.unique_offsets[u], s + o);
     st_int(&R[h].uidx, (int)u);
+    // an empty IDMap slot goes to whichever thread's CAS takes it
+    auto claim = [&](unsigned long long q) {
+      return atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
+                       (unsigned long long)key) == (unsigned long long)kEmptyKey;
+    };
+    const ProbeOut po = idmap_probe(t, key, c, find_only, claim);
+    err |= po.err;
+    key_outputs(L, u, c, po, sum, sum_long);
   }
+  if (err) atomicOr(&t.ctr->error, err);
+  if (sum) atomicAdd(&s_sum, sum);
+  if (sum_long) atomicAdd(&s_sum_long, sum_long);
   __syncthreads();
+  if (tid == 0) {
+    L.blk_sums[b] = s_sum;
+    L.blk_long[b] = s_sum_long;
+  }
   for (int i = tid; i < m; i += kThreads) {
     const PartEntry e = L.part[s + i];
     unsigned long long h = (fib_mix(e.key) >> 20) % cap;
@@ -428,6 +545,9 @@ __device__ void bucket_global(const LookupLaunch& L, int b, int& s_nd, int& s_cu
     const int pos = atomicSub(&R[h].count, 1) - 1;  // the group is filled from its end
     L.res.grouped[ld_int(&L.res.unique_offsets[u]) + pos] = e.g;
     L.res.inverse[e.occ] = u;
+    const long long v = (long long)__hip_atomic_load(reinterpret_cast<unsigned long long*>(&L.res.unique_rows[u]),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    occref[e.occ] = ref_of_row(t, v, e.key);
   }
   __syncthreads();
   for (unsigned long long h = tid; h < cap; h += kThreads) {
@@ -440,36 +560,50 @@ __device__ void bucket_global(const LookupLaunch& L, int b, int& s_nd, int& s_cu
 // distinct counts (so the distinct keys get dense indices without a global
 // counter, which thousands of blocks would serialise on).  Both launches
 // deduplicate the bucket in an LDS table of TAB entries (at most 3/4 full; a
-// bucket with more distinct keys takes bucket_global instead).
-// COUNT writes the bucket's distinct count; EMIT writes the distinct keys
-// (index ubase[b] + their order in the table), counts and group offsets
-// inside the bucket's range, then every occurrence's inverse index and
-// grouped-list entry.
+// bucket with more distinct keys takes bucket_global instead).  COUNT writes
+// the bucket's distinct count.  EMIT writes the distinct keys (index
+// ubase[b] + their order in the table), counts and group offsets inside the
+// bucket's range; probes the IDMap for each of them -- the block owns every
+// IDMap region of its bucket, so empty slots are shared out through an LDS
+// set instead of global atomics -- and writes its row and the bucket's sums
+// (rows to allocate, keys inserted, long keys, chunks); then every
+// occurrence's inverse index, grouped-list entry and forward reference.
 template <int TAB, bool EMIT>
-__global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L) {
+__global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t) {
   constexpr int kMaxDistinct = TAB / 4 * 3;
   constexpr int kTabBits = TAB == 1024 ? 10 : (TAB == 2048 ? 11 : 0);
   static_assert(kTabBits > 0, "TAB is 1024 or 2048");
   __shared__ long long s_key[TAB];
   __shared__ int s_cnt[TAB];
   __shared__ int s_u[EMIT ? TAB : 1];
+  __shared__ long long s_ref[EMIT ? TAB : 1];
+  __shared__ unsigned s_claim[EMIT ? TAB : 1];  // IDMap slots taken by this block (~0u: free)
   __shared__ unsigned short s_list[kMaxDistinct];
   __shared__ int s_nd, s_over, s_cursor;
+  __shared__ unsigned long long s_sum, s_sum_long;
+  __shared__ unsigned s_err;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int s = L.bbase[b], m = L.bbase[b + 1] - s;
   if (m == 0) {
-    if (!EMIT && tid == 0) L.ubase[b] = 0;
+    if (tid == 0) {
+      if (!EMIT) L.ubase[b] = 0;
+      else L.blk_sums[b] = L.blk_long[b] = 0;
+    }
     return;
   }
   for (int i = tid; i < TAB; i += kThreads) {
     s_key[i] = kEmptyKey;
     s_cnt[i] = 0;
+    if (EMIT) s_claim[i] = ~0u;
   }
   if (tid == 0) {
     s_nd = 0;
     s_over = 0;
     s_cursor = 0;
+    s_sum = 0;
+    s_sum_long = 0;
+    s_err = 0;
   }
   __syncthreads();
   // the bits below the bucket bits index the table
@@ -507,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L) {
   }
   __syncthreads();
   if (s_over) {  // rare: colliding inputs only
-    bucket_global<EMIT>(L, b, s_nd, s_cursor);
+    bucket_global<EMIT>(L, t, b, s_nd, s_cursor, s_sum, s_sum_long);
     return;
   }
   if (!EMIT) {
@@ -516,18 +650,50 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L) {
   }
   const int nd = s_nd;
   const long long ub = L.ubase[b];
+  const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
+  // an empty IDMap slot goes to the first thread that enters it in the set
+  // (slot indices are below 2^32; the last index of a 2^32-slot table, equal
+  // to the set's free mark, is never handed out)
+  auto claim = [&](unsigned long long p) {
+    const unsigned v = (unsigned)p;
+    if (v == ~0u) return false;
+    unsigned h = (unsigned)((p * 0x9E3779B97F4A7C15ull) >> (64 - kTabBits));
+    for (int n = 0; n < TAB; ++n) {
+      const unsigned o = atomicCAS(&s_claim[h], ~0u, v);
+      if (o == ~0u) return true;
+      if (o == v) return false;
+      h = (h + 1) & (TAB - 1);
+    }
+    return false;  // not reached: fewer claims than kMaxDistinct
+  };
+  unsigned long long sum = 0, sum_long = 0;
+  unsigned err = 0;
   for (int idx = tid; idx < nd; idx += kThreads) {
     const int h = s_list[idx];
     const long long u = ub + idx;
+    const long long key = s_key[h];
     const int c = s_cnt[h];
     const int o = atomicAdd(&s_cursor, c);
-    L.res.unique_keys[u] = s_key[h];
+    L.res.unique_keys[u] = key;
     L.res.counts[u] = c;
     L.res.unique_offsets[u] = s + o;
     s_u[h] = (int)u;
     s_cnt[h] = o;  // from here on: the next free position of the key's group
+    const ProbeOut po = idmap_probe(t, key, c, find_only, claim);
+    err |= po.err;
+    key_outputs(L, u, c, po, sum, sum_long);
+    s_ref[h] = occ_ref(t, po, key);
   }
+  if (err) atomicOr(&s_err, err);
+  if (sum) atomicAdd(&s_sum, sum);
+  if (sum_long) atomicAdd(&s_sum_long, sum_long);
   __syncthreads();
+  if (tid == 0) {
+    L.blk_sums[b] = s_sum;
+    L.blk_long[b] = s_sum_long;
+    if (s_err) atomicOr(&t.ctr->error, s_err);
+  }
+  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
   for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
     PartEntry e[kBucketPer];
 #pragma unroll
@@ -543,99 +709,8 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L) {
       const int pos = atomicAdd(&s_cnt[h], 1);
       L.res.grouped[s + pos] = e[k].g;
       L.res.inverse[e[k].occ] = s_u[h];
+      occref[e[k].occ] = s_ref[h];
     }
-  }
-}
-
-// ---------------------------------------------------------- k_key_probe
-// One distinct key per thread.  The first probe loads the whole 16-byte slot,
-// so a hit costs one dependent access after the key itself.
-__global__ __launch_bounds__(kThreads) void k_key_probe(LookupLaunch L, TableDev t) {
-  __shared__ unsigned s_err;
-  const long long U = *L.res.num_unique;
-  const long long t0 = (long long)blockIdx.x * kKeyTile;
-  if (t0 >= U) {
-    if (threadIdx.x == 0) {
-      L.blk_sums[blockIdx.x] = 0;
-      L.blk_long[blockIdx.x] = 0;
-    }
-    return;
-  }
-  if (threadIdx.x == 0) s_err = 0;
-  __syncthreads();
-  const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
-  unsigned* idslot = reinterpret_cast<unsigned*>(L.res.plan + plan_layout(L.res.capacity).o_idslot);
-  unsigned long long acc = 0, acc_long = 0;
-  unsigned ins = 0, err = 0;
-  const long long u = t0 + threadIdx.x;
-  if (u < U) {
-    const long long key = L.res.unique_keys[u];
-    const int c = L.res.counts[u];
-    long long row = -1;
-    unsigned sl = 0xFFFFFFFFu;
-    int need = 0;
-    if (key >= 0) {
-      unsigned long long p = slot_of(key, t.slot_shift);
-      Slot s = t.slots[p];
-      bool found = false, inserted = false;
-      for (unsigned long long n = 0; n <= t.slot_mask; ++n) {
-        if (n > 0) s = t.slots[p];
-        if (s.key == key) {
-          found = true;
-          break;
-        }
-        if (s.key == kEmptyKey) {
-          if (find_only) break;
-          const long long o = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
-                                                   (unsigned long long)kEmptyKey, (unsigned long long)key);
-          if (o == kEmptyKey) {
-            inserted = true;
-            break;
-          }
-          if (o == key) {  // not expected: keys are distinct within a call
-            s = t.slots[p];
-            found = true;
-            break;
-          }
-        }
-        p = (p + 1) & t.slot_mask;
-      }
-      if (!found && !inserted) {
-        if (!find_only) err |= kErrCapacity;
-      } else if (find_only) {
-        row = s.row;
-        sl = (unsigned)p;
-      } else {
-        const unsigned c0 = inserted ? 0u : s.count;
-        const unsigned long long cs = (unsigned long long)c0 + (unsigned)c;
-        const unsigned cnt = cs > 0xFFFFFFFFull ? 0xFFFFFFFFu : (unsigned)cs;
-        t.slots[p].count = cnt;
-        const int r = inserted ? -1 : s.row;
-        if (r < 0 && cnt >= t.admit) need = 1;
-        else row = r;
-        sl = (unsigned)p;
-        ins = inserted ? 1u : 0u;
-      }
-    }
-    // a pending row is reported with the fresh mark (its values may still be
-    // the initializer's); -2 marks a key that needs a row from this call
-    if (row >= 0 && (row & kPendingRow)) row = (row & ~(long long)kPendingRow) | kFreshRow;
-    L.res.unique_rows[u] = need ? -2 : row;
-    idslot[u] = sl;
-    acc = ((unsigned long long)need << 32) | ins;
-    // a key that will have a row and more than kShortMax occurrences is
-    // reduced in chunks by the backward
-    if (c > kShortMax && (need || row >= 0))
-      acc_long = (1ull << 32) | (unsigned long long)((c + kChunk - 1) / kChunk);
-  }
-  if (err) atomicOr(&s_err, err);
-  unsigned long long total, total_long;
-  block_exclusive_scan(acc, &total);
-  block_exclusive_scan(acc_long, &total_long);
-  if (threadIdx.x == 0) {
-    L.blk_sums[blockIdx.x] = total;
-    L.blk_long[blockIdx.x] = total_long;
-    if (s_err) atomicOr(&t.ctr->error, s_err);
   }
 }
 
@@ -684,12 +759,12 @@ __device__ unsigned long long scan_tiles(unsigned long long* a, long long n) {
   return all;
 }
 
-// One block: prefix sums of the key tiles' (rows to allocate, keys inserted)
+// One block: prefix sums of the buckets' (rows to allocate, keys inserted)
 // and (long keys, chunks); the row sources of this call; the key and chunk
 // counts of the backward plan.
 __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, TableDev t) {
   const long long U = *L.res.num_unique;
-  const long long nblk = (U + kKeyTile - 1) / kKeyTile;
+  const long long nblk = L.N > 0 ? L.nbk : 0;  // per-bucket sums
   const unsigned long long all = scan_tiles(L.blk_sums, nblk);
   const unsigned long long all_long = scan_tiles(L.blk_long, nblk);
   if (threadIdx.x == 0) {
@@ -712,43 +787,50 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
 }
 
 // ------------------------------------------------------- k_key_finalize
+// One bucket per block: its distinct keys in index order, 256 at a time; a
+// block scan ranks the keys that need a row and the long keys, on top of the
+// bucket's prefix from k_key_scan.  Rows come from the free list first, then
+// from the bump pointer; a new row is marked pending, not written (its values
+// are the initializer's until its first update).  Long keys get their entry
+// and chunks in the backward plan.
 __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, TableDev t) {
   __shared__ unsigned s_err;
-  const long long U = *L.res.num_unique;
-  const long long t0 = (long long)blockIdx.x * kKeyTile;
-  if (t0 >= U) return;
+  const int b = blockIdx.x;
+  const long long ub = L.ubase[b], nd = L.ubase[b + 1] - ub;
+  if (nd == 0) return;
   if (threadIdx.x == 0) s_err = 0;
-  const long long u = t0 + threadIdx.x;
-  const bool valid = u < U;
-  int cnt = 0;
-  long long mark = -1;
-  if (valid) {
-    cnt = L.res.counts[u];
-    mark = L.res.unique_rows[u];
-  }
-  const unsigned long long acc = valid ? ((unsigned long long)(mark == -2) << 32) : 0ull;
-  const bool is_long = valid && cnt > kShortMax && mark != -1;  // as k_key_probe counted it
-  const int nch = (cnt + kChunk - 1) / kChunk;
-  const unsigned long long acc_long = is_long ? ((1ull << 32) | (unsigned long long)nch) : 0ull;
-  unsigned long long total;
-  const unsigned long long run = block_exclusive_scan(acc, &total) + L.blk_sums[blockIdx.x];
-  const unsigned long long run_long = block_exclusive_scan(acc_long, &total) + L.blk_long[blockIdx.x];
+  const PlanLayout pl = plan_layout(L.res.capacity);
+  int* plan = L.res.plan;
+  const unsigned* idslot = reinterpret_cast<const unsigned*>(plan + pl.o_idslot);
+  const long long take = t.ctr->take_free, ftop = t.ctr->free_top_old, base = t.ctr->bump_base;
+  unsigned long long run0 = L.blk_sums[b], run0_long = L.blk_long[b];
   unsigned err = 0;
-  if (valid) {
-    const PlanLayout pl = plan_layout(L.res.capacity);
-    int* plan = L.res.plan;
-    const unsigned* idslot = reinterpret_cast<const unsigned*>(plan + pl.o_idslot);
-    const long long take = t.ctr->take_free, ftop = t.ctr->free_top_old, base = t.ctr->bump_base;
-    long long row = mark;
-    if (row == -2) {
+  for (long long c0 = 0; c0 < nd; c0 += kThreads) {
+    const long long u = ub + c0 + threadIdx.x;
+    const bool valid = c0 + threadIdx.x < nd;
+    int cnt = 0;
+    long long mark = -1;
+    if (valid) {
+      cnt = L.res.counts[u];
+      mark = L.res.unique_rows[u];
+    }
+    const unsigned long long acc = valid ? ((unsigned long long)(mark == -2) << 32) : 0ull;
+    const bool is_long = valid && cnt > kShortMax && mark != -1;  // as k_bucket counted it
+    const int nch = (cnt + kChunk - 1) / kChunk;
+    const unsigned long long acc_long = is_long ? ((1ull << 32) | (unsigned long long)nch) : 0ull;
+    unsigned long long total, total_long;
+    const unsigned long long run = block_exclusive_scan(acc, &total) + run0;
+    const unsigned long long run_long = block_exclusive_scan(acc_long, &total_long) + run0_long;
+    run0 += total;
+    run0_long += total_long;
+    if (!valid) continue;
+    if (mark == -2) {
       const long long i = (long long)(run >> 32);
-      row = i < take ? (long long)t.free_list[ftop - 1 - i] : base + (i - take);
+      const long long row = i < take ? (long long)t.free_list[ftop - 1 - i] : base + (i - take);
       if (row >= t.rows_limit) {
-        row = -1;
         err |= kErrCapacity;
         L.res.unique_rows[u] = -1;
       } else {
-        // allocated but not written: its first update materialises it
         t.slots[idslot[u]].row = (int)row | kPendingRow;
         L.res.unique_rows[u] = row | kFreshRow;
       }
@@ -767,34 +849,6 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
   if (threadIdx.x == 0 && s_err) atomicOr(&t.ctr->error, s_err);
 }
 
-// ------------------------------------------------------------- k_occref
-// Per occurrence: the reference the forward reads while the lookup is
-// current -- the row's device address, the pending key, or no row.
-__global__ __launch_bounds__(kThreads) void k_occref(LookupLaunch L, TableDev t) {
-  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
-  const long long j0 = (long long)blockIdx.x * kOccTile + threadIdx.x;
-  int u[kOccPerThread];
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    const long long j = j0 + (long long)k * kThreads;
-    u[k] = j < L.N ? L.res.inverse[j] : -1;
-  }
-  long long r[kOccPerThread];
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) r[k] = u[k] >= 0 ? L.res.unique_rows[u[k]] : -1;
-  // second dependent batch: the pending key, or the row's block base
-  long long v[kOccPerThread];
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k) {
-    if (r[k] < 0) v[k] = kOccNoRow;
-    else if (r[k] & kFreshRow) v[k] = (long long)(kOccPendingBit | (unsigned long long)L.res.unique_keys[u[k]]);
-    else v[k] = (long long)row_ptr(t.rs, r[k]);
-  }
-#pragma unroll
-  for (int k = 0; k < kOccPerThread; ++k)
-    if (u[k] >= 0) occref[j0 + (long long)k * kThreads] = v[k];
-}
-
 }  // namespace
 
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
@@ -809,22 +863,18 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
     RECIS_LAUNCH("k_part_scatter", k_part_scatter, dim3(G), dim3(kPartThreads), s, L);
     const dim3 nb_grid((unsigned)L.nbk);
     if (L.big_tab)
-      RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), nb_grid, dim3(kThreads), s, L);
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), nb_grid, dim3(kThreads), s, L, t);
     else
-      RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), nb_grid, dim3(kThreads), s, L);
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), nb_grid, dim3(kThreads), s, L, t);
     RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.ubase, L.nbk,
-                       reinterpret_cast<long long*>(L.res.num_unique));
+                 reinterpret_cast<long long*>(L.res.num_unique));
     if (L.big_tab)
-      RECIS_LAUNCH("k_bucket_emit", (k_bucket<2048, true>), nb_grid, dim3(kThreads), s, L);
+      RECIS_LAUNCH("k_bucket_emit", (k_bucket<2048, true>), nb_grid, dim3(kThreads), s, L, t);
     else
-      RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true>), nb_grid, dim3(kThreads), s, L);
-    RECIS_LAUNCH("k_key_probe", k_key_probe, dim3((unsigned)L.key_tiles), dim3(kThreads), s, L, t);
+      RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true>), nb_grid, dim3(kThreads), s, L, t);
   }
   RECIS_LAUNCH("k_key_scan", k_key_scan, dim3(1), dim3(kScanThreads), s, L, t);
-  if (L.N > 0) {
-    RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.key_tiles), dim3(kThreads), s, L, t);
-    RECIS_LAUNCH("k_occref", k_occref, dim3((unsigned)((L.N + kOccTile - 1) / kOccTile)), dim3(kThreads), s, L, t);
-  }
+  if (L.N > 0) RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.nbk), dim3(kThreads), s, L, t);
 }
 
 }  // namespace recis

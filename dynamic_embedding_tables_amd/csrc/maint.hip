@@ -38,14 +38,14 @@ __global__ void k_fill_dedup(DedupSlot* dd, long long cap) {
 // Insert `key` (absent, unique among concurrent inserters) into t's IDMap.
 __device__ __forceinline__ long long claim_slot(const TableDev& t, long long key) {
   unsigned long long p = slot_of(key, t.slot_shift);
-  for (unsigned long long n = 0; n <= t.slot_mask; ++n) {
+  for (unsigned long long n = 0; n <= t.region_mask; ++n) {
     const long long cur = t.slots[p].key;
     if (cur == kEmptyKey) {
       const long long old = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
                                                  (unsigned long long)kEmptyKey, (unsigned long long)key);
       if (old == kEmptyKey) return (long long)p;
     }
-    p = (p + 1) & t.slot_mask;
+    p = next_slot(t, p);
   }
   return -1;
 }
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void k_wb_apply(TableDev t, const float* rows,
       unsigned long long p = slot_of(key, t.slot_shift);
       long long at = -1;
       bool inserted = false;
-      for (unsigned long long n = 0; n <= t.slot_mask; ++n) {
+      for (unsigned long long n = 0; n <= t.region_mask; ++n) {
         const long long cur = t.slots[p].key;
         if (cur == key) {
           at = (long long)p;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void k_wb_apply(TableDev t, const float* rows,
             break;
           }
         }
-        p = (p + 1) & t.slot_mask;
+        p = next_slot(t, p);
       }
       if (at < 0) {
         atomicOr(&t.ctr->error, kErrCapacity);

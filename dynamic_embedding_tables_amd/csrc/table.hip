@@ -190,6 +190,13 @@ recis_status ensure_capacity(recis_table* t, long long n, hipStream_t s) {
   return RECIS_OK;
 }
 
+// IDMap regions: as many as the lookup's buckets can be (kMaxBuckets), but
+// none smaller than 2^kMinRegionSlotBits slots.
+int region_bits_for(long long slot_cap) {
+  const int sb = log2_exact(slot_cap);
+  return std::max(0, std::min(kMaxBucketBits, sb - kMinRegionSlotBits));
+}
+
 // Hash-partition geometry of a call with n occurrences: buckets of about
 // kBucketOcc occurrences (a power of two, at most kMaxBuckets), partition
 // blocks of about kPartOcc occurrences (at most kMaxPartBlocks).
@@ -197,10 +204,12 @@ struct PartGeom {
   int nbits, nbk, blocks, big;
   long long range;
 };
-PartGeom part_geom(long long n) {
+// Buckets never outnumber the IDMap's regions (max_bits), so that each
+// bucket's block owns whole regions.
+PartGeom part_geom(long long n, int max_bits = kMaxBucketBits) {
   PartGeom g;
   const long long want = std::max<long long>(1, (n + kBucketOcc - 1) / kBucketOcc);
-  g.nbk = (int)std::min<long long>(next_pow2(want), kMaxBuckets);
+  g.nbk = (int)std::min<long long>(next_pow2(want), 1ll << max_bits);
   g.nbits = log2_exact(g.nbk);
   g.blocks = (int)std::min<long long>(std::max<long long>(1, (n + kPartOcc - 1) / kPartOcc), kMaxPartBlocks);
   g.range = std::max<long long>(1, (n + g.blocks - 1) / g.blocks);
@@ -220,7 +229,7 @@ ScratchSizes scratch_sizes(long long cap, int dim) {
   z.hist = (size_t)g.blocks * (size_t)g.nbk * 4;
   z.bbase = (size_t)(kMaxBuckets + 1) * 4 * 2;  // bbase, then ubase
   z.uslot = (size_t)cap * 4;
-  z.blk = (size_t)(cap / kKeyTile + 2) * 8 * 2;  // blk_sums, then blk_long
+  z.blk = (size_t)(kMaxBuckets + 2) * 8 * 2;  // per-bucket sums: blk_sums, then blk_long
   z.wb = (size_t)cap * 8;
   z.partials = (size_t)plan_layout(cap).max_chunks * (size_t)dim * 8;
   return z;
@@ -306,6 +315,8 @@ TableDev recis_table::dev() const {
   d.slots = slots;
   d.slot_mask = (unsigned long long)(slot_cap - 1);
   d.slot_shift = 64 - log2_exact(slot_cap);
+  d.region_bits = region_bits_for(slot_cap);
+  d.region_mask = (unsigned long long)((slot_cap >> d.region_bits) - 1);
   d.ctr = ctr;
   d.free_list = free_list;
   d.rs.blocks = d_blocks;
@@ -352,7 +363,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   *out = nullptr;
   if (cfg->dtype != RECIS_DTYPE_F32 && cfg->dtype != RECIS_DTYPE_BF16) return RECIS_ERR_INVALID_ARG;
   if (cfg->optim < RECIS_OPTIM_NONE || cfg->optim > RECIS_OPTIM_ADAM) return RECIS_ERR_INVALID_ARG;
-  if (!(cfg->max_load > 0.f && cfg->max_load <= 0.9f)) return RECIS_ERR_INVALID_ARG;
+  if (!(cfg->max_load > 0.f && cfg->max_load <= 0.75f)) return RECIS_ERR_INVALID_ARG;
   if (!std::isfinite(cfg->init_bound) || cfg->init_bound < 0.f) return RECIS_ERR_INVALID_ARG;
   if (cfg->slot_capacity < 1 || cfg->slot_capacity > (1ll << 32)) return RECIS_ERR_INVALID_ARG;
   if (cfg->block_rows < 1 || cfg->block_rows > (1ll << 30)) return RECIS_ERR_INVALID_ARG;
@@ -496,7 +507,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.flags = flags;
   L.res = *res;
   L.dd = t->dd;
-  const PartGeom g = part_geom(N);
+  const PartGeom g = part_geom(N, region_bits_for(t->slot_cap));
   L.nbits = g.nbits;
   L.nbk = g.nbk;
   L.part_blocks = g.blocks;
@@ -507,8 +518,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.ubase = t->ubase;
   L.part = t->part;
   L.blk_sums = t->blk_sums;
-  L.blk_long = t->blk_sums + (t->scr_cap / kKeyTile + 2);
-  L.key_tiles = (N + kKeyTile - 1) / kKeyTile;
+  L.blk_long = t->blk_sums + (kMaxBuckets + 2);
   launch_lookup(L, t->dev(), s);
   return check_launch();
 }

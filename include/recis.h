@@ -51,7 +51,7 @@ typedef int32_t recis_status;
 #define RECIS_OK 0
 #define RECIS_ERR_INVALID_ARG 1   /* bad pointer, size, enum, unsorted boundaries, small buffer */
 #define RECIS_ERR_OUT_OF_MEMORY 2 /* the allocator returned NULL */
-#define RECIS_ERR_CAPACITY 3      /* max_rows / IDMap probe space exhausted (device, sticky) */
+#define RECIS_ERR_CAPACITY 3      /* max_rows, or a key's IDMap region, exhausted (device, sticky) */
 #define RECIS_ERR_KEY_RANGE 4     /* transformed id outside [0, 2^48) or slot >= 2^15 (device) */
 #define RECIS_ERR_HIP 5           /* a HIP runtime call failed */
 #define RECIS_ERR_UNSUPPORTED 6   /* a valid but unimplemented combination */
@@ -89,7 +89,10 @@ typedef struct {
   uint32_t admit_threshold; /* a key gets a row once its count reaches this (0 or 1: at once) */
   uint64_t seed;            /* initializer seed */
   float init_bound;         /* rows start uniform on [-init_bound, init_bound) */
-  float max_load;           /* IDMap occupancy that triggers growth, in (0, 0.9] */
+  float max_load;           /* IDMap occupancy that triggers growth, in (0, 0.75]: the IDMap is
+                               split into regions by the top bits of the key hash (each
+                               probe stays in its region), and this bound keeps every
+                               region from filling unless keys collide in those bits */
   int64_t slot_capacity;    /* initial IDMap slots (rounded up to a power of two) */
   int64_t block_rows;       /* rows per EmbeddingBlock (rounded up to a power of two) */
   int64_t max_rows;         /* hard row limit (<= 2^30 - 1) */
