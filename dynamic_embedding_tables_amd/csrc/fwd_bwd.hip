@@ -582,8 +582,8 @@ __device__ __forceinline__ void stage_key(const BwdArgs& a, int q, int nact, int
 // gives each key its staged-entry base and its place in an order with the
 // pending rows first, so the groups of a wave mostly agree on whether to run
 // the initializer.  Phase 2: the keys' gradient references, staged in LDS
-// when they fit.  Phase 3: each group of KL lanes walks its keys, with the
-// next key's loads issued before the current key's update and stores.
+// when they fit.  Phase 3: each group of KL lanes walks its keys, the row and
+// gradient loads of a key in flight together.
 template <int D, typename TP, int OPT, int KL>
 __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
   constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
@@ -664,15 +664,11 @@ __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
     }
     const int nact = s_nact;
     if (staged) {
-      // Software-pipelined over the group's keys: the loads of the next key
-      // (row, first GB gradient rows) are issued before the current key's
-      // update and stores.  The vector-memory counter retires in issue order,
-      // so waiting for those loads then does not wait for the stores too.
-      KeyStage<D, TP, KL, GB> cur, nxt;
-      int q = tid / KL;
-      stage_key<D, TP, OPT, KL, GB>(a, q, nact, lane, s_perm, s_c, s_st, s_eo, s_ptr, s_key, s_grow, cur);
-      while (q < nact) {
-        stage_key<D, TP, OPT, KL, GB>(a, q + GPB, nact, lane, s_perm, s_c, s_st, s_eo, s_ptr, s_key, s_grow, nxt);
+      // one key per group at a time: its row and first GB gradient rows are
+      // loaded together, further gradient rows GB at a time
+      for (int q = tid / KL; q < nact; q += GPB) {
+        KeyStage<D, TP, KL, GB> cur;
+        stage_key<D, TP, OPT, KL, GB>(a, q, nact, lane, s_perm, s_c, s_st, s_eo, s_ptr, s_key, s_grow, cur);
         double acc[CH][E];
 #pragma unroll
         for (int ch = 0; ch < CH; ++ch)
@@ -717,8 +713,6 @@ __global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
           if (cur.st == 2) a.t.slots[s_sl[cur.k]].row = row;
           a.urows[t0 + cur.k] = row;
         }
-        cur = nxt;
-        q += GPB;
       }
     } else {
       // more entries than the stage holds: one key at a time, the entries

@@ -716,47 +716,59 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
 
 // ----------------------------------------------------------- k_key_scan
 constexpr int kScanThreads = 1024;
-// In-place exclusive scan of a[0..n) by one block; returns the total.
-__device__ unsigned long long scan_tiles(unsigned long long* a, long long n) {
-  constexpr int kPer = 8;  // loads a thread keeps in flight
-  __shared__ unsigned long long s_w[kScanThreads / 64];
-  const long long per = (n + kScanThreads - 1) / kScanThreads;
-  const long long b0 = (long long)threadIdx.x * per;
-  const long long b1 = b0 + per < n ? b0 + per : n;
-  unsigned long long sum = 0;
-  for (long long c = b0; c < b1; c += kPer) {
-    unsigned long long v[kPer];
+// In-place exclusive scans of a[0..n) and c[0..n) (n <= kMaxBuckets) by one
+// block, every load in flight at once; returns the totals.
+__device__ void scan_two(unsigned long long* a, unsigned long long* c, long long n, unsigned long long* ta,
+                         unsigned long long* tc) {
+  constexpr int kPer = kMaxBuckets / kScanThreads;
+  __shared__ unsigned long long s_w[2][kScanThreads / 64];
+  const long long b0 = (long long)threadIdx.x * kPer;
+  unsigned long long va[kPer], vc[kPer], sa = 0, sc = 0;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = c + k < b1 ? a[c + k] : 0ull;
+  for (int k = 0; k < kPer; ++k) {
+    va[k] = b0 + k < n ? a[b0 + k] : 0ull;
+    vc[k] = b0 + k < n ? c[b0 + k] : 0ull;
+  }
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) sum += v[k];
+  for (int k = 0; k < kPer; ++k) {
+    sa += va[k];
+    sc += vc[k];
   }
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  unsigned long long x = sum;
+  unsigned long long xa = sa, xc = sc;
   for (int d = 1; d < 64; d <<= 1) {
-    unsigned long long y = (unsigned long long)shfl64((long long)x, lane >= d ? lane - d : lane);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) s_w[wid] = x;
-  __syncthreads();
-  unsigned long long before = 0, all = 0;
-  for (int w = 0; w < kScanThreads / 64; ++w) {
-    if (w < wid) before += s_w[w];
-    all += s_w[w];
-  }
-  __syncthreads();
-  unsigned long long run = before + x - sum;
-  for (long long c = b0; c < b1; c += kPer) {
-    unsigned long long v[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = c + k < b1 ? a[c + k] : 0ull;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      if (c + k < b1) a[c + k] = run;
-      run += v[k];
+    const unsigned long long ya = (unsigned long long)shfl64((long long)xa, lane >= d ? lane - d : lane);
+    const unsigned long long yc = (unsigned long long)shfl64((long long)xc, lane >= d ? lane - d : lane);
+    if (lane >= d) {
+      xa += ya;
+      xc += yc;
     }
   }
-  return all;
+  if (lane == 63) {
+    s_w[0][wid] = xa;
+    s_w[1][wid] = xc;
+  }
+  __syncthreads();
+  unsigned long long ra = xa - sa, rc = xc - sc, alla = 0, allc = 0;
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    if (w < wid) {
+      ra += s_w[0][w];
+      rc += s_w[1][w];
+    }
+    alla += s_w[0][w];
+    allc += s_w[1][w];
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (b0 + k < n) {
+      a[b0 + k] = ra;
+      c[b0 + k] = rc;
+    }
+    ra += va[k];
+    rc += vc[k];
+  }
+  *ta = alla;
+  *tc = allc;
 }
 
 // One block: prefix sums of the buckets' (rows to allocate, keys inserted)
@@ -765,8 +777,8 @@ __device__ unsigned long long scan_tiles(unsigned long long* a, long long n) {
 __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, TableDev t) {
   const long long U = *L.res.num_unique;
   const long long nblk = L.N > 0 ? L.nbk : 0;  // per-bucket sums
-  const unsigned long long all = scan_tiles(L.blk_sums, nblk);
-  const unsigned long long all_long = scan_tiles(L.blk_long, nblk);
+  unsigned long long all, all_long;
+  scan_two(L.blk_sums, L.blk_long, nblk, &all, &all_long);
   if (threadIdx.x == 0) {
     const long long R = (long long)(all >> 32);
     const long long Fr = t.ctr->free_top > 0 ? t.ctr->free_top : 0;
