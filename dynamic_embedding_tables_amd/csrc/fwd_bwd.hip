@@ -39,7 +39,7 @@ template <>
 struct Vec<float> {
   static constexpr int E = 4;
   __device__ static void load(const void* p, float (&v)[4]) {
-    const float4 x = *reinterpret_cast<const float4*>(p);
+    const f32x4 x = *gread<f32x4>(p);
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
   }
   __device__ static void unpack(uint4 x, float (&v)[4]) {
@@ -47,7 +47,8 @@ struct Vec<float> {
     v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
   }
   __device__ static void store(void* p, const float (&v)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    const f32x4 x = {v[0], v[1], v[2], v[3]};
+    *gwrite<f32x4>(p) = x;
   }
 };
 struct bf16_t {
@@ -64,14 +65,18 @@ struct Vec<bf16_t> {
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
-  __device__ static void load(const void* p, float (&v)[8]) { unpack(*reinterpret_cast<const uint4*>(p), v); }
+  __device__ static void load(const void* p, float (&v)[8]) {
+    const u32x4 x = *gread<u32x4>(p);
+    unpack(make_uint4(x.x, x.y, x.z, x.w), v);
+  }
   __device__ static void store(void* p, const float (&v)[8]) {
     uint4 x;
     x.x = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
     x.y = (unsigned)f32_to_bf16(v[2]) | ((unsigned)f32_to_bf16(v[3]) << 16);
     x.z = (unsigned)f32_to_bf16(v[4]) | ((unsigned)f32_to_bf16(v[5]) << 16);
     x.w = (unsigned)f32_to_bf16(v[6]) | ((unsigned)f32_to_bf16(v[7]) << 16);
-    *reinterpret_cast<uint4*>(p) = x;
+    const u32x4 y = {x.x, x.y, x.z, x.w};
+    *gwrite<u32x4>(p) = y;
   }
 };
 
@@ -234,7 +239,8 @@ __global__ __launch_bounds__(256) void k_fwd_gather(FwdArgs a) {
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (r == kOccNoRow) {
   } else if (r >= 0) {
-    v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(r) + lane * 16);
+    const u32x4 x = *gread<u32x4>(reinterpret_cast<const char*>(r) + lane * 16);
+    v = make_uint4(x.x, x.y, x.z, x.w);
   } else {
     v = init_chunk(a.t, (long long)((unsigned long long)r & ~kOccPendingBit), lane);
   }

@@ -137,6 +137,22 @@ __device__ __forceinline__ char* row_ptr(const RowSpace& rs, long long r) {
   return rs.blocks[ri >> rs.lb] + (unsigned long long)(ri & (unsigned)rs.mb) * (unsigned)rs.stride;
 }
 
+// Global-memory views of pointers that were themselves loaded from memory
+// (row addresses, block bases): without the address space the compiler emits
+// FLAT accesses, which also count against the LDS wait counter, so every
+// wait for an LDS read would wait for the row traffic too.
+#define RECIS_GLOBAL __attribute__((address_space(1)))
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ const RECIS_GLOBAL T* gread(const void* p) {
+  return (const RECIS_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ RECIS_GLOBAL T* gwrite(void* p) {
+  return (RECIS_GLOBAL T*)p;
+}
+
 // Multiplicative (Fibonacci) hash of a key to a slot of a 2^k table; shift = 64 - k.
 __device__ __forceinline__ unsigned long long slot_of(long long key, int shift) {
   return ((unsigned long long)key * 0x9E3779B97F4A7C15ull) >> shift;

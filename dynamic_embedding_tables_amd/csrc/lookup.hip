@@ -166,7 +166,7 @@ __device__ __forceinline__ long long key_of(const LookupLaunch& L, FeatCursor& c
     c.lo = c.fd.base;
     c.hi = c.fd.base + c.fd.n;
   }
-  return transform_value(c.fd.values[j - c.fd.base], c.fd, L.bnd_pool, err);
+  return transform_value(*gread<long long>(c.fd.values + (j - c.fd.base)), c.fd, L.bnd_pool, err);
 }
 
 __global__ __launch_bounds__(kPartThreads) void k_part_hist(LookupLaunch L, TableDev t) {
