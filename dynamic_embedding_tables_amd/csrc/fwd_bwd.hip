@@ -46,9 +46,11 @@ struct Vec<float> {
     v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y);
     v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
   }
+  // Row stores are non-temporal: an updated row is not read again within the
+  // step, and streaming it past the caches keeps them for the reads.
   __device__ static void store(void* p, const float (&v)[4]) {
     const f32x4 x = {v[0], v[1], v[2], v[3]};
-    *gwrite<f32x4>(p) = x;
+    __builtin_nontemporal_store(x, gwrite<f32x4>(p));
   }
 };
 struct bf16_t {
@@ -76,7 +78,7 @@ struct Vec<bf16_t> {
     x.z = (unsigned)f32_to_bf16(v[4]) | ((unsigned)f32_to_bf16(v[5]) << 16);
     x.w = (unsigned)f32_to_bf16(v[6]) | ((unsigned)f32_to_bf16(v[7]) << 16);
     const u32x4 y = {x.x, x.y, x.z, x.w};
-    *gwrite<u32x4>(p) = y;
+    __builtin_nontemporal_store(y, gwrite<u32x4>(p));
   }
 };
 
