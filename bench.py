@@ -193,6 +193,8 @@ def _kernel_label(name):
     import re
     m = re.search(r"(k_[a-z_]+)", name)
     if m:
+        if m.group(1) == "k_bucket":  # the two launches of the bucket kernel
+            return "k_bucket_emit" if "true>" in name else "k_bucket_count"
         return m.group(1)
     if "copy" in name:
         return "copy"
