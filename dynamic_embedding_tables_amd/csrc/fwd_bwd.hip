@@ -38,6 +38,7 @@ struct Vec;
 template <>
 struct Vec<float> {
   static constexpr int E = 4;
+  static constexpr bool kBF16 = false;
   __device__ static void load(const void* p, float (&v)[4]) {
     const f32x4 x = *gread<f32x4>(p);
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
@@ -59,6 +60,7 @@ struct bf16_t {
 template <>
 struct Vec<bf16_t> {
   static constexpr int E = 8;
+  static constexpr bool kBF16 = true;
   __device__ static void unpack(uint4 x, float (&v)[8]) {
     const unsigned w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -165,58 +167,145 @@ __device__ __forceinline__ long long occurrence_ref(const FwdArgs& a, long long 
   return (long long)row_ptr(a.t.rs, r);
 }
 
-template <typename TP, int E>
-__device__ __forceinline__ void fetch_values(const TableDev& t, long long ref, int lane, float (&v)[E]) {
-  if (ref == kOccNoRow) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = 0.f;
-  } else if (ref >= 0) {
-    Vec<TP>::load(reinterpret_cast<const char*>(ref) + lane * 16, v);
+// Value of lane x of this lane's group of C lanes (x uniform).  A group of 16
+// is one DPP row: row_newbcast copies lane x of every row to the whole row in
+// one VALU move; other widths go through LDS (ds_bpermute).  A source lane
+// that is off yields `old`.
+template <int C>
+__device__ __forceinline__ int group_bcast(int v, int x, int gbase, int old) {
+  if constexpr (C == 16) {
+    switch (x) {
+      case 0: return __builtin_amdgcn_update_dpp(old, v, 0x150, 0xF, 0xF, false);
+      case 1: return __builtin_amdgcn_update_dpp(old, v, 0x151, 0xF, 0xF, false);
+      case 2: return __builtin_amdgcn_update_dpp(old, v, 0x152, 0xF, 0xF, false);
+      case 3: return __builtin_amdgcn_update_dpp(old, v, 0x153, 0xF, 0xF, false);
+      case 4: return __builtin_amdgcn_update_dpp(old, v, 0x154, 0xF, 0xF, false);
+      case 5: return __builtin_amdgcn_update_dpp(old, v, 0x155, 0xF, 0xF, false);
+      case 6: return __builtin_amdgcn_update_dpp(old, v, 0x156, 0xF, 0xF, false);
+      case 7: return __builtin_amdgcn_update_dpp(old, v, 0x157, 0xF, 0xF, false);
+      case 8: return __builtin_amdgcn_update_dpp(old, v, 0x158, 0xF, 0xF, false);
+      case 9: return __builtin_amdgcn_update_dpp(old, v, 0x159, 0xF, 0xF, false);
+      case 10: return __builtin_amdgcn_update_dpp(old, v, 0x15A, 0xF, 0xF, false);
+      case 11: return __builtin_amdgcn_update_dpp(old, v, 0x15B, 0xF, 0xF, false);
+      case 12: return __builtin_amdgcn_update_dpp(old, v, 0x15C, 0xF, 0xF, false);
+      case 13: return __builtin_amdgcn_update_dpp(old, v, 0x15D, 0xF, 0xF, false);
+      case 14: return __builtin_amdgcn_update_dpp(old, v, 0x15E, 0xF, 0xF, false);
+      default: return __builtin_amdgcn_update_dpp(old, v, 0x15F, 0xF, 0xF, false);
+    }
   } else {
-    Vec<TP>::unpack(init_chunk(t, (long long)((unsigned long long)ref & ~kOccPendingBit), lane), v);
+    return __shfl(v, gbase + x);
   }
 }
+template <int C>
+__device__ __forceinline__ long long group_bcast64(long long v, int x, int gbase, long long old) {
+  const int lo = group_bcast<C>((int)(unsigned long long)v, x, gbase, (int)(unsigned long long)old);
+  const int hi = group_bcast<C>((int)((unsigned long long)v >> 32), x, gbase, (int)((unsigned long long)old >> 32));
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
 
-// Pooling: a group of C = D / E lanes per bag.  The group reads the
-// references of up to C occurrences at once (one per lane), then broadcasts
-// them kFwdBatch at a time and keeps those rows' loads in flight together;
-// the sum runs in occurrence order.
+// Pooling: a group of C = D / E lanes per bag, GPW = 64 / C bags per wave.
+// Each round a group reads the references of its next C occurrences, one per
+// lane, and walks them BF at a time with those rows' loads in flight
+// together, summing in occurrence order.  Rows still pending (values = the
+// initializer's) are left out of the walk and queued per wave in LDS; as
+// soon as GPW are queued the wave computes them in one pass, one row per
+// group, and each row's group adds it.  The initializer then runs once per
+// GPW pending rows; run inside the walk it would cost the whole wave a pass
+// each time any one group met a pending row.  The order of the additions
+// depends only on the data, so runs repeat exactly.
 constexpr int kFwdBatch = 4;
 
 template <int D, typename TP>
 __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
   constexpr int E = Vec<TP>::E;
-  constexpr int C = D / E;  // lanes per bag
-  constexpr int GPB = 256 / C;
+  constexpr int C = D / E;      // lanes per bag
+  constexpr int GPW = 64 / C;   // bags per wave
+  constexpr int GPB = 256 / C;  // bags per block
   constexpr int BF = kFwdBatch < C ? kFwdBatch : C;
-  const int wl = threadIdx.x & 63;
-  const int lane = wl % C, gbase = wl - lane;
+  constexpr int QL = 128;       // queue ring (at most GPW - 1 + 64 entries wait)
+  __shared__ long long s_qkey[4][QL];
+  __shared__ unsigned char s_qown[4][QL];
+  __shared__ uint4 s_stage[4][GPW * C];
+  const int wid = threadIdx.x >> 6, wl = threadIdx.x & 63;
+  const int lane = wl % C, g = wl / C, gbase = wl - lane;
+  long long* qkey = s_qkey[wid];
+  unsigned char* qown = s_qown[wid];
+  uint4* stage = s_stage[wid];
+  // every lane stays to the end: the wave's broadcasts, ballots and passes
+  // need all of them; a group past the last bag has no occurrences
   const long long bag = (long long)blockIdx.x * GPB + threadIdx.x / C;
-  if (bag >= a.nbags) return;
-  long long lo = a.off[bag], hi = a.off[bag + 1];
-  lo = lo < 0 ? 0 : (lo > a.N ? a.N : lo);
-  hi = hi < lo ? lo : (hi > a.N ? a.N : hi);
+  long long lo = 0, hi = 0;
+  if (bag < a.nbags) {
+    lo = a.off[bag];
+    hi = a.off[bag + 1];
+    lo = lo < 0 ? 0 : (lo > a.N ? a.N : lo);
+    hi = hi < lo ? lo : (hi > a.N ? a.N : hi);
+  }
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (long long base = lo; base < hi; base += C) {
-    const int cnt = (int)(hi - base < C ? hi - base : C);
+  int qhead = 0, qlen = 0;  // uniform
+  // the first `take` queued rows: group g computes row g, then every row's
+  // group adds it, in queue order
+  auto pass = [&](int take) {
+    const long long key = qkey[(qhead + (g < take ? g : 0)) & (QL - 1)];
+    if (g < take) stage[g * C + lane] = init_chunk_as<Vec<TP>::kBF16>(a.t, key, lane);
+    for (int k = 0; k < take; ++k) {
+      if (qown[(qhead + k) & (QL - 1)] == g) {
+        float v[E];
+        Vec<TP>::unpack(stage[k * C + lane], v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += v[e];
+      }
+    }
+    qhead = (qhead + take) & (QL - 1);
+    qlen -= take;
+  };
+  for (long long base = lo;; base += C) {
+    const int cnt = (int)(hi - base < C ? (hi - base > 0 ? hi - base : 0) : C);
+    if (__ballot(cnt > 0) == 0) break;
     const long long ref = lane < cnt ? occurrence_ref(a, base + lane) : kOccNoRow;
-    // the group's lanes run the same trip counts, so every shuffle source
-    // (a lane of the same group) is active
-    for (int q = 0; q < cnt; q += BF) {
+    const bool pend = ref < 0;  // kOccPendingBit
+    const unsigned long long pm = __ballot(pend);
+    if (pend) {
+      const int at = (qhead + qlen +
+                      (int)__builtin_amdgcn_mbcnt_hi((unsigned)(pm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)pm, 0u))) &
+                     (QL - 1);
+      qkey[at] = (long long)((unsigned long long)ref & ~kOccPendingBit);
+      qown[at] = (unsigned char)g;
+    }
+    qlen += __popcll(pm);
+    while (qlen >= GPW) pass(GPW);
+    int cmax = cnt;
+#pragma unroll
+    for (int m = C; m < 64; m <<= 1) {
+      const int o = __shfl_xor(cmax, m);
+      cmax = o > cmax ? o : cmax;
+    }
+    cmax = __builtin_amdgcn_readfirstlane(cmax);
+#pragma unroll
+    for (int q = 0; q < C; q += BF) {  // unrolled: broadcast sources are constants
+      if (q >= cmax) break;
+      long long r[BF];
       float v[BF][E];
 #pragma unroll
       for (int x = 0; x < BF; ++x) {
-        const long long r = shfl64(ref, gbase + (q + x < cnt ? q + x : 0));
-        fetch_values<TP, E>(a.t, q + x < cnt ? r : kOccNoRow, lane, v[x]);
+        r[x] = group_bcast64<C>(ref, q + x, gbase, kOccNoRow);
+        if (q + x >= cnt) r[x] = kOccNoRow;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[x][e] = 0.f;
       }
+#pragma unroll
+      for (int x = 0; x < BF; ++x)
+        if (r[x] >= 0 && r[x] != kOccNoRow) Vec<TP>::load(reinterpret_cast<const char*>(r[x]) + lane * 16, v[x]);
 #pragma unroll
       for (int x = 0; x < BF; ++x)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] += v[x][e];
     }
   }
+  if (qlen > 0) pass(qlen);
+  if (bag >= a.nbags) return;
   if (a.pool == RECIS_POOL_MEAN && hi > lo) {
     const float len = (float)(hi - lo);
 #pragma unroll
@@ -244,7 +333,7 @@ __global__ __launch_bounds__(256) void k_fwd_gather(FwdArgs a) {
     const u32x4 x = *gread<u32x4>(reinterpret_cast<const char*>(r) + lane * 16);
     v = make_uint4(x.x, x.y, x.z, x.w);
   } else {
-    v = init_chunk(a.t, (long long)((unsigned long long)r & ~kOccPendingBit), lane);
+    v = init_chunk_as<Vec<TP>::kBF16>(a.t, (long long)((unsigned long long)r & ~kOccPendingBit), lane);
   }
   reinterpret_cast<uint4*>(static_cast<char*>(a.out) + (j * D * (long long)sizeof(TP)))[lane] = v;
 }
@@ -319,7 +408,7 @@ __device__ __forceinline__ void load_row(const BwdArgs& a, const char* rp, bool 
   if (pending) {
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
-      Vec<TP>::unpack(init_chunk(a.t, key, ch * KL + lane), w[ch]);
+      Vec<TP>::unpack(init_chunk_as<Vec<TP>::kBF16>(a.t, key, ch * KL + lane), w[ch]);
 #pragma unroll
       for (int e = 0; e < E; ++e) s0[ch][e] = s1[ch][e] = 0.f;
     }

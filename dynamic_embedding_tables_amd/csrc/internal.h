@@ -239,18 +239,25 @@ __device__ __forceinline__ unsigned long long next_slot(const TableDev& t, unsig
 }
 
 // Initial values of 16-byte parameter chunk c of the row of `key`, in the
-// storage format (4 fp32 or 8 bf16 elements).
-__device__ __forceinline__ uint4 init_chunk(const TableDev& t, long long key, int c) {
-  if (t.dtype == RECIS_DTYPE_BF16) {
+// storage format (4 fp32 or 8 bf16 elements).  Kernels built for one storage
+// type take the compile-time form: the other type's code would still count
+// toward their registers.
+template <bool BF16>
+__device__ __forceinline__ uint4 init_chunk_as(const TableDev& t, long long key, int c) {
+  if constexpr (BF16) {
     const float4 a = init4(t.seed, key, 2u * c, t.init_scale);
     const float4 b = init4(t.seed, key, 2u * c + 1u, t.init_scale);
     return make_uint4((unsigned)f32_to_bf16(a.x) | ((unsigned)f32_to_bf16(a.y) << 16),
                       (unsigned)f32_to_bf16(a.z) | ((unsigned)f32_to_bf16(a.w) << 16),
                       (unsigned)f32_to_bf16(b.x) | ((unsigned)f32_to_bf16(b.y) << 16),
                       (unsigned)f32_to_bf16(b.z) | ((unsigned)f32_to_bf16(b.w) << 16));
+  } else {
+    const float4 a = init4(t.seed, key, (unsigned)c, t.init_scale);
+    return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
   }
-  const float4 a = init4(t.seed, key, (unsigned)c, t.init_scale);
-  return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
+}
+__device__ __forceinline__ uint4 init_chunk(const TableDev& t, long long key, int c) {
+  return t.dtype == RECIS_DTYPE_BF16 ? init_chunk_as<true>(t, key, c) : init_chunk_as<false>(t, key, c);
 }
 
 // Instrumentation: launches of the kernel named `name` are bracketed by the

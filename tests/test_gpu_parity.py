@@ -218,6 +218,36 @@ def test_empty_batches_and_empty_bags():
     assert res.U() == 0 and table.get_error() == 0
 
 
+def _ragged_pool_batch(seed, B, dim, key_space, num_feats=2):
+    """Bag lengths that stress the pooled forward's occurrence runs: many
+    empty bags (a run of 100 of them, more than one 64-bag window), short
+    bags, bags longer than a run, and one bag spanning several runs."""
+    rng = W.rng_for(seed)
+    feats = []
+    for f in range(num_feats):
+        lens = rng.choice([0, 1, 2, 3, 5, 8, 13, 40], B, p=[0.2, 0.2, 0.15, 0.15, 0.1, 0.1, 0.06, 0.04])
+        lens[100:200] = 0
+        lens[300] = 400
+        lens[301:305] = 70
+        lens[-1] = 0
+        off = W.offsets_from_lengths(lens)
+        vals = rng.integers(0, key_space, int(off[-1]), dtype=np.int64)
+        feats.append(W.FeatureInput(values=vals, bag_offsets=off, slot=f + 1))
+    return W.Batch(feats, B, rng.standard_normal((B, num_feats * dim), dtype=np.float32))
+
+
+@pytest.mark.parametrize("dtype,dim,pool", [("f32", d, "mean") for d in (8, 16, 32, 64, 128, 256)]
+                         + [("f32", 64, "sum")]
+                         + [("bf16", d, p) for d in (8, 64, 256) for p in ("sum", "mean")])
+def test_pooled_forward_bag_shapes(dtype, dim, pool):
+    """Pooled forward over ragged bags, first with every row pending (the
+    initializer's values), then with stored and pending rows mixed."""
+    spec = W.TableSpec(dim=dim, dtype=dtype, optim="adagrad", pool=pool, lr=0.01)
+    a = _ragged_pool_batch(31, 700, dim, 3000)
+    b = _ragged_pool_batch(32, 700, dim, 6000)
+    run_parity(spec, [a, b])
+
+
 @pytest.mark.parametrize("optim", ["adam", "adagrad"])
 def test_interleaved_lookups(optim):
     """Lookup A, lookup B (sharing keys that are new in A), update A, then
