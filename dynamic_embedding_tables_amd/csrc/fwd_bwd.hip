@@ -204,47 +204,73 @@ __device__ __forceinline__ long long group_bcast64(long long v, int x, int gbase
 }
 
 // Pooling: a group of C = D / E lanes per bag, GPW = 64 / C bags per wave.
-// Each round a group reads the references of its next C occurrences, one per
-// lane, and walks them BF at a time with those rows' loads in flight
-// together, summing in occurrence order.  Rows still pending (values = the
-// initializer's) are left out of the walk and queued per wave in LDS; as
-// soon as GPW are queued the wave computes them in one pass, one row per
-// group, and each row's group adds it.  The initializer then runs once per
-// GPW pending rows; run inside the walk it would cost the whole wave a pass
-// each time any one group met a pending row.  The order of the additions
-// depends only on the data, so runs repeat exactly.
+// A block takes BB consecutive bags, ranks them by length in LDS and deals
+// them out in that order, GPB at a time (one per group), so the groups of a
+// wave walk bags of about the same length and few lanes idle while the
+// longest one finishes.  Each round a group reads the references of its
+// bag's next C occurrences, one per lane, and walks them BF at a time with
+// those rows' loads in flight together, summing in occurrence order.  Rows
+// still pending (values = the initializer's) are left out of the walk and
+// queued per wave in LDS; as soon as GPW are queued the wave computes them in
+// one pass, one row per group, and each row's group adds it.  The
+// initializer then runs once per GPW pending rows; run inside the walk it
+// would cost the whole wave a pass each time any one group met a pending
+// row.  The order of the additions depends only on the data, so runs repeat
+// exactly.
 constexpr int kFwdBatch = 4;
+
+template <int C>
+struct FwdShape {
+  static constexpr int GPW = 64 / C;                    // bags per wave at a time
+  static constexpr int GPB = 256 / C;                   // bags per block at a time
+  static constexpr int BB = GPB > 64 ? GPB : 64;        // bags per block
+  static constexpr int NSTEP = BB / GPB;                // bags per group
+};
 
 template <int D, typename TP>
 __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
   constexpr int E = Vec<TP>::E;
-  constexpr int C = D / E;      // lanes per bag
-  constexpr int GPW = 64 / C;   // bags per wave
-  constexpr int GPB = 256 / C;  // bags per block
+  constexpr int C = D / E;  // lanes per bag
+  using S = FwdShape<C>;
+  constexpr int GPW = S::GPW, GPB = S::GPB, BB = S::BB;
   constexpr int BF = kFwdBatch < C ? kFwdBatch : C;
-  constexpr int QL = 128;       // queue ring (at most GPW - 1 + 64 entries wait)
+  constexpr int QL = 128;  // queue ring (at most GPW - 1 + 64 entries wait)
+  __shared__ int s_lo[BB], s_len[BB];
+  __shared__ unsigned short s_order[BB];
   __shared__ long long s_qkey[4][QL];
   __shared__ unsigned char s_qown[4][QL];
   __shared__ uint4 s_stage[4][GPW * C];
-  const int wid = threadIdx.x >> 6, wl = threadIdx.x & 63;
+  const int tid = threadIdx.x, wid = tid >> 6, wl = tid & 63;
   const int lane = wl % C, g = wl / C, gbase = wl - lane;
   long long* qkey = s_qkey[wid];
   unsigned char* qown = s_qown[wid];
   uint4* stage = s_stage[wid];
-  // every lane stays to the end: the wave's broadcasts, ballots and passes
-  // need all of them; a group past the last bag has no occurrences
-  const long long bag = (long long)blockIdx.x * GPB + threadIdx.x / C;
-  long long lo = 0, hi = 0;
-  if (bag < a.nbags) {
-    lo = a.off[bag];
-    hi = a.off[bag + 1];
-    lo = lo < 0 ? 0 : (lo > a.N ? a.N : lo);
-    hi = hi < lo ? lo : (hi > a.N ? a.N : hi);
+  const long long b0 = (long long)blockIdx.x * BB;
+  for (int t = tid; t < BB; t += 256) {
+    const long long b = b0 + t;
+    long long lo = 0, hi = -1;  // past the last bag: length -1, ranked last
+    if (b < a.nbags) {
+      lo = a.off[b];
+      hi = a.off[b + 1];
+      lo = lo < 0 ? 0 : (lo > a.N ? a.N : lo);
+      hi = hi < lo ? lo : (hi > a.N ? a.N : hi);
+    }
+    s_lo[t] = (int)lo;
+    s_len[t] = (int)(hi - lo);
   }
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  __syncthreads();
+  for (int t = tid; t < BB; t += 256) {  // rank: longer first, then by index
+    const int L = s_len[t];
+    int rk = 0;
+    for (int k = 0; k < BB; ++k) {
+      const int Lk = s_len[k];
+      rk += (Lk > L || (Lk == L && k < t)) ? 1 : 0;
+    }
+    s_order[rk] = (unsigned short)t;
+  }
+  __syncthreads();
   int qhead = 0, qlen = 0;  // uniform
+  float acc[E];
   // the first `take` queued rows: group g computes row g, then every row's
   // group adds it, in queue order
   auto pass = [&](int take) {
@@ -261,61 +287,75 @@ __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
     qhead = (qhead + take) & (QL - 1);
     qlen -= take;
   };
-  for (long long base = lo;; base += C) {
-    const int cnt = (int)(hi - base < C ? (hi - base > 0 ? hi - base : 0) : C);
-    if (__ballot(cnt > 0) == 0) break;
-    const long long ref = lane < cnt ? occurrence_ref(a, base + lane) : kOccNoRow;
-    const bool pend = ref < 0;  // kOccPendingBit
-    const unsigned long long pm = __ballot(pend);
-    if (pend) {
-      const int at = (qhead + qlen +
-                      (int)__builtin_amdgcn_mbcnt_hi((unsigned)(pm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)pm, 0u))) &
-                     (QL - 1);
-      qkey[at] = (long long)((unsigned long long)ref & ~kOccPendingBit);
-      qown[at] = (unsigned char)g;
-    }
-    qlen += __popcll(pm);
-    while (qlen >= GPW) pass(GPW);
-    int cmax = cnt;
+  // every lane stays to the end: the wave's broadcasts, ballots and passes
+  // need all of them; a group without a bag has no occurrences
+  for (int st = 0; st < S::NSTEP; ++st) {
+    const int t = s_order[st * GPB + tid / C];
+    const long long bag = b0 + t;
+    const long long lo = s_lo[t];
+    const long long hi = lo + (s_len[t] > 0 ? s_len[t] : 0);
 #pragma unroll
-    for (int m = C; m < 64; m <<= 1) {
-      const int o = __shfl_xor(cmax, m);
-      cmax = o > cmax ? o : cmax;
-    }
-    cmax = __builtin_amdgcn_readfirstlane(cmax);
-#pragma unroll
-    for (int q = 0; q < C; q += BF) {  // unrolled: broadcast sources are constants
-      if (q >= cmax) break;
-      long long r[BF];
-      float v[BF][E];
-#pragma unroll
-      for (int x = 0; x < BF; ++x) {
-        r[x] = group_bcast64<C>(ref, q + x, gbase, kOccNoRow);
-        if (q + x >= cnt) r[x] = kOccNoRow;
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[x][e] = 0.f;
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (long long base = lo;; base += C) {
+      const int cnt = (int)(hi - base < C ? (hi - base > 0 ? hi - base : 0) : C);
+      if (__ballot(cnt > 0) == 0) break;
+      const long long ref = lane < cnt ? occurrence_ref(a, base + lane) : kOccNoRow;
+      const bool pend = ref < 0;  // kOccPendingBit
+      const unsigned long long pm = __ballot(pend);
+      if (pend) {
+        const int at =
+            (qhead + qlen +
+             (int)__builtin_amdgcn_mbcnt_hi((unsigned)(pm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)pm, 0u))) &
+            (QL - 1);
+        qkey[at] = (long long)((unsigned long long)ref & ~kOccPendingBit);
+        qown[at] = (unsigned char)g;
       }
+      qlen += __popcll(pm);
+      while (qlen >= GPW) pass(GPW);
+      int cmax = cnt;
 #pragma unroll
-      for (int x = 0; x < BF; ++x)
-        if (r[x] >= 0 && r[x] != kOccNoRow) Vec<TP>::load(reinterpret_cast<const char*>(r[x]) + lane * 16, v[x]);
+      for (int m = C; m < 64; m <<= 1) {
+        const int o = __shfl_xor(cmax, m);
+        cmax = o > cmax ? o : cmax;
+      }
+      cmax = __builtin_amdgcn_readfirstlane(cmax);
 #pragma unroll
-      for (int x = 0; x < BF; ++x)
+      for (int q = 0; q < C; q += BF) {  // unrolled: broadcast sources are constants
+        if (q >= cmax) break;
+        long long r[BF];
+        float v[BF][E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += v[x][e];
+        for (int x = 0; x < BF; ++x) {
+          r[x] = group_bcast64<C>(ref, q + x, gbase, kOccNoRow);
+          if (q + x >= cnt) r[x] = kOccNoRow;
+#pragma unroll
+          for (int e = 0; e < E; ++e) v[x][e] = 0.f;
+        }
+        // the loads write v only: a branch that also wrote v would have to
+        // wait for every load in flight
+#pragma unroll
+        for (int x = 0; x < BF; ++x)
+          if (r[x] >= 0 && r[x] != kOccNoRow) Vec<TP>::load(reinterpret_cast<const char*>(r[x]) + lane * 16, v[x]);
+#pragma unroll
+        for (int x = 0; x < BF; ++x)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] += v[x][e];
+      }
+    }
+    if (qlen > 0) pass(qlen);  // the bags change: settle the queue
+    if (bag < a.nbags) {
+      if (a.pool == RECIS_POOL_MEAN && hi > lo) {
+        const float len = (float)(hi - lo);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = acc[e] / len;
+      }
+      const int f = (int)(bag / a.B), i = (int)(bag - (long long)f * a.B);
+      float* o = static_cast<float*>(a.out) + ((long long)i * a.F + f) * D + lane * E;
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q)
+        reinterpret_cast<float4*>(o)[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
     }
   }
-  if (qlen > 0) pass(qlen);
-  if (bag >= a.nbags) return;
-  if (a.pool == RECIS_POOL_MEAN && hi > lo) {
-    const float len = (float)(hi - lo);
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = acc[e] / len;
-  }
-  const int f = (int)(bag / a.B), i = (int)(bag - (long long)f * a.B);
-  float* o = static_cast<float*>(a.out) + ((long long)i * a.F + f) * D + lane * E;
-#pragma unroll
-  for (int q = 0; q < E / 4; ++q)
-    reinterpret_cast<float4*>(o)[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
 }
 
 template <int D, typename TP>
@@ -854,7 +894,8 @@ void fwd_dispatch(const FwdArgs& a, int pool, hipStream_t s) {
     RECIS_LAUNCH("k_fwd_gather", (k_fwd_gather<D, TP>), dim3((unsigned)((a.N + GPB - 1) / GPB)), dim3(256), s, a);
   } else {
     if (a.nbags == 0) return;
-    RECIS_LAUNCH("k_fwd_pool", (k_fwd_pool<D, TP>), dim3((unsigned)((a.nbags + GPB - 1) / GPB)), dim3(256), s, a);
+    constexpr int BB = FwdShape<C>::BB;
+    RECIS_LAUNCH("k_fwd_pool", (k_fwd_pool<D, TP>), dim3((unsigned)((a.nbags + BB - 1) / BB)), dim3(256), s, a);
   }
 }
 
