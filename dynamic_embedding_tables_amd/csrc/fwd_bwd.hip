@@ -401,7 +401,7 @@ struct BwdArgs {
 constexpr int kBwdKeys = kThreads;  // distinct keys per block tile (short path)
 constexpr int kBwdStage = 1024;     // gradient entries staged in LDS per tile
 #ifndef RECIS_BWD_LANES
-#define RECIS_BWD_LANES 16
+#define RECIS_BWD_LANES 64
 #endif
 constexpr int kBwdLanes = RECIS_BWD_LANES;  // lanes per key in the short path (at most)
 #ifndef RECIS_BWD_BATCH
@@ -721,8 +721,15 @@ __device__ __forceinline__ void stage_key(const BwdArgs& a, int q, int nact, int
 // the initializer.  Phase 2: the keys' gradient references, staged in LDS
 // when they fit.  Phase 3: each group of KL lanes walks its keys, the row and
 // gradient loads of a key in flight together.
+// With one chunk per lane, fp32 rows fit 80 registers without spilling: ask
+// for six waves per SIMD there (one more than the allocator picks by itself).
+template <int D, typename TP>
+constexpr int bwd_short_waves() {
+  return Vec<TP>::E == 4 && D <= 64 * Vec<TP>::E ? 6 : 1;
+}
+
 template <int D, typename TP, int OPT, int KL>
-__global__ __launch_bounds__(256) void k_bwd_short(BwdArgs a) {
+__global__ __launch_bounds__(256, (bwd_short_waves<D, TP>())) void k_bwd_short(BwdArgs a) {
   constexpr int E = Vec<TP>::E, CH = RowMap<D, TP, KL>::CH;
   constexpr int GPB = 256 / KL;
   constexpr int GB = CH * E >= kBwdBatchElems ? 1 : kBwdBatchElems / (CH * E);  // gradient rows per batch
