@@ -8,11 +8,12 @@
 //   next to the parameters in the EmbeddingBlocks.
 //
 // Work layout: a row is split into 16-byte chunks (4 fp32 or 8 bf16
-// elements); a "group" of C = row_bytes / 16 lanes of one 64-lane wavefront
-// owns one bag (forward) or one distinct key (backward), so a wave moves
-// 64 / C rows per instruction with full 16-byte loads.  A group first fetches
-// the indices of up to C occurrences at once (one lane each), then walks them
-// with cross-lane broadcasts, so up to C row loads are in flight per group.
+// elements); a "group" of lanes of one 64-lane wavefront owns one bag
+// (forward, C = row_bytes / 16 lanes) or one distinct key (backward, one
+// chunk per lane), so a wave moves whole rows with full 16-byte loads.  A
+// forward group fetches the references of up to C occurrences at once (one
+// lane each), then walks them with cross-lane broadcasts, several row loads
+// in flight per group.
 //
 // Rows allocated by insert_find stay pending until their first update: their
 // values are the initializer's, recomputed here from (seed, key) instead of
