@@ -1,21 +1,29 @@
 #!/usr/bin/env python3
 """Throughput of the dynamic-embedding hot path on one MI355X.
 
-Workload: the CTR ranking batch -- 26 sparse features merged into one logical
-table (dim 64, fp32 parameters, sparse Adam with two fp32 moments per row),
-batch 8192, bag lengths Zipf(1.05) truncated to 1..50, raw IDs Zipf(1.05)
-over 2^40 through the fused Hash + Mod(1e8) transform, mean pooling, with
-about 20M resident rows.  The table is filled by running full steps from
-empty until 20M rows are resident; then W warm-up steps; then K timed steps.
+Default workload (--workload ctr): the CTR ranking batch -- 26 sparse
+features merged into one logical table (dim 64, fp32 parameters, sparse Adam
+with two fp32 moments per row), batch 8192, bag lengths Zipf(1.05) truncated
+to 1..50, raw IDs Zipf(1.05) over 2^40 through the fused Hash + Mod(1e8)
+transform, mean pooling, with about 20M resident rows.  The table is filled
+by running full steps from empty until 20M rows are resident; then W warm-up
+steps; then K timed steps.
+
+--workload seq: the lifelong behaviour sequence (1 feature, length 1000,
+batch 2048, dim 128 bf16 storage, gather only, bf16 gradients, Adagrad),
+10 full steps from empty before the warm-up.  --workload capacity: the
+capacity stress (200M pre-populated rows of dim 64 fp32 + Adam, 100 features,
+batch 65536, Poisson(8) bags, 2% novel IDs, sum pooling).
 
 A step is one pass of the whole path through the C ABI: insert_find
 (transform, dedup, IDMap insert / find) -> lookup_pool_fwd -> pool_bwd_update
-(duplicate-gradient reduce + Adam).  Inputs (IDs, bag offsets, upstream
+(duplicate-gradient reduce + optimizer).  Inputs (IDs, bag offsets, upstream
 gradients) are resident in HBM before the timed region starts.
 
 Prints one JSON line: IDs/s over the timed steps, the roofline of the
 dominant kernel (algorithmic bytes per launch / its mean duration from HIP
-events on the launch stream), and the CPU oracle timed on a bounded sample.
+events on the launch stream), and (CTR) the CPU oracle timed on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -39,14 +47,51 @@ HBM_PEAK_GBS = 8000.0
 RESIDENT_TARGET = 20_000_000
 
 
-def _gen(step):
-    b = W.ctr_batch(step)
+# The workloads: table spec, shape, how the table is filled before the
+# warm-up, default step counts, and the kernels the warm-up times to find the
+# dominant one.
+WORKLOADS = {
+    "ctr": {
+        "title": "CTR ranking batch: 26 features merged, dim 64 fp32, batch 8192, Zipf(1.05) bag lengths "
+                 "1..50 and IDs over 2^40, Hash+Mod(1e8), mean pooling, sparse Adam, ~20M resident rows",
+        "spec": W.spec_ctr, "F": 26, "B": 8192, "fill": "resident", "steps": 20, "warmup": 5,
+        "new_per_step": 1_000_000,
+        "table": {"slot_capacity": 1 << 27, "block_rows": 1 << 20},
+        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bucket_count"),
+    },
+    "seq": {
+        "title": "Lifelong behaviour sequence: 1 feature of length 1000, batch 2048, dim 128 bf16 storage "
+                 "(fp32 accumulate), Zipf(1.2) IDs over 1e8 items, gather only (output [2048,1000,128] "
+                 "bf16), bf16 gradients, Adagrad; 10 steps from empty before the warm-up",
+        "spec": W.spec_seq, "F": 1, "B": 2048, "fill": "steps", "fill_steps": 10, "steps": 20, "warmup": 5,
+        "new_per_step": 250_000,
+        "table": {"slot_capacity": 1 << 23, "block_rows": 1 << 20},
+        "candidates": ("k_bwd_short", "k_fwd_gather", "k_bwd_long_partial", "k_bucket_emit", "k_part_scatter"),
+    },
+    "capacity": {
+        "title": "Capacity stress: 200M pre-populated rows x dim 64 fp32 + Adam m/v, 100 features, batch 65536, "
+                 "bag length Poisson(8), Zipf(1.2) IDs with 2% novel per step, sum pooling",
+        "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 3,
+        # 1.68 GB per gradient: one N(0,1) draw serves every step
+        "shared_grad": True,
+        "table": {"slot_capacity": 1 << 29, "block_rows": 1 << 20},
+        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit"),
+    },
+}
+
+
+def _gen(arg):
+    name, step = arg
+    fn = {"ctr": W.ctr_batch, "seq": W.seq_batch, "capacity": W.capacity_batch}[name]
+    b = fn(step, grad=False)
     return [(f.values, f.bag_offsets, f.slot, f.ops, f.mod) for f in b.features], b.batch
 
 
-def gen_batches(steps, workers):
+def gen_batches(name, steps, workers):
     with ProcessPoolExecutor(max_workers=workers) as ex:
-        return list(ex.map(_gen, steps))
+        return list(ex.map(_gen, [(name, s) for s in steps]))
+
+
 
 
 def host_info():
@@ -87,8 +132,6 @@ def cpu_baseline(seconds_budget=20.0):
                       f"{t_total:.1f} s"}
 
 
-# kernels the warm-up steps time, one per step, to pick the dominant one
-CANDIDATE_KERNELS = ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bucket_count")
 COPY_BYTES = 1 << 30
 
 
@@ -132,29 +175,35 @@ def step_shapes(results, U, resident0):
 SHORT_MAX = 64   # occurrences up to which the backward treats a key as short
 
 
-def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D):
-    """Bytes the method must move, per launch / per step (fp32 params s = 4,
-    Adam S = 2 state words per element; P = D s + S D 4 = 768 B per row).
+def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=True):
+    """Bytes the method must move, per launch / per step (s = parameter bytes,
+    S = fp32 state words per element, gs = gradient bytes; P = D s + S D 4
+    bytes per row: 768 for the CTR and capacity tables).
       k_bwd_short: per short key 16 (count, group offset, row) + its grouped
         entries 4 each; resident rows read and written 2P, new rows written P;
-        the upstream gradient Bg D 4 once.
+        the upstream gradient, Bg D gs once when pooled, else one row per entry.
       k_fwd_pool: per occurrence its row reference 8; offsets 4 (Bg + 1);
         resident rows' params D s; the output Bg D 4.
+      k_fwd_gather: per occurrence its row reference 8 and its output row D s;
+        resident rows' params D s.
       k_key_probe: per distinct key its key and count 12, the IDMap slot 16,
         its row and slot index 12; per new key the slot written 16.
       step: insert_find 12 N + 4 (Bg + 1) + 32 U + 16 U_new, forward
-        4 N + 8 U + U_hit D s + Bg D 4, backward 4 N + 8 U + U_hit 2P + U_new P
-        + Bg D 4."""
-    s, S = 4, 2
+        4 N + 8 U + U_hit D s + output, backward 4 N + 8 U + U_hit 2P
+        + U_new P + gradient; output and gradient Bg D 4 each when pooled,
+        N D s and N D gs when not."""
     P = D * s + S * D * 4
     Us, Usn = shape["U_s"], shape["U_s_new"]
-    bwd_short = 16 * Us + 4 * shape["E_s"] + (Us - Usn) * 2 * P + Usn * P + Bg * D * 4
+    g_short = Bg * D * gs if pooled else shape["E_s"] * D * gs
+    bwd_short = 16 * Us + 4 * shape["E_s"] + (Us - Usn) * 2 * P + Usn * P + g_short
     fwd = 8 * N + 4 * (Bg + 1) + Uhit * D * s + Bg * D * 4
+    gather = 8 * N + Uhit * D * s + N * D * s
     probe = 40 * Um + 16 * Unew
+    out_b, grad_b = (Bg * D * 4, Bg * D * 4) if pooled else (N * D * s, N * D * gs)
     ins = 12 * N + 4 * (Bg + 1) + 32 * Um + 16 * Unew
-    fwd_call = 4 * N + 8 * Um + Uhit * D * s + Bg * D * 4
-    bwd_call = 4 * N + 8 * Um + Uhit * 2 * P + Unew * P + Bg * D * 4
-    return {"k_bwd_short": bwd_short, "k_fwd_pool": fwd, "k_key_probe": probe,
+    fwd_call = 4 * N + 8 * Um + Uhit * D * s + out_b
+    bwd_call = 4 * N + 8 * Um + Uhit * 2 * P + Unew * P + grad_b
+    return {"k_bwd_short": bwd_short, "k_fwd_pool": fwd, "k_fwd_gather": gather, "k_key_probe": probe,
             "step": ins + fwd_call + bwd_call}
 
 
@@ -168,12 +217,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel):
+def read_traffic(kernel, workload="ctr"):
     """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/<kernel>_ctr_counters.txt: FETCH_SIZE / WRITE_SIZE in KiB per
-    dispatch, scaled by the copy-kernel factors), or None when there is none or
-    the kernel sources changed since the counters were taken."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_ctr_counters.txt")
+    (profiles/<kernel>_<workload>_counters.txt: FETCH_SIZE / WRITE_SIZE in KiB
+    per dispatch, scaled by the copy-kernel factors), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(p):
         return None
     kv = {}
@@ -201,7 +250,7 @@ def _kernel_label(name):
     return name[:60]
 
 
-def summarize(prof_dir, kernel, command, out_path):
+def summarize(prof_dir, kernel, command, out_path, workload="ctr"):
     """Writes the committed summary of a profiled bench run: per-kernel mean
     durations (rocprofv3 --kernel-trace --stats, csv) from prof_dir/trace, and
     for `kernel` the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch, from
@@ -209,8 +258,7 @@ def summarize(prof_dir, kernel, command, out_path):
     plain copies of COPY_BYTES that --copy-calibration runs."""
     import csv
     stats = list(csv.DictReader(open(os.path.join(prof_dir, "trace", "p_kernel_stats.csv"))))
-    lines = [f"# rocprofv3 summary: {kernel} on the CTR workload (26 features merged, batch 8192,",
-             "# dim 64 fp32, Hash+Mod, mean pooling, sparse Adam, ~20M resident rows)",
+    lines = [f"# rocprofv3 summary: {kernel} on the workload: {WORKLOADS[workload]['title']}",
              f"# command: {command}", f"kernel={kernel}", f"source_hash={kernel_source_hash()}"]
     dur = {}
     for r in stats:
@@ -255,9 +303,10 @@ def summarize(prof_dir, kernel, command, out_path):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--resident", type=int, default=RESIDENT_TARGET)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="ctr")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: the workload's)")
+    ap.add_argument("--resident", type=int, default=RESIDENT_TARGET, help="CTR: rows resident before warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workers", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -268,64 +317,107 @@ def main():
     ap.add_argument("--command", default="")
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
+    wl = WORKLOADS[args.workload]
     if args.summarize:
         summarize(args.summarize, args.kernel, args.command,
-                  args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_ctr_counters.txt"))
+                  args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{args.workload}_counters.txt"),
+                  args.workload)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
-    K, Wm = args.steps, args.warmup
+    K = args.steps if args.steps is not None else wl["steps"]
+    Wm = args.warmup if args.warmup is not None else wl["warmup"]
+    spec = wl["spec"]()
+    F, B, D = wl["F"], wl["B"], spec.dim
+    pooled = spec.pool != "none"
+    s_bytes = 2 if spec.dtype == "bf16" else 4
+    S = {"adam": 2, "adagrad": 1}[spec.optim]
+    gs = 2 if spec.grad_dtype == "bf16" else 4
     # ---- inputs: generate before the GPU is touched (process pool)
     t_gen = time.perf_counter()
-    prefill_steps = int(np.ceil(args.resident / 850_000)) + 4
-    all_steps = list(range(prefill_steps + Wm + K))
-    batches = gen_batches(all_steps, args.workers)
+    if wl["fill"] == "resident":
+        fill_steps = int(np.ceil(args.resident / 850_000)) + 4
+    elif wl["fill"] == "steps":
+        fill_steps = wl["fill_steps"]
+    else:
+        fill_steps = 0
+    batches = gen_batches(args.workload, list(range(fill_steps + Wm + K)), args.workers)
+    resident_keys = list(W.capacity_resident_keys()) if wl["fill"] == "keys" else []
     t_gen = time.perf_counter() - t_gen
-    print(f"[bench] generated {len(batches)} batches in {t_gen:.1f}s", file=sys.stderr, flush=True)
+    print(f"[bench] {args.workload}: generated {len(batches)} batches in {t_gen:.1f}s", file=sys.stderr, flush=True)
 
     import torch
     from dynamic_embedding_tables_amd import recis
     recis.load_library()
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    spec = W.spec_ctr()
-    F, B, D = 26, 8192, spec.dim
+    cap = max(sum(v.shape[0] for (v, *_r) in b[0]) for b in batches)
+    pre_rows = sum(k.shape[0] for _, k in resident_keys)
+    if wl["fill"] == "keys":  # a call may add up to its N rows; 2% of N are new per step
+        reserve = pre_rows + cap + (Wm + K + 1) * (cap // 30)
+    else:
+        reserve = (args.resident if wl["fill"] == "resident" else 0) + (fill_steps + Wm + K + 2) * wl["new_per_step"]
     table = recis.Table(D, spec.dtype, spec.optim, seed=spec.seed, init_bound=spec.init_bound,
-                        slot_capacity=1 << 27, block_rows=1 << 20,
-                        reserve_rows=args.resident + (prefill_steps + Wm + K) * 1_000_000)
+                        admit_threshold=spec.admit_threshold, reserve_rows=reserve, **wl["table"])
     gen = torch.Generator(device=dev)
     gen.manual_seed(20250925)
+    pdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    gdt = torch.bfloat16 if spec.grad_dtype == "bf16" else torch.float32
+    flags = 0 if pooled else recis.RECIS_GROUP_BY_OCCURRENCE
+
+    shared = {}
 
     def upload(batch):
         feats, bsz = batch
-        dfs = [recis.DeviceFeature(torch.from_numpy(v).to(dev), torch.from_numpy(o).to(dev), s, ops, mod)
-               for (v, o, s, ops, mod) in feats]
+        dfs = [recis.DeviceFeature(torch.from_numpy(v).to(dev), torch.from_numpy(o).to(dev), sl, ops, mod)
+               for (v, o, sl, ops, mod) in feats]
         n = sum(f.n for f in dfs)
-        grad = torch.randn(bsz, F * D, device=dev, generator=gen, dtype=torch.float32)
+        shape = (bsz, F * D) if pooled else (n, D)
+        if wl.get("shared_grad") and "g" in shared:
+            grad = shared["g"]
+        else:
+            grad = torch.randn(*shape, device=dev, generator=gen, dtype=torch.float32).to(gdt)
+            shared["g"] = grad
         return dfs, recis.make_descs(dfs), n, grad
 
-    out = torch.empty(B, F * D, device=dev, dtype=torch.float32)
-    cap = max(sum(v.shape[0] for (v, *_r) in b[0]) for b in batches)
+    out = torch.empty(B, F * D, device=dev, dtype=torch.float32) if pooled else \
+        torch.empty(cap, D, device=dev, dtype=pdt)
     res_pool = [recis.LookupResult(cap, F * B) for _ in range(2)]
 
-    def step(dfs, descs, grad, res):
-        table.insert_find(dfs, B, res, descs=descs)
-        table.forward(res, "mean", out)
-        table.backward_update(res, "mean", grad, "f32", lr=spec.lr, beta1=spec.beta1, beta2=spec.beta2,
-                              eps=spec.eps)
+    def fwd(res):
+        table.forward(res, spec.pool, out)
 
-    # ---- prefill to the resident target (untimed, full steps)
+    def bwd(res, grad):
+        table.backward_update(res, spec.pool, grad, spec.grad_dtype, lr=spec.lr, beta1=spec.beta1,
+                              beta2=spec.beta2, eps=spec.eps)
+
+    def step(dfs, descs, grad, res):
+        table.insert_find(dfs, B, res, flags=flags, descs=descs)
+        fwd(res)
+        bwd(res, grad)
+
+    # ---- fill the table (untimed)
     i = 0
-    while True:
-        dfs, descs, n, grad = upload(batches[i])
-        step(dfs, descs, grad, res_pool[i % 2])
-        i += 1
-        if table.stats().rows_in_use >= args.resident or i >= prefill_steps:
-            break
+    if wl["fill"] == "keys":  # pre-populate: each feature's resident IDs, one per bag
+        for f, keys in resident_keys:
+            kd = torch.from_numpy(keys).to(dev)
+            od = torch.arange(keys.shape[0] + 1, dtype=torch.int32, device=dev)
+            r = recis.LookupResult(keys.shape[0], keys.shape[0])
+            table.insert_find([recis.DeviceFeature(kd, od, f)], keys.shape[0], r)
+            del r, kd, od
+        torch.cuda.synchronize()
+        table.check()
+    else:
+        while i < fill_steps:
+            dfs, descs, n, grad = upload(batches[i])
+            step(dfs, descs, grad, res_pool[i % 2])
+            i += 1
+            if wl["fill"] == "resident" and table.stats().rows_in_use >= args.resident:
+                break
     resident0 = table.stats().rows_in_use
-    print(f"[bench] prefill: {i} steps, {resident0} resident rows", file=sys.stderr, flush=True)
+    print(f"[bench] fill: {i} steps, {resident0} resident rows", file=sys.stderr, flush=True)
 
     # ---- stage warm-up + timed inputs in HBM
     staged = [upload(batches[j]) for j in range(i, i + Wm + K)]
@@ -340,10 +432,11 @@ def main():
 
     # warm-up; each warm-up step also times one candidate kernel, to find the
     # dominant one (the kernel with the longest launch)
+    cands = wl["candidates"]
     probe_ms = {}
     for w in range(Wm):
         dfs, descs, n, grad = staged[w]
-        name = CANDIDATE_KERNELS[w % len(CANDIDATE_KERNELS)]
+        name = cands[w % len(cands)]
         a, b = event_pair()
         table.profile_kernel(name, a, b)
         step(dfs, descs, grad, res_pool[w % 2])
@@ -364,12 +457,11 @@ def main():
         e = ev[k]
         table.profile_kernel(dom, *kev[k])
         e[0].record(stream)
-        table.insert_find(dfs, B, res, descs=descs)
+        table.insert_find(dfs, B, res, flags=flags, descs=descs)
         e[1].record(stream)
-        table.forward(res, "mean", out)
+        fwd(res)
         e[2].record(stream)
-        table.backward_update(res, "mean", grad, "f32", lr=spec.lr, beta1=spec.beta1, beta2=spec.beta2,
-                              eps=spec.eps)
+        bwd(res, grad)
         e[3].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -386,6 +478,7 @@ def main():
     t_ins = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
     t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    t_steps = [e[0].elapsed_time(e[3]) for e in ev]
 
     # Measured shape of each timed step: N, U, and per distinct key its count and
     # whether its row is new (allocated in this step: no eviction runs here, so a
@@ -397,11 +490,11 @@ def main():
     Uhit = Um - Unew
     Bg = F * B
     shape = step_shapes(timed_res, U, int(st0.rows_in_use))
-    alg = algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D)
+    alg = algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s_bytes, S, gs, pooled)
     a_bytes = alg[dom] if dom in alg else None
     achieved = a_bytes / t_dom / 1e9 if a_bytes else None
     step_bytes = alg["step"]
-    traffic = read_traffic(dom)
+    traffic = read_traffic(dom, args.workload)
 
     result = {
         "metric": "lookup+pool+update IDs/sec and achieved HBM GB/s vs peak, 1xMI355X",
@@ -417,16 +510,15 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "CTR ranking batch: 26 features merged, dim 64 fp32, batch 8192, "
-                        "Zipf(1.05) bag lengths 1..50 and IDs over 2^40, Hash+Mod(1e8), mean pooling, "
-                        "sparse Adam, ~20M resident rows",
-            "global_batch": B, "num_features": F, "dim": D,
+            "workload": wl["title"],
+            "global_batch": B, "num_features": F, "dim": D, "storage": spec.dtype,
             "ids_per_step": N, "unique_per_step": Um, "new_rows_per_step": Unew,
             "resident_rows_start": int(st0.rows_in_use), "resident_rows_end": int(st1.rows_in_use),
             "parallelism": "single GPU",
         },
         "step_breakdown_ms": {"insert_find": t_ins * 1e3, "lookup_pool_fwd": t_fwd * 1e3,
                               "pool_bwd_update": t_bwd * 1e3},
+        "step_ms_median_p90": [float(np.median(t_steps)), float(np.percentile(t_steps, 90))],
         "step_algorithmic_bytes": step_bytes,
         "step_achieved_GBps": step_bytes / (elapsed / K) / 1e9,
         "roofline": {"bound": "hbm", "kernel": dom, "kernel_ms": t_dom * 1e3,
@@ -436,7 +528,7 @@ def main():
         "warmup_kernel_ms": {k: float(np.mean(v)) for k, v in probe_ms.items()},
         "backward_key_split": shape,
     }
-    if not args.no_cpu_baseline:
+    if args.workload == "ctr" and not args.no_cpu_baseline:
         table.close()
         torch.cuda.synchronize()
         result["cpu_baseline"] = cpu_baseline()

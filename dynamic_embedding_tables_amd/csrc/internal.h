@@ -352,6 +352,12 @@ constexpr int kMaxBucketBits = 13;
 constexpr int kMaxBuckets = 1 << kMaxBucketBits;
 constexpr int kBagWin = 4096;        // merged bag offsets a partition block keeps in LDS
 constexpr int kBucketPer = 4;        // occurrences per thread per pass of k_bucket
+// A bucket of more than kHeavyOcc occurrences (a hot key's bucket) is cut into
+// slices of kSliceOcc (at most 3/4 of the smaller LDS table, so a slice never
+// overflows it), each deduplicated by its own block.
+constexpr int kHeavyOcc = 16384;
+constexpr int kSliceOcc = 768;
+constexpr int kHeavyBlocks = 1024;  // blocks that share out the heavy slices
 
 struct LookupLaunch {
   const FeatDev* feats;
@@ -371,6 +377,9 @@ struct LookupLaunch {
   PartEntry* part;            // N
   unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
   unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
+  int* klist;                    // N: heavy buckets' distinct keys (dedup-table slots), by bucket range
+  int* hslice;                   // heavy slices: count, then (bucket, slice) pairs
+  long long hmax;                // bound on the heavy slices of the call (their grids)
 };
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);
 

@@ -10,9 +10,10 @@
 //
 // Kernel sequence of one call (all on one stream, no host read-back):
 //   k_prep      merged bag offsets, offset validation, per-call counters
-//   k_part_hist / k_part_colscan / k_scan_small / k_part_scatter
+//   k_part_hist / k_part_colscan / k_bucket_plan / k_part_scatter
 //               transform + tag every occurrence and partition the call by
-//               the top bits of the key's hash (one radix-sort pass)
+//               the top bits of the key's hash (one radix-sort pass); the
+//               plan also cuts heavy buckets (hot keys) into slices
 //   k_bucket    one bucket per block, twice around a scan of the per-bucket
 //               distinct counts: dedup in LDS, counts, distinct-key indices,
 //               group offsets; in the second launch also the IDMap probe /
@@ -21,8 +22,9 @@
 //               regions), then each occurrence's inverse index, grouped bag /
 //               occurrence entry and forward reference (a bucket that
 //               overflows the LDS table, from colliding inputs, uses a global
-//               one)
-//   k_key_scan  one block: exclusive scan of the per-bucket sums; rows come
+//               one; a heavy bucket is counted slice by slice and its
+//               occurrences are written by k_key_scan's other blocks)
+//   k_key_scan  block 0: exclusive scan of the per-bucket sums; rows come
 //               from the free list first, then from the bump pointer -- by
 //               prefix sum, not by atomics
 //   k_key_finalize  per bucket: row assignment (the new row is marked
@@ -65,6 +67,33 @@ __device__ unsigned long long block_exclusive_scan(unsigned long long v, unsigne
   __syncthreads();
   *total = all;
   return before + x - v;
+}
+
+// Adds 1 to a[h] for every lane with `act`, returning the value a[h] had
+// before this lane's add (lanes of one index get consecutive values).  The
+// index of the first active lane is served by one atomic for all the lanes
+// that share it: a hot key fills most lanes of a wave, and thousands of LDS
+// atomics on one address would queue.  Call with the whole wave converged.
+__device__ __forceinline__ int lds_add1(int* a, unsigned h, bool act) {
+  const unsigned long long am = __ballot(act);
+  int res = 0;
+  if (am) {
+    const int lead = __ffsll((long long)am) - 1;
+    const unsigned hl = (unsigned)__builtin_amdgcn_readlane((int)h, lead);
+    const unsigned long long same = __ballot(act && h == hl);
+    if (__popcll(same) > 1) {
+      int base = 0;
+      if ((int)(threadIdx.x & 63) == lead) base = atomicAdd(&a[hl], __popcll(same));
+      base = __builtin_amdgcn_readlane(base, lead);
+      if (act && h == hl) {
+        res = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(same >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((unsigned)same, 0u));
+        act = false;
+      }
+    }
+  }
+  if (act) res = atomicAdd(&a[h], 1);
+  return res;
 }
 
 // Hash -> Mod, or Bucketize, then the feature tag.
@@ -269,6 +298,71 @@ __global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long
   if (tid == 0) {
     a[n] = all;
     if (total_ll) *total_ll = all;
+  }
+}
+
+// Exclusive scan of one int per thread over a block of kPartThreads.
+__device__ __forceinline__ int block_scan_part(int x, int* total) {
+  __shared__ int s_w[kPartThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int y = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int z = __shfl(y, lane >= d ? lane - d : lane);
+    if (lane >= d) y += z;
+  }
+  if (lane == 63) s_w[w] = y;
+  __syncthreads();
+  int run = y - x, all = 0;
+#pragma unroll
+  for (int q = 0; q < kPartThreads / 64; ++q) {
+    run += q < w ? s_w[q] : 0;
+    all += s_w[q];
+  }
+  __syncthreads();
+  *total = all;
+  return run;
+}
+
+// One block: bucket positions from the bucket sizes (bbase, as k_scan_small),
+// and the heavy buckets' slices -- a bucket of m > kHeavyOcc occurrences gets
+// ceil(m / kSliceOcc) of them, listed as (bucket, slice) pairs after their
+// count.  Zeroes every bucket's distinct count: a heavy bucket's slices add to
+// it, a light bucket's block writes it.
+__global__ __launch_bounds__(kPartThreads) void k_bucket_plan(LookupLaunch L) {
+  constexpr int kPer = kMaxBuckets / kPartThreads;
+  const int n = L.nbk;
+  int* a = L.bbase;
+  const int b0 = threadIdx.x * kPer;
+  int v[kPer], ns[kPer];
+  int sum = 0, hs = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = b0 + k < n ? a[b0 + k] : 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    ns[k] = v[k] > kHeavyOcc ? (v[k] + kSliceOcc - 1) / kSliceOcc : 0;
+    sum += v[k];
+    hs += ns[k];
+  }
+  int all, hall;
+  int run = block_scan_part(sum, &all);
+  int hrun = block_scan_part(hs, &hall);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (b0 + k < n) {
+      a[b0 + k] = run;
+      L.ubase[b0 + k] = 0;
+      for (int q = 0; q < ns[k]; ++q) {
+        L.hslice[1 + 2 * (hrun + q)] = b0 + k;
+        L.hslice[2 + 2 * (hrun + q)] = q;
+      }
+    }
+    run += v[k];
+    hrun += ns[k];
+  }
+  if (threadIdx.x == 0) {
+    a[n] = all;
+    L.hslice[0] = hall;
   }
 }
 
@@ -556,6 +650,63 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
   }
 }
 
+// Heavy buckets (more than kHeavyOcc occurrences: a hot key's bucket).  One
+// block would take the whole bucket, so it is cut into slices of kSliceOcc,
+// each deduplicated in LDS by its own block; the slices meet in the bucket's
+// region of the dedup table (2 slots per occurrence):
+//  - COUNT, per slice: each of the slice's distinct keys is added to the
+//    region with its count; the slice whose CAS enters a key lists it (the
+//    next index of the bucket's distinct count -> klist);
+//  - EMIT, one block per bucket: the listed keys in list order get their
+//    index, group offset (a block scan of their counts) and IDMap probe /
+//    insert (empty slots taken by CAS: the bucket's keys are spread over
+//    its block and the slices);
+//  - k_bucket_occ, per slice: each distinct key reserves its slice's span of
+//    the key's group (one atomic per key and slice), then every occurrence
+//    takes a position in it;
+//  - k_key_finalize empties the region again.
+// Only the keys that many slices share (the hot ones) meet in global atomics,
+// once per slice.
+
+// Region probe of a heavy bucket's dedup table: the slot of `key` (entered
+// by the count pass), or cap if it is not there (never: bounded all the same).
+__device__ __forceinline__ unsigned long long dd_find(const DedupSlot* R, unsigned long long cap, long long key) {
+  unsigned long long h = (fib_mix(key) >> 20) % cap;
+  for (unsigned long long n = 0; n < cap; ++n) {
+    if (R[h].key == key) return h;
+    h = h + 1 == cap ? 0 : h + 1;
+  }
+  return cap;
+}
+
+// The slice [s0, s1) of a heavy bucket into the LDS table: its distinct keys
+// (s_list) with their counts in the slice.
+template <int TAB, int NT>
+__device__ __forceinline__ void slice_dedup(const LookupLaunch& L, int s0, int s1, int hs, long long* s_key,
+                                            int* s_cnt, unsigned short* s_list, int& s_nd) {
+  const int tid = threadIdx.x;
+  for (int i0 = s0; i0 < s1; i0 += NT) {
+    const int i = i0 + tid;
+    const bool act = i < s1;
+    unsigned h = 0;
+    if (act) {
+      const long long key = L.part[i].key;
+      h = (unsigned)(fib_mix(key) >> hs) & (TAB - 1);
+      while (true) {  // a slice has fewer distinct keys than the table has free slots
+        const long long o = (long long)atomicCAS((unsigned long long*)&s_key[h], (unsigned long long)kEmptyKey,
+                                                 (unsigned long long)key);
+        if (o == kEmptyKey) {
+          s_list[atomicAdd(&s_nd, 1)] = (unsigned short)h;
+          break;
+        }
+        if (o == key) break;
+        h = (h + 1) & (TAB - 1);
+      }
+    }
+    lds_add1(s_cnt, h, act);
+  }
+}
+
 // One bucket per block, in two launches around a scan of the per-bucket
 // distinct counts (so the distinct keys get dense indices without a global
 // counter, which thousands of blocks would serialise on).  Both launches
@@ -568,11 +719,14 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
 // set instead of global atomics -- and writes its row and the bucket's sums
 // (rows to allocate, keys inserted, long keys, chunks); then every
 // occurrence's inverse index, grouped-list entry and forward reference.
+// COUNT's grid has the heavy slices after the buckets; a heavy bucket's own
+// block skips COUNT and does EMIT's key pass (see above).
 template <int TAB, bool EMIT>
 __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t) {
   constexpr int kMaxDistinct = TAB / 4 * 3;
   constexpr int kTabBits = TAB == 1024 ? 10 : (TAB == 2048 ? 11 : 0);
   static_assert(kTabBits > 0, "TAB is 1024 or 2048");
+  static_assert(kSliceOcc <= kMaxDistinct, "a slice fits the LDS table");
   __shared__ long long s_key[TAB];
   __shared__ int s_cnt[TAB];
   __shared__ int s_u[EMIT ? TAB : 1];
@@ -583,12 +737,108 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   __shared__ unsigned long long s_sum, s_sum_long;
   __shared__ unsigned s_err;
   const int tid = threadIdx.x;
+  // the bits below the bucket bits index the table
+  const int hs = 64 - L.nbits - kTabBits;
+  if (!EMIT && (int)blockIdx.x >= L.nbk) {  // heavy slices, a share of them per block
+    const int H = L.hslice[0], nsb = (int)gridDim.x - L.nbk;
+    for (int e = (int)blockIdx.x - L.nbk; e < H; e += nsb) {
+    const int b = L.hslice[1 + 2 * e], k = L.hslice[2 + 2 * e];
+    const int s = L.bbase[b], m = L.bbase[b + 1] - s;
+    const int s0 = s + k * kSliceOcc, s1 = s0 + kSliceOcc < s + m ? s0 + kSliceOcc : s + m;
+    for (int i = tid; i < TAB; i += kThreads) {
+      s_key[i] = kEmptyKey;
+      s_cnt[i] = 0;
+    }
+    if (tid == 0) s_nd = 0;
+    __syncthreads();
+    slice_dedup<TAB, kThreads>(L, s0, s1, hs, s_key, s_cnt, s_list, s_nd);
+    __syncthreads();
+    DedupSlot* R = L.dd + 2ll * s;
+    const unsigned long long cap = 2ull * (unsigned long long)m;
+    for (int idx = tid; idx < s_nd; idx += kThreads) {
+      const int hl = s_list[idx];
+      const long long key = s_key[hl];
+      unsigned long long h = (fib_mix(key) >> 20) % cap;
+      while (true) {
+        const long long c = ld_key(&R[h]);
+        if (c == key) break;
+        if (c == kEmptyKey) {
+          const long long o = (long long)atomicCAS((unsigned long long*)&R[h].key, (unsigned long long)kEmptyKey,
+                                                   (unsigned long long)key);
+          if (o == kEmptyKey) {
+            const int lidx = atomicAdd(&L.ubase[b], 1);
+            st_int(&R[h].uidx, lidx);
+            L.klist[s + lidx] = (int)h;
+            break;
+          }
+          if (o == key) break;
+        }
+        h = h + 1 == cap ? 0 : h + 1;
+      }
+      atomicAdd(&R[h].count, s_cnt[hl]);
+    }
+    __syncthreads();  // the LDS table is reused by the next slice
+    }
+    return;
+  }
   const int b = blockIdx.x;
   const int s = L.bbase[b], m = L.bbase[b + 1] - s;
   if (m == 0) {
     if (tid == 0) {
       if (!EMIT) L.ubase[b] = 0;
       else L.blk_sums[b] = L.blk_long[b] = 0;
+    }
+    return;
+  }
+  if (m > kHeavyOcc) {
+    if (!EMIT) return;  // its slices count it
+    // EMIT's key pass of a heavy bucket: the listed keys in list order
+    const long long ub = L.ubase[b], nd = L.ubase[b + 1] - ub;
+    const DedupSlot* R = L.dd + 2ll * s;
+    const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
+    unsigned long long sum = 0, sum_long = 0, run = 0;
+    unsigned err = 0;
+    if (tid == 0) {
+      s_sum = 0;
+      s_sum_long = 0;
+      s_err = 0;
+    }
+    __syncthreads();
+    for (long long c0 = 0; c0 < nd; c0 += kThreads) {
+      const long long idx = c0 + tid;
+      const bool valid = idx < nd;
+      long long key = 0;
+      int c = 0;
+      if (valid) {
+        const int h = L.klist[s + idx];
+        key = R[h].key;
+        c = R[h].count;
+      }
+      unsigned long long tot;
+      const long long o = (long long)(block_exclusive_scan((unsigned long long)c, &tot) + run);
+      run += tot;
+      if (!valid) continue;
+      const long long u = ub + idx;
+      L.res.unique_keys[u] = key;
+      L.res.counts[u] = c;
+      L.res.unique_offsets[u] = (int)(s + o);
+      // an empty IDMap slot goes to whichever thread's CAS takes it
+      auto claim = [&](unsigned long long q) {
+        return atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
+                         (unsigned long long)key) == (unsigned long long)kEmptyKey;
+      };
+      const ProbeOut po = idmap_probe(t, key, c, find_only, claim);
+      err |= po.err;
+      key_outputs(L, u, c, po, sum, sum_long);
+    }
+    if (err) atomicOr(&s_err, err);
+    if (sum) atomicAdd(&s_sum, sum);
+    if (sum_long) atomicAdd(&s_sum_long, sum_long);
+    __syncthreads();
+    if (tid == 0) {
+      L.blk_sums[b] = s_sum;
+      L.blk_long[b] = s_sum_long;
+      if (s_err) atomicOr(&t.ctr->error, s_err);
     }
     return;
   }
@@ -606,8 +856,6 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     s_err = 0;
   }
   __syncthreads();
-  // the bits below the bucket bits index the table
-  const int hs = 64 - L.nbits - kTabBits;
   for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
     long long key[kBucketPer];
 #pragma unroll
@@ -617,26 +865,31 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     }
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
-      if (i0 + tid + k * kThreads >= m) continue;
-      unsigned h = (unsigned)(fib_mix(key[k]) >> hs) & (TAB - 1);
-      int steps = 0;
-      while (true) {
-        const long long o = (long long)atomicCAS((unsigned long long*)&s_key[h], (unsigned long long)kEmptyKey,
-                                                 (unsigned long long)key[k]);
-        if (o == kEmptyKey) {
-          const int idx = atomicAdd(&s_nd, 1);
-          if (idx < kMaxDistinct) s_list[idx] = (unsigned short)h;
-          else s_over = 1;
-          break;
+      const bool act = i0 + tid + k * kThreads < m;
+      unsigned h = 0;
+      bool counted = false;
+      if (act) {
+        h = (unsigned)(fib_mix(key[k]) >> hs) & (TAB - 1);
+        int steps = 0;
+        while (true) {
+          const long long o = (long long)atomicCAS((unsigned long long*)&s_key[h], (unsigned long long)kEmptyKey,
+                                                   (unsigned long long)key[k]);
+          if (o == kEmptyKey) {
+            const int idx = atomicAdd(&s_nd, 1);
+            if (idx < kMaxDistinct) s_list[idx] = (unsigned short)h;
+            else s_over = 1;
+            break;
+          }
+          if (o == key[k]) break;
+          h = (h + 1) & (TAB - 1);
+          if (++steps == TAB) {  // full: only after the distinct limit was passed
+            s_over = 1;
+            break;
+          }
         }
-        if (o == key[k]) break;
-        h = (h + 1) & (TAB - 1);
-        if (++steps == TAB) {  // full: only after the distinct limit was passed
-          s_over = 1;
-          break;
-        }
+        counted = steps < TAB;
       }
-      if (steps < TAB) atomicAdd(&s_cnt[h], 1);
+      lds_add1(s_cnt, h, counted);
     }
   }
   __syncthreads();
@@ -703,14 +956,92 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     }
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
-      if (i0 + tid + k * kThreads >= m) continue;
-      unsigned h = (unsigned)(fib_mix(e[k].key) >> hs) & (TAB - 1);
-      while (s_key[h] != e[k].key) h = (h + 1) & (TAB - 1);
-      const int pos = atomicAdd(&s_cnt[h], 1);
-      L.res.grouped[s + pos] = e[k].g;
-      L.res.inverse[e[k].occ] = s_u[h];
-      occref[e[k].occ] = s_ref[h];
+      const bool act = i0 + tid + k * kThreads < m;
+      unsigned h = 0;
+      if (act) {
+        h = (unsigned)(fib_mix(e[k].key) >> hs) & (TAB - 1);
+        while (s_key[h] != e[k].key) h = (h + 1) & (TAB - 1);
+      }
+      const int pos = lds_add1(s_cnt, h, act);
+      if (act) {
+        L.res.grouped[s + pos] = e[k].g;
+        L.res.inverse[e[k].occ] = s_u[h];
+        occref[e[k].occ] = s_ref[h];
+      }
     }
+  }
+}
+
+// The occurrences of the heavy buckets, slices e0, e0 + step, ... by one block
+// of NT threads (after EMIT's key pass): a slice's distinct keys reserve their
+// spans of the keys' groups, then every occurrence gets its inverse index,
+// grouped-list entry and forward reference.
+template <int TAB, int NT>
+__device__ void heavy_occ(const LookupLaunch& L, const TableDev& t, int e0, int step) {
+  constexpr int kMaxDistinct = TAB / 4 * 3;
+  constexpr int kTabBits = TAB == 1024 ? 10 : (TAB == 2048 ? 11 : 0);
+  __shared__ long long s_key[TAB];
+  __shared__ int s_cnt[TAB];
+  __shared__ int s_u[TAB];
+  __shared__ long long s_ref[TAB];
+  __shared__ unsigned short s_list[kMaxDistinct];
+  __shared__ int s_nd;
+  const int tid = threadIdx.x;
+  const int H = L.hslice[0];
+  const int hs = 64 - L.nbits - kTabBits;
+  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
+  for (int e = e0; e < H; e += step) {
+  const int b = L.hslice[1 + 2 * e], k = L.hslice[2 + 2 * e];
+  const int s = L.bbase[b], m = L.bbase[b + 1] - s;
+  const int s0 = s + k * kSliceOcc, s1 = s0 + kSliceOcc < s + m ? s0 + kSliceOcc : s + m;
+  for (int i = tid; i < TAB; i += NT) {
+    s_key[i] = kEmptyKey;
+    s_cnt[i] = 0;
+  }
+  if (tid == 0) s_nd = 0;
+  __syncthreads();
+  slice_dedup<TAB, NT>(L, s0, s1, hs, s_key, s_cnt, s_list, s_nd);
+  __syncthreads();
+  DedupSlot* R = L.dd + 2ll * s;
+  const unsigned long long cap = 2ull * (unsigned long long)m;
+  const long long ub = L.ubase[b];
+  for (int idx = tid; idx < s_nd; idx += NT) {
+    const int hl = s_list[idx];
+    const long long key = s_key[hl];
+    const int lc = s_cnt[hl];
+    const unsigned long long h = dd_find(R, cap, key);
+    if (h == cap) {  // not reached
+      atomicOr(&t.ctr->error, kErrInvalid);
+      s_u[hl] = 0;
+      s_ref[hl] = kOccNoRow;
+      s_cnt[hl] = s;
+      continue;
+    }
+    const long long u = ub + R[h].uidx;
+    const int base = atomicSub(&R[h].count, lc) - lc;  // the group is filled from its end
+    s_u[hl] = (int)u;
+    s_ref[hl] = ref_of_row(t, L.res.unique_rows[u], key);
+    s_cnt[hl] = L.res.unique_offsets[u] + base;  // from here on: the slice's next position
+  }
+  __syncthreads();
+  for (int i0 = s0; i0 < s1; i0 += NT) {
+    const int i = i0 + tid;
+    const bool act = i < s1;
+    PartEntry en;
+    unsigned h = 0;
+    if (act) {
+      en = L.part[i];
+      h = (unsigned)(fib_mix(en.key) >> hs) & (TAB - 1);
+      while (s_key[h] != en.key) h = (h + 1) & (TAB - 1);
+    }
+    const int pos = lds_add1(s_cnt, h, act);
+    if (act) {
+      L.res.grouped[pos] = en.g;
+      L.res.inverse[en.occ] = s_u[h];
+      occref[en.occ] = s_ref[h];
+    }
+  }
+  __syncthreads();  // the LDS table is reused by the next slice
   }
 }
 
@@ -774,7 +1105,12 @@ __device__ void scan_two(unsigned long long* a, unsigned long long* c, long long
 // One block: prefix sums of the buckets' (rows to allocate, keys inserted)
 // and (long keys, chunks); the row sources of this call; the key and chunk
 // counts of the backward plan.
+// Its other blocks write the heavy buckets' occurrences (heavy_occ).
 __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, TableDev t) {
+  if (blockIdx.x > 0) {
+    heavy_occ<1024, kScanThreads>(L, t, (int)blockIdx.x - 1, (int)gridDim.x - 1);
+    return;
+  }
   const long long U = *L.res.num_unique;
   const long long nblk = L.N > 0 ? L.nbk : 0;  // per-bucket sums
   unsigned long long all, all_long;
@@ -807,6 +1143,7 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
 // and chunks in the backward plan.
 __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, TableDev t) {
   __shared__ unsigned s_err;
+  __shared__ int s_cend[kThreads], s_cidx[kThreads];
   const int b = blockIdx.x;
   const long long ub = L.ubase[b], nd = L.ubase[b + 1] - ub;
   if (nd == 0) return;
@@ -833,10 +1170,10 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
     unsigned long long total, total_long;
     const unsigned long long run = block_exclusive_scan(acc, &total) + run0;
     const unsigned long long run_long = block_exclusive_scan(acc_long, &total_long) + run0_long;
+    const int chunk0 = (int)(run0_long & 0xFFFFFFFFull);
     run0 += total;
     run0_long += total_long;
-    if (!valid) continue;
-    if (mark == -2) {
+    if (valid && mark == -2) {
       const long long i = (long long)(run >> 32);
       const long long row = i < take ? (long long)t.free_list[ftop - 1 - i] : base + (i - take);
       if (row >= t.rows_limit) {
@@ -847,13 +1184,43 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
         L.res.unique_rows[u] = row | kFreshRow;
       }
     }
-    if (is_long) {  // a failed allocation (row -1) is skipped by the backward
-      const int idx = (int)(run_long >> 32);
-      const int cb = (int)(run_long & 0xFFFFFFFFull);
+    // a failed allocation (row -1) is skipped by the backward
+    const int idx = (int)(run_long >> 32);
+    const int cb = (int)(run_long & 0xFFFFFFFFull);
+    if (is_long) {
       plan[pl.o_long_u + idx] = (int)u;
       plan[pl.o_long_base + idx] = cb;
       plan[pl.o_long_nch + idx] = nch;
-      for (int q = 0; q < nch; ++q) plan[pl.o_chunk_owner + cb + q] = idx;
+    }
+    // chunk owners: these keys' chunks are [chunk0, chunk0 + chunks), in
+    // thread order; the whole block fills them (a hot key has thousands)
+    const int nchunks = (int)(total_long & 0xFFFFFFFFull);
+    if (nchunks > 0) {
+      s_cend[threadIdx.x] = cb + (is_long ? nch : 0);
+      s_cidx[threadIdx.x] = idx;
+      __syncthreads();
+      for (int j = threadIdx.x; j < nchunks; j += kThreads) {
+        const int cj = chunk0 + j;
+        int lo = 0, hi = kThreads - 1;  // the first thread whose chunks end after cj
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_cend[mid] > cj) hi = mid;
+          else lo = mid + 1;
+        }
+        plan[pl.o_chunk_owner + cj] = s_cidx[lo];
+      }
+      __syncthreads();
+    }
+  }
+  // a heavy bucket empties its region of the dedup table (the slots it listed)
+  const int s = L.bbase[b];
+  if (L.bbase[b + 1] - s > kHeavyOcc) {
+    DedupSlot* R = L.dd + 2ll * s;
+    for (long long i = threadIdx.x; i < nd; i += kThreads) {
+      const int h = L.klist[s + i];
+      R[h].key = kEmptyKey;
+      R[h].count = 0;
+      R[h].uidx = 0;
     }
   }
   if (err) atomicOr(&s_err, err);
@@ -871,13 +1238,15 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
     const unsigned G = (unsigned)L.part_blocks;
     RECIS_LAUNCH("k_part_hist", k_part_hist, dim3(G), dim3(kPartThreads), s, L, t);
     RECIS_LAUNCH("k_part_colscan", k_part_colscan, dim3((unsigned)((L.nbk + 63) / 64)), dim3(kPartThreads), s, L);
-    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.bbase, L.nbk, (long long*)nullptr);
+    RECIS_LAUNCH("k_bucket_plan", k_bucket_plan, dim3(1), dim3(kPartThreads), s, L);
     RECIS_LAUNCH("k_part_scatter", k_part_scatter, dim3(G), dim3(kPartThreads), s, L);
-    const dim3 nb_grid((unsigned)L.nbk);
+    // heavy slices: at most kHeavyBlocks blocks, each taking every kHeavyBlocks-th slice
+    const long long hb = L.hmax < kHeavyBlocks ? L.hmax : kHeavyBlocks;
+    const dim3 nb_grid((unsigned)L.nbk), count_grid((unsigned)(L.nbk + hb));
     if (L.big_tab)
-      RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), nb_grid, dim3(kThreads), s, L, t);
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), count_grid, dim3(kThreads), s, L, t);
     else
-      RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), nb_grid, dim3(kThreads), s, L, t);
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), count_grid, dim3(kThreads), s, L, t);
     RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.ubase, L.nbk,
                  reinterpret_cast<long long*>(L.res.num_unique));
     if (L.big_tab)
@@ -885,7 +1254,9 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
     else
       RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true>), nb_grid, dim3(kThreads), s, L, t);
   }
-  RECIS_LAUNCH("k_key_scan", k_key_scan, dim3(1), dim3(kScanThreads), s, L, t);
+  // block 0 scans; the others (N > 0 only) write the heavy buckets' occurrences
+  const long long kb = L.N > 0 ? 1 + (L.hmax < kHeavyBlocks / 4 ? L.hmax : kHeavyBlocks / 4) : 1;
+  RECIS_LAUNCH("k_key_scan", k_key_scan, dim3((unsigned)kb), dim3(kScanThreads), s, L, t);
   if (L.N > 0) RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.nbk), dim3(kThreads), s, L, t);
 }
 

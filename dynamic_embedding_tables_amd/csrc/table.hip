@@ -519,6 +519,12 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.part = t->part;
   L.blk_sums = t->blk_sums;
   L.blk_long = t->blk_sums + (kMaxBuckets + 2);
+  // heavy-bucket bookkeeping lives in the writeback scratch (the two never
+  // share a call): the distinct-key list in uslot (N ints), the slice list in
+  // wb_keys (2 N ints)
+  L.klist = t->uslot;
+  L.hslice = reinterpret_cast<int*>(t->wb_keys);
+  L.hmax = N / kSliceOcc + N / kHeavyOcc + 1;
   launch_lookup(L, t->dev(), s);
   return check_launch();
 }

@@ -297,6 +297,48 @@ def test_one_key_dominates():
     run_parity(spec, [b, b])
 
 
+@pytest.mark.parametrize("pool,admit", [("mean", 1), ("sum", 2)])
+def test_heavy_buckets(pool, admit):
+    """Hot keys whose buckets exceed the single-block size (tens of thousands
+    of occurrences each, sliced across blocks) next to a tail of ordinary
+    keys; a second step mixes new and stored rows, a third looks up only."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.TableSpec(dim=32, dtype="f32", optim="adam", pool=pool, lr=1e-3, eps=1e-8, admit_threshold=admit)
+    rng = W.rng_for(123, admit)
+    B = 6000
+
+    def batch(step):
+        r = W.rng_for(124, admit, step)
+        lens = r.poisson(16, B)
+        off = W.offsets_from_lengths(lens)
+        n = int(off[-1])
+        hot = np.array([11, 22, 33, 44], np.int64) + step
+        p = r.random(n)
+        vals = np.where(p < 0.30, hot[0], np.where(p < 0.50, hot[1], np.where(p < 0.62, hot[2],
+                        np.where(p < 0.64, hot[3], r.integers(1000, 40000, n)))))
+        return W.Batch([W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=3)], B,
+                       r.standard_normal((B, 32), dtype=np.float32))
+    run_parity(spec, [batch(0), batch(1)])
+    # find-only over the same table (hot keys present and absent)
+    table = make_table(spec)
+    otab = oracle.OracleTable(spec)
+    for st in range(2):
+        b = batch(st)
+        res = recis.LookupResult(b.n, B)
+        gpu_step(table, spec, b, res)
+        oracle_step(otab, spec, b)
+    b = batch(5)
+    res = recis.LookupResult(b.n, B)
+    out, _ = gpu_step(table, spec, b, res, find_only=True, with_backward=False)
+    r, oout, oab = oracle_step(otab, spec, b, find_only=True, with_backward=False)
+    torch.cuda.synchronize()
+    assert table.get_error() == 0
+    check_lookup(canon_lookup(res), r)
+    check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+    table.close()
+
+
 def _ids_in_first_hash_bucket(count, bits, rng):
     """Ids (slot 0, no transform: key == id) whose Fibonacci hash has `bits`
     leading zero bits, i.e. that all land in the first hash bucket of the

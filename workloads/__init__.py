@@ -77,7 +77,7 @@ class TableSpec:
 class Batch:
     features: List[FeatureInput]
     batch: int
-    grad: np.ndarray                  # float32: [B, F*D] pooled, [N, D] for pool "none"
+    grad: np.ndarray                  # float32: [B, F*D] pooled, [N, D] for pool "none" (None: not drawn)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -230,7 +230,7 @@ def tiny_batch(step: int, batch: int = 256, id_space: int = 100_000, dim: int = 
 
 
 def ctr_batch(step: int, batch: int = 8192, num_feats: int = 26, dim: int = 64,
-              alpha: float = 1.05, max_len: int = 50, mod: int = 100_000_000) -> Batch:
+              alpha: float = 1.05, max_len: int = 50, mod: int = 100_000_000, grad: bool = True) -> Batch:
     """26 features; bag length Zipf(alpha) truncated to 1..max_len (the ID law's
     exponent is reused for lengths); raw IDs Zipf(alpha) ranks over 2**40 mapped
     through a per-feature bijection; the features ask for Hash then Mod(mod)."""
@@ -242,11 +242,11 @@ def ctr_batch(step: int, batch: int = 8192, num_feats: int = 26, dim: int = 64,
         ranks = zipf_truncated(rng, alpha, ID_SPACE_2_40, int(off[-1]))
         vals = permute_2_40(ranks - 1, feature_key(2, 0, f))
         feats.append(FeatureInput(values=vals, bag_offsets=off, slot=f, ops=OP_HASH | OP_MOD, mod=mod))
-    return Batch(feats, batch, _grad(2, step, (batch, num_feats * dim)))
+    return Batch(feats, batch, _grad(2, step, (batch, num_feats * dim)) if grad else None)
 
 
 def seq_batch(step: int, batch: int = 2048, seq_len: int = 1000, dim: int = 128,
-              alpha: float = 1.2, items: int = 100_000_000) -> Batch:
+              alpha: float = 1.2, items: int = 100_000_000, grad: bool = True) -> Batch:
     """1 feature of fixed-length sequences; IDs Zipf(alpha) over `items`, ranks
     mapped by a bijection of [0, items); upstream gradient N(0,1) per position."""
     rng = rng_for(3, step, 0)
@@ -254,7 +254,7 @@ def seq_batch(step: int, batch: int = 2048, seq_len: int = 1000, dim: int = 128,
     ranks = zipf_truncated(rng, alpha, items, batch * seq_len)
     vals = permute_below(ranks - 1, items, feature_key(3, 0, 0))
     f = FeatureInput(values=vals, bag_offsets=off, slot=0)
-    return Batch([f], batch, _grad(3, step, (batch * seq_len, dim)))
+    return Batch([f], batch, _grad(3, step, (batch * seq_len, dim)) if grad else None)
 
 
 def capacity_resident_keys(num_feats: int = 100, per_feature: int = 2_000_000):
@@ -267,7 +267,7 @@ def capacity_resident_keys(num_feats: int = 100, per_feature: int = 2_000_000):
 
 def capacity_batch(step: int, batch: int = 65536, num_feats: int = 100, dim: int = 64,
                    alpha: float = 1.2, resident_per_feature: int = 2_000_000,
-                   novel_frac: float = 0.02) -> Batch:
+                   novel_frac: float = 0.02, grad: bool = True) -> Batch:
     """Bag length Poisson(8) (empty bags allowed); each occurrence is, with
     probability novel_frac, a never-used ID, else a Zipf(alpha) rank truncated to
     the resident ranks; ranks map to IDs through a per-feature bijection of 2**40."""
@@ -284,7 +284,7 @@ def capacity_batch(step: int, batch: int = 65536, num_feats: int = 100, dim: int
         ranks[novel] = resident_per_feature + step * (1 << 26) + np.arange(k, dtype=np.int64)
         vals = permute_2_40(ranks, feature_key(4, 0, f))
         feats.append(FeatureInput(values=vals, bag_offsets=off, slot=f))
-    return Batch(feats, batch, _grad(4, step, (batch, num_feats * dim)))
+    return Batch(feats, batch, _grad(4, step, (batch, num_feats * dim)) if grad else None)
 
 
 def multi_batch(step: int, table: int, batch: int = 32768, num_feats: int = 60,
