@@ -21,8 +21,9 @@
 //
 // Backward, no atomics on data: each key's occurrences were grouped by
 // insert_find.  Keys with more than kShortMax occurrences take two launches:
-// one wave per kChunk-occurrence chunk writes a double-precision partial sum,
-// then one wave per key sums its partials in a fixed order and applies the
+// one wave per chunk of kChunk occurrences (more for a hot key) writes a
+// double-precision partial sum, then one wave per key sums its partials in a
+// fixed order and applies the
 // update (a launch boundary instead of fences and completion counters, which
 // serialise on the per-XCD L2 writeback).  The other keys take a third
 // launch: a block stages the metadata and gradient references of 256
@@ -544,11 +545,13 @@ __device__ __forceinline__ long long block_scan_ll(long long v, long long* total
   return before + x - v;
 }
 
-// Long keys, pass 1: one wave per kChunk-entry chunk.  The chunk's entries
-// sit one per lane; each group of C = D / E lanes sums a contiguous share of
-// them (up to 8 rows in flight), a butterfly across the groups merges the
-// shares, and the chunk's double-precision partial is stored.  No atomics and
-// no cross-block waits: the finishing pass runs as the next launch.
+// Long keys, pass 1: one wave per chunk (long_chunk(count) entries: kChunk,
+// or a multiple of it for a hot key, so that it has at most kMaxKeyChunks
+// chunks).  The chunk is taken kChunk entries at a time, one per lane; each
+// group of C = D / E lanes sums a contiguous share of them (up to 8 rows in
+// flight), a butterfly across the groups merges the shares, and the chunk's
+// double-precision partial is stored.  No atomics and no cross-block waits:
+// the finishing pass runs as the next launch.
 template <int D, typename TP>
 __global__ __launch_bounds__(256) void k_bwd_long_partial(BwdArgs a) {
   constexpr int E = Vec<TP>::E;
@@ -567,37 +570,41 @@ __global__ __launch_bounds__(256) void k_bwd_long_partial(BwdArgs a) {
     const int idx = owner[q];
     const int u = long_u[idx], cb = long_base[idx];
     const int o = a.uoff[u], c = a.counts[u];
-    const int k0 = (int)(q - cb) * kChunk;
-    const int cnt = c - k0 < kChunk ? c - k0 : kChunk;
-    int gr = 0;
-    double scale = 0.0;
-    if (wl < cnt) grad_ref<D>(a, a.grouped[o + k0 + wl], gr, scale);
+    const int csz = long_chunk(c);
+    const int k0 = (int)(q - cb) * csz;
+    const int cend = c - k0 < csz ? c - k0 : csz;
     double acc[1][E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[0][e] = 0.0;
-    // All 64 lanes take part in every shuffle: the trip counts are constants
-    // and each group masks its own loads.
 #pragma unroll 1
-    for (int x0 = 0; x0 < PER; x0 += GF) {
-      float gv[GF][E];
-      double sv[GF];
+    for (int s0 = 0; s0 < cend; s0 += kChunk) {
+      const int cnt = cend - s0 < kChunk ? cend - s0 : kChunk;
+      int gr = 0;
+      double scale = 0.0;
+      if (wl < cnt) grad_ref<D>(a, a.grouped[o + k0 + s0 + wl], gr, scale);
+      // All 64 lanes take part in every shuffle: the trip counts are
+      // constants and each group masks its own loads.
+#pragma unroll 1
+      for (int x0 = 0; x0 < PER; x0 += GF) {
+        float gv[GF][E];
+        double sv[GF];
 #pragma unroll
-      for (int x = 0; x < GF; ++x) {
-        const int src = g * PER + x0 + x;
-        const int s = src < cnt ? src : 0;
-        const int gi = __shfl(gr, s);
-        sv[x] = shfl_d(scale, s);
-        if (src < cnt) {
-          load_grad<E>(a.grad, (long long)gi * D + lane * E, a.gdt, gv[x]);
-        } else {
+        for (int x = 0; x < GF; ++x) {
+          const int src = g * PER + x0 + x;
+          const int sl = src < cnt ? src : 0;
+          const int gi = __shfl(gr, sl);
+          sv[x] = shfl_d(scale, sl);
 #pragma unroll
           for (int e = 0; e < E; ++e) gv[x][e] = 0.f;
+          // the loads write gv only after its zeros, never under an else
+          // (that would wait for every load in flight)
+          if (src < cnt) load_grad<E>(a.grad, (long long)gi * D + lane * E, a.gdt, gv[x]);
         }
+#pragma unroll
+        for (int x = 0; x < GF; ++x)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[0][e] += (double)gv[x][e] * sv[x];
       }
-#pragma unroll
-      for (int x = 0; x < GF; ++x)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[0][e] += (double)gv[x][e] * sv[x];
     }
 #pragma unroll
     for (int m = C; m < 64; m <<= 1)

@@ -47,6 +47,18 @@ static_assert(kLdsTab == 2 * kOccTile, "block-local dedup table at most half ful
 // Backward: keys with more occurrences than kShortMax are split into chunks.
 constexpr int kShortMax = 64;
 constexpr int kChunk = 64;  // one grouped entry per lane of a wave
+// A long key is cut into at most kMaxKeyChunks chunks of a multiple of
+// kChunk entries: a hot key's partial sums stay few enough for one wave to
+// merge them.
+constexpr int kMaxKeyChunks = 256;
+__host__ __device__ inline int long_chunk(int c) {
+  const int per = (c + kChunk * kMaxKeyChunks - 1) / (kChunk * kMaxKeyChunks);
+  return kChunk * (per > 1 ? per : 1);
+}
+__host__ __device__ inline int long_chunks(int c) {
+  const int z = long_chunk(c);
+  return (c + z - 1) / z;
+}
 
 struct __align__(16) Slot {
   long long key;

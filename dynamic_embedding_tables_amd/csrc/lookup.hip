@@ -533,7 +533,7 @@ __device__ __forceinline__ void key_outputs(const LookupLaunch& L, long long u, 
   sum += ((unsigned long long)o.need << 32) | (unsigned)o.ins;
   // a key that will have a row and more than kShortMax occurrences is reduced
   // in chunks by the backward
-  if (c > kShortMax && (o.need || o.row >= 0)) sum_long += (1ull << 32) | (unsigned)((c + kChunk - 1) / kChunk);
+  if (c > kShortMax && (o.need || o.row >= 0)) sum_long += (1ull << 32) | (unsigned)long_chunks(c);
 }
 
 // A bucket whose distinct keys overflow the LDS table (only inputs built to
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
         }
         counted = steps < TAB;
       }
-      lds_add1(s_cnt, h, counted);
+      if (counted) atomicAdd(&s_cnt[h], 1);
     }
   }
   __syncthreads();
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
         h = (unsigned)(fib_mix(e[k].key) >> hs) & (TAB - 1);
         while (s_key[h] != e[k].key) h = (h + 1) & (TAB - 1);
       }
-      const int pos = lds_add1(s_cnt, h, act);
+      const int pos = act ? atomicAdd(&s_cnt[h], 1) : 0;
       if (act) {
         L.res.grouped[s + pos] = e[k].g;
         L.res.inverse[e[k].occ] = s_u[h];
@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
     }
     const unsigned long long acc = valid ? ((unsigned long long)(mark == -2) << 32) : 0ull;
     const bool is_long = valid && cnt > kShortMax && mark != -1;  // as k_bucket counted it
-    const int nch = (cnt + kChunk - 1) / kChunk;
+    const int nch = long_chunks(cnt);
     const unsigned long long acc_long = is_long ? ((1ull << 32) | (unsigned long long)nch) : 0ull;
     unsigned long long total, total_long;
     const unsigned long long run = block_exclusive_scan(acc, &total) + run0;
