@@ -50,7 +50,7 @@ constexpr int kChunk = 64;  // one grouped entry per lane of a wave
 // A long key is cut into at most kMaxKeyChunks chunks of a multiple of
 // kChunk entries: a hot key's partial sums stay few enough for one wave to
 // merge them.
-constexpr int kMaxKeyChunks = 256;
+constexpr int kMaxKeyChunks = 1024;
 __host__ __device__ inline int long_chunk(int c) {
   const int per = (c + kChunk * kMaxKeyChunks - 1) / (kChunk * kMaxKeyChunks);
   return kChunk * (per > 1 ? per : 1);
