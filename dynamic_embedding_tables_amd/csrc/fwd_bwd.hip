@@ -360,24 +360,40 @@ __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
   }
 }
 
+// Gather (no pooling): a group of C lanes copies kGatherPer consecutive
+// occurrences' rows, all their loads in flight together; the output is
+// written with non-temporal stores (it is not read again by this step).
+constexpr int kGatherPer = 4;
+
 template <int D, typename TP>
 __global__ __launch_bounds__(256) void k_fwd_gather(FwdArgs a) {
   constexpr int E = Vec<TP>::E;
   constexpr int C = D / E;
   constexpr int GPB = 256 / C;
   const int lane = threadIdx.x % C;
-  const long long j = (long long)blockIdx.x * GPB + threadIdx.x / C;
-  if (j >= a.N) return;
-  const long long r = occurrence_ref(a, j);
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (r == kOccNoRow) {
-  } else if (r >= 0) {
-    const u32x4 x = *gread<u32x4>(reinterpret_cast<const char*>(r) + lane * 16);
-    v = make_uint4(x.x, x.y, x.z, x.w);
-  } else {
-    v = init_chunk_as<Vec<TP>::kBF16>(a.t, (long long)((unsigned long long)r & ~kOccPendingBit), lane);
+  const long long j0 = ((long long)blockIdx.x * GPB + threadIdx.x / C) * kGatherPer;
+  if (j0 >= a.N) return;
+  long long r[kGatherPer];
+#pragma unroll
+  for (int x = 0; x < kGatherPer; ++x) r[x] = j0 + x < a.N ? occurrence_ref(a, j0 + x) : kOccNoRow;
+  u32x4 v[kGatherPer];
+#pragma unroll
+  for (int x = 0; x < kGatherPer; ++x) {
+    v[x] = u32x4{0u, 0u, 0u, 0u};
+    // loads write v only after its zeros (never under an else: that would
+    // wait for every load in flight)
+    if (r[x] >= 0 && r[x] != kOccNoRow) v[x] = *gread<u32x4>(reinterpret_cast<const char*>(r[x]) + lane * 16);
   }
-  reinterpret_cast<uint4*>(static_cast<char*>(a.out) + (j * D * (long long)sizeof(TP)))[lane] = v;
+#pragma unroll
+  for (int x = 0; x < kGatherPer; ++x) {
+    if (j0 + x >= a.N) break;
+    u32x4 y = v[x];
+    if (r[x] < 0) {
+      const uint4 p = init_chunk_as<Vec<TP>::kBF16>(a.t, (long long)((unsigned long long)r[x] & ~kOccPendingBit), lane);
+      y = u32x4{p.x, p.y, p.z, p.w};
+    }
+    __builtin_nontemporal_store(y, gwrite<u32x4>(static_cast<char*>(a.out) + ((j0 + x) * D * (long long)sizeof(TP)) + lane * 16));
+  }
 }
 
 // ------------------------------------------------------------ backward
@@ -906,7 +922,8 @@ void fwd_dispatch(const FwdArgs& a, int pool, hipStream_t s) {
   constexpr int GPB = 256 / C;
   if (pool == RECIS_POOL_NONE) {
     if (a.N == 0) return;
-    RECIS_LAUNCH("k_fwd_gather", (k_fwd_gather<D, TP>), dim3((unsigned)((a.N + GPB - 1) / GPB)), dim3(256), s, a);
+    const long long per_block = (long long)GPB * kGatherPer;
+    RECIS_LAUNCH("k_fwd_gather", (k_fwd_gather<D, TP>), dim3((unsigned)((a.N + per_block - 1) / per_block)), dim3(256), s, a);
   } else {
     if (a.nbags == 0) return;
     constexpr int BB = FwdShape<C>::BB;
