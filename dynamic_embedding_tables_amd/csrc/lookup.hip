@@ -10,10 +10,10 @@
 //
 // Kernel sequence of one call (all on one stream, no host read-back):
 //   k_prep      merged bag offsets, offset validation, per-call counters
-//   k_part_hist / k_part_colscan / k_bucket_plan / k_part_scatter
+//   k_part_hist / k_part_colscan / k_scan_small / k_part_scatter
 //               transform + tag every occurrence and partition the call by
 //               the top bits of the key's hash (one radix-sort pass); the
-//               plan also cuts heavy buckets (hot keys) into slices
+//               column scan also cuts heavy buckets (hot keys) into slices
 //   k_bucket    one bucket per block, twice around a scan of the per-bucket
 //               distinct counts: dedup in LDS, counts, distinct-key indices,
 //               group offsets; in the second launch also the IDMap probe /
@@ -139,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
     *L.res.num_unique = 0;
     L.res.plan[0] = 0;  // long keys
     L.res.plan[1] = 0;  // chunks
+    L.hslice[0] = 0;    // heavy slices (listed by k_part_colscan)
   }
   if (idx > nb) return;
   if (idx == nb) {
@@ -258,7 +259,18 @@ __global__ __launch_bounds__(kPartThreads) void k_part_colscan(LookupLaunch L) {
       *p = run;
       run += v;
     }
-    if (w == 0) L.bbase[b] = all;  // total, scanned by k_part_bscan
+    if (w == 0) {
+      L.bbase[b] = all;  // total, scanned by k_scan_small
+      L.ubase[b] = 0;    // a light bucket's block writes it, a heavy one's slices add to it
+      if (all > kHeavyOcc) {  // a heavy bucket: list its slices (few buckets, so one atomic each)
+        const int ns = (all + kSliceOcc - 1) / kSliceOcc;
+        const int e0 = atomicAdd(&L.hslice[0], ns);
+        for (int q = 0; q < ns; ++q) {
+          L.hslice[1 + 2 * (e0 + q)] = b;
+          L.hslice[2 + 2 * (e0 + q)] = q;
+        }
+      }
+    }
   }
 }
 
@@ -298,71 +310,6 @@ __global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long
   if (tid == 0) {
     a[n] = all;
     if (total_ll) *total_ll = all;
-  }
-}
-
-// Exclusive scan of one int per thread over a block of kPartThreads.
-__device__ __forceinline__ int block_scan_part(int x, int* total) {
-  __shared__ int s_w[kPartThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int y = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int z = __shfl(y, lane >= d ? lane - d : lane);
-    if (lane >= d) y += z;
-  }
-  if (lane == 63) s_w[w] = y;
-  __syncthreads();
-  int run = y - x, all = 0;
-#pragma unroll
-  for (int q = 0; q < kPartThreads / 64; ++q) {
-    run += q < w ? s_w[q] : 0;
-    all += s_w[q];
-  }
-  __syncthreads();
-  *total = all;
-  return run;
-}
-
-// One block: bucket positions from the bucket sizes (bbase, as k_scan_small),
-// and the heavy buckets' slices -- a bucket of m > kHeavyOcc occurrences gets
-// ceil(m / kSliceOcc) of them, listed as (bucket, slice) pairs after their
-// count.  Zeroes every bucket's distinct count: a heavy bucket's slices add to
-// it, a light bucket's block writes it.
-__global__ __launch_bounds__(kPartThreads) void k_bucket_plan(LookupLaunch L) {
-  constexpr int kPer = kMaxBuckets / kPartThreads;
-  const int n = L.nbk;
-  int* a = L.bbase;
-  const int b0 = threadIdx.x * kPer;
-  int v[kPer], ns[kPer];
-  int sum = 0, hs = 0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) v[k] = b0 + k < n ? a[b0 + k] : 0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    ns[k] = v[k] > kHeavyOcc ? (v[k] + kSliceOcc - 1) / kSliceOcc : 0;
-    sum += v[k];
-    hs += ns[k];
-  }
-  int all, hall;
-  int run = block_scan_part(sum, &all);
-  int hrun = block_scan_part(hs, &hall);
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (b0 + k < n) {
-      a[b0 + k] = run;
-      L.ubase[b0 + k] = 0;
-      for (int q = 0; q < ns[k]; ++q) {
-        L.hslice[1 + 2 * (hrun + q)] = b0 + k;
-        L.hslice[2 + 2 * (hrun + q)] = q;
-      }
-    }
-    run += v[k];
-    hrun += ns[k];
-  }
-  if (threadIdx.x == 0) {
-    a[n] = all;
-    L.hslice[0] = hall;
   }
 }
 
@@ -1238,7 +1185,7 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
     const unsigned G = (unsigned)L.part_blocks;
     RECIS_LAUNCH("k_part_hist", k_part_hist, dim3(G), dim3(kPartThreads), s, L, t);
     RECIS_LAUNCH("k_part_colscan", k_part_colscan, dim3((unsigned)((L.nbk + 63) / 64)), dim3(kPartThreads), s, L);
-    RECIS_LAUNCH("k_bucket_plan", k_bucket_plan, dim3(1), dim3(kPartThreads), s, L);
+    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.bbase, L.nbk, (long long*)nullptr);
     RECIS_LAUNCH("k_part_scatter", k_part_scatter, dim3(G), dim3(kPartThreads), s, L);
     // heavy slices: at most kHeavyBlocks blocks, each taking every kHeavyBlocks-th slice
     const long long hb = L.hmax < kHeavyBlocks ? L.hmax : kHeavyBlocks;
