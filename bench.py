@@ -71,11 +71,11 @@ WORKLOADS = {
     "capacity": {
         "title": "Capacity stress: 200M pre-populated rows x dim 64 fp32 + Adam m/v, 100 features, batch 65536, "
                  "bag length Poisson(8), Zipf(1.2) IDs with 2% novel per step, sum pooling",
-        "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 3,
+        "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 5,
         # 1.68 GB per gradient: one N(0,1) draw serves every step
         "shared_grad": True,
         "table": {"slot_capacity": 1 << 29, "block_rows": 1 << 20},
-        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit"),
+        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bwd_long_partial"),
     },
 }
 
@@ -166,13 +166,24 @@ def step_shapes(results, U, resident0):
         new[c[is_first[pos:pos + c.size]]] = True
         pos += c.size
         short = counts <= SHORT_MAX
+        lc = counts[~short & has]
         out.append({"U_s": int((short & has).sum()), "U_s_new": int((short & new).sum()),
                     "E_s": int(counts[short & has].sum()), "U_l": int((~short & has).sum()),
-                    "E_l": int(counts[~short & has].sum())})
+                    "E_l": int(lc.sum()), "chunks_l": int(long_chunks(lc).sum())})
     return {k: float(np.mean([o[k] for o in out])) for k in out[0]}
 
 
 SHORT_MAX = 64   # occurrences up to which the backward treats a key as short
+MAX_KEY_CHUNKS = 1024  # a long key is summed in at most this many chunks
+
+
+def long_chunks(c):
+    """Chunks of a long key with c entries: chunks of a multiple of 64 entries,
+    at most MAX_KEY_CHUNKS of them."""
+    c = np.asarray(c, np.int64)
+    per = np.maximum((c + SHORT_MAX * MAX_KEY_CHUNKS - 1) // (SHORT_MAX * MAX_KEY_CHUNKS), 1)
+    z = SHORT_MAX * per
+    return (c + z - 1) // z
 
 
 def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=True):
@@ -186,8 +197,16 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
         resident rows' params D s; the output Bg D 4.
       k_fwd_gather: per occurrence its row reference 8 and its output row D s;
         resident rows' params D s.
-      k_key_probe: per distinct key its key and count 12, the IDMap slot 16,
-        its row and slot index 12; per new key the slot written 16.
+      k_part_scatter: per occurrence its raw ID 8 read and its partition
+        record (key, occurrence, bag) 16 written.
+      k_bucket_count: per occurrence its record's key 8.
+      k_bucket_emit: per occurrence its record 16 read, and its inverse index 4,
+        grouped entry 4 and forward reference 8 written; per distinct key its
+        key and count 12, group offset 4, IDMap slot read 16 and slot index 8;
+        per new key its IDMap slot written 16.
+      k_bwd_long_partial: per long entry 4; per chunk a partial of D fp64
+        written; the gradient rows of the bags its entries touch, at most
+        min(E_l, Bg) pooled (one row per entry when not pooled).
       step: insert_find 12 N + 4 (Bg + 1) + 32 U + 16 U_new, forward
         4 N + 8 U + U_hit D s + output, backward 4 N + 8 U + U_hit 2P
         + U_new P + gradient; output and gradient Bg D 4 each when pooled,
@@ -198,13 +217,19 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
     bwd_short = 16 * Us + 4 * shape["E_s"] + (Us - Usn) * 2 * P + Usn * P + g_short
     fwd = 8 * N + 4 * (Bg + 1) + Uhit * D * s + Bg * D * 4
     gather = 8 * N + Uhit * D * s + N * D * s
-    probe = 40 * Um + 16 * Unew
+    scatter = 24 * N
+    count = 8 * N
+    emit = 32 * N + 40 * Um + 16 * Unew
+    El = shape["E_l"]
+    g_long = min(El, Bg) * D * gs if pooled else El * D * gs
+    long_partial = 4 * El + shape["chunks_l"] * D * 8 + g_long
     out_b, grad_b = (Bg * D * 4, Bg * D * 4) if pooled else (N * D * s, N * D * gs)
     ins = 12 * N + 4 * (Bg + 1) + 32 * Um + 16 * Unew
     fwd_call = 4 * N + 8 * Um + Uhit * D * s + out_b
     bwd_call = 4 * N + 8 * Um + Uhit * 2 * P + Unew * P + grad_b
-    return {"k_bwd_short": bwd_short, "k_fwd_pool": fwd, "k_fwd_gather": gather, "k_key_probe": probe,
-            "step": ins + fwd_call + bwd_call}
+    return {"k_bwd_short": bwd_short, "k_fwd_pool": fwd, "k_fwd_gather": gather,
+            "k_part_scatter": scatter, "k_bucket_count": count, "k_bucket_emit": emit,
+            "k_bwd_long_partial": long_partial, "step": ins + fwd_call + bwd_call}
 
 
 def kernel_source_hash():
@@ -526,6 +551,13 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
                      "traffic": traffic},
         "warmup_kernel_ms": {k: float(np.mean(v)) for k, v in probe_ms.items()},
+        # every kernel timed in the warm-up (one launch each), against the same
+        # algorithmic bytes as the roofline above
+        "kernel_rooflines": {k: {"ms": float(np.mean(v)), "algorithmic_bytes": alg.get(k),
+                                 "GBps": alg[k] / (np.mean(v) * 1e-3) / 1e9 if alg.get(k) else None,
+                                 "frac": alg[k] / (np.mean(v) * 1e-3) / 1e9 / HBM_PEAK_GBS
+                                 if alg.get(k) else None}
+                             for k, v in probe_ms.items()},
         "backward_key_split": shape,
     }
     if args.workload == "ctr" and not args.no_cpu_baseline:
