@@ -354,6 +354,15 @@ void launch_fill_slots(Slot* slots, long long cap, hipStream_t s);
 void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s);
 void launch_rehash(const Slot* old_slots, long long old_cap, const TableDev& t, hipStream_t s);
 
+// Logical index of workgroup i of a grid of G.  Workgroups are dealt to the
+// 8 XCDs round robin (i mod 8); this gives the workgroups of one XCD
+// consecutive logical indices, so that what they write side by side is
+// merged in that XCD's L2 before it goes to memory.
+__device__ __forceinline__ int xcd_block(int i, int G) {
+  const int x = i & 7, k = i >> 3, q = G >> 3, r = G & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // Hash partition of a lookup call.
 constexpr int kPartThreads = 1024;   // partition kernels' block size
 constexpr int kPartPer = 8;          // occurrences per thread per pass

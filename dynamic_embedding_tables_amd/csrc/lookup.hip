@@ -203,7 +203,8 @@ __global__ __launch_bounds__(kPartThreads) void k_part_hist(LookupLaunch L, Tabl
   __shared__ int s_h[kMaxBuckets];
   __shared__ unsigned s_err;
   const int tid = threadIdx.x;
-  const long long j0 = (long long)blockIdx.x * L.part_range;
+  const int pb = xcd_block((int)blockIdx.x, (int)gridDim.x);  // partition block
+  const long long j0 = (long long)pb * L.part_range;
   const long long j1 = j0 + L.part_range < L.N ? j0 + L.part_range : L.N;
   for (int b = tid; b < L.nbk; b += kPartThreads) s_h[b] = 0;
   if (tid == 0) s_err = 0;
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(kPartThreads) void k_part_hist(LookupLaunch L, Tabl
   }
   if (err) atomicOr(&s_err, err);
   __syncthreads();
-  int* row = L.hist + (long long)blockIdx.x * L.nbk;
+  int* row = L.hist + (long long)pb * L.nbk;
   for (int b = tid; b < L.nbk; b += kPartThreads) row[b] = s_h[b];
   if (tid == 0 && s_err) atomicOr(&t.ctr->error, s_err);
 }
@@ -314,52 +315,59 @@ __global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long
 }
 
 // Grouped-list value of merged occurrence j: its bag (f * B + i), found by a
-// binary search over the block's window of merged bag offsets (kept in LDS
+// binary search over the pass's window of merged bag offsets (kept in LDS
 // when it fits), or j itself when grouping by occurrence.
 __global__ __launch_bounds__(kPartThreads) void k_part_scatter(LookupLaunch L) {
   __shared__ int s_h[kMaxBuckets];
   __shared__ int s_off[kBagWin];
   __shared__ int s_blo, s_bhi;
   const int tid = threadIdx.x;
-  const long long j0 = (long long)blockIdx.x * L.part_range;
+  // the same partition block as in k_part_hist; the blocks of one XCD write
+  // neighbouring records of every bucket
+  const int pb = xcd_block((int)blockIdx.x, (int)gridDim.x);
+  const long long j0 = (long long)pb * L.part_range;
   const long long j1 = j0 + L.part_range < L.N ? j0 + L.part_range : L.N;
   const bool by_occ = (L.flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
   const int* off = L.res.bag_offsets;  // merged, F * B + 1 entries
   const int nbags = L.F * L.B;
-  const int* row = L.hist + (long long)blockIdx.x * L.nbk;
+  const int* row = L.hist + (long long)pb * L.nbk;
   for (int b = tid; b < L.nbk; b += kPartThreads) s_h[b] = L.bbase[b] + row[b];
-  if (!by_occ && tid < 2) {
-    // bag of occurrence j: the last i with off[i] <= j (empty bags skipped)
-    const long long j = tid == 0 ? j0 : j1 - 1;
-    int lo = 0, hi = nbags;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if ((long long)off[mid] <= j) lo = mid + 1;
-      else hi = mid;
-    }
-    const int b = lo - 1 < 0 ? 0 : lo - 1;
-    if (tid == 0) s_blo = b;
-    else s_bhi = b;
-  }
-  __syncthreads();
-  const int blo = by_occ ? 0 : s_blo, wn = by_occ ? 0 : s_bhi - s_blo + 2;
-  const bool win = wn > 0 && wn <= kBagWin;
-  if (win)
-    for (int i = tid; i < wn; i += kPartThreads) s_off[i] = off[blo + i];
-  __syncthreads();
   FeatCursor fc;
   unsigned err = 0;
-  for (long long c0 = j0; c0 < j1; c0 += (long long)kPartThreads * kPartPer) {
+  for (long long c0 = j0; c0 < j1; c0 += (long long)kPartOcc) {
+    const long long c1 = c0 + kPartOcc < j1 ? c0 + kPartOcc : j1;
     long long key[kPartPer];
 #pragma unroll
     for (int k = 0; k < kPartPer; ++k) {
       const long long j = c0 + tid + (long long)k * kPartThreads;
-      key[k] = j < j1 ? key_of(L, fc, j, err) : 0;
+      key[k] = j < c1 ? key_of(L, fc, j, err) : 0;
     }
+    // the bags of this pass's occurrences: [s_blo, s_bhi], their offsets to
+    // LDS when they fit (a pass of kPartOcc occurrences spans few bags
+    // unless most of them are empty)
+    if (!by_occ && tid < 2) {
+      // bag of occurrence j: the last i with off[i] <= j (empty bags skipped)
+      const long long j = tid == 0 ? c0 : c1 - 1;
+      int lo = 0, hi = nbags;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((long long)off[mid] <= j) lo = mid + 1;
+        else hi = mid;
+      }
+      const int b = lo - 1 < 0 ? 0 : lo - 1;
+      if (tid == 0) s_blo = b;
+      else s_bhi = b;
+    }
+    __syncthreads();
+    const int blo = by_occ ? 0 : s_blo, wn = by_occ ? 0 : s_bhi - s_blo + 2;
+    const bool win = wn > 0 && wn <= kBagWin;
+    if (win)
+      for (int i = tid; i < wn; i += kPartThreads) s_off[i] = off[blo + i];
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kPartPer; ++k) {
       const long long j = c0 + tid + (long long)k * kPartThreads;
-      if (j >= j1) continue;
+      if (j >= c1) continue;
       int g;
       if (by_occ) {
         g = (int)j;
@@ -393,6 +401,7 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(LookupLaunch L) {
       e.g = g;
       L.part[pos] = e;
     }
+    __syncthreads();  // the next pass reloads the window
   }
 }
 
