@@ -80,6 +80,16 @@ struct __align__(16) PartEntry {
   int g;
 };
 
+// What the bucket kernels leave in place of an occurrence's record once its
+// key is resolved: the forward reference and the distinct-key index.  The
+// lookup's last kernel copies them out in occurrence order.
+struct __align__(16) PartOut {
+  long long ref;
+  int u;
+  int pad;
+};
+static_assert(sizeof(PartOut) == sizeof(PartEntry), "written in place of the record");
+
 struct DevCounters {
   unsigned long long next_row;  // bump pointer over EmbeddingBlocks
   long long free_top;           // entries in the free list
@@ -332,6 +342,7 @@ struct recis_table {
   int* bbase = nullptr;
   int* ubase = nullptr;
   int* uslot = nullptr;
+  int* posmap = nullptr;
   unsigned long long* blk_sums = nullptr;
   long long* wb_keys = nullptr;
   double* partials = nullptr;
@@ -396,6 +407,7 @@ struct LookupLaunch {
   int* bbase;                 // nbk + 1: first position of each bucket
   int* ubase;                 // nbk + 1: distinct keys per bucket, then their first index
   PartEntry* part;            // N
+  int* posmap;                // N: position of each occurrence's record in part
   unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
   unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
   int* klist;                    // N: heavy buckets' distinct keys (dedup-table slots), by bucket range

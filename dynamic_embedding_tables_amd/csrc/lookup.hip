@@ -19,8 +19,9 @@
 //               group offsets; in the second launch also the IDMap probe /
 //               insert of every distinct key (count, admission decision,
 //               without global atomics: the block owns the bucket's IDMap
-//               regions), then each occurrence's inverse index, grouped bag /
-//               occurrence entry and forward reference (a bucket that
+//               regions), then each occurrence's grouped bag / occurrence
+//               entry, and its inverse index and forward reference in place
+//               of its partition record (a bucket that
 //               overflows the LDS table, from colliding inputs, uses a global
 //               one; a heavy bucket is counted slice by slice and its
 //               occurrences are written by k_key_scan's other blocks)
@@ -30,6 +31,8 @@
 //   k_key_finalize  per bucket: row assignment (the new row is marked
 //               pending, not written: its values are the initializer's until
 //               its first update), backward plan for long keys
+//   k_occ_out   inverse index and forward reference of every occurrence, in
+//               occurrence order, gathered from the partition array
 // Memory accesses that do not depend on each other are issued as one batch
 // per thread (all loads of a phase before any use), so that each thread
 // waits once per phase rather than once per item.
@@ -400,6 +403,7 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(LookupLaunch L) {
       e.occ = (int)j;
       e.g = g;
       L.part[pos] = e;
+      L.posmap[j] = pos;
     }
     __syncthreads();  // the next pass reloads the window
   }
@@ -498,7 +502,8 @@ __device__ __forceinline__ void key_outputs(const LookupLaunch& L, long long u, 
 // dedup table, 2 slots per occurrence -- and atomics.  Slow but bounded.
 // COUNT inserts the bucket's keys and counts them (the distinct count goes to
 // ubase[b]); EMIT (after the scan) writes the distinct keys' outputs and the
-// occurrences' inverse and grouped entries, then empties the region again.
+// occurrences' grouped entries and resolved records, then empties the
+// region again.
 __device__ __forceinline__ long long ld_key(const DedupSlot* d) {
   return (long long)__hip_atomic_load(reinterpret_cast<const unsigned long long*>(&d->key), __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
@@ -515,6 +520,17 @@ __device__ __forceinline__ long long ref_of_row(const TableDev& t, long long v, 
   if (v == -2 || (v >= 0 && (v & kFreshRow))) return (long long)(kOccPendingBit | (unsigned long long)key);
   if (v < 0) return kOccNoRow;
   return (long long)row_ptr(t.rs, v);
+}
+
+// The resolved occurrence at partition position p (in place of its record,
+// which its thread has read): written in bucket order, so the stores of a
+// wave are contiguous; k_occ_out turns them into occurrence order.
+__device__ __forceinline__ void put_out(const LookupLaunch& L, long long p, long long ref, int u) {
+  PartOut o;
+  o.ref = ref;
+  o.u = u;
+  o.pad = 0;
+  reinterpret_cast<PartOut*>(L.part)[p] = o;
 }
 
 template <bool EMIT>
@@ -557,7 +573,6 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
   }
   const long long ub = L.ubase[b];
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
-  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
   unsigned long long sum = 0, sum_long = 0;
   unsigned err = 0;
   for (unsigned long long h = tid; h < cap; h += kThreads) {
@@ -594,10 +609,9 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     const int u = ld_int(&R[h].uidx);
     const int pos = atomicSub(&R[h].count, 1) - 1;  // the group is filled from its end
     L.res.grouped[ld_int(&L.res.unique_offsets[u]) + pos] = e.g;
-    L.res.inverse[e.occ] = u;
     const long long v = (long long)__hip_atomic_load(reinterpret_cast<unsigned long long*>(&L.res.unique_rows[u]),
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    occref[e.occ] = ref_of_row(t, v, e.key);
+    put_out(L, s + i, ref_of_row(t, v, e.key), u);
   }
   __syncthreads();
   for (unsigned long long h = tid; h < cap; h += kThreads) {
@@ -674,7 +688,8 @@ __device__ __forceinline__ void slice_dedup(const LookupLaunch& L, int s0, int s
 // IDMap region of its bucket, so empty slots are shared out through an LDS
 // set instead of global atomics -- and writes its row and the bucket's sums
 // (rows to allocate, keys inserted, long keys, chunks); then every
-// occurrence's inverse index, grouped-list entry and forward reference.
+// occurrence's grouped-list entry, and its distinct-key index and forward
+// reference in place of its partition record.
 // COUNT's grid has the heavy slices after the buckets; a heavy bucket's own
 // block skips COUNT and does EMIT's key pass (see above).
 template <int TAB, bool EMIT>
@@ -902,7 +917,6 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     L.blk_long[b] = s_sum_long;
     if (s_err) atomicOr(&t.ctr->error, s_err);
   }
-  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
   for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
     PartEntry e[kBucketPer];
 #pragma unroll
@@ -921,8 +935,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
       const int pos = act ? atomicAdd(&s_cnt[h], 1) : 0;
       if (act) {
         L.res.grouped[s + pos] = e[k].g;
-        L.res.inverse[e[k].occ] = s_u[h];
-        occref[e[k].occ] = s_ref[h];
+        put_out(L, s + i0 + tid + k * kThreads, s_ref[h], s_u[h]);
       }
     }
   }
@@ -945,7 +958,6 @@ __device__ void heavy_occ(const LookupLaunch& L, const TableDev& t, int e0, int 
   const int tid = threadIdx.x;
   const int H = L.hslice[0];
   const int hs = 64 - L.nbits - kTabBits;
-  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
   for (int e = e0; e < H; e += step) {
   const int b = L.hslice[1 + 2 * e], k = L.hslice[2 + 2 * e];
   const int s = L.bbase[b], m = L.bbase[b + 1] - s;
@@ -993,8 +1005,7 @@ __device__ void heavy_occ(const LookupLaunch& L, const TableDev& t, int e0, int 
     const int pos = lds_add1(s_cnt, h, act);
     if (act) {
       L.res.grouped[pos] = en.g;
-      L.res.inverse[en.occ] = s_u[h];
-      occref[en.occ] = s_ref[h];
+      put_out(L, i, s_ref[h], s_u[h]);
     }
   }
   __syncthreads();  // the LDS table is reused by the next slice
@@ -1184,6 +1195,38 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
   if (threadIdx.x == 0 && s_err) atomicOr(&t.ctr->error, s_err);
 }
 
+// Each occurrence's inverse index and forward reference, in occurrence
+// order: one gather from the partition array through the position the
+// scatter noted, then contiguous stores.  Written in bucket order by the
+// bucket kernels instead, the 4- and 8-byte stores would land one per cache
+// line.  Blocks of one XCD take consecutive occurrences, as the partition
+// blocks did, so the lines they gather from are shared within its L2.
+constexpr int kOutPer = 4;
+__global__ __launch_bounds__(kThreads) void k_occ_out(LookupLaunch L) {
+  const int vb = xcd_block((int)blockIdx.x, (int)gridDim.x);
+  const long long j0 = (long long)vb * (kThreads * kOutPer) + threadIdx.x;
+  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
+  const PartOut* po = reinterpret_cast<const PartOut*>(L.part);
+  int p[kOutPer];
+#pragma unroll
+  for (int k = 0; k < kOutPer; ++k) {
+    const long long j = j0 + k * kThreads;
+    p[k] = j < L.N ? L.posmap[j] : 0;
+  }
+  PartOut o[kOutPer];
+#pragma unroll
+  for (int k = 0; k < kOutPer; ++k)
+    if (j0 + k * kThreads < L.N) o[k] = po[p[k]];
+#pragma unroll
+  for (int k = 0; k < kOutPer; ++k) {
+    const long long j = j0 + k * kThreads;
+    if (j < L.N) {
+      L.res.inverse[j] = o[k].u;
+      occref[j] = o[k].ref;
+    }
+  }
+}
+
 }  // namespace
 
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
@@ -1213,7 +1256,11 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
   // block 0 scans; the others (N > 0 only) write the heavy buckets' occurrences
   const long long kb = L.N > 0 ? 1 + (L.hmax < kHeavyBlocks / 4 ? L.hmax : kHeavyBlocks / 4) : 1;
   RECIS_LAUNCH("k_key_scan", k_key_scan, dim3((unsigned)kb), dim3(kScanThreads), s, L, t);
-  if (L.N > 0) RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.nbk), dim3(kThreads), s, L, t);
+  if (L.N > 0) {
+    RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.nbk), dim3(kThreads), s, L, t);
+    const long long ob = (L.N + kThreads * kOutPer - 1) / (kThreads * kOutPer);
+    RECIS_LAUNCH("k_occ_out", k_occ_out, dim3((unsigned)ob), dim3(kThreads), s, L);
+  }
 }
 
 }  // namespace recis

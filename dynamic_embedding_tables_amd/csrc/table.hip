@@ -219,7 +219,7 @@ PartGeom part_geom(long long n, int max_bits = kMaxBucketBits) {
 
 // Bytes of each per-step scratch array for cap occurrences.
 struct ScratchSizes {
-  size_t dd, part, hist, bbase, uslot, blk, wb, partials;
+  size_t dd, part, hist, bbase, uslot, posmap, blk, wb, partials;
 };
 ScratchSizes scratch_sizes(long long cap, int dim) {
   ScratchSizes z;
@@ -229,6 +229,7 @@ ScratchSizes scratch_sizes(long long cap, int dim) {
   z.hist = (size_t)g.blocks * (size_t)g.nbk * 4;
   z.bbase = (size_t)(kMaxBuckets + 1) * 4 * 2;  // bbase, then ubase
   z.uslot = (size_t)cap * 4;
+  z.posmap = (size_t)cap * 4;
   z.blk = (size_t)(kMaxBuckets + 2) * 8 * 2;  // per-bucket sums: blk_sums, then blk_long
   z.wb = (size_t)cap * 8;
   z.partials = (size_t)plan_layout(cap).max_chunks * (size_t)dim * 8;
@@ -243,12 +244,13 @@ void free_scratch(recis_table* t, hipStream_t s) {
   tab_free(t, t->hist, z.hist, s);
   tab_free(t, t->bbase, z.bbase, s);
   tab_free(t, t->uslot, z.uslot, s);
+  tab_free(t, t->posmap, z.posmap, s);
   tab_free(t, t->blk_sums, z.blk, s);
   tab_free(t, t->wb_keys, z.wb, s);
   tab_free(t, t->partials, z.partials, s);
   t->dd = nullptr;
   t->part = nullptr;
-  t->hist = t->bbase = t->ubase = t->uslot = nullptr;
+  t->hist = t->bbase = t->ubase = t->uslot = t->posmap = nullptr;
   t->blk_sums = nullptr;
   t->wb_keys = nullptr;
   t->partials = nullptr;
@@ -271,10 +273,11 @@ recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
   t->bbase = static_cast<int*>(tab_alloc(t, z.bbase, s));
   t->ubase = t->bbase ? t->bbase + (kMaxBuckets + 1) : nullptr;
   t->uslot = static_cast<int*>(tab_alloc(t, z.uslot, s));
+  t->posmap = static_cast<int*>(tab_alloc(t, z.posmap, s));
   t->blk_sums = static_cast<unsigned long long*>(tab_alloc(t, z.blk, s));
   t->wb_keys = static_cast<long long*>(tab_alloc(t, z.wb, s));
   t->partials = static_cast<double*>(tab_alloc(t, z.partials, s));
-  if (!t->dd || !t->part || !t->hist || !t->bbase || !t->uslot || !t->blk_sums || !t->wb_keys ||
+  if (!t->dd || !t->part || !t->hist || !t->bbase || !t->uslot || !t->posmap || !t->blk_sums || !t->wb_keys ||
       !t->partials) {
     free_scratch(t, s);
     return RECIS_ERR_OUT_OF_MEMORY;
@@ -517,6 +520,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.bbase = t->bbase;
   L.ubase = t->ubase;
   L.part = t->part;
+  L.posmap = t->posmap;
   L.blk_sums = t->blk_sums;
   L.blk_long = t->blk_sums + (kMaxBuckets + 2);
   // heavy-bucket bookkeeping lives in the writeback scratch (the two never
