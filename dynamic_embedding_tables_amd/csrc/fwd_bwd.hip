@@ -634,63 +634,126 @@ __global__ __launch_bounds__(256) void k_bwd_long_partial(BwdArgs a) {
   }
 }
 
-// Long keys, pass 2: one wave per long key sums its chunk partials (every
-// group loads kMergeBatch partials at a time, then a butterfly across the
-// groups; a fixed order, so runs repeat exactly) and applies the update.
+// Long keys, pass 2: the chunk partials of each long key are summed (each
+// group of lanes loads kMergeBatch partials at a time, then a butterfly
+// across the groups, in a fixed order) and the update applied.  A block
+// takes up to four keys at a time.  Those with more partials than a wave loads in
+// one round (a hot key has up to kMaxKeyChunks) are summed one after another
+// by all four waves, whose sums meet in LDS; then each wave sums its own key
+// if it has fewer.  With few long keys a block takes one or two at a time.
+template <int D, typename TP, int G_STRIDE, int E>
+__device__ __forceinline__ void sum_partials(const BwdArgs& a, int cb, int nch, int grp, int lane,
+                                             double (&G)[1][E]) {
+  constexpr int kMergeBatch = 4;
+#pragma unroll
+  for (int e = 0; e < E; ++e) G[0][e] = 0.0;
+  for (int p0 = 0; p0 < nch; p0 += G_STRIDE * kMergeBatch) {
+    double part[kMergeBatch][E];
+#pragma unroll
+    for (int m = 0; m < kMergeBatch; ++m) {
+      const int p = p0 + m * G_STRIDE + grp;
+      const double* pp = a.partials + (long long)(cb + (p < nch ? p : 0)) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part[m][e] = p < nch ? pp[e] : 0.0;
+    }
+#pragma unroll
+    for (int m = 0; m < kMergeBatch; ++m)
+#pragma unroll
+      for (int e = 0; e < E; ++e) G[0][e] += part[m][e];
+  }
+}
+
+// The update of long key u (row entry r >= 0) with its summed gradient, by
+// one group of C lanes.
+template <int D, typename TP, int OPT>
+__device__ __forceinline__ void long_update(const BwdArgs& a, int u, long long r, int lane, bool lead,
+                                            double (&G)[1][Vec<TP>::E]) {
+  constexpr int E = Vec<TP>::E;
+  constexpr int C = D / E;
+  const bool fresh = (r & kFreshRow) != 0;
+  r &= ~kFreshRow;
+  unsigned sl = 0;
+  bool pending = false;
+  if (fresh) {
+    sl = a.idslot[u];
+    pending = a.current ? true : (a.t.slots[sl].row & kPendingRow) != 0;
+  }
+  float wv[1][E], s0[1][E], s1[1][E];
+  char* rp = row_ptr(a.t.rs, r);
+  load_row<D, TP, OPT, C>(a, rp, pending, pending ? a.ukeys[u] : 0, lane, wv, s0, s1);
+  update_store<D, TP, OPT, C>(a, rp, lane, G, wv, s0, s1);
+  if (lead && fresh) {
+    if (pending) a.t.slots[sl].row = (int)r;
+    a.urows[u] = r;
+  }
+}
+
 template <int D, typename TP, int OPT>
 __global__ __launch_bounds__(256) void k_bwd_long_final(BwdArgs a) {
   constexpr int E = Vec<TP>::E;
   constexpr int C = D / E;
-  constexpr int GPW = 64 / C;
-  constexpr int kMergeBatch = 4;
-  const int wl = threadIdx.x & 63;
-  const int lane = wl % C, g = wl / C;
+  constexpr int GPW = 64 / C;   // groups per wave
+  constexpr int GPB = 256 / C;  // groups per block
+  constexpr int kWaveMerge = GPW * 4;  // partials one wave sums in one round
+  __shared__ double s_g[4][D];
+  __shared__ int s_u[4], s_cb[4], s_nch[4];
+  __shared__ long long s_r[4];
+  const int wl = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = wl % C;
   const int nlong = a.plan[0];
-  const long long nwaves = (long long)gridDim.x * 4;
-  for (long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); idx < nlong; idx += nwaves) {
-    const int u = a.plan[a.pl.o_long_u + idx];
-    const int cb = a.plan[a.pl.o_long_base + idx], nch = a.plan[a.pl.o_long_nch + idx];
-    long long r = a.urows[u];
-    if (r < 0) continue;  // no row (FIND_ONLY miss): nothing to update
-    const bool fresh = (r & kFreshRow) != 0;
-    r &= ~kFreshRow;
-    unsigned sl = 0;
-    bool pending = false;
-    if (fresh) {
-      sl = a.idslot[u];
-      pending = a.current ? true : (a.t.slots[sl].row & kPendingRow) != 0;
+  // keys per block and round: 1, 2 or 4, as few as the grid allows, so that
+  // the hot keys land in different blocks when there are few long keys
+  const int K = nlong <= (int)gridDim.x ? 1 : (nlong <= 2 * (int)gridDim.x ? 2 : 4);
+  for (long long q = blockIdx.x; q * K < nlong; q += gridDim.x) {
+    const long long idx = q * K + w;
+    int u = 0, cb = 0, nch = 0;
+    long long r = -1;  // no row (FIND_ONLY miss, or no key): nothing to update
+    if (w < K && idx < nlong) {
+      u = a.plan[a.pl.o_long_u + idx];
+      cb = a.plan[a.pl.o_long_base + idx];
+      nch = a.plan[a.pl.o_long_nch + idx];
+      r = a.urows[u];
     }
-    double G[1][E];
+    if (wl == 0) {
+      s_u[w] = u;
+      s_cb[w] = cb;
+      s_nch[w] = nch;
+      s_r[w] = r;
+    }
+    __syncthreads();
+    // the block's keys with many partials, one after another by all waves
+    for (int k = 0; k < 4; ++k) {
+      const long long rk = s_r[k];
+      if (rk < 0 || s_nch[k] <= kWaveMerge) continue;  // the same for the whole block
+      double G[1][E];
+      sum_partials<D, TP, GPB, E>(a, s_cb[k], s_nch[k], (int)threadIdx.x / C, lane, G);
 #pragma unroll
-    for (int e = 0; e < E; ++e) G[0][e] = 0.0;
-    for (int p0 = 0; p0 < nch; p0 += GPW * kMergeBatch) {
-      double part[kMergeBatch][E];
+      for (int m = C; m < 64; m <<= 1)
 #pragma unroll
-      for (int m = 0; m < kMergeBatch; ++m) {
-        const int p = p0 + m * GPW + g;
-        const double* pp = a.partials + (long long)(cb + (p < nch ? p : 0)) * D + lane * E;
+        for (int e = 0; e < E; ++e) G[0][e] += shfl_xor_d(G[0][e], m);
+      if (wl < C)
 #pragma unroll
-        for (int e = 0; e < E; ++e) part[m][e] = p < nch ? pp[e] : 0.0;
+        for (int e = 0; e < E; ++e) s_g[w][lane * E + e] = G[0][e];
+      __syncthreads();
+      if (w == 0 && wl < C) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          G[0][e] = ((s_g[0][lane * E + e] + s_g[1][lane * E + e]) + s_g[2][lane * E + e]) + s_g[3][lane * E + e];
+        long_update<D, TP, OPT>(a, s_u[k], rk, lane, wl == 0, G);
       }
-#pragma unroll
-      for (int m = 0; m < kMergeBatch; ++m)
-#pragma unroll
-        for (int e = 0; e < E; ++e) G[0][e] += part[m][e];
+      __syncthreads();  // s_g is reused by the next key
     }
+    // the others, each by its own wave
+    if (r >= 0 && nch <= kWaveMerge) {
+      double G[1][E];
+      sum_partials<D, TP, GPW, E>(a, cb, nch, wl / C, lane, G);
 #pragma unroll
-    for (int m = C; m < 64; m <<= 1)
+      for (int m = C; m < 64; m <<= 1)
 #pragma unroll
-      for (int e = 0; e < E; ++e) G[0][e] += shfl_xor_d(G[0][e], m);
-    if (g == 0) {
-      float w[1][E], s0[1][E], s1[1][E];
-      char* rp = row_ptr(a.t.rs, r);
-      load_row<D, TP, OPT, C>(a, rp, pending, pending ? a.ukeys[u] : 0, lane, w, s0, s1);
-      update_store<D, TP, OPT, C>(a, rp, lane, G, w, s0, s1);
+        for (int e = 0; e < E; ++e) G[0][e] += shfl_xor_d(G[0][e], m);
+      if (wl < C) long_update<D, TP, OPT>(a, u, r, lane, wl == 0, G);
     }
-    if (wl == 0 && fresh) {
-      if (pending) a.t.slots[sl].row = (int)r;
-      a.urows[u] = r;
-    }
+    __syncthreads();  // the key slots are reused by the next four keys
   }
 }
 
@@ -737,7 +800,10 @@ __device__ __forceinline__ void stage_key(const BwdArgs& a, int q, int nact, int
   }
 }
 
-// Short keys (<= kShortMax entries).  A block takes kBwdKeys consecutive keys.
+// Short keys (<= kShortMax entries).  A block takes a tile of consecutive
+// keys: kBwdKeys, or fewer when there are not enough keys for a full tile
+// per block (a call with few distinct keys would otherwise leave most of
+// the chip idle).
 // Phase 1, one thread per key: metadata and the row's address (the block
 // table is read here once, not per update), and one packed block scan that
 // gives each key its staged-entry base and its place in an order with the
@@ -771,12 +837,16 @@ __global__ __launch_bounds__(256, (bwd_short_waves<D, TP>())) void k_bwd_short(B
   __shared__ double s_sc[kBwdStage];
   __shared__ int s_nact;
   const long long U = *a.num_unique;
-  for (long long t0 = (long long)blockIdx.x * kBwdKeys; t0 < U; t0 += (long long)gridDim.x * kBwdKeys) {
+  // keys per tile: kBwdKeys, or fewer (a multiple of 32) when the call has
+  // too few distinct keys to give every block a full tile
+  const long long per = (U + gridDim.x - 1) / gridDim.x;
+  const int T = per >= kBwdKeys ? kBwdKeys : (per <= 32 ? 32 : (int)((per + 31) & ~31ll));
+  for (long long t0 = (long long)blockIdx.x * T; t0 < U; t0 += (long long)gridDim.x * T) {
     const long long u = t0 + tid;
     int c = 0, o = 0, st = 0;  // st: 0 written row, 1 fresh but written, 2 pending
     long long r = -1, key = 0;
     unsigned sl = 0;
-    if (u < U) {
+    if (tid < T && u < U) {
       c = a.counts[u];
       o = a.uoff[u];
       r = a.urows[u];
@@ -938,8 +1008,8 @@ void bwd_dispatch(BwdArgs a, long long n, hipStream_t s) {
   long long lb = (n / kChunk + 4) / 4;
   lb = lb > 2048 ? 2048 : (lb < 1 ? 1 : lb);
   RECIS_LAUNCH("k_bwd_long_partial", (k_bwd_long_partial<D, TP>), dim3((unsigned)lb), dim3(256), s, a);
-  long long fb = (n / kShortMax + 4) / 4;  // long keys <= n / (kShortMax + 1)
-  fb = fb > 1024 ? 1024 : (fb < 1 ? 1 : fb);
+  long long fb = (n / (kShortMax + 1) + 4) / 4;  // long keys <= n / (kShortMax + 1), four per block
+  fb = fb > 2048 ? 2048 : (fb < 1 ? 1 : fb);
   RECIS_LAUNCH("k_bwd_long_final", (k_bwd_long_final<D, TP, OPT>), dim3((unsigned)fb), dim3(256), s, a);
   long long sb = (n + kBwdKeys - 1) / kBwdKeys;
   sb = sb > 4096 ? 4096 : (sb < 1 ? 1 : sb);
