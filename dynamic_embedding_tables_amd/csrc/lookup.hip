@@ -263,16 +263,27 @@ __global__ __launch_bounds__(kPartThreads) void k_part_colscan(LookupLaunch L) {
       *p = run;
       run += v;
     }
-    if (w == 0) {
+  }
+  if (w == 0) {
+    int ns = 0, e0 = 0;
+    if (b < L.nbk) {
       L.bbase[b] = all;  // total, scanned by k_scan_small
       L.ubase[b] = 0;    // a light bucket's block writes it, a heavy one's slices add to it
-      if (all > kHeavyOcc) {  // a heavy bucket: list its slices (few buckets, so one atomic each)
-        const int ns = (all + kSliceOcc - 1) / kSliceOcc;
-        const int e0 = atomicAdd(&L.hslice[0], ns);
-        for (int q = 0; q < ns; ++q) {
-          L.hslice[1 + 2 * (e0 + q)] = b;
-          L.hslice[2 + 2 * (e0 + q)] = q;
-        }
+      if (all > kHeavyOcc) {  // a heavy bucket: its slices (few buckets, so one atomic each)
+        ns = (all + kSliceOcc - 1) / kSliceOcc;
+        e0 = atomicAdd(&L.hslice[0], ns);
+      }
+    }
+    // the wave lists each heavy bucket's slices together (a hot key's bucket
+    // has hundreds)
+    unsigned long long hv = __ballot(ns > 0);
+    while (hv) {
+      const int l = __ffsll((long long)hv) - 1;
+      hv &= hv - 1;
+      const int nsl = __shfl(ns, l), e0l = __shfl(e0, l), bl = __shfl(b, l);
+      for (int q = lane; q < nsl; q += 64) {
+        L.hslice[1 + 2 * (e0l + q)] = bl;
+        L.hslice[2 + 2 * (e0l + q)] = q;
       }
     }
   }
