@@ -297,6 +297,34 @@ def test_one_key_dominates():
     run_parity(spec, [b, b])
 
 
+def _long_keys_batch(seed, step, nkeys, per_key, hot, hot_count):
+    """nkeys keys (drawn from `seed`) with per_key occurrences each plus `hot`
+    keys with hot_count each, shuffled (by `step`) over bags of 8, the last
+    one taking the rest."""
+    keys = W.rng_for(seed).choice(1 << 40, nkeys + hot, replace=False).astype(np.int64)
+    rng = W.rng_for(seed, step)
+    vals = np.concatenate([np.repeat(keys[:nkeys], per_key), np.repeat(keys[nkeys:], hot_count)])
+    rng.shuffle(vals)
+    B = vals.size // 8
+    lens = np.full(B, 8, dtype=np.int64)
+    lens[-1] += vals.size - 8 * B
+    off = W.offsets_from_lengths(lens)
+    return W.Batch([W.FeatureInput(values=vals, bag_offsets=off, slot=1)], B,
+                   rng.standard_normal((B, 64), dtype=np.float32))
+
+
+@pytest.mark.parametrize("per_key", [100, 200])
+def test_many_long_keys(per_key):
+    """Thousands of keys just past the short path's 64 occurrences, so that
+    the merge of the chunk partials takes four (100 occurrences each) or two
+    (200 each) keys per block, mixed with hot keys whose partials a whole
+    block merges; the same keys again in a second step (stored rows)."""
+    spec = W.TableSpec(dim=64, dtype="f32", optim="adam", pool="sum", lr=1e-3, eps=1e-8)
+    a = _long_keys_batch(90 + per_key, 0, 3000, per_key, 4, 5000)
+    b = _long_keys_batch(90 + per_key, 1, 3000, per_key, 4, 5000)
+    run_parity(spec, [a, b])
+
+
 @pytest.mark.parametrize("pool,admit", [("mean", 1), ("sum", 2)])
 def test_heavy_buckets(pool, admit):
     """Hot keys whose buckets exceed the single-block size (tens of thousands
