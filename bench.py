@@ -15,6 +15,10 @@ batch 2048, dim 128 bf16 storage, gather only, bf16 gradients, Adagrad),
 capacity stress (200M pre-populated rows of dim 64 fp32 + Adam, 100 features,
 batch 65536, Poisson(8) bags, 2% novel IDs, sum pooling).
 
+--block-memory host puts the EmbeddingBlocks in pinned host memory (the
+IDMap and scratch stay in HBM); the roofline is then taken against the host
+link, and the line also gives a pinned copy's rate in each direction.
+
 A step is one pass of the whole path through the C ABI: insert_find
 (transform, dedup, IDMap insert / find) -> lookup_pool_fwd -> pool_bwd_update
 (duplicate-gradient reduce + optimizer).  Inputs (IDs, bag offsets, upstream
@@ -44,6 +48,8 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# the host link of an MI355X: PCIe 5.0 x16, 64 GB/s in each direction
+LINK_PEAK_GBS = 64.0
 RESIDENT_TARGET = 20_000_000
 
 
@@ -232,6 +238,34 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
             "k_bwd_long_partial": long_partial, "step": ins + fwd_call + bwd_call}
 
 
+def link_bytes(kernel, shape, Uhit, D, s=4, S=2):
+    """(read, written) bytes of EmbeddingBlock rows that `kernel` moves across
+    the host link per launch when the blocks are in host memory (the IDMap,
+    inputs, outputs and scratch stay in HBM): the rows the method must read
+    and write, as in algorithmic_bytes."""
+    P = D * s + S * D * 4
+    Us, Usn = shape["U_s"], shape["U_s_new"]
+    return {"k_bwd_short": ((Us - Usn) * P, Us * P),
+            "k_fwd_pool": (Uhit * D * s, 0), "k_fwd_gather": (Uhit * D * s, 0),
+            "k_bwd_long_final": (shape["U_l"] * P, shape["U_l"] * P)}.get(kernel, (0, 0))
+
+
+def host_link_copy(torch, dev, nbytes=1 << 30):
+    """GB/s of one pinned host-to-device and one device-to-host copy."""
+    h = torch.empty(nbytes // 4, dtype=torch.float32, pin_memory=True)
+    d = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    out = {}
+    for name, (dst, src) in (("h2d", (d, h)), ("d2h", (h, d))):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src, non_blocking=True)  # once untimed
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = nbytes / (a.elapsed_time(b) * 1e-3) / 1e9
+    return out
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -333,6 +367,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: the workload's)")
     ap.add_argument("--resident", type=int, default=RESIDENT_TARGET, help="CTR: rows resident before warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-memory", choices=["device", "host"], default="device",
+                    help="where the EmbeddingBlocks live: HBM, or pinned host memory across the host link")
     ap.add_argument("--workers", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run plain device copies of known size (for HBM counter scaling)")
@@ -382,10 +418,13 @@ def main():
     pre_rows = sum(k.shape[0] for _, k in resident_keys)
     if wl["fill"] == "keys":  # a call may add up to its N rows; 2% of N are new per step
         reserve = pre_rows + cap + (Wm + K + 1) * (cap // 30)
+    elif wl["fill"] == "resident":  # the fill stops within one step of the target
+        reserve = args.resident + (Wm + K + 3) * wl["new_per_step"]
     else:
-        reserve = (args.resident if wl["fill"] == "resident" else 0) + (fill_steps + Wm + K + 2) * wl["new_per_step"]
+        reserve = (fill_steps + Wm + K + 2) * wl["new_per_step"]
     table = recis.Table(D, spec.dtype, spec.optim, seed=spec.seed, init_bound=spec.init_bound,
-                        admit_threshold=spec.admit_threshold, reserve_rows=reserve, **wl["table"])
+                        admit_threshold=spec.admit_threshold, reserve_rows=reserve,
+                        block_memory=args.block_memory, **wl["table"])
     gen = torch.Generator(device=dev)
     gen.manual_seed(20250925)
     pdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -549,7 +588,15 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "kernel_ms": t_dom * 1e3,
                      "algorithmic_bytes": a_bytes, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
-                     "traffic": traffic},
+                     "traffic": traffic} if args.block_memory == "device" else
+        # rows in host memory: the dominant kernel against the host link, in
+        # the direction that carries more of its row bytes
+        {"bound": "host-link", "kernel": dom, "kernel_ms": t_dom * 1e3,
+         "link_bytes_read_written": list(link_bytes(dom, shape, Uhit, D, s_bytes, S)),
+         "achieved": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9,
+         "peak": LINK_PEAK_GBS, "unit": "GB/s",
+         "frac": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9 / LINK_PEAK_GBS,
+         "traffic": None},
         "warmup_kernel_ms": {k: float(np.mean(v)) for k, v in probe_ms.items()},
         # every kernel timed in the warm-up (one launch each), against the same
         # algorithmic bytes as the roofline above
@@ -560,7 +607,10 @@ def main():
                              for k, v in probe_ms.items()},
         "backward_key_split": shape,
     }
-    if args.workload == "ctr" and not args.no_cpu_baseline:
+    if args.block_memory == "host":
+        result["config"]["block_memory"] = "host (pinned, mapped; IDMap and scratch in HBM)"
+        result["host_link_copy_GBps"] = host_link_copy(torch, dev)
+    if args.workload == "ctr" and args.block_memory == "device" and not args.no_cpu_baseline:
         table.close()
         torch.cuda.synchronize()
         result["cpu_baseline"] = cpu_baseline()

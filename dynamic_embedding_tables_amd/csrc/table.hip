@@ -97,6 +97,29 @@ recis_status check_launch() {
 }
 
 // Adds blocks until at least `rows` rows are covered (capped at max_rows).
+// One EmbeddingBlock: device memory from the allocator, or pinned host
+// memory mapped for the GPU (non-coherent, so the GPU may cache it within a
+// kernel; nothing else writes it while kernels run).
+char* block_alloc(recis_table* t, size_t bytes, hipStream_t s) {
+  if (t->cfg.block_memory != RECIS_MEM_HOST) return static_cast<char*>(tab_alloc(t, bytes, s));
+  void* h = nullptr;
+  if (hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocNonCoherent) != hipSuccess) return nullptr;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess || d != h) {  // one address for both sides
+    (void)hipHostFree(h);
+    return nullptr;
+  }
+  return static_cast<char*>(h);
+}
+
+void block_free(recis_table* t, char* b, hipStream_t s) {
+  if (t->cfg.block_memory != RECIS_MEM_HOST) {
+    tab_free(t, b, (size_t)(t->cfg.block_rows * t->row_bytes), s);
+    return;
+  }
+  (void)hipHostFree(b);
+}
+
 recis_status grow_rows(recis_table* t, long long rows, hipStream_t s) {
   rows = std::min<long long>(rows, t->cfg.max_rows);
   if (rows <= t->rows_alloc) return RECIS_OK;
@@ -114,7 +137,7 @@ recis_status grow_rows(recis_table* t, long long rows, hipStream_t s) {
     t->d_blocks_cap = cap;
   }
   while ((long long)t->blocks.size() < nblocks) {
-    char* b = static_cast<char*>(tab_alloc(t, (size_t)(br * t->row_bytes), s));
+    char* b = block_alloc(t, (size_t)(br * t->row_bytes), s);
     if (!b) return RECIS_ERR_OUT_OF_MEMORY;
     t->blocks.push_back(b);
   }
@@ -372,6 +395,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   if (cfg->block_rows < 1 || cfg->block_rows > (1ll << 30)) return RECIS_ERR_INVALID_ARG;
   if (cfg->max_rows < 1 || cfg->max_rows > kMaxRows) return RECIS_ERR_INVALID_ARG;
   if (cfg->reserve_rows < 0) return RECIS_ERR_INVALID_ARG;
+  if (cfg->block_memory != RECIS_MEM_DEVICE && cfg->block_memory != RECIS_MEM_HOST) return RECIS_ERR_INVALID_ARG;
   if (alloc && (!alloc->alloc || !alloc->free)) return RECIS_ERR_INVALID_ARG;
   if (!valid_dim(cfg->dim)) return RECIS_ERR_UNSUPPORTED;
 
@@ -415,7 +439,7 @@ recis_status recis_idmap_destroy(recis_table* t) {
   ScopedProbe sp(t);
   hipStream_t s = nullptr;
   (void)hipDeviceSynchronize();
-  for (char* b : t->blocks) tab_free(t, b, (size_t)(t->cfg.block_rows * t->row_bytes), s);
+  for (char* b : t->blocks) block_free(t, b, s);
   tab_free(t, t->d_blocks, t->d_blocks_cap * sizeof(char*), s);
   tab_free(t, t->free_list, (size_t)t->free_cap * 4, s);
   tab_free(t, t->slots, (size_t)t->slot_cap * sizeof(Slot), s);

@@ -31,6 +31,8 @@ RECIS_DTYPE_BF16 = 1
 RECIS_OPTIM_NONE = 0
 RECIS_OPTIM_ADAGRAD = 1
 RECIS_OPTIM_ADAM = 2
+RECIS_MEM_DEVICE = 0
+RECIS_MEM_HOST = 1
 RECIS_POOL_SUM = 0
 RECIS_POOL_MEAN = 1
 RECIS_POOL_NONE = 2
@@ -56,7 +58,7 @@ class recis_table_config(C.Structure):
     _fields_ = [("dim", C.c_int32), ("dtype", C.c_int32), ("optim", C.c_int32),
                 ("admit_threshold", C.c_uint32), ("seed", C.c_uint64), ("init_bound", C.c_float),
                 ("max_load", C.c_float), ("slot_capacity", C.c_int64), ("block_rows", C.c_int64),
-                ("max_rows", C.c_int64), ("reserve_rows", C.c_int64)]
+                ("max_rows", C.c_int64), ("reserve_rows", C.c_int64), ("block_memory", C.c_int32)]
 
 
 class recis_allocator(C.Structure):
@@ -290,12 +292,13 @@ class Table:
     def __init__(self, dim: int, dtype: str = "f32", optim: str = "adagrad", seed: int = 20250925,
                  init_bound: float = 0.05, admit_threshold: int = 1, slot_capacity: int = 1 << 20,
                  block_rows: int = 1 << 20, max_rows: int = (1 << 30) - 1, reserve_rows: int = 0,
-                 max_load: float = 0.5, stream=None):
+                 max_load: float = 0.5, block_memory: str = "device", stream=None):
         cfg = recis_table_config_default()
         cfg.dim, cfg.dtype, cfg.optim = dim, DTYPES[dtype], OPTIMS[optim]
         cfg.seed, cfg.init_bound, cfg.admit_threshold = seed, init_bound, admit_threshold
         cfg.slot_capacity, cfg.block_rows, cfg.max_rows = slot_capacity, block_rows, max_rows
         cfg.reserve_rows, cfg.max_load = reserve_rows, max_load
+        cfg.block_memory = {"device": RECIS_MEM_DEVICE, "host": RECIS_MEM_HOST}[block_memory]
         self.dim, self.dtype, self.optim = dim, dtype, optim
         self.h = recis_idmap_create(cfg, stream)
 

@@ -64,6 +64,15 @@ typedef int32_t recis_status;
 #define RECIS_OPTIM_ADAGRAD 1 /* 1 state word per element: accumulated G^2 */
 #define RECIS_OPTIM_ADAM 2    /* 2 state words per element: m, v */
 
+/* Where the EmbeddingBlocks live (the pages let both tiers sit on the GPU or
+ * the CPU: page "RecIS (Recommendation Intelligence System)" README, section
+ * "Key optimisations > Efficient dynamic Embedding").  HOST blocks are pinned
+ * host memory mapped into the GPU's address space: the kernels read and write
+ * rows across the host link, and the table can hold more rows than HBM.  The
+ * IDMap and all scratch stay in HBM either way. */
+#define RECIS_MEM_DEVICE 0
+#define RECIS_MEM_HOST 1
+
 #define RECIS_POOL_SUM 0
 #define RECIS_POOL_MEAN 1
 #define RECIS_POOL_NONE 2 /* gather only: one output row per occurrence */
@@ -97,10 +106,14 @@ typedef struct {
   int64_t block_rows;       /* rows per EmbeddingBlock (rounded up to a power of two) */
   int64_t max_rows;         /* hard row limit (<= 2^30 - 1) */
   int64_t reserve_rows;     /* rows allocated at creation (rounded up to whole blocks) */
+  int32_t block_memory;     /* RECIS_MEM_DEVICE (from the allocator) or RECIS_MEM_HOST
+                               (hipHostMalloc, non-coherent: rows may be cached by the GPU
+                               during a call, so the host must not touch them directly) */
 } recis_table_config;
 
 /* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
- * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0). */
+ * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0,
+ * blocks in device memory). */
 void recis_table_config_default(recis_table_config* cfg);
 
 /* Device-memory provider.  alloc returns `bytes` of device memory (256-byte
@@ -170,7 +183,7 @@ typedef struct {
   int64_t blocks;
   int64_t slot_capacity;
   int64_t adam_step;
-  int64_t bytes;          /* device bytes owned by the table */
+  int64_t bytes;          /* device bytes owned by the table (host blocks not included) */
 } recis_table_stats;
 
 /* Creates a table.  Allocates the IDMap and `reserve_rows` worth of blocks

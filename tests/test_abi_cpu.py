@@ -72,6 +72,7 @@ def test_config_defaults_and_plan_words(lib):
     c = lib.recis_table_config_default()
     assert c.dim == 64 and c.dtype == lib.RECIS_DTYPE_F32 and c.optim == lib.RECIS_OPTIM_ADAGRAD
     assert abs(c.init_bound - 0.05) < 1e-9 and c.max_load == 0.5 and c.max_rows == 2**30 - 1
+    assert c.block_memory == lib.RECIS_MEM_DEVICE
     assert lib.recis_plan_words(0) > 0
     assert lib.recis_plan_words(1 << 20) > lib.recis_plan_words(1 << 10)
     assert lib.recis_plan_words(-1) == -1
@@ -91,7 +92,7 @@ def test_invalid_arguments_return_synchronously(lib):
     assert L.recis_idmap_create(C.byref(c), None, None, None) == lib.RECIS_ERR_INVALID_ARG
     for field, bad in [("dtype", 7), ("optim", 9), ("max_load", 0.0), ("max_load", 0.8),
                        ("slot_capacity", 0), ("block_rows", 0), ("max_rows", 0), ("max_rows", 2**30),
-                       ("reserve_rows", -1), ("init_bound", -1.0)]:
+                       ("reserve_rows", -1), ("init_bound", -1.0), ("block_memory", 2)]:
         c = lib.recis_table_config_default()
         setattr(c, field, bad)
         assert L.recis_idmap_create(C.byref(c), None, None, C.byref(h)) == lib.RECIS_ERR_INVALID_ARG, field
@@ -149,3 +150,13 @@ def test_binding_fails_loudly_without_library(lib, monkeypatch, tmp_path):
     with pytest.raises(ImportError):
         r.load_library()
     importlib.reload(r)
+
+
+def test_binding_constants_match_the_header(lib):
+    """Every integer #define of include/recis.h has the same value in the binding."""
+    import re
+    text = open(os.path.join(ROOT, "include", "recis.h")).read()
+    found = re.findall(r"^#define (RECIS_[A-Z0-9_]+) (\d+)u?\b", text, flags=re.M)
+    assert len(found) > 20
+    for name, value in found:
+        assert getattr(lib, name) == int(value), name

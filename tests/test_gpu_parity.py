@@ -124,6 +124,24 @@ def test_growth_of_idmap_and_blocks():
                table_kw=dict(slot_capacity=64, block_rows=64))
 
 
+# ---- EmbeddingBlocks in pinned host memory (the IDMap and scratch in HBM)
+def test_host_memory_blocks_ctr():
+    """The CTR step with small blocks, so rows spread over many host blocks
+    that are added as the table grows."""
+    run_parity(W.spec_ctr(), [W.ctr_batch(s, batch=256) for s in range(3)],
+               table_kw=dict(block_rows=4096, block_memory="host"))
+
+
+def test_host_memory_blocks_sequence_and_eviction():
+    """The bf16 gather with hot keys, and a table with admission and an
+    eviction pass, both on host blocks."""
+    run_parity(W.spec_seq(), [W.seq_batch(s, batch=12, seq_len=1000) for s in range(2)],
+               table_kw=dict(block_memory="host"))
+    spec = W.spec_multi(1)
+    run_parity(spec, [W.multi_batch(s, 1, batch=128, num_feats=6) for s in range(4)], evict_every=2,
+               table_kw=dict(block_memory="host"))
+
+
 def test_initial_rows_bit_exact():
     import torch
     from dynamic_embedding_tables_amd import recis
