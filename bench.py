@@ -309,15 +309,17 @@ def _kernel_label(name):
     return name[:60]
 
 
-def summarize(prof_dir, kernel, command, out_path, workload="ctr"):
+def summarize(prof_dir, kernel, command, out_path, workload="ctr", block_memory="device"):
     """Writes the committed summary of a profiled bench run: per-kernel mean
     durations (rocprofv3 --kernel-trace --stats, csv) from prof_dir/trace, and
     for `kernel` the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch, from
-    prof_dir/fetch and prof_dir/write) scaled by the same counters of the
-    plain copies of COPY_BYTES that --copy-calibration runs."""
+    prof_dir/fetch and prof_dir/write, when those runs exist) scaled by the
+    same counters of the plain copies of COPY_BYTES that --copy-calibration
+    runs."""
     import csv
     stats = list(csv.DictReader(open(os.path.join(prof_dir, "trace", "p_kernel_stats.csv"))))
-    lines = [f"# rocprofv3 summary: {kernel} on the workload: {WORKLOADS[workload]['title']}",
+    where = "" if block_memory == "device" else " (EmbeddingBlocks in pinned host memory)"
+    lines = [f"# rocprofv3 summary: {kernel} on the workload: {WORKLOADS[workload]['title']}{where}",
              f"# command: {command}", f"kernel={kernel}", f"source_hash={kernel_source_hash()}"]
     dur = {}
     for r in stats:
@@ -328,6 +330,13 @@ def summarize(prof_dir, kernel, command, out_path, workload="ctr"):
         lines.append(f"kernel_avg_us[{lab}]={avg / 1e3:.2f}  calls={sum(c for _, c, _ in v)}  "
                      f"pct={sum(p for *_, p in v):.2f}")
     lines.append(f"avg_duration_us={sum(a * c for a, c, _ in dur[kernel]) / sum(c for _, c, _ in dur[kernel]) / 1e3:.2f}")
+    # the timed steps are the last dispatches of the run (the table fill
+    # before the warm-up can call the same kernel on other sizes)
+    trace = [r for r in csv.DictReader(open(os.path.join(prof_dir, "trace", "p_kernel_trace.csv")))
+             if _kernel_label(r["Kernel_Name"]) == kernel]
+    last = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace[-5:]]
+    if last:
+        lines.append(f"timed_steps_avg_duration_us={np.mean(last) / 1e3:.2f}  (last {len(last)} dispatches)")
 
     def counter(sub, cname):
         rows = list(csv.DictReader(open(os.path.join(prof_dir, sub, "p_counter_collection.csv"))))
@@ -343,6 +352,10 @@ def summarize(prof_dir, kernel, command, out_path, workload="ctr"):
                 continue
             per.setdefault(lab, []).append(v)
         return per
+    if not os.path.isdir(os.path.join(prof_dir, "fetch")):  # a kernel-trace run only
+        open(out_path, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
     cf, cw = fetch.get("copy", [])[-3:], write.get("copy", [])[-3:]
     kf, kw = fetch.get(kernel, []), write.get(kernel, [])
@@ -382,7 +395,7 @@ def main():
     if args.summarize:
         summarize(args.summarize, args.kernel, args.command,
                   args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{args.workload}_counters.txt"),
-                  args.workload)
+                  args.workload, args.block_memory)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
