@@ -266,6 +266,41 @@ def host_link_copy(torch, dev, nbytes=1 << 30):
     return out
 
 
+def export_import(torch, recis, table, spec, wl, D, s, S, block_memory):
+    """The device side of a save and restore: the whole table exported to
+    device arrays, then imported into a new table with room for it.  The
+    import kernel moves per key its key, row flag and count (20 B) and its
+    IDMap slot (16 B), and per key with a row the row's P bytes read and P
+    written."""
+    P = D * s + S * D * 4
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ex = table.export()
+    torch.cuda.synchronize()
+    t_export = time.perf_counter() - t0
+    n = int(ex["keys"].shape[0])
+    nrow = int((ex["rows"] >= 0).sum().item())
+    fresh = recis.Table(D, spec.dtype, spec.optim, seed=spec.seed, init_bound=spec.init_bound,
+                        admit_threshold=spec.admit_threshold, reserve_rows=nrow + 1,
+                        slot_capacity=wl["table"]["slot_capacity"], block_rows=wl["table"]["block_rows"],
+                        block_memory=block_memory)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    counts = ex["counts"]
+    a.record()
+    fresh.import_(ex["keys"], ex["rows"], counts, ex["params"], ex["state"] if S else None)
+    b.record()
+    torch.cuda.synchronize()
+    fresh.check()
+    st = fresh.stats()
+    assert st.keys == n and st.rows_in_use == nrow, (st.keys, n, st.rows_in_use, nrow)
+    t_import = a.elapsed_time(b) * 1e-3
+    alg = 36 * n + 2 * P * nrow
+    fresh.close()
+    return {"keys": n, "rows": nrow, "export_s": t_export, "import_ms": t_import * 1e3,
+            "import_algorithmic_bytes": alg, "import_GBps": alg / t_import / 1e9,
+            "import_frac": alg / t_import / 1e9 / HBM_PEAK_GBS}
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -380,6 +415,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: the workload's)")
     ap.add_argument("--resident", type=int, default=RESIDENT_TARGET, help="CTR: rows resident before warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--export-import", action="store_true",
+                    help="after the timed steps, export the whole table and import it into a new one (the "
+                         "device side of saving and restoring), timed against the HBM roofline")
     ap.add_argument("--block-memory", choices=["device", "host"], default="device",
                     help="where the EmbeddingBlocks live: HBM, or pinned host memory across the host link")
     ap.add_argument("--workers", type=int, default=8)
@@ -620,6 +658,8 @@ def main():
                              for k, v in probe_ms.items()},
         "backward_key_split": shape,
     }
+    if args.export_import:
+        result["export_import"] = export_import(torch, recis, table, spec, wl, D, s_bytes, S, args.block_memory)
     if args.block_memory == "host":
         result["config"]["block_memory"] = "host (pinned, mapped; IDMap and scratch in HBM)"
         result["host_link_copy_GBps"] = host_link_copy(torch, dev)

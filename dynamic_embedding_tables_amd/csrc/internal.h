@@ -436,5 +436,7 @@ void launch_export(const TableDev& t, long long cap, long long* keys, long long*
                    unsigned* counts, hipStream_t s);
 void launch_export_rows(const TableDev& t, long long n, const long long* keys, long long* rows, void* params,
                         float* state, hipStream_t s);
+void launch_import(const TableDev& t, long long n, const long long* keys, const long long* rows,
+                   const unsigned* counts, const void* params, const float* state, hipStream_t s);
 
 }  // namespace recis

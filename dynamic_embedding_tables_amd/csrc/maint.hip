@@ -281,22 +281,135 @@ __global__ void k_export_rows(TableDev t, long long n, const long long* keys, lo
   const int es = t.dtype == RECIS_DTYPE_BF16 ? 2 : 4;
   const long long pbytes = (long long)t.dim * es;
   const int sw = t.state_words * t.dim;
-  for (long long k = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); k < n; k += (long long)gridDim.x * 4) {
-    long long r = rows[k];
+  const int pchunks = (int)(pbytes >> 4), schunks = state ? sw >> 2 : 0;  // 16-byte chunks (rows are 16-aligned)
+  const int cpr = pchunks + schunks;
+  constexpr int kCopy = 4;
+  for (long long k0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64; k0 < n;
+       k0 += (long long)gridDim.x * 4 * 64) {
+    // one key per lane: its row, without the pending mark
+    const long long k = k0 + lane;
+    long long r = k < n ? rows[k] : -1;
     const bool pending = r >= 0 && (r & kPendingRow);
     if (pending) r &= ~(long long)kPendingRow;
-    const char* rp = r >= 0 && !pending ? row_ptr(t.rs, r) : nullptr;
-    if (pending) {
-      for (int c = lane; c < (int)(pbytes >> 4); c += 64)
-        reinterpret_cast<uint4*>(params + k * pbytes)[c] = init_chunk(t, keys[k], c);
-    } else {
-      for (long long b = lane; b < pbytes; b += 64) params[k * pbytes + b] = rp ? rp[b] : 0;
+    const long long key = k < n ? keys[k] : 0;
+    // then the wave's rows as one list of 16-byte chunks (key j, chunk c);
+    // a pending row is the initializer's, a key without a row gets zeros
+    for (int i0 = 0; i0 < 64 * cpr; i0 += 64 * kCopy) {
+      uint4 v[kCopy];
+      uint4* dst[kCopy];
+#pragma unroll
+      for (int x = 0; x < kCopy; ++x) {
+        const int idx = i0 + x * 64 + lane;
+        const int j = idx / cpr, c = idx - j * cpr;
+        const int js = j < 64 ? j : 0;
+        const long long rj = __shfl(r, js);
+        const bool pj = __shfl((int)pending, js) != 0;
+        const long long keyj = __shfl(key, js);
+        const long long kj = k0 + j;
+        v[x] = make_uint4(0, 0, 0, 0);
+        dst[x] = nullptr;
+        if (idx >= 64 * cpr || kj >= n) continue;
+        dst[x] = c < pchunks ? reinterpret_cast<uint4*>(params) + kj * pchunks + c
+                             : reinterpret_cast<uint4*>(state) + kj * schunks + (c - pchunks);
+        if (rj >= 0 && pj) {
+          if (c < pchunks) v[x] = init_chunk(t, keyj, c);
+        } else if (rj >= 0) {
+          v[x] = reinterpret_cast<const uint4*>(row_ptr(t.rs, rj))[c];
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < kCopy; ++x)
+        if (dst[x]) *dst[x] = v[x];
     }
-    if (state) {
-      const float* st = rp ? reinterpret_cast<const float*>(rp + pbytes) : nullptr;
-      for (int e = lane; e < sw; e += 64) state[k * sw + e] = st ? st[e] : 0.f;
+    if (k < n) rows[k] = r;
+  }
+}
+
+// Import (the inverse of export, into an empty table).  One key per lane:
+// it is entered into the IDMap with its count (a key already there is an
+// input error), and the keys that had a row get the next rows of the bump
+// pointer, one atomic per wave.  Then the wave copies its keys' rows, 16
+// bytes per lane: the parameters as given (storage dtype), then the state.
+__global__ __launch_bounds__(256) void k_import(TableDev t, long long n, const long long* keys,
+                                                const long long* rows_in, const unsigned* counts,
+                                                const char* params, const float* state) {
+  const int lane = threadIdx.x & 63;
+  const int es = t.dtype == RECIS_DTYPE_BF16 ? 2 : 4;
+  const long long pbytes = (long long)t.dim * es;
+  const long long sbytes = (long long)t.state_words * t.dim * 4;
+  const int pchunks = (int)(pbytes >> 4), schunks = (int)(sbytes >> 4);
+  for (long long k0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64; k0 < n;
+       k0 += (long long)gridDim.x * 4 * 64) {
+    const long long k = k0 + lane;
+    long long at = -1;
+    bool want_row = false;
+    unsigned err = 0;
+    if (k < n) {
+      const long long key = keys[k];
+      if (key < 0) {
+        err = kErrKeyRange;
+      } else {
+        unsigned long long p = slot_of(key, t.slot_shift);
+        for (unsigned long long q = 0; q <= t.region_mask; ++q) {
+          const long long cur = t.slots[p].key;
+          if (cur == key) {
+            err = kErrInvalid;  // the key is in the input twice
+            break;
+          }
+          if (cur == kEmptyKey) {
+            const long long old = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
+                                                       (unsigned long long)kEmptyKey, (unsigned long long)key);
+            if (old == kEmptyKey) {
+              at = (long long)p;
+              break;
+            }
+            if (old == key) {
+              err = kErrInvalid;
+              break;
+            }
+          }
+          p = next_slot(t, p);
+        }
+        if (at < 0 && !err) err = kErrCapacity;
+      }
+      want_row = at >= 0 && rows_in[k] >= 0;
     }
-    if (lane == 0) rows[k] = r;
+    const long long row = wave_add(&t.ctr->next_row, want_row);
+    (void)wave_add(&t.ctr->num_keys, at >= 0);
+    long long r = -1;
+    if (at >= 0) {
+      t.slots[at].count = counts[k];
+      if (want_row && row < t.rows_limit) r = row;
+      else if (want_row) err |= kErrCapacity;
+      t.slots[at].row = r >= 0 ? (int)r : -1;
+    }
+    if (err) atomicOr(&t.ctr->error, err);
+    // the wave's rows as one list of 16-byte chunks (row j, chunk c), kCopy
+    // loads in flight per lane
+    constexpr int kCopy = 4;
+    const int cpr = pchunks + schunks;
+    for (int i0 = 0; i0 < 64 * cpr; i0 += 64 * kCopy) {
+      uint4 v[kCopy];
+      long long rr[kCopy];
+      int cc[kCopy];
+#pragma unroll
+      for (int x = 0; x < kCopy; ++x) {
+        const int idx = i0 + x * 64 + lane;
+        const int j = idx / cpr, c = idx - j * cpr;
+        rr[x] = __shfl(r, j < 64 ? j : 0);
+        cc[x] = c;
+        if (idx >= 64 * cpr) rr[x] = -1;
+        v[x] = make_uint4(0, 0, 0, 0);
+        if (rr[x] >= 0) {
+          const long long kj = k0 + j;
+          v[x] = c < pchunks ? reinterpret_cast<const uint4*>(params + kj * pbytes)[c]
+                             : reinterpret_cast<const uint4*>(state + kj * (sbytes >> 2))[c - pchunks];
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < kCopy; ++x)
+        if (rr[x] >= 0) reinterpret_cast<uint4*>(row_ptr(t.rs, rr[x]))[cc[x]] = v[x];
+    }
   }
 }
 
@@ -349,10 +462,17 @@ void launch_export(const TableDev& t, long long cap, long long* keys, long long*
                      keys, rows, counts);
 }
 
+void launch_import(const TableDev& t, long long n, const long long* keys, const long long* rows,
+                   const unsigned* counts, const void* params, const float* state, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_import, dim3(grid_for((n + 63) / 64, 4)), dim3(256), 0, s, t, n, keys, rows, counts,
+                     static_cast<const char*>(params), state);
+}
+
 void launch_export_rows(const TableDev& t, long long n, const long long* keys, long long* rows, void* params,
                         float* state, hipStream_t s) {
   if (n <= 0) return;
-  hipLaunchKernelGGL(k_export_rows, dim3(grid_for(n, 4)), dim3(256), 0, s, t, n, keys, rows,
+  hipLaunchKernelGGL(k_export_rows, dim3(grid_for((n + 63) / 64, 4)), dim3(256), 0, s, t, n, keys, rows,
                      static_cast<char*>(params), state);
 }
 

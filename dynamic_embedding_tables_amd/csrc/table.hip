@@ -641,11 +641,37 @@ recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, con
   return check_launch();
 }
 
+recis_status recis_idmap_import(recis_table* t, int64_t n, const int64_t* keys, const int64_t* rows,
+                                const uint32_t* counts, const void* params, const float* state, int64_t adam_step,
+                                hipStream_t s) {
+  if (!t || n < 0 || adam_step < 0 || n > (1ll << 31) - 1) return RECIS_ERR_INVALID_ARG;
+  if (n > 0 && (!keys || !rows || !counts || !params)) return RECIS_ERR_INVALID_ARG;
+  if (n > 0 && t->state_words > 0 && !state) return RECIS_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(params) | reinterpret_cast<uintptr_t>(state)) & 15) return RECIS_ERR_INVALID_ARG;
+  ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
+  if (t->keys_hi > 0 || t->rows_hi > 0) {  // the bounds say it may hold keys: ask the device
+    DevCounters c;
+    recis_status st = read_counters(t, &c, s);
+    if (st != RECIS_OK) return st;
+    if (c.num_keys != 0 || c.next_row != 0) return RECIS_ERR_INVALID_ARG;
+    t->keys_hi = t->rows_hi = 0;
+  }
+  recis_status st = ensure_capacity(t, n, s);
+  if (st != RECIS_OK) return st;
+  t->update_epoch += 1;
+  t->adam_step = adam_step;
+  launch_import(t->dev(), n, reinterpret_cast<const long long*>(keys), reinterpret_cast<const long long*>(rows),
+                counts, params, t->state_words > 0 ? state : nullptr, s);
+  return check_launch();
+}
+
 recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int64_t* rows, uint32_t* counts,
                                 void* params, float* state, int64_t* n, hipStream_t s) {
   if (!t || !n || cap < 0) return RECIS_ERR_INVALID_ARG;
   if (cap > 0 && (!keys || !rows || !counts || !params)) return RECIS_ERR_INVALID_ARG;
   if (cap > 0 && t->state_words > 0 && !state) return RECIS_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(params) | reinterpret_cast<uintptr_t>(state)) & 15) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
   ScopedProbe sp(t);
   launch_export(t->dev(), cap, reinterpret_cast<long long*>(keys), reinterpret_cast<long long*>(rows), counts, s);

@@ -49,7 +49,7 @@ POOLS = {"sum": RECIS_POOL_SUM, "mean": RECIS_POOL_MEAN, "none": RECIS_POOL_NONE
 EXPORTED_SYMBOLS = (
     "recis_table_config_default", "recis_plan_words", "recis_idmap_create", "recis_idmap_destroy",
     "recis_idmap_insert_find", "recis_idmap_evict", "recis_lookup_pool_fwd", "recis_pool_bwd_update",
-    "recis_writeback", "recis_idmap_export", "recis_idmap_stats", "recis_get_error",
+    "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats", "recis_get_error",
     "recis_status_string", "recis_profile_kernel",
 )
 
@@ -121,6 +121,7 @@ def load_library() -> C.CDLL:
                                         C.POINTER(recis_optim_params), p]
     L.recis_writeback.argtypes = [p, p, i64, p, p]
     L.recis_idmap_export.argtypes = [p, i64, p, p, p, p, p, C.POINTER(i64), p]
+    L.recis_idmap_import.argtypes = [p, i64, p, p, p, p, p, i64, p]
     L.recis_idmap_stats.argtypes = [p, C.POINTER(recis_table_stats), p]
     L.recis_get_error.argtypes = [p, p]
     L.recis_profile_kernel.argtypes = [p, C.c_char_p, p, p]
@@ -128,7 +129,8 @@ def load_library() -> C.CDLL:
     L.recis_status_string.restype = C.c_char_p
     for name in ("recis_idmap_create", "recis_idmap_destroy", "recis_idmap_insert_find",
                  "recis_idmap_evict", "recis_lookup_pool_fwd", "recis_pool_bwd_update",
-                 "recis_writeback", "recis_idmap_export", "recis_idmap_stats", "recis_get_error"):
+                 "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats",
+                 "recis_get_error"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -217,6 +219,11 @@ def recis_idmap_export(h, cap: int, keys, rows, counts, params, state, stream=No
     return int(n.value)
 
 
+def recis_idmap_import(h, n: int, keys, rows, counts, params, state, adam_step: int, stream=None):
+    _check(load_library().recis_idmap_import(h, n, _ptr(keys), _ptr(rows), _ptr(counts), _ptr(params),
+                                             _ptr(state), adam_step, _stream(stream)), "recis_idmap_import")
+
+
 def recis_idmap_stats(h, stream=None) -> recis_table_stats:
     st = recis_table_stats()
     _check(load_library().recis_idmap_stats(h, C.byref(st), _stream(stream)), "recis_idmap_stats")
@@ -300,6 +307,8 @@ class Table:
         cfg.reserve_rows, cfg.max_load = reserve_rows, max_load
         cfg.block_memory = {"device": RECIS_MEM_DEVICE, "host": RECIS_MEM_HOST}[block_memory]
         self.dim, self.dtype, self.optim = dim, dtype, optim
+        self.config = {"seed": seed, "init_bound": init_bound, "admit_threshold": admit_threshold,
+                       "block_memory": block_memory}
         self.h = recis_idmap_create(cfg, stream)
 
     def close(self):
@@ -363,3 +372,20 @@ class Table:
         assert n <= cap
         return {"keys": keys[:n], "rows": rows[:n], "counts": counts[:n], "params": params[:n],
                 "state": state[:n, :sw]}
+
+    def import_(self, keys, rows, counts, params, state, adam_step: int = 0, stream=None):
+        """Loads exported arrays (device tensors) into this never-used table."""
+        import torch
+        n = int(keys.shape[0])
+        sw = {"none": 0, "adagrad": 1, "adam": 2}[self.optim] * self.dim
+        pdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        if params.dtype != pdt or tuple(params.shape) != (n, self.dim):
+            raise ValueError(f"params must be {pdt} [{n}, {self.dim}]")
+        if sw and (state is None or state.dtype != torch.float32 or tuple(state.shape) != (n, sw)):
+            raise ValueError(f"state must be float32 [{n}, {sw}]")
+        keys = keys.to(torch.int64).contiguous()
+        rows = rows.to(torch.int64).contiguous()
+        counts = counts.to(torch.int32).contiguous()
+        params = params.contiguous()
+        state = state.contiguous() if sw else None
+        recis_idmap_import(self.h, n, keys, rows, counts, params, state, adam_step, stream)

@@ -242,11 +242,28 @@ recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, con
 /* Copies the table out (synchronises `s`): keys device [cap], rows device
  * [cap] (-1 = no row), counts device [cap], params device [cap, dim] in the
  * storage dtype, state device float32 [cap, slots*dim] (may be NULL when the
- * optimizer has none).  *n receives the number of keys (host); when it
+ * optimizer has none); params and state 16-byte aligned.  *n receives the number of keys (host); when it
  * exceeds cap only cap entries are written.  Order unspecified. */
 recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int64_t* rows,
                                 uint32_t* counts, void* params, float* state, int64_t* n,
                                 hipStream_t s);
+
+/* Restores a table saved from recis_idmap_export into this table, which must
+ * never have held a key (else RECIS_ERR_INVALID_ARG at once).  Key i gets the
+ * count counts[i] and, when rows[i] >= 0, a row holding params[i] (storage
+ * dtype) and state[i] (float32; may be NULL when the optimizer has none);
+ * rows[i] < 0 keeps the key without a row, as admission left it.  The row
+ * numbers themselves are not kept.  adam_step (>= 0) sets the table's Adam
+ * step counter.  keys, rows, counts: device [n]; params device [n, dim];
+ * state device [n, slots*dim]; params and state 16-byte aligned.  Keys must be distinct and >= 0: a repeated
+ * key records RECIS_ERR_INVALID_ARG and a negative one RECIS_ERR_KEY_RANGE in
+ * the device error word.  The pages store and deliver sparse parameters in
+ * the SafeTensors format (page "RecIS (Recommendation Intelligence System)"
+ * README, section "Core architecture > Saver"); the file itself is written
+ * and read above this call. */
+recis_status recis_idmap_import(recis_table* t, int64_t n, const int64_t* keys, const int64_t* rows,
+                                const uint32_t* counts, const void* params, const float* state,
+                                int64_t adam_step, hipStream_t s);
 
 /* Table statistics (synchronises `s`); st: host. */
 recis_status recis_idmap_stats(recis_table* t, recis_table_stats* st, hipStream_t s);

@@ -472,3 +472,85 @@ def test_device_errors_are_reported():
     # argument errors surface as exceptions
     with pytest.raises(recis.RecisError):
         recis.Table(dim=48)
+
+
+# ---- save / restore through a SafeTensors file (export -> file -> import)
+def _save_load_resume(spec, before, after, path, load_kw):
+    """Steps `before` on a table and on the oracle; the table saved to `path`
+    and restored into a new table laid out by load_kw; its content checked
+    against the oracle's; then the steps `after` on the restored table and on
+    the oracle (which never stopped), checked step by step."""
+    import torch
+    from dynamic_embedding_tables_amd import recis, saver
+    table = make_table(spec)
+    otab = oracle.OracleTable(spec)
+    for b in before:
+        res = recis.LookupResult(max(b.n, 1), b.num_feats * b.batch)
+        gpu_step(table, spec, b, res)
+        oracle_step(otab, spec, b)
+    torch.cuda.synchronize()
+    assert table.get_error() == 0
+    n = saver.save(table, path)
+    assert n == otab.size()
+    adam_step = table.stats().adam_step
+    table.close()
+    restored = saver.load(path, **load_kw)
+    assert restored.get_error() == 0
+    st = restored.stats()
+    assert st.adam_step == adam_step and st.keys == otab.size() and st.rows_in_use == otab.rows_in_use()
+    check_export(canon_export(restored), otab.export(), spec)
+    for step, b in enumerate(after):
+        print(f"[resume] step {step} N={b.n}", flush=True)
+        res = recis.LookupResult(max(b.n, 1), b.num_feats * b.batch)
+        out, _ = gpu_step(restored, spec, b, res)
+        r, oout, oab = oracle_step(otab, spec, b)
+        torch.cuda.synchronize()
+        assert restored.get_error() == 0
+        check_lookup(canon_lookup(res), r)
+        check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+    check_export(canon_export(restored), otab.export(), spec)
+    restored.close()
+
+
+def test_save_load_resume_ctr_adam(tmp_path):
+    """Adam (its step counter travels in the file), restored into a small
+    table that grows while the keys are imported."""
+    spec = W.spec_ctr()
+    _save_load_resume(spec, [W.ctr_batch(s, batch=256) for s in range(2)], [W.ctr_batch(2, batch=256)],
+                      str(tmp_path / "ctr.safetensors"), dict(slot_capacity=64, block_rows=256))
+
+
+def test_save_load_resume_admission_and_bf16(tmp_path):
+    """Keys still waiting for admission (no row, count kept), restored into
+    host-memory blocks; and the bf16 sequence table with its hot keys."""
+    spec = W.spec_multi(2)
+    _save_load_resume(spec, [W.multi_batch(s, 2, batch=128, num_feats=6) for s in range(2)],
+                      [W.multi_batch(s, 2, batch=128, num_feats=6) for s in range(2, 4)],
+                      str(tmp_path / "multi.safetensors"), dict(block_memory="host"))
+    _save_load_resume(W.spec_seq(), [W.seq_batch(0, batch=12, seq_len=1000)], [W.seq_batch(1, batch=12, seq_len=1000)],
+                      str(tmp_path / "seq.safetensors"), {})
+
+
+def test_import_rejects_used_tables_and_repeated_keys():
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_tiny()
+    keys = torch.tensor([5, 9, 5], dtype=torch.int64, device="cuda")
+    rows = torch.zeros(3, dtype=torch.int64, device="cuda")
+    counts = torch.ones(3, dtype=torch.int32, device="cuda")
+    params = torch.zeros(3, spec.dim, dtype=torch.float32, device="cuda")
+    state = torch.zeros(3, spec.dim, dtype=torch.float32, device="cuda")
+    t = make_table(spec)
+    t.import_(keys, rows, counts, params, state)           # 5 twice
+    assert t.get_error() == recis.RECIS_ERR_INVALID_ARG
+    with pytest.raises(recis.RecisError) as e:              # the table now holds keys
+        t.import_(keys[:2], rows[:2], counts[:2], params[:2], state[:2])
+    assert e.value.status == recis.RECIS_ERR_INVALID_ARG
+    t.close()
+    t = make_table(spec)
+    b = W.tiny_batch(0)
+    res = recis.LookupResult(b.n, b.batch)
+    gpu_step(t, spec, b, res)
+    with pytest.raises(recis.RecisError):
+        t.import_(keys[:2], rows[:2], counts[:2], params[:2], state[:2])
+    t.close()
