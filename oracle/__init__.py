@@ -77,6 +77,8 @@ def lib():
                                           C.c_double]
         L.orc_evict.restype = C.c_int64
         L.orc_evict.argtypes = [p, C.c_uint32]
+        L.orc_evict_decay.restype = C.c_int64
+        L.orc_evict_decay.argtypes = [p, C.c_uint32, C.c_double]
         L.orc_writeback.restype = C.c_int
         L.orc_writeback.argtypes = [p, p, C.c_int64, p]
         L.orc_size.restype = C.c_int64
@@ -237,8 +239,10 @@ class OracleTable:
                                          POOL[pool], _ptr(g), DT[grad_dtype], s.lr, s.beta1,
                                          s.beta2, s.eps)
 
-    def evict(self, min_count: int) -> int:
-        return int(lib().orc_evict(self.h, min_count))
+    def evict(self, min_count: int, decay: float = 0.0) -> int:
+        if decay == 0.0:
+            return int(lib().orc_evict(self.h, min_count))
+        return int(lib().orc_evict_decay(self.h, min_count, decay))
 
     def writeback(self, keys: np.ndarray, rows: np.ndarray) -> int:
         k = _c(keys, np.int64)

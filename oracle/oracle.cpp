@@ -534,13 +534,15 @@ int orc_backward_update(void* h, const int64_t* unique_rows, const int32_t* inve
 // Eviction pass.  [README] Embedding Engine: feature eviction and admission.
 // Reading: every key (with or without a row) whose count since the last pass
 // is below min_count leaves the map and releases its row; the surviving keys
-// restart their count at 0.  Returns the number of keys removed.
-int64_t orc_evict(void* h, uint32_t min_count) {
+// keep floor(count * decay) of their count (decay in [0, 1]: 0 restarts the
+// window, 1 keeps the running total, in between the counts decay with time).
+// Returns the number of keys removed.
+int64_t orc_evict_decay(void* h, uint32_t min_count, double decay) {
   Table& t = *static_cast<Table*>(h);
   std::vector<int64_t> gone;
   for (auto& kv : t.idmap) {
     if (kv.second.count < min_count) gone.push_back(kv.first);
-    else kv.second.count = 0;
+    else kv.second.count = uint32_t(std::floor(double(kv.second.count) * decay));
   }
   std::sort(gone.begin(), gone.end());
   for (int64_t key : gone) {
@@ -550,6 +552,8 @@ int64_t orc_evict(void* h, uint32_t min_count) {
   }
   return int64_t(gone.size());
 }
+
+int64_t orc_evict(void* h, uint32_t min_count) { return orc_evict_decay(h, min_count, 0.0); }
 
 // Writeback.  [ML] What carries the argument / Summary: the item tower's
 // output e is written into the cache row M[key] as an exact assignment (the

@@ -9,6 +9,8 @@ Adagrad    -> torch.optim.Adagrad (sparse gradients)
 Adam       -> torch.optim.SparseAdam (lazy, one step counter per table)
 writeback  -> torch.optim.SGD(lr=1) on 0.5*||M - e||^2, and last-writer brute force
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -96,12 +98,19 @@ class DictTable:
             out[k] = e[0]
         return out
 
-    def evict(self, t):
+    def evict(self, t, decay=0.0):
+        """Survivors keep floor(count * decay): written with integer
+        arithmetic where the factor allows (0, 1/2, 1), else in binary64."""
         gone = [k for k, e in self.m.items() if e[1] < t]
         for k in gone:
             del self.m[k]
         for e in self.m.values():
-            e[1] = 0
+            if decay == 0.0:
+                e[1] = 0
+            elif decay == 0.5:
+                e[1] >>= 1
+            elif decay != 1.0:
+                e[1] = math.floor(e[1] * decay)
         return len(gone)
 
 
@@ -346,6 +355,45 @@ def test_bf16_update_rounds_once():
         got = ex["params"][i].view(np.uint32) >> 16
         assert np.all(np.abs(got.astype(np.int64) - wb.astype(np.int64)) <= 1)
         assert (got == wb).mean() > 0.5
+
+
+@pytest.mark.parametrize("decay", [0.0, 0.5, 1.0, 0.3])
+def test_evict_decay_against_brute_force(decay):
+    """Eviction passes whose survivors keep floor(count * decay), with
+    admission at 2: the evicted sets, counts, admissions and rows step by step
+    against the dict."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum", admit_threshold=2)
+    tab, ref = oracle.OracleTable(spec), DictTable(2)
+    for step in range(14):
+        feats = small_features(300 + step, nfeat=2, batch=9, id_space=30)
+        r = tab.insert_find(feats, 9)
+        assert r.status == 0
+        want = ref.step(keys_of(feats), False)
+        got = {int(k): int(row) >= 0 for k, row in zip(r.unique_keys[:r.U], r.unique_rows[:r.U])}
+        assert got == {int(k): v for k, v in want.items()}
+        if step % 3 == 2:
+            assert tab.evict(3, decay) == ref.evict(3, decay)
+        ex = tab.export()
+        assert [int(k) for k in ex["keys"]] == sorted(int(k) for k in ref.m)
+        assert [int(c) for c in ex["counts"]] == [ref.m[k][1] for k in sorted(ref.m)]
+        assert [bool(r_ >= 0) for r_ in ex["rows"]] == [ref.m[k][0] for k in sorted(ref.m)]
+
+
+def test_evict_decay_one_keeps_running_totals():
+    """decay = 1 and no key evicted: every count is the key's total number of
+    occurrences since it was first seen (np.unique over all inputs)."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum")
+    tab = oracle.OracleTable(spec)
+    seen = []
+    for step in range(6):
+        feats = small_features(400 + step, nfeat=2, batch=9, id_space=30)
+        assert tab.insert_find(feats, 9).status == 0
+        seen.append(keys_of(feats))
+        assert tab.evict(1, 1.0) == 0
+    keys, counts = np.unique(np.concatenate(seen), return_counts=True)
+    ex = tab.export()
+    np.testing.assert_array_equal(ex["keys"], keys)
+    np.testing.assert_array_equal(ex["counts"], counts)
 
 
 # --------------------------------------------------------------------- evict
