@@ -301,6 +301,27 @@ def export_import(torch, recis, table, spec, wl, D, s, S, block_memory):
             "import_frac": alg / t_import / 1e9 / HBM_PEAK_GBS}
 
 
+def evict_pass(torch, table, min_count=2, decay=0.5):
+    """One eviction pass over the whole table, wall-clock (the call reads the
+    device counters back, so it synchronises).  It moves per IDMap slot 16 B
+    read by the marking pass, and for the rebuild 16 B filled and 16 B read;
+    per surviving key 16 B written."""
+    st0 = table.stats()
+    slots = int(st0.slot_capacity)
+    ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    table.evict(min_count, ne, decay=decay)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    table.check()
+    st1 = table.stats()
+    alg = 48 * slots + 16 * int(st1.keys)
+    return {"min_count": min_count, "decay": decay, "keys_before": int(st0.keys), "evicted": int(ne.item()),
+            "keys_after": int(st1.keys), "slots": slots, "ms": dt * 1e3, "algorithmic_bytes": alg,
+            "GBps": alg / dt / 1e9, "frac": alg / dt / 1e9 / HBM_PEAK_GBS}
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -418,6 +439,9 @@ def main():
     ap.add_argument("--export-import", action="store_true",
                     help="after the timed steps, export the whole table and import it into a new one (the "
                          "device side of saving and restoring), timed against the HBM roofline")
+    ap.add_argument("--evict-pass", action="store_true",
+                    help="after the timed steps, one eviction pass with decayed counts (min count 2, decay "
+                         "0.5) over the whole table, timed against the HBM roofline")
     ap.add_argument("--block-memory", choices=["device", "host"], default="device",
                     help="where the EmbeddingBlocks live: HBM, or pinned host memory across the host link")
     ap.add_argument("--workers", type=int, default=8)
@@ -660,6 +684,8 @@ def main():
     }
     if args.export_import:
         result["export_import"] = export_import(torch, recis, table, spec, wl, D, s_bytes, S, args.block_memory)
+    if args.evict_pass:
+        result["evict_pass"] = evict_pass(torch, table)
     if args.block_memory == "host":
         result["config"]["block_memory"] = "host (pinned, mapped; IDMap and scratch in HBM)"
         result["host_link_copy_GBps"] = host_link_copy(torch, dev)

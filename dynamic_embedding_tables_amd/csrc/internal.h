@@ -428,7 +428,7 @@ recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, 
                              const void* grad, int grad_dtype, const OptConsts& oc,
                              double* partials, bool current, hipStream_t s);
 
-void launch_evict(const TableDev& t, unsigned min_count, long long* num_evicted, hipStream_t s);
+void launch_evict(const TableDev& t, unsigned min_count, double decay, long long* num_evicted, hipStream_t s);
 void launch_writeback(const TableDev& t, const long long* keys, long long n, const float* rows,
                       DedupSlot* dd, unsigned long long dd_mask, int dd_shift, long long* wb_keys,
                       int* uslot, hipStream_t s);

@@ -81,30 +81,56 @@ __global__ void k_set_scratch(DevCounters* c) { c->scratch_count = 0; }
 
 // Eviction: keys whose window count is below min_count leave (their slot is
 // marked gone and the IDMap is rebuilt afterwards); their rows go to the free
-// list; survivors restart their count at 0.
-__global__ void k_evict_mark(TableDev t, unsigned min_count) {
-  for (long long i0 = (long long)blockIdx.x * blockDim.x; i0 <= (long long)t.slot_mask;
-       i0 += (long long)gridDim.x * blockDim.x) {
-    const long long i = i0 + threadIdx.x;
-    bool gone = false, frees = false;
+// list; survivors keep floor(count * decay) (0: the window restarts).  A
+// block takes kEvictSpan slots and gathers its freed rows in LDS (wave-wide
+// counters), then reserves its share of the free list with one atomic:
+// device atomics on one address execute one after another at the memory
+// side, so one per wave would serialise the pass.
+constexpr int kEvictSpan = 4096;
+__global__ __launch_bounds__(256) void k_evict_mark(TableDev t, unsigned min_count, double decay) {
+  __shared__ int s_rows[kEvictSpan];
+  __shared__ int s_nfree, s_ngone;
+  __shared__ long long s_base;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) {
+    s_nfree = 0;
+    s_ngone = 0;
+  }
+  __syncthreads();
+  const long long b0 = (long long)blockIdx.x * kEvictSpan;
+  for (int k0 = 0; k0 < kEvictSpan; k0 += 256) {
+    const long long i = b0 + k0 + threadIdx.x;
+    bool gone = false;
     int row = -1;
     if (i <= (long long)t.slot_mask) {
-      Slot s = t.slots[i];
+      const Slot s = t.slots[i];
       if (s.key >= 0) {
         if (s.count < min_count) {
           gone = true;
           row = s.row < 0 ? -1 : (s.row & ~kPendingRow);
-          frees = row >= 0;
           t.slots[i].key = kGoneKey;
         } else {
-          t.slots[i].count = 0;
+          t.slots[i].count = decay == 0.0 ? 0u : (unsigned)floor((double)s.count * decay);
         }
       }
     }
-    const long long at = wave_add((unsigned long long*)&t.ctr->free_top, frees);
-    if (frees) t.free_list[at] = row;
-    wave_add(&t.ctr->scratch_count, gone);
+    const bool frees = row >= 0;
+    const unsigned long long mf = __ballot(frees), mg = __ballot(gone);
+    int base = 0;
+    if (lane == 0) {
+      if (mf) base = atomicAdd(&s_nfree, __popcll(mf));
+      if (mg) atomicAdd(&s_ngone, __popcll(mg));
+    }
+    base = __shfl(base, 0);
+    if (frees) s_rows[base + __popcll(mf & ((1ull << lane) - 1ull))] = row;
   }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s_base = s_nfree ? (long long)atomicAdd((unsigned long long*)&t.ctr->free_top, (unsigned long long)s_nfree) : 0;
+    if (s_ngone) atomicAdd(&t.ctr->scratch_count, (unsigned long long)s_ngone);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < s_nfree; k += 256) t.free_list[s_base + k] = s_rows[k];
 }
 
 __global__ void k_evict_done(DevCounters* c, long long* num_evicted) {
@@ -434,10 +460,10 @@ void launch_rehash(const Slot* old_slots, long long old_cap, const TableDev& t, 
   hipLaunchKernelGGL(k_rehash, dim3(grid_for(old_cap, 256)), dim3(256), 0, s, old_slots, old_cap, t);
 }
 
-void launch_evict(const TableDev& t, unsigned min_count, long long* num_evicted, hipStream_t s) {
+void launch_evict(const TableDev& t, unsigned min_count, double decay, long long* num_evicted, hipStream_t s) {
   hipLaunchKernelGGL(k_set_scratch, dim3(1), dim3(1), 0, s, t.ctr);
-  hipLaunchKernelGGL(k_evict_mark, dim3(grid_for((long long)t.slot_mask + 1, 256)), dim3(256), 0, s, t,
-                     min_count);
+  const long long nb = ((long long)t.slot_mask + kEvictSpan) / kEvictSpan;
+  hipLaunchKernelGGL(k_evict_mark, dim3((unsigned)nb), dim3(256), 0, s, t, min_count, decay);
   hipLaunchKernelGGL(k_evict_done, dim3(1), dim3(1), 0, s, t.ctr, num_evicted);
 }
 

@@ -557,12 +557,13 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   return check_launch();
 }
 
-recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted, hipStream_t s) {
-  if (!t) return RECIS_ERR_INVALID_ARG;
+recis_status recis_idmap_evict_decay(recis_table* t, uint32_t min_count, double decay, int64_t* num_evicted,
+                                     hipStream_t s) {
+  if (!t || !(decay >= 0.0 && decay <= 1.0)) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
   ScopedProbe sp(t);
   t->update_epoch += 1;
-  launch_evict(t->dev(), min_count, reinterpret_cast<long long*>(num_evicted), s);
+  launch_evict(t->dev(), min_count, decay, reinterpret_cast<long long*>(num_evicted), s);
   recis_status st = check_launch();
   if (st != RECIS_OK) return st;
   st = rebuild_idmap(t, t->slot_cap, s);
@@ -573,6 +574,10 @@ recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_
   t->rows_hi = (long long)c.next_row;
   t->keys_hi = (long long)c.num_keys;
   return RECIS_OK;
+}
+
+recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted, hipStream_t s) {
+  return recis_idmap_evict_decay(t, min_count, 0.0, num_evicted, s);
 }
 
 recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_result* res, int32_t pool, void* out,

@@ -48,7 +48,8 @@ POOLS = {"sum": RECIS_POOL_SUM, "mean": RECIS_POOL_MEAN, "none": RECIS_POOL_NONE
 
 EXPORTED_SYMBOLS = (
     "recis_table_config_default", "recis_plan_words", "recis_idmap_create", "recis_idmap_destroy",
-    "recis_idmap_insert_find", "recis_idmap_evict", "recis_lookup_pool_fwd", "recis_pool_bwd_update",
+    "recis_idmap_insert_find", "recis_idmap_evict", "recis_idmap_evict_decay", "recis_lookup_pool_fwd",
+    "recis_pool_bwd_update",
     "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats", "recis_get_error",
     "recis_status_string", "recis_profile_kernel",
 )
@@ -116,6 +117,7 @@ def load_library() -> C.CDLL:
     L.recis_idmap_insert_find.argtypes = [p, C.POINTER(recis_feature_desc), i32, i32, u32,
                                           C.POINTER(recis_lookup_result), p]
     L.recis_idmap_evict.argtypes = [p, u32, p, p]
+    L.recis_idmap_evict_decay.argtypes = [p, u32, C.c_double, p, p]
     L.recis_lookup_pool_fwd.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, p]
     L.recis_pool_bwd_update.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, i32,
                                         C.POINTER(recis_optim_params), p]
@@ -128,7 +130,7 @@ def load_library() -> C.CDLL:
     L.recis_status_string.argtypes = [i32]
     L.recis_status_string.restype = C.c_char_p
     for name in ("recis_idmap_create", "recis_idmap_destroy", "recis_idmap_insert_find",
-                 "recis_idmap_evict", "recis_lookup_pool_fwd", "recis_pool_bwd_update",
+                 "recis_idmap_evict", "recis_idmap_evict_decay", "recis_lookup_pool_fwd", "recis_pool_bwd_update",
                  "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats",
                  "recis_get_error"):
         getattr(L, name).restype = i32
@@ -186,6 +188,11 @@ def recis_idmap_insert_find(h, descs, num_feats: int, batch: int, flags: int,
 def recis_idmap_evict(h, min_count: int, num_evicted=None, stream=None):
     _check(load_library().recis_idmap_evict(h, min_count, _ptr(num_evicted), _stream(stream)),
            "recis_idmap_evict")
+
+
+def recis_idmap_evict_decay(h, min_count: int, decay: float, num_evicted=None, stream=None):
+    _check(load_library().recis_idmap_evict_decay(h, min_count, decay, _ptr(num_evicted), _stream(stream)),
+           "recis_idmap_evict_decay")
 
 
 def recis_lookup_pool_fwd(h, res: recis_lookup_result, pool: int, out, stream=None):
@@ -338,8 +345,12 @@ class Table:
         opt = recis_optim_params(lr, beta1, beta2, eps)
         recis_pool_bwd_update(self.h, res.c, POOLS[pool], grad, DTYPES[grad_dtype], opt, stream)
 
-    def evict(self, min_count: int, num_evicted=None, stream=None):
-        recis_idmap_evict(self.h, min_count, num_evicted, stream)
+    def evict(self, min_count: int, num_evicted=None, stream=None, decay: float = 0.0):
+        """Eviction pass; survivors keep floor(count * decay) (0: restart)."""
+        if decay == 0.0:
+            recis_idmap_evict(self.h, min_count, num_evicted, stream)
+        else:
+            recis_idmap_evict_decay(self.h, min_count, decay, num_evicted, stream)
 
     def writeback(self, keys, rows, stream=None):
         recis_writeback(self.h, keys, int(keys.numel()), rows, stream)

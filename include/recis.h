@@ -215,6 +215,18 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
 recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted,
                                hipStream_t s);
 
+/* Eviction pass with time-decayed counts: as recis_idmap_evict, except that
+ * the surviving keys keep floor(count * decay) of their count instead of
+ * restarting at 0 (decay in [0, 1]; 0 is recis_idmap_evict, 1 keeps running
+ * totals).  A key then has to keep being seen to stay, with older
+ * occurrences weighing less at every pass: one of the richer eviction and
+ * admission strategies the pages leave open (page "RecIS (Recommendation
+ * Intelligence System)" README, section "Core architecture > Embedding
+ * Engine").  Admission still compares the count with admit_threshold.
+ * Errors: INVALID_ARG (decay outside [0, 1]); as recis_idmap_evict. */
+recis_status recis_idmap_evict_decay(recis_table* t, uint32_t min_count, double decay,
+                                     int64_t* num_evicted, hipStream_t s);
+
 /* Forward: SUM / MEAN write float32 out [batch, num_feats * dim] with
  * out[i, f*dim + d] = pooled element d of bag (f, i) (mean divides by the bag
  * length; an empty bag gives 0; a key without a row adds zeros); NONE writes

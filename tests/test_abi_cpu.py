@@ -106,6 +106,8 @@ def test_invalid_arguments_return_synchronously(lib):
     res = lib.recis_lookup_result()
     assert L.recis_idmap_insert_find(None, None, 0, 0, 0, C.byref(res), None) == lib.RECIS_ERR_INVALID_ARG
     assert L.recis_idmap_evict(None, 1, None, None) == lib.RECIS_ERR_INVALID_ARG
+    assert L.recis_idmap_evict_decay(None, 1, 0.5, None, None) == lib.RECIS_ERR_INVALID_ARG
+    assert L.recis_idmap_import(None, 0, None, None, None, None, None, 0, None) == lib.RECIS_ERR_INVALID_ARG
     assert L.recis_lookup_pool_fwd(None, C.byref(res), 0, None, None) == lib.RECIS_ERR_INVALID_ARG
     opt = lib.recis_optim_params(0.01, 0.9, 0.999, 1e-8)
     assert L.recis_pool_bwd_update(None, C.byref(res), 0, None, 0, C.byref(opt), None) == lib.RECIS_ERR_INVALID_ARG

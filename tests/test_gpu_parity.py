@@ -30,7 +30,7 @@ def _gpu():
 
 
 def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopulate=None,
-               export_every=1):
+               export_every=1, evict_decay=0.0):
     import torch
     from dynamic_embedding_tables_amd import recis
     table = make_table(spec, **(table_kw or {}))
@@ -53,8 +53,8 @@ def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopu
         check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats, exact=step == 0 and prepopulate is None)
         if evict_every and (step + 1) % evict_every == 0:
             ne = torch.zeros(1, dtype=torch.int64, device="cuda")
-            table.evict(evict_min, ne)
-            assert int(ne.item()) == otab.evict(evict_min)
+            table.evict(evict_min, ne, decay=evict_decay)
+            assert int(ne.item()) == otab.evict(evict_min, evict_decay)
         if (step + 1) % export_every == 0 or step == len(batches) - 1:
             check_export(canon_export(table), otab.export(), spec)
     st = table.stats()
@@ -90,6 +90,16 @@ def test_multi_table_config_scaled_with_eviction(table):
     spec = W.spec_multi(table)
     batches = [W.multi_batch(s, table, batch=128, num_feats=6) for s in range(6)]
     run_parity(spec, batches, evict_every=2)
+
+
+@pytest.mark.parametrize("decay", [0.5, 0.3, 1.0])
+def test_eviction_with_decayed_counts(decay):
+    """Eviction passes whose survivors keep floor(count * decay), on the
+    multi-table config with admission at 2: evicted counts, key sets, counts,
+    rows and their reuse step by step."""
+    spec = W.spec_multi(3)
+    batches = [W.multi_batch(s, 3, batch=128, num_feats=6) for s in range(8)]
+    run_parity(spec, batches, evict_every=2, evict_min=3, evict_decay=decay)
 
 
 # ---- full sizes: the bench's workload and table configuration, and the
