@@ -110,6 +110,7 @@ struct FeatDev {
   long long n;
   long long base;       // global index of its first occurrence
   unsigned long long mod;
+  unsigned long long mod_inv;  // floor((2^64 - 1) / mod), for the remainder by multiplication
   unsigned slot;
   unsigned ops;
   int bnd_off;

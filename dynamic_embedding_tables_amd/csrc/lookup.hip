@@ -99,6 +99,20 @@ __device__ __forceinline__ int lds_add1(int* a, unsigned h, bool act) {
   return res;
 }
 
+// x mod d with inv = floor((2^64 - 1) / d): the quotient estimate
+// floor(x * inv / 2^64) is at most 2 below floor(x / d), so at most two
+// subtractions finish the remainder (division by an invariant integer through
+// multiplication, after Granlund and Montgomery).  A generic 64-bit
+// remainder is a long instruction sequence on this GPU.
+__device__ __forceinline__ unsigned long long mod_by(unsigned long long x, unsigned long long d,
+                                                    unsigned long long inv) {
+  const unsigned long long q = __umul64hi(x, inv);
+  unsigned long long r = x - q * d;
+  if (r >= d) r -= d;
+  if (r >= d) r -= d;
+  return r;
+}
+
 // Hash -> Mod, or Bucketize, then the feature tag.
 __device__ __forceinline__ long long transform_value(long long v, const FeatDev& fd,
                                                      const long long* bnd, unsigned& err) {
@@ -114,12 +128,12 @@ __device__ __forceinline__ long long transform_value(long long v, const FeatDev&
     id = (unsigned long long)lo;
   } else if (fd.ops & RECIS_OP_HASH) {
     id = fmix64((unsigned long long)v);
-    if (fd.ops & RECIS_OP_MOD) id %= fd.mod;
+    if (fd.ops & RECIS_OP_MOD) id = mod_by(id, fd.mod, fd.mod_inv);
   } else if (fd.ops & RECIS_OP_MOD) {
-    const long long m = (long long)fd.mod;
-    long long r = v % m;
-    if (r < 0) r += m;
-    id = (unsigned long long)r;
+    // the floor remainder in [0, mod) (mod <= 2^63 - 1 here): a negative v
+    // through -(v + 1), which cannot overflow
+    id = v >= 0 ? mod_by((unsigned long long)v, fd.mod, fd.mod_inv)
+                : fd.mod - 1 - mod_by((unsigned long long)(-(v + 1)), fd.mod, fd.mod_inv);
   } else {
     if (v < 0) {
       err |= kErrKeyRange;

@@ -505,6 +505,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
     fd[f].n = d.n;
     fd[f].base = base;
     fd[f].mod = d.mod;
+    fd[f].mod_inv = (d.ops & RECIS_OP_MOD) ? ~0ull / d.mod : 0;
     fd[f].slot = d.slot;
     fd[f].ops = d.ops;
     fd[f].bnd_off = (int)boff;

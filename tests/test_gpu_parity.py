@@ -209,6 +209,26 @@ def test_transforms_hash_mod_bucketize_and_find_only():
     check_export(canon_export(table), otab.export(), spec)
 
 
+def test_mod_transform_edges():
+    """The remainder by multiplication at the edges: the extreme int64 values,
+    moduli 1, 3, 2^47 + 12345 and 2^48 (the largest that keeps every key in
+    range), on raw signed values (floor remainder) and after Hash."""
+    spec = W.TableSpec(dim=16, dtype="f32", optim="adagrad", pool="sum", lr=0.01, eps=1e-10)
+    rng = W.rng_for(44)
+    edges = np.array([-2**63, -2**63 + 1, -2**48 - 1, -2**48, -2**47, -1, 0, 1, 2**47, 2**48 - 1, 2**48,
+                      2**63 - 1, 2**63 - 2], dtype=np.int64)
+    vals = np.concatenate([edges, rng.integers(-2**63, 2**63 - 1, 400, dtype=np.int64, endpoint=True)])
+    B = vals.size
+    off = W.offsets_from_lengths(np.ones(B, np.int64))
+    feats = [W.FeatureInput(values=vals, bag_offsets=off, slot=1, ops=W.OP_MOD, mod=2**48),
+             W.FeatureInput(values=vals, bag_offsets=off, slot=2, ops=W.OP_MOD, mod=1),
+             W.FeatureInput(values=vals, bag_offsets=off, slot=3, ops=W.OP_MOD, mod=2**47 + 12345),
+             W.FeatureInput(values=vals, bag_offsets=off, slot=4, ops=W.OP_HASH | W.OP_MOD, mod=2**48),
+             W.FeatureInput(values=vals, bag_offsets=off, slot=5, ops=W.OP_HASH | W.OP_MOD, mod=3)]
+    g = W.rng_for(45).standard_normal((B, len(feats) * 16), dtype=np.float32)
+    run_parity(spec, [W.Batch(feats, B, g)])
+
+
 def test_empty_batches_and_empty_bags():
     import torch
     from dynamic_embedding_tables_amd import recis
