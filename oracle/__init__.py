@@ -79,6 +79,8 @@ def lib():
         L.orc_evict.argtypes = [p, C.c_uint32]
         L.orc_evict_decay.restype = C.c_int64
         L.orc_evict_decay.argtypes = [p, C.c_uint32, C.c_double]
+        L.orc_evict_lru.restype = C.c_int64
+        L.orc_evict_lru.argtypes = [p, C.c_int64]
         L.orc_writeback.restype = C.c_int
         L.orc_writeback.argtypes = [p, p, C.c_int64, p]
         L.orc_size.restype = C.c_int64
@@ -243,6 +245,9 @@ class OracleTable:
         if decay == 0.0:
             return int(lib().orc_evict(self.h, min_count))
         return int(lib().orc_evict_decay(self.h, min_count, decay))
+
+    def evict_lru(self, max_keys: int) -> int:
+        return int(lib().orc_evict_lru(self.h, max_keys))
 
     def writeback(self, keys: np.ndarray, rows: np.ndarray) -> int:
         k = _c(keys, np.int64)

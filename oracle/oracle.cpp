@@ -175,8 +175,9 @@ float bf16_value(uint16_t b) {
 // waits for admission ([README] Embedding Engine: eviction and admission).
 // ---------------------------------------------------------------------------
 struct Entry {
-  int64_t row;     // -1: no row (not yet admitted, or refused for capacity)
-  uint32_t count;  // occurrences since the last eviction pass
+  int64_t row;        // -1: no row (not yet admitted, or refused for capacity)
+  uint32_t count;     // occurrences since the last eviction pass
+  uint32_t last_use;  // the counting lookup that last saw the key (Table::step)
 };
 
 struct Table {
@@ -192,6 +193,7 @@ struct Table {
   std::vector<int64_t> free_rows;   // rows released by eviction, reused last-in first-out
   int64_t next_row = 0;
   int64_t adam_step = 0;
+  uint32_t step = 0;                // counting lookups so far (insert_find without FIND_ONLY)
 };
 
 float store_param(const Table& t, double v) {
@@ -339,6 +341,7 @@ int orc_insert_find(void* h, int32_t nfeat, int32_t batch, const int64_t* values
   // 4: IDMap.
   int status = ST_OK;
   const bool find_only = (flags & FLAG_FIND_ONLY) != 0;
+  if (!find_only) ++t.step;
   for (int64_t u = 0; u < u_count; ++u) {
     const int64_t key = uniq[u];
     auto it = t.idmap.find(key);
@@ -352,9 +355,10 @@ int orc_insert_find(void* h, int32_t nfeat, int32_t batch, const int64_t* values
         unique_rows[u] = -1;
         continue;
       }
-      it = t.idmap.emplace(key, Entry{-1, 0}).first;
+      it = t.idmap.emplace(key, Entry{-1, 0, 0}).first;
     }
     Entry& e = it->second;
+    e.last_use = t.step;
     uint64_t c = uint64_t(e.count) + uint64_t(counts[u]);
     e.count = c > 0xFFFFFFFFull ? 0xFFFFFFFFu : uint32_t(c);
     if (e.row < 0 && e.count >= t.admit) {
@@ -555,12 +559,42 @@ int64_t orc_evict_decay(void* h, uint32_t min_count, double decay) {
 
 int64_t orc_evict(void* h, uint32_t min_count) { return orc_evict_decay(h, min_count, 0.0); }
 
+// LRU-bounded capacity (one of the richer eviction strategies the README's
+// Embedding Engine leaves open).  Reading: a key's age is the number of
+// counting lookups since one last counted it (0: the latest), with every age
+// of 255 or more taken as 255.  The pass keeps the youngest ages whole, as
+// many of them as fit in max_keys keys together, and removes every older key
+// (releasing its row); counts are untouched.  Returns the number removed.
+int64_t orc_evict_lru(void* h, int64_t max_keys) {
+  Table& t = *static_cast<Table*>(h);
+  std::vector<int64_t> hist(256, 0);
+  auto age = [&](const Entry& e) { return std::min<uint32_t>(t.step - e.last_use, 255u); };
+  for (auto& kv : t.idmap) hist[age(kv.second)] += 1;
+  int64_t keep = 0;
+  int oldest_kept = -1;
+  for (int a = 0; a < 256 && keep + hist[a] <= max_keys; ++a) {
+    keep += hist[a];
+    oldest_kept = a;
+  }
+  std::vector<int64_t> gone;
+  for (auto& kv : t.idmap)
+    if (int(age(kv.second)) > oldest_kept) gone.push_back(kv.first);
+  std::sort(gone.begin(), gone.end());
+  for (int64_t key : gone) {
+    auto it = t.idmap.find(key);
+    if (it->second.row >= 0) t.free_rows.push_back(it->second.row);
+    t.idmap.erase(it);
+  }
+  return int64_t(gone.size());
+}
+
 // Writeback.  [ML] What carries the argument / Summary: the item tower's
 // output e is written into the cache row M[key] as an exact assignment (the
 // eta = 1 SGD step on (M - e) lands exactly on e).  Reading for repeated keys
 // in one batch: the writes happen in batch order, so the last one stays.  An
 // absent key is inserted and given a row at once (no admission wait, count
-// untouched); the stored value is e rounded once to the storage dtype.
+// untouched, last use = the latest lookup); the stored value is e rounded
+// once to the storage dtype.
 int orc_writeback(void* h, const int64_t* keys, int64_t n, const float* rows) {
   Table& t = *static_cast<Table*>(h);
   const int D = t.dim;
@@ -573,7 +607,7 @@ int orc_writeback(void* h, const int64_t* keys, int64_t n, const float* rows) {
         status = ST_CAPACITY;
         continue;
       }
-      it = t.idmap.emplace(keys[i], Entry{-1, 0}).first;
+      it = t.idmap.emplace(keys[i], Entry{-1, 0, t.step}).first;
     }
     if (it->second.row < 0) {
       it->second.row = allocate_row(t, keys[i]);

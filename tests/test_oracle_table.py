@@ -79,13 +79,19 @@ def test_empty_batch():
 
 # --------------------------------------------------------------------- IDMap
 class DictTable:
-    """Brute force: key -> [has_row, count]."""
+    """Brute force: key -> [has_row, count], and per key the number of the
+    counting lookup that last saw it."""
 
     def __init__(self, admit):
         self.m, self.admit = {}, admit
+        self.last, self.now = {}, 0
 
     def step(self, keys, find_only=False):
         out = {}
+        if not find_only:
+            self.now += 1
+            for k in np.unique(keys):
+                self.last[k] = self.now
         for k in np.unique(keys):
             c = int((keys == k).sum())
             if find_only:
@@ -97,6 +103,24 @@ class DictTable:
                 e[0] = True
             out[k] = e[0]
         return out
+
+    def evict_lru(self, max_keys):
+        """Keeps the keys seen most recently, whole lookups at a time (ages
+        from 255 on are one), within max_keys; returns how many left."""
+        by_age = sorted(self.m, key=lambda k: min(self.now - self.last[k], 255))
+        ages = [min(self.now - self.last[k], 255) for k in by_age]
+        kept, i = 0, 0
+        while i < len(by_age):
+            j = i
+            while j < len(by_age) and ages[j] == ages[i]:
+                j += 1
+            if kept + (j - i) > max_keys:
+                break
+            kept, i = kept + (j - i), j
+        gone = by_age[i:]
+        for k in gone:
+            del self.m[k]
+        return len(gone)
 
     def evict(self, t, decay=0.0):
         """Survivors keep floor(count * decay): written with integer
@@ -377,6 +401,43 @@ def test_evict_decay_against_brute_force(decay):
         assert [int(k) for k in ex["keys"]] == sorted(int(k) for k in ref.m)
         assert [int(c) for c in ex["counts"]] == [ref.m[k][1] for k in sorted(ref.m)]
         assert [bool(r_ >= 0) for r_ in ex["rows"]] == [ref.m[k][0] for k in sorted(ref.m)]
+
+
+@pytest.mark.parametrize("cap", [0, 15, 40, 10**6])
+def test_evict_lru_against_brute_force(cap):
+    """LRU-bounded passes (at most `cap` keys kept, youngest lookups first)
+    mixed with admission at 2 and a FIND_ONLY lookup, against the dict."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum", admit_threshold=2)
+    tab, ref = oracle.OracleTable(spec), DictTable(2)
+    for step in range(16):
+        feats = small_features(500 + step, nfeat=2, batch=7, id_space=40)
+        find_only = step % 7 == 6
+        r = tab.insert_find(feats, 7, flags=oracle.FIND_ONLY if find_only else 0)
+        assert r.status == 0
+        want = ref.step(keys_of(feats), find_only)
+        got = {int(k): int(row) >= 0 for k, row in zip(r.unique_keys[:r.U], r.unique_rows[:r.U])}
+        assert got == {int(k): v for k, v in want.items()}
+        if step % 3 == 1:
+            n = tab.evict_lru(cap)
+            assert n == ref.evict_lru(cap)
+            assert tab.size() <= cap
+        ex = tab.export()
+        assert [int(k) for k in ex["keys"]] == sorted(int(k) for k in ref.m)
+        assert [int(c) for c in ex["counts"]] == [ref.m[k][1] for k in sorted(ref.m)]
+        assert [bool(r_ >= 0) for r_ in ex["rows"]] == [ref.m[k][0] for k in sorted(ref.m)]
+
+
+def test_evict_lru_keeps_exactly_the_latest_lookup():
+    """A bound equal to the latest lookup's distinct keys keeps exactly those."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum")
+    tab = oracle.OracleTable(spec)
+    for step in range(4):
+        feats = small_features(600 + step, nfeat=1, batch=7, id_space=50)
+        assert tab.insert_find(feats, 7).status == 0
+    last = np.unique(keys_of(feats))
+    n_before = tab.size()
+    assert tab.evict_lru(last.size) == n_before - last.size
+    np.testing.assert_array_equal(tab.export()["keys"], last)
 
 
 def test_evict_decay_one_keeps_running_totals():
