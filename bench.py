@@ -301,6 +301,27 @@ def export_import(torch, recis, table, spec, wl, D, s, S, block_memory):
             "import_frac": alg / t_import / 1e9 / HBM_PEAK_GBS}
 
 
+def evict_lru_pass(torch, table):
+    """One LRU-bounded pass to half the table's keys, wall-clock (it
+    synchronises).  It moves per IDMap slot 16 B read and 4 B of stamp read
+    by the age histogram, the same again by the marking, and 32 B by the
+    rebuild; per surviving key 16 B written."""
+    st0 = table.stats()
+    slots = int(st0.slot_capacity)
+    ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    table.evict_lru(int(st0.keys) // 2, ne)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    table.check()
+    st1 = table.stats()
+    alg = 72 * slots + 16 * int(st1.keys)
+    return {"max_keys": int(st0.keys) // 2, "keys_before": int(st0.keys), "evicted": int(ne.item()),
+            "keys_after": int(st1.keys), "slots": slots, "ms": dt * 1e3, "algorithmic_bytes": alg,
+            "GBps": alg / dt / 1e9, "frac": alg / dt / 1e9 / HBM_PEAK_GBS}
+
+
 def evict_pass(torch, table, min_count=2, decay=0.5):
     """One eviction pass over the whole table, wall-clock (the call reads the
     device counters back, so it synchronises).  It moves per IDMap slot 16 B
@@ -441,7 +462,10 @@ def main():
                          "device side of saving and restoring), timed against the HBM roofline")
     ap.add_argument("--evict-pass", action="store_true",
                     help="after the timed steps, one eviction pass with decayed counts (min count 2, decay "
-                         "0.5) over the whole table, timed against the HBM roofline")
+                         "0.5) over the whole table, timed against the HBM roofline (with --track-last-use, "
+                         "first an LRU-bounded pass to half the keys)")
+    ap.add_argument("--track-last-use", action="store_true",
+                    help="the table stamps every key a lookup counts (for LRU-bounded eviction)")
     ap.add_argument("--block-memory", choices=["device", "host"], default="device",
                     help="where the EmbeddingBlocks live: HBM, or pinned host memory across the host link")
     ap.add_argument("--workers", type=int, default=8)
@@ -499,7 +523,7 @@ def main():
         reserve = (fill_steps + Wm + K + 2) * wl["new_per_step"]
     table = recis.Table(D, spec.dtype, spec.optim, seed=spec.seed, init_bound=spec.init_bound,
                         admit_threshold=spec.admit_threshold, reserve_rows=reserve,
-                        block_memory=args.block_memory, **wl["table"])
+                        block_memory=args.block_memory, track_last_use=args.track_last_use, **wl["table"])
     gen = torch.Generator(device=dev)
     gen.manual_seed(20250925)
     pdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -684,7 +708,11 @@ def main():
     }
     if args.export_import:
         result["export_import"] = export_import(torch, recis, table, spec, wl, D, s_bytes, S, args.block_memory)
+    if args.track_last_use:
+        result["config"]["track_last_use"] = True
     if args.evict_pass:
+        if args.track_last_use:
+            result["evict_lru_pass"] = evict_lru_pass(torch, table)
         result["evict_pass"] = evict_pass(torch, table)
     if args.block_memory == "host":
         result["config"]["block_memory"] = "host (pinned, mapped; IDMap and scratch in HBM)"

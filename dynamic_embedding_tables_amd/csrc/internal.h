@@ -255,6 +255,9 @@ struct TableDev {
   unsigned long long seed;
   float init_scale;                    // bound * 2^-23
   long long rows_limit;                // rows covered by blocks
+  unsigned* last_use;                  // per IDMap slot: the counting lookup that last saw its key
+                                       // (nullptr when the table does not track it)
+  unsigned step;                       // counting lookups so far
 };
 
 __device__ __forceinline__ unsigned long long next_slot(const TableDev& t, unsigned long long p) {
@@ -345,6 +348,8 @@ struct recis_table {
   int* uslot = nullptr;
   int* posmap = nullptr;
   unsigned long long* blk_sums = nullptr;
+  unsigned* last_use = nullptr;  // [slot_cap] when cfg.track_last_use
+  unsigned step = 0;             // counting lookups so far
   long long* wb_keys = nullptr;
   double* partials = nullptr;
 
@@ -364,7 +369,8 @@ namespace recis {
 // Launchers (defined in the .hip files; all enqueue on `s`).
 void launch_fill_slots(Slot* slots, long long cap, hipStream_t s);
 void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s);
-void launch_rehash(const Slot* old_slots, long long old_cap, const TableDev& t, hipStream_t s);
+void launch_rehash(const Slot* old_slots, const unsigned* old_last_use, long long old_cap, const TableDev& t,
+                   hipStream_t s);
 
 // Logical index of workgroup i of a grid of G.  Workgroups are dealt to the
 // 8 XCDs round robin (i mod 8); this gives the workgroups of one XCD
@@ -414,6 +420,8 @@ struct LookupLaunch {
   int* klist;                    // N: heavy buckets' distinct keys (dedup-table slots), by bucket range
   int* hslice;                   // heavy slices: count, then (bucket, slice) pairs
   long long hmax;                // bound on the heavy slices of the call (their grids)
+  unsigned* last_use;            // stamped with `step` for every key the call counts (or nullptr)
+  unsigned step;
 };
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);
 
@@ -430,6 +438,10 @@ recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, 
                              double* partials, bool current, hipStream_t s);
 
 void launch_evict(const TableDev& t, unsigned min_count, double decay, long long* num_evicted, hipStream_t s);
+// LRU-bounded pass: keeps the youngest ages whole within max_keys; `work`
+// holds age_hist_words(slot_cap) ints of device scratch.
+long long age_hist_words(long long slot_cap);
+void launch_evict_lru(const TableDev& t, long long max_keys, int* work, long long* num_evicted, hipStream_t s);
 void launch_writeback(const TableDev& t, const long long* keys, long long n, const float* rows,
                       DedupSlot* dd, unsigned long long dd_mask, int dd_shift, long long* wb_keys,
                       int* uslot, hipStream_t s);

@@ -515,6 +515,8 @@ __device__ __forceinline__ void key_outputs(const LookupLaunch& L, long long u, 
   unsigned* idslot = reinterpret_cast<unsigned*>(L.res.plan + plan_layout(L.res.capacity).o_idslot);
   L.res.unique_rows[u] = o.need ? -2 : o.row;  // -2: needs a row from this call
   idslot[u] = o.sl;
+  // the key's last use (tables that keep it; counting calls only)
+  if (L.last_use && o.sl != 0xFFFFFFFFu) L.last_use[o.sl] = L.step;
   sum += ((unsigned long long)o.need << 32) | (unsigned)o.ins;
   // a key that will have a row and more than kShortMax occurrences is reduced
   // in chunks by the backward

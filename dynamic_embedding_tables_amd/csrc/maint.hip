@@ -50,7 +50,7 @@ __device__ __forceinline__ long long claim_slot(const TableDev& t, long long key
   return -1;
 }
 
-__global__ void k_rehash(const Slot* old_slots, long long old_cap, TableDev t) {
+__global__ void k_rehash(const Slot* old_slots, const unsigned* old_last_use, long long old_cap, TableDev t) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < old_cap;
        i += (long long)gridDim.x * blockDim.x) {
     const Slot s = old_slots[i];
@@ -62,6 +62,7 @@ __global__ void k_rehash(const Slot* old_slots, long long old_cap, TableDev t) {
     }
     t.slots[p].row = s.row;
     t.slots[p].count = s.count;
+    if (t.last_use) t.last_use[p] = old_last_use[i];
   }
 }
 
@@ -79,6 +80,15 @@ __device__ __forceinline__ long long wave_add(unsigned long long* ctr, bool take
 
 __global__ void k_set_scratch(DevCounters* c) { c->scratch_count = 0; }
 
+// A key's age for the LRU pass: counting lookups since one last counted it,
+// ages from kAgeBins - 1 on taken as one.
+constexpr int kAgeBins = 256;
+constexpr long long kAgeSpan = 1 << 16;
+__device__ __forceinline__ int age_of(const TableDev& t, long long i) {
+  const unsigned a = t.step - t.last_use[i];
+  return a < (unsigned)kAgeBins ? (int)a : kAgeBins - 1;
+}
+
 // Eviction: keys whose window count is below min_count leave (their slot is
 // marked gone and the IDMap is rebuilt afterwards); their rows go to the free
 // list; survivors keep floor(count * decay) (0: the window restarts).  A
@@ -87,7 +97,8 @@ __global__ void k_set_scratch(DevCounters* c) { c->scratch_count = 0; }
 // device atomics on one address execute one after another at the memory
 // side, so one per wave would serialise the pass.
 constexpr int kEvictSpan = 4096;
-__global__ __launch_bounds__(256) void k_evict_mark(TableDev t, unsigned min_count, double decay) {
+__global__ __launch_bounds__(256) void k_evict_mark(TableDev t, unsigned min_count, double decay,
+                                                    const int* lru_cut) {
   __shared__ int s_rows[kEvictSpan];
   __shared__ int s_nfree, s_ngone;
   __shared__ long long s_base;
@@ -97,6 +108,7 @@ __global__ __launch_bounds__(256) void k_evict_mark(TableDev t, unsigned min_cou
     s_ngone = 0;
   }
   __syncthreads();
+  const int cut = lru_cut ? *lru_cut : 0;  // LRU pass: the oldest age kept; counts stay as they are
   const long long b0 = (long long)blockIdx.x * kEvictSpan;
   for (int k0 = 0; k0 < kEvictSpan; k0 += 256) {
     const long long i = b0 + k0 + threadIdx.x;
@@ -104,7 +116,13 @@ __global__ __launch_bounds__(256) void k_evict_mark(TableDev t, unsigned min_cou
     int row = -1;
     if (i <= (long long)t.slot_mask) {
       const Slot s = t.slots[i];
-      if (s.key >= 0) {
+      if (s.key >= 0 && lru_cut) {
+        if (age_of(t, i) > cut) {
+          gone = true;
+          row = s.row < 0 ? -1 : (s.row & ~kPendingRow);
+          t.slots[i].key = kGoneKey;
+        }
+      } else if (s.key >= 0) {
         if (s.count < min_count) {
           gone = true;
           row = s.row < 0 ? -1 : (s.row & ~kPendingRow);
@@ -244,7 +262,10 @@ __global__ __launch_bounds__(256) void k_wb_apply(TableDev t, const float* rows,
       if (at < 0) {
         atomicOr(&t.ctr->error, kErrCapacity);
       } else {
-        if (inserted) atomicAdd(&t.ctr->num_keys, 1ull);
+        if (inserted) {
+          atomicAdd(&t.ctr->num_keys, 1ull);
+          if (t.last_use) t.last_use[at] = t.step;
+        }
         row = inserted ? -1 : t.slots[at].row;
         if (row >= 0 && (row & kPendingRow)) {  // allocated, never written: written now
           row &= ~(long long)kPendingRow;
@@ -405,6 +426,7 @@ __global__ __launch_bounds__(256) void k_import(TableDev t, long long n, const l
     long long r = -1;
     if (at >= 0) {
       t.slots[at].count = counts[k];
+      if (t.last_use) t.last_use[at] = t.step;
       if (want_row && row < t.rows_limit) r = row;
       else if (want_row) err |= kErrCapacity;
       t.slots[at].row = r >= 0 ? (int)r : -1;
@@ -439,6 +461,45 @@ __global__ __launch_bounds__(256) void k_import(TableDev t, long long n, const l
   }
 }
 
+// LRU-bounded eviction.  A key's age is the number of counting lookups since
+// one last counted it, with ages from 255 on taken as 255.  k_age_hist: per
+// block of kAgeSpan slots, the histogram of ages in LDS, written as that
+// block's row of `work`.  k_age_cut: one block sums the rows and finds the
+// oldest age that can stay: the youngest ages are kept whole while their
+// keys fit in max_keys.  k_evict_mark then removes every older key.
+
+__global__ __launch_bounds__(256) void k_age_hist(TableDev t, int* work) {
+  __shared__ int s_h[kAgeBins];
+  s_h[threadIdx.x] = 0;
+  __syncthreads();
+  const long long b0 = (long long)blockIdx.x * kAgeSpan;
+  for (long long k = threadIdx.x; k < kAgeSpan; k += 256) {
+    const long long i = b0 + k;
+    if (i > (long long)t.slot_mask) break;
+    if (t.slots[i].key >= 0) atomicAdd(&s_h[age_of(t, i)], 1);
+  }
+  __syncthreads();
+  work[(long long)blockIdx.x * kAgeBins + threadIdx.x] = s_h[threadIdx.x];
+}
+
+// work[nblocks * kAgeBins] holds the cut afterwards: the oldest age kept (-1: none)
+__global__ __launch_bounds__(256) void k_age_cut(int* work, long long nblocks, long long max_keys) {
+  __shared__ long long s_c[kAgeBins];
+  long long c = 0;
+  for (long long b = 0; b < nblocks; ++b) c += work[b * kAgeBins + threadIdx.x];
+  s_c[threadIdx.x] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long keep = 0;
+    int oldest = -1;
+    for (int a = 0; a < kAgeBins && keep + s_c[a] <= max_keys; ++a) {
+      keep += s_c[a];
+      oldest = a;
+    }
+    work[nblocks * kAgeBins] = oldest;
+  }
+}
+
 unsigned grid_for(long long n, int threads) {
   long long g = (n + threads - 1) / threads;
   if (g > 65536) g = 65536;
@@ -456,14 +517,28 @@ void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_dedup, dim3(grid_for(cap, 256)), dim3(256), 0, s, dd, cap);
 }
 
-void launch_rehash(const Slot* old_slots, long long old_cap, const TableDev& t, hipStream_t s) {
-  hipLaunchKernelGGL(k_rehash, dim3(grid_for(old_cap, 256)), dim3(256), 0, s, old_slots, old_cap, t);
+void launch_rehash(const Slot* old_slots, const unsigned* old_last_use, long long old_cap, const TableDev& t,
+                   hipStream_t s) {
+  hipLaunchKernelGGL(k_rehash, dim3(grid_for(old_cap, 256)), dim3(256), 0, s, old_slots, old_last_use, old_cap, t);
 }
 
 void launch_evict(const TableDev& t, unsigned min_count, double decay, long long* num_evicted, hipStream_t s) {
   hipLaunchKernelGGL(k_set_scratch, dim3(1), dim3(1), 0, s, t.ctr);
   const long long nb = ((long long)t.slot_mask + kEvictSpan) / kEvictSpan;
-  hipLaunchKernelGGL(k_evict_mark, dim3((unsigned)nb), dim3(256), 0, s, t, min_count, decay);
+  hipLaunchKernelGGL(k_evict_mark, dim3((unsigned)nb), dim3(256), 0, s, t, min_count, decay, (const int*)nullptr);
+  hipLaunchKernelGGL(k_evict_done, dim3(1), dim3(1), 0, s, t.ctr, num_evicted);
+}
+
+long long age_hist_words(long long slot_cap) { return (slot_cap + kAgeSpan - 1) / kAgeSpan * kAgeBins + 1; }
+
+void launch_evict_lru(const TableDev& t, long long max_keys, int* work, long long* num_evicted, hipStream_t s) {
+  const long long hb = ((long long)t.slot_mask + kAgeSpan) / kAgeSpan;
+  hipLaunchKernelGGL(k_set_scratch, dim3(1), dim3(1), 0, s, t.ctr);
+  hipLaunchKernelGGL(k_age_hist, dim3((unsigned)hb), dim3(256), 0, s, t, work);
+  hipLaunchKernelGGL(k_age_cut, dim3(1), dim3(256), 0, s, work, hb, max_keys);
+  const long long nb = ((long long)t.slot_mask + kEvictSpan) / kEvictSpan;
+  hipLaunchKernelGGL(k_evict_mark, dim3((unsigned)nb), dim3(256), 0, s, t, 0u, 0.0,
+                     (const int*)(work + hb * kAgeBins));
   hipLaunchKernelGGL(k_evict_done, dim3(1), dim3(1), 0, s, t.ctr, num_evicted);
 }
 

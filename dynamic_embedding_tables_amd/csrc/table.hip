@@ -164,16 +164,27 @@ recis_status grow_rows(recis_table* t, long long rows, hipStream_t s) {
 // Rebuilds the IDMap into `new_cap` slots (growth or after eviction).
 recis_status rebuild_idmap(recis_table* t, long long new_cap, hipStream_t s) {
   Slot* old = t->slots;
+  unsigned* old_lu = t->last_use;
   const long long old_cap = t->slot_cap;
   Slot* ns = static_cast<Slot*>(tab_alloc(t, (size_t)new_cap * sizeof(Slot), s));
   if (!ns) return RECIS_ERR_OUT_OF_MEMORY;
+  unsigned* nlu = nullptr;
+  if (old_lu) {  // last-use stamps move with their keys
+    nlu = static_cast<unsigned*>(tab_alloc(t, (size_t)new_cap * sizeof(unsigned), s));
+    if (!nlu) {
+      tab_free(t, ns, (size_t)new_cap * sizeof(Slot), s);
+      return RECIS_ERR_OUT_OF_MEMORY;
+    }
+  }
   launch_fill_slots(ns, new_cap, s);
   t->slots = ns;
+  t->last_use = nlu;
   t->slot_cap = new_cap;
-  launch_rehash(old, old_cap, t->dev(), s);
+  launch_rehash(old, old_lu, old_cap, t->dev(), s);
   recis_status st = check_launch();
   HIP_TRY(hipStreamSynchronize(s));
   tab_free(t, old, (size_t)old_cap * sizeof(Slot), s);
+  if (old_lu) tab_free(t, old_lu, (size_t)old_cap * sizeof(unsigned), s);
   return st;
 }
 
@@ -357,6 +368,8 @@ TableDev recis_table::dev() const {
   d.seed = cfg.seed;
   d.init_scale = std::ldexp(cfg.init_bound, -23);
   d.rows_limit = rows_alloc;
+  d.last_use = last_use;
+  d.step = step;
   return d;
 }
 
@@ -396,6 +409,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   if (cfg->max_rows < 1 || cfg->max_rows > kMaxRows) return RECIS_ERR_INVALID_ARG;
   if (cfg->reserve_rows < 0) return RECIS_ERR_INVALID_ARG;
   if (cfg->block_memory != RECIS_MEM_DEVICE && cfg->block_memory != RECIS_MEM_HOST) return RECIS_ERR_INVALID_ARG;
+  if (cfg->track_last_use != 0 && cfg->track_last_use != 1) return RECIS_ERR_INVALID_ARG;
   if (alloc && (!alloc->alloc || !alloc->free)) return RECIS_ERR_INVALID_ARG;
   if (!valid_dim(cfg->dim)) return RECIS_ERR_UNSUPPORTED;
 
@@ -424,6 +438,10 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   t->slot_cap = std::max<long long>(next_pow2(cfg->slot_capacity), 64);
   t->slots = static_cast<Slot*>(tab_alloc(t, (size_t)t->slot_cap * sizeof(Slot), s));
   if (!t->slots) return fail(RECIS_ERR_OUT_OF_MEMORY);
+  if (cfg->track_last_use) {  // stamped whenever a key enters; empty slots' stamps are never read
+    t->last_use = static_cast<unsigned*>(tab_alloc(t, (size_t)t->slot_cap * sizeof(unsigned), s));
+    if (!t->last_use) return fail(RECIS_ERR_OUT_OF_MEMORY);
+  }
   launch_fill_slots(t->slots, t->slot_cap, s);
   if (check_launch() != RECIS_OK) return fail(RECIS_ERR_HIP);
   recis_status st = grow_rows(t, std::max<long long>(cfg->reserve_rows, 1), s);
@@ -443,6 +461,7 @@ recis_status recis_idmap_destroy(recis_table* t) {
   tab_free(t, t->d_blocks, t->d_blocks_cap * sizeof(char*), s);
   tab_free(t, t->free_list, (size_t)t->free_cap * 4, s);
   tab_free(t, t->slots, (size_t)t->slot_cap * sizeof(Slot), s);
+  tab_free(t, t->last_use, (size_t)t->slot_cap * sizeof(unsigned), s);
   tab_free(t, t->ctr, sizeof(DevCounters), s);
   free_scratch(t, s);
   for (int k = 0; k < recis_table::kRing; ++k) {
@@ -554,6 +573,10 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.klist = t->uslot;
   L.hslice = reinterpret_cast<int*>(t->wb_keys);
   L.hmax = N / kSliceOcc + N / kHeavyOcc + 1;
+  const bool counting = (flags & RECIS_FIND_ONLY) == 0;
+  if (counting) t->step += 1;
+  L.last_use = counting ? t->last_use : nullptr;
+  L.step = t->step;
   launch_lookup(L, t->dev(), s);
   return check_launch();
 }
@@ -579,6 +602,28 @@ recis_status recis_idmap_evict_decay(recis_table* t, uint32_t min_count, double 
 
 recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted, hipStream_t s) {
   return recis_idmap_evict_decay(t, min_count, 0.0, num_evicted, s);
+}
+
+recis_status recis_idmap_evict_lru(recis_table* t, int64_t max_keys, int64_t* num_evicted, hipStream_t s) {
+  if (!t || max_keys < 0) return RECIS_ERR_INVALID_ARG;
+  if (!t->last_use) return RECIS_ERR_UNSUPPORTED;
+  ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
+  const size_t wbytes = (size_t)age_hist_words(t->slot_cap) * sizeof(int);
+  int* work = static_cast<int*>(tab_alloc(t, wbytes, s));
+  if (!work) return RECIS_ERR_OUT_OF_MEMORY;
+  t->update_epoch += 1;
+  launch_evict_lru(t->dev(), max_keys, work, reinterpret_cast<long long*>(num_evicted), s);
+  recis_status st = check_launch();
+  if (st == RECIS_OK) st = rebuild_idmap(t, t->slot_cap, s);  // synchronises: work is idle after
+  tab_free(t, work, wbytes, s);
+  if (st != RECIS_OK) return st;
+  DevCounters c;
+  st = read_counters(t, &c, s);
+  if (st != RECIS_OK) return st;
+  t->rows_hi = (long long)c.next_row;
+  t->keys_hi = (long long)c.num_keys;
+  return RECIS_OK;
 }
 
 recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_result* res, int32_t pool, void* out,

@@ -48,7 +48,8 @@ POOLS = {"sum": RECIS_POOL_SUM, "mean": RECIS_POOL_MEAN, "none": RECIS_POOL_NONE
 
 EXPORTED_SYMBOLS = (
     "recis_table_config_default", "recis_plan_words", "recis_idmap_create", "recis_idmap_destroy",
-    "recis_idmap_insert_find", "recis_idmap_evict", "recis_idmap_evict_decay", "recis_lookup_pool_fwd",
+    "recis_idmap_insert_find", "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru",
+    "recis_lookup_pool_fwd",
     "recis_pool_bwd_update",
     "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats", "recis_get_error",
     "recis_status_string", "recis_profile_kernel",
@@ -59,7 +60,8 @@ class recis_table_config(C.Structure):
     _fields_ = [("dim", C.c_int32), ("dtype", C.c_int32), ("optim", C.c_int32),
                 ("admit_threshold", C.c_uint32), ("seed", C.c_uint64), ("init_bound", C.c_float),
                 ("max_load", C.c_float), ("slot_capacity", C.c_int64), ("block_rows", C.c_int64),
-                ("max_rows", C.c_int64), ("reserve_rows", C.c_int64), ("block_memory", C.c_int32)]
+                ("max_rows", C.c_int64), ("reserve_rows", C.c_int64), ("block_memory", C.c_int32),
+                ("track_last_use", C.c_int32)]
 
 
 class recis_allocator(C.Structure):
@@ -118,6 +120,7 @@ def load_library() -> C.CDLL:
                                           C.POINTER(recis_lookup_result), p]
     L.recis_idmap_evict.argtypes = [p, u32, p, p]
     L.recis_idmap_evict_decay.argtypes = [p, u32, C.c_double, p, p]
+    L.recis_idmap_evict_lru.argtypes = [p, i64, p, p]
     L.recis_lookup_pool_fwd.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, p]
     L.recis_pool_bwd_update.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, i32,
                                         C.POINTER(recis_optim_params), p]
@@ -130,7 +133,8 @@ def load_library() -> C.CDLL:
     L.recis_status_string.argtypes = [i32]
     L.recis_status_string.restype = C.c_char_p
     for name in ("recis_idmap_create", "recis_idmap_destroy", "recis_idmap_insert_find",
-                 "recis_idmap_evict", "recis_idmap_evict_decay", "recis_lookup_pool_fwd", "recis_pool_bwd_update",
+                 "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru", "recis_lookup_pool_fwd",
+                 "recis_pool_bwd_update",
                  "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats",
                  "recis_get_error"):
         getattr(L, name).restype = i32
@@ -188,6 +192,11 @@ def recis_idmap_insert_find(h, descs, num_feats: int, batch: int, flags: int,
 def recis_idmap_evict(h, min_count: int, num_evicted=None, stream=None):
     _check(load_library().recis_idmap_evict(h, min_count, _ptr(num_evicted), _stream(stream)),
            "recis_idmap_evict")
+
+
+def recis_idmap_evict_lru(h, max_keys: int, num_evicted=None, stream=None):
+    _check(load_library().recis_idmap_evict_lru(h, max_keys, _ptr(num_evicted), _stream(stream)),
+           "recis_idmap_evict_lru")
 
 
 def recis_idmap_evict_decay(h, min_count: int, decay: float, num_evicted=None, stream=None):
@@ -306,13 +315,15 @@ class Table:
     def __init__(self, dim: int, dtype: str = "f32", optim: str = "adagrad", seed: int = 20250925,
                  init_bound: float = 0.05, admit_threshold: int = 1, slot_capacity: int = 1 << 20,
                  block_rows: int = 1 << 20, max_rows: int = (1 << 30) - 1, reserve_rows: int = 0,
-                 max_load: float = 0.5, block_memory: str = "device", stream=None):
+                 max_load: float = 0.5, block_memory: str = "device", track_last_use: bool = False,
+                 stream=None):
         cfg = recis_table_config_default()
         cfg.dim, cfg.dtype, cfg.optim = dim, DTYPES[dtype], OPTIMS[optim]
         cfg.seed, cfg.init_bound, cfg.admit_threshold = seed, init_bound, admit_threshold
         cfg.slot_capacity, cfg.block_rows, cfg.max_rows = slot_capacity, block_rows, max_rows
         cfg.reserve_rows, cfg.max_load = reserve_rows, max_load
         cfg.block_memory = {"device": RECIS_MEM_DEVICE, "host": RECIS_MEM_HOST}[block_memory]
+        cfg.track_last_use = 1 if track_last_use else 0
         self.dim, self.dtype, self.optim = dim, dtype, optim
         self.config = {"seed": seed, "init_bound": init_bound, "admit_threshold": admit_threshold,
                        "block_memory": block_memory}
@@ -351,6 +362,11 @@ class Table:
             recis_idmap_evict(self.h, min_count, num_evicted, stream)
         else:
             recis_idmap_evict_decay(self.h, min_count, decay, num_evicted, stream)
+
+    def evict_lru(self, max_keys: int, num_evicted=None, stream=None):
+        """Keeps at most max_keys keys, the most recently used (needs
+        track_last_use)."""
+        recis_idmap_evict_lru(self.h, max_keys, num_evicted, stream)
 
     def writeback(self, keys, rows, stream=None):
         recis_writeback(self.h, keys, int(keys.numel()), rows, stream)

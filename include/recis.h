@@ -109,11 +109,13 @@ typedef struct {
   int32_t block_memory;     /* RECIS_MEM_DEVICE (from the allocator) or RECIS_MEM_HOST
                                (hipHostMalloc, non-coherent: rows may be cached by the GPU
                                during a call, so the host must not touch them directly) */
+  int32_t track_last_use;   /* 1: every counting insert_find stamps the keys it sees (4
+                               bytes per IDMap slot), for recis_idmap_evict_lru; 0: off */
 } recis_table_config;
 
 /* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
  * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0,
- * blocks in device memory). */
+ * blocks in device memory, no last-use stamps). */
 void recis_table_config_default(recis_table_config* cfg);
 
 /* Device-memory provider.  alloc returns `bytes` of device memory (256-byte
@@ -226,6 +228,20 @@ recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_
  * Errors: INVALID_ARG (decay outside [0, 1]); as recis_idmap_evict. */
 recis_status recis_idmap_evict_decay(recis_table* t, uint32_t min_count, double decay,
                                      int64_t* num_evicted, hipStream_t s);
+
+/* LRU-bounded capacity: keeps at most max_keys keys, the most recently used.
+ * A key's age is the number of counting insert_find calls (not FIND_ONLY)
+ * since one last counted it (writeback and import stamp the keys they add
+ * with the latest call); ages of 255 or more count as 255.  The pass keeps
+ * the youngest ages whole, as many of them as fit in max_keys keys together,
+ * and removes every older key, returning its row to the free list; counts are
+ * untouched.  Another of the eviction strategies the pages leave open (page
+ * "RecIS (Recommendation Intelligence System)" README, section "Core
+ * architecture > Embedding Engine").  Needs track_last_use (else
+ * UNSUPPORTED); max_keys >= 0.  num_evicted: device [1] (may be NULL).
+ * Synchronises `s`. */
+recis_status recis_idmap_evict_lru(recis_table* t, int64_t max_keys, int64_t* num_evicted,
+                                   hipStream_t s);
 
 /* Forward: SUM / MEAN write float32 out [batch, num_feats * dim] with
  * out[i, f*dim + d] = pooled element d of bag (f, i) (mean divides by the bag

@@ -92,7 +92,7 @@ def test_invalid_arguments_return_synchronously(lib):
     assert L.recis_idmap_create(C.byref(c), None, None, None) == lib.RECIS_ERR_INVALID_ARG
     for field, bad in [("dtype", 7), ("optim", 9), ("max_load", 0.0), ("max_load", 0.8),
                        ("slot_capacity", 0), ("block_rows", 0), ("max_rows", 0), ("max_rows", 2**30),
-                       ("reserve_rows", -1), ("init_bound", -1.0), ("block_memory", 2)]:
+                       ("reserve_rows", -1), ("init_bound", -1.0), ("block_memory", 2), ("track_last_use", 2)]:
         c = lib.recis_table_config_default()
         setattr(c, field, bad)
         assert L.recis_idmap_create(C.byref(c), None, None, C.byref(h)) == lib.RECIS_ERR_INVALID_ARG, field
@@ -107,6 +107,7 @@ def test_invalid_arguments_return_synchronously(lib):
     assert L.recis_idmap_insert_find(None, None, 0, 0, 0, C.byref(res), None) == lib.RECIS_ERR_INVALID_ARG
     assert L.recis_idmap_evict(None, 1, None, None) == lib.RECIS_ERR_INVALID_ARG
     assert L.recis_idmap_evict_decay(None, 1, 0.5, None, None) == lib.RECIS_ERR_INVALID_ARG
+    assert L.recis_idmap_evict_lru(None, 1, None, None) == lib.RECIS_ERR_INVALID_ARG
     assert L.recis_idmap_import(None, 0, None, None, None, None, None, 0, None) == lib.RECIS_ERR_INVALID_ARG
     assert L.recis_lookup_pool_fwd(None, C.byref(res), 0, None, None) == lib.RECIS_ERR_INVALID_ARG
     opt = lib.recis_optim_params(0.01, 0.9, 0.999, 1e-8)

@@ -30,11 +30,12 @@ def _gpu():
 
 
 def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopulate=None,
-               export_every=1, evict_decay=0.0):
+               export_every=1, evict_decay=0.0, lru_max=None, find_only_steps=()):
     import torch
     from dynamic_embedding_tables_amd import recis
     table = make_table(spec, **(table_kw or {}))
     otab = oracle.OracleTable(spec)
+    passes = []  # LRU passes: (keys before, keys evicted)
     if prepopulate is not None:
         cap = max(prepopulate.n, 1)
         res = recis.LookupResult(cap, prepopulate.num_feats * prepopulate.batch)
@@ -45,22 +46,30 @@ def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopu
     for step, b in enumerate(batches):
         print(f"[parity] step {step} N={b.n}", flush=True)
         res = recis.LookupResult(max(b.n, 1), b.num_feats * b.batch)
-        out, _ = gpu_step(table, spec, b, res)
-        r, oout, oab = oracle_step(otab, spec, b)
+        fo = step in find_only_steps
+        out, _ = gpu_step(table, spec, b, res, find_only=fo, with_backward=not fo)
+        r, oout, oab = oracle_step(otab, spec, b, find_only=fo, with_backward=not fo)
         torch.cuda.synchronize()
         assert table.get_error() == 0
         check_lookup(canon_lookup(res), r)
         check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats, exact=step == 0 and prepopulate is None)
         if evict_every and (step + 1) % evict_every == 0:
             ne = torch.zeros(1, dtype=torch.int64, device="cuda")
-            table.evict(evict_min, ne, decay=evict_decay)
-            assert int(ne.item()) == otab.evict(evict_min, evict_decay)
+            if lru_max is not None:
+                before = otab.size()
+                table.evict_lru(lru_max, ne)
+                assert int(ne.item()) == otab.evict_lru(lru_max)
+                passes.append((before, int(ne.item())))
+            else:
+                table.evict(evict_min, ne, decay=evict_decay)
+                assert int(ne.item()) == otab.evict(evict_min, evict_decay)
         if (step + 1) % export_every == 0 or step == len(batches) - 1:
             check_export(canon_export(table), otab.export(), spec)
     st = table.stats()
     assert st.keys == otab.size()
     assert st.rows_in_use == otab.rows_in_use()
     table.close()
+    return passes
 
 
 def test_tiny_config_all_ten_steps():
@@ -100,6 +109,28 @@ def test_eviction_with_decayed_counts(decay):
     spec = W.spec_multi(3)
     batches = [W.multi_batch(s, 3, batch=128, num_feats=6) for s in range(8)]
     run_parity(spec, batches, evict_every=2, evict_min=3, evict_decay=decay)
+
+
+@pytest.mark.parametrize("lru_max", [0, 2500, 4000])
+def test_eviction_lru_bounded(lru_max):
+    """LRU-bounded passes every other step (at most lru_max keys kept, whole
+    lookups youngest first) on the multi-table config with admission at 2
+    and a FIND_ONLY lookup between (which must not refresh ages): the
+    evicted counts, key sets, counts and rows step by step."""
+    spec = W.spec_multi(4)
+    batches = [W.multi_batch(s, 4, batch=64, num_feats=4) for s in range(9)]
+    passes = run_parity(spec, batches, table_kw=dict(track_last_use=True), evict_every=2, lru_max=lru_max,
+                        find_only_steps=(4,))
+    if lru_max > 0:  # some pass kept part of the table and removed the rest
+        assert any(0 < ev < before for before, ev in passes), passes
+
+
+def test_eviction_lru_after_growth():
+    """The stamps move with their keys when the IDMap grows (64 slots to
+    start) and when a pass rebuilds it."""
+    spec = W.spec_ctr()
+    run_parity(spec, [W.ctr_batch(s, batch=64, num_feats=8) for s in range(6)],
+               table_kw=dict(slot_capacity=64, block_rows=64, track_last_use=True), evict_every=2, lru_max=2000)
 
 
 # ---- full sizes: the bench's workload and table configuration, and the
