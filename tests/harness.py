@@ -122,9 +122,12 @@ def check_forward(out_gpu, spec, oracle_out, oracle_abs, merged_offsets=None, nu
     """gather: a copy of the stored rows -- bit-exact while every row still holds
     its initial values (exact=True, the first step), afterwards within the
     parameter tolerance (rows updated on both sides may differ by an ulp).
-    pooled: |y - y_ref| <= 1e-5 * (sum |terms| + terms * lr), the summation-order
+    pooled: |y - y_ref| <= tol * (sum |terms| + terms * lr), the summation-order
     bound of fp32 plus the parameter tolerance that earlier updates may already
-    have used (terms = bag length for sum, 1 for mean)."""
+    have used (terms = bag length for sum, 1 for mean); tol = 1e-5, or 1e-2 for
+    bf16 storage once rows have been updated (the stored rows themselves may
+    then differ by a bf16 rounding step, within the 1e-2 relative bar for bf16
+    storage on pooled outputs and updated rows)."""
     if spec.pool == "none":
         import torch
         if spec.dtype == "bf16":
@@ -142,12 +145,13 @@ def check_forward(out_gpu, spec, oracle_out, oracle_abs, merged_offsets=None, nu
         return
     g = out_gpu.cpu().numpy()
     err = np.abs(g.astype(np.float64) - oracle_out.astype(np.float64))
-    bound = 1e-5 * oracle_abs
+    tol = 1e-2 if spec.dtype == "bf16" and not exact and spec.optim != "none" else 1e-5
+    bound = tol * oracle_abs
     if merged_offsets is not None and spec.optim != "none":
         B = g.shape[0]
         lens = np.diff(merged_offsets.astype(np.int64)).reshape(num_feats, B).T   # [B, F]
         terms = lens if spec.pool == "sum" else (lens > 0).astype(np.int64)
-        bound = bound + 1e-5 * spec.lr * np.repeat(terms, spec.dim, axis=1)
+        bound = bound + tol * spec.lr * np.repeat(terms, spec.dim, axis=1)
     bad = err > bound + 1e-30
     assert not bad.any(), f"{bad.sum()} pooled elements off; worst {np.max(err - bound)}"
 

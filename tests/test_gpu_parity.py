@@ -327,6 +327,26 @@ def test_pooled_forward_bag_shapes(dtype, dim, pool):
     run_parity(spec, [a, b])
 
 
+@pytest.mark.parametrize("dtype,optim,pool,grad_dtype,dim", [
+    ("bf16", "adam", "mean", "f32", 64), ("bf16", "adam", "sum", "bf16", 128),
+    ("f32", "adam", "none", "f32", 32), ("bf16", "adam", "none", "bf16", 256),
+    ("f32", "adagrad", "none", "bf16", 16)])
+def test_storage_optimizer_pooling_combinations(dtype, optim, pool, grad_dtype, dim):
+    """Storage dtype x optimizer x pooling x gradient dtype combinations the
+    workload configs leave out, over three steps with hot and cold keys."""
+    spec = W.TableSpec(dim=dim, dtype=dtype, optim=optim, pool=pool, lr=1e-3 if optim == "adam" else 0.01,
+                       eps=1e-8 if optim == "adam" else 1e-10, grad_dtype=grad_dtype)
+    batches = []
+    for step in range(3):
+        b = _ragged_pool_batch(60 + step, 700, dim, 2000)
+        if pool == "none":
+            b.grad = W.rng_for(61, step).standard_normal((b.n, dim), dtype=np.float32)
+        else:
+            b.grad = W.rng_for(61, step).standard_normal((b.batch, b.num_feats * dim), dtype=np.float32)
+        batches.append(b)
+    run_parity(spec, batches)
+
+
 @pytest.mark.parametrize("optim", ["adam", "adagrad"])
 def test_interleaved_lookups(optim):
     """Lookup A, lookup B (sharing keys that are new in A), update A, then
