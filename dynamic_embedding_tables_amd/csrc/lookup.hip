@@ -453,22 +453,41 @@ __device__ __forceinline__ ProbeOut idmap_probe(const TableDev& t, long long key
   ProbeOut o;
   if (key < 0) return o;  // a failed transform
   unsigned long long p = slot_of(key, t.slot_shift);
-  bool found = false, inserted = false;
+  bool found = false, inserted = false, stop = false;
   Slot sv;
-  for (unsigned long long n = 0; n <= t.region_mask; ++n) {
-    sv = t.slots[p];
-    if (sv.key == key) {
-      found = true;
-      break;
-    }
-    if (sv.key == kEmptyKey) {
-      if (find_only) break;
-      if (claim(p)) {
-        inserted = true;
-        break;
+  // kProbeBatch consecutive slots per round trip, examined in probe order: at
+  // the table's load a linear probe ends within the first few slots, so one
+  // round trip usually settles the key instead of one per slot
+  constexpr int kProbeBatch = 4;
+  for (unsigned long long n = 0; n <= t.region_mask && !stop; n += kProbeBatch) {
+    unsigned long long q[kProbeBatch];
+    Slot v[kProbeBatch];
+    q[0] = p;
+#pragma unroll
+    for (int k = 1; k < kProbeBatch; ++k) q[k] = next_slot(t, q[k - 1]);
+#pragma unroll
+    for (int k = 0; k < kProbeBatch; ++k) v[k] = t.slots[q[k]];
+#pragma unroll
+    for (int k = 0; k < kProbeBatch; ++k) {
+      if (stop) continue;
+      if (n + k > t.region_mask) {  // the whole region seen
+        stop = true;
+        continue;
+      }
+      if (v[k].key == key) {
+        found = stop = true;
+        p = q[k];
+        sv = v[k];
+      } else if (v[k].key == kEmptyKey) {
+        if (find_only) {
+          stop = true;
+        } else if (claim(q[k])) {
+          inserted = stop = true;
+          p = q[k];
+        }
       }
     }
-    p = next_slot(t, p);
+    p = stop ? p : next_slot(t, q[kProbeBatch - 1]);
   }
   if (!found && !inserted) {
     if (!find_only) o.err = kErrCapacity;  // the key's region is full
