@@ -449,6 +449,27 @@ def summarize(prof_dir, kernel, command, out_path, workload="ctr", block_memory=
     print("\n".join(lines))
 
 
+def summarize_atomics(prof_dir, command, out_path, workload="ctr", last=5):
+    """Writes the committed summary of a TCC_ATOMIC / TCC_EA0_ATOMIC run
+    (rocprofv3 --pmc, csv, in prof_dir/atomics): device-scope atomics per
+    dispatch of every kernel over its last `last` dispatches (the timed
+    steps) -- the IDMap's insert / find and the rest of the step."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(prof_dir, "atomics", "p_counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        lab = _kernel_label(r["Kernel_Name"])
+        per.setdefault((lab, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 summary: device atomics per dispatch on the workload: {WORKLOADS[workload]['title']}",
+             f"# command: {command}", f"source_hash={kernel_source_hash()}"]
+    for (lab, cname), v in sorted(per.items()):
+        if lab == "copy" or lab.startswith("void at::"):
+            continue
+        lines.append(f"{cname}[{lab}]={np.mean(v[-last:]):.0f}  (last {min(last, len(v))} dispatches)")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,10 +495,15 @@ def main():
     ap.add_argument("--summarize", metavar="PROF_DIR",
                     help="write the profiles/ summary of a profiled run (see summarize()) and exit")
     ap.add_argument("--kernel", default="k_bwd_short")
+    ap.add_argument("--summarize-atomics", metavar="PROF_DIR")
     ap.add_argument("--command", default="")
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
     wl = WORKLOADS[args.workload]
+    if args.summarize_atomics:
+        summarize_atomics(args.summarize_atomics, args.command,
+                          args.out or os.path.join(ROOT, "profiles", f"atomics_{args.workload}.txt"), args.workload)
+        return
     if args.summarize:
         summarize(args.summarize, args.kernel, args.command,
                   args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{args.workload}_counters.txt"),
