@@ -408,6 +408,13 @@ struct BwdArgs {
   const int* plan;
   const unsigned* idslot;
   PlanLayout pl;
+  // the long-key plan: per long key its distinct index, first chunk and
+  // chunk count, and per chunk its key (the lookup's, or the same reordered
+  // feature by feature)
+  const int* long_u;
+  const int* long_base;
+  const int* long_nch;
+  const int* owner;
   int F, B, pool, gdt;
   const void* grad;
   OptConsts oc;
@@ -579,9 +586,9 @@ __global__ __launch_bounds__(256) void k_bwd_long_partial(BwdArgs a) {
   const int lane = wl % C, g = wl / C;
   const int nchunks = a.plan[1];
   const long long nwaves = (long long)gridDim.x * 4;
-  const int* long_u = a.plan + a.pl.o_long_u;
-  const int* long_base = a.plan + a.pl.o_long_base;
-  const int* owner = a.plan + a.pl.o_chunk_owner;
+  const int* long_u = a.long_u;
+  const int* long_base = a.long_base;
+  const int* owner = a.owner;
   for (long long q = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); q < nchunks; q += nwaves) {
     const int idx = owner[q];
     const int u = long_u[idx], cb = long_base[idx];
@@ -709,9 +716,9 @@ __global__ __launch_bounds__(256) void k_bwd_long_final(BwdArgs a) {
     int u = 0, cb = 0, nch = 0;
     long long r = -1;  // no row (FIND_ONLY miss, or no key): nothing to update
     if (w < K && idx < nlong) {
-      u = a.plan[a.pl.o_long_u + idx];
-      cb = a.plan[a.pl.o_long_base + idx];
-      nch = a.plan[a.pl.o_long_nch + idx];
+      u = a.long_u[idx];
+      cb = a.long_base[idx];
+      nch = a.long_nch[idx];
       r = a.urows[u];
     }
     if (wl == 0) {
@@ -1001,6 +1008,83 @@ void fwd_dispatch(const FwdArgs& a, int pool, hipStream_t s) {
   }
 }
 
+// The long keys' plan in feature order.  Chunks of one feature then run
+// together, and the waves in flight share that feature's rows of the
+// upstream gradient in the memory-side cache instead of each fetching its
+// own from HBM -- worth it when the gradient is larger than that cache.
+// Three launches over the long keys (bin = the key's slot, in kFeatBins
+// bins): k_long_hist counts keys and chunks per bin (block histograms in
+// LDS, one global add per bin and block); k_long_scan turns the bins into
+// bases (one block); k_long_place gives every key its place and first chunk
+// with one 64-bit add on its bin (place << 32 | chunks), so places and chunk
+// bases rise together, and writes its chunks' owner.
+constexpr int kFeatBins = 4096;
+__global__ void k_zero_u64(unsigned long long* p, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+__device__ __forceinline__ int feat_bin(const BwdArgs& a, int u) {
+  return (int)(((unsigned long long)a.ukeys[u] >> 48) & (kFeatBins - 1));
+}
+
+__global__ __launch_bounds__(256) void k_long_hist(BwdArgs a, unsigned long long* bins) {
+  __shared__ unsigned long long s_b[kFeatBins];
+  const int nlong = a.plan[0];
+  if ((long long)blockIdx.x * 256 >= nlong) return;
+  for (int i = threadIdx.x; i < kFeatBins; i += 256) s_b[i] = 0;
+  __syncthreads();
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx < nlong) {
+    const int u = a.plan[a.pl.o_long_u + idx], nch = a.plan[a.pl.o_long_nch + idx];
+    atomicAdd(&s_b[feat_bin(a, u)], (1ull << 32) | (unsigned)nch);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kFeatBins; i += 256)
+    if (s_b[i]) atomicAdd(&bins[i], s_b[i]);
+}
+
+// In place: bins[i] becomes the exclusive prefix of (keys << 32 | chunks).
+__global__ __launch_bounds__(1024) void k_long_scan(unsigned long long* bins) {
+  constexpr int kPer = kFeatBins / 1024;
+  __shared__ unsigned long long s_w[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  unsigned long long v[kPer], run = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    v[k] = bins[tid * kPer + k];
+    run += v[k];
+  }
+  unsigned long long inc = run;  // inclusive over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const unsigned long long y = (unsigned long long)__shfl_up((long long)inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  unsigned long long base = inc - run;
+  for (int x = 0; x < w; ++x) base += s_w[x];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    bins[tid * kPer + k] = base;
+    base += v[k];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_long_place(BwdArgs a, unsigned long long* bins, int* out_u, int* out_base,
+                                                    int* out_nch, int* out_owner) {
+  const int nlong = a.plan[0];
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nlong) return;
+  const int u = a.plan[a.pl.o_long_u + idx], nch = a.plan[a.pl.o_long_nch + idx];
+  const unsigned long long at = atomicAdd(&bins[feat_bin(a, u)], (1ull << 32) | (unsigned)nch);
+  const int pos = (int)(at >> 32), cb = (int)(at & 0xFFFFFFFFull);
+  out_u[pos] = u;
+  out_nch[pos] = nch;
+  out_base[pos] = cb;
+  for (int k = 0; k < nch; ++k) out_owner[cb + k] = pos;
+}
+
 template <int D, typename TP, int OPT>
 void bwd_dispatch(BwdArgs a, long long n, hipStream_t s) {
   constexpr int NCH = D / Vec<TP>::E;
@@ -1066,7 +1150,8 @@ void launch_forward(const recis_lookup_result& res, const TableDev& t, int pool,
 
 recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, int pool,
                              const void* grad, int grad_dtype, const OptConsts& oc,
-                             double* partials, bool current, hipStream_t s) {
+                             double* partials, int* reorder, long long reorder_ints, bool current,
+                             hipStream_t s) {
   if (res.n == 0) return RECIS_OK;
   BwdArgs a;
   a.current = current ? 1 : 0;
@@ -1088,6 +1173,33 @@ recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, 
   a.oc = oc;
   a.t = t;
   a.partials = partials;
+  a.long_u = res.plan + a.pl.o_long_u;
+  a.long_base = res.plan + a.pl.o_long_base;
+  a.long_nch = res.plan + a.pl.o_long_nch;
+  a.owner = res.plan + a.pl.o_chunk_owner;
+  // pooled gradients larger than the memory-side cache: the long keys'
+  // chunks go feature by feature (see k_long_place)
+  const double grad_bytes = (double)res.num_feats * res.batch * t.dim * (grad_dtype == RECIS_DTYPE_BF16 ? 2 : 4);
+  if (pool != RECIS_POOL_NONE && grad_bytes > kMemCacheBytes && reorder_ints > 0) {
+    const long long maxl = res.n / (kShortMax + 1) + 1, maxc = res.n / kChunk + maxl + 1;
+    const long long bins_at = (3 * maxl + maxc + 1) & ~1ll;  // 8-byte aligned (the scratch is)
+    if (bins_at + 2 * (long long)kFeatBins <= reorder_ints) {
+      int* ou = reorder;
+      int* ob = ou + maxl;
+      int* on = ob + maxl;
+      int* oo = on + maxl;
+      unsigned long long* bins = reinterpret_cast<unsigned long long*>(reorder + bins_at);
+      const unsigned kb = (unsigned)((maxl + 255) / 256);
+      RECIS_LAUNCH("k_long_zero", k_zero_u64, dim3(kFeatBins / 256), dim3(256), s, bins, (long long)kFeatBins);
+      RECIS_LAUNCH("k_long_hist", k_long_hist, dim3(kb), dim3(256), s, a, bins);
+      RECIS_LAUNCH("k_long_scan", k_long_scan, dim3(1), dim3(1024), s, bins);
+      RECIS_LAUNCH("k_long_place", k_long_place, dim3(kb), dim3(256), s, a, bins, ou, ob, on, oo);
+      a.long_u = ou;
+      a.long_base = ob;
+      a.long_nch = on;
+      a.owner = oo;
+    }
+  }
   if (t.dtype == RECIS_DTYPE_BF16) {
     if (t.optim == RECIS_OPTIM_ADAGRAD) bwd_dim<bf16_t, RECIS_OPTIM_ADAGRAD>(a, t.dim, res.n, s);
     else bwd_dim<bf16_t, RECIS_OPTIM_ADAM>(a, t.dim, res.n, s);

@@ -433,9 +433,13 @@ void launch_forward(const recis_lookup_result& res, const TableDev& t, int pool,
 struct OptConsts {
   float lr, b1, omb1, b2, omb2, eps, step_size;  // omb = 1 - beta, formed in double
 };
+// reorder: device scratch of reorder_ints ints for the long keys' plan in
+// feature order (used when the pooled gradient exceeds kMemCacheBytes).
+constexpr double kMemCacheBytes = 256.0 * 1024 * 1024;  // the memory-side (Infinity) cache
 recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, int pool,
                              const void* grad, int grad_dtype, const OptConsts& oc,
-                             double* partials, bool current, hipStream_t s);
+                             double* partials, int* reorder, long long reorder_ints, bool current,
+                             hipStream_t s);
 
 void launch_evict(const TableDev& t, unsigned min_count, double decay, long long* num_evicted, hipStream_t s);
 // LRU-bounded pass: keeps the youngest ages whole within max_keys; `work`

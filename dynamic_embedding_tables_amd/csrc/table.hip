@@ -673,7 +673,9 @@ recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* re
   }
   const bool current = res->epoch == t->update_epoch;
   t->update_epoch += 1;
-  recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, t->partials, current, s);
+  // the writeback scratch (2 ints per occurrence) is free during a backward
+  recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, t->partials,
+                                    reinterpret_cast<int*>(t->wb_keys), 2 * t->scr_cap, current, s);
   if (st != RECIS_OK) return st;
   return check_launch();
 }

@@ -425,6 +425,29 @@ def test_many_long_keys(per_key):
     run_parity(spec, [a, b])
 
 
+def test_long_keys_by_feature_large_gradient():
+    """A pooled gradient larger than the memory-side cache (4 features x 270k
+    bags x 64 fp32 = 276 MB), so the long keys' chunks are reordered feature
+    by feature; every feature has hot keys and a cold tail; two steps."""
+    spec = W.TableSpec(dim=64, dtype="f32", optim="adam", pool="mean", lr=1e-3, eps=1e-8)
+    B, F = 270_000, 4
+    batches = []
+    for step in range(2):
+        rng = W.rng_for(97, step)
+        feats = []
+        for f in range(F):
+            lens = rng.integers(1, 4, B)
+            off = W.offsets_from_lengths(lens)
+            n = int(off[-1])
+            hot = rng.integers(0, 300, n)                 # 300 hot keys: ~1.8k occurrences each
+            cold = rng.integers(1000, 2_000_000, n)
+            vals = np.where(rng.random(n) < 0.5, hot, cold).astype(np.int64)
+            feats.append(W.FeatureInput(values=vals, bag_offsets=off, slot=f + 1))
+        batches.append(W.Batch(feats, B, rng.standard_normal((B, F * 64), dtype=np.float32)))
+    assert B * F * 64 * 4 > 256 * 2**20
+    run_parity(spec, batches, export_every=2)
+
+
 @pytest.mark.parametrize("pool,admit", [("mean", 1), ("sum", 2)])
 def test_heavy_buckets(pool, admit):
     """Hot keys whose buckets exceed the single-block size (tens of thousands
