@@ -81,6 +81,8 @@ def lib():
         L.orc_evict_decay.argtypes = [p, C.c_uint32, C.c_double]
         L.orc_evict_lru.restype = C.c_int64
         L.orc_evict_lru.argtypes = [p, C.c_int64]
+        L.orc_set_sketch.restype = C.c_int
+        L.orc_set_sketch.argtypes = [p, C.c_int]
         L.orc_writeback.restype = C.c_int
         L.orc_writeback.argtypes = [p, p, C.c_int64, p]
         L.orc_size.restype = C.c_int64
@@ -245,6 +247,10 @@ class OracleTable:
         if decay == 0.0:
             return int(lib().orc_evict(self.h, min_count))
         return int(lib().orc_evict_decay(self.h, min_count, decay))
+
+    def set_sketch(self, bits: int) -> None:
+        """Count-min sketch admission with 4 x 2**bits counters (0: off)."""
+        assert lib().orc_set_sketch(self.h, bits) == 0
 
     def evict_lru(self, max_keys: int) -> int:
         return int(lib().orc_evict_lru(self.h, max_keys))

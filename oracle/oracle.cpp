@@ -194,7 +194,21 @@ struct Table {
   int64_t next_row = 0;
   int64_t adam_step = 0;
   uint32_t step = 0;                // counting lookups so far (insert_find without FIND_ONLY)
+  // count-min sketch admission (sketch_bits > 0): kSketchRows rows of
+  // 2^sketch_bits counters for the keys not yet in the map
+  int sketch_bits = 0;
+  std::vector<uint32_t> sketch;
 };
+
+// The sketch's counter of `key` in row r: the top sketch_bits bits of
+// MurmurHash3's finalizer of the key xor a per-row salt (odd multiples of
+// the 64-bit golden ratio).  Counters are 32-bit and wrap.
+constexpr int kSketchRows = 4;
+size_t sketch_index(const Table& t, int64_t key, int r) {
+  const uint64_t salt = 0x9E3779B97F4A7C15ull * uint64_t(2 * r + 1);
+  const uint64_t h = murmur3_fmix64(uint64_t(key) ^ salt);
+  return size_t(r) * (size_t(1) << t.sketch_bits) + size_t(h >> (64 - t.sketch_bits));
+}
 
 float store_param(const Table& t, double v) {
   return t.dtype == DT_BF16 ? round_to_bf16(v) : static_cast<float>(v);
@@ -272,6 +286,18 @@ void* orc_create(int dim, int dtype, int optim, uint64_t seed, float bound, int6
 
 void orc_destroy(void* h) { delete static_cast<Table*>(h); }
 
+// Count-min sketch admission ([README] Embedding Engine: admission
+// strategies).  Reading: with bits > 0, a key not in the map is counted in a
+// sketch of kSketchRows x 2^bits counters and enters the map only when its
+// estimate reaches admit_threshold; eviction passes clear the sketch.
+int orc_set_sketch(void* h, int bits) {
+  Table& t = *static_cast<Table*>(h);
+  if (bits < 0 || bits > 30) return ST_INVALID;
+  t.sketch_bits = bits;
+  t.sketch.assign(bits > 0 ? size_t(kSketchRows) << bits : 0, 0u);
+  return ST_OK;
+}
+
 // One lookup of a batch of `nfeat` features with `batch` samples each.
 //   values        int64 [N]  the features' values, feature after feature
 //   feat_n        int64 [nfeat]
@@ -342,6 +368,14 @@ int orc_insert_find(void* h, int32_t nfeat, int32_t batch, const int64_t* values
   int status = ST_OK;
   const bool find_only = (flags & FLAG_FIND_ONLY) != 0;
   if (!find_only) ++t.step;
+  // count-min sketch admission, phase 1: every key of this call that is not
+  // in the map adds its occurrences to its counters (all of them before any
+  // estimate is read, so the order of the keys does not matter)
+  const bool sketching = !find_only && t.sketch_bits > 0;
+  if (sketching)
+    for (int64_t u = 0; u < u_count; ++u)
+      if (t.idmap.find(uniq[u]) == t.idmap.end())
+        for (int r = 0; r < kSketchRows; ++r) t.sketch[sketch_index(t, uniq[u], r)] += uint32_t(counts[u]);
   for (int64_t u = 0; u < u_count; ++u) {
     const int64_t key = uniq[u];
     auto it = t.idmap.find(key);
@@ -349,7 +383,20 @@ int orc_insert_find(void* h, int32_t nfeat, int32_t batch, const int64_t* values
       unique_rows[u] = (it == t.idmap.end()) ? -1 : it->second.row;
       continue;
     }
+    uint64_t add = uint64_t(counts[u]);
     if (it == t.idmap.end()) {
+      if (sketching) {
+        // phase 2: the key enters the map (with its estimate as its count)
+        // only once the estimate -- the smallest of its counters -- reaches
+        // the admission threshold; until then it has no slot and no row
+        uint32_t est = 0xFFFFFFFFu;
+        for (int r = 0; r < kSketchRows; ++r) est = std::min(est, t.sketch[sketch_index(t, key, r)]);
+        if (est < t.admit) {
+          unique_rows[u] = -1;
+          continue;
+        }
+        add = est;
+      }
       if (int64_t(t.idmap.size()) >= t.max_keys) {
         status = ST_CAPACITY;
         unique_rows[u] = -1;
@@ -359,7 +406,7 @@ int orc_insert_find(void* h, int32_t nfeat, int32_t batch, const int64_t* values
     }
     Entry& e = it->second;
     e.last_use = t.step;
-    uint64_t c = uint64_t(e.count) + uint64_t(counts[u]);
+    uint64_t c = uint64_t(e.count) + add;
     e.count = c > 0xFFFFFFFFull ? 0xFFFFFFFFu : uint32_t(c);
     if (e.row < 0 && e.count >= t.admit) {
       e.row = allocate_row(t, key);
@@ -543,6 +590,7 @@ int orc_backward_update(void* h, const int64_t* unique_rows, const int32_t* inve
 // Returns the number of keys removed.
 int64_t orc_evict_decay(void* h, uint32_t min_count, double decay) {
   Table& t = *static_cast<Table*>(h);
+  std::fill(t.sketch.begin(), t.sketch.end(), 0u);  // the sketch's window restarts with every pass
   std::vector<int64_t> gone;
   for (auto& kv : t.idmap) {
     if (kv.second.count < min_count) gone.push_back(kv.first);
@@ -567,6 +615,7 @@ int64_t orc_evict(void* h, uint32_t min_count) { return orc_evict_decay(h, min_c
 // (releasing its row); counts are untouched.  Returns the number removed.
 int64_t orc_evict_lru(void* h, int64_t max_keys) {
   Table& t = *static_cast<Table*>(h);
+  std::fill(t.sketch.begin(), t.sketch.end(), 0u);
   std::vector<int64_t> hist(256, 0);
   auto age = [&](const Entry& e) { return std::min<uint32_t>(t.step - e.last_use, 255u); };
   for (auto& kv : t.idmap) hist[age(kv.second)] += 1;

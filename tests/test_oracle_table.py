@@ -440,6 +440,112 @@ def test_evict_lru_keeps_exactly_the_latest_lookup():
     np.testing.assert_array_equal(tab.export()["keys"], last)
 
 
+def _fmix64(x):
+    """MurmurHash3's 64-bit finalizer, restated in Python."""
+    m = (1 << 64) - 1
+    x ^= x >> 33
+    x = (x * 0xFF51AFD7ED558CCD) & m
+    x ^= x >> 33
+    x = (x * 0xC4CEB9FE1A85EC53) & m
+    x ^= x >> 33
+    return x
+
+
+class SketchDict:
+    """Brute force of count-min sketch admission: a dict of admitted keys
+    (key -> [has_row, count]) and a list-of-lists sketch for the rest."""
+
+    def __init__(self, admit, bits):
+        self.m, self.admit, self.bits = {}, admit, bits
+        self.sk = [[0] * (1 << bits) for _ in range(4)]
+
+    def idx(self, key, r):
+        salt = (0x9E3779B97F4A7C15 * (2 * r + 1)) & ((1 << 64) - 1)
+        return _fmix64((int(key) & ((1 << 64) - 1)) ^ salt) >> (64 - self.bits)
+
+    def step(self, keys):
+        u, c = np.unique(keys, return_counts=True)
+        for k, n in zip(u, c):       # all adds first
+            if k not in self.m:
+                for r in range(4):
+                    i = self.idx(k, r)
+                    self.sk[r][i] = (self.sk[r][i] + int(n)) & 0xFFFFFFFF
+        out = {}
+        for k, n in zip(u, c):
+            if k in self.m:
+                e = self.m[k]
+                e[1] += int(n)
+            else:
+                est = min(self.sk[r][self.idx(k, r)] for r in range(4))
+                if est < self.admit:
+                    out[k] = False
+                    continue
+                e = self.m[k] = [False, est]
+            if not e[0] and e[1] >= self.admit:
+                e[0] = True
+            out[k] = e[0]
+        return out
+
+    def evict(self, t):
+        gone = [k for k, e in self.m.items() if e[1] < t]
+        for k in gone:
+            del self.m[k]
+        for e in self.m.values():
+            e[1] = 0
+        self.sk = [[0] * (1 << self.bits) for _ in range(4)]
+        return len(gone)
+
+
+@pytest.mark.parametrize("bits", [1, 4, 12])
+def test_sketch_admission_against_brute_force(bits):
+    """Count-min sketch admission at 3, with an eviction pass every fourth
+    step: per-step admissions, the admitted keys and their counts."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum", admit_threshold=3)
+    tab, ref = oracle.OracleTable(spec), SketchDict(3, bits)
+    tab.set_sketch(bits)
+    for step in range(12):
+        feats = small_features(700 + step, nfeat=2, batch=9, id_space=60)
+        r = tab.insert_find(feats, 9)
+        assert r.status == 0
+        want = ref.step(keys_of(feats))
+        got = {int(k): int(row) >= 0 for k, row in zip(r.unique_keys[:r.U], r.unique_rows[:r.U])}
+        assert got == {int(k): v for k, v in want.items()}
+        if step % 4 == 3:
+            assert tab.evict(2) == ref.evict(2)
+        ex = tab.export()
+        assert [int(k) for k in ex["keys"]] == sorted(int(k) for k in ref.m)
+        assert [int(c) for c in ex["counts"]] == [ref.m[k][1] for k in sorted(ref.m)]
+
+
+def test_sketch_without_collisions_admits_as_the_exact_counts():
+    """With a sketch far larger than the keys (no shared counters), a key is
+    admitted in the same step as with exact counts, with the same count; the
+    keys still waiting simply stay out of the map."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum", admit_threshold=3)
+    exact, sk = oracle.OracleTable(spec), oracle.OracleTable(spec)
+    sk.set_sketch(20)
+    for step in range(10):
+        feats = small_features(800 + step, nfeat=2, batch=9, id_space=60)
+        a, b = exact.insert_find(feats, 9), sk.insert_find(feats, 9)
+        np.testing.assert_array_equal(a.unique_rows[:a.U] >= 0, b.unique_rows[:b.U] >= 0)
+        ea, eb = exact.export(), sk.export()
+        has = ea["rows"] >= 0
+        np.testing.assert_array_equal(eb["keys"], ea["keys"][has])
+        np.testing.assert_array_equal(eb["counts"], ea["counts"][has])
+
+
+def test_sketch_never_admits_later_than_exact_counts():
+    """A count-min estimate never falls below the true count: with a tiny
+    sketch (many collisions) every key the exact counts admit is admitted."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum", admit_threshold=4)
+    exact, sk = oracle.OracleTable(spec), oracle.OracleTable(spec)
+    sk.set_sketch(2)
+    for step in range(10):
+        feats = small_features(900 + step, nfeat=2, batch=9, id_space=80)
+        a, b = exact.insert_find(feats, 9), sk.insert_find(feats, 9)
+        assert np.all((a.unique_rows[:a.U] >= 0) <= (b.unique_rows[:b.U] >= 0))
+
+
 def test_evict_decay_one_keeps_running_totals():
     """decay = 1 and no key evicted: every count is the key's total number of
     occurrences since it was first seen (np.unique over all inputs)."""
