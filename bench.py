@@ -487,6 +487,9 @@ def main():
                          "first an LRU-bounded pass to half the keys)")
     ap.add_argument("--track-last-use", action="store_true",
                     help="the table stamps every key a lookup counts (for LRU-bounded eviction)")
+    ap.add_argument("--admit-sketch-bits", type=int, default=0,
+                    help="count-min sketch admission with 4 x 2^bits counters (the workload's admission "
+                         "threshold; timing only: the default line keeps exact admission)")
     ap.add_argument("--block-memory", choices=["device", "host"], default="device",
                     help="where the EmbeddingBlocks live: HBM, or pinned host memory across the host link")
     ap.add_argument("--workers", type=int, default=8)
@@ -549,7 +552,8 @@ def main():
         reserve = (fill_steps + Wm + K + 2) * wl["new_per_step"]
     table = recis.Table(D, spec.dtype, spec.optim, seed=spec.seed, init_bound=spec.init_bound,
                         admit_threshold=spec.admit_threshold, reserve_rows=reserve,
-                        block_memory=args.block_memory, track_last_use=args.track_last_use, **wl["table"])
+                        block_memory=args.block_memory, track_last_use=args.track_last_use,
+                        admit_sketch_bits=args.admit_sketch_bits, **wl["table"])
     gen = torch.Generator(device=dev)
     gen.manual_seed(20250925)
     pdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -736,6 +740,8 @@ def main():
         result["export_import"] = export_import(torch, recis, table, spec, wl, D, s_bytes, S, args.block_memory)
     if args.track_last_use:
         result["config"]["track_last_use"] = True
+    if args.admit_sketch_bits:
+        result["config"]["admit_sketch_bits"] = args.admit_sketch_bits
     if args.evict_pass:
         if args.track_last_use:
             result["evict_lru_pass"] = evict_lru_pass(torch, table)

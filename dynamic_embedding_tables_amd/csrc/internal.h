@@ -258,7 +258,32 @@ struct TableDev {
   unsigned* last_use;                  // per IDMap slot: the counting lookup that last saw its key
                                        // (nullptr when the table does not track it)
   unsigned step;                       // counting lookups so far
+  unsigned* sketch;                    // count-min admission: kSketchRows x 2^sketch_bits (or nullptr)
+  int sketch_bits;
 };
+
+// Count-min sketch admission: counter of `key` in row r = the top
+// sketch_bits bits of fmix64(key ^ salt_r), salt_r an odd multiple of the
+// 64-bit golden ratio.
+constexpr int kSketchRows = 4;
+__device__ __forceinline__ unsigned long long sketch_at(const TableDev& t, long long key, int r) {
+  const unsigned long long salt = 0x9E3779B97F4A7C15ull * (unsigned long long)(2 * r + 1);
+  return ((unsigned long long)r << t.sketch_bits) +
+         (fmix64((unsigned long long)key ^ salt) >> (64 - t.sketch_bits));
+}
+__device__ __forceinline__ void sketch_add(const TableDev& t, long long key, unsigned c) {
+#pragma unroll
+  for (int r = 0; r < kSketchRows; ++r) atomicAdd(&t.sketch[sketch_at(t, key, r)], c);
+}
+__device__ __forceinline__ unsigned sketch_estimate(const TableDev& t, long long key) {
+  unsigned v[kSketchRows];
+#pragma unroll
+  for (int r = 0; r < kSketchRows; ++r) v[r] = t.sketch[sketch_at(t, key, r)];
+  unsigned e = v[0];
+#pragma unroll
+  for (int r = 1; r < kSketchRows; ++r) e = v[r] < e ? v[r] : e;
+  return e;
+}
 
 __device__ __forceinline__ unsigned long long next_slot(const TableDev& t, unsigned long long p) {
   return (p & ~t.region_mask) | ((p + 1) & t.region_mask);
@@ -350,6 +375,7 @@ struct recis_table {
   unsigned long long* blk_sums = nullptr;
   unsigned* last_use = nullptr;  // [slot_cap] when cfg.track_last_use
   unsigned step = 0;             // counting lookups so far
+  unsigned* sketch = nullptr;    // [kSketchRows << cfg.admit_sketch_bits] when sketch admission is on
   long long* wb_keys = nullptr;
   double* partials = nullptr;
 
@@ -368,6 +394,7 @@ namespace recis {
 
 // Launchers (defined in the .hip files; all enqueue on `s`).
 void launch_fill_slots(Slot* slots, long long cap, hipStream_t s);
+void launch_zero_u32(unsigned* p, long long n, hipStream_t s);
 void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s);
 void launch_rehash(const Slot* old_slots, const unsigned* old_last_use, long long old_cap, const TableDev& t,
                    hipStream_t s);
@@ -422,6 +449,7 @@ struct LookupLaunch {
   long long hmax;                // bound on the heavy slices of the call (their grids)
   unsigned* last_use;            // stamped with `step` for every key the call counts (or nullptr)
   unsigned step;
+  int sketching;                 // count-min admission in this (counting) call
 };
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);
 

@@ -449,9 +449,15 @@ struct ProbeOut {
 // caller's block owns the key's region, so the slot stores need no atomics.
 template <typename Claim>
 __device__ __forceinline__ ProbeOut idmap_probe(const TableDev& t, long long key, int c, bool find_only,
-                                                Claim claim) {
+                                                Claim claim, bool sketching = false) {
   ProbeOut o;
   if (key < 0) return o;  // a failed transform
+  // count-min admission: an absent key enters only once its estimate (all of
+  // this call's counts are in the sketch already) reaches the threshold, and
+  // then with the estimate as its count
+  unsigned est = 0;
+  if (sketching) est = sketch_estimate(t, key);
+  const bool admit_absent = !sketching || est >= t.admit;
   unsigned long long p = slot_of(key, t.slot_shift);
   bool found = false, inserted = false, stop = false;
   Slot sv;
@@ -479,7 +485,7 @@ __device__ __forceinline__ ProbeOut idmap_probe(const TableDev& t, long long key
         p = q[k];
         sv = v[k];
       } else if (v[k].key == kEmptyKey) {
-        if (find_only) {
+        if (find_only || !admit_absent) {
           stop = true;
         } else if (claim(q[k])) {
           inserted = stop = true;
@@ -490,15 +496,15 @@ __device__ __forceinline__ ProbeOut idmap_probe(const TableDev& t, long long key
     p = stop ? p : next_slot(t, q[kProbeBatch - 1]);
   }
   if (!found && !inserted) {
-    if (!find_only) o.err = kErrCapacity;  // the key's region is full
-    return o;
+    if (!find_only && admit_absent) o.err = kErrCapacity;  // the key's region is full
+    return o;  // (or a key the sketch does not admit yet: no slot, no row)
   }
   o.sl = (unsigned)p;
   if (find_only) {
     o.row = sv.row;
   } else {
     const unsigned c0 = inserted ? 0u : sv.count;
-    const unsigned long long cs = (unsigned long long)c0 + (unsigned)c;
+    const unsigned long long cs = (unsigned long long)c0 + (inserted && sketching ? est : (unsigned)c);
     const unsigned cnt = cs > 0xFFFFFFFFull ? 0xFFFFFFFFu : (unsigned)cs;
     if (inserted) {
       Slot ns;
@@ -518,6 +524,14 @@ __device__ __forceinline__ ProbeOut idmap_probe(const TableDev& t, long long key
   // the initializer's)
   if (o.row >= 0 && (o.row & kPendingRow)) o.row = (o.row & ~(long long)kPendingRow) | kFreshRow;
   return o;
+}
+
+// Count-min admission, phase 1 (the count launch): a distinct key of the
+// call that is not in the IDMap adds its c occurrences to its counters.
+__device__ __forceinline__ void sketch_count(const TableDev& t, long long key, int c) {
+  if (key < 0 || c <= 0) return;
+  const ProbeOut o = idmap_probe(t, key, 0, true, [](unsigned long long) { return false; });
+  if (o.sl == 0xFFFFFFFFu) sketch_add(t, key, (unsigned)c);
 }
 
 // The forward's reference for the occurrences of a key (see kOccNoRow).
@@ -611,8 +625,12 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
       atomicAdd(&R[h].count, 1);
     }
     __syncthreads();
-    for (unsigned long long h = tid; h < cap; h += kThreads)
-      if (ld_key(&R[h]) != kEmptyKey) atomicAdd(&s_nd, 1);
+    for (unsigned long long h = tid; h < cap; h += kThreads) {
+      const long long key = ld_key(&R[h]);
+      if (key == kEmptyKey) continue;
+      atomicAdd(&s_nd, 1);
+      if (L.sketching) sketch_count(t, key, ld_int(&R[h].count));
+    }
     __syncthreads();
     if (tid == 0) L.ubase[b] = s_nd;
     return;
@@ -636,7 +654,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
       return atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
                        (unsigned long long)key) == (unsigned long long)kEmptyKey;
     };
-    const ProbeOut po = idmap_probe(t, key, c, find_only, claim);
+    const ProbeOut po = idmap_probe(t, key, c, find_only, claim, L.sketching != 0);
     err |= po.err;
     key_outputs(L, u, c, po, sum, sum_long);
   }
@@ -793,6 +811,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
         h = h + 1 == cap ? 0 : h + 1;
       }
       atomicAdd(&R[h].count, s_cnt[hl]);
+      if (L.sketching) sketch_count(t, key, s_cnt[hl]);
     }
     __syncthreads();  // the LDS table is reused by the next slice
     }
@@ -844,7 +863,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
         return atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
                          (unsigned long long)key) == (unsigned long long)kEmptyKey;
       };
-      const ProbeOut po = idmap_probe(t, key, c, find_only, claim);
+      const ProbeOut po = idmap_probe(t, key, c, find_only, claim, L.sketching != 0);
       err |= po.err;
       key_outputs(L, u, c, po, sum, sum_long);
     }
@@ -916,6 +935,8 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   }
   if (!EMIT) {
     if (tid == 0) L.ubase[b] = s_nd;
+    if (L.sketching)
+      for (int idx = tid; idx < s_nd; idx += kThreads) sketch_count(t, s_key[s_list[idx]], s_cnt[s_list[idx]]);
     return;
   }
   const int nd = s_nd;
@@ -949,7 +970,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     L.res.unique_offsets[u] = s + o;
     s_u[h] = (int)u;
     s_cnt[h] = o;  // from here on: the next free position of the key's group
-    const ProbeOut po = idmap_probe(t, key, c, find_only, claim);
+    const ProbeOut po = idmap_probe(t, key, c, find_only, claim, L.sketching != 0);
     err |= po.err;
     key_outputs(L, u, c, po, sum, sum_long);
     s_ref[h] = occ_ref(t, po, key);

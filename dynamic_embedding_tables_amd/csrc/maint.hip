@@ -513,6 +513,15 @@ void launch_fill_slots(Slot* slots, long long cap, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_slots, dim3(grid_for(cap, 256)), dim3(256), 0, s, slots, cap);
 }
 
+__global__ void k_zero_u32(unsigned* p, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+void launch_zero_u32(unsigned* p, long long n, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_u32, dim3(grid_for(n, 256)), dim3(256), 0, s, p, n);
+}
+
 void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_dedup, dim3(grid_for(cap, 256)), dim3(256), 0, s, dd, cap);
 }

@@ -370,6 +370,8 @@ TableDev recis_table::dev() const {
   d.rows_limit = rows_alloc;
   d.last_use = last_use;
   d.step = step;
+  d.sketch = sketch;
+  d.sketch_bits = cfg.admit_sketch_bits;
   return d;
 }
 
@@ -410,6 +412,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   if (cfg->reserve_rows < 0) return RECIS_ERR_INVALID_ARG;
   if (cfg->block_memory != RECIS_MEM_DEVICE && cfg->block_memory != RECIS_MEM_HOST) return RECIS_ERR_INVALID_ARG;
   if (cfg->track_last_use != 0 && cfg->track_last_use != 1) return RECIS_ERR_INVALID_ARG;
+  if (cfg->admit_sketch_bits < 0 || cfg->admit_sketch_bits > 30) return RECIS_ERR_INVALID_ARG;
   if (alloc && (!alloc->alloc || !alloc->free)) return RECIS_ERR_INVALID_ARG;
   if (!valid_dim(cfg->dim)) return RECIS_ERR_UNSUPPORTED;
 
@@ -438,6 +441,12 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   t->slot_cap = std::max<long long>(next_pow2(cfg->slot_capacity), 64);
   t->slots = static_cast<Slot*>(tab_alloc(t, (size_t)t->slot_cap * sizeof(Slot), s));
   if (!t->slots) return fail(RECIS_ERR_OUT_OF_MEMORY);
+  if (cfg->admit_sketch_bits > 0) {
+    const long long n = (long long)kSketchRows << cfg->admit_sketch_bits;
+    t->sketch = static_cast<unsigned*>(tab_alloc(t, (size_t)n * sizeof(unsigned), s));
+    if (!t->sketch) return fail(RECIS_ERR_OUT_OF_MEMORY);
+    launch_zero_u32(t->sketch, n, s);
+  }
   if (cfg->track_last_use) {  // stamped whenever a key enters; empty slots' stamps are never read
     t->last_use = static_cast<unsigned*>(tab_alloc(t, (size_t)t->slot_cap * sizeof(unsigned), s));
     if (!t->last_use) return fail(RECIS_ERR_OUT_OF_MEMORY);
@@ -462,6 +471,7 @@ recis_status recis_idmap_destroy(recis_table* t) {
   tab_free(t, t->free_list, (size_t)t->free_cap * 4, s);
   tab_free(t, t->slots, (size_t)t->slot_cap * sizeof(Slot), s);
   tab_free(t, t->last_use, (size_t)t->slot_cap * sizeof(unsigned), s);
+  tab_free(t, t->sketch, (size_t)((long long)kSketchRows << t->cfg.admit_sketch_bits) * sizeof(unsigned), s);
   tab_free(t, t->ctr, sizeof(DevCounters), s);
   free_scratch(t, s);
   for (int k = 0; k < recis_table::kRing; ++k) {
@@ -577,6 +587,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   if (counting) t->step += 1;
   L.last_use = counting ? t->last_use : nullptr;
   L.step = t->step;
+  L.sketching = counting && t->sketch ? 1 : 0;
   launch_lookup(L, t->dev(), s);
   return check_launch();
 }
@@ -587,6 +598,7 @@ recis_status recis_idmap_evict_decay(recis_table* t, uint32_t min_count, double 
   ScopedDevice sd(t->device);
   ScopedProbe sp(t);
   t->update_epoch += 1;
+  if (t->sketch) launch_zero_u32(t->sketch, (long long)kSketchRows << t->cfg.admit_sketch_bits, s);
   launch_evict(t->dev(), min_count, decay, reinterpret_cast<long long*>(num_evicted), s);
   recis_status st = check_launch();
   if (st != RECIS_OK) return st;
@@ -613,6 +625,7 @@ recis_status recis_idmap_evict_lru(recis_table* t, int64_t max_keys, int64_t* nu
   int* work = static_cast<int*>(tab_alloc(t, wbytes, s));
   if (!work) return RECIS_ERR_OUT_OF_MEMORY;
   t->update_epoch += 1;
+  if (t->sketch) launch_zero_u32(t->sketch, (long long)kSketchRows << t->cfg.admit_sketch_bits, s);
   launch_evict_lru(t->dev(), max_keys, work, reinterpret_cast<long long*>(num_evicted), s);
   recis_status st = check_launch();
   if (st == RECIS_OK) st = rebuild_idmap(t, t->slot_cap, s);  // synchronises: work is idle after

@@ -61,7 +61,7 @@ class recis_table_config(C.Structure):
                 ("admit_threshold", C.c_uint32), ("seed", C.c_uint64), ("init_bound", C.c_float),
                 ("max_load", C.c_float), ("slot_capacity", C.c_int64), ("block_rows", C.c_int64),
                 ("max_rows", C.c_int64), ("reserve_rows", C.c_int64), ("block_memory", C.c_int32),
-                ("track_last_use", C.c_int32)]
+                ("track_last_use", C.c_int32), ("admit_sketch_bits", C.c_int32)]
 
 
 class recis_allocator(C.Structure):
@@ -316,7 +316,7 @@ class Table:
                  init_bound: float = 0.05, admit_threshold: int = 1, slot_capacity: int = 1 << 20,
                  block_rows: int = 1 << 20, max_rows: int = (1 << 30) - 1, reserve_rows: int = 0,
                  max_load: float = 0.5, block_memory: str = "device", track_last_use: bool = False,
-                 stream=None):
+                 admit_sketch_bits: int = 0, stream=None):
         cfg = recis_table_config_default()
         cfg.dim, cfg.dtype, cfg.optim = dim, DTYPES[dtype], OPTIMS[optim]
         cfg.seed, cfg.init_bound, cfg.admit_threshold = seed, init_bound, admit_threshold
@@ -324,6 +324,7 @@ class Table:
         cfg.reserve_rows, cfg.max_load = reserve_rows, max_load
         cfg.block_memory = {"device": RECIS_MEM_DEVICE, "host": RECIS_MEM_HOST}[block_memory]
         cfg.track_last_use = 1 if track_last_use else 0
+        cfg.admit_sketch_bits = admit_sketch_bits
         self.dim, self.dtype, self.optim = dim, dtype, optim
         self.config = {"seed": seed, "init_bound": init_bound, "admit_threshold": admit_threshold,
                        "block_memory": block_memory}

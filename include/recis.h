@@ -111,11 +111,22 @@ typedef struct {
                                during a call, so the host must not touch them directly) */
   int32_t track_last_use;   /* 1: every counting insert_find stamps the keys it sees (4
                                bytes per IDMap slot), for recis_idmap_evict_lru; 0: off */
+  int32_t admit_sketch_bits; /* 0: admission on exact counts kept in the IDMap.  1..30:
+                               count-min sketch admission -- a key not in the IDMap is
+                               counted in 4 x 2^bits 32-bit counters (its counters gain
+                               its occurrences of every counting insert_find, all before
+                               any estimate is read) and enters the IDMap, with its
+                               estimate (the least of its counters) as its count and a
+                               row, once that estimate reaches admit_threshold; until
+                               then it takes no slot.  Eviction passes clear the sketch.
+                               (Page "RecIS (Recommendation Intelligence System)" README,
+                               section "Core architecture > Embedding Engine": admission
+                               strategies.) */
 } recis_table_config;
 
 /* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
  * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0,
- * blocks in device memory, no last-use stamps). */
+ * blocks in device memory, no last-use stamps, exact admission). */
 void recis_table_config_default(recis_table_config* cfg);
 
 /* Device-memory provider.  alloc returns `bytes` of device memory (256-byte

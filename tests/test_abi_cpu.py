@@ -92,7 +92,8 @@ def test_invalid_arguments_return_synchronously(lib):
     assert L.recis_idmap_create(C.byref(c), None, None, None) == lib.RECIS_ERR_INVALID_ARG
     for field, bad in [("dtype", 7), ("optim", 9), ("max_load", 0.0), ("max_load", 0.8),
                        ("slot_capacity", 0), ("block_rows", 0), ("max_rows", 0), ("max_rows", 2**30),
-                       ("reserve_rows", -1), ("init_bound", -1.0), ("block_memory", 2), ("track_last_use", 2)]:
+                       ("reserve_rows", -1), ("init_bound", -1.0), ("block_memory", 2), ("track_last_use", 2),
+                       ("admit_sketch_bits", -1), ("admit_sketch_bits", 31)]:
         c = lib.recis_table_config_default()
         setattr(c, field, bad)
         assert L.recis_idmap_create(C.byref(c), None, None, C.byref(h)) == lib.RECIS_ERR_INVALID_ARG, field

@@ -36,6 +36,8 @@ def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopu
     from dynamic_embedding_tables_amd import recis
     table = make_table(spec, **(table_kw or {}))
     otab = oracle.OracleTable(spec)
+    if (table_kw or {}).get("admit_sketch_bits"):
+        otab.set_sketch(table_kw["admit_sketch_bits"])
     passes = []  # LRU passes: (keys before, keys evicted)
     if prepopulate is not None:
         cap = max(prepopulate.n, 1)
@@ -132,6 +134,34 @@ def test_eviction_lru_after_growth():
     spec = W.spec_ctr()
     run_parity(spec, [W.ctr_batch(s, batch=64, num_feats=8) for s in range(6)],
                table_kw=dict(slot_capacity=64, block_rows=64, track_last_use=True), evict_every=2, lru_max=2000)
+
+
+@pytest.mark.parametrize("bits", [6, 18])
+def test_count_min_sketch_admission(bits):
+    """Count-min sketch admission (admission at 2, keys outside the IDMap
+    counted in 4 x 2^bits counters) on the multi-table config with eviction
+    passes that clear the sketch, and a FIND_ONLY lookup; a 6-bit sketch
+    collides heavily, an 18-bit one hardly."""
+    spec = W.spec_multi(1)
+    batches = [W.multi_batch(s, 1, batch=128, num_feats=6) for s in range(8)]
+    run_parity(spec, batches, table_kw=dict(admit_sketch_bits=bits), evict_every=3, find_only_steps=(4,))
+
+
+def test_count_min_sketch_admission_hot_keys():
+    """Sketch admission at 3 through the heavy-bucket path (one key with 20k
+    occurrences per step, sliced across blocks) and a cold tail."""
+    spec = W.TableSpec(dim=32, dtype="f32", optim="adagrad", pool="sum", lr=0.01, eps=1e-10, admit_threshold=3)
+    batches = []
+    for step in range(3):
+        rng = W.rng_for(78, step)
+        B = 2000
+        lens = rng.poisson(12, B)
+        off = W.offsets_from_lengths(lens)
+        n = int(off[-1])
+        vals = np.where(rng.random(n) < 0.8, 123456789, rng.integers(0, 4000, n))
+        batches.append(W.Batch([W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=1)], B,
+                               rng.standard_normal((B, 32), dtype=np.float32)))
+    run_parity(spec, batches, table_kw=dict(admit_sketch_bits=10))
 
 
 # ---- full sizes: the bench's workload and table configuration, and the
