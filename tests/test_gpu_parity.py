@@ -164,6 +164,45 @@ def test_count_min_sketch_admission_hot_keys():
     run_parity(spec, batches, table_kw=dict(admit_sketch_bits=10))
 
 
+def test_all_table_options_together():
+    """Host-memory blocks, last-use stamps and sketch admission on one table,
+    with a decayed-count pass and an LRU pass between lookups (one of them
+    FIND_ONLY), a writeback of some keys, and the bf16 storage of Adam rows."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.TableSpec(dim=32, dtype="bf16", optim="adam", pool="mean", lr=1e-3, eps=1e-8, admit_threshold=2)
+    table = make_table(spec, block_memory="host", track_last_use=True, admit_sketch_bits=9, block_rows=512)
+    otab = oracle.OracleTable(spec)
+    otab.set_sketch(9)
+    ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for step in range(8):
+        b = W.multi_batch(step, 2, batch=96, num_feats=5)
+        b.grad = W.rng_for(79, step).standard_normal((b.batch, b.num_feats * 32), dtype=np.float32)
+        fo = step == 5
+        res = recis.LookupResult(max(b.n, 1), b.num_feats * b.batch)
+        out, _ = gpu_step(table, spec, b, res, find_only=fo, with_backward=not fo)
+        r, oout, oab = oracle_step(otab, spec, b, find_only=fo, with_backward=not fo)
+        torch.cuda.synchronize()
+        assert table.get_error() == 0
+        check_lookup(canon_lookup(res), r)
+        check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats, exact=step == 0)
+        if step == 2:
+            table.evict(2, ne, decay=0.5)
+            assert int(ne.item()) == otab.evict(2, 0.5)
+        if step == 4:
+            table.evict_lru(600, ne)
+            assert int(ne.item()) == otab.evict_lru(600)
+        if step == 6:
+            keys = np.unique(np.concatenate([(np.int64(f.slot) << np.int64(48)) | f.values for f in b.features]))[:50]
+            rows = W.rng_for(80).standard_normal((keys.size, 32), dtype=np.float32)
+            table.writeback(torch.from_numpy(keys).cuda(), torch.from_numpy(rows).cuda())
+            assert otab.writeback(keys, rows) == 0
+        check_export(canon_export(table), otab.export(), spec)
+    st = table.stats()
+    assert st.keys == otab.size() and st.rows_in_use == otab.rows_in_use()
+    table.close()
+
+
 # ---- full sizes: the bench's workload and table configuration, and the
 # largest per-table shape of the multi-table config (which takes the lookup's
 # large-bucket path)
