@@ -395,6 +395,7 @@ namespace recis {
 // Launchers (defined in the .hip files; all enqueue on `s`).
 void launch_fill_slots(Slot* slots, long long cap, hipStream_t s);
 void launch_zero_u32(unsigned* p, long long n, hipStream_t s);
+void launch_key_ages(const TableDev& t, const long long* keys, long long n, unsigned* ages, bool set, hipStream_t s);
 void launch_fill_dedup(DedupSlot* dd, long long cap, hipStream_t s);
 void launch_rehash(const Slot* old_slots, const unsigned* old_last_use, long long old_cap, const TableDev& t,
                    hipStream_t s);

@@ -513,9 +513,41 @@ void launch_fill_slots(Slot* slots, long long cap, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_slots, dim3(grid_for(cap, 256)), dim3(256), 0, s, slots, cap);
 }
 
+// Ages of given keys for a save (set: stamps from saved ages for a restore).
+// An age counts the counting lookups since one last counted the key; absent
+// keys report ~0u (and are skipped when setting).
+__global__ void k_key_ages(TableDev t, const long long* keys, long long n, unsigned* ages, int set) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    const long long key = keys[i];
+    long long at = -1;
+    if (key >= 0) {
+      unsigned long long p = slot_of(key, t.slot_shift);
+      for (unsigned long long q = 0; q <= t.region_mask; ++q) {
+        const long long cur = t.slots[p].key;
+        if (cur == key) {
+          at = (long long)p;
+          break;
+        }
+        if (cur == kEmptyKey) break;
+        p = next_slot(t, p);
+      }
+    }
+    if (set) {
+      if (at >= 0) t.last_use[at] = t.step - ages[i];
+    } else {
+      ages[i] = at >= 0 ? t.step - t.last_use[at] : ~0u;
+    }
+  }
+}
+
 __global__ void k_zero_u32(unsigned* p, long long n) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
     p[i] = 0u;
+}
+
+void launch_key_ages(const TableDev& t, const long long* keys, long long n, unsigned* ages, bool set, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_key_ages, dim3(grid_for(n, 256)), dim3(256), 0, s, t, keys, n, ages, set ? 1 : 0);
 }
 
 void launch_zero_u32(unsigned* p, long long n, hipStream_t s) {

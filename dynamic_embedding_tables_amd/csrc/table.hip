@@ -732,6 +732,26 @@ recis_status recis_idmap_import(recis_table* t, int64_t n, const int64_t* keys, 
   return check_launch();
 }
 
+recis_status recis_idmap_key_ages(recis_table* t, const int64_t* keys, int64_t n, uint32_t* ages, int32_t set,
+                                  hipStream_t s) {
+  if (!t || n < 0 || (n > 0 && (!keys || !ages)) || (set != 0 && set != 1)) return RECIS_ERR_INVALID_ARG;
+  if (!t->last_use) return RECIS_ERR_UNSUPPORTED;
+  ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
+  launch_key_ages(t->dev(), reinterpret_cast<const long long*>(keys), n, ages, set != 0, s);
+  return check_launch();
+}
+
+recis_status recis_idmap_sketch(recis_table* t, uint32_t* counters, int32_t set, hipStream_t s) {
+  if (!t || !counters || (set != 0 && set != 1)) return RECIS_ERR_INVALID_ARG;
+  if (!t->sketch) return RECIS_ERR_UNSUPPORTED;
+  ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
+  const size_t bytes = ((size_t)kSketchRows << t->cfg.admit_sketch_bits) * sizeof(unsigned);
+  HIP_TRY(hipMemcpyAsync(set ? t->sketch : counters, set ? counters : t->sketch, bytes, hipMemcpyDeviceToDevice, s));
+  return RECIS_OK;
+}
+
 recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int64_t* rows, uint32_t* counts,
                                 void* params, float* state, int64_t* n, hipStream_t s) {
   if (!t || !n || cap < 0) return RECIS_ERR_INVALID_ARG;

@@ -51,7 +51,8 @@ EXPORTED_SYMBOLS = (
     "recis_idmap_insert_find", "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru",
     "recis_lookup_pool_fwd",
     "recis_pool_bwd_update",
-    "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats", "recis_get_error",
+    "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_key_ages", "recis_idmap_sketch",
+    "recis_idmap_stats", "recis_get_error",
     "recis_status_string", "recis_profile_kernel",
 )
 
@@ -127,6 +128,8 @@ def load_library() -> C.CDLL:
     L.recis_writeback.argtypes = [p, p, i64, p, p]
     L.recis_idmap_export.argtypes = [p, i64, p, p, p, p, p, C.POINTER(i64), p]
     L.recis_idmap_import.argtypes = [p, i64, p, p, p, p, p, i64, p]
+    L.recis_idmap_key_ages.argtypes = [p, p, i64, p, i32, p]
+    L.recis_idmap_sketch.argtypes = [p, p, i32, p]
     L.recis_idmap_stats.argtypes = [p, C.POINTER(recis_table_stats), p]
     L.recis_get_error.argtypes = [p, p]
     L.recis_profile_kernel.argtypes = [p, C.c_char_p, p, p]
@@ -135,8 +138,8 @@ def load_library() -> C.CDLL:
     for name in ("recis_idmap_create", "recis_idmap_destroy", "recis_idmap_insert_find",
                  "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru", "recis_lookup_pool_fwd",
                  "recis_pool_bwd_update",
-                 "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_stats",
-                 "recis_get_error"):
+                 "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_key_ages",
+                 "recis_idmap_sketch", "recis_idmap_stats", "recis_get_error"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -240,6 +243,16 @@ def recis_idmap_import(h, n: int, keys, rows, counts, params, state, adam_step: 
                                              _ptr(state), adam_step, _stream(stream)), "recis_idmap_import")
 
 
+def recis_idmap_key_ages(h, keys, n: int, ages, set_: bool, stream=None):
+    _check(load_library().recis_idmap_key_ages(h, _ptr(keys), n, _ptr(ages), 1 if set_ else 0, _stream(stream)),
+           "recis_idmap_key_ages")
+
+
+def recis_idmap_sketch(h, counters, set_: bool, stream=None):
+    _check(load_library().recis_idmap_sketch(h, _ptr(counters), 1 if set_ else 0, _stream(stream)),
+           "recis_idmap_sketch")
+
+
 def recis_idmap_stats(h, stream=None) -> recis_table_stats:
     st = recis_table_stats()
     _check(load_library().recis_idmap_stats(h, C.byref(st), _stream(stream)), "recis_idmap_stats")
@@ -309,6 +322,13 @@ def make_descs(feats: Sequence[DeviceFeature]):
     return arr
 
 
+def _as_u32_bits(x):
+    """int32 tensor holding the bits of uint32 values given as int64."""
+    import torch
+    v = x.to(torch.int64) & 0xFFFFFFFF
+    return torch.where(v >= 2**31, v - 2**32, v).to(torch.int32).contiguous()
+
+
 class Table:
     """Owns one recis table handle."""
 
@@ -327,7 +347,8 @@ class Table:
         cfg.admit_sketch_bits = admit_sketch_bits
         self.dim, self.dtype, self.optim = dim, dtype, optim
         self.config = {"seed": seed, "init_bound": init_bound, "admit_threshold": admit_threshold,
-                       "block_memory": block_memory}
+                       "block_memory": block_memory, "track_last_use": bool(track_last_use),
+                       "admit_sketch_bits": int(admit_sketch_bits)}
         self.h = recis_idmap_create(cfg, stream)
 
     def close(self):
@@ -368,6 +389,28 @@ class Table:
         """Keeps at most max_keys keys, the most recently used (needs
         track_last_use)."""
         recis_idmap_evict_lru(self.h, max_keys, num_evicted, stream)
+
+    def key_ages(self, keys, stream=None):
+        """uint32 ages of the given keys (device int64 tensor) as an int64 tensor
+        (0xFFFFFFFF: not in the table); needs track_last_use."""
+        import torch
+        ages = torch.empty(keys.shape[0], dtype=torch.int32, device="cuda")
+        recis_idmap_key_ages(self.h, keys.contiguous(), int(keys.shape[0]), ages, False, stream)
+        return ages.to(torch.int64) & 0xFFFFFFFF
+
+    def set_key_ages(self, keys, ages, stream=None):
+        a = _as_u32_bits(ages)
+        recis_idmap_key_ages(self.h, keys.contiguous(), int(keys.shape[0]), a, True, stream)
+
+    def sketch_counters(self, stream=None):
+        """The count-min sketch's counters (int64 tensor of the uint32 values)."""
+        import torch
+        c = torch.empty(4 << self.config["admit_sketch_bits"], dtype=torch.int32, device="cuda")
+        recis_idmap_sketch(self.h, c, False, stream)
+        return c.to(torch.int64) & 0xFFFFFFFF
+
+    def set_sketch_counters(self, counters, stream=None):
+        recis_idmap_sketch(self.h, _as_u32_bits(counters), True, stream)
 
     def writeback(self, keys, rows, stream=None):
         recis_writeback(self.h, keys, int(keys.numel()), rows, stream)

@@ -16,8 +16,13 @@ File layout (tensor names, shapes, dtypes; n keys, unsorted):
                                  where has_row is 0
     state    f32     [n, s*dim]  optimizer state (s = 2 for Adam: m then v;
                                  1 for Adagrad); absent when there is none
+    last_use_age int64 [n]      (tables with last-use stamps) each key's age in
+                                 counting lookups
+    sketch   int64   [4 << bits] (tables with count-min admission) the
+                                 sketch's counters, row after row
 and the string metadata
-    format, dim, dtype, optim, seed, init_bound, admit_threshold, adam_step.
+    format, dim, dtype, optim, seed, init_bound, admit_threshold, adam_step,
+    track_last_use, admit_sketch_bits.
 """
 from __future__ import annotations
 
@@ -60,9 +65,15 @@ def save(table: "recis.Table", path: str, stream=None) -> int:
     }
     if ex["state"].shape[1] > 0:
         tensors["state"] = ex["state"].cpu()
+    if cfg["track_last_use"]:
+        tensors["last_use_age"] = table.key_ages(ex["keys"], stream).cpu()
+    if cfg["admit_sketch_bits"]:
+        tensors["sketch"] = table.sketch_counters(stream).cpu()
     write(path, tensors, {"dim": table.dim, "dtype": table.dtype, "optim": table.optim, "seed": cfg["seed"],
                           "init_bound": repr(float(cfg["init_bound"])),
-                          "admit_threshold": cfg["admit_threshold"], "adam_step": int(st.adam_step)})
+                          "admit_threshold": cfg["admit_threshold"], "adam_step": int(st.adam_step),
+                          "track_last_use": int(cfg["track_last_use"]),
+                          "admit_sketch_bits": int(cfg["admit_sketch_bits"])})
     return int(ex["keys"].shape[0])
 
 
@@ -74,9 +85,15 @@ def load(path: str, stream=None, **table_kw) -> "recis.Table":
     t, meta = read(path)
     table = recis.Table(int(meta["dim"]), meta["dtype"], meta["optim"], seed=int(meta["seed"]),
                         init_bound=float(meta["init_bound"]), admit_threshold=int(meta["admit_threshold"]),
-                        **table_kw)
+                        track_last_use=bool(int(meta.get("track_last_use", "0"))),
+                        admit_sketch_bits=int(meta.get("admit_sketch_bits", "0")), **table_kw)
+    keys = t["keys"].cuda()
     rows = torch.where(t["has_row"].to(torch.bool), 0, -1).to(torch.int64)
     state: Optional[torch.Tensor] = t["state"].cuda() if "state" in t else None
-    table.import_(t["keys"].cuda(), rows.cuda(), t["counts"].cuda(), t["params"].cuda(), state,
+    table.import_(keys, rows.cuda(), t["counts"].cuda(), t["params"].cuda(), state,
                   adam_step=int(meta["adam_step"]), stream=stream)
+    if "last_use_age" in t:
+        table.set_key_ages(keys, t["last_use_age"].cuda(), stream)
+    if "sketch" in t:
+        table.set_sketch_counters(t["sketch"].cuda(), stream)
     return table

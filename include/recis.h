@@ -304,6 +304,20 @@ recis_status recis_idmap_import(recis_table* t, int64_t n, const int64_t* keys, 
                                 const uint32_t* counts, const void* params, const float* state,
                                 int64_t adam_step, hipStream_t s);
 
+/* The admission state beside the exported keys, so a save of a table that
+ * keeps last-use stamps or a count-min sketch restores whole.
+ * recis_idmap_key_ages: set 0 writes to ages[i] the age of keys[i] (counting
+ * insert_find calls since one last counted it; ~0 for a key not in the
+ * table); set 1 gives each key present the stamp that makes its age ages[i].
+ * keys device [n], ages device [n].  Needs track_last_use (else UNSUPPORTED).
+ * recis_idmap_sketch: set 0 copies the sketch's 4 x 2^admit_sketch_bits
+ * counters (row after row) to `counters`; set 1 loads them from there.
+ * counters: device.  Needs admit_sketch_bits > 0 (else UNSUPPORTED).
+ * Both are stream-ordered; for restoring, call them after recis_idmap_import. */
+recis_status recis_idmap_key_ages(recis_table* t, const int64_t* keys, int64_t n, uint32_t* ages,
+                                  int32_t set, hipStream_t s);
+recis_status recis_idmap_sketch(recis_table* t, uint32_t* counters, int32_t set, hipStream_t s);
+
 /* Table statistics (synchronises `s`); st: host. */
 recis_status recis_idmap_stats(recis_table* t, recis_table_stats* st, hipStream_t s);
 

@@ -705,6 +705,44 @@ def test_save_load_resume_admission_and_bf16(tmp_path):
                       str(tmp_path / "seq.safetensors"), {})
 
 
+def test_save_load_resume_admission_state(tmp_path):
+    """A table with last-use stamps and count-min admission saved and
+    restored (the ages and the sketch travel in the file), then LRU-bounded
+    and sketch-admitted steps against the oracle that never stopped."""
+    import torch
+    from dynamic_embedding_tables_amd import recis, saver
+    spec = W.spec_multi(3)
+    table = make_table(spec, track_last_use=True, admit_sketch_bits=8)
+    otab = oracle.OracleTable(spec)
+    otab.set_sketch(8)
+    for s in range(3):
+        b = W.multi_batch(s, 3, batch=96, num_feats=5)
+        gpu_step(table, spec, b, recis.LookupResult(max(b.n, 1), b.num_feats * b.batch))
+        oracle_step(otab, spec, b)
+    torch.cuda.synchronize()
+    assert table.get_error() == 0
+    path = str(tmp_path / "adm.safetensors")
+    saver.save(table, path)
+    table.close()
+    restored = saver.load(path)
+    check_export(canon_export(restored), otab.export(), spec)
+    ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for s in range(3, 7):
+        b = W.multi_batch(s, 3, batch=96, num_feats=5)
+        res = recis.LookupResult(max(b.n, 1), b.num_feats * b.batch)
+        out, _ = gpu_step(restored, spec, b, res)
+        r, oout, oab = oracle_step(otab, spec, b)
+        torch.cuda.synchronize()
+        assert restored.get_error() == 0
+        check_lookup(canon_lookup(res), r)
+        check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+        if s == 4:
+            restored.evict_lru(1500, ne)
+            assert int(ne.item()) == otab.evict_lru(1500)
+        check_export(canon_export(restored), otab.export(), spec)
+    restored.close()
+
+
 def test_import_rejects_used_tables_and_repeated_keys():
     import torch
     from dynamic_embedding_tables_amd import recis
