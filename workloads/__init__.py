@@ -288,7 +288,7 @@ def capacity_batch(step: int, batch: int = 65536, num_feats: int = 100, dim: int
 
 
 def multi_batch(step: int, table: int, batch: int = 32768, num_feats: int = 60,
-                alpha: float = 1.1) -> Batch:
+                alpha: float = 1.1, grad: bool = True) -> Batch:
     """One of the five merged tables: bag length max(1, Poisson(4)); IDs Zipf(alpha)
     over 2**40 through a per-(table, feature) bijection; slot = feature index."""
     dim = MULTI_DIMS[table]
@@ -300,7 +300,7 @@ def multi_batch(step: int, table: int, batch: int = 32768, num_feats: int = 60,
         ranks = zipf_truncated(rng, alpha, ID_SPACE_2_40, int(off[-1]))
         vals = permute_2_40(ranks - 1, feature_key(5, table, f))
         feats.append(FeatureInput(values=vals, bag_offsets=off, slot=f))
-    return Batch(feats, batch, _grad(5, step * 8 + table, (batch, num_feats * dim)))
+    return Batch(feats, batch, _grad(5, step * 8 + table, (batch, num_feats * dim)) if grad else None)
 
 
 def cache_keys(num_keys: int = 10_000_000) -> np.ndarray:
