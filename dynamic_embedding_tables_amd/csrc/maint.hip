@@ -221,6 +221,59 @@ __device__ long long alloc_one_row(const TableDev& t) {
   return r;
 }
 
+// Writeback: find or insert key in the IDMap and give it a row if it has
+// none (a pending row becomes written).  row = -1 on a full IDMap or row
+// space (the error is raised); fresh = 1 when the row's state starts at zero.
+__device__ void wb_find_row(const TableDev& t, long long key, long long& row, int& fresh) {
+  row = -1;
+  fresh = 0;
+  unsigned long long p = slot_of(key, t.slot_shift);
+  long long at = -1;
+  bool inserted = false;
+  for (unsigned long long n = 0; n <= t.region_mask; ++n) {
+    const long long cur = t.slots[p].key;
+    if (cur == key) {
+      at = (long long)p;
+      break;
+    }
+    if (cur == kEmptyKey) {
+      const long long old = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
+                                                 (unsigned long long)kEmptyKey, (unsigned long long)key);
+      if (old == kEmptyKey) {
+        at = (long long)p;
+        inserted = true;
+        break;
+      }
+      if (old == key) {
+        at = (long long)p;
+        break;
+      }
+    }
+    p = next_slot(t, p);
+  }
+  if (at < 0) {
+    atomicOr(&t.ctr->error, kErrCapacity);
+  } else {
+    if (inserted) {
+      atomicAdd(&t.ctr->num_keys, 1ull);
+      if (t.last_use) t.last_use[at] = t.step;
+    }
+    row = inserted ? -1 : t.slots[at].row;
+    if (row >= 0 && (row & kPendingRow)) {  // allocated, never written: written now
+      row &= ~(long long)kPendingRow;
+      t.slots[at].row = (int)row;
+      fresh = 1;
+    } else if (row < 0) {
+      row = alloc_one_row(t);
+      if (row < 0) atomicOr(&t.ctr->error, kErrCapacity);
+      else {
+        t.slots[at].row = (int)row;
+        fresh = 1;
+      }
+    }
+  }
+}
+
 // Writeback, step 2: one wave per distinct key: find or insert it, give it a
 // row if it has none, and store the last occurrence's values.
 template <typename TP>
@@ -234,53 +287,7 @@ __global__ __launch_bounds__(256) void k_wb_apply(TableDev t, const float* rows,
     const int last = d->count;
     long long row = -1;
     int fresh = 0;
-    if (lane == 0) {
-      unsigned long long p = slot_of(key, t.slot_shift);
-      long long at = -1;
-      bool inserted = false;
-      for (unsigned long long n = 0; n <= t.region_mask; ++n) {
-        const long long cur = t.slots[p].key;
-        if (cur == key) {
-          at = (long long)p;
-          break;
-        }
-        if (cur == kEmptyKey) {
-          const long long old = (long long)atomicCAS((unsigned long long*)&t.slots[p].key,
-                                                     (unsigned long long)kEmptyKey, (unsigned long long)key);
-          if (old == kEmptyKey) {
-            at = (long long)p;
-            inserted = true;
-            break;
-          }
-          if (old == key) {
-            at = (long long)p;
-            break;
-          }
-        }
-        p = next_slot(t, p);
-      }
-      if (at < 0) {
-        atomicOr(&t.ctr->error, kErrCapacity);
-      } else {
-        if (inserted) {
-          atomicAdd(&t.ctr->num_keys, 1ull);
-          if (t.last_use) t.last_use[at] = t.step;
-        }
-        row = inserted ? -1 : t.slots[at].row;
-        if (row >= 0 && (row & kPendingRow)) {  // allocated, never written: written now
-          row &= ~(long long)kPendingRow;
-          t.slots[at].row = (int)row;
-          fresh = 1;
-        } else if (row < 0) {
-          row = alloc_one_row(t);
-          if (row < 0) atomicOr(&t.ctr->error, kErrCapacity);
-          else {
-            t.slots[at].row = (int)row;
-            fresh = 1;
-          }
-        }
-      }
-    }
+    if (lane == 0) wb_find_row(t, key, row, fresh);
     row = __shfl(row, 0);
     fresh = __shfl(fresh, 0);
     if (row >= 0) {
@@ -296,6 +303,60 @@ __global__ __launch_bounds__(256) void k_wb_apply(TableDev t, const float* rows,
       }
     }
     if (lane == 0) {
+      d->key = kEmptyKey;
+      d->count = 0;
+    }
+  }
+}
+
+// Writeback, step 2, for rows 16-byte aligned: sixteen lanes per distinct
+// key, four keys per wave, so that one round of waves covers a batch of
+// cache writes.  Each group loads its key's last row before its leader looks
+// the key up, so the row's fetch overlaps the IDMap round trips.
+template <typename TP>
+__global__ __launch_bounds__(256) void k_wb_apply_vec(TableDev t, const float* rows, DedupSlot* dd,
+                                                      const long long* wb_keys, const int* uslot) {
+  constexpr int G = 16;              // lanes per key
+  constexpr int MAXC = 256 / 4 / G;  // 16-byte chunks per lane at the largest dim
+  const long long U = (long long)t.ctr->scratch_count;
+  const int lane = threadIdx.x & 63, gl = lane & (G - 1), lead = lane & ~(G - 1);
+  const int nc = t.dim >> 2;
+  const long long ngroups = (long long)gridDim.x * (blockDim.x / G);
+  // a group's lanes share u, so every shuffle below reads an active leader
+  for (long long u = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / G; u < U; u += ngroups) {
+    const long long key = wb_keys[u];
+    DedupSlot* d = &dd[uslot[u]];
+    const float4* src = reinterpret_cast<const float4*>(rows + (long long)d->count * t.dim);
+    float4 v[MAXC];
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (gl + j * G < nc) v[j] = src[gl + j * G];
+    }
+    long long row = -1;
+    int fresh = 0;
+    if (gl == 0) wb_find_row(t, key, row, fresh);
+    row = __shfl(row, lead);
+    fresh = __shfl(fresh, lead);
+    if (row >= 0) {
+      char* rp = row_ptr(t.rs, row);
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int c = gl + j * G;
+        if (c >= nc) continue;
+        if (sizeof(TP) == 2)
+          reinterpret_cast<uint2*>(rp)[c] =
+              make_uint2((unsigned)f32_to_bf16(v[j].x) | ((unsigned)f32_to_bf16(v[j].y) << 16),
+                         (unsigned)f32_to_bf16(v[j].z) | ((unsigned)f32_to_bf16(v[j].w) << 16));
+        else
+          reinterpret_cast<float4*>(rp)[c] = v[j];
+      }
+      if (fresh) {
+        float4* st = reinterpret_cast<float4*>(rp + (long long)t.dim * (long long)sizeof(TP));
+        for (int c = gl; c < (t.state_words * t.dim) >> 2; c += G) st[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    if (gl == 0) {
       d->key = kEmptyKey;
       d->count = 0;
     }
@@ -590,6 +651,14 @@ void launch_writeback(const TableDev& t, const long long* keys, long long n, con
   if (n == 0) return;
   hipLaunchKernelGGL(k_wb_dedup, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, t, keys, n, dd,
                      dd_mask, dd_shift, wb_keys, uslot);
+  if ((reinterpret_cast<uintptr_t>(rows) & 15) == 0) {  // sixteen keys per block
+    const unsigned g = grid_for(n, 16);
+    if (t.dtype == RECIS_DTYPE_BF16)
+      hipLaunchKernelGGL(k_wb_apply_vec<unsigned short>, dim3(g), dim3(256), 0, s, t, rows, dd, wb_keys, uslot);
+    else
+      hipLaunchKernelGGL(k_wb_apply_vec<float>, dim3(g), dim3(256), 0, s, t, rows, dd, wb_keys, uslot);
+    return;
+  }
   const unsigned g = grid_for(n, 4);
   if (t.dtype == RECIS_DTYPE_BF16)
     hipLaunchKernelGGL(k_wb_apply<unsigned short>, dim3(g), dim3(256), 0, s, t, rows, dd, wb_keys, uslot);

@@ -588,21 +588,31 @@ def test_bucket_overflow_path():
     run_parity(spec, [b, b])
 
 
-def test_writeback_cache_last_writer_wins():
+@pytest.mark.parametrize("row_offset", [0, 1])
+def test_writeback_cache_last_writer_wins(row_offset):
+    """row_offset 1 hands the rows over 4 bytes past a 16-byte boundary (the
+    one-wave-per-key path); 0 takes the sixteen-lanes-per-key path."""
     import torch
     from dynamic_embedding_tables_amd import recis
     spec = W.spec_cache()
     table = make_table(spec)
     otab = oracle.OracleTable(spec)
     keys = W.cache_keys(5000)
+
+    def dev_rows(e):
+        buf = torch.empty(e.size + row_offset, dtype=torch.float32, device="cuda")
+        rows = buf[row_offset:].view(e.shape)
+        rows.copy_(torch.from_numpy(e))
+        assert (rows.data_ptr() % 16 == 0) == (row_offset == 0)
+        return rows
     # pre-insert the cache keys, then write batches with repeated keys
-    table.writeback(torch.from_numpy(keys).cuda(), torch.zeros(keys.size, 256, device="cuda"))
+    table.writeback(torch.from_numpy(keys).cuda(), dev_rows(np.zeros((keys.size, 256), np.float32)))
     otab.writeback(keys, np.zeros((keys.size, 256), np.float32))
     for step in range(3):
         k, e = W.cache_writes(step, keys, n=3000)
         k = np.concatenate([k, np.array([1 << 45, 1 << 45], np.int64)])   # a miss, written twice
         e = np.concatenate([e, W.rng_for(step, 99).standard_normal((2, 256), dtype=np.float32)])
-        table.writeback(torch.from_numpy(k).cuda(), torch.from_numpy(e).cuda())
+        table.writeback(torch.from_numpy(k).cuda(), dev_rows(e))
         assert otab.writeback(k, e) == 0
         torch.cuda.synchronize()
         assert table.get_error() == 0
