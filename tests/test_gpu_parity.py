@@ -229,6 +229,46 @@ def test_multi_table_full_size_with_eviction():
     run_parity(spec, [W.multi_batch(s, 0) for s in range(3)], evict_every=2, export_every=2)
 
 
+@pytest.mark.timeout(900)
+def test_cache_writeback_full_size():
+    """The item cache at full size, laid out as the benchmark's table: 10M
+    keys inserted with zero rows, then two calls of 16,384 writes drawn with
+    replacement.  Read back by a FIND_ONLY gather, every written key holds
+    the RNE of its last write (the oracle's writeback of the same pairs) and
+    a sample of the other keys still holds zeros."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_cache()
+    keys = W.cache_keys()
+    table = make_table(spec, slot_capacity=1 << 25, block_rows=1 << 20, reserve_rows=keys.size + (1 << 20))
+    chunk = 1 << 20
+    zero = torch.zeros(chunk, spec.dim, device="cuda")
+    for c0 in range(0, keys.size, chunk):
+        kd = torch.from_numpy(keys[c0:c0 + chunk]).cuda()
+        table.writeback(kd, zero[:kd.numel()])
+    otab = oracle.OracleTable(spec)
+    for step in range(2):
+        k, e = W.cache_writes(step, keys)
+        table.writeback(torch.from_numpy(k).cuda(), torch.from_numpy(e).cuda())
+        assert otab.writeback(k, e) == 0
+    torch.cuda.synchronize()
+    assert table.get_error() == 0
+    assert table.stats().keys == keys.size
+    o = otab.export()
+    rng = np.random.default_rng(7)
+    others = np.setdiff1d(keys[rng.integers(0, keys.size, 4000)], o["keys"])[:2000]
+    probe = np.concatenate([o["keys"], others])
+    b = W.Batch([W.FeatureInput(values=probe, bag_offsets=np.arange(probe.size + 1, dtype=np.int32), slot=0)],
+                int(probe.size), None)
+    res = recis.LookupResult(int(probe.size), int(probe.size))
+    out, _ = gpu_step(table, spec, b, res, find_only=True, with_backward=False)
+    got = out.float().cpu().numpy()
+    nw = o["keys"].size
+    np.testing.assert_array_equal(got[:nw], o["params"])
+    assert not got[nw:].any()
+    table.close()
+
+
 def test_growth_of_idmap_and_blocks():
     spec = W.spec_ctr()
     run_parity(spec, [W.ctr_batch(s, batch=64, num_feats=8) for s in range(3)],
