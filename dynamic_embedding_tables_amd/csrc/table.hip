@@ -509,6 +509,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
     N += d.n;
   }
   if (N > (1ll << 30) || N > res->capacity) return RECIS_ERR_INVALID_ARG;
+  if ((long long)num_feats * batch > res->bag_capacity) return RECIS_ERR_INVALID_ARG;
   if (!res->bag_offsets || !res->num_unique || !res->unique_offsets || !res->plan) return RECIS_ERR_INVALID_ARG;
   if (N > 0 && (!res->unique_keys || !res->unique_rows || !res->inverse || !res->counts || !res->grouped))
     return RECIS_ERR_INVALID_ARG;

@@ -79,7 +79,7 @@ class recis_lookup_result(C.Structure):
     _fields_ = [("unique_keys", C.c_void_p), ("unique_rows", C.c_void_p), ("inverse", C.c_void_p),
                 ("counts", C.c_void_p), ("bag_offsets", C.c_void_p), ("num_unique", C.c_void_p),
                 ("unique_offsets", C.c_void_p), ("grouped", C.c_void_p), ("plan", C.c_void_p),
-                ("capacity", C.c_int64), ("n", C.c_int64), ("num_feats", C.c_int32),
+                ("capacity", C.c_int64), ("bag_capacity", C.c_int64), ("n", C.c_int64), ("num_feats", C.c_int32),
                 ("batch", C.c_int32), ("flags", C.c_uint32), ("epoch", C.c_uint64)]
 
 
@@ -285,7 +285,7 @@ class LookupResult:
             self.unique_keys.data_ptr(), self.unique_rows.data_ptr(), self.inverse.data_ptr(),
             self.counts.data_ptr(), self.bag_offsets.data_ptr(), self.num_unique.data_ptr(),
             self.unique_offsets.data_ptr(), self.grouped.data_ptr(), self.plan.data_ptr(),
-            cap, 0, 0, 0, 0, 0)
+            cap, max(int(nbags), 0), 0, 0, 0, 0, 0)
         self.capacity = cap
         self.nbags = nbags
 

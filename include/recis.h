@@ -163,13 +163,17 @@ typedef struct {
                               the bit) -- the row offset is the value without it */
   int32_t* inverse;        /* [capacity] occurrence -> index into unique_* */
   int32_t* counts;         /* [capacity] occurrences of each distinct key */
-  int32_t* bag_offsets;    /* [num_feats * batch + 1] merged CSR, bag f*batch + i */
+  int32_t* bag_offsets;    /* [bag_capacity + 1]; insert_find writes its first
+                              num_feats * batch + 1: merged CSR, bag f*batch + i */
   int64_t* num_unique;     /* [1] */
   int32_t* unique_offsets; /* [capacity + 1] start of each key's group in `grouped` */
   int32_t* grouped;        /* [capacity] bag ids (or occurrence ids) grouped by key */
   int32_t* plan;           /* [recis_plan_words(capacity)] opaque: backward work plan,
                               per-key IDMap slots, per-occurrence row references */
   int64_t capacity;
+  int64_t bag_capacity;    /* merged bags bag_offsets has room for: insert_find returns
+                              RECIS_ERR_INVALID_ARG, before any work, when
+                              num_feats * batch exceeds it */
   int64_t n;               /* occurrences of the last insert_find */
   int32_t num_feats;
   int32_t batch;

@@ -230,6 +230,61 @@ def test_multi_table_full_size_with_eviction():
 
 
 @pytest.mark.timeout(900)
+def test_capacity_full_size_two_features_checked():
+    """The capacity configuration at full size, laid out as the benchmark's
+    table: 100 features x 2M resident IDs (200M rows of dim 64 fp32 + Adam),
+    then one full step (65536 bags per feature, Poisson(8), 52.4M IDs).  Keys
+    carry their feature's slot, so one feature's bags, keys and gradient
+    columns do not depend on the other features: the oracle recomputes two
+    whole features, their pooled outputs and, after the Adam update, the
+    parameters of every key they touched (read back by a FIND_ONLY gather)."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_capacity()
+    D = spec.dim
+    b = W.capacity_batch(0)
+    # the benchmark's reservation: resident rows, one step's IDs, and 2% new
+    # rows for each of its eleven other steps
+    table = make_table(spec, slot_capacity=1 << 29, block_rows=1 << 20,
+                       reserve_rows=200_000_000 + b.n + 11 * (b.n // 30))
+    try:
+        for f, ids in W.capacity_resident_keys():
+            kd = torch.from_numpy(ids).cuda()
+            od = torch.arange(ids.size + 1, dtype=torch.int32, device="cuda")
+            r = recis.LookupResult(ids.size, ids.size)
+            table.insert_find([recis.DeviceFeature(kd, od, f)], ids.size, r)
+            del r, kd, od
+        torch.cuda.synchronize()
+        assert table.get_error() == 0
+        assert table.stats().rows_in_use == 200_000_000
+        res = recis.LookupResult(b.n, b.num_feats * b.batch)
+        out, _ = gpu_step(table, spec, b, res)
+        torch.cuda.synchronize()
+        assert table.get_error() == 0
+        for f in (0, 77):
+            cols = slice(f * D, (f + 1) * D)
+            sub = W.Batch([b.features[f]], b.batch, np.ascontiguousarray(b.grad[:, cols]))
+            otab = oracle.OracleTable(spec)
+            r, o_out, o_abs = oracle_step(otab, spec, sub)
+            check_forward(out[:, cols].contiguous(), spec, o_out, o_abs, r.merged_offsets, 1, exact=True)
+            ex = otab.export()
+            ids = ex["keys"] & ((1 << 48) - 1)
+            nk = int(ids.size)
+            fd = [recis.DeviceFeature(torch.from_numpy(ids).cuda(),
+                                      torch.arange(nk + 1, dtype=torch.int32, device="cuda"), f)]
+            rr = recis.LookupResult(nk, nk)
+            table.insert_find(fd, nk, rr, flags=recis.RECIS_GROUP_BY_OCCURRENCE | recis.RECIS_FIND_ONLY)
+            g = torch.empty(nk, D, dtype=torch.float32, device="cuda")
+            table.forward(rr, "none", g)
+            gv = g.cpu().numpy().astype(np.float64)
+            ov = ex["params"].astype(np.float64)
+            bad = np.abs(gv - ov) > 1e-5 * np.maximum(np.abs(ov), spec.lr)
+            assert not bad.any(), f"feature {f}: {bad.sum()} updated parameters off"
+    finally:
+        table.close()
+
+
+@pytest.mark.timeout(900)
 def test_cache_writeback_full_size():
     """The item cache at full size, laid out as the benchmark's table: 10M
     keys inserted with zero rows, then two calls of 16,384 writes drawn with
@@ -267,6 +322,22 @@ def test_cache_writeback_full_size():
     np.testing.assert_array_equal(got[:nw], o["params"])
     assert not got[nw:].any()
     table.close()
+
+
+def test_lookup_rejects_a_small_bag_buffer():
+    """A result whose bag_offsets buffer holds fewer than num_feats * batch
+    bags is refused before any work (INVALID_ARG), and the table stays
+    usable; the same lookup with room for every bag then matches the oracle."""
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_ctr()
+    b = W.ctr_batch(0, batch=64, num_feats=3)
+    table = make_table(spec)
+    small = recis.LookupResult(b.n, b.batch)   # room for one feature's bags only
+    with pytest.raises(recis.RecisError) as e:
+        table.insert_find(device_features(b), b.batch, small)
+    assert e.value.status == recis.RECIS_ERR_INVALID_ARG
+    table.close()
+    run_parity(spec, [b])
 
 
 def test_growth_of_idmap_and_blocks():
