@@ -85,6 +85,8 @@ def lib():
         L.orc_set_sketch.argtypes = [p, C.c_int]
         L.orc_writeback.restype = C.c_int
         L.orc_writeback.argtypes = [p, p, C.c_int64, p]
+        L.orc_current_rows.restype = C.c_int
+        L.orc_current_rows.argtypes = [p, p, C.c_int64, p]
         L.orc_size.restype = C.c_int64
         L.orc_size.argtypes = [p]
         L.orc_rows_in_use.restype = C.c_int64
@@ -201,6 +203,14 @@ class OracleTable:
         r.num_feats, r.batch = F, batch
         return r
 
+    def current_rows(self, r: LookupResult) -> np.ndarray:
+        """The rows the map holds now for r's distinct keys (-1: none): what
+        the lookup's forward and backward act on."""
+        rows = np.zeros(max(r.U, 1), dtype=np.int64)
+        keys = _c(r.unique_keys[:max(r.U, 1)], np.int64)
+        assert lib().orc_current_rows(self.h, _ptr(keys), r.U, _ptr(rows)) == 0
+        return rows
+
     def forward(self, r: LookupResult, pool: str, with_abs: bool = False):
         D = self.dim
         if pool == "none":
@@ -211,7 +221,8 @@ class OracleTable:
             shape = (r.batch, r.num_feats * D)
             out = np.zeros(shape, dtype=np.float32)
             ab = np.zeros(shape, dtype=np.float64) if with_abs else None
-        st = lib().orc_forward(self.h, _ptr(r.unique_rows), _ptr(r.inverse), _ptr(r.merged_offsets),
+        rows = self.current_rows(r)
+        st = lib().orc_forward(self.h, _ptr(rows), _ptr(r.inverse), _ptr(r.merged_offsets),
                                r.num_feats, r.batch, POOL[pool], _ptr(out), _ptr(ab))
         assert st == 0, st
         return (out, ab) if with_abs else out
@@ -232,13 +243,15 @@ class OracleTable:
         s = self.spec
         G = _c(G, np.float64)
         o = None if only is None else _c(only, np.uint8)
-        return lib().orc_apply_update(self.h, _ptr(r.unique_rows), r.U, _ptr(G), s.lr, s.beta1,
+        rows = self.current_rows(r)
+        return lib().orc_apply_update(self.h, _ptr(rows), r.U, _ptr(G), s.lr, s.beta1,
                                       s.beta2, s.eps, _ptr(o))
 
     def backward_update(self, r: LookupResult, pool: str, grad: np.ndarray, grad_dtype: str = "f32") -> int:
         s = self.spec
         g = _c(grad, np.uint16 if grad_dtype == "bf16" else np.float32)
-        return lib().orc_backward_update(self.h, _ptr(r.unique_rows), _ptr(r.inverse),
+        rows = self.current_rows(r)
+        return lib().orc_backward_update(self.h, _ptr(rows), _ptr(r.inverse),
                                          _ptr(r.merged_offsets), r.U, r.num_feats, r.batch,
                                          POOL[pool], _ptr(g), DT[grad_dtype], s.lr, s.beta1,
                                          s.beta2, s.eps)

@@ -671,6 +671,20 @@ int orc_writeback(void* h, const int64_t* keys, int64_t n, const float* rows) {
   return status;
 }
 
+// The rows the map holds now for `keys` (-1: absent, or present without a
+// row).  A lookup's forward and backward act on the rows its keys hold when
+// they run: the IDMap is the map from ID to offset ([README] Efficient
+// dynamic Embedding), so a key evicted since the lookup has no row, and a
+// row never moves while its key stays.
+int orc_current_rows(void* h, const int64_t* keys, int64_t n, int64_t* rows) {
+  const Table& t = *static_cast<Table*>(h);
+  for (int64_t i = 0; i < n; ++i) {
+    auto it = t.idmap.find(keys[i]);
+    rows[i] = it == t.idmap.end() ? -1 : it->second.row;
+  }
+  return ST_OK;
+}
+
 int64_t orc_size(void* h) { return int64_t(static_cast<Table*>(h)->idmap.size()); }
 int64_t orc_rows_in_use(void* h) {
   const Table& t = *static_cast<Table*>(h);

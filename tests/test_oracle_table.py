@@ -377,8 +377,62 @@ def test_bf16_update_rounds_once():
         np.testing.assert_array_equal(ex["state"][i], a.astype(np.float32))
         wb = oracle.round_bf16(want)
         got = ex["params"][i].view(np.uint32) >> 16
-        assert np.all(np.abs(got.astype(np.int64) - wb.astype(np.int64)) <= 1)
-        assert (got == wb).mean() > 0.5
+        np.testing.assert_array_equal(got, wb)
+
+
+def test_bf16_update_rounds_once_at_a_tie_of_the_float_rounding():
+    """Adagrad with eps = 0 from a row written to exactly 1.0: the new value is
+    exactly 1 - lr in binary64 (lr * g / |g| = lr exactly).  Each lr puts
+    1 - lr a quarter of a float32 unit above (or below) a midpoint between two
+    bfloat16 neighbours.  Rounded once, it goes to the neighbour on its side;
+    rounded to float32 first, it would land on the midpoint and tie to the even
+    neighbour.  The expected bits are fixed by that construction, not by the
+    oracle's own rounding routine."""
+    cases = []  # (lr, expected bf16 bits of 1 - lr)
+    for k in (100, 37, 64, 3):
+        lo = 0.5 + k * 2.0**-8            # bf16 neighbours in [0.5, 1): spacing 2^-8
+        mid = lo + 2.0**-9
+        even_is_lo = k % 2 == 0
+        # a quarter float32 unit on the odd neighbour's side of the midpoint:
+        # single rounding gives the odd neighbour, double rounding the even one
+        want = mid + (2.0**-26 if even_is_lo else -2.0**-26)
+        odd = lo + 2.0**-8 if even_is_lo else lo
+        bits = int(np.array([odd], np.float32).view(np.uint32)[0] >> 16)
+        assert np.array([odd], np.float32).view(np.uint32)[0] & 0xFFFF == 0
+        cases.append((1.0 - want, bits))
+    for lr, bits in cases:
+        spec = TableSpec(dim=8, dtype="bf16", optim="adagrad", pool="none", lr=lr, eps=0.0, grad_dtype="bf16")
+        tab = oracle.OracleTable(spec)
+        assert tab.writeback(np.array([11], np.int64), np.ones((1, 8), np.float32)) == 0
+        f = [FeatureInput(values=np.array([11], np.int64), bag_offsets=np.array([0, 1], np.int32), slot=0)]
+        r = tab.insert_find(f, 1)
+        g = to_bf16_bits(np.full((1, 8), 0.75, np.float32))
+        assert tab.backward_update(r, "none", g, "bf16") == 0
+        got = tab.export()["params"][0].view(np.uint32) >> 16
+        np.testing.assert_array_equal(got, np.full(8, bits, np.uint32))
+
+
+def test_stale_lookup_acts_on_current_rows():
+    """A lookup's backward after an eviction pass and a later insert: the
+    evicted key gets nothing, and the key that took over its row keeps its
+    initial values; the surviving key gets the closed-form Adagrad step."""
+    spec = TableSpec(dim=4, dtype="f32", optim="adagrad", pool="sum", lr=0.01, eps=1e-10)
+    tab = oracle.OracleTable(spec)
+    f = [FeatureInput(values=np.array([1, 1, 2], np.int64), bag_offsets=np.array([0, 2, 3], np.int32), slot=0)]
+    ra = tab.insert_find(f, 2)                       # key 1 twice, key 2 once
+    assert tab.evict(2) == 1                         # key 2 leaves, its row is freed
+    fb = [FeatureInput(values=np.array([7], np.int64), bag_offsets=np.array([0, 1], np.int32), slot=0)]
+    tab.insert_find(fb, 1)                           # key 7 takes the freed row
+    g = np.array([[1, -2, 3, -4], [5, 6, -7, 8]], np.float32)
+    assert tab.backward_update(ra, "sum", g) == 0
+    ex = tab.export()
+    assert list(ex["keys"]) == [1, 7]
+    G1 = 2.0 * g[0].astype(np.float64)               # key 1 sits twice in bag 0
+    w1 = oracle.init_row(spec.seed, 1, 4).astype(np.float64)
+    np.testing.assert_allclose(ex["params"][0], (w1 - spec.lr * G1 / (np.abs(G1) + spec.eps)).astype(np.float32),
+                               rtol=2e-7)
+    np.testing.assert_array_equal(ex["params"][1], oracle.init_row(spec.seed, 7, 4))
+    np.testing.assert_array_equal(ex["state"][1], np.zeros(4, np.float32))
 
 
 @pytest.mark.parametrize("decay", [0.0, 0.5, 1.0, 0.3])
