@@ -77,11 +77,20 @@ WORKLOADS = {
     "capacity": {
         "title": "Capacity stress: 200M pre-populated rows x dim 64 fp32 + Adam m/v, 100 features, batch 65536, "
                  "bag length Poisson(8), Zipf(1.2) IDs with 2% novel per step, sum pooling",
-        "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 5,
-        # 1.68 GB per gradient: one N(0,1) draw serves every step
-        "shared_grad": True,
+        "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 10,
         "table": {"slot_capacity": 1 << 29, "block_rows": 1 << 20},
         "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bwd_long_partial"),
+        # the oracle baseline: these features of the first timed step (5.2M IDs)
+        "cpu_features": 10,
+    },
+    # config 1: ten steps from an empty table; launch-bound, so its figure is
+    # the step latency
+    "tiny": {
+        "title": "Tiny single table: dim 16 fp32, 1 feature, batch 256, bag length max(1, Poisson(4)), IDs "
+                 "uniform over [0, 1e5), sum pooling, Adagrad lr 0.01; 10 steps from an empty table",
+        "spec": W.spec_tiny, "F": 1, "B": 256, "fill": "none", "steps": 10, "warmup": 0,
+        "table": {"slot_capacity": 1 << 16, "block_rows": 1 << 14},
+        "candidates": (),
     },
     # the five tables of one model, each with its own handle (see run_multi)
     "multi": {
@@ -109,6 +118,9 @@ def _gen(arg):
     if name == "multi":  # step = (step, table)
         b = W.multi_batch(step[0], step[1], grad=False)
         return [(f.values, f.bag_offsets, f.slot, f.ops, f.mod) for f in b.features], b.batch
+    if name == "tiny":
+        b = W.tiny_batch(step)
+        return [(f.values, f.bag_offsets, f.slot, f.ops, f.mod) for f in b.features], b.batch
     fn = {"ctr": W.ctr_batch, "seq": W.seq_batch, "capacity": W.capacity_batch}[name]
     b = fn(step, grad=False)
     return [(f.values, f.bag_offsets, f.slot, f.ops, f.mod) for f in b.features], b.batch
@@ -133,30 +145,38 @@ def host_info():
     return os.cpu_count(), model
 
 
-def cpu_baseline(seconds_budget=20.0):
-    """The oracle, single-threaded, on full-size CTR batches (2.2M IDs each) from
-    an empty table, for as many steps as fit the budget (at least one)."""
+def cpu_baseline(spec, timed, grads, nfeat=None, seconds_budget=20.0, what=""):
+    """The oracle, single-threaded, on the timed steps' own inputs: the first
+    timed step (only its first `nfeat` features when given), then further
+    timed steps while the time stays within the budget.  The oracle's table
+    starts empty and holds only the keys these steps touch: a row the GPU
+    table holds but the step has not touched is, by the initializer's
+    definition, the same as a row made on first touch, so the oracle does the
+    same work per distinct key (one row made or read, one update).  The
+    gradients are the timed steps' own (the first nfeat features' columns)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     oracle.build(force=False)
-    spec = W.spec_ctr()
     tab = oracle.OracleTable(spec)
     ids, steps, t_total = 0, 0, 0.0
-    while True:
-        b = W.ctr_batch(10_000 + steps)
+    for (feats, bsz), grad in zip(timed, grads):
+        fs = feats if nfeat is None else feats[:nfeat]
+        fin = [W.FeatureInput(values=v, bag_offsets=o, slot=sl, ops=ops, mod=mod) for (v, o, sl, ops, mod) in fs]
+        g = grad(len(fs))
         t0 = time.perf_counter()
-        r = tab.insert_find(b.features, b.batch)
+        r = tab.insert_find(fin, bsz)
         tab.forward(r, spec.pool)
-        tab.backward_update(r, spec.pool, b.grad)
+        tab.backward_update(r, spec.pool, g, spec.grad_dtype)
         t_total += time.perf_counter() - t0
-        ids += b.n
+        ids += sum(f.n for f in fin)
         steps += 1
-        if t_total >= seconds_budget or steps >= 8:
+        if t_total >= seconds_budget or nfeat is not None:
             break
+    part = f"features 0..{nfeat - 1} of " if nfeat is not None else ""
     return {"value": ids / t_total, "unit": "IDs/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full-size CTR steps (insert_find+forward+backward/Adam, "
-                      f"{ids} IDs) from an empty table, single-threaded g++ -O2 oracle, "
-                      f"{t_total:.1f} s"}
+            "sample": f"{part}{steps} timed step(s) of the {what} workload, the GPU's own inputs and "
+                      f"upstream gradients ({ids} IDs; insert_find + forward + backward/update), oracle "
+                      f"table holding only the touched keys, single-threaded g++ -O2 oracle, {t_total:.1f} s"}
 
 
 COPY_BYTES = 1 << 30
@@ -532,29 +552,34 @@ def run_multi(args, wl):
               for sp in specs]
     gen = torch.Generator(device=dev)
     gen.manual_seed(20250925)
-    # one N(0,1) gradient per table serves every step (1.95 GB for the five)
-    grads = [torch.randn(B, F * sp.dim, device=dev, generator=gen, dtype=torch.float32) for sp in specs]
+
+    def fresh_grad(t):
+        """A new N(0,1) upstream gradient for one step of table t."""
+        return torch.randn(B, F * specs[t].dim, device=dev, generator=gen, dtype=torch.float32)
+
     outs = [torch.empty(B, F * sp.dim, device=dev, dtype=torch.float32) for sp in specs]
     res = [recis.LookupResult(cap, F * B) for _ in range(T)]
     big = T - 1
 
-    def step_table(t, dfs, descs, r):
+    def step_table(t, dfs, descs, r, grad):
         sp = specs[t]
         tables[t].insert_find(dfs, B, r, descs=descs)
         tables[t].forward(r, sp.pool, outs[t])
-        tables[t].backward_update(r, sp.pool, grads[t], sp.grad_dtype, lr=sp.lr, beta1=sp.beta1,
+        tables[t].backward_update(r, sp.pool, grad, sp.grad_dtype, lr=sp.lr, beta1=sp.beta1,
                                   beta2=sp.beta2, eps=sp.eps)
 
     for s in range(nfill):
         for t in range(T):
             dfs, descs, _ = _upload(torch, recis, dev, batches[s * T + t])
-            step_table(t, dfs, descs, res[t])
+            step_table(t, dfs, descs, res[t], fresh_grad(t))
         torch.cuda.synchronize()
-    staged = [_upload(torch, recis, dev, batches[j]) for j in range(nfill * T, (nfill + Wm + K) * T)]
+    # warm-up and timed inputs in HBM, each step with its own gradient
+    staged = [_upload(torch, recis, dev, batches[j]) + (fresh_grad(j % T),)
+              for j in range(nfill * T, (nfill + Wm + K) * T)]
     for w in range(Wm):
         for t in range(T):
-            dfs, descs, _ = staged[w * T + t]
-            step_table(t, dfs, descs, res[t])
+            dfs, descs, _, g = staged[w * T + t]
+            step_table(t, dfs, descs, res[t], g)
     for tb in tables:
         tb.check()
     st0 = [tb.stats() for tb in tables]
@@ -572,10 +597,10 @@ def run_multi(args, wl):
     for k in range(K):
         ev[k][0].record(stream)
         for t in range(T):
-            dfs, descs, _ = staged[(Wm + k) * T + t]
+            dfs, descs, _, g = staged[(Wm + k) * T + t]
             if t == big:
                 tables[t].profile_kernel("k_bwd_short", *kev[k])
-            step_table(t, dfs, descs, timed_res[k] if t == big else res[t])
+            step_table(t, dfs, descs, timed_res[k] if t == big else res[t], g)
             if t == big:
                 tables[t].profile_kernel(None)
             ev[k][t + 1].record(stream)
@@ -677,12 +702,15 @@ def run_cache(args, wl):
     print(json.dumps(result))
 
 
-def main():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="ctr")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None,
+                    help="one workload alone (default: the capacity line, with the tiny, CTR and sequence "
+                         "workloads as extra keys)")
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: the workload's)")
+    ap.add_argument("--no-extras", action="store_true", help="default line: skip the extra workloads")
     ap.add_argument("--resident", type=int, default=RESIDENT_TARGET, help="CTR: rows resident before warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--export-import", action="store_true",
@@ -708,34 +736,30 @@ def main():
     ap.add_argument("--summarize-atomics", metavar="PROF_DIR")
     ap.add_argument("--command", default="")
     ap.add_argument("--out", default=None)
-    args = ap.parse_args()
-    wl = WORKLOADS[args.workload]
-    if args.summarize_atomics:
-        summarize_atomics(args.summarize_atomics, args.command,
-                          args.out or os.path.join(ROOT, "profiles", f"atomics_{args.workload}.txt"), args.workload)
-        return
-    if args.summarize:
-        summarize(args.summarize, args.kernel, args.command,
-                  args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{args.workload}_counters.txt"),
-                  args.workload, args.block_memory)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
-        sys.exit(2)
+    return ap.parse_args(argv)
 
-    if wl.get("special") == "multi":
-        return run_multi(args, wl)
-    if wl.get("special") == "cache":
-        return run_cache(args, wl)
-    K = args.steps if args.steps is not None else wl["steps"]
-    Wm = args.warmup if args.warmup is not None else wl["warmup"]
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
+    """One of the single-table workloads (tiny, ctr, seq, capacity) through K
+    timed steps; returns the result dict.  extra: a shorter run for the extra
+    keys of the default line (no export, eviction or host-memory options)."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    wl = WORKLOADS[name]
+    K = K if K is not None else (args.steps if args.steps is not None and not extra else wl["steps"])
+    Wm = Wm if Wm is not None else (args.warmup if args.warmup is not None and not extra else wl["warmup"])
+    block_memory = "device" if extra else args.block_memory
     spec = wl["spec"]()
     F, B, D = wl["F"], wl["B"], spec.dim
     pooled = spec.pool != "none"
     s_bytes = 2 if spec.dtype == "bf16" else 4
     S = {"adam": 2, "adagrad": 1}[spec.optim]
     gs = 2 if spec.grad_dtype == "bf16" else 4
-    # ---- inputs: generate before the GPU is touched (process pool)
+    # ---- inputs: generated in a process pool (the first call before the GPU is touched)
     t_gen = time.perf_counter()
     if wl["fill"] == "resident":
         fill_steps = int(np.ceil(args.resident / 850_000)) + 4
@@ -743,13 +767,10 @@ def main():
         fill_steps = wl["fill_steps"]
     else:
         fill_steps = 0
-    batches = gen_batches(args.workload, list(range(fill_steps + Wm + K)), args.workers)
+    batches = gen_batches(name, list(range(fill_steps + Wm + K)), args.workers)
     resident_keys = list(W.capacity_resident_keys()) if wl["fill"] == "keys" else []
-    t_gen = time.perf_counter() - t_gen
-    print(f"[bench] {args.workload}: generated {len(batches)} batches in {t_gen:.1f}s", file=sys.stderr, flush=True)
+    log(f"{name}: generated {len(batches)} batches in {time.perf_counter() - t_gen:.1f}s")
 
-    import torch
-    from dynamic_embedding_tables_amd import recis
     recis.load_library()
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
@@ -759,31 +780,29 @@ def main():
         reserve = pre_rows + cap + (Wm + K + 1) * (cap // 30)
     elif wl["fill"] == "resident":  # the fill stops within one step of the target
         reserve = args.resident + (Wm + K + 3) * wl["new_per_step"]
-    else:
+    elif wl["fill"] == "steps":
         reserve = (fill_steps + Wm + K + 2) * wl["new_per_step"]
+    else:
+        reserve = (Wm + K) * cap
     table = recis.Table(D, spec.dtype, spec.optim, seed=spec.seed, init_bound=spec.init_bound,
                         admit_threshold=spec.admit_threshold, reserve_rows=reserve,
-                        block_memory=args.block_memory, track_last_use=args.track_last_use,
-                        admit_sketch_bits=args.admit_sketch_bits, **wl["table"])
+                        block_memory=block_memory, track_last_use=args.track_last_use and not extra,
+                        admit_sketch_bits=0 if extra else args.admit_sketch_bits, **wl["table"])
     gen = torch.Generator(device=dev)
     gen.manual_seed(20250925)
     pdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
     gdt = torch.bfloat16 if spec.grad_dtype == "bf16" else torch.float32
     flags = 0 if pooled else recis.RECIS_GROUP_BY_OCCURRENCE
 
-    shared = {}
-
     def upload(batch):
+        """The batch's IDs and offsets in HBM, and a fresh N(0,1) upstream
+        gradient for its step."""
         feats, bsz = batch
         dfs = [recis.DeviceFeature(torch.from_numpy(v).to(dev), torch.from_numpy(o).to(dev), sl, ops, mod)
                for (v, o, sl, ops, mod) in feats]
         n = sum(f.n for f in dfs)
         shape = (bsz, F * D) if pooled else (n, D)
-        if wl.get("shared_grad") and "g" in shared:
-            grad = shared["g"]
-        else:
-            grad = torch.randn(*shape, device=dev, generator=gen, dtype=torch.float32).to(gdt)
-            shared["g"] = grad
+        grad = torch.randn(*shape, device=dev, generator=gen, dtype=torch.float32).to(gdt)
         return dfs, recis.make_descs(dfs), n, grad
 
     out = torch.empty(B, F * D, device=dev, dtype=torch.float32) if pooled else \
@@ -821,9 +840,10 @@ def main():
             if wl["fill"] == "resident" and table.stats().rows_in_use >= args.resident:
                 break
     resident0 = table.stats().rows_in_use
-    print(f"[bench] fill: {i} steps, {resident0} resident rows", file=sys.stderr, flush=True)
+    log(f"{name} fill: {i} steps, {resident0} resident rows")
 
     # ---- stage warm-up + timed inputs in HBM
+    first_timed = i + Wm
     staged = [upload(batches[j]) for j in range(i, i + Wm + K)]
     timed_res = [recis.LookupResult(cap, F * B) for _ in range(K)]
     stream = torch.cuda.current_stream()
@@ -840,14 +860,16 @@ def main():
     probe_ms = {}
     for w in range(Wm):
         dfs, descs, n, grad = staged[w]
-        name = cands[w % len(cands)]
-        a, b = event_pair()
-        table.profile_kernel(name, a, b)
+        name_k = cands[w % len(cands)] if cands else None
+        if name_k:
+            a, b = event_pair()
+            table.profile_kernel(name_k, a, b)
         step(dfs, descs, grad, res_pool[w % 2])
         torch.cuda.synchronize()
-        probe_ms.setdefault(name, []).append(a.elapsed_time(b))
+        if name_k:
+            probe_ms.setdefault(name_k, []).append(a.elapsed_time(b))
     table.profile_kernel(None)
-    dom = max(probe_ms, key=lambda k: np.mean(probe_ms[k])) if probe_ms else "k_bwd_short"
+    dom = max(probe_ms, key=lambda k: np.mean(probe_ms[k])) if probe_ms else None
     table.check()
     st0 = table.stats()
 
@@ -859,7 +881,8 @@ def main():
         dfs, descs, n, grad = staged[Wm + k]
         res = timed_res[k]
         e = ev[k]
-        table.profile_kernel(dom, *kev[k])
+        if dom:
+            table.profile_kernel(dom, *kev[k])
         e[0].record(stream)
         table.insert_find(dfs, B, res, flags=flags, descs=descs)
         e[1].record(stream)
@@ -872,8 +895,8 @@ def main():
     table.profile_kernel(None)
     table.check()
     st1 = table.stats()
-    t_dom = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e-3
-    if args.copy_calibration:
+    t_dom = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e-3 if dom else None
+    if args.copy_calibration and not extra:
         copy_calibration(torch, dev)
 
     ids = sum(staged[Wm + k][2] for k in range(K))
@@ -898,7 +921,9 @@ def main():
     a_bytes = alg[dom] if dom in alg else None
     achieved = a_bytes / t_dom / 1e9 if a_bytes else None
     step_bytes = alg["step"]
-    traffic = read_traffic(dom, args.workload)
+    traffic = read_traffic(dom, name) if dom else None
+    claims = (st1.claim_attempts - st0.claim_attempts) / K
+    lost = (st1.claim_failures - st0.claim_failures) / K
 
     result = {
         "metric": "lookup+pool+update IDs/sec and achieved HBM GB/s vs peak, 1xMI355X",
@@ -923,23 +948,28 @@ def main():
         "step_breakdown_ms": {"insert_find": t_ins * 1e3, "lookup_pool_fwd": t_fwd * 1e3,
                               "pool_bwd_update": t_bwd * 1e3},
         "step_ms_median_p90": [float(np.median(t_steps)), float(np.percentile(t_steps, 90))],
-        "step_algorithmic_bytes": step_bytes,
-        "step_achieved_GBps": step_bytes / (elapsed / K) / 1e9,
-        "roofline": {"bound": "hbm", "kernel": dom, "kernel_ms": t_dom * 1e3,
-                     "algorithmic_bytes": a_bytes, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
-                     "traffic": traffic} if args.block_memory == "device" else
-        # rows in host memory: the dominant kernel against the host link, in
-        # the direction that carries more of its row bytes
-        {"bound": "host-link", "kernel": dom, "kernel_ms": t_dom * 1e3,
-         "link_bytes_read_written": list(link_bytes(dom, shape, Uhit, D, s_bytes, S)),
-         "achieved": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9,
-         "peak": LINK_PEAK_GBS, "unit": "GB/s",
-         "frac": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9 / LINK_PEAK_GBS,
-         "traffic": None},
+        # the whole step against the HBM roofline: the step's algorithmic bytes
+        # over the wall-clock time per step
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": step_bytes,
+                          "achieved": step_bytes / (elapsed / K) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": step_bytes / (elapsed / K) / 1e9 / HBM_PEAK_GBS},
+        "idmap_claims_per_step": {"attempts": claims, "lost": lost,
+                                  "attempts_per_s": claims / (elapsed / K)},
+        "roofline": ({"bound": "hbm", "kernel": dom, "kernel_ms": t_dom * 1e3,
+                      "algorithmic_bytes": a_bytes, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
+                      "traffic": traffic} if block_memory == "device" else
+                     # rows in host memory: the dominant kernel against the host link, in
+                     # the direction that carries more of its row bytes
+                     {"bound": "host-link", "kernel": dom, "kernel_ms": t_dom * 1e3,
+                      "link_bytes_read_written": list(link_bytes(dom, shape, Uhit, D, s_bytes, S)),
+                      "achieved": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9,
+                      "peak": LINK_PEAK_GBS, "unit": "GB/s",
+                      "frac": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9 / LINK_PEAK_GBS,
+                      "traffic": None}) if dom else None,
         "warmup_kernel_ms": {k: float(np.mean(v)) for k, v in probe_ms.items()},
-        # every kernel timed in the warm-up (one launch each), against the same
-        # algorithmic bytes as the roofline above
+        # every kernel timed in the warm-up, against the same algorithmic
+        # bytes as the roofline above
         "kernel_rooflines": {k: {"ms": float(np.mean(v)), "algorithmic_bytes": alg.get(k),
                                  "GBps": alg[k] / (np.mean(v) * 1e-3) / 1e9 if alg.get(k) else None,
                                  "frac": alg[k] / (np.mean(v) * 1e-3) / 1e9 / HBM_PEAK_GBS
@@ -947,25 +977,103 @@ def main():
                              for k, v in probe_ms.items()},
         "backward_key_split": shape,
     }
-    if args.export_import:
-        result["export_import"] = export_import(torch, recis, table, spec, wl, D, s_bytes, S, args.block_memory)
-    if args.track_last_use:
-        result["config"]["track_last_use"] = True
-    if args.admit_sketch_bits:
-        result["config"]["admit_sketch_bits"] = args.admit_sketch_bits
-    if args.evict_pass:
+    if not extra:
+        if args.export_import:
+            result["export_import"] = export_import(torch, recis, table, spec, wl, D, s_bytes, S, block_memory)
         if args.track_last_use:
-            result["evict_lru_pass"] = evict_lru_pass(torch, table)
-        result["evict_pass"] = evict_pass(torch, table)
-    if args.block_memory == "host":
-        result["config"]["block_memory"] = "host (pinned, mapped; IDMap and scratch in HBM)"
-        result["host_link_copy_GBps"] = host_link_copy(torch, dev)
-    if args.workload == "ctr" and args.block_memory == "device" and not args.no_cpu_baseline:
-        table.close()
-        torch.cuda.synchronize()
-        result["cpu_baseline"] = cpu_baseline()
+            result["config"]["track_last_use"] = True
+        if args.admit_sketch_bits:
+            result["config"]["admit_sketch_bits"] = args.admit_sketch_bits
+        if args.evict_pass:
+            if args.track_last_use:
+                result["evict_lru_pass"] = evict_lru_pass(torch, table)
+            result["evict_pass"] = evict_pass(torch, table)
+        if block_memory == "host":
+            result["config"]["block_memory"] = "host (pinned, mapped; IDMap and scratch in HBM)"
+            result["host_link_copy_GBps"] = host_link_copy(torch, dev)
+    cpu_src = None
+    if cpu and block_memory == "device" and not args.no_cpu_baseline:
+        # the timed steps' inputs and gradients, kept for the oracle
+        nf = wl.get("cpu_features")
+        cpu_src = ([batches[j] for j in range(first_timed, first_timed + K)],
+                   [staged[Wm + k][3] for k in range(K)], nf)
+    table.close()
+    del staged, timed_res, res_pool, out
+    torch.cuda.synchronize()
+    if cpu_src is not None:
+        timed, grads, nf = cpu_src
+
+        def host_grad(g):
+            def cols(nfe):
+                x = g[:, :nfe * D] if pooled and nf is not None else g
+                if spec.grad_dtype == "bf16":
+                    return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                return x.contiguous().cpu().numpy()
+            return cols
+        result["cpu_baseline"] = cpu_baseline(spec, timed, [host_grad(g) for g in grads], nf,
+                                              what=name)
         ncpu, model = host_info()
         result["cpu_baseline"]["host"] = f"{ncpu} logical CPUs, {model}"
+    return result
+
+
+def run_tiny(args):
+    """Config 1: ten steps from an empty table, each timed alone (HIP events
+    around the step); the figure is the step latency (launch-bound)."""
+    r = run_standard("tiny", args, K=10, Wm=0, cpu=False, extra=True)
+    return {"ms_per_step_median": r["step_ms_median_p90"][0], "ms_per_step_p90": r["step_ms_median_p90"][1],
+            "ids_per_step": r["config"]["ids_per_step"], "value": r["value"], "unit": "IDs/s",
+            "step_breakdown_ms": r["step_breakdown_ms"], "workload": r["config"]["workload"]}
+
+
+def brief(r):
+    """The extra-key form of a workload's result line."""
+    return {"workload": r["config"]["workload"], "value": r["value"], "unit": r["unit"],
+            "ms_per_step": r["ms_per_step"], "steps": r["steps"], "ids_per_step": r["config"]["ids_per_step"],
+            "step_breakdown_ms": r["step_breakdown_ms"], "step_roofline": r["step_roofline"],
+            "roofline": r["roofline"], "kernel_rooflines": r["kernel_rooflines"]}
+
+
+def main():
+    args = parse_args()
+    if args.summarize_atomics:
+        w = args.workload or "capacity"
+        summarize_atomics(args.summarize_atomics, args.command,
+                          args.out or os.path.join(ROOT, "profiles", f"atomics_{w}.txt"), w)
+        return
+    if args.summarize:
+        w = args.workload or "capacity"
+        summarize(args.summarize, args.kernel, args.command,
+                  args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{w}_counters.txt"),
+                  w, args.block_memory)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    if args.workload is not None:
+        wl = WORKLOADS[args.workload]
+        if wl.get("special") == "multi":
+            return run_multi(args, wl)
+        if wl.get("special") == "cache":
+            return run_cache(args, wl)
+        if args.workload == "tiny":
+            print(json.dumps(run_tiny(args)))
+            return
+        print(json.dumps(run_standard(args.workload, args)))
+        return
+    # the default line: the capacity configuration (the largest that fits one
+    # GPU); then the tiny, CTR and sequence configurations as extra keys
+    result = run_standard("capacity", args)
+    result["config"]["workload_id"] = "capacity (config 4 of 5)"
+    if not args.no_extras:
+        extras = {}
+        extras["tiny"] = run_tiny(args)
+        log("tiny done")
+        extras["ctr"] = brief(run_standard("ctr", args, K=10, Wm=5, cpu=False, extra=True))
+        log("ctr done")
+        extras["seq"] = brief(run_standard("seq", args, K=10, Wm=5, cpu=False, extra=True))
+        log("seq done")
+        result["other_configs"] = extras
     print(json.dumps(result))
 
 

@@ -30,6 +30,9 @@ constexpr long long kGoneKey = -3;   // evicted, awaiting rebuild
 constexpr int kPendingRow = 1 << 30;               // in Slot.row
 constexpr long long kFreshRow = 1ll << 62;         // in unique_rows: row may be pending
 constexpr long long kMaxRows = (1ll << 30) - 1;
+// IDMap slot indices are kept in 32 bits with 0xFFFFFFFF meaning "no slot":
+// the IDMap never grows past 2^31 slots, so no real index reaches the mark.
+constexpr long long kMaxSlots = 1ll << 31;
 
 constexpr unsigned kErrInvalid = 1u << RECIS_ERR_INVALID_ARG;
 constexpr unsigned kErrCapacity = 1u << RECIS_ERR_CAPACITY;
@@ -101,6 +104,11 @@ struct DevCounters {
   long long free_top_old;
   long long bump_base;
   unsigned long long scratch_count;  // writeback distinct keys / export count / evicted
+  // IDMap slot claims made by insert_find since creation: attempts, and
+  // those that lost the slot to another key (summed per bucket, added by
+  // the scan kernel once per call)
+  unsigned long long claim_attempts;
+  unsigned long long claim_failures;
 };
 
 // Device view of one feature of a call.
@@ -359,6 +367,11 @@ struct recis_table {
   // bumped by every call that writes rows or frees them (update, writeback,
   // eviction); a lookup result records the value it was made at
   unsigned long long update_epoch = 1;
+  // bumped by every call that can change which key holds which IDMap slot or
+  // row: a counting insert_find (inserts, admissions, growth), writeback,
+  // import and eviction.  A lookup result records the value after its own
+  // insert_find; forward and backward re-probe its keys when it differs.
+  unsigned long long map_version = 1;
 
   recis::KernelProbe probe;
 
@@ -445,6 +458,7 @@ struct LookupLaunch {
   int* posmap;                // N: position of each occurrence's record in part
   unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
   unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
+  unsigned long long* blk_claim; // per key tile: IDMap slot claims << 32 | claims lost
   int* klist;                    // N: heavy buckets' distinct keys (dedup-table slots), by bucket range
   int* hslice;                   // heavy slices: count, then (bucket, slice) pairs
   long long hmax;                // bound on the heavy slices of the call (their grids)
@@ -453,6 +467,12 @@ struct LookupLaunch {
   int sketching;                 // count-min admission in this (counting) call
 };
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s);
+// Re-probes every distinct key of a lookup (find only): its IDMap slot and
+// row as the table holds them now, for a lookup made before the IDMap last
+// changed (later inserts, growth, writeback, import or eviction).
+void launch_refresh(const recis_lookup_result& res, const TableDev& t, hipStream_t s);
+// Clears `bits` of the device error word.
+void launch_clear_error(DevCounters* ctr, unsigned bits, hipStream_t s);
 
 // `current`: no update, writeback or eviction ran on the table since the
 // lookup, so its fresh marks and per-occurrence row references still hold

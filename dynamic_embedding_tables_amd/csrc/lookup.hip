@@ -551,9 +551,10 @@ __device__ __forceinline__ void key_outputs(const LookupLaunch& L, long long u, 
   // the key's last use (tables that keep it; counting calls only)
   if (L.last_use && o.sl != 0xFFFFFFFFu) L.last_use[o.sl] = L.step;
   sum += ((unsigned long long)o.need << 32) | (unsigned)o.ins;
-  // a key that will have a row and more than kShortMax occurrences is reduced
-  // in chunks by the backward
-  if (c > kShortMax && (o.need || o.row >= 0)) sum_long += (1ull << 32) | (unsigned)long_chunks(c);
+  // a key with more than kShortMax occurrences is reduced in chunks by the
+  // backward (also one without a row now: a later lookup may give it one
+  // before this lookup's backward runs, which then re-probes its keys)
+  if (c > kShortMax) sum_long += (1ull << 32) | (unsigned)long_chunks(c);
 }
 
 // A bucket whose distinct keys overflow the LDS table (only inputs built to
@@ -595,7 +596,8 @@ __device__ __forceinline__ void put_out(const LookupLaunch& L, long long p, long
 
 template <bool EMIT>
 __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, int& s_nd, int& s_cursor,
-                              unsigned long long& s_sum, unsigned long long& s_sum_long) {
+                              unsigned long long& s_sum, unsigned long long& s_sum_long,
+                              unsigned long long& s_claims) {
   const int tid = threadIdx.x;
   const int s = L.bbase[b], m = L.bbase[b + 1] - s;
   DedupSlot* R = L.dd + 2ll * s;
@@ -606,6 +608,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     s_cursor = 0;
     s_sum = 0;
     s_sum_long = 0;
+    s_claims = 0;
   }
   __syncthreads();
   if (!EMIT) {
@@ -637,7 +640,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
   }
   const long long ub = L.ubase[b];
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
-  unsigned long long sum = 0, sum_long = 0;
+  unsigned long long sum = 0, sum_long = 0, claims = 0;
   unsigned err = 0;
   for (unsigned long long h = tid; h < cap; h += kThreads) {
     const long long key = ld_key(&R[h]);
@@ -651,8 +654,10 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     st_int(&R[h].uidx, (int)u);
     // an empty IDMap slot goes to whichever thread's CAS takes it
     auto claim = [&](unsigned long long q) {
-      return atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
-                       (unsigned long long)key) == (unsigned long long)kEmptyKey;
+      const bool won = atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
+                                 (unsigned long long)key) == (unsigned long long)kEmptyKey;
+      claims += (1ull << 32) | (won ? 0u : 1u);
+      return won;
     };
     const ProbeOut po = idmap_probe(t, key, c, find_only, claim, L.sketching != 0);
     err |= po.err;
@@ -661,10 +666,12 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
   if (err) atomicOr(&t.ctr->error, err);
   if (sum) atomicAdd(&s_sum, sum);
   if (sum_long) atomicAdd(&s_sum_long, sum_long);
+  if (claims) atomicAdd(&s_claims, claims);
   __syncthreads();
   if (tid == 0) {
     L.blk_sums[b] = s_sum;
     L.blk_long[b] = s_sum_long;
+    L.blk_claim[b] = s_claims;
   }
   for (int i = tid; i < m; i += kThreads) {
     const PartEntry e = L.part[s + i];
@@ -769,7 +776,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   __shared__ unsigned s_claim[EMIT ? TAB : 1];  // IDMap slots taken by this block (~0u: free)
   __shared__ unsigned short s_list[kMaxDistinct];
   __shared__ int s_nd, s_over, s_cursor;
-  __shared__ unsigned long long s_sum, s_sum_long;
+  __shared__ unsigned long long s_sum, s_sum_long, s_claims;
   __shared__ unsigned s_err;
   const int tid = threadIdx.x;
   // the bits below the bucket bits index the table
@@ -822,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   if (m == 0) {
     if (tid == 0) {
       if (!EMIT) L.ubase[b] = 0;
-      else L.blk_sums[b] = L.blk_long[b] = 0;
+      else L.blk_sums[b] = L.blk_long[b] = L.blk_claim[b] = 0;
     }
     return;
   }
@@ -832,11 +839,12 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     const long long ub = L.ubase[b], nd = L.ubase[b + 1] - ub;
     const DedupSlot* R = L.dd + 2ll * s;
     const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
-    unsigned long long sum = 0, sum_long = 0, run = 0;
+    unsigned long long sum = 0, sum_long = 0, run = 0, claims = 0;
     unsigned err = 0;
     if (tid == 0) {
       s_sum = 0;
       s_sum_long = 0;
+      s_claims = 0;
       s_err = 0;
     }
     __syncthreads();
@@ -860,8 +868,10 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
       L.res.unique_offsets[u] = (int)(s + o);
       // an empty IDMap slot goes to whichever thread's CAS takes it
       auto claim = [&](unsigned long long q) {
-        return atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
-                         (unsigned long long)key) == (unsigned long long)kEmptyKey;
+        const bool won = atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
+                                   (unsigned long long)key) == (unsigned long long)kEmptyKey;
+        claims += (1ull << 32) | (won ? 0u : 1u);
+        return won;
       };
       const ProbeOut po = idmap_probe(t, key, c, find_only, claim, L.sketching != 0);
       err |= po.err;
@@ -870,10 +880,12 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     if (err) atomicOr(&s_err, err);
     if (sum) atomicAdd(&s_sum, sum);
     if (sum_long) atomicAdd(&s_sum_long, sum_long);
+    if (claims) atomicAdd(&s_claims, claims);
     __syncthreads();
     if (tid == 0) {
       L.blk_sums[b] = s_sum;
       L.blk_long[b] = s_sum_long;
+      L.blk_claim[b] = s_claims;
       if (s_err) atomicOr(&t.ctr->error, s_err);
     }
     return;
@@ -889,6 +901,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     s_cursor = 0;
     s_sum = 0;
     s_sum_long = 0;
+    s_claims = 0;
     s_err = 0;
   }
   __syncthreads();
@@ -930,7 +943,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   }
   __syncthreads();
   if (s_over) {  // rare: colliding inputs only
-    bucket_global<EMIT>(L, t, b, s_nd, s_cursor, s_sum, s_sum_long);
+    bucket_global<EMIT>(L, t, b, s_nd, s_cursor, s_sum, s_sum_long, s_claims);
     return;
   }
   if (!EMIT) {
@@ -945,14 +958,19 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   // an empty IDMap slot goes to the first thread that enters it in the set
   // (slot indices are below 2^32; the last index of a 2^32-slot table, equal
   // to the set's free mark, is never handed out)
+  unsigned long long claims = 0;  // attempts << 32 | lost
   auto claim = [&](unsigned long long p) {
     const unsigned v = (unsigned)p;
     if (v == ~0u) return false;
+    claims += 1ull << 32;
     unsigned h = (unsigned)((p * 0x9E3779B97F4A7C15ull) >> (64 - kTabBits));
     for (int n = 0; n < TAB; ++n) {
       const unsigned o = atomicCAS(&s_claim[h], ~0u, v);
       if (o == ~0u) return true;
-      if (o == v) return false;
+      if (o == v) {
+        claims += 1;
+        return false;
+      }
       h = (h + 1) & (TAB - 1);
     }
     return false;  // not reached: fewer claims than kMaxDistinct
@@ -978,10 +996,12 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   if (err) atomicOr(&s_err, err);
   if (sum) atomicAdd(&s_sum, sum);
   if (sum_long) atomicAdd(&s_sum_long, sum_long);
+  if (claims) atomicAdd(&s_claims, claims);
   __syncthreads();
   if (tid == 0) {
     L.blk_sums[b] = s_sum;
     L.blk_long[b] = s_sum_long;
+    L.blk_claim[b] = s_claims;
     if (s_err) atomicOr(&t.ctr->error, s_err);
   }
   for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
@@ -1149,7 +1169,23 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
   const long long nblk = L.N > 0 ? L.nbk : 0;  // per-bucket sums
   unsigned long long all, all_long;
   scan_two(L.blk_sums, L.blk_long, nblk, &all, &all_long);
+  // IDMap slot claims of the call (attempts << 32 | lost), summed over the
+  // buckets; each bucket's figures fit 32 bits, the call's total 64
+  __shared__ unsigned long long s_cl[2];
+  if (threadIdx.x == 0) s_cl[0] = s_cl[1] = 0;
+  __syncthreads();
+  unsigned long long ca = 0, cf = 0;
+  for (long long b = threadIdx.x; b < nblk; b += kScanThreads) {
+    const unsigned long long v = L.blk_claim[b];
+    ca += v >> 32;
+    cf += v & 0xFFFFFFFFull;
+  }
+  if (ca) atomicAdd(&s_cl[0], ca);
+  if (cf) atomicAdd(&s_cl[1], cf);
+  __syncthreads();
   if (threadIdx.x == 0) {
+    t.ctr->claim_attempts += s_cl[0];
+    t.ctr->claim_failures += s_cl[1];
     const long long R = (long long)(all >> 32);
     const long long Fr = t.ctr->free_top > 0 ? t.ctr->free_top : 0;
     const long long take = R < Fr ? R : Fr;
@@ -1198,7 +1234,7 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
       mark = L.res.unique_rows[u];
     }
     const unsigned long long acc = valid ? ((unsigned long long)(mark == -2) << 32) : 0ull;
-    const bool is_long = valid && cnt > kShortMax && mark != -1;  // as k_bucket counted it
+    const bool is_long = valid && cnt > kShortMax;  // as k_bucket counted it
     const int nch = long_chunks(cnt);
     const unsigned long long acc_long = is_long ? ((1ull << 32) | (unsigned long long)nch) : 0ull;
     unsigned long long total, total_long;
@@ -1294,7 +1330,38 @@ __global__ __launch_bounds__(kThreads) void k_occ_out(LookupLaunch L) {
   }
 }
 
+// A lookup made before the IDMap last changed: each distinct key is probed
+// again (find only, no count) and its IDMap slot and row entry rewritten as
+// the table holds them now -- a key evicted since gets no slot and row -1, a
+// key admitted since gets its row, and a row still pending is reported with
+// the fresh mark, as insert_find reports it.
+__global__ __launch_bounds__(kThreads) void k_refresh(recis_lookup_result res, TableDev t) {
+  const long long U = *res.num_unique;
+  unsigned* idslot = reinterpret_cast<unsigned*>(res.plan + plan_layout(res.capacity).o_idslot);
+  for (long long u = (long long)blockIdx.x * kThreads + threadIdx.x; u < U; u += (long long)gridDim.x * kThreads) {
+    const long long key = res.unique_keys[u];
+    const ProbeOut o = idmap_probe(t, key, 0, true, [](unsigned long long) { return false; });
+    idslot[u] = o.sl;
+    res.unique_rows[u] = o.row;
+  }
+}
+
+__global__ void k_clear_error(DevCounters* ctr, unsigned bits) {
+  if (threadIdx.x == 0) atomicAnd(&ctr->error, ~bits);
+}
+
 }  // namespace
+
+void launch_refresh(const recis_lookup_result& res, const TableDev& t, hipStream_t s) {
+  // a grid for the largest call; blocks past the distinct count exit at once
+  long long nb = (res.n + kThreads - 1) / kThreads;
+  nb = nb < 1 ? 1 : (nb > 8192 ? 8192 : nb);
+  RECIS_LAUNCH("k_refresh", k_refresh, dim3((unsigned)nb), dim3(kThreads), s, res, t);
+}
+
+void launch_clear_error(DevCounters* ctr, unsigned bits, hipStream_t s) {
+  RECIS_LAUNCH("k_clear_error", k_clear_error, dim3(1), dim3(64), s, ctr, bits);
+}
 
 void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
   const long long nb = (long long)L.F * L.B + 1;

@@ -214,7 +214,7 @@ recis_status ensure_capacity(recis_table* t, long long n, hipStream_t s) {
     long long cap = t->slot_cap;
     while ((long long)(t->cfg.max_load * (double)cap) < t->keys_hi + n) cap *= 2;
     if (cap != t->slot_cap) {
-      if (cap > (1ll << 32)) return RECIS_ERR_CAPACITY;
+      if (cap > kMaxSlots) return RECIS_ERR_CAPACITY;
       st = rebuild_idmap(t, cap, s);
       if (st != RECIS_OK) return st;
     }
@@ -264,7 +264,7 @@ ScratchSizes scratch_sizes(long long cap, int dim) {
   z.bbase = (size_t)(kMaxBuckets + 1) * 4 * 2;  // bbase, then ubase
   z.uslot = (size_t)cap * 4;
   z.posmap = (size_t)cap * 4;
-  z.blk = (size_t)(kMaxBuckets + 2) * 8 * 2;  // per-bucket sums: blk_sums, then blk_long
+  z.blk = (size_t)(kMaxBuckets + 2) * 8 * 3;  // per-bucket sums: blk_sums, blk_long, blk_claim
   z.wb = (size_t)cap * 8;
   z.partials = (size_t)plan_layout(cap).max_chunks * (size_t)dim * 8;
   return z;
@@ -406,7 +406,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   if (cfg->optim < RECIS_OPTIM_NONE || cfg->optim > RECIS_OPTIM_ADAM) return RECIS_ERR_INVALID_ARG;
   if (!(cfg->max_load > 0.f && cfg->max_load <= 0.75f)) return RECIS_ERR_INVALID_ARG;
   if (!std::isfinite(cfg->init_bound) || cfg->init_bound < 0.f) return RECIS_ERR_INVALID_ARG;
-  if (cfg->slot_capacity < 1 || cfg->slot_capacity > (1ll << 32)) return RECIS_ERR_INVALID_ARG;
+  if (cfg->slot_capacity < 1 || cfg->slot_capacity > kMaxSlots) return RECIS_ERR_INVALID_ARG;
   if (cfg->block_rows < 1 || cfg->block_rows > (1ll << 30)) return RECIS_ERR_INVALID_ARG;
   if (cfg->max_rows < 1 || cfg->max_rows > kMaxRows) return RECIS_ERR_INVALID_ARG;
   if (cfg->reserve_rows < 0) return RECIS_ERR_INVALID_ARG;
@@ -555,6 +555,8 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   res->batch = batch;
   res->flags = flags;
   res->epoch = t->update_epoch;
+  if (!(flags & RECIS_FIND_ONLY)) t->map_version += 1;  // inserts, admissions, growth
+  res->map_version = t->map_version;
 
   LookupLaunch L;
   L.feats = static_cast<const FeatDev*>(dev);
@@ -578,6 +580,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.posmap = t->posmap;
   L.blk_sums = t->blk_sums;
   L.blk_long = t->blk_sums + (kMaxBuckets + 2);
+  L.blk_claim = t->blk_sums + 2 * (kMaxBuckets + 2);
   // heavy-bucket bookkeeping lives in the writeback scratch (the two never
   // share a call): the distinct-key list in uslot (N ints), the slice list in
   // wb_keys (2 N ints)
@@ -599,12 +602,14 @@ recis_status recis_idmap_evict_decay(recis_table* t, uint32_t min_count, double 
   ScopedDevice sd(t->device);
   ScopedProbe sp(t);
   t->update_epoch += 1;
+  t->map_version += 1;
   if (t->sketch) launch_zero_u32(t->sketch, (long long)kSketchRows << t->cfg.admit_sketch_bits, s);
   launch_evict(t->dev(), min_count, decay, reinterpret_cast<long long*>(num_evicted), s);
   recis_status st = check_launch();
   if (st != RECIS_OK) return st;
   st = rebuild_idmap(t, t->slot_cap, s);
   if (st != RECIS_OK) return st;
+  launch_clear_error(t->ctr, kErrCapacity, s);  // the pass may have made room
   DevCounters c;
   st = read_counters(t, &c, s);
   if (st != RECIS_OK) return st;
@@ -626,12 +631,14 @@ recis_status recis_idmap_evict_lru(recis_table* t, int64_t max_keys, int64_t* nu
   int* work = static_cast<int*>(tab_alloc(t, wbytes, s));
   if (!work) return RECIS_ERR_OUT_OF_MEMORY;
   t->update_epoch += 1;
+  t->map_version += 1;
   if (t->sketch) launch_zero_u32(t->sketch, (long long)kSketchRows << t->cfg.admit_sketch_bits, s);
   launch_evict_lru(t->dev(), max_keys, work, reinterpret_cast<long long*>(num_evicted), s);
   recis_status st = check_launch();
   if (st == RECIS_OK) st = rebuild_idmap(t, t->slot_cap, s);  // synchronises: work is idle after
   tab_free(t, work, wbytes, s);
   if (st != RECIS_OK) return st;
+  launch_clear_error(t->ctr, kErrCapacity, s);  // the pass may have made room
   DevCounters c;
   st = read_counters(t, &c, s);
   if (st != RECIS_OK) return st;
@@ -649,7 +656,9 @@ recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_resu
   if (res->n > res->capacity || res->n < 0) return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
   ScopedProbe sp(t);
-  launch_forward(*res, t->dev(), pool, out, res->epoch == t->update_epoch, s);
+  const bool moved = res->map_version != t->map_version;
+  if (moved && res->n > 0) launch_refresh(*res, t->dev(), s);
+  launch_forward(*res, t->dev(), pool, out, !moved && res->epoch == t->update_epoch, s);
   return check_launch();
 }
 
@@ -685,7 +694,9 @@ recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* re
     recis_status st = ensure_scratch(t, res->n, s);
     if (st != RECIS_OK) return st;
   }
-  const bool current = res->epoch == t->update_epoch;
+  const bool moved = res->map_version != t->map_version;
+  if (moved && res->n > 0) launch_refresh(*res, t->dev(), s);
+  const bool current = !moved && res->epoch == t->update_epoch;
   t->update_epoch += 1;
   // the writeback scratch (2 ints per occurrence) is free during a backward
   recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, t->partials,
@@ -703,6 +714,7 @@ recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, con
   st = ensure_capacity(t, n, s);
   if (st != RECIS_OK) return st;
   t->update_epoch += 1;
+  t->map_version += 1;
   launch_writeback(t->dev(), reinterpret_cast<const long long*>(keys), n, rows, t->dd,
                    (unsigned long long)(t->dd_cap - 1), 64 - log2_exact(t->dd_cap), t->wb_keys, t->uslot, s);
   return check_launch();
@@ -727,6 +739,7 @@ recis_status recis_idmap_import(recis_table* t, int64_t n, const int64_t* keys, 
   recis_status st = ensure_capacity(t, n, s);
   if (st != RECIS_OK) return st;
   t->update_epoch += 1;
+  t->map_version += 1;
   t->adam_step = adam_step;
   launch_import(t->dev(), n, reinterpret_cast<const long long*>(keys), reinterpret_cast<const long long*>(rows),
                 counts, params, t->state_words > 0 ? state : nullptr, s);
@@ -791,6 +804,9 @@ recis_status recis_idmap_stats(recis_table* t, recis_table_stats* out, hipStream
   out->slot_capacity = t->slot_cap;
   out->adam_step = t->adam_step;
   out->bytes = t->bytes;
+  out->probationary_keys = out->keys - out->rows_in_use;
+  out->claim_attempts = (int64_t)c.claim_attempts;
+  out->claim_failures = (int64_t)c.claim_failures;
   return RECIS_OK;
 }
 
@@ -801,14 +817,16 @@ recis_status recis_get_error(recis_table* t, hipStream_t s) {
   HIP_TRY(hipStreamSynchronize(s));
   unsigned err = 0;
   HIP_TRY(hipMemcpy(&err, &t->ctr->error, sizeof(err), hipMemcpyDeviceToHost));
-  if (err) {
-    unsigned zero = 0;
-    HIP_TRY(hipMemcpy(&t->ctr->error, &zero, sizeof(zero), hipMemcpyHostToDevice));
+  // One error per call.  KEY_RANGE and INVALID_ARG are cleared as they are
+  // returned, and come first, so that a standing CAPACITY never hides them;
+  // CAPACITY stays until an eviction pass clears it.
+  const unsigned bit = (err & kErrKeyRange) ? kErrKeyRange : ((err & kErrInvalid) ? kErrInvalid : 0u);
+  if (bit) {
+    const unsigned keep = err & ~bit;
+    HIP_TRY(hipMemcpy(&t->ctr->error, &keep, sizeof(keep), hipMemcpyHostToDevice));
+    return bit == kErrKeyRange ? RECIS_ERR_KEY_RANGE : RECIS_ERR_INVALID_ARG;
   }
-  if (err & kErrCapacity) return RECIS_ERR_CAPACITY;
-  if (err & kErrKeyRange) return RECIS_ERR_KEY_RANGE;
-  if (err & kErrInvalid) return RECIS_ERR_INVALID_ARG;
-  return RECIS_OK;
+  return (err & kErrCapacity) ? RECIS_ERR_CAPACITY : RECIS_OK;
 }
 
 recis_status recis_profile_kernel(recis_table* t, const char* kernel, hipEvent_t start, hipEvent_t stop) {

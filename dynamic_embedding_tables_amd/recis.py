@@ -80,7 +80,8 @@ class recis_lookup_result(C.Structure):
                 ("counts", C.c_void_p), ("bag_offsets", C.c_void_p), ("num_unique", C.c_void_p),
                 ("unique_offsets", C.c_void_p), ("grouped", C.c_void_p), ("plan", C.c_void_p),
                 ("capacity", C.c_int64), ("bag_capacity", C.c_int64), ("n", C.c_int64), ("num_feats", C.c_int32),
-                ("batch", C.c_int32), ("flags", C.c_uint32), ("epoch", C.c_uint64)]
+                ("batch", C.c_int32), ("flags", C.c_uint32), ("epoch", C.c_uint64),
+                ("map_version", C.c_uint64)]
 
 
 class recis_optim_params(C.Structure):
@@ -90,7 +91,8 @@ class recis_optim_params(C.Structure):
 class recis_table_stats(C.Structure):
     _fields_ = [("keys", C.c_int64), ("rows_in_use", C.c_int64), ("rows_allocated", C.c_int64),
                 ("blocks", C.c_int64), ("slot_capacity", C.c_int64), ("adam_step", C.c_int64),
-                ("bytes", C.c_int64)]
+                ("bytes", C.c_int64), ("probationary_keys", C.c_int64), ("claim_attempts", C.c_int64),
+                ("claim_failures", C.c_int64)]
 
 
 class RecisError(RuntimeError):
@@ -115,7 +117,7 @@ def load_library() -> C.CDLL:
     L.recis_table_config_default.restype = None
     L.recis_plan_words.argtypes = [i64]
     L.recis_plan_words.restype = i64
-    L.recis_idmap_create.argtypes = [C.POINTER(recis_table_config), p, p, C.POINTER(p)]
+    L.recis_idmap_create.argtypes = [C.POINTER(recis_table_config), C.POINTER(recis_allocator), p, C.POINTER(p)]
     L.recis_idmap_destroy.argtypes = [p]
     L.recis_idmap_insert_find.argtypes = [p, C.POINTER(recis_feature_desc), i32, i32, u32,
                                           C.POINTER(recis_lookup_result), p]
@@ -175,9 +177,53 @@ def recis_plan_words(capacity: int) -> int:
     return int(load_library().recis_plan_words(capacity))
 
 
-def recis_idmap_create(cfg: recis_table_config, stream=None) -> C.c_void_p:
+# ------------------------------------------------ allocator bridge to torch
+# The table's device memory (IDMap, EmbeddingBlocks, scratch) comes from
+# torch's caching allocator through these two callbacks, so the library never
+# calls hipMalloc when torch drives it and torch's memory statistics include
+# the table.  A block is tied to the stream of the call that asked for it;
+# the library frees memory only after that stream's work on it has finished.
+_ALLOC_FN = C.CFUNCTYPE(C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p)
+_FREE_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p, C.c_void_p)
+_allocator_calls = {"alloc": 0, "free": 0}
+
+
+def _torch_alloc(ctx, nbytes, stream):
+    try:
+        import torch
+        p = torch.cuda.caching_allocator_alloc(int(nbytes), stream=int(stream or 0))
+        _allocator_calls["alloc"] += 1
+        return p
+    except Exception:  # out of memory (or torch unusable): the library sees NULL
+        return None
+
+
+def _torch_free(ctx, p, stream):
+    try:
+        import torch
+        torch.cuda.caching_allocator_delete(int(p))
+        _allocator_calls["free"] += 1
+    except Exception:  # interpreter shutdown: the process is ending anyway
+        pass
+
+
+_torch_alloc_c = _ALLOC_FN(_torch_alloc)
+_torch_free_c = _FREE_FN(_torch_free)
+TORCH_ALLOCATOR = recis_allocator(None, C.cast(_torch_alloc_c, C.c_void_p), C.cast(_torch_free_c, C.c_void_p))
+
+
+def allocator_calls() -> dict:
+    """Calls made through the torch allocator bridge so far (alloc, free)."""
+    return dict(_allocator_calls)
+
+
+def recis_idmap_create(cfg: recis_table_config, stream=None, allocator: Optional[recis_allocator] = None
+                       ) -> C.c_void_p:
+    """allocator: a recis_allocator (e.g. TORCH_ALLOCATOR), or None for the
+    library's own hipMalloc / hipFree."""
     h = C.c_void_p()
-    _check(load_library().recis_idmap_create(C.byref(cfg), None, _stream(stream), C.byref(h)),
+    a = C.byref(allocator) if allocator is not None else None
+    _check(load_library().recis_idmap_create(C.byref(cfg), a, _stream(stream), C.byref(h)),
            "recis_idmap_create")
     return h
 
@@ -285,7 +331,7 @@ class LookupResult:
             self.unique_keys.data_ptr(), self.unique_rows.data_ptr(), self.inverse.data_ptr(),
             self.counts.data_ptr(), self.bag_offsets.data_ptr(), self.num_unique.data_ptr(),
             self.unique_offsets.data_ptr(), self.grouped.data_ptr(), self.plan.data_ptr(),
-            cap, max(int(nbags), 0), 0, 0, 0, 0, 0)
+            cap, max(int(nbags), 0), 0, 0, 0, 0, 0, 0)
         self.capacity = cap
         self.nbags = nbags
 
@@ -336,7 +382,7 @@ class Table:
                  init_bound: float = 0.05, admit_threshold: int = 1, slot_capacity: int = 1 << 20,
                  block_rows: int = 1 << 20, max_rows: int = (1 << 30) - 1, reserve_rows: int = 0,
                  max_load: float = 0.5, block_memory: str = "device", track_last_use: bool = False,
-                 admit_sketch_bits: int = 0, stream=None):
+                 admit_sketch_bits: int = 0, stream=None, allocator: str = "torch"):
         cfg = recis_table_config_default()
         cfg.dim, cfg.dtype, cfg.optim = dim, DTYPES[dtype], OPTIMS[optim]
         cfg.seed, cfg.init_bound, cfg.admit_threshold = seed, init_bound, admit_threshold
@@ -349,7 +395,10 @@ class Table:
         self.config = {"seed": seed, "init_bound": init_bound, "admit_threshold": admit_threshold,
                        "block_memory": block_memory, "track_last_use": bool(track_last_use),
                        "admit_sketch_bits": int(admit_sketch_bits)}
-        self.h = recis_idmap_create(cfg, stream)
+        if allocator not in ("torch", "hip"):
+            raise ValueError("allocator is 'torch' (torch's caching allocator) or 'hip' (hipMalloc)")
+        self.allocator = allocator
+        self.h = recis_idmap_create(cfg, stream, TORCH_ALLOCATOR if allocator == "torch" else None)
 
     def close(self):
         if getattr(self, "h", None):

@@ -181,7 +181,15 @@ typedef struct {
   uint64_t epoch;          /* the table's update count at the lookup: while no update,
                               writeback or eviction has run since, forward and
                               backward use the lookup's row references directly;
-                              otherwise they re-read the IDMap */
+                              otherwise they re-read each key's IDMap slot */
+  uint64_t map_version;    /* the table's IDMap version after this lookup.  Every call
+                              that can move a key to another slot or give it another
+                              row bumps it: a counting insert_find (inserts, admissions,
+                              growth), writeback, import and every eviction pass.  When
+                              it differs at forward / backward, the call first re-probes
+                              each distinct key (find only) and rewrites unique_rows and
+                              the plan's per-key slots: a stale lookup then computes on
+                              the rows its keys hold now (a key evicted since has none) */
 } recis_lookup_result;
 
 /* int32 words needed by recis_lookup_result.plan for `capacity` occurrences. */
@@ -201,6 +209,14 @@ typedef struct {
   int64_t slot_capacity;
   int64_t adam_step;
   int64_t bytes;          /* device bytes owned by the table (host blocks not included) */
+  int64_t probationary_keys; /* keys in the IDMap without a row: admission has not
+                                given them one yet (keys - rows_in_use) */
+  int64_t claim_attempts; /* empty IDMap slots insert_find has tried to claim for a new
+                             key since creation (a compare-and-swap: in the bucket's
+                             shared-memory claim set, or on the slot itself for
+                             overflowed and hot buckets) */
+  int64_t claim_failures; /* of those, claims that found the slot already taken by
+                             another key of the same call (the probe then moves on) */
 } recis_table_stats;
 
 /* Creates a table.  Allocates the IDMap and `reserve_rows` worth of blocks

@@ -156,12 +156,42 @@ def check_forward(out_gpu, spec, oracle_out, oracle_abs, merged_offsets=None, nu
     assert not bad.any(), f"{bad.sum()} pooled elements off; worst {np.max(err - bound)}"
 
 
-def gpu_step(table, spec, batch, res, find_only=False, with_backward=True):
-    """insert_find -> forward -> backward+update on the current stream."""
+def check_gather_is_copy(out_gpu, table, res, spec):
+    """POOL_NONE: every output row is bit for bit the row the table itself
+    holds for that occurrence's key (its export, read between the forward and
+    the backward), zeros for a key without a row."""
+    import torch
+    ex = table.export()
+    ekeys = ex["keys"].cpu().numpy()
+    order = np.argsort(ekeys, kind="stable")
+    ekeys = ekeys[order]
+    erows = ex["rows"].cpu().numpy()[order]
+    p = ex["params"]
+    eparams = (p.view(torch.int16).cpu().numpy().view(np.uint16) if p.dtype == torch.bfloat16
+               else p.cpu().numpy().view(np.uint32))[order]
+    g = out_gpu[:res.n]
+    g = g.view(torch.int16).cpu().numpy().view(np.uint16) if g.dtype == torch.bfloat16 else g.cpu().numpy().view(np.uint32)
+    U = res.U()
+    occ_keys = res.unique_keys[:U].cpu().numpy()[res.inverse[:res.n].cpu().numpy()]
+    pos = np.searchsorted(ekeys, occ_keys)
+    pos_c = np.minimum(pos, max(ekeys.size - 1, 0))
+    found = (pos < ekeys.size) & (ekeys[pos_c] == occ_keys) if ekeys.size else np.zeros(occ_keys.size, bool)
+    has = np.zeros(occ_keys.size, bool)
+    has[found] = erows[pos_c[found]] >= 0
+    want = np.zeros_like(g)
+    want[has] = eparams[pos_c[has]]
+    np.testing.assert_array_equal(g, want)
+
+
+def gpu_step(table, spec, batch, res, find_only=False, with_backward=True, after_forward=None):
+    """insert_find -> forward -> backward+update on the current stream;
+    after_forward(out) runs between the forward and the backward."""
     feats = device_features(batch)
     table.insert_find(feats, batch.batch, res, flags=lookup_flags(spec, find_only))
     out = forward_out(spec, batch, res)
     table.forward(res, spec.pool, out)
+    if after_forward is not None:
+        after_forward(out)
     if with_backward and spec.optim != "none":
         g, _ = device_grad(batch, spec)
         table.backward_update(res, spec.pool, g, spec.grad_dtype, lr=spec.lr, beta1=spec.beta1,

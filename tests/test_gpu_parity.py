@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads as W
-from harness import (canon_export, canon_lookup, check_export, check_forward, check_lookup,
+from harness import (canon_export, canon_lookup, check_export, check_forward, check_gather_is_copy, check_lookup,
                      device_features, forward_out, gpu_step, lookup_flags, make_table, oracle_step)
 
 pytestmark = pytest.mark.gpu
@@ -50,7 +50,9 @@ def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopu
         print(f"[parity] step {step} N={b.n}", flush=True)
         res = recis.LookupResult(max(b.n, 1), b.num_feats * b.batch)
         fo = step in find_only_steps
-        out, _ = gpu_step(table, spec, b, res, find_only=fo, with_backward=not fo)
+        # a gather is a copy: its rows are the table's own, bit for bit
+        copy_check = (lambda out: check_gather_is_copy(out, table, res, spec)) if spec.pool == "none" else None
+        out, _ = gpu_step(table, spec, b, res, find_only=fo, with_backward=not fo, after_forward=copy_check)
         r, oout, oab = oracle_step(otab, spec, b, find_only=fo, with_backward=not fo)
         torch.cuda.synchronize()
         assert table.get_error() == 0
@@ -229,6 +231,102 @@ def test_multi_table_full_size_with_eviction():
     run_parity(spec, [W.multi_batch(s, 0) for s in range(3)], evict_every=2, export_every=2)
 
 
+def lookup_by_feature(res):
+    """Host copies of a full-size lookup's distinct keys, counts, inverse and
+    merged offsets, for per-feature checks."""
+    U = res.U()
+    return {"keys": res.unique_keys[:U].cpu().numpy(), "counts": res.counts[:U].cpu().numpy(),
+            "rows": res.unique_rows[:U].cpu().numpy(), "inverse": res.inverse[:res.n].cpu().numpy(),
+            "offsets": res.bag_offsets.cpu().numpy()}
+
+
+def check_feature_lookup(look, batch, f, r, sub=None):
+    """Feature f of a merged lookup against the oracle's lookup of a sub-batch
+    of features (`sub`: their indices in `batch`, default [f]); keys carry the
+    feature's slot, so they are the same keys: each of f's occurrences' key,
+    its distinct keys with their counts and row presence, and its bags'
+    merged offsets -- all bit-exact."""
+    sub = [f] if sub is None else list(sub)
+    k = sub.index(f)
+    base = sum(batch.features[x].n for x in range(f))
+    sbase = sum(batch.features[x].n for x in sub[:k])
+    n_f = batch.features[f].n
+    B = batch.batch
+    np.testing.assert_array_equal(look["keys"][look["inverse"][base:base + n_f]],
+                                  r.unique_keys[r.inverse[sbase:sbase + n_f]])
+    slot = batch.features[f].slot
+    sel = (look["keys"] >> 48) == slot
+    kg, cg, rg = look["keys"][sel], look["counts"][sel], look["rows"][sel]
+    order = np.argsort(kg, kind="stable")
+    osel = (r.unique_keys[:r.U] >> 48) == slot
+    np.testing.assert_array_equal(kg[order], r.unique_keys[:r.U][osel])
+    np.testing.assert_array_equal(cg[order], r.counts[:r.U][osel])
+    np.testing.assert_array_equal(rg[order] >= 0, r.unique_rows[:r.U][osel] >= 0)
+    np.testing.assert_array_equal(look["offsets"][f * B:(f + 1) * B + 1] - base,
+                                  r.merged_offsets[k * B:(k + 1) * B + 1] - sbase)
+
+
+def canon_export_slots(table, slots):
+    """canon_export restricted on the device to the keys of the given feature
+    slots (a full-size table is too large to copy whole)."""
+    import torch
+    ex = table.export()
+    sl = torch.bitwise_right_shift(ex["keys"], 48)
+    m = torch.zeros_like(sl, dtype=torch.bool)
+    for x in slots:
+        m |= sl == x
+    keys = ex["keys"][m].cpu().numpy()
+    order = np.argsort(keys, kind="stable")
+    params = ex["params"][m]
+    params = params.float() if params.dtype == torch.bfloat16 else params
+    return {"keys": keys[order], "rows": ex["rows"][m].cpu().numpy()[order],
+            "counts": ex["counts"][m].cpu().numpy().astype(np.uint32)[order],
+            "params": params.cpu().numpy()[order], "state": ex["state"][m].cpu().numpy()[order]}
+
+
+@pytest.mark.timeout(900)
+def test_multi_table_dim128_full_size_with_eviction():
+    """The dim-128 table of the multi-table config at full size (32768 x 60
+    features, 7.9M IDs per step, mean pooling, Adagrad, a row at the 2nd
+    occurrence), three steps with an eviction pass (count < 2) after the
+    second.  Keys carry their feature's slot, so the oracle recomputes two
+    whole features: their lookups, pooled outputs, and after every step the
+    keys, counts, row presence, parameters and state of every key of theirs
+    the table holds."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_multi(4)
+    D = spec.dim
+    checked = (0, 41)
+    table = make_table(spec, slot_capacity=1 << 24, block_rows=1 << 20, reserve_rows=1 << 23)
+    otab = oracle.OracleTable(spec)
+    try:
+        for step in range(3):
+            b = W.multi_batch(step, 4)
+            print(f"[multi128] step {step} N={b.n}", flush=True)
+            res = recis.LookupResult(b.n, b.num_feats * b.batch)
+            out, _ = gpu_step(table, spec, b, res)
+            sub = W.Batch([b.features[f] for f in checked], b.batch,
+                          np.ascontiguousarray(np.concatenate([b.grad[:, f * D:(f + 1) * D] for f in checked], 1)))
+            r, o_out, o_abs = oracle_step(otab, spec, sub)
+            torch.cuda.synchronize()
+            assert table.get_error() == 0
+            look = lookup_by_feature(res)
+            for k, f in enumerate(checked):
+                check_feature_lookup(look, b, f, r, sub=checked)
+                cols, ocols = slice(f * D, (f + 1) * D), slice(k * D, (k + 1) * D)
+                check_forward(out[:, cols].contiguous(), spec, np.ascontiguousarray(o_out[:, ocols]),
+                              np.ascontiguousarray(o_abs[:, ocols]),
+                              r.merged_offsets[k * b.batch:(k + 1) * b.batch + 1], 1, exact=step == 0)
+            if step == 1:
+                ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+                table.evict(2, ne)
+                assert int(ne.item()) >= otab.evict(2) > 0
+            check_export(canon_export_slots(table, checked), otab.export(), spec)
+    finally:
+        table.close()
+
+
 @pytest.mark.timeout(900)
 def test_capacity_full_size_two_features_checked():
     """The capacity configuration at full size, laid out as the benchmark's
@@ -261,11 +359,13 @@ def test_capacity_full_size_two_features_checked():
         out, _ = gpu_step(table, spec, b, res)
         torch.cuda.synchronize()
         assert table.get_error() == 0
+        look = lookup_by_feature(res)
         for f in (0, 77):
             cols = slice(f * D, (f + 1) * D)
             sub = W.Batch([b.features[f]], b.batch, np.ascontiguousarray(b.grad[:, cols]))
             otab = oracle.OracleTable(spec)
             r, o_out, o_abs = oracle_step(otab, spec, sub)
+            check_feature_lookup(look, b, f, r)
             check_forward(out[:, cols].contiguous(), spec, o_out, o_abs, r.merged_offsets, 1, exact=True)
             ex = otab.export()
             ids = ex["keys"] & ((1 << 48) - 1)
@@ -562,6 +662,162 @@ def test_interleaved_lookups(optim):
         check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
     check_export(canon_export(table), otab.export(), spec)
     table.close()
+
+
+def _stale_pair(spec, table, otab, a, b, between):
+    """Lookup A; `between` (GPU, oracle) runs; lookup B; then A's forward and
+    backward, then B's -- each checked against the oracle, whose forward and
+    backward act on the rows the keys hold when they run."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    ra = recis.LookupResult(a.n, a.num_feats * a.batch)
+    rb = recis.LookupResult(b.n, b.num_feats * b.batch)
+    table.insert_find(device_features(a), a.batch, ra)
+    oa = otab.insert_find(a.features, a.batch)
+    between()
+    table.insert_find(device_features(b), b.batch, rb)
+    ob = otab.insert_find(b.features, b.batch)
+    torch.cuda.synchronize()
+    assert table.get_error() == 0
+    check_lookup(canon_lookup(rb), ob)
+    for batch, res, r in ((a, ra, oa), (b, rb, ob)):
+        out = forward_out(spec, batch, res)
+        table.forward(res, spec.pool, out)
+        g = torch.from_numpy(batch.grad).cuda()
+        table.backward_update(res, spec.pool, g, "f32", lr=spec.lr, beta1=spec.beta1, beta2=spec.beta2,
+                              eps=spec.eps)
+        oout, oab = otab.forward(r, spec.pool, with_abs=True)
+        assert otab.backward_update(r, spec.pool, batch.grad) == 0
+        torch.cuda.synchronize()
+        assert table.get_error() == 0
+        check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats)
+        check_export(canon_export(table), otab.export(), spec)
+    st = table.stats()
+    assert st.keys == otab.size() and st.rows_in_use == otab.rows_in_use()
+
+
+@pytest.mark.parametrize("optim", ["adagrad", "adam"])
+def test_interleaved_lookups_across_idmap_growth(optim):
+    """Lookup A on a 64-slot IDMap, then lookup B, which grows it (every key
+    moves to a new slot): A's forward and backward must find A's keys at their
+    new slots, not write through the old slot indices."""
+    spec = W.TableSpec(dim=32, dtype="f32", optim=optim, pool="mean", lr=1e-3 if optim == "adam" else 0.01,
+                       eps=1e-8 if optim == "adam" else 1e-10)
+    table = make_table(spec, slot_capacity=64, block_rows=64)
+    otab = oracle.OracleTable(spec)
+    a = W.ctr_batch(0, batch=40, num_feats=2, dim=32)
+    b = W.ctr_batch(1, batch=300, num_feats=3, dim=32)
+    slots0 = table.stats().slot_capacity
+    _stale_pair(spec, table, otab, a, b, lambda: None)
+    assert table.stats().slot_capacity > slots0
+    table.close()
+
+
+@pytest.mark.parametrize("admit", [1, 2])
+def test_eviction_between_a_lookup_and_its_backward(admit):
+    """Lookup A; an eviction pass (A's once-seen keys leave and free their
+    rows); lookup B (new keys take the freed rows); then A's forward and
+    backward: the evicted keys get zeros and no update, and the rows now held
+    by B's keys are not touched by A's gradient."""
+    import torch
+    spec = W.TableSpec(dim=16, dtype="f32", optim="adagrad", pool="sum", lr=0.01, eps=1e-10, admit_threshold=admit)
+    table = make_table(spec, slot_capacity=1 << 12, block_rows=256)
+    otab = oracle.OracleTable(spec)
+    a = W.tiny_batch(0, id_space=3000)
+    b = W.tiny_batch(1, id_space=3000)
+
+    def evict():
+        ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+        table.evict(2, ne)
+        assert int(ne.item()) == otab.evict(2) > 0
+
+    _stale_pair(spec, table, otab, a, b, evict)
+    table.close()
+
+
+def test_capacity_error_is_sticky_until_an_eviction_pass():
+    """A row limit reached on the device: CAPACITY stays reported (while
+    KEY_RANGE, read and cleared, still comes through first) until an eviction
+    pass makes room."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_tiny()
+    table = make_table(spec, max_rows=100, block_rows=64)
+    b = W.tiny_batch(0, id_space=100000)
+    res = recis.LookupResult(b.n, b.batch)
+    table.insert_find(device_features(b), b.batch, res)
+    torch.cuda.synchronize()
+    assert table.get_error() == recis.RECIS_ERR_CAPACITY
+    assert table.get_error() == recis.RECIS_ERR_CAPACITY
+    bad = W.Batch([W.FeatureInput(values=np.array([-4], np.int64), bag_offsets=np.array([0, 1], np.int32),
+                                  slot=0)], 1, np.ones((1, 16), np.float32))
+    r2 = recis.LookupResult(1, 1)
+    table.insert_find(device_features(bad), 1, r2)
+    assert table.get_error() == recis.RECIS_ERR_KEY_RANGE
+    assert table.get_error() == recis.RECIS_ERR_CAPACITY
+    st = table.stats()
+    assert st.rows_in_use == 100 and st.probationary_keys == st.keys - 100 > 0
+    ne = torch.zeros(1, dtype=torch.int64, device="cuda")
+    table.evict(2, ne)
+    assert int(ne.item()) > 0
+    assert table.get_error() == 0
+    table.close()
+
+
+def test_stats_count_idmap_claims():
+    """Every key a counting lookup inserts claims one empty IDMap slot: the
+    claim attempts are at least the inserted keys, and a FIND_ONLY lookup
+    adds none."""
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_ctr()
+    table = make_table(spec)
+    b = W.ctr_batch(0, batch=512, num_feats=4)
+    res = recis.LookupResult(b.n, b.num_feats * b.batch)
+    table.insert_find(device_features(b), b.batch, res)
+    torch.cuda.synchronize()
+    st = table.stats()
+    assert st.keys == res.U() and st.probationary_keys == 0
+    assert st.claim_attempts >= st.keys and 0 <= st.claim_failures <= st.claim_attempts - st.keys
+    table.insert_find(device_features(b), b.batch, res, flags=recis.RECIS_FIND_ONLY)
+    st2 = table.stats()
+    assert st2.claim_attempts == st.claim_attempts and st2.claim_failures == st.claim_failures
+    table.close()
+
+
+def test_torch_allocator_bridge():
+    """A table created through the torch allocator bridge takes all its device
+    memory from torch's caching allocator (and gives it back at close), and
+    computes what a table on the library's own hipMalloc computes."""
+    import gc
+    import torch
+    from dynamic_embedding_tables_amd import recis
+    spec = W.spec_ctr()
+    gc.collect()
+    torch.cuda.synchronize()
+    before = recis.allocator_calls()
+    mem0 = torch.cuda.memory_allocated()
+    t_torch = make_table(spec, allocator="torch", reserve_rows=5000)
+    assert recis.allocator_calls()["alloc"] > before["alloc"]
+    assert torch.cuda.memory_allocated() - mem0 >= t_torch.stats().bytes
+    t_hip = make_table(spec, allocator="hip", reserve_rows=5000)
+    outs = []
+    for t in (t_torch, t_hip):
+        for s in range(2):
+            b = W.ctr_batch(s, batch=128, num_feats=3)
+            res = recis.LookupResult(b.n, b.num_feats * b.batch)
+            out, _ = gpu_step(t, spec, b, res)
+        torch.cuda.synchronize()
+        assert t.get_error() == 0
+        outs.append((out.cpu(), canon_export(t)))
+    assert torch.equal(outs[0][0], outs[1][0])
+    for k in ("keys", "counts", "params", "state"):
+        np.testing.assert_array_equal(outs[0][1][k], outs[1][1][k])
+    t_torch.close()
+    t_hip.close()
+    after = recis.allocator_calls()
+    # everything the table took through the bridge went back through it
+    assert after["alloc"] - before["alloc"] == after["free"] - before["free"] > 0
 
 
 def test_one_key_dominates():
