@@ -788,7 +788,8 @@ def test_stats_count_idmap_claims():
 def test_torch_allocator_bridge():
     """A table created through the torch allocator bridge takes all its device
     memory from torch's caching allocator (and gives it back at close), and
-    computes what a table on the library's own hipMalloc computes."""
+    computes what a table on the library's own hipMalloc computes (to the
+    parity bar)."""
     import gc
     import torch
     from dynamic_embedding_tables_amd import recis
@@ -810,9 +811,11 @@ def test_torch_allocator_bridge():
         torch.cuda.synchronize()
         assert t.get_error() == 0
         outs.append((out.cpu(), canon_export(t)))
-    assert torch.equal(outs[0][0], outs[1][0])
-    for k in ("keys", "counts", "params", "state"):
-        np.testing.assert_array_equal(outs[0][1][k], outs[1][1][k])
+    # the same keys, counts and rows; values to the parity bar (a key's
+    # occurrences are grouped in an order that can differ from run to run, and
+    # double sums in another order can round differently)
+    np.testing.assert_allclose(outs[0][0].numpy(), outs[1][0].numpy(), rtol=1e-5, atol=1e-7)
+    check_export(outs[0][1], outs[1][1], spec)
     t_torch.close()
     t_hip.close()
     after = recis.allocator_calls()
