@@ -29,9 +29,39 @@
 // launch: a block stages the metadata and gradient references of 256
 // consecutive keys in LDS, then each group of KL lanes reduces and updates
 // one key at a time with all of the key's loads in flight together.
+#include <mutex>
+
 #include "internal.h"
 
 namespace recis {
+
+// ------------------------------------------- allocation-free backward scratch
+// The long keys' chunk partials of recis_pool_bwd_update_noalloc.  Host code
+// never passes the array's name to a kernel (in host code it is a stand-in,
+// not a device address): it passes the address hipGetSymbolAddress gives for
+// the current device, looked up once per device and kept.
+static __device__ __align__(256) double scratch[kNoAllocScratchBytes / sizeof(double)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+recis_status noalloc_scratch(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return RECIS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return RECIS_ERR_HIP;
+    }
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return RECIS_OK;
+}
 
 namespace {
 

@@ -490,6 +490,13 @@ recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, 
                              double* partials, int* reorder, long long reorder_ints, bool current,
                              hipStream_t s);
 
+// The fixed device scratch of the allocation-free backward: the long keys'
+// chunk partials, kNoAllocScratchBytes on each GPU the library runs it on,
+// held until the process ends and shared by every such call on that GPU.
+constexpr long long kNoAllocScratchBytes = 64ll << 20;
+// Its address on `device` (which must be current), looked up once per device.
+recis_status noalloc_scratch(int device, void** out);
+
 void launch_evict(const TableDev& t, unsigned min_count, double decay, long long* num_evicted, hipStream_t s);
 // LRU-bounded pass: keeps the youngest ages whole within max_keys; `work`
 // holds age_hist_words(slot_cap) ints of device scratch.

@@ -662,19 +662,48 @@ recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_resu
   return check_launch();
 }
 
-recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* res, int32_t pool,
-                                   const void* grad_out, int32_t grad_dtype, const recis_optim_params* opt,
-                                   hipStream_t s) {
+namespace {
+
+// The backward of both entry points.  noalloc: the long keys' chunk partials
+// go to the library's fixed device scratch instead of the table's (grown on
+// demand), and the long keys keep the lookup's order (the feature-ordered
+// plan needs scratch of its own; the order changes no sum).
+recis_status pool_bwd_update(recis_table* t, const recis_lookup_result* res, int32_t pool, const void* grad_out,
+                             int32_t grad_dtype, const recis_optim_params* opt, hipStream_t s, bool noalloc) {
   if (!t || !res || !opt) return RECIS_ERR_INVALID_ARG;
   if (pool != RECIS_POOL_SUM && pool != RECIS_POOL_MEAN && pool != RECIS_POOL_NONE) return RECIS_ERR_INVALID_ARG;
   if (grad_dtype != RECIS_DTYPE_F32 && grad_dtype != RECIS_DTYPE_BF16) return RECIS_ERR_INVALID_ARG;
   const bool by_occ = (res->flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
   if ((pool == RECIS_POOL_NONE) != by_occ) return RECIS_ERR_INVALID_ARG;
+  if (res->n < 0 || res->n > res->capacity) return RECIS_ERR_INVALID_ARG;
   if (res->n > 0 && !grad_out) return RECIS_ERR_INVALID_ARG;
   if (t->cfg.optim == RECIS_OPTIM_NONE) return RECIS_ERR_UNSUPPORTED;
   if (!(opt->lr >= 0.0) || !(opt->eps >= 0.0)) return RECIS_ERR_INVALID_ARG;
+  const bool adam = t->cfg.optim == RECIS_OPTIM_ADAM;
+  if (adam && !(opt->beta1 >= 0.0 && opt->beta1 < 1.0 && opt->beta2 >= 0.0 && opt->beta2 < 1.0))
+    return RECIS_ERR_INVALID_ARG;
   ScopedDevice sd(t->device);
   ScopedProbe sp(t);
+  double* partials = t->partials;
+  int* reorder = reinterpret_cast<int*>(t->wb_keys);  // the writeback scratch is free during a backward
+  long long reorder_ints = 2 * t->scr_cap;
+  if (noalloc) {
+    // every chunk partial the call can have: max_chunks(n) rows of dim doubles
+    const long long need = plan_layout(res->n).max_chunks * (long long)t->cfg.dim * (long long)sizeof(double);
+    if (need > kNoAllocScratchBytes) return RECIS_ERR_INVALID_ARG;
+    void* p = nullptr;
+    recis_status st = noalloc_scratch(t->device, &p);
+    if (st != RECIS_OK) return st;
+    partials = static_cast<double*>(p);
+    reorder = nullptr;
+    reorder_ints = 0;
+  } else if (res->n > t->scr_cap) {
+    recis_status st = ensure_scratch(t, res->n, s);
+    if (st != RECIS_OK) return st;
+    partials = t->partials;
+    reorder = reinterpret_cast<int*>(t->wb_keys);
+    reorder_ints = 2 * t->scr_cap;
+  }
   OptConsts oc;
   oc.lr = (float)opt->lr;
   oc.eps = (float)opt->eps;
@@ -683,27 +712,36 @@ recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* re
   oc.omb1 = (float)(1.0 - opt->beta1);
   oc.omb2 = (float)(1.0 - opt->beta2);
   oc.step_size = 0.f;
-  if (t->cfg.optim == RECIS_OPTIM_ADAM) {
-    if (!(opt->beta1 >= 0.0 && opt->beta1 < 1.0 && opt->beta2 >= 0.0 && opt->beta2 < 1.0))
-      return RECIS_ERR_INVALID_ARG;
+  if (adam) {
     t->adam_step += 1;
     const double n = (double)t->adam_step;
     oc.step_size = (float)(opt->lr * std::sqrt(1.0 - std::pow(opt->beta2, n)) / (1.0 - std::pow(opt->beta1, n)));
-  }
-  if (res->n > t->scr_cap) {
-    recis_status st = ensure_scratch(t, res->n, s);
-    if (st != RECIS_OK) return st;
   }
   const bool moved = res->map_version != t->map_version;
   if (moved && res->n > 0) launch_refresh(*res, t->dev(), s);
   const bool current = !moved && res->epoch == t->update_epoch;
   t->update_epoch += 1;
-  // the writeback scratch (2 ints per occurrence) is free during a backward
-  recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, t->partials,
-                                    reinterpret_cast<int*>(t->wb_keys), 2 * t->scr_cap, current, s);
+  recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, partials, reorder, reorder_ints,
+                                    current, s);
   if (st != RECIS_OK) return st;
   return check_launch();
 }
+
+}  // namespace
+
+recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* res, int32_t pool,
+                                   const void* grad_out, int32_t grad_dtype, const recis_optim_params* opt,
+                                   hipStream_t s) {
+  return pool_bwd_update(t, res, pool, grad_out, grad_dtype, opt, s, false);
+}
+
+recis_status recis_pool_bwd_update_noalloc(recis_table* t, const recis_lookup_result* res, int32_t pool,
+                                           const void* grad_out, int32_t grad_dtype,
+                                           const recis_optim_params* opt, hipStream_t s) {
+  return pool_bwd_update(t, res, pool, grad_out, grad_dtype, opt, s, true);
+}
+
+int64_t recis_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, const float* rows, hipStream_t s) {
   if (!t || n < 0 || (n > 0 && (!keys || !rows)) || n > (1ll << 30)) return RECIS_ERR_INVALID_ARG;

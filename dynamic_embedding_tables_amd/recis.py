@@ -50,7 +50,7 @@ EXPORTED_SYMBOLS = (
     "recis_table_config_default", "recis_plan_words", "recis_idmap_create", "recis_idmap_destroy",
     "recis_idmap_insert_find", "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru",
     "recis_lookup_pool_fwd",
-    "recis_pool_bwd_update",
+    "recis_pool_bwd_update", "recis_pool_bwd_update_noalloc", "recis_noalloc_scratch_bytes",
     "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_key_ages", "recis_idmap_sketch",
     "recis_idmap_stats", "recis_get_error",
     "recis_status_string", "recis_profile_kernel",
@@ -127,6 +127,10 @@ def load_library() -> C.CDLL:
     L.recis_lookup_pool_fwd.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, p]
     L.recis_pool_bwd_update.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, i32,
                                         C.POINTER(recis_optim_params), p]
+    L.recis_pool_bwd_update_noalloc.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, i32,
+                                                C.POINTER(recis_optim_params), p]
+    L.recis_noalloc_scratch_bytes.argtypes = []
+    L.recis_noalloc_scratch_bytes.restype = i64
     L.recis_writeback.argtypes = [p, p, i64, p, p]
     L.recis_idmap_export.argtypes = [p, i64, p, p, p, p, p, C.POINTER(i64), p]
     L.recis_idmap_import.argtypes = [p, i64, p, p, p, p, p, i64, p]
@@ -139,7 +143,7 @@ def load_library() -> C.CDLL:
     L.recis_status_string.restype = C.c_char_p
     for name in ("recis_idmap_create", "recis_idmap_destroy", "recis_idmap_insert_find",
                  "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru", "recis_lookup_pool_fwd",
-                 "recis_pool_bwd_update",
+                 "recis_pool_bwd_update", "recis_pool_bwd_update_noalloc",
                  "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_key_ages",
                  "recis_idmap_sketch", "recis_idmap_stats", "recis_get_error"):
         getattr(L, name).restype = i32
@@ -262,6 +266,17 @@ def recis_pool_bwd_update(h, res: recis_lookup_result, pool: int, grad, grad_dty
                           opt: recis_optim_params, stream=None):
     _check(load_library().recis_pool_bwd_update(h, C.byref(res), pool, _ptr(grad), grad_dtype,
                                                 C.byref(opt), _stream(stream)), "recis_pool_bwd_update")
+
+
+def recis_pool_bwd_update_noalloc(h, res: recis_lookup_result, pool: int, grad, grad_dtype: int,
+                                  opt: recis_optim_params, stream=None):
+    _check(load_library().recis_pool_bwd_update_noalloc(h, C.byref(res), pool, _ptr(grad), grad_dtype,
+                                                        C.byref(opt), _stream(stream)),
+           "recis_pool_bwd_update_noalloc")
+
+
+def recis_noalloc_scratch_bytes() -> int:
+    return int(load_library().recis_noalloc_scratch_bytes())
 
 
 def recis_profile_kernel(h, kernel: Optional[str], start=None, stop=None):
@@ -423,9 +438,12 @@ class Table:
 
     def backward_update(self, res: LookupResult, pool: str, grad, grad_dtype: str = "f32",
                         lr: float = 0.01, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-10,
-                        stream=None):
+                        stream=None, noalloc: bool = False):
+        """noalloc: the allocation-free entry point (fixed scratch; see
+        recis_pool_bwd_update_noalloc)."""
         opt = recis_optim_params(lr, beta1, beta2, eps)
-        recis_pool_bwd_update(self.h, res.c, POOLS[pool], grad, DTYPES[grad_dtype], opt, stream)
+        fn = recis_pool_bwd_update_noalloc if noalloc else recis_pool_bwd_update
+        fn(self.h, res.c, POOLS[pool], grad, DTYPES[grad_dtype], opt, stream)
 
     def evict(self, min_count: int, num_evicted=None, stream=None, decay: float = 0.0):
         """Eviction pass; survivors keep floor(count * decay) (0: restart)."""

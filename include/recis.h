@@ -291,6 +291,27 @@ recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* re
                                    const void* grad_out, int32_t grad_dtype,
                                    const recis_optim_params* opt, hipStream_t s);
 
+/* Allocation-free backward + update, for callers that cannot allocate device
+ * memory while they run: code under HIP graph capture, tight training or
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, results and
+ * errors as recis_pool_bwd_update, through the same kernels, but it calls no
+ * allocator at all (neither hipMalloc nor the table's).  Its one scratch
+ * buffer -- the long keys' double-precision chunk partials -- is a fixed array
+ * of recis_noalloc_scratch_bytes() bytes (64 MiB) of device memory, one per
+ * GPU, held until the process ends.  A call whose partials could exceed it
+ * (at most n/32 + 2 chunks of dim doubles for n occurrences, about
+ * n * dim / 4 bytes) returns RECIS_ERR_INVALID_ARG at once, before any work
+ * (at dim 64: up to about 4.1M occurrences).  Every call on one GPU shares
+ * the array, and each chunk's partial is written before it is read, so
+ * nothing needs clearing between calls; calls that overlap on one GPU (other
+ * streams, other tables) race on it and give undefined results. */
+recis_status recis_pool_bwd_update_noalloc(recis_table* t, const recis_lookup_result* res, int32_t pool,
+                                           const void* grad_out, int32_t grad_dtype,
+                                           const recis_optim_params* opt, hipStream_t s);
+
+/* Bytes of the fixed scratch array of recis_pool_bwd_update_noalloc. */
+int64_t recis_noalloc_scratch_bytes(void);
+
 /* Exact-assignment writeback: for i in order, row(keys[i]) <- rows[i] rounded
  * to the storage dtype, so the last occurrence of a repeated key wins.  An
  * absent key is inserted and given a row at once; counts are not touched.
