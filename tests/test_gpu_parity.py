@@ -887,6 +887,41 @@ def test_long_keys_by_feature_large_gradient():
     run_parity(spec, batches, export_every=2)
 
 
+@pytest.mark.parametrize("pool,admit", [("sum", 1), ("mean", 2)])
+def test_long_keys_extremes_large_gradient(pool, admit):
+    """A pooled gradient larger than the memory-side cache (the long keys'
+    plan rebuilt feature by feature) with one key of about 160k occurrences
+    (past 64 x 1024 entries, so its chunks grow to 192), hot keys of 700 to
+    2800 occurrences, long keys of about 150 and a cold tail, in 4 features
+    of 270k bags, with empty bags for sum pooling; two steps."""
+    spec = W.TableSpec(dim=64, dtype="f32", optim="adam", pool=pool, lr=1e-3, eps=1e-8, admit_threshold=admit)
+    B, F = 270_000, 4
+    batches = []
+    for step in range(2):
+        rng = W.rng_for(98, step)
+        feats = []
+        for f in range(F):
+            lens = rng.integers(0 if pool == "sum" else 1, 5, B)
+            off = W.offsets_from_lengths(lens)
+            n = int(off[-1])
+            r = rng.random(n)
+            vals = rng.integers(100_000, 5_000_000, n)                          # cold tail
+            vals = np.where(r < 0.35, rng.integers(10_000, 11_000, n), vals)    # ~150 each
+            # 20 hot keys, rates 1..2 x 1/400: from about 1300 down to 700
+            hot = (20 * rng.random(n) ** 1.4).astype(np.int64)
+            vals = np.where(r < 0.05, hot, vals)
+            if f == 0:
+                vals = np.where(rng.random(n) < 0.30, 7, vals)                  # ~160k of key 7
+            feats.append(W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=f + 1))
+        batches.append(W.Batch(feats, B, rng.standard_normal((B, F * 64), dtype=np.float32)))
+    assert B * F * 64 * 4 > 256 * 2**20
+    v0 = batches[0].features[0].values
+    counts = np.bincount(v0[v0 < 64])
+    assert (counts[:20] >= 1024).any() and (counts[:20] < 1024).any()
+    assert np.count_nonzero(batches[0].features[0].values == 7) > 131072
+    run_parity(spec, batches, export_every=2)
+
+
 @pytest.mark.parametrize("pool,admit", [("mean", 1), ("sum", 2)])
 def test_heavy_buckets(pool, admit):
     """Hot keys whose buckets exceed the single-block size (tens of thousands
