@@ -727,6 +727,11 @@ def parse_args(argv=None):
                          "threshold; timing only: the default line keeps exact admission)")
     ap.add_argument("--block-memory", choices=["device", "host"], default="device",
                     help="where the EmbeddingBlocks live: HBM, or pinned host memory across the host link")
+    ap.add_argument("--device-rows", type=int, default=0,
+                    help="with --block-memory host: rows of the HBM tier in front of the host blocks")
+    ap.add_argument("--retier-every", type=int, default=0,
+                    help="with an HBM tier: a hot-tier pass (recis_idmap_retier) after every K-th step, "
+                         "warm-up and timed steps alike (its time is part of the step time)")
     ap.add_argument("--workers", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run plain device copies of known size (for HBM counter scaling)")
@@ -787,7 +792,9 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     table = recis.Table(D, spec.dtype, spec.optim, seed=spec.seed, init_bound=spec.init_bound,
                         admit_threshold=spec.admit_threshold, reserve_rows=reserve,
                         block_memory=block_memory, track_last_use=args.track_last_use and not extra,
-                        admit_sketch_bits=0 if extra else args.admit_sketch_bits, **wl["table"])
+                        admit_sketch_bits=0 if extra else args.admit_sketch_bits,
+                        device_rows=args.device_rows if block_memory == "host" else 0, **wl["table"])
+    retier_every = args.retier_every if block_memory == "host" and args.device_rows > 0 else 0
     gen = torch.Generator(device=dev)
     gen.manual_seed(20250925)
     pdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -820,6 +827,16 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
         table.insert_find(dfs, B, res, flags=flags, descs=descs)
         fwd(res)
         bwd(res, grad)
+
+    retier_ms = []
+
+    def maybe_retier(k):
+        """The hot-tier pass after every retier_every-th step (it synchronises)."""
+        if retier_every and (k + 1) % retier_every == 0:
+            moved = torch.zeros(1, dtype=torch.int64, device=dev)
+            t0 = time.perf_counter()
+            table.retier(moved)
+            retier_ms.append(((time.perf_counter() - t0) * 1e3, int(moved.item())))
 
     # ---- fill the table (untimed)
     i = 0
@@ -868,6 +885,7 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
         torch.cuda.synchronize()
         if name_k:
             probe_ms.setdefault(name_k, []).append(a.elapsed_time(b))
+        maybe_retier(w)
     table.profile_kernel(None)
     dom = max(probe_ms, key=lambda k: np.mean(probe_ms[k])) if probe_ms else None
     table.check()
@@ -890,6 +908,7 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
         e[2].record(stream)
         bwd(res, grad)
         e[3].record(stream)
+        maybe_retier(Wm + k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     table.profile_kernel(None)
@@ -991,6 +1010,22 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
         if block_memory == "host":
             result["config"]["block_memory"] = "host (pinned, mapped; IDMap and scratch in HBM)"
             result["host_link_copy_GBps"] = host_link_copy(torch, dev)
+            H = int(st1.hbm_rows)
+            result["config"]["hbm_tier_rows"] = H
+            result["config"]["retier_every"] = retier_every
+            if retier_ms:
+                result["retier_passes"] = [{"ms": m, "rows_moved": n} for m, n in retier_ms]
+            # row traffic across the host link per timed step, from the rows the
+            # timed lookups handed out: keys on host rows read their row in the
+            # forward and read + write it with its state in the update
+            P = D * s_bytes + S * D * 4
+            host_keys = []
+            for r, u in zip(timed_res, U):
+                rw = r.unique_rows[:u].cpu().numpy()
+                rw = rw[rw >= 0] & ((1 << 62) - 1)
+                host_keys.append(int(np.count_nonzero(rw >= H)))
+            result["host_tier_keys_per_step"] = float(np.mean(host_keys))
+            result["host_link_row_bytes_per_step"] = float(np.mean(host_keys)) * (D * s_bytes + 2 * P)
     cpu_src = None
     if cpu and block_memory == "device" and not args.no_cpu_baseline:
         # the timed steps' inputs and gradients, kept for the oracle

@@ -498,6 +498,10 @@ constexpr long long kNoAllocScratchBytes = 64ll << 20;
 recis_status noalloc_scratch(int device, void** out);
 
 void launch_evict(const TableDev& t, unsigned min_count, double decay, long long* num_evicted, hipStream_t s);
+// Hot-tier placement: rows [0, hbm_rows) are in HBM.  `work` holds
+// retier_words(slot_cap, hbm_rows) ints of device scratch.
+long long retier_words(long long slot_cap, long long hbm_rows);
+void launch_retier(const TableDev& t, long long hbm_rows, int* work, long long* num_moved, hipStream_t s);
 // LRU-bounded pass: keeps the youngest ages whole within max_keys; `work`
 // holds age_hist_words(slot_cap) ints of device scratch.
 long long age_hist_words(long long slot_cap);

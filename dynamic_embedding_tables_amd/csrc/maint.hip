@@ -561,6 +561,205 @@ __global__ __launch_bounds__(256) void k_age_cut(int* work, long long nblocks, l
   }
 }
 
+// ------------------------------------------------------ hot-tier placement
+// Rows [0, H) live in HBM blocks, the rest in host blocks.  A key's class is
+// floor(log2(count)) + 1 (0 for a zero count); the top classes whose keys fit
+// H rows together are hot.  Six launches: per-block class histograms; the
+// cut (one block); per-block counts of the two lists (hot keys on host rows,
+// cooler keys on HBM rows); their scan (one block); the lists, each block's
+// part at its scanned base; then one wave per pair swaps the two rows and
+// their IDMap entries.  No global atomics.
+constexpr int kTierBins = 33;
+constexpr long long kTierSpan = 1 << 16;  // IDMap slots per block
+__device__ __forceinline__ int tier_class(unsigned c) { return 32 - __clz((int)c); }
+
+struct TierWork {
+  int* hist;         // [nb][kTierBins]
+  int* cnt;          // [2][nb]: per-block list sizes, then (scanned) bases
+  long long* ctl;    // [0] hot class cut, [1] pairs, [2] list A size, [3] list B size
+  unsigned* list_a;  // [H] slots of hot keys holding host rows
+  unsigned* list_b;  // [H] slots of cooler keys holding HBM rows
+};
+__host__ __device__ inline long long tier_blocks(long long slot_cap) { return (slot_cap + kTierSpan - 1) / kTierSpan; }
+inline TierWork tier_work(int* w, long long slot_cap, long long H) {
+  const long long nb = tier_blocks(slot_cap);
+  TierWork tw;
+  tw.hist = w;
+  tw.cnt = w + nb * kTierBins;
+  const long long ctl_at = (nb * kTierBins + 2 * nb + 1) & ~1ll;  // 8-byte aligned (the scratch is)
+  tw.ctl = reinterpret_cast<long long*>(w + ctl_at);
+  tw.list_a = reinterpret_cast<unsigned*>(w + ctl_at + 8);
+  tw.list_b = tw.list_a + H;
+  return tw;
+}
+
+__global__ __launch_bounds__(256) void k_tier_hist(TableDev t, TierWork w) {
+  __shared__ int s_h[kTierBins];
+  if (threadIdx.x < kTierBins) s_h[threadIdx.x] = 0;
+  __syncthreads();
+  const long long b0 = (long long)blockIdx.x * kTierSpan;
+  for (long long k = threadIdx.x; k < kTierSpan; k += 256) {
+    const long long i = b0 + k;
+    if (i > (long long)t.slot_mask) break;
+    const Slot sl = t.slots[i];
+    if (sl.key >= 0 && sl.row >= 0) atomicAdd(&s_h[tier_class(sl.count)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < kTierBins) w.hist[(long long)blockIdx.x * kTierBins + threadIdx.x] = s_h[threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void k_tier_cut(TierWork w, long long nb, long long H) {
+  __shared__ long long s_tot[kTierBins];
+  if (threadIdx.x < kTierBins) s_tot[threadIdx.x] = 0;
+  __syncthreads();
+  long long v[kTierBins];  // this thread's blocks, every class
+#pragma unroll
+  for (int j = 0; j < kTierBins; ++j) v[j] = 0;
+  for (long long b = threadIdx.x; b < nb; b += 256)
+#pragma unroll
+    for (int j = 0; j < kTierBins; ++j) v[j] += w.hist[b * kTierBins + j];
+#pragma unroll
+  for (int j = 0; j < kTierBins; ++j)
+    if (v[j]) atomicAdd((unsigned long long*)&s_tot[j], (unsigned long long)v[j]);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // the lowest class such that it and the classes above fit in H rows
+    long long acc = 0;
+    int cut = 0;
+    for (int j = kTierBins - 1; j >= 0; --j) {
+      acc += s_tot[j];
+      if (acc > H) {
+        cut = j + 1;
+        break;
+      }
+    }
+    w.ctl[0] = cut;
+  }
+}
+
+// Which list slot i of the IDMap goes to: 1 (A: hot on a host row), 2 (B: not
+// hot on an HBM row), 0 none.
+__device__ __forceinline__ int tier_list(const TableDev& t, long long i, int cut, long long H) {
+  const Slot sl = t.slots[i];
+  if (sl.key < 0 || sl.row < 0) return 0;
+  const long long r = sl.row & ~kPendingRow;
+  const bool hot = tier_class(sl.count) >= cut;
+  if (hot && r >= H) return 1;
+  if (!hot && r < H) return 2;
+  return 0;
+}
+
+// Per block: list sizes (COUNT) or the lists at the scanned bases (PLACE),
+// in slot order within the block.
+template <bool PLACE>
+__global__ __launch_bounds__(256) void k_tier_lists(TableDev t, TierWork w, long long nb, long long H) {
+  __shared__ int s_w[2][4];
+  __shared__ int s_run[2];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int cut = (int)w.ctl[0];
+  if (threadIdx.x < 2) s_run[threadIdx.x] = 0;
+  const long long b0 = (long long)blockIdx.x * kTierSpan;
+  const long long base_a = PLACE ? w.cnt[blockIdx.x] : 0, base_b = PLACE ? w.cnt[nb + blockIdx.x] : 0;
+  for (long long k0 = 0; k0 < kTierSpan; k0 += 256) {
+    const long long i = b0 + k0 + threadIdx.x;
+    const int which = i <= (long long)t.slot_mask ? tier_list(t, i, cut, H) : 0;
+    const unsigned long long ma = __ballot(which == 1), mb = __ballot(which == 2);
+    __syncthreads();  // the previous round's reads of s_w are done
+    if (lane == 0) {
+      s_w[0][wid] = __popcll(ma);
+      s_w[1][wid] = __popcll(mb);
+    }
+    __syncthreads();
+    int pa = s_run[0], pb = s_run[1];
+    for (int x = 0; x < wid; ++x) {
+      pa += s_w[0][x];
+      pb += s_w[1][x];
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    if (PLACE && which == 1) w.list_a[base_a + pa + __popcll(ma & below)] = (unsigned)i;
+    if (PLACE && which == 2) w.list_b[base_b + pb + __popcll(mb & below)] = (unsigned)i;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      s_run[0] += s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
+      s_run[1] += s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
+    }
+  }
+  __syncthreads();
+  if (!PLACE && threadIdx.x == 0) {
+    w.cnt[blockIdx.x] = s_run[0];
+    w.cnt[nb + blockIdx.x] = s_run[1];
+  }
+}
+
+// One block: exclusive scans of the two per-block size arrays (each thread
+// a contiguous run of blocks, its loads in flight together); the pairs are
+// as many as the shorter list.
+__global__ __launch_bounds__(1024) void k_tier_scan(TierWork w, long long nb) {
+  __shared__ long long s_w[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const long long per = (nb + 1023) / 1024, b0 = (long long)tid * per;
+  for (int l = 0; l < 2; ++l) {
+    int* c = w.cnt + l * nb;
+    long long sum = 0;
+    for (long long b = b0; b < b0 + per && b < nb; ++b) sum += c[b];
+    long long x = sum;  // inclusive scan over the wave
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) s_w[l][wid] = x;
+    __syncthreads();
+    long long run = x - sum, all = 0;
+    for (int q = 0; q < 16; ++q) {
+      run += q < wid ? s_w[l][q] : 0;
+      all += s_w[l][q];
+    }
+    for (long long b = b0; b < b0 + per && b < nb; ++b) {
+      const int v = c[b];
+      c[b] = (int)run;
+      run += v;
+    }
+    if (tid == 0) w.ctl[2 + l] = all;
+    __syncthreads();
+  }
+  if (tid == 0) w.ctl[1] = w.ctl[2] < w.ctl[3] ? w.ctl[2] : w.ctl[3];
+}
+
+// One wave per pair: key a (hot, host row) and key b (cooler, HBM row)
+// exchange rows -- each written row's bytes copied to the other row first
+// (a row never written moves as its pending mark alone) -- and IDMap
+// entries.
+__global__ __launch_bounds__(256) void k_tier_swap(TableDev t, TierWork w, long long* num_moved) {
+  const long long np = w.ctl[1];
+  const int lane = threadIdx.x & 63;
+  const int nc = (int)(t.rs.stride >> 4);  // 16-byte chunks per row
+  for (long long q = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); q < np; q += (long long)gridDim.x * 4) {
+    const unsigned sa = w.list_a[q], sb = w.list_b[q];
+    const int rowa = t.slots[sa].row, rowb = t.slots[sb].row;
+    const int pa = rowa & kPendingRow, pb = rowb & kPendingRow;
+    const int ra = rowa & ~kPendingRow, rb = rowb & ~kPendingRow;
+    uint4* A = reinterpret_cast<uint4*>(row_ptr(t.rs, ra));
+    uint4* B = reinterpret_cast<uint4*>(row_ptr(t.rs, rb));
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const int c = c0 + lane;
+      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+      if (c < nc) {
+        if (!pa) va = A[c];
+        if (!pb) vb = B[c];
+      }
+      if (c < nc) {
+        if (!pa) B[c] = va;
+        if (!pb) A[c] = vb;
+      }
+    }
+    if (lane == 0) {
+      t.slots[sa].row = rb | pa;
+      t.slots[sb].row = ra | pb;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && num_moved) *num_moved = np;
+}
+
 unsigned grid_for(long long n, int threads) {
   long long g = (n + threads - 1) / threads;
   if (g > 65536) g = 65536;
@@ -629,6 +828,22 @@ void launch_evict(const TableDev& t, unsigned min_count, double decay, long long
   const long long nb = ((long long)t.slot_mask + kEvictSpan) / kEvictSpan;
   hipLaunchKernelGGL(k_evict_mark, dim3((unsigned)nb), dim3(256), 0, s, t, min_count, decay, (const int*)nullptr);
   hipLaunchKernelGGL(k_evict_done, dim3(1), dim3(1), 0, s, t.ctr, num_evicted);
+}
+
+long long retier_words(long long slot_cap, long long hbm_rows) {
+  const long long nb = tier_blocks(slot_cap);
+  return ((nb * kTierBins + 2 * nb + 1) & ~1ll) + 8 + 2 * hbm_rows + 2;
+}
+
+void launch_retier(const TableDev& t, long long hbm_rows, int* work, long long* num_moved, hipStream_t s) {
+  const long long nb = tier_blocks((long long)t.slot_mask + 1);
+  const TierWork w = tier_work(work, (long long)t.slot_mask + 1, hbm_rows);
+  hipLaunchKernelGGL(k_tier_hist, dim3((unsigned)nb), dim3(256), 0, s, t, w);
+  hipLaunchKernelGGL(k_tier_cut, dim3(1), dim3(256), 0, s, w, nb, hbm_rows);
+  hipLaunchKernelGGL((k_tier_lists<false>), dim3((unsigned)nb), dim3(256), 0, s, t, w, nb, hbm_rows);
+  hipLaunchKernelGGL(k_tier_scan, dim3(1), dim3(1024), 0, s, w, nb);
+  hipLaunchKernelGGL((k_tier_lists<true>), dim3((unsigned)nb), dim3(256), 0, s, t, w, nb, hbm_rows);
+  hipLaunchKernelGGL(k_tier_swap, dim3(grid_for(hbm_rows, 4)), dim3(256), 0, s, t, w, num_moved);
 }
 
 long long age_hist_words(long long slot_cap) { return (slot_cap + kAgeSpan - 1) / kAgeSpan * kAgeBins + 1; }

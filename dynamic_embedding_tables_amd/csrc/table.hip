@@ -100,8 +100,16 @@ recis_status check_launch() {
 // One EmbeddingBlock: device memory from the allocator, or pinned host
 // memory mapped for the GPU (non-coherent, so the GPU may cache it within a
 // kernel; nothing else writes it while kernels run).
+// Block i of a host-memory table goes to HBM while i is below the HBM tier's
+// block count.
+bool block_in_hbm(const recis_table* t, long long i) {
+  if (t->cfg.block_memory != RECIS_MEM_HOST) return true;
+  const long long br = t->cfg.block_rows;
+  return i < (t->cfg.device_rows + br - 1) / br;
+}
+
 char* block_alloc(recis_table* t, size_t bytes, hipStream_t s) {
-  if (t->cfg.block_memory != RECIS_MEM_HOST) return static_cast<char*>(tab_alloc(t, bytes, s));
+  if (block_in_hbm(t, (long long)t->blocks.size())) return static_cast<char*>(tab_alloc(t, bytes, s));
   void* h = nullptr;
   if (hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocNonCoherent) != hipSuccess) return nullptr;
   void* d = nullptr;
@@ -112,8 +120,8 @@ char* block_alloc(recis_table* t, size_t bytes, hipStream_t s) {
   return static_cast<char*>(h);
 }
 
-void block_free(recis_table* t, char* b, hipStream_t s) {
-  if (t->cfg.block_memory != RECIS_MEM_HOST) {
+void block_free(recis_table* t, long long i, char* b, hipStream_t s) {
+  if (block_in_hbm(t, i)) {
     tab_free(t, b, (size_t)(t->cfg.block_rows * t->row_bytes), s);
     return;
   }
@@ -345,6 +353,14 @@ recis_status stage(recis_table* t, const void* src, size_t bytes, hipStream_t s,
   return RECIS_OK;
 }
 
+// Rows whose blocks are in HBM (the allocated ones).
+long long hbm_rows(const recis_table* t) {
+  if (t->cfg.block_memory != RECIS_MEM_HOST) return t->rows_alloc;
+  const long long br = t->cfg.block_rows;
+  const long long nb = std::min<long long>((long long)t->blocks.size(), (t->cfg.device_rows + br - 1) / br);
+  return std::min<long long>(nb * br, t->rows_alloc);
+}
+
 }  // namespace
 
 TableDev recis_table::dev() const {
@@ -413,6 +429,7 @@ recis_status recis_idmap_create(const recis_table_config* cfg, const recis_alloc
   if (cfg->block_memory != RECIS_MEM_DEVICE && cfg->block_memory != RECIS_MEM_HOST) return RECIS_ERR_INVALID_ARG;
   if (cfg->track_last_use != 0 && cfg->track_last_use != 1) return RECIS_ERR_INVALID_ARG;
   if (cfg->admit_sketch_bits < 0 || cfg->admit_sketch_bits > 30) return RECIS_ERR_INVALID_ARG;
+  if (cfg->device_rows < 0) return RECIS_ERR_INVALID_ARG;
   if (alloc && (!alloc->alloc || !alloc->free)) return RECIS_ERR_INVALID_ARG;
   if (!valid_dim(cfg->dim)) return RECIS_ERR_UNSUPPORTED;
 
@@ -466,7 +483,7 @@ recis_status recis_idmap_destroy(recis_table* t) {
   ScopedProbe sp(t);
   hipStream_t s = nullptr;
   (void)hipDeviceSynchronize();
-  for (char* b : t->blocks) block_free(t, b, s);
+  for (size_t i = 0; i < t->blocks.size(); ++i) block_free(t, (long long)i, t->blocks[i], s);
   tab_free(t, t->d_blocks, t->d_blocks_cap * sizeof(char*), s);
   tab_free(t, t->free_list, (size_t)t->free_cap * 4, s);
   tab_free(t, t->slots, (size_t)t->slot_cap * sizeof(Slot), s);
@@ -645,6 +662,24 @@ recis_status recis_idmap_evict_lru(recis_table* t, int64_t max_keys, int64_t* nu
   t->rows_hi = (long long)c.next_row;
   t->keys_hi = (long long)c.num_keys;
   return RECIS_OK;
+}
+
+recis_status recis_idmap_retier(recis_table* t, int64_t* num_moved, hipStream_t s) {
+  if (!t) return RECIS_ERR_INVALID_ARG;
+  if (t->cfg.block_memory != RECIS_MEM_HOST || t->cfg.device_rows <= 0) return RECIS_ERR_UNSUPPORTED;
+  ScopedDevice sd(t->device);
+  ScopedProbe sp(t);
+  const long long H = hbm_rows(t);
+  const size_t wbytes = (size_t)retier_words(t->slot_cap, H) * sizeof(int);
+  int* work = static_cast<int*>(tab_alloc(t, wbytes, s));
+  if (!work) return RECIS_ERR_OUT_OF_MEMORY;
+  t->update_epoch += 1;  // rows move: lookups made before re-probe their keys
+  t->map_version += 1;
+  launch_retier(t->dev(), H, work, reinterpret_cast<long long*>(num_moved), s);
+  recis_status st = check_launch();
+  if (hipStreamSynchronize(s) != hipSuccess) st = RECIS_ERR_HIP;
+  tab_free(t, work, wbytes, s);
+  return st;
 }
 
 recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_result* res, int32_t pool, void* out,
@@ -843,6 +878,7 @@ recis_status recis_idmap_stats(recis_table* t, recis_table_stats* out, hipStream
   out->adam_step = t->adam_step;
   out->bytes = t->bytes;
   out->probationary_keys = out->keys - out->rows_in_use;
+  out->hbm_rows = hbm_rows(t);
   out->claim_attempts = (int64_t)c.claim_attempts;
   out->claim_failures = (int64_t)c.claim_failures;
   return RECIS_OK;

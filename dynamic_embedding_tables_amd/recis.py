@@ -49,6 +49,7 @@ POOLS = {"sum": RECIS_POOL_SUM, "mean": RECIS_POOL_MEAN, "none": RECIS_POOL_NONE
 EXPORTED_SYMBOLS = (
     "recis_table_config_default", "recis_plan_words", "recis_idmap_create", "recis_idmap_destroy",
     "recis_idmap_insert_find", "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru",
+    "recis_idmap_retier",
     "recis_lookup_pool_fwd",
     "recis_pool_bwd_update", "recis_pool_bwd_update_noalloc", "recis_noalloc_scratch_bytes",
     "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_key_ages", "recis_idmap_sketch",
@@ -62,7 +63,7 @@ class recis_table_config(C.Structure):
                 ("admit_threshold", C.c_uint32), ("seed", C.c_uint64), ("init_bound", C.c_float),
                 ("max_load", C.c_float), ("slot_capacity", C.c_int64), ("block_rows", C.c_int64),
                 ("max_rows", C.c_int64), ("reserve_rows", C.c_int64), ("block_memory", C.c_int32),
-                ("track_last_use", C.c_int32), ("admit_sketch_bits", C.c_int32)]
+                ("track_last_use", C.c_int32), ("admit_sketch_bits", C.c_int32), ("device_rows", C.c_int64)]
 
 
 class recis_allocator(C.Structure):
@@ -92,7 +93,7 @@ class recis_table_stats(C.Structure):
     _fields_ = [("keys", C.c_int64), ("rows_in_use", C.c_int64), ("rows_allocated", C.c_int64),
                 ("blocks", C.c_int64), ("slot_capacity", C.c_int64), ("adam_step", C.c_int64),
                 ("bytes", C.c_int64), ("probationary_keys", C.c_int64), ("claim_attempts", C.c_int64),
-                ("claim_failures", C.c_int64)]
+                ("claim_failures", C.c_int64), ("hbm_rows", C.c_int64)]
 
 
 class RecisError(RuntimeError):
@@ -124,6 +125,7 @@ def load_library() -> C.CDLL:
     L.recis_idmap_evict.argtypes = [p, u32, p, p]
     L.recis_idmap_evict_decay.argtypes = [p, u32, C.c_double, p, p]
     L.recis_idmap_evict_lru.argtypes = [p, i64, p, p]
+    L.recis_idmap_retier.argtypes = [p, p, p]
     L.recis_lookup_pool_fwd.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, p]
     L.recis_pool_bwd_update.argtypes = [p, C.POINTER(recis_lookup_result), i32, p, i32,
                                         C.POINTER(recis_optim_params), p]
@@ -142,7 +144,8 @@ def load_library() -> C.CDLL:
     L.recis_status_string.argtypes = [i32]
     L.recis_status_string.restype = C.c_char_p
     for name in ("recis_idmap_create", "recis_idmap_destroy", "recis_idmap_insert_find",
-                 "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru", "recis_lookup_pool_fwd",
+                 "recis_idmap_evict", "recis_idmap_evict_decay", "recis_idmap_evict_lru", "recis_idmap_retier",
+                 "recis_lookup_pool_fwd",
                  "recis_pool_bwd_update", "recis_pool_bwd_update_noalloc",
                  "recis_writeback", "recis_idmap_export", "recis_idmap_import", "recis_idmap_key_ages",
                  "recis_idmap_sketch", "recis_idmap_stats", "recis_get_error"):
@@ -250,6 +253,10 @@ def recis_idmap_evict(h, min_count: int, num_evicted=None, stream=None):
 def recis_idmap_evict_lru(h, max_keys: int, num_evicted=None, stream=None):
     _check(load_library().recis_idmap_evict_lru(h, max_keys, _ptr(num_evicted), _stream(stream)),
            "recis_idmap_evict_lru")
+
+
+def recis_idmap_retier(h, num_moved=None, stream=None):
+    _check(load_library().recis_idmap_retier(h, _ptr(num_moved), _stream(stream)), "recis_idmap_retier")
 
 
 def recis_idmap_evict_decay(h, min_count: int, decay: float, num_evicted=None, stream=None):
@@ -397,7 +404,7 @@ class Table:
                  init_bound: float = 0.05, admit_threshold: int = 1, slot_capacity: int = 1 << 20,
                  block_rows: int = 1 << 20, max_rows: int = (1 << 30) - 1, reserve_rows: int = 0,
                  max_load: float = 0.5, block_memory: str = "device", track_last_use: bool = False,
-                 admit_sketch_bits: int = 0, stream=None, allocator: str = "torch"):
+                 admit_sketch_bits: int = 0, stream=None, allocator: str = "torch", device_rows: int = 0):
         cfg = recis_table_config_default()
         cfg.dim, cfg.dtype, cfg.optim = dim, DTYPES[dtype], OPTIMS[optim]
         cfg.seed, cfg.init_bound, cfg.admit_threshold = seed, init_bound, admit_threshold
@@ -406,10 +413,11 @@ class Table:
         cfg.block_memory = {"device": RECIS_MEM_DEVICE, "host": RECIS_MEM_HOST}[block_memory]
         cfg.track_last_use = 1 if track_last_use else 0
         cfg.admit_sketch_bits = admit_sketch_bits
+        cfg.device_rows = device_rows
         self.dim, self.dtype, self.optim = dim, dtype, optim
         self.config = {"seed": seed, "init_bound": init_bound, "admit_threshold": admit_threshold,
                        "block_memory": block_memory, "track_last_use": bool(track_last_use),
-                       "admit_sketch_bits": int(admit_sketch_bits)}
+                       "admit_sketch_bits": int(admit_sketch_bits), "device_rows": int(device_rows)}
         if allocator not in ("torch", "hip"):
             raise ValueError("allocator is 'torch' (torch's caching allocator) or 'hip' (hipMalloc)")
         self.allocator = allocator
@@ -456,6 +464,11 @@ class Table:
         """Keeps at most max_keys keys, the most recently used (needs
         track_last_use)."""
         recis_idmap_evict_lru(self.h, max_keys, num_evicted, stream)
+
+    def retier(self, num_moved=None, stream=None):
+        """Host-memory blocks with an HBM tier: the most frequent keys move
+        into the HBM rows (see recis_idmap_retier)."""
+        recis_idmap_retier(self.h, num_moved, stream)
 
     def key_ages(self, keys, stream=None):
         """uint32 ages of the given keys (device int64 tensor) as an int64 tensor

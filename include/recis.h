@@ -122,11 +122,17 @@ typedef struct {
                                (Page "RecIS (Recommendation Intelligence System)" README,
                                section "Core architecture > Embedding Engine": admission
                                strategies.) */
+  int64_t device_rows;      /* RECIS_MEM_HOST only: the first device_rows rows (rounded up to
+                               whole blocks) are EmbeddingBlocks in HBM, the hot tier in front
+                               of the pinned host blocks; new rows are handed out from the
+                               start, so they fill the HBM tier first, and recis_idmap_retier
+                               moves the most frequent keys into it.  0: every block in host
+                               memory.  Ignored for RECIS_MEM_DEVICE (every row in HBM). */
 } recis_table_config;
 
 /* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
  * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0,
- * blocks in device memory, no last-use stamps, exact admission). */
+ * blocks in device memory, no last-use stamps, exact admission, no HBM tier). */
 void recis_table_config_default(recis_table_config* cfg);
 
 /* Device-memory provider.  alloc returns `bytes` of device memory (256-byte
@@ -217,6 +223,8 @@ typedef struct {
                              overflowed and hot buckets) */
   int64_t claim_failures; /* of those, claims that found the slot already taken by
                              another key of the same call (the probe then moves on) */
+  int64_t hbm_rows;       /* rows whose EmbeddingBlocks are in HBM: all of them for
+                             RECIS_MEM_DEVICE, the hot tier for RECIS_MEM_HOST */
 } recis_table_stats;
 
 /* Creates a table.  Allocates the IDMap and `reserve_rows` worth of blocks
@@ -273,6 +281,24 @@ recis_status recis_idmap_evict_decay(recis_table* t, uint32_t min_count, double 
  * Synchronises `s`. */
 recis_status recis_idmap_evict_lru(recis_table* t, int64_t max_keys, int64_t* num_evicted,
                                    hipStream_t s);
+
+/* Hot-tier placement for a table whose EmbeddingBlocks are in host memory
+ * with an HBM tier (device_rows > 0): swaps rows so that the keys with the
+ * highest counts hold the HBM rows.  Keys are ranked by their count since the
+ * last eviction pass, in classes floor(log2(count)) + 1: the top classes that
+ * fit the HBM tier together are hot.  Each hot key holding a host row
+ * changes places with a key of a lower class holding an HBM row -- as many
+ * pairs as both lists allow -- the two rows' parameters and optimizer state
+ * (a row not yet written moves as its pending mark) and their IDMap entries
+ * exchanged.  Content is unchanged: only where rows live.  The pages let
+ * both levels of the table sit on the GPU or the CPU (page "RecIS
+ * (Recommendation Intelligence System)" README, section "Key optimisations >
+ * Efficient dynamic Embedding"); this keeps the frequent rows in HBM.
+ * num_moved: device [1] (may be NULL), the keys moved into HBM.  Uses
+ * 8 bytes per HBM row of temporary device memory from the allocator and
+ * synchronises `s`.  Errors: UNSUPPORTED (blocks not in host memory, or no
+ * HBM tier), OUT_OF_MEMORY, HIP. */
+recis_status recis_idmap_retier(recis_table* t, int64_t* num_moved, hipStream_t s);
 
 /* Forward: SUM / MEAN write float32 out [batch, num_feats * dim] with
  * out[i, f*dim + d] = pooled element d of bag (f, i) (mean divides by the bag

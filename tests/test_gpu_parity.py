@@ -30,8 +30,35 @@ def _gpu():
     print(f"\n[gpu] {torch.cuda.get_device_name(0)}", flush=True)
 
 
+def check_tiers(table):
+    """After a hot-tier pass: with H HBM rows and keys ranked in classes
+    floor(log2(count)) + 1, the top classes that fit H rows are hot; either no
+    hot key is left on a host row or no cooler key on an HBM row (the pass
+    swaps as many pairs as both lists allow).  Brute force over the export."""
+    ex = table.export()
+    rows = ex["rows"].cpu().numpy()
+    counts = ex["counts"].cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    has = rows >= 0
+    H = table.stats().hbm_rows
+    cls = np.zeros(counts.size, np.int64)
+    nz = counts > 0
+    cls[nz] = np.floor(np.log2(counts[nz])).astype(np.int64) + 1
+    hist = np.bincount(cls[has], minlength=33)
+    acc, cut = 0, 0
+    for j in range(32, -1, -1):
+        acc += hist[j]
+        if acc > H:
+            cut = j + 1
+            break
+    hot = cls >= cut
+    a = np.count_nonzero(has & hot & (rows >= H))
+    b = np.count_nonzero(has & ~hot & (rows < H))
+    assert a == 0 or b == 0, (a, b, H, cut)
+    return np.count_nonzero(has & (rows < H)), np.count_nonzero(has & hot)
+
+
 def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopulate=None,
-               export_every=1, evict_decay=0.0, lru_max=None, find_only_steps=()):
+               export_every=1, evict_decay=0.0, lru_max=None, find_only_steps=(), retier_every=0):
     import torch
     from dynamic_embedding_tables_amd import recis
     table = make_table(spec, **(table_kw or {}))
@@ -58,6 +85,11 @@ def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopu
         assert table.get_error() == 0
         check_lookup(canon_lookup(res), r)
         check_forward(out, spec, oout, oab, r.merged_offsets, r.num_feats, exact=step == 0 and prepopulate is None)
+        if retier_every and (step + 1) % retier_every == 0:
+            moved = torch.zeros(1, dtype=torch.int64, device="cuda")
+            table.retier(moved)
+            in_hbm, n_hot = check_tiers(table)
+            print(f"[parity] retier: moved {int(moved.item())}, rows in HBM {in_hbm}, hot keys {n_hot}", flush=True)
         if evict_every and (step + 1) % evict_every == 0:
             ne = torch.zeros(1, dtype=torch.int64, device="cuda")
             if lru_max is not None:
@@ -447,6 +479,51 @@ def test_growth_of_idmap_and_blocks():
 
 
 # ---- EmbeddingBlocks in pinned host memory (the IDMap and scratch in HBM)
+@pytest.mark.parametrize("optim,pool", [("adam", "mean"), ("adagrad", "sum")])
+def test_hbm_tier_in_front_of_host_blocks(optim, pool):
+    """EmbeddingBlocks in host memory with a two-block HBM tier (128 rows of
+    64): new rows fill the HBM tier first, then host blocks; after every step
+    the hot-tier pass moves the most frequent keys into HBM.  Content is
+    checked against the oracle at every step (the tiers change where rows
+    live, not what they hold), and the placement by brute force."""
+    spec = W.TableSpec(dim=32, dtype="f32", optim=optim, pool=pool, lr=1e-3 if optim == "adam" else 0.01,
+                       eps=1e-8 if optim == "adam" else 1e-10)
+    run_parity(spec, [W.ctr_batch(s, batch=96, num_feats=3, dim=32) for s in range(6)],
+               table_kw=dict(block_memory="host", block_rows=64, device_rows=100), retier_every=1)
+
+
+def test_hbm_tier_with_eviction_and_admission():
+    """The hot tier with admission at 2 and eviction passes: probationary keys
+    hold no row and take no part; freed rows of either tier are reused."""
+    spec = W.spec_multi(2)
+    run_parity(spec, [W.multi_batch(s, 2, batch=128, num_feats=6) for s in range(6)],
+               table_kw=dict(block_memory="host", block_rows=256, device_rows=512), retier_every=1, evict_every=2)
+
+
+def test_hbm_tier_between_a_lookup_and_its_backward():
+    """A hot-tier pass between a lookup and its forward / backward: rows have
+    moved, so the stale lookup re-probes its keys."""
+    import torch
+    spec = W.TableSpec(dim=32, dtype="f32", optim="adam", pool="mean", lr=1e-3, eps=1e-8)
+    table = make_table(spec, block_memory="host", block_rows=64, device_rows=64)
+    otab = oracle.OracleTable(spec)
+    from dynamic_embedding_tables_amd import recis
+    warm = W.ctr_batch(5, batch=200, num_feats=2, dim=32)
+    res = recis.LookupResult(warm.n, warm.num_feats * warm.batch)
+    gpu_step(table, spec, warm, res)
+    oracle_step(otab, spec, warm)
+
+    def retier():
+        moved = torch.zeros(1, dtype=torch.int64, device="cuda")
+        table.retier(moved)
+        assert int(moved.item()) > 0
+        check_tiers(table)
+
+    _stale_pair(spec, table, otab, W.ctr_batch(6, batch=200, num_feats=2, dim=32),
+                W.ctr_batch(7, batch=100, num_feats=2, dim=32), retier)
+    table.close()
+
+
 def test_host_memory_blocks_ctr():
     """The CTR step with small blocks, so rows spread over many host blocks
     that are added as the table grows."""
