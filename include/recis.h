@@ -132,12 +132,18 @@ typedef struct {
 
 /* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
  * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0,
- * blocks in device memory, no last-use stamps, exact admission, no HBM tier). */
+ * blocks in device memory, no last-use stamps, exact admission, no HBM tier).
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Key optimisations > Distributed optimisation"
+ * (a table's attributes: dimension, initializer). */
 void recis_table_config_default(recis_table_config* cfg);
 
 /* Device-memory provider.  alloc returns `bytes` of device memory (256-byte
  * aligned) or NULL; free releases it.  Both may be called with the stream of
- * the call that needs the memory. */
+ * the call that needs the memory.  The Python binding passes callbacks over
+ * torch's caching allocator (the pages build on PyTorch: page "RecIS: Sparse
+ * to Dense, A Unified Training Framework for Recommendation Models",
+ * abstract), so a table takes its device memory from the same pool as the
+ * model; with NULL the library uses hipMalloc / hipFree. */
 typedef struct {
   void* ctx;
   void* (*alloc)(void* ctx, size_t bytes, hipStream_t s);
@@ -198,7 +204,8 @@ typedef struct {
                               the rows its keys hold now (a key evicted since has none) */
 } recis_lookup_result;
 
-/* int32 words needed by recis_lookup_result.plan for `capacity` occurrences. */
+/* int32 words needed by recis_lookup_result.plan for `capacity` occurrences.
+ * (Layout support for the lookup result; no passage of the pages.) */
 int64_t recis_plan_words(int64_t capacity);
 
 /* Hyper-parameters in double: the library derives 1 - beta1 and 1 - beta2 in
@@ -229,11 +236,17 @@ typedef struct {
 
 /* Creates a table.  Allocates the IDMap and `reserve_rows` worth of blocks
  * (synchronises `s` once).  Errors: INVALID_ARG (bad config, NULL out),
- * UNSUPPORTED (dim/dtype), OUT_OF_MEMORY, HIP. */
+ * UNSUPPORTED (dim/dtype), OUT_OF_MEMORY, HIP.
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Key optimisations > Efficient dynamic Embedding"
+ * (a two-level store: IDMap of feature ID -> Offset over EmbeddingBlocks that
+ * hold parameters and optimizer state, extended block by block) and section
+ * "Key optimisations > Distributed optimisation" (tables of the same
+ * attributes -- dimension, initializer -- merged into one). */
 recis_status recis_idmap_create(const recis_table_config* cfg, const recis_allocator* alloc,
                                 hipStream_t s, recis_table** out);
 
-/* Releases everything the table owns.  No work on `t` may be pending. */
+/* Releases everything the table owns.  No work on `t` may be pending.
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Key optimisations > Efficient dynamic Embedding". */
 recis_status recis_idmap_destroy(recis_table* t);
 
 /* Lookup of one batch: transform + tag every value, merge the features
@@ -245,14 +258,23 @@ recis_status recis_idmap_destroy(recis_table* t);
  * batch could exceed them (may synchronise `s` then).
  * feats: host array [num_feats].  Errors: INVALID_ARG, OUT_OF_MEMORY, HIP,
  * CAPACITY (max_rows reached, host-detected); device: CAPACITY, KEY_RANGE,
- * INVALID_ARG (bag offsets). */
+ * INVALID_ARG (bag offsets).
+ * Passage: page "RecIS (Recommendation Intelligence System)" README -- section "Core architecture > Feature Engine" (Hash, Mod,
+ * Bucketize, fused); section "Key optimisations > Distributed optimisation"
+ * (requests to tables of the same attributes merged and deduplicated);
+ * section "Core architecture > Embedding Engine" (collision-free table,
+ * admission); section "Key optimisations > Efficient dynamic Embedding"
+ * (IDMap: feature ID as key, Offset as value). */
 recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* feats,
                                      int32_t num_feats, int32_t batch, uint32_t flags,
                                      recis_lookup_result* res, hipStream_t s);
 
 /* Eviction pass: removes every key whose count since the last pass is below
  * min_count (with or without a row), returns its row to the free list, and
- * restarts the surviving counts at 0.  num_evicted: device [1] (may be NULL). */
+ * restarts the surviving counts at 0.  num_evicted: device [1] (may be NULL).
+ * Clears a standing CAPACITY error (the pass may have made room).
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Core architecture > Embedding Engine" (feature
+ * eviction and admission strategies). */
 recis_status recis_idmap_evict(recis_table* t, uint32_t min_count, int64_t* num_evicted,
                                hipStream_t s);
 
@@ -303,7 +325,11 @@ recis_status recis_idmap_retier(recis_table* t, int64_t* num_moved, hipStream_t 
 /* Forward: SUM / MEAN write float32 out [batch, num_feats * dim] with
  * out[i, f*dim + d] = pooled element d of bag (f, i) (mean divides by the bag
  * length; an empty bag gives 0; a key without a row adds zeros); NONE writes
- * out [N, dim] in the storage dtype, one row per occurrence. */
+ * out [N, dim] in the storage dtype, one row per occurrence.  Reads the rows
+ * the lookup's keys hold when it runs (see map_version).
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Key optimisations > Efficient use of hardware >
+ * Operator implementation" (vectorised memory access) and section "Key
+ * optimisations > Efficient dynamic Embedding" (the Offset names the row). */
 recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_result* res,
                                    int32_t pool, void* out, hipStream_t s);
 
@@ -312,7 +338,11 @@ recis_status recis_lookup_pool_fwd(const recis_table* t, const recis_lookup_resu
  * for MEAN; grad_out [N, dim] for NONE, which needs RECIS_GROUP_BY_OCCURRENCE
  * at insert_find), summed in double, then one optimizer step on every
  * distinct key that has a row.  Adam's step counter is the table's and grows
- * by one per call.  grad_dtype: RECIS_DTYPE_F32 or RECIS_DTYPE_BF16. */
+ * by one per call.  grad_dtype: RECIS_DTYPE_F32 or RECIS_DTYPE_BF16.
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Key optimisations > Efficient use of hardware >
+ * Operator implementation" (reductions merged within a warp rather than by
+ * atomics) and section "Key optimisations > Efficient dynamic Embedding"
+ * (optimizer state stored in the EmbeddingBlocks beside the parameters). */
 recis_status recis_pool_bwd_update(recis_table* t, const recis_lookup_result* res, int32_t pool,
                                    const void* grad_out, int32_t grad_dtype,
                                    const recis_optim_params* opt, hipStream_t s);
@@ -341,15 +371,22 @@ int64_t recis_noalloc_scratch_bytes(void);
 /* Exact-assignment writeback: for i in order, row(keys[i]) <- rows[i] rounded
  * to the storage dtype, so the last occurrence of a repeated key wins.  An
  * absent key is inserted and given a row at once; counts are not touched.
- * keys: device [n] (>= 0); rows: device float32 [n, dim]. */
+ * keys: device [n] (>= 0); rows: device float32 [n, dim].
+ * Passage: page "Memory Layer: Train the In-Model Cache for Recommendation
+ * Models", sections "What carries the argument" and "Referee Report >
+ * Summary" (the item tower's output written into the cache row by exact
+ * assignment). */
 recis_status recis_writeback(recis_table* t, const int64_t* keys, int64_t n, const float* rows,
                              hipStream_t s);
 
 /* Copies the table out (synchronises `s`): keys device [cap], rows device
  * [cap] (-1 = no row), counts device [cap], params device [cap, dim] in the
  * storage dtype, state device float32 [cap, slots*dim] (may be NULL when the
- * optimizer has none); params and state 16-byte aligned.  *n receives the number of keys (host); when it
- * exceeds cap only cap entries are written.  Order unspecified. */
+ * optimizer has none); params and state 16-byte aligned.  *n receives the
+ * number of keys (host); when it exceeds cap only cap entries are written.
+ * Order unspecified.
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Core architecture > Saver" (sparse parameters
+ * stored and delivered as SafeTensors; this call is the device side). */
 recis_status recis_idmap_export(recis_table* t, int64_t cap, int64_t* keys, int64_t* rows,
                                 uint32_t* counts, void* params, float* state, int64_t* n,
                                 hipStream_t s);
@@ -380,18 +417,26 @@ recis_status recis_idmap_import(recis_table* t, int64_t n, const int64_t* keys, 
  * recis_idmap_sketch: set 0 copies the sketch's 4 x 2^admit_sketch_bits
  * counters (row after row) to `counters`; set 1 loads them from there.
  * counters: device.  Needs admit_sketch_bits > 0 (else UNSUPPORTED).
- * Both are stream-ordered; for restoring, call them after recis_idmap_import. */
+ * Both are stream-ordered; for restoring, call them after recis_idmap_import.
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, sections "Core architecture > Saver" and "Core
+ * architecture > Embedding Engine" (admission state saved with the table). */
 recis_status recis_idmap_key_ages(recis_table* t, const int64_t* keys, int64_t n, uint32_t* ages,
                                   int32_t set, hipStream_t s);
 recis_status recis_idmap_sketch(recis_table* t, uint32_t* counters, int32_t set, hipStream_t s);
 
-/* Table statistics (synchronises `s`); st: host. */
+/* Table statistics (synchronises `s`); st: host.
+ * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Key optimisations > Efficient dynamic Embedding"
+ * (IDMap, EmbeddingBlocks and where they live). */
 recis_status recis_idmap_stats(recis_table* t, recis_table_stats* st, hipStream_t s);
 
-/* Synchronises `s` and returns the first error recorded on the device since
- * the last call, clearing it. */
+/* Synchronises `s` and returns one error recorded on the device: KEY_RANGE,
+ * then INVALID_ARG, each cleared as it is returned; then CAPACITY, which
+ * stays (every later call returns it) until an eviction pass clears it.
+ * RECIS_OK when none is recorded.  (The pages give no error model; the
+ * sticky CAPACITY keeps a full table from being mistaken for a healthy one.) */
 recis_status recis_get_error(recis_table* t, hipStream_t s);
 
+/* Text of a status code (no passage of the pages: error reporting). */
 const char* recis_status_string(recis_status st);
 
 /* Instrumentation (not part of the method): while set, every launch of the
