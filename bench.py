@@ -80,8 +80,8 @@ WORKLOADS = {
         "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 10,
         "table": {"slot_capacity": 1 << 29, "block_rows": 1 << 20},
         "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bwd_long_partial"),
-        # the oracle baseline: these features of the first timed step (5.2M IDs)
-        "cpu_features": 10,
+        # the oracle baseline: these features of the first timed step (21M IDs)
+        "cpu_features": 40,
     },
     # config 1: ten steps from an empty table; launch-bound, so its figure is
     # the step latency
