@@ -63,7 +63,7 @@ WORKLOADS = {
         "spec": W.spec_ctr, "F": 26, "B": 8192, "fill": "resident", "steps": 20, "warmup": 5,
         "new_per_step": 1_000_000,
         "table": {"slot_capacity": 1 << 27, "block_rows": 1 << 20},
-        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bucket_count"),
+        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_occ_tile", "k_tile"),
     },
     "seq": {
         "title": "Lifelong behaviour sequence: 1 feature of length 1000, batch 2048, dim 128 bf16 storage "
@@ -72,14 +72,14 @@ WORKLOADS = {
         "spec": W.spec_seq, "F": 1, "B": 2048, "fill": "steps", "fill_steps": 10, "steps": 20, "warmup": 5,
         "new_per_step": 250_000,
         "table": {"slot_capacity": 1 << 23, "block_rows": 1 << 20},
-        "candidates": ("k_bwd_short", "k_fwd_gather", "k_bwd_long_partial", "k_bucket_emit", "k_part_scatter"),
+        "candidates": ("k_bwd_short", "k_fwd_gather", "k_bwd_long_partial", "k_bucket_emit", "k_occ_tile"),
     },
     "capacity": {
         "title": "Capacity stress: 200M pre-populated rows x dim 64 fp32 + Adam m/v, 100 features, batch 65536, "
                  "bag length Poisson(8), Zipf(1.2) IDs with 2% novel per step, sum pooling",
         "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 10,
         "table": {"slot_capacity": 1 << 29, "block_rows": 1 << 20},
-        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bucket_emit", "k_part_scatter", "k_bwd_long_partial"),
+        "candidates": ("k_bwd_short", "k_fwd_pool", "k_bwd_long_partial", "k_occ_tile", "k_bucket_emit"),
         # the oracle baseline: these features of the first timed step (21M IDs)
         "cpu_features": 40,
     },
@@ -244,13 +244,20 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
         resident rows' params D s; the output Bg D 4.
       k_fwd_gather: per occurrence its row reference 8 and its output row D s;
         resident rows' params D s.
-      k_part_scatter: per occurrence its raw ID 8 read and its partition
-        record (key, occurrence, bag) 16 written.
-      k_bucket_count: per occurrence its record's key 8.
-      k_bucket_emit: per occurrence its record 16 read, and its inverse index 4,
-        grouped entry 4 and forward reference 8 written; per distinct key its
-        key and count 12, group offset 4, IDMap slot read 16 and slot index 8;
-        per new key its IDMap slot written 16.
+      Lookup kernels, with Pp the (key, tile) pairs of the call: the
+      distinct keys of each tile of 4096 consecutive occurrences, summed.
+      k_tile: per occurrence its raw ID 8 read and its index among its
+        tile's pairs 2 written; per pair its key and count 12 written.
+      k_pair_scatter: per pair its key and count 12 read, and its partition
+        record (key, pair, count) 16 and the record's position 4 written.
+      k_bucket_count: per pair its record's key and count 12.
+      k_bucket_emit: per pair its record 16 read and its resolved record
+        (forward reference, distinct-key index, group position) 16 written;
+        per distinct key its key and count 12, group offset 4, IDMap slot read
+        16 and slot index 8; per new key its IDMap slot written 16.
+      k_occ_tile: per occurrence its pair index 2 read, and its inverse index
+        4, grouped entry 4 and forward reference 8 written; per pair its
+        record's position 4 and resolved record 16 read; offsets 4 (Bg + 1).
       k_bwd_long_partial: per long entry 4; per chunk a partial of D fp64
         written; the gradient rows of the bags its entries touch, at most
         min(E_l, Bg) pooled (one row per entry when not pooled).
@@ -264,9 +271,12 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
     bwd_short = 16 * Us + 4 * shape["E_s"] + (Us - Usn) * 2 * P + Usn * P + g_short
     fwd = 8 * N + 4 * (Bg + 1) + Uhit * D * s + Bg * D * 4
     gather = 8 * N + Uhit * D * s + N * D * s
-    scatter = 24 * N
-    count = 8 * N
-    emit = 32 * N + 40 * Um + 16 * Unew
+    Pp = shape.get("pairs", 0)
+    tile = 10 * N + 12 * Pp
+    scatter = 32 * Pp
+    count = 12 * Pp
+    emit = 32 * Pp + 40 * Um + 16 * Unew
+    occ = 18 * N + 20 * Pp + 4 * (Bg + 1)
     El = shape["E_l"]
     g_long = min(El, Bg) * D * gs if pooled else El * D * gs
     long_partial = 4 * El + shape["chunks_l"] * D * 8 + g_long
@@ -275,7 +285,8 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
     fwd_call = 4 * N + 8 * Um + Uhit * D * s + out_b
     bwd_call = 4 * N + 8 * Um + Uhit * 2 * P + Unew * P + grad_b
     return {"k_bwd_short": bwd_short, "k_fwd_pool": fwd, "k_fwd_gather": gather,
-            "k_part_scatter": scatter, "k_bucket_count": count, "k_bucket_emit": emit,
+            "k_tile": tile, "k_pair_scatter": scatter, "k_bucket_count": count, "k_bucket_emit": emit,
+            "k_occ_tile": occ,
             "k_bwd_long_partial": long_partial, "step": ins + fwd_call + bwd_call}
 
 
@@ -936,6 +947,7 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     Uhit = Um - Unew
     Bg = F * B
     shape = step_shapes(timed_res, U, int(st0.rows_in_use))
+    shape["pairs"] = (st1.lookup_pairs - st0.lookup_pairs) / K
     alg = algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s_bytes, S, gs, pooled)
     a_bytes = alg[dom] if dom in alg else None
     achieved = a_bytes / t_dom / 1e9 if a_bytes else None

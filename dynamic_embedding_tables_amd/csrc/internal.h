@@ -75,21 +75,24 @@ struct __align__(16) DedupSlot {
   int uidx;   // index of the key among the call's distinct keys
 };
 
-// One occurrence in its hash bucket: key, merged occurrence index, and its
-// grouped-list value (bag or occurrence).
+// One tile-distinct key in its hash bucket (the lookup deduplicates each
+// tile of kTileOcc occurrences first): the key, its pair index (tile *
+// kTileOcc + its index among the tile's distinct keys) and its occurrences
+// in the tile.
 struct __align__(16) PartEntry {
   long long key;
-  int occ;
-  int g;
+  int pid;
+  int w;
 };
 
-// What the bucket kernels leave in place of an occurrence's record once its
-// key is resolved: the forward reference and the distinct-key index.  The
-// lookup's last kernel copies them out in occurrence order.
+// What the bucket kernels leave in place of a pair's record once its key is
+// resolved: the forward reference, the distinct-key index, and where the
+// pair's occurrences start in the key's group.  The lookup's last kernel
+// reads them tile by tile.
 struct __align__(16) PartOut {
   long long ref;
   int u;
-  int pad;
+  int gpos;
 };
 static_assert(sizeof(PartOut) == sizeof(PartEntry), "written in place of the record");
 
@@ -109,6 +112,9 @@ struct DevCounters {
   // the scan kernel once per call)
   unsigned long long claim_attempts;
   unsigned long long claim_failures;
+  // (key, tile) pairs: distinct keys of each tile of kTileOcc consecutive
+  // occurrences, summed over the tiles of every insert_find since creation
+  unsigned long long lookup_pairs;
 };
 
 // Device view of one feature of a call.
@@ -385,6 +391,10 @@ struct recis_table {
   int* ubase = nullptr;
   int* uslot = nullptr;
   int* posmap = nullptr;
+  long long* tkey = nullptr;  // tile-distinct keys, their counts, per-tile sizes
+  int* tcnt = nullptr;
+  int* tile_n = nullptr;
+  unsigned short* occ_local = nullptr;  // occurrence -> index among its tile's distinct keys
   unsigned long long* blk_sums = nullptr;
   unsigned* last_use = nullptr;  // [slot_cap] when cfg.track_last_use
   unsigned step = 0;             // counting lookups so far
@@ -422,10 +432,12 @@ __device__ __forceinline__ int xcd_block(int i, int G) {
   return x * q + (x < r ? x : r) + k;
 }
 
-// Hash partition of a lookup call.
+// Hash partition of a lookup call.  Tiles of kTileOcc consecutive
+// occurrences are deduplicated in LDS first; their distinct keys (pairs)
+// are what the partition and the bucket kernels handle.
+constexpr int kTileOcc = 4096;
+constexpr int kTileTab = 2 * kTileOcc;  // the tile's LDS table, at most half full
 constexpr int kPartThreads = 1024;   // partition kernels' block size
-constexpr int kPartPer = 8;          // occurrences per thread per pass
-constexpr int kPartOcc = kPartThreads * kPartPer;
 constexpr int kMaxPartBlocks = 1024;
 constexpr int kBucketOcc = 384;      // target occurrences per bucket
 constexpr int kMaxBucketBits = 13;
@@ -449,13 +461,20 @@ struct LookupLaunch {
   DedupSlot* dd;  // empty between calls; regions of it back overflowed buckets
   int nbits, nbk;             // hash buckets: nbk = 2^nbits
   int part_blocks;            // partition blocks
-  long long part_range;       // occurrences per partition block
+  long long tiles_per_block;  // tiles per partition block
+  long long ntiles;           // tiles of the call
+  long long* tkey;            // [ntiles * kTileOcc]: each tile's distinct keys, from its start
+  int* tcnt;                  // [ntiles * kTileOcc]: their occurrences in the tile
+  int* tile_n;                // [ntiles]: distinct keys per tile
+  int* tile_bag;              // [ntiles]: the bag of each tile's first occurrence
+  unsigned short* occ_local;  // N: each occurrence's index among its tile's distinct keys
+  int* obase;                 // nbk + 1: occurrences per bucket, then the first grouped position
   int big_tab;                // buckets average more than kBucketOcc occurrences
   int* hist;                  // [part_blocks][nbk]
   int* bbase;                 // nbk + 1: first position of each bucket
   int* ubase;                 // nbk + 1: distinct keys per bucket, then their first index
-  PartEntry* part;            // N
-  int* posmap;                // N: position of each occurrence's record in part
+  PartEntry* part;            // pairs (at most N)
+  int* posmap;                // [ntiles * kTileOcc]: position of each pair's record in part
   unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
   unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
   unsigned long long* blk_claim; // per key tile: IDMap slot claims << 32 | claims lost

@@ -10,29 +10,33 @@
 //
 // Kernel sequence of one call (all on one stream, no host read-back):
 //   k_prep      merged bag offsets, offset validation, per-call counters
-//   k_part_hist / k_part_colscan / k_scan_small / k_part_scatter
-//               transform + tag every occurrence and partition the call by
-//               the top bits of the key's hash (one radix-sort pass); the
-//               column scan also cuts heavy buckets (hot keys) into slices
+//   k_tile      transform + tag every occurrence and deduplicate each tile of
+//               kTileOcc consecutive occurrences in LDS: the tile's distinct
+//               keys with their counts (its pairs), each occurrence's index
+//               among them, and per partition block a histogram of the
+//               pairs' hash buckets (the top bits of the key's hash)
+//   k_part_colscan / k_scan_small / k_pair_scatter
+//               the pairs partitioned by hash bucket (one radix-sort pass);
+//               the column scan also cuts heavy buckets into slices
 //   k_bucket    one bucket per block, twice around a scan of the per-bucket
-//               distinct counts: dedup in LDS, counts, distinct-key indices,
+//               distinct counts and occurrences: dedup of the bucket's pairs
+//               in LDS, counts (summed over the pairs), distinct-key indices,
 //               group offsets; in the second launch also the IDMap probe /
 //               insert of every distinct key (count, admission decision,
 //               without global atomics: the block owns the bucket's IDMap
-//               regions), then each occurrence's grouped bag / occurrence
-//               entry, and its inverse index and forward reference in place
-//               of its partition record (a bucket that
-//               overflows the LDS table, from colliding inputs, uses a global
-//               one; a heavy bucket is counted slice by slice and its
-//               occurrences are written by k_key_scan's other blocks)
+//               regions), then for each pair its distinct-key index, forward
+//               reference and span of its key's group, in place of its record
+//               (a bucket that overflows the LDS table, from colliding inputs,
+//               uses a global one; a heavy bucket is counted slice by slice
+//               and its pairs are resolved by k_key_scan's other blocks)
 //   k_key_scan  block 0: exclusive scan of the per-bucket sums; rows come
 //               from the free list first, then from the bump pointer -- by
 //               prefix sum, not by atomics
 //   k_key_finalize  per bucket: row assignment (the new row is marked
 //               pending, not written: its values are the initializer's until
 //               its first update), backward plan for long keys
-//   k_occ_out   inverse index and forward reference of every occurrence, in
-//               occurrence order, gathered from the partition array
+//   k_occ_tile  per tile: every occurrence's inverse index, forward reference
+//               and grouped entry, from its pair's resolved record
 // Memory accesses that do not depend on each other are issued as one batch
 // per thread (all loads of a phase before any use), so that each thread
 // waits once per phase rather than once per item.
@@ -172,6 +176,11 @@ __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
   if (bad) atomicOr(&t.ctr->error, kErrInvalid);
   const long long oc = o < 0 ? 0 : ((long long)o > fd.n ? fd.n : o);
   L.res.bag_offsets[idx] = (int)(fd.base + oc);
+  // the tiles whose first occurrence falls in this bag (a bag is rarely
+  // longer than a tile): with valid offsets every tile gets exactly one
+  const long long oc1 = o1 < 0 ? 0 : ((long long)o1 > fd.n ? fd.n : o1);
+  const long long m0 = fd.base + oc, m1 = fd.base + oc1;
+  for (long long tl = (m0 + kTileOcc - 1) / kTileOcc; tl * kTileOcc < m1; ++tl) L.tile_bag[tl] = (int)idx;
 }
 
 // ------------------------------------------------------ hash partition
@@ -207,39 +216,125 @@ struct FeatCursor {
   FeatDev fd;
   long long lo = 1, hi = 0;  // [lo, hi) of the cached feature
 };
-__device__ __forceinline__ long long key_of(const LookupLaunch& L, FeatCursor& c, long long j, unsigned& err) {
+__device__ __forceinline__ void cursor_to(const LookupLaunch& L, FeatCursor& c, long long j) {
   if (j < c.lo || j >= c.hi) {
     c.fd = L.feats[feature_of(L.feats, L.F, j)];
     c.lo = c.fd.base;
     c.hi = c.fd.base + c.fd.n;
   }
-  return transform_value(*gread<long long>(c.fd.values + (j - c.fd.base)), c.fd, L.bnd_pool, err);
 }
 
-__global__ __launch_bounds__(kPartThreads) void k_part_hist(LookupLaunch L, TableDev t) {
+// First-level dedup, one tile of kTileOcc consecutive occurrences at a time
+// (a partition block takes tiles_per_block of them): transform + tag every
+// occurrence, deduplicate the tile in an LDS table, note each occurrence's
+// index among the tile's distinct keys, and write the tile's distinct keys
+// with their counts (its pairs) from the tile's start in tkey / tcnt.  The
+// block's histogram counts pairs per hash bucket.  Skewed inputs repeat
+// keys within a tile (0.27 pairs per occurrence on the capacity workload),
+// so everything up to the last pass handles pairs, not occurrences.
+__global__ __launch_bounds__(kPartThreads) void k_tile(LookupLaunch L, TableDev t) {
+  constexpr int kPer = kTileOcc / kPartThreads;
+  __shared__ long long s_key[kTileTab];
+  __shared__ int s_cnt[kTileTab];
+  __shared__ unsigned short s_idx[kTileTab];
+  __shared__ unsigned short s_list[kTileOcc];
   __shared__ int s_h[kMaxBuckets];
+  __shared__ int s_nd;
   __shared__ unsigned s_err;
   const int tid = threadIdx.x;
   const int pb = xcd_block((int)blockIdx.x, (int)gridDim.x);  // partition block
-  const long long j0 = (long long)pb * L.part_range;
-  const long long j1 = j0 + L.part_range < L.N ? j0 + L.part_range : L.N;
+  const long long t0 = (long long)pb * L.tiles_per_block;
+  const long long t1 = t0 + L.tiles_per_block < L.ntiles ? t0 + L.tiles_per_block : L.ntiles;
   for (int b = tid; b < L.nbk; b += kPartThreads) s_h[b] = 0;
   if (tid == 0) s_err = 0;
-  __syncthreads();
-  FeatCursor fc;
+  // The raw IDs of the next tile are loaded while this one is deduplicated:
+  // the addresses first (the feature cursor may have to wait for a feature's
+  // descriptor), then the loads together, so that each thread has all of
+  // them in flight at once.  fl follows the loads, fu the transforms.
+  FeatCursor fl, fu;
   unsigned err = 0;
-  for (long long c0 = j0; c0 < j1; c0 += (long long)kPartThreads * kPartPer) {
-    long long key[kPartPer];
+  long long nraw[kPer];
+  auto load_tile = [&](long long tl) {
+    const long long a0 = tl * kTileOcc;
+    const long long a1 = a0 + kTileOcc < L.N ? a0 + kTileOcc : L.N;
+    const long long* src[kPer];
 #pragma unroll
-    for (int k = 0; k < kPartPer; ++k) {
-      const long long j = c0 + tid + (long long)k * kPartThreads;
-      key[k] = j < j1 ? key_of(L, fc, j, err) : 0;
+    for (int k = 0; k < kPer; ++k) {
+      const long long j = a0 + tid + (long long)k * kPartThreads;
+      src[k] = nullptr;
+      if (j < a1) {
+        cursor_to(L, fl, j);
+        src[k] = fl.fd.values + (j - fl.fd.base);
+      }
     }
 #pragma unroll
-    for (int k = 0; k < kPartPer; ++k) {
-      const long long j = c0 + tid + (long long)k * kPartThreads;
-      if (j < j1) atomicAdd(&s_h[bucket_of(key[k], L.nbits)], 1);
+    for (int k = 0; k < kPer; ++k) nraw[k] = src[k] ? *gread<long long>(src[k]) : 0;
+  };
+  if (t0 < t1) load_tile(t0);
+  for (long long tile = t0; tile < t1; ++tile) {
+    for (int i = tid; i < kTileTab; i += kPartThreads) {
+      s_key[i] = kEmptyKey;
+      s_cnt[i] = 0;
     }
+    if (tid == 0) s_nd = 0;
+    __syncthreads();
+    const long long j0 = tile * kTileOcc;
+    const long long j1 = j0 + kTileOcc < L.N ? j0 + kTileOcc : L.N;
+    long long raw[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) raw[k] = nraw[k];
+    long long key[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const long long j = j0 + tid + (long long)k * kPartThreads;
+      key[k] = 0;
+      if (j < j1) {
+        cursor_to(L, fu, j);
+        key[k] = transform_value(raw[k], fu.fd, L.bnd_pool, err);
+      }
+    }
+    // after the transforms: the wait at the end of a cursor update would
+    // otherwise wait for these loads too
+    if (tile + 1 < t1) load_tile(tile + 1);
+    unsigned h[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool act = j0 + tid + (long long)k * kPartThreads < j1;
+      h[k] = 0;
+      if (act) {
+        unsigned q = (unsigned)(fib_mix(key[k]) >> 32) & (kTileTab - 1);
+        while (true) {  // at most kTileOcc keys in kTileTab slots: a free slot is always found
+          const long long o = (long long)atomicCAS((unsigned long long*)&s_key[q], (unsigned long long)kEmptyKey,
+                                                   (unsigned long long)key[k]);
+          if (o == kEmptyKey) {
+            const int l = atomicAdd(&s_nd, 1);
+            s_list[l] = (unsigned short)q;
+            s_idx[q] = (unsigned short)l;
+            break;
+          }
+          if (o == key[k]) break;
+          q = (q + 1) & (kTileTab - 1);
+        }
+        h[k] = q;
+      }
+      lds_add1(s_cnt, h[k], act);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const long long j = j0 + tid + (long long)k * kPartThreads;
+      if (j < j1) L.occ_local[j] = s_idx[h[k]];
+    }
+    const int nd = s_nd;
+    for (int l = tid; l < nd; l += kPartThreads) {
+      const int q = s_list[l];
+      const long long kk = s_key[q];
+      L.tkey[j0 + l] = kk;
+      L.tcnt[j0 + l] = s_cnt[q];
+      atomicAdd(&s_h[bucket_of(kk, L.nbits)], 1);
+    }
+    if (tid == 0) L.tile_n[tile] = nd;
+    __syncthreads();  // the next tile reuses the table
   }
   if (err) atomicOr(&s_err, err);
   __syncthreads();
@@ -282,7 +377,8 @@ __global__ __launch_bounds__(kPartThreads) void k_part_colscan(LookupLaunch L) {
     int ns = 0, e0 = 0;
     if (b < L.nbk) {
       L.bbase[b] = all;  // total, scanned by k_scan_small
-      L.ubase[b] = 0;    // a light bucket's block writes it, a heavy one's slices add to it
+      L.ubase[b] = 0;    // a light bucket's block writes these, a heavy one's slices add to them
+      L.obase[b] = 0;
       if (all > kHeavyOcc) {  // a heavy bucket: its slices (few buckets, so one atomic each)
         ns = (all + kSliceOcc - 1) / kSliceOcc;
         e0 = atomicAdd(&L.hslice[0], ns);
@@ -304,9 +400,18 @@ __global__ __launch_bounds__(kPartThreads) void k_part_colscan(LookupLaunch L) {
 }
 
 // In-place exclusive scan of a[0..n) (n <= kMaxBuckets), a[n] = total, and
-// the total also to *total_ll when given.  Bucket positions (bbase) and the
-// distinct-key bases of the buckets (ubase).
-__global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long long* total_ll) {
+// the total also to *total_ll when given.  Bucket positions (bbase), and the
+// distinct-key and occurrence bases of the buckets (ubase, obase: the second
+// array, scanned by the same launch).
+__device__ void scan_small(int* a, int n, long long* total_ll);
+__global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int* a2, int n, long long* total_ll) {
+  scan_small(a, n, total_ll);
+  if (a2) {
+    __syncthreads();
+    scan_small(a2, n, nullptr);
+  }
+}
+__device__ void scan_small(int* a, int n, long long* total_ll) {
   constexpr int kPer = kMaxBuckets / kPartThreads;  // n <= kMaxBuckets
   __shared__ int s_w[kPartThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -342,95 +447,42 @@ __global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int n, long
   }
 }
 
-// Grouped-list value of merged occurrence j: its bag (f * B + i), found by a
-// binary search over the pass's window of merged bag offsets (kept in LDS
-// when it fits), or j itself when grouping by occurrence.
-__global__ __launch_bounds__(kPartThreads) void k_part_scatter(LookupLaunch L) {
+// Every pair of the block's tiles to its bucket's range (the same partition
+// block as in k_tile; the blocks of one XCD write neighbouring records of
+// every bucket), noting where each pair's record went.
+__global__ __launch_bounds__(kPartThreads) void k_pair_scatter(LookupLaunch L) {
+  constexpr int kPer = kTileOcc / kPartThreads;
   __shared__ int s_h[kMaxBuckets];
-  __shared__ int s_off[kBagWin];
-  __shared__ int s_blo, s_bhi;
   const int tid = threadIdx.x;
-  // the same partition block as in k_part_hist; the blocks of one XCD write
-  // neighbouring records of every bucket
   const int pb = xcd_block((int)blockIdx.x, (int)gridDim.x);
-  const long long j0 = (long long)pb * L.part_range;
-  const long long j1 = j0 + L.part_range < L.N ? j0 + L.part_range : L.N;
-  const bool by_occ = (L.flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
-  const int* off = L.res.bag_offsets;  // merged, F * B + 1 entries
-  const int nbags = L.F * L.B;
+  const long long t0 = (long long)pb * L.tiles_per_block;
+  const long long t1 = t0 + L.tiles_per_block < L.ntiles ? t0 + L.tiles_per_block : L.ntiles;
   const int* row = L.hist + (long long)pb * L.nbk;
   for (int b = tid; b < L.nbk; b += kPartThreads) s_h[b] = L.bbase[b] + row[b];
-  FeatCursor fc;
-  unsigned err = 0;
-  for (long long c0 = j0; c0 < j1; c0 += (long long)kPartOcc) {
-    const long long c1 = c0 + kPartOcc < j1 ? c0 + kPartOcc : j1;
-    long long key[kPartPer];
+  __syncthreads();
+  for (long long tile = t0; tile < t1; ++tile) {
+    const int nd = L.tile_n[tile];
+    const long long p0 = tile * kTileOcc;
+    long long key[kPer];
+    int w[kPer];
 #pragma unroll
-    for (int k = 0; k < kPartPer; ++k) {
-      const long long j = c0 + tid + (long long)k * kPartThreads;
-      key[k] = j < c1 ? key_of(L, fc, j, err) : 0;
+    for (int k = 0; k < kPer; ++k) {
+      const int l = tid + k * kPartThreads;
+      key[k] = l < nd ? L.tkey[p0 + l] : 0;
+      w[k] = l < nd ? L.tcnt[p0 + l] : 0;
     }
-    // the bags of this pass's occurrences: [s_blo, s_bhi], their offsets to
-    // LDS when they fit (a pass of kPartOcc occurrences spans few bags
-    // unless most of them are empty)
-    if (!by_occ && tid < 2) {
-      // bag of occurrence j: the last i with off[i] <= j (empty bags skipped)
-      const long long j = tid == 0 ? c0 : c1 - 1;
-      int lo = 0, hi = nbags;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((long long)off[mid] <= j) lo = mid + 1;
-        else hi = mid;
-      }
-      const int b = lo - 1 < 0 ? 0 : lo - 1;
-      if (tid == 0) s_blo = b;
-      else s_bhi = b;
-    }
-    __syncthreads();
-    const int blo = by_occ ? 0 : s_blo, wn = by_occ ? 0 : s_bhi - s_blo + 2;
-    const bool win = wn > 0 && wn <= kBagWin;
-    if (win)
-      for (int i = tid; i < wn; i += kPartThreads) s_off[i] = off[blo + i];
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kPartPer; ++k) {
-      const long long j = c0 + tid + (long long)k * kPartThreads;
-      if (j >= c1) continue;
-      int g;
-      if (by_occ) {
-        g = (int)j;
-      } else {
-        int lo, hi;
-        if (win) {
-          lo = 0;
-          hi = wn - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((long long)s_off[mid] <= j) lo = mid + 1;
-            else hi = mid;
-          }
-          lo += blo;
-        } else {
-          lo = 0;
-          hi = nbags;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((long long)off[mid] <= j) lo = mid + 1;
-            else hi = mid;
-          }
-        }
-        g = lo - 1;
-        g = g < 0 ? 0 : (g > nbags - 1 ? nbags - 1 : g);
-      }
+    for (int k = 0; k < kPer; ++k) {
+      const int l = tid + k * kPartThreads;
+      if (l >= nd) continue;
       const int pos = atomicAdd(&s_h[bucket_of(key[k], L.nbits)], 1);
       PartEntry e;
       e.key = key[k];
-      e.occ = (int)j;
-      e.g = g;
+      e.pid = (int)(p0 + l);
+      e.w = w[k];
       L.part[pos] = e;
-      L.posmap[j] = pos;
+      L.posmap[p0 + l] = pos;
     }
-    __syncthreads();  // the next pass reloads the window
   }
 }
 
@@ -583,14 +635,14 @@ __device__ __forceinline__ long long ref_of_row(const TableDev& t, long long v, 
   return (long long)row_ptr(t.rs, v);
 }
 
-// The resolved occurrence at partition position p (in place of its record,
-// which its thread has read): written in bucket order, so the stores of a
-// wave are contiguous; k_occ_out turns them into occurrence order.
-__device__ __forceinline__ void put_out(const LookupLaunch& L, long long p, long long ref, int u) {
+// The resolved pair at partition position p (in place of its record, which
+// its thread has read): written in bucket order, so the stores of a wave are
+// contiguous; k_occ_tile reads them tile by tile.
+__device__ __forceinline__ void put_out(const LookupLaunch& L, long long p, long long ref, int u, int gpos) {
   PartOut o;
   o.ref = ref;
   o.u = u;
-  o.pad = 0;
+  o.gpos = gpos;
   reinterpret_cast<PartOut*>(L.part)[p] = o;
 }
 
@@ -612,8 +664,11 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
   }
   __syncthreads();
   if (!EMIT) {
+    int wsum = 0;  // the bucket's occurrences
     for (int i = tid; i < m; i += kThreads) {
-      const long long key = L.part[s + i].key;
+      const PartEntry e = L.part[s + i];
+      const long long key = e.key;
+      wsum += e.w;
       unsigned long long h = (fib_mix(key) >> 20) % cap;
       while (true) {
         const long long c = ld_key(&R[h]);
@@ -625,8 +680,9 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
         }
         h = h + 1 == cap ? 0 : h + 1;
       }
-      atomicAdd(&R[h].count, 1);
+      atomicAdd(&R[h].count, e.w);
     }
+    atomicAdd(&s_cursor, wsum);
     __syncthreads();
     for (unsigned long long h = tid; h < cap; h += kThreads) {
       const long long key = ld_key(&R[h]);
@@ -635,10 +691,14 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
       if (L.sketching) sketch_count(t, key, ld_int(&R[h].count));
     }
     __syncthreads();
-    if (tid == 0) L.ubase[b] = s_nd;
+    if (tid == 0) {
+      L.ubase[b] = s_nd;
+      L.obase[b] = s_cursor;
+    }
     return;
   }
   const long long ub = L.ubase[b];
+  const int ob = L.obase[b];  // the bucket's first grouped position
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
   unsigned long long sum = 0, sum_long = 0, claims = 0;
   unsigned err = 0;
@@ -650,7 +710,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     const int o = atomicAdd(&s_cursor, c);
     L.res.unique_keys[u] = key;
     L.res.counts[u] = c;
-    st_int(&L.res.unique_offsets[u], s + o);
+    st_int(&L.res.unique_offsets[u], ob + o);
     st_int(&R[h].uidx, (int)u);
     // an empty IDMap slot goes to whichever thread's CAS takes it
     auto claim = [&](unsigned long long q) {
@@ -678,11 +738,10 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     unsigned long long h = (fib_mix(e.key) >> 20) % cap;
     while (ld_key(&R[h]) != e.key) h = h + 1 == cap ? 0 : h + 1;
     const int u = ld_int(&R[h].uidx);
-    const int pos = atomicSub(&R[h].count, 1) - 1;  // the group is filled from its end
-    L.res.grouped[ld_int(&L.res.unique_offsets[u]) + pos] = e.g;
+    const int pos = atomicSub(&R[h].count, e.w) - e.w;  // the group is filled from its end
     const long long v = (long long)__hip_atomic_load(reinterpret_cast<unsigned long long*>(&L.res.unique_rows[u]),
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    put_out(L, s + i, ref_of_row(t, v, e.key), u);
+    put_out(L, s + i, ref_of_row(t, v, e.key), u, ld_int(&L.res.unique_offsets[u]) + pos);
   }
   __syncthreads();
   for (unsigned long long h = tid; h < cap; h += kThreads) {
@@ -730,8 +789,11 @@ __device__ __forceinline__ void slice_dedup(const LookupLaunch& L, int s0, int s
     const int i = i0 + tid;
     const bool act = i < s1;
     unsigned h = 0;
+    int w = 0;
     if (act) {
-      const long long key = L.part[i].key;
+      const PartEntry e = L.part[i];
+      const long long key = e.key;
+      w = e.w;
       h = (unsigned)(fib_mix(key) >> hs) & (TAB - 1);
       while (true) {  // a slice has fewer distinct keys than the table has free slots
         const long long o = (long long)atomicCAS((unsigned long long*)&s_key[h], (unsigned long long)kEmptyKey,
@@ -744,7 +806,7 @@ __device__ __forceinline__ void slice_dedup(const LookupLaunch& L, int s0, int s
         h = (h + 1) & (TAB - 1);
       }
     }
-    lds_add1(s_cnt, h, act);
+    if (act) atomicAdd(&s_cnt[h], w);
   }
 }
 
@@ -794,12 +856,14 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     if (tid == 0) s_nd = 0;
     __syncthreads();
     slice_dedup<TAB, kThreads>(L, s0, s1, hs, s_key, s_cnt, s_list, s_nd);
+    if (tid == 0) s_cursor = 0;
     __syncthreads();
     DedupSlot* R = L.dd + 2ll * s;
     const unsigned long long cap = 2ull * (unsigned long long)m;
     for (int idx = tid; idx < s_nd; idx += kThreads) {
       const int hl = s_list[idx];
       const long long key = s_key[hl];
+      atomicAdd(&s_cursor, s_cnt[hl]);  // the slice's occurrences
       unsigned long long h = (fib_mix(key) >> 20) % cap;
       while (true) {
         const long long c = ld_key(&R[h]);
@@ -821,6 +885,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
       if (L.sketching) sketch_count(t, key, s_cnt[hl]);
     }
     __syncthreads();  // the LDS table is reused by the next slice
+    if (tid == 0) atomicAdd(&L.obase[b], s_cursor);
     }
     return;
   }
@@ -828,7 +893,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   const int s = L.bbase[b], m = L.bbase[b + 1] - s;
   if (m == 0) {
     if (tid == 0) {
-      if (!EMIT) L.ubase[b] = 0;
+      if (!EMIT) L.ubase[b] = L.obase[b] = 0;
       else L.blk_sums[b] = L.blk_long[b] = L.blk_claim[b] = 0;
     }
     return;
@@ -837,6 +902,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     if (!EMIT) return;  // its slices count it
     // EMIT's key pass of a heavy bucket: the listed keys in list order
     const long long ub = L.ubase[b], nd = L.ubase[b + 1] - ub;
+    const int ob = L.obase[b];
     const DedupSlot* R = L.dd + 2ll * s;
     const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
     unsigned long long sum = 0, sum_long = 0, run = 0, claims = 0;
@@ -865,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
       const long long u = ub + idx;
       L.res.unique_keys[u] = key;
       L.res.counts[u] = c;
-      L.res.unique_offsets[u] = (int)(s + o);
+      L.res.unique_offsets[u] = (int)(ob + o);
       // an empty IDMap slot goes to whichever thread's CAS takes it
       auto claim = [&](unsigned long long q) {
         const bool won = atomicCAS((unsigned long long*)&t.slots[q].key, (unsigned long long)kEmptyKey,
@@ -907,10 +973,16 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   __syncthreads();
   for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
     long long key[kBucketPer];
+    int w[kBucketPer];
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
       const int i = i0 + tid + k * kThreads;
-      key[k] = i < m ? L.part[s + i].key : 0;
+      PartEntry e;
+      e.key = 0;
+      e.w = 0;
+      if (i < m) e = L.part[s + i];
+      key[k] = e.key;
+      w[k] = e.w;
     }
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
@@ -938,7 +1010,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
         }
         counted = steps < TAB;
       }
-      if (counted) atomicAdd(&s_cnt[h], 1);
+      if (counted) atomicAdd(&s_cnt[h], w[k]);
     }
   }
   __syncthreads();
@@ -947,13 +1019,21 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     return;
   }
   if (!EMIT) {
-    if (tid == 0) L.ubase[b] = s_nd;
-    if (L.sketching)
-      for (int idx = tid; idx < s_nd; idx += kThreads) sketch_count(t, s_key[s_list[idx]], s_cnt[s_list[idx]]);
+    for (int idx = tid; idx < s_nd; idx += kThreads) {
+      const int c = s_cnt[s_list[idx]];
+      atomicAdd(&s_cursor, c);  // the bucket's occurrences
+      if (L.sketching) sketch_count(t, s_key[s_list[idx]], c);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      L.ubase[b] = s_nd;
+      L.obase[b] = s_cursor;
+    }
     return;
   }
   const int nd = s_nd;
   const long long ub = L.ubase[b];
+  const int ob = L.obase[b];  // the bucket's first grouped position
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
   // an empty IDMap slot goes to the first thread that enters it in the set
   // (slot indices are below 2^32; the last index of a 2^32-slot table, equal
@@ -985,7 +1065,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     const int o = atomicAdd(&s_cursor, c);
     L.res.unique_keys[u] = key;
     L.res.counts[u] = c;
-    L.res.unique_offsets[u] = s + o;
+    L.res.unique_offsets[u] = ob + o;
     s_u[h] = (int)u;
     s_cnt[h] = o;  // from here on: the next free position of the key's group
     const ProbeOut po = idmap_probe(t, key, c, find_only, claim, L.sketching != 0);
@@ -1019,11 +1099,8 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
         h = (unsigned)(fib_mix(e[k].key) >> hs) & (TAB - 1);
         while (s_key[h] != e[k].key) h = (h + 1) & (TAB - 1);
       }
-      const int pos = act ? atomicAdd(&s_cnt[h], 1) : 0;
-      if (act) {
-        L.res.grouped[s + pos] = e[k].g;
-        put_out(L, s + i0 + tid + k * kThreads, s_ref[h], s_u[h]);
-      }
+      const int pos = act ? atomicAdd(&s_cnt[h], e[k].w) : 0;
+      if (act) put_out(L, s + i0 + tid + k * kThreads, s_ref[h], s_u[h], ob + pos);
     }
   }
 }
@@ -1089,11 +1166,8 @@ __device__ void heavy_occ(const LookupLaunch& L, const TableDev& t, int e0, int 
       h = (unsigned)(fib_mix(en.key) >> hs) & (TAB - 1);
       while (s_key[h] != en.key) h = (h + 1) & (TAB - 1);
     }
-    const int pos = lds_add1(s_cnt, h, act);
-    if (act) {
-      L.res.grouped[pos] = en.g;
-      put_out(L, i, s_ref[h], s_u[h]);
-    }
+    const int pos = act ? atomicAdd(&s_cnt[h], en.w) : 0;
+    if (act) put_out(L, i, s_ref[h], s_u[h], pos);
   }
   __syncthreads();  // the LDS table is reused by the next slice
   }
@@ -1186,6 +1260,7 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
   if (threadIdx.x == 0) {
     t.ctr->claim_attempts += s_cl[0];
     t.ctr->claim_failures += s_cl[1];
+    if (L.N > 0) t.ctr->lookup_pairs += (unsigned long long)L.bbase[L.nbk];
     const long long R = (long long)(all >> 32);
     const long long Fr = t.ctr->free_top > 0 ? t.ctr->free_top : 0;
     const long long take = R < Fr ? R : Fr;
@@ -1298,35 +1373,108 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
   if (threadIdx.x == 0 && s_err) atomicOr(&t.ctr->error, s_err);
 }
 
-// Each occurrence's inverse index and forward reference, in occurrence
-// order: one gather from the partition array through the position the
-// scatter noted, then contiguous stores.  Written in bucket order by the
-// bucket kernels instead, the 4- and 8-byte stores would land one per cache
-// line.  Blocks of one XCD take consecutive occurrences, as the partition
-// blocks did, so the lines they gather from are shared within its L2.
-constexpr int kOutPer = 4;
-__global__ __launch_bounds__(kThreads) void k_occ_out(LookupLaunch L) {
-  const int vb = xcd_block((int)blockIdx.x, (int)gridDim.x);
-  const long long j0 = (long long)vb * (kThreads * kOutPer) + threadIdx.x;
-  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
+// Each occurrence's outputs, one tile per block.  The tile's resolved pairs
+// (read through the positions the scatter noted, bucket order) go to LDS;
+// then every occurrence takes its pair's distinct-key index and forward
+// reference (stored contiguously, in occurrence order) and the next place in
+// its pair's span of the key's group, where its grouped entry goes: its bag
+// (f * B + i, found by a binary search over the tile's window of merged bag
+// offsets, kept in LDS when it fits), or the occurrence itself when grouping
+// by occurrence.
+constexpr int kOccThreads = 1024;
+constexpr int kOccPer = kTileOcc / kOccThreads;
+__global__ __launch_bounds__(kOccThreads) void k_occ_tile(LookupLaunch L) {
+  __shared__ long long s_ref[kTileOcc];
+  __shared__ int s_u[kTileOcc];
+  __shared__ int s_g[kTileOcc];
+  __shared__ int s_off[kBagWin];
+  const int tid = threadIdx.x;
+  const long long tile = blockIdx.x;
+  const long long j0 = tile * kTileOcc;
+  const long long j1 = j0 + kTileOcc < L.N ? j0 + kTileOcc : L.N;
+  const int nd = L.tile_n[tile];
   const PartOut* po = reinterpret_cast<const PartOut*>(L.part);
-  int p[kOutPer];
+  const bool by_occ = (L.flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
+  const int* off = L.res.bag_offsets;  // merged, F * B + 1 entries
+  const int nbags = L.F * L.B;
+  {
+    int p[kOccPer];
 #pragma unroll
-  for (int k = 0; k < kOutPer; ++k) {
-    const long long j = j0 + k * kThreads;
-    p[k] = j < L.N ? L.posmap[j] : 0;
-  }
-  PartOut o[kOutPer];
-#pragma unroll
-  for (int k = 0; k < kOutPer; ++k)
-    if (j0 + k * kThreads < L.N) o[k] = po[p[k]];
-#pragma unroll
-  for (int k = 0; k < kOutPer; ++k) {
-    const long long j = j0 + k * kThreads;
-    if (j < L.N) {
-      L.res.inverse[j] = o[k].u;
-      occref[j] = o[k].ref;
+    for (int k = 0; k < kOccPer; ++k) {
+      const int l = tid + k * kOccThreads;
+      p[k] = l < nd ? L.posmap[j0 + l] : 0;
     }
+#pragma unroll
+    for (int k = 0; k < kOccPer; ++k) {
+      const int l = tid + k * kOccThreads;
+      if (l < nd) {
+        const PartOut o = po[p[k]];
+        s_ref[l] = o.ref;
+        s_u[l] = o.u;
+        s_g[l] = o.gpos;
+      }
+    }
+  }
+  // the bags of the tile's occurrences: from the bag of its first occurrence
+  // to that of the next tile's first (k_prep's table), their offsets to LDS
+  // when they fit (a tile spans few bags unless most of them are empty).
+  // Invalid offsets (reported by k_prep) may leave entries of an earlier
+  // call: clamped, they keep every access in bounds.
+  int blo = 0, wn = 0;
+  if (!by_occ) {
+    int b0 = L.tile_bag[tile];
+    int b1 = tile + 1 < L.ntiles ? L.tile_bag[tile + 1] : nbags - 1;
+    b0 = b0 < 0 ? 0 : (b0 > nbags - 1 ? nbags - 1 : b0);
+    b1 = b1 < b0 ? b0 : (b1 > nbags - 1 ? nbags - 1 : b1);
+    blo = b0;
+    wn = b1 - b0 + 2;
+  }
+  const bool win = wn > 0 && wn <= kBagWin;
+  if (win)
+    for (int i = tid; i < wn; i += kOccThreads) s_off[i] = off[blo + i];
+  __syncthreads();
+  long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
+  int loc[kOccPer];
+#pragma unroll
+  for (int k = 0; k < kOccPer; ++k) {
+    const long long j = j0 + tid + k * kOccThreads;
+    loc[k] = j < j1 ? (int)L.occ_local[j] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kOccPer; ++k) {
+    const long long j = j0 + tid + k * kOccThreads;
+    if (j >= j1) continue;
+    int g;
+    if (by_occ) {
+      g = (int)j;
+    } else {
+      int lo, hi;
+      if (win) {
+        lo = 0;
+        hi = wn - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((long long)s_off[mid] <= j) lo = mid + 1;
+          else hi = mid;
+        }
+        lo += blo;
+      } else {
+        lo = 0;
+        hi = nbags;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((long long)off[mid] <= j) lo = mid + 1;
+          else hi = mid;
+        }
+      }
+      g = lo - 1;
+      g = g < 0 ? 0 : (g > nbags - 1 ? nbags - 1 : g);
+    }
+    const int l = loc[k];
+    const int pos = atomicAdd(&s_g[l], 1);
+    L.res.grouped[pos] = g;
+    L.res.inverse[j] = s_u[l];
+    occref[j] = s_ref[l];
   }
 }
 
@@ -1369,10 +1517,11 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
                      L, t);
   if (L.N > 0) {
     const unsigned G = (unsigned)L.part_blocks;
-    RECIS_LAUNCH("k_part_hist", k_part_hist, dim3(G), dim3(kPartThreads), s, L, t);
+    RECIS_LAUNCH("k_tile", k_tile, dim3(G), dim3(kPartThreads), s, L, t);
     RECIS_LAUNCH("k_part_colscan", k_part_colscan, dim3((unsigned)((L.nbk + 63) / 64)), dim3(kPartThreads), s, L);
-    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.bbase, L.nbk, (long long*)nullptr);
-    RECIS_LAUNCH("k_part_scatter", k_part_scatter, dim3(G), dim3(kPartThreads), s, L);
+    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.bbase, (int*)nullptr, L.nbk,
+                 (long long*)nullptr);
+    RECIS_LAUNCH("k_pair_scatter", k_pair_scatter, dim3(G), dim3(kPartThreads), s, L);
     // heavy slices: at most kHeavyBlocks blocks, each taking every kHeavyBlocks-th slice
     const long long hb = L.hmax < kHeavyBlocks ? L.hmax : kHeavyBlocks;
     const dim3 nb_grid((unsigned)L.nbk), count_grid((unsigned)(L.nbk + hb));
@@ -1380,20 +1529,19 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
       RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), count_grid, dim3(kThreads), s, L, t);
     else
       RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), count_grid, dim3(kThreads), s, L, t);
-    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.ubase, L.nbk,
+    RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.ubase, L.obase, L.nbk,
                  reinterpret_cast<long long*>(L.res.num_unique));
     if (L.big_tab)
       RECIS_LAUNCH("k_bucket_emit", (k_bucket<2048, true>), nb_grid, dim3(kThreads), s, L, t);
     else
       RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true>), nb_grid, dim3(kThreads), s, L, t);
   }
-  // block 0 scans; the others (N > 0 only) write the heavy buckets' occurrences
+  // block 0 scans; the others (N > 0 only) resolve the heavy buckets' pairs
   const long long kb = L.N > 0 ? 1 + (L.hmax < kHeavyBlocks / 4 ? L.hmax : kHeavyBlocks / 4) : 1;
   RECIS_LAUNCH("k_key_scan", k_key_scan, dim3((unsigned)kb), dim3(kScanThreads), s, L, t);
   if (L.N > 0) {
     RECIS_LAUNCH("k_key_finalize", k_key_finalize, dim3((unsigned)L.nbk), dim3(kThreads), s, L, t);
-    const long long ob = (L.N + kThreads * kOutPer - 1) / (kThreads * kOutPer);
-    RECIS_LAUNCH("k_occ_out", k_occ_out, dim3((unsigned)ob), dim3(kThreads), s, L);
+    RECIS_LAUNCH("k_occ_tile", k_occ_tile, dim3((unsigned)L.ntiles), dim3(kOccThreads), s, L);
   }
 }
 

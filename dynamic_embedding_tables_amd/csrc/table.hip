@@ -240,11 +240,12 @@ int region_bits_for(long long slot_cap) {
 }
 
 // Hash-partition geometry of a call with n occurrences: buckets of about
-// kBucketOcc occurrences (a power of two, at most kMaxBuckets), partition
-// blocks of about kPartOcc occurrences (at most kMaxPartBlocks).
+// kBucketOcc occurrences (a power of two, at most kMaxBuckets), tiles of
+// kTileOcc occurrences, partition blocks of whole tiles (at most
+// kMaxPartBlocks of them).
 struct PartGeom {
   int nbits, nbk, blocks, big;
-  long long range;
+  long long ntiles, tiles_per_block;
 };
 // Buckets never outnumber the IDMap's regions (max_bits), so that each
 // bucket's block owns whole regions.
@@ -253,25 +254,33 @@ PartGeom part_geom(long long n, int max_bits = kMaxBucketBits) {
   const long long want = std::max<long long>(1, (n + kBucketOcc - 1) / kBucketOcc);
   g.nbk = (int)std::min<long long>(next_pow2(want), 1ll << max_bits);
   g.nbits = log2_exact(g.nbk);
-  g.blocks = (int)std::min<long long>(std::max<long long>(1, (n + kPartOcc - 1) / kPartOcc), kMaxPartBlocks);
-  g.range = std::max<long long>(1, (n + g.blocks - 1) / g.blocks);
+  g.ntiles = std::max<long long>(1, (n + kTileOcc - 1) / kTileOcc);
+  g.tiles_per_block = (g.ntiles + kMaxPartBlocks - 1) / kMaxPartBlocks;
+  g.blocks = (int)((g.ntiles + g.tiles_per_block - 1) / g.tiles_per_block);
   g.big = n > (long long)g.nbk * kBucketOcc ? 1 : 0;
   return g;
 }
 
 // Bytes of each per-step scratch array for cap occurrences.
 struct ScratchSizes {
-  size_t dd, part, hist, bbase, uslot, posmap, blk, wb, partials;
+  size_t dd, part, hist, bbase, uslot, posmap, blk, wb, partials, tkey, tcnt, tile_n, occ_local;
 };
 ScratchSizes scratch_sizes(long long cap, int dim) {
   ScratchSizes z;
   const PartGeom g = part_geom(cap);
   z.dd = (size_t)(2 * cap) * sizeof(DedupSlot);
   z.part = (size_t)cap * sizeof(PartEntry);
-  z.hist = (size_t)g.blocks * (size_t)g.nbk * 4;
-  z.bbase = (size_t)(kMaxBuckets + 1) * 4 * 2;  // bbase, then ubase
+  // a call of n <= cap occurrences has at most min(kMaxPartBlocks, its tiles)
+  // partition blocks and at most cap's buckets
+  z.hist = (size_t)std::min<long long>(kMaxPartBlocks, g.ntiles) * (size_t)g.nbk * 4;
+  z.bbase = (size_t)(kMaxBuckets + 1) * 4 * 3;  // bbase, ubase, obase
   z.uslot = (size_t)cap * 4;
-  z.posmap = (size_t)cap * 4;
+  const size_t tiled = (size_t)g.ntiles * kTileOcc;  // pair slots, whole tiles
+  z.posmap = tiled * 4;
+  z.tkey = tiled * 8;
+  z.tcnt = tiled * 4;
+  z.tile_n = (size_t)(g.ntiles + 1) * 4 * 2;  // tile_n, then tile_bag
+  z.occ_local = (size_t)cap * 2;
   z.blk = (size_t)(kMaxBuckets + 2) * 8 * 3;  // per-bucket sums: blk_sums, blk_long, blk_claim
   z.wb = (size_t)cap * 8;
   z.partials = (size_t)plan_layout(cap).max_chunks * (size_t)dim * 8;
@@ -290,6 +299,13 @@ void free_scratch(recis_table* t, hipStream_t s) {
   tab_free(t, t->blk_sums, z.blk, s);
   tab_free(t, t->wb_keys, z.wb, s);
   tab_free(t, t->partials, z.partials, s);
+  tab_free(t, t->tkey, z.tkey, s);
+  tab_free(t, t->tcnt, z.tcnt, s);
+  tab_free(t, t->tile_n, z.tile_n, s);
+  tab_free(t, t->occ_local, z.occ_local, s);
+  t->tkey = nullptr;
+  t->tcnt = t->tile_n = nullptr;
+  t->occ_local = nullptr;
   t->dd = nullptr;
   t->part = nullptr;
   t->hist = t->bbase = t->ubase = t->uslot = t->posmap = nullptr;
@@ -319,8 +335,12 @@ recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
   t->blk_sums = static_cast<unsigned long long*>(tab_alloc(t, z.blk, s));
   t->wb_keys = static_cast<long long*>(tab_alloc(t, z.wb, s));
   t->partials = static_cast<double*>(tab_alloc(t, z.partials, s));
+  t->tkey = static_cast<long long*>(tab_alloc(t, z.tkey, s));
+  t->tcnt = static_cast<int*>(tab_alloc(t, z.tcnt, s));
+  t->tile_n = static_cast<int*>(tab_alloc(t, z.tile_n, s));
+  t->occ_local = static_cast<unsigned short*>(tab_alloc(t, z.occ_local, s));
   if (!t->dd || !t->part || !t->hist || !t->bbase || !t->uslot || !t->posmap || !t->blk_sums || !t->wb_keys ||
-      !t->partials) {
+      !t->partials || !t->tkey || !t->tcnt || !t->tile_n || !t->occ_local) {
     free_scratch(t, s);
     return RECIS_ERR_OUT_OF_MEMORY;
   }
@@ -588,7 +608,14 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.nbits = g.nbits;
   L.nbk = g.nbk;
   L.part_blocks = g.blocks;
-  L.part_range = g.range;
+  L.tiles_per_block = g.tiles_per_block;
+  L.ntiles = g.ntiles;
+  L.tkey = t->tkey;
+  L.tcnt = t->tcnt;
+  L.tile_n = t->tile_n;
+  L.tile_bag = t->tile_n + (g.ntiles + 1);
+  L.occ_local = t->occ_local;
+  L.obase = t->bbase + 2 * (kMaxBuckets + 1);
   L.big_tab = g.big;
   L.hist = t->hist;
   L.bbase = t->bbase;
@@ -881,6 +908,7 @@ recis_status recis_idmap_stats(recis_table* t, recis_table_stats* out, hipStream
   out->hbm_rows = hbm_rows(t);
   out->claim_attempts = (int64_t)c.claim_attempts;
   out->claim_failures = (int64_t)c.claim_failures;
+  out->lookup_pairs = (int64_t)c.lookup_pairs;
   return RECIS_OK;
 }
 

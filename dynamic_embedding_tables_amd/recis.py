@@ -93,7 +93,8 @@ class recis_table_stats(C.Structure):
     _fields_ = [("keys", C.c_int64), ("rows_in_use", C.c_int64), ("rows_allocated", C.c_int64),
                 ("blocks", C.c_int64), ("slot_capacity", C.c_int64), ("adam_step", C.c_int64),
                 ("bytes", C.c_int64), ("probationary_keys", C.c_int64), ("claim_attempts", C.c_int64),
-                ("claim_failures", C.c_int64), ("hbm_rows", C.c_int64)]
+                ("claim_failures", C.c_int64), ("hbm_rows", C.c_int64),
+                ("lookup_pairs", C.c_int64)]
 
 
 class RecisError(RuntimeError):

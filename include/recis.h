@@ -232,6 +232,12 @@ typedef struct {
                              another key of the same call (the probe then moves on) */
   int64_t hbm_rows;       /* rows whose EmbeddingBlocks are in HBM: all of them for
                              RECIS_MEM_DEVICE, the hot tier for RECIS_MEM_HOST */
+  int64_t lookup_pairs;   /* insert_find deduplicates each tile of 4096 consecutive
+                             occurrences (merged order: feature-major, then bag) on
+                             its own first: the distinct keys of each tile, summed
+                             over the tiles of every call since creation.  The
+                             later passes move one record per such pair, not one
+                             per occurrence */
 } recis_table_stats;
 
 /* Creates a table.  Allocates the IDMap and `reserve_rows` worth of blocks
