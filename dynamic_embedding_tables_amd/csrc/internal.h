@@ -442,7 +442,6 @@ constexpr int kMaxPartBlocks = 1024;
 constexpr int kBucketOcc = 384;      // target occurrences per bucket
 constexpr int kMaxBucketBits = 13;
 constexpr int kMaxBuckets = 1 << kMaxBucketBits;
-constexpr int kBagWin = 4096;        // merged bag offsets a partition block keeps in LDS
 constexpr int kBucketPer = 4;        // occurrences per thread per pass of k_bucket
 // A bucket of more than kHeavyOcc occurrences (a hot key's bucket) is cut into
 // slices of kSliceOcc (at most 3/4 of the smaller LDS table, so a slice never

@@ -52,10 +52,11 @@ __device__ __forceinline__ long long shfl64(long long v, int src) {
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-// Block-wide exclusive scan of one uint64 per thread; returns the prefix and
-// writes the block total to *total.  kThreads = 256 = 4 waves.
+// Block-wide exclusive scan of one uint64 per thread of an NT-thread block;
+// returns the prefix and writes the block total to *total.
+template <int NT = kThreads>
 __device__ unsigned long long block_exclusive_scan(unsigned long long v, unsigned long long* total) {
-  __shared__ unsigned long long s_w[kThreads / 64];
+  __shared__ unsigned long long s_w[NT / 64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   unsigned long long x = v;
 #pragma unroll
@@ -67,7 +68,7 @@ __device__ unsigned long long block_exclusive_scan(unsigned long long v, unsigne
   __syncthreads();
   unsigned long long before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     if (w < wid) before += s_w[w];
     all += s_w[w];
   }
@@ -646,7 +647,7 @@ __device__ __forceinline__ void put_out(const LookupLaunch& L, long long p, long
   reinterpret_cast<PartOut*>(L.part)[p] = o;
 }
 
-template <bool EMIT>
+template <bool EMIT, int NT>
 __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, int& s_nd, int& s_cursor,
                               unsigned long long& s_sum, unsigned long long& s_sum_long,
                               unsigned long long& s_claims) {
@@ -665,7 +666,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
   __syncthreads();
   if (!EMIT) {
     int wsum = 0;  // the bucket's occurrences
-    for (int i = tid; i < m; i += kThreads) {
+    for (int i = tid; i < m; i += NT) {
       const PartEntry e = L.part[s + i];
       const long long key = e.key;
       wsum += e.w;
@@ -684,7 +685,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     }
     atomicAdd(&s_cursor, wsum);
     __syncthreads();
-    for (unsigned long long h = tid; h < cap; h += kThreads) {
+    for (unsigned long long h = tid; h < cap; h += NT) {
       const long long key = ld_key(&R[h]);
       if (key == kEmptyKey) continue;
       atomicAdd(&s_nd, 1);
@@ -702,7 +703,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
   unsigned long long sum = 0, sum_long = 0, claims = 0;
   unsigned err = 0;
-  for (unsigned long long h = tid; h < cap; h += kThreads) {
+  for (unsigned long long h = tid; h < cap; h += NT) {
     const long long key = ld_key(&R[h]);
     if (key == kEmptyKey) continue;
     const long long u = ub + atomicAdd(&s_nd, 1);
@@ -733,7 +734,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     L.blk_long[b] = s_sum_long;
     L.blk_claim[b] = s_claims;
   }
-  for (int i = tid; i < m; i += kThreads) {
+  for (int i = tid; i < m; i += NT) {
     const PartEntry e = L.part[s + i];
     unsigned long long h = (fib_mix(e.key) >> 20) % cap;
     while (ld_key(&R[h]) != e.key) h = h + 1 == cap ? 0 : h + 1;
@@ -744,7 +745,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     put_out(L, s + i, ref_of_row(t, v, e.key), u, ld_int(&L.res.unique_offsets[u]) + pos);
   }
   __syncthreads();
-  for (unsigned long long h = tid; h < cap; h += kThreads) {
+  for (unsigned long long h = tid; h < cap; h += NT) {
     R[h].key = kEmptyKey;
     R[h].count = 0;
   }
@@ -810,6 +811,13 @@ __device__ __forceinline__ void slice_dedup(const LookupLaunch& L, int s0, int s
   }
 }
 
+// Block size of the bucket kernels when the buckets are fuller than the
+// target (the call's occurrences outnumber kMaxBuckets * kBucketOcc: the
+// 2048-entry table).  More threads put more of a bucket's IDMap probes in
+// flight at once; 512 measured faster than 256 and 1024 on the capacity
+// workload (1024: registers allow one block per CU).
+constexpr int kBigBucketThreads = 512;
+
 // One bucket per block, in two launches around a scan of the per-bucket
 // distinct counts (so the distinct keys get dense indices without a global
 // counter, which thousands of blocks would serialise on).  Both launches
@@ -825,8 +833,8 @@ __device__ __forceinline__ void slice_dedup(const LookupLaunch& L, int s0, int s
 // reference in place of its partition record.
 // COUNT's grid has the heavy slices after the buckets; a heavy bucket's own
 // block skips COUNT and does EMIT's key pass (see above).
-template <int TAB, bool EMIT>
-__global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t) {
+template <int TAB, bool EMIT, int NT>
+__global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
   constexpr int kMaxDistinct = TAB / 4 * 3;
   constexpr int kTabBits = TAB == 1024 ? 10 : (TAB == 2048 ? 11 : 0);
   static_assert(kTabBits > 0, "TAB is 1024 or 2048");
@@ -849,18 +857,18 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     const int b = L.hslice[1 + 2 * e], k = L.hslice[2 + 2 * e];
     const int s = L.bbase[b], m = L.bbase[b + 1] - s;
     const int s0 = s + k * kSliceOcc, s1 = s0 + kSliceOcc < s + m ? s0 + kSliceOcc : s + m;
-    for (int i = tid; i < TAB; i += kThreads) {
+    for (int i = tid; i < TAB; i += NT) {
       s_key[i] = kEmptyKey;
       s_cnt[i] = 0;
     }
     if (tid == 0) s_nd = 0;
     __syncthreads();
-    slice_dedup<TAB, kThreads>(L, s0, s1, hs, s_key, s_cnt, s_list, s_nd);
+    slice_dedup<TAB, NT>(L, s0, s1, hs, s_key, s_cnt, s_list, s_nd);
     if (tid == 0) s_cursor = 0;
     __syncthreads();
     DedupSlot* R = L.dd + 2ll * s;
     const unsigned long long cap = 2ull * (unsigned long long)m;
-    for (int idx = tid; idx < s_nd; idx += kThreads) {
+    for (int idx = tid; idx < s_nd; idx += NT) {
       const int hl = s_list[idx];
       const long long key = s_key[hl];
       atomicAdd(&s_cursor, s_cnt[hl]);  // the slice's occurrences
@@ -914,7 +922,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
       s_err = 0;
     }
     __syncthreads();
-    for (long long c0 = 0; c0 < nd; c0 += kThreads) {
+    for (long long c0 = 0; c0 < nd; c0 += NT) {
       const long long idx = c0 + tid;
       const bool valid = idx < nd;
       long long key = 0;
@@ -925,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
         c = R[h].count;
       }
       unsigned long long tot;
-      const long long o = (long long)(block_exclusive_scan((unsigned long long)c, &tot) + run);
+      const long long o = (long long)(block_exclusive_scan<NT>((unsigned long long)c, &tot) + run);
       run += tot;
       if (!valid) continue;
       const long long u = ub + idx;
@@ -956,7 +964,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     }
     return;
   }
-  for (int i = tid; i < TAB; i += kThreads) {
+  for (int i = tid; i < TAB; i += NT) {
     s_key[i] = kEmptyKey;
     s_cnt[i] = 0;
     if (EMIT) s_claim[i] = ~0u;
@@ -971,12 +979,12 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     s_err = 0;
   }
   __syncthreads();
-  for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
+  for (int i0 = 0; i0 < m; i0 += NT * kBucketPer) {
     long long key[kBucketPer];
     int w[kBucketPer];
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
-      const int i = i0 + tid + k * kThreads;
+      const int i = i0 + tid + k * NT;
       PartEntry e;
       e.key = 0;
       e.w = 0;
@@ -986,7 +994,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     }
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
-      const bool act = i0 + tid + k * kThreads < m;
+      const bool act = i0 + tid + k * NT < m;
       unsigned h = 0;
       bool counted = false;
       if (act) {
@@ -1015,11 +1023,11 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   }
   __syncthreads();
   if (s_over) {  // rare: colliding inputs only
-    bucket_global<EMIT>(L, t, b, s_nd, s_cursor, s_sum, s_sum_long, s_claims);
+    bucket_global<EMIT, NT>(L, t, b, s_nd, s_cursor, s_sum, s_sum_long, s_claims);
     return;
   }
   if (!EMIT) {
-    for (int idx = tid; idx < s_nd; idx += kThreads) {
+    for (int idx = tid; idx < s_nd; idx += NT) {
       const int c = s_cnt[s_list[idx]];
       atomicAdd(&s_cursor, c);  // the bucket's occurrences
       if (L.sketching) sketch_count(t, s_key[s_list[idx]], c);
@@ -1057,7 +1065,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
   };
   unsigned long long sum = 0, sum_long = 0;
   unsigned err = 0;
-  for (int idx = tid; idx < nd; idx += kThreads) {
+  for (int idx = tid; idx < nd; idx += NT) {
     const int h = s_list[idx];
     const long long u = ub + idx;
     const long long key = s_key[h];
@@ -1084,23 +1092,23 @@ __global__ __launch_bounds__(kThreads) void k_bucket(LookupLaunch L, TableDev t)
     L.blk_claim[b] = s_claims;
     if (s_err) atomicOr(&t.ctr->error, s_err);
   }
-  for (int i0 = 0; i0 < m; i0 += kThreads * kBucketPer) {
+  for (int i0 = 0; i0 < m; i0 += NT * kBucketPer) {
     PartEntry e[kBucketPer];
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
-      const int i = i0 + tid + k * kThreads;
+      const int i = i0 + tid + k * NT;
       if (i < m) e[k] = L.part[s + i];
     }
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
-      const bool act = i0 + tid + k * kThreads < m;
+      const bool act = i0 + tid + k * NT < m;
       unsigned h = 0;
       if (act) {
         h = (unsigned)(fib_mix(e[k].key) >> hs) & (TAB - 1);
         while (s_key[h] != e[k].key) h = (h + 1) & (TAB - 1);
       }
       const int pos = act ? atomicAdd(&s_cnt[h], e[k].w) : 0;
-      if (act) put_out(L, s + i0 + tid + k * kThreads, s_ref[h], s_u[h], ob + pos);
+      if (act) put_out(L, s + i0 + tid + k * NT, s_ref[h], s_u[h], ob + pos);
     }
   }
 }
@@ -1383,38 +1391,62 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
 // by occurrence.
 constexpr int kOccThreads = 1024;
 constexpr int kOccPer = kTileOcc / kOccThreads;
+constexpr int kOccBagWin = 3072;  // offsets kept in LDS: two blocks per CU fit
+// The tile's resolved pairs to LDS, K per thread: the record positions, then
+// the records, each batch of loads in flight together.
+template <int K>
+__device__ __forceinline__ void occ_pairs(const LookupLaunch& L, long long j0, int nd, long long* s_ref, int* s_u,
+                                          int* s_g) {
+  const int tid = threadIdx.x;
+  const int lastl = nd > 0 ? nd - 1 : 0;
+  const PartOut* po = reinterpret_cast<const PartOut*>(L.part);
+  int p[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int l = tid + k * kOccThreads;
+    p[k] = L.posmap[j0 + (l < nd ? l : lastl)];
+  }
+  PartOut o[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) o[k] = po[p[k]];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int l = tid + k * kOccThreads;
+    if (l < nd) {
+      s_ref[l] = o[k].ref;
+      s_u[l] = o[k].u;
+      s_g[l] = o[k].gpos;
+    }
+  }
+}
 __global__ __launch_bounds__(kOccThreads) void k_occ_tile(LookupLaunch L) {
   __shared__ long long s_ref[kTileOcc];
   __shared__ int s_u[kTileOcc];
   __shared__ int s_g[kTileOcc];
-  __shared__ int s_off[kBagWin];
+  __shared__ int s_off[kOccBagWin];
   const int tid = threadIdx.x;
   const long long tile = blockIdx.x;
   const long long j0 = tile * kTileOcc;
   const long long j1 = j0 + kTileOcc < L.N ? j0 + kTileOcc : L.N;
   const int nd = L.tile_n[tile];
-  const PartOut* po = reinterpret_cast<const PartOut*>(L.part);
   const bool by_occ = (L.flags & RECIS_GROUP_BY_OCCURRENCE) != 0;
   const int* off = L.res.bag_offsets;  // merged, F * B + 1 entries
   const int nbags = L.F * L.B;
-  {
-    int p[kOccPer];
+  // Loads in as few round trips as their dependences allow, each from an
+  // index clamped into the tile (a tile has at least one pair and one
+  // occurrence) so that none sits in a branch of its own, where the copy
+  // out of it would wait for it at once.  The pairs take only as many
+  // passes of the block as the tile has pairs for (a uniform choice).
+  int loc[kOccPer];
 #pragma unroll
-    for (int k = 0; k < kOccPer; ++k) {
-      const int l = tid + k * kOccThreads;
-      p[k] = l < nd ? L.posmap[j0 + l] : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < kOccPer; ++k) {
-      const int l = tid + k * kOccThreads;
-      if (l < nd) {
-        const PartOut o = po[p[k]];
-        s_ref[l] = o.ref;
-        s_u[l] = o.u;
-        s_g[l] = o.gpos;
-      }
-    }
+  for (int k = 0; k < kOccPer; ++k) {
+    const long long j = j0 + tid + k * kOccThreads;
+    loc[k] = (int)L.occ_local[j < j1 ? j : j1 - 1];
   }
+  const int passes = (nd + kOccThreads - 1) / kOccThreads;
+  if (passes <= 1) occ_pairs<1>(L, j0, nd, s_ref, s_u, s_g);
+  else if (passes == 2) occ_pairs<2>(L, j0, nd, s_ref, s_u, s_g);
+  else occ_pairs<kOccPer>(L, j0, nd, s_ref, s_u, s_g);
   // the bags of the tile's occurrences: from the bag of its first occurrence
   // to that of the next tile's first (k_prep's table), their offsets to LDS
   // when they fit (a tile spans few bags unless most of them are empty).
@@ -1429,17 +1461,11 @@ __global__ __launch_bounds__(kOccThreads) void k_occ_tile(LookupLaunch L) {
     blo = b0;
     wn = b1 - b0 + 2;
   }
-  const bool win = wn > 0 && wn <= kBagWin;
+  const bool win = wn > 0 && wn <= kOccBagWin;
   if (win)
     for (int i = tid; i < wn; i += kOccThreads) s_off[i] = off[blo + i];
   __syncthreads();
   long long* occref = reinterpret_cast<long long*>(L.res.plan + plan_layout(L.res.capacity).o_occref);
-  int loc[kOccPer];
-#pragma unroll
-  for (int k = 0; k < kOccPer; ++k) {
-    const long long j = j0 + tid + k * kOccThreads;
-    loc[k] = j < j1 ? (int)L.occ_local[j] : 0;
-  }
 #pragma unroll
   for (int k = 0; k < kOccPer; ++k) {
     const long long j = j0 + tid + k * kOccThreads;
@@ -1526,15 +1552,17 @@ void launch_lookup(const LookupLaunch& L, const TableDev& t, hipStream_t s) {
     const long long hb = L.hmax < kHeavyBlocks ? L.hmax : kHeavyBlocks;
     const dim3 nb_grid((unsigned)L.nbk), count_grid((unsigned)(L.nbk + hb));
     if (L.big_tab)
-      RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false>), count_grid, dim3(kThreads), s, L, t);
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<2048, false, kBigBucketThreads>), count_grid,
+                   dim3(kBigBucketThreads), s, L, t);
     else
-      RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false>), count_grid, dim3(kThreads), s, L, t);
+      RECIS_LAUNCH("k_bucket_count", (k_bucket<1024, false, kThreads>), count_grid, dim3(kThreads), s, L, t);
     RECIS_LAUNCH("k_scan_small", k_scan_small, dim3(1), dim3(kPartThreads), s, L.ubase, L.obase, L.nbk,
                  reinterpret_cast<long long*>(L.res.num_unique));
     if (L.big_tab)
-      RECIS_LAUNCH("k_bucket_emit", (k_bucket<2048, true>), nb_grid, dim3(kThreads), s, L, t);
+      RECIS_LAUNCH("k_bucket_emit", (k_bucket<2048, true, kBigBucketThreads>), nb_grid,
+                   dim3(kBigBucketThreads), s, L, t);
     else
-      RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true>), nb_grid, dim3(kThreads), s, L, t);
+      RECIS_LAUNCH("k_bucket_emit", (k_bucket<1024, true, kThreads>), nb_grid, dim3(kThreads), s, L, t);
   }
   // block 0 scans; the others (N > 0 only) resolve the heavy buckets' pairs
   const long long kb = L.N > 0 ? 1 + (L.hmax < kHeavyBlocks / 4 ? L.hmax : kHeavyBlocks / 4) : 1;
