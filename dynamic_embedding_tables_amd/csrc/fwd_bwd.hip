@@ -30,6 +30,7 @@
 // consecutive keys in LDS, then each group of KL lanes reduces and updates
 // one key at a time with all of the key's loads in flight together.
 #include <mutex>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -451,6 +452,26 @@ struct BwdArgs {
   TableDev t;
   double* partials;
   int current;  // no update since the lookup: a fresh row is still pending
+  // the chunks of the long-key plan when it was rebuilt here (else plan[1])
+  const int* nchunks;
+  // hot keys (hot != 0): per bin the count-class histogram of the eligible
+  // long keys, the class threshold, hot-key count, first hot index and
+  // placement counter; per distinct key its index among its bin's hot keys
+  // (-1: none); per occurrence the same (-1: none); the hot keys' partials,
+  // hot index * hot_nc + bag block, D doubles each
+  int hot, hot_nc, hot_min;
+  unsigned* hot_cls;
+  int* hot_thr;
+  int* hot_n;
+  int* hot_base;
+  int* hot_cnt;
+  unsigned char* hot_of;  // kHotNone: no hot index
+  unsigned* hot_ent;  // per (feature, stage): its hot occurrences sorted by key, (key << 16 | bag),
+                      // from the stage's first occurrence slot on
+  int* hot_scnt;      // per (feature, stage): that entry count
+  int hot_spf;        // stages per feature
+  long long n_occ;    // occurrences of the lookup
+  double* hot_partials;
 };
 
 constexpr int kBwdKeys = kThreads;  // distinct keys per block tile (short path)
@@ -614,7 +635,7 @@ __global__ __launch_bounds__(256) void k_bwd_long_partial(BwdArgs a) {
   constexpr int GF = PER < 8 ? PER : 8;  // gradient rows in flight per group
   const int wl = threadIdx.x & 63;
   const int lane = wl % C, g = wl / C;
-  const int nchunks = a.plan[1];
+  const int nchunks = a.nchunks ? *a.nchunks : a.plan[1];
   const long long nwaves = (long long)gridDim.x * 4;
   const int* long_u = a.long_u;
   const int* long_base = a.long_base;
@@ -678,18 +699,26 @@ __global__ __launch_bounds__(256) void k_bwd_long_partial(BwdArgs a) {
 // one round (a hot key has up to kMaxKeyChunks) are summed one after another
 // by all four waves, whose sums meet in LDS; then each wave sums its own key
 // if it has fewer.  With few long keys a block takes one or two at a time.
+// A key's first partial: cb >= 0 a chunk of the chunked plan, cb < 0 the
+// row -1 - cb of the hot keys' partials.
+template <int D>
+__device__ __forceinline__ const double* partial_base(const BwdArgs& a, int cb) {
+  return cb >= 0 ? a.partials + (long long)cb * D : a.hot_partials + (long long)(-1 - cb) * D;
+}
+
 template <int D, typename TP, int G_STRIDE, int E>
 __device__ __forceinline__ void sum_partials(const BwdArgs& a, int cb, int nch, int grp, int lane,
                                              double (&G)[1][E]) {
   constexpr int kMergeBatch = 4;
 #pragma unroll
   for (int e = 0; e < E; ++e) G[0][e] = 0.0;
+  const double* base = partial_base<D>(a, cb);
   for (int p0 = 0; p0 < nch; p0 += G_STRIDE * kMergeBatch) {
     double part[kMergeBatch][E];
 #pragma unroll
     for (int m = 0; m < kMergeBatch; ++m) {
       const int p = p0 + m * G_STRIDE + grp;
-      const double* pp = a.partials + (long long)(cb + (p < nch ? p : 0)) * D + lane * E;
+      const double* pp = base + (long long)(p < nch ? p : 0) * D + lane * E;
 #pragma unroll
       for (int e = 0; e < E; ++e) part[m][e] = p < nch ? pp[e] : 0.0;
     }
@@ -1042,19 +1071,102 @@ void fwd_dispatch(const FwdArgs& a, int pool, hipStream_t s) {
 // together, and the waves in flight share that feature's rows of the
 // upstream gradient in the memory-side cache instead of each fetching its
 // own from HBM -- worth it when the gradient is larger than that cache.
-// Three launches over the long keys (bin = the key's slot, in kFeatBins
-// bins): k_long_hist counts keys and chunks per bin (block histograms in
-// LDS, one global add per bin and block); k_long_scan turns the bins into
-// bases (one block); k_long_place gives every key its place and first chunk
-// with one 64-bit add on its bin (place << 32 | chunks), so places and chunk
-// bases rise together, and writes its chunks' owner.
-constexpr int kFeatBins = 4096;
+// Three launches over the long keys (bin = the key's feature bin):
+// k_long_hist counts keys and chunks per bin (block histograms in LDS, one
+// global add per bin and block); k_long_scan turns the bins into bases (one
+// block); k_long_place gives every key its place and first chunk with one
+// 64-bit add on its bin (place << 32 | chunks), so places and chunk bases
+// rise together, and writes its chunks' owner.
+//
+// With hot keys (pooled gradients): before these, k_hot_hist counts the
+// eligible long keys of each bin by count class (floor(log2 count)) and
+// k_hot_plan picks, per bin, the classes from the top down while they hold
+// at most the pass's key limit: those keys are the bin's hot keys.  A hot
+// key gets no chunks; k_long_place gives it its index among its bin's hot
+// keys and its partial rows (one per block of kHotBags bags), which
+// k_bwd_hot writes and the final pass sums like chunk partials.
 __global__ void k_zero_u64(unsigned long long* p, long long n) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
 }
 __device__ __forceinline__ int feat_bin(const BwdArgs& a, int u) {
   return (int)(((unsigned long long)a.ukeys[u] >> 48) & (kFeatBins - 1));
+}
+__device__ __forceinline__ int count_class(int c) { return 31 - __clz(c); }
+// A long key is eligible when its count is at least hot_min and it is a
+// key (not the mark of failed transforms, whose bin is no feature's); it is
+// hot when its class reached its bin's threshold (kHotClasses: no hot keys
+// in the bin).
+__device__ __forceinline__ bool hot_eligible(const BwdArgs& a, int u, int c) {
+  return c >= a.hot_min && a.ukeys[u] >= 0;
+}
+__device__ __forceinline__ bool is_hot(const BwdArgs& a, int u, int bin) {
+  if (!a.hot) return false;
+  const int c = a.counts[u];
+  return hot_eligible(a, u, c) && count_class(c) >= a.hot_thr[bin];
+}
+
+__global__ __launch_bounds__(256) void k_hot_hist(BwdArgs a) {
+  const int nlong = a.plan[0];
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nlong || !a.plan[kPlanHotOk]) return;
+  const int u = a.plan[a.pl.o_long_u + idx];
+  const int c = a.counts[u];
+  if (hot_eligible(a, u, c)) atomicAdd(&a.hot_cls[feat_bin(a, u) * kHotClasses + count_class(c)], 1u);
+}
+
+// One block: per bin the threshold class and hot-key count, then the bins'
+// first hot indices (an exclusive scan).
+template <int KMAX>
+__global__ __launch_bounds__(1024) void k_hot_plan(BwdArgs a) {
+  constexpr int kPer = kFeatBins / 1024;
+  __shared__ int s_w[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool ok = a.plan[kPlanHotOk] != 0;
+  int n[kPer], run = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = tid * kPer + k;
+    unsigned x[kHotClasses];
+    const uint4* p = reinterpret_cast<const uint4*>(a.hot_cls + b * kHotClasses);
+#pragma unroll
+    for (int q = 0; q < kHotClasses / 4; ++q) {
+      const uint4 v = p[q];
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+    // the classes from the top down while they fit; the lowest one taken
+    // (with keys) is the threshold
+    int thr = kHotClasses, tot = 0;
+    bool open = ok;
+#pragma unroll
+    for (int c = kHotClasses - 1; c >= 0; --c) {
+      open = open && tot + (int)x[c] <= KMAX;
+      if (open) {
+        tot += (int)x[c];
+        if (x[c]) thr = c;
+      }
+    }
+    a.hot_thr[b] = tot ? thr : kHotClasses;
+    a.hot_n[b] = tot;
+    a.hot_cnt[b] = 0;
+    n[k] = tot;
+    run += tot;
+  }
+  int inc = run;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  int base = inc - run;
+  for (int x = 0; x < w; ++x) base += s_w[x];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    a.hot_base[tid * kPer + k] = base;
+    base += n[k];
+  }
 }
 
 __global__ __launch_bounds__(256) void k_long_hist(BwdArgs a, unsigned long long* bins) {
@@ -1066,15 +1178,17 @@ __global__ __launch_bounds__(256) void k_long_hist(BwdArgs a, unsigned long long
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx < nlong) {
     const int u = a.plan[a.pl.o_long_u + idx], nch = a.plan[a.pl.o_long_nch + idx];
-    atomicAdd(&s_b[feat_bin(a, u)], (1ull << 32) | (unsigned)nch);
+    const int bin = feat_bin(a, u);
+    atomicAdd(&s_b[bin], (1ull << 32) | (unsigned)(is_hot(a, u, bin) ? 0 : nch));
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kFeatBins; i += 256)
     if (s_b[i]) atomicAdd(&bins[i], s_b[i]);
 }
 
-// In place: bins[i] becomes the exclusive prefix of (keys << 32 | chunks).
-__global__ __launch_bounds__(1024) void k_long_scan(unsigned long long* bins) {
+// In place: bins[i] becomes the exclusive prefix of (keys << 32 | chunks);
+// the chunks in all to *nchunks.
+__global__ __launch_bounds__(1024) void k_long_scan(unsigned long long* bins, int* nchunks) {
   constexpr int kPer = kFeatBins / 1024;
   __shared__ unsigned long long s_w[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1099,6 +1213,7 @@ __global__ __launch_bounds__(1024) void k_long_scan(unsigned long long* bins) {
     bins[tid * kPer + k] = base;
     base += v[k];
   }
+  if (tid == 1023) *nchunks = (int)(base & 0xFFFFFFFFull);
 }
 
 __global__ __launch_bounds__(256) void k_long_place(BwdArgs a, unsigned long long* bins, int* out_u, int* out_base,
@@ -1107,12 +1222,317 @@ __global__ __launch_bounds__(256) void k_long_place(BwdArgs a, unsigned long lon
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= nlong) return;
   const int u = a.plan[a.pl.o_long_u + idx], nch = a.plan[a.pl.o_long_nch + idx];
-  const unsigned long long at = atomicAdd(&bins[feat_bin(a, u)], (1ull << 32) | (unsigned)nch);
+  const int bin = feat_bin(a, u);
+  const bool hot = is_hot(a, u, bin);
+  const unsigned long long at = atomicAdd(&bins[bin], (1ull << 32) | (unsigned)(hot ? 0 : nch));
   const int pos = (int)(at >> 32), cb = (int)(at & 0xFFFFFFFFull);
   out_u[pos] = u;
+  if (hot) {
+    const int h = atomicAdd(&a.hot_cnt[bin], 1);  // below hot_n[bin]: the same test counted it
+    a.hot_of[u] = (unsigned char)h;
+    out_nch[pos] = a.hot_nc;
+    out_base[pos] = -1 - (a.hot_base[bin] + h) * a.hot_nc;
+    return;
+  }
   out_nch[pos] = nch;
   out_base[pos] = cb;
   for (int k = 0; k < nch; ++k) out_owner[cb + k] = pos;
+}
+
+// Per distinct key: no hot index yet (a byte each, the hot indices being
+// below hot_kmax <= kHotNone).
+constexpr unsigned char kHotNone = 255;
+__global__ __launch_bounds__(256) void k_hot_fill(BwdArgs a) {
+  const long long U = *a.num_unique;
+  for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < U; u += (long long)gridDim.x * 256)
+    a.hot_of[u] = kHotNone;
+}
+
+// Hot keys, bag-major, in two launches.  A stage is STAGE consecutive bags
+// of one feature.
+//  - k_hot_sort, one block per stage: the stage's occurrences that belong to
+//    a hot key, sorted by hot index (a counting sort in LDS), written as
+//    (key << 16 | bag within the stage) from the stage's first occurrence
+//    slot on, and their count.  This launch does the per-occurrence lookups
+//    (occurrence -> distinct key -> hot index), with little LDS per block and
+//    so many blocks in flight to hide them.
+//  - k_bwd_hot, one block per (block of kHotBags bags, feature): the bags'
+//    gradient rows are read once and staged in LDS a stage at a time, with
+//    the stage's sorted entries; the waves split the entries evenly and sum
+//    each run of one key in double precision in registers, adding the run to
+//    the key's LDS sum at its end (an LDS double add; runs of one key meet
+//    only where a wave's share starts or ends).  The block writes one partial
+//    per hot key of its feature's bin, zero where the key does not occur.
+//    The next stage's rows and entries are loaded while one is summed.
+// A key's gradient sum is the same set of terms (row * scale, the scale 1 /
+// bag length for mean pooling) as in the chunked plan, in another order.
+constexpr int kHotThreads = 1024;
+constexpr int kHotUnroll = 8;
+constexpr int kHotEnt = 4096;  // sorted entries staged at a time (a stage has more only with long bags)
+template <int D>
+struct HotShape {
+  static constexpr int E = D / 64;        // gradient elements per lane (D = 64 or 128)
+  static constexpr int KMAX = 8192 / D;   // hot keys per bin: 64 KB of sums (hot_kmax)
+  static constexpr int STAGE = 16384 / D; // bags staged at a time: 64 KB of fp32 rows (hot_stage)
+  static constexpr int LOADS = STAGE * D / 4 / kHotThreads;  // 4-element loads per thread and stage
+  static constexpr int EPT = kHotEnt / kHotThreads;          // staged entries per thread
+};
+
+constexpr int kSortThreads = 256;
+constexpr int kSortPer = 4;
+template <int D>
+__global__ __launch_bounds__(kSortThreads) void k_hot_sort(BwdArgs a, const int* inverse) {
+  constexpr int STAGE = HotShape<D>::STAGE, KMAX = HotShape<D>::KMAX;
+  constexpr int BATCH = kSortThreads * kSortPer;
+  static_assert(STAGE <= 256, "a bag within the stage fits a byte");
+  static_assert(KMAX <= kHotNone, "a hot index fits a byte below kHotNone");
+  __shared__ int s_off[STAGE + 1];
+  __shared__ unsigned char s_obag[BATCH];
+  __shared__ int s_kc[KMAX];
+  __shared__ int s_ks[KMAX + 1];
+  if (!a.plan[kPlanHotOk]) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = blockIdx.x;
+  const int f = g / a.hot_spf, st = g - f * a.hot_spf;
+  const int nh = a.hot_n[a.plan[a.pl.o_fbin + f]];
+  if (nh == 0) return;  // the same for the whole block
+  const int i0 = st * STAGE;
+  const int sn = a.B - i0 < STAGE ? a.B - i0 : STAGE;
+  const long long fb = (long long)f * a.B + i0;
+  for (int i = tid; i <= sn; i += kSortThreads) s_off[i] = a.off[fb + i];
+  for (int i = tid; i < KMAX; i += kSortThreads) s_kc[i] = 0;
+  __syncthreads();
+  const int jlo = s_off[0], jhi = s_off[sn];
+  int count = 0;
+  for (int jb = jlo; jb < jhi; jb += BATCH) {
+    const int je = jhi - jb < BATCH ? jhi : jb + BATCH;
+    // each bag of the stage marks its occurrences in the batch
+    for (int t = tid; t < sn; t += kSortThreads) {
+      int j = s_off[t], j1 = s_off[t + 1];
+      j = j > jb ? j : jb;
+      j1 = j1 < je ? j1 : je;
+      for (; j < j1; ++j) s_obag[j - jb] = (unsigned char)t;
+    }
+    // hot indices, every load from an index inside the batch
+    int u[kSortPer], h[kSortPer], rk[kSortPer];
+#pragma unroll
+    for (int k = 0; k < kSortPer; ++k) {
+      const int j = jb + tid + k * kSortThreads;
+      u[k] = inverse[j < je ? j : je - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kSortPer; ++k) {
+      const int x = a.hot_of[u[k]];
+      h[k] = x == kHotNone ? -1 : x;
+    }
+#pragma unroll
+    for (int k = 0; k < kSortPer; ++k) {
+      if (jb + tid + k * kSortThreads >= je) h[k] = -1;
+      rk[k] = h[k] >= 0 ? atomicAdd(&s_kc[h[k]], 1) : 0;
+    }
+    __syncthreads();
+    if (w == 0) {  // exclusive scan of the per-key counts; the counts back to zero
+      constexpr int P = (KMAX + 63) / 64;
+      int v[P], sum = 0;
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int x = lane * P + q;
+        v[q] = x < nh ? s_kc[x] : 0;
+        if (x < KMAX) s_kc[x] = 0;
+        sum += v[q];
+      }
+      int inc = sum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(inc, d);
+        if (lane >= d) inc += y;
+      }
+      int run = inc - sum;
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int x = lane * P + q;
+        if (x < nh) s_ks[x] = run;
+        run += v[q];
+      }
+      if (lane == 63) s_ks[nh] = inc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSortPer; ++k)
+      if (h[k] >= 0)
+        a.hot_ent[(long long)jlo + count + s_ks[h[k]] + rk[k]] =
+            ((unsigned)h[k] << 16) | (unsigned)s_obag[tid + k * kSortThreads];
+    count += s_ks[nh];
+    __syncthreads();  // s_obag and s_ks are reused by the next batch
+  }
+  if (tid == 0) a.hot_scnt[g] = count;
+}
+
+template <int D>
+__global__ __launch_bounds__(kHotThreads) void k_bwd_hot(BwdArgs a) {
+  using S = HotShape<D>;
+  constexpr int E = S::E, KMAX = S::KMAX, STAGE = S::STAGE, LOADS = S::LOADS, EPT = S::EPT;
+  static_assert(LOADS >= 1 && STAGE * D == LOADS * 4 * kHotThreads, "a stage is whole loads");
+  static_assert(kHotBags % STAGE == 0, "a block is whole stages");
+  __shared__ double s_acc[KMAX * D];
+  __shared__ float s_grad[(STAGE + 1) * D];  // row STAGE stays zero: the padding entries' row
+  __shared__ double s_scale[STAGE + 1];
+  __shared__ unsigned s_list[kHotEnt];
+  __shared__ int s_off[kHotBags + 1];
+  if (!a.plan[kPlanHotOk]) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = blockIdx.x, f = blockIdx.y;
+  const int bin = a.plan[a.pl.o_fbin + f];
+  const int nh = a.hot_n[bin];
+  if (nh == 0) return;  // the same for the whole block
+  const int hb = a.hot_base[bin];
+  const int i0 = c * kHotBags;
+  const int nb = a.B - i0 < kHotBags ? a.B - i0 : kHotBags;
+  const long long fb = (long long)f * a.B + i0;  // merged index of the first bag
+  const int g0 = f * a.hot_spf + c * (kHotBags / STAGE);  // the block's first stage
+  const bool mean = a.pool == RECIS_POOL_MEAN;
+  for (int i = tid; i < nh * D; i += kHotThreads) s_acc[i] = 0.0;
+  for (int i = tid; i <= nb; i += kHotThreads) s_off[i] = a.off[fb + i];
+  if (tid < D) s_grad[STAGE * D + tid] = 0.f;
+  if (tid == 0) s_scale[STAGE] = 0.0;
+  __syncthreads();
+  // a stage's loads: LOADS gradient quads and the first kHotEnt of its
+  // sorted entries, from indices clamped into range
+  float gq[LOADS][4];
+  unsigned ge[EPT];
+  int gcnt = 0;
+  auto load_stage = [&](int sb0) {
+    const int sn = nb - sb0 < STAGE ? nb - sb0 : STAGE;
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int x = tid + k * kHotThreads;  // quad x: bag x / (D / 4), quad x % (D / 4)
+      int bl = x / (D / 4);
+      bl = bl < sn ? bl : sn - 1;
+      const long long i = i0 + sb0 + bl;  // bag within the feature
+      load_grad<4>(a.grad, (i * a.F + f) * D + (x % (D / 4)) * 4, a.gdt, gq[k]);
+    }
+    gcnt = a.hot_scnt[g0 + sb0 / STAGE];
+    const long long jlo = s_off[sb0];
+    const int last = gcnt > 0 ? gcnt - 1 : 0;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = tid + k * kHotThreads;
+      // an entry of the stage; with none, the stage's first occurrence slot
+      // (or slot 0 past the last occurrence): read, never used
+      const long long j = gcnt > 0 ? jlo + (e < gcnt ? e : last) : (jlo < a.n_occ ? jlo : 0);
+      ge[k] = a.hot_ent[j];
+    }
+  };
+  // The share [r0, r1) of one wave in entries [0, ne) of s_list, 64 entries
+  // at a time: each lane reads one entry, its row's place and (mean pooling)
+  // its bag's scale, and notes whether a run ends there (the next entry has
+  // another key, or it is the last one); one ballot gives the wave those
+  // ends, and the wave takes the entries one by one from those lanes, the
+  // 64 positions unrolled.  Per entry that is one LDS read, a conversion and
+  // a double add on the vector side and one bit test on the scalar side (the
+  // CU's one scalar unit, shared by all its waves, would otherwise bound the
+  // pass); a run's end is a branch the wave takes or skips.  Entries past the
+  // share read the zero row.
+  auto accumulate = [&](int ne, auto mean_tag) __attribute__((always_inline)) {
+    constexpr bool MEAN = decltype(mean_tag)::value;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int r0 = __builtin_amdgcn_readfirstlane((int)((long long)ne * wu / (kHotThreads / 64)));
+    const int r1 = __builtin_amdgcn_readfirstlane((int)((long long)ne * (wu + 1) / (kHotThreads / 64)));
+    double acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0;
+    for (int rb = r0; rb < r1; rb += 64) {
+      const int cnt = r1 - rb < 64 ? r1 - rb : 64;
+      const bool valid = lane < cnt;
+      const unsigned my_en = s_list[valid ? rb + lane : r1 - 1];
+      const int my_key = (int)(my_en >> 16);
+      const int my_bag = valid ? (int)(my_en & 0xFFFFu) : STAGE;
+      const int my_row = my_bag * D;
+      double my_sc = 1.0;
+      if constexpr (MEAN) my_sc = s_scale[my_bag];
+      const int my_lo = __double2loint(my_sc), my_hi = __double2hiint(my_sc);
+      const int next_key = __shfl_down(my_key, 1);
+      const unsigned long long ends = __ballot(valid && (lane == cnt - 1 || next_key != my_key));
+#pragma unroll
+      for (int gi = 0; gi < 64 / kHotUnroll; ++gi) {
+        if (gi * kHotUnroll >= cnt) break;  // the same for the whole wave
+        float gv[kHotUnroll][E];
+#pragma unroll
+        for (int v = 0; v < kHotUnroll; ++v) {
+          const int row = __builtin_amdgcn_readlane(my_row, gi * kHotUnroll + v);
+#pragma unroll
+          for (int e = 0; e < E; ++e) gv[v][e] = s_grad[row + e * 64 + lane];
+        }
+#pragma unroll
+        for (int v = 0; v < kHotUnroll; ++v) {
+          const int q = gi * kHotUnroll + v;
+          if constexpr (MEAN) {
+            const double sc =
+                __hiloint2double(__builtin_amdgcn_readlane(my_hi, q), __builtin_amdgcn_readlane(my_lo, q));
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += (double)gv[v][e] * sc;
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += (double)gv[v][e];
+          }
+          if (ends & (1ull << q)) {
+            const int h = __builtin_amdgcn_readlane(my_key, q);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              atomicAdd(&s_acc[h * D + e * 64 + lane], acc[e]);
+              acc[e] = 0.0;
+            }
+          }
+        }
+      }
+    }
+  };
+  auto accumulate_any = [&](int ne) __attribute__((always_inline)) {
+    if (mean) accumulate(ne, std::true_type{});
+    else accumulate(ne, std::false_type{});
+  };
+  if (nb > 0) load_stage(0);
+  for (int sb0 = 0; sb0 < nb; sb0 += STAGE) {
+    const int sn = nb - sb0 < STAGE ? nb - sb0 : STAGE;
+    const int cnt = gcnt;
+    const long long jlo = s_off[sb0];
+    __syncthreads();  // the previous stage's rows and entries are no longer read
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int x = tid + k * kHotThreads;
+      const int bl = x / (D / 4), q = x % (D / 4);
+      if (bl < sn)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_grad[bl * D + q * 4 + e] = gq[k][e];
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = tid + k * kHotThreads;
+      if (e < cnt) s_list[e] = ge[k];
+    }
+    if (tid < sn) {
+      const int len = s_off[sb0 + tid + 1] - s_off[sb0 + tid];
+      s_scale[tid] = mean ? 1.0 / (double)(len > 0 ? len : 1) : 1.0;
+    }
+    __syncthreads();
+    if (sb0 + STAGE < nb) load_stage(sb0 + STAGE);  // in flight while this stage is summed
+    accumulate_any(cnt < kHotEnt ? cnt : kHotEnt);
+    // a stage with more entries than s_list holds (long bags): the rest, a
+    // part at a time (their loads also wait for the prefetch: rare)
+    for (int e0 = kHotEnt; e0 < cnt; e0 += kHotEnt) {
+      const int ne = cnt - e0 < kHotEnt ? cnt - e0 : kHotEnt;
+      __syncthreads();
+      for (int e = tid; e < ne; e += kHotThreads) s_list[e] = a.hot_ent[jlo + e0 + e];
+      __syncthreads();
+      accumulate_any(ne);
+    }
+  }
+  __syncthreads();
+  // partial (hb + h) * hot_nc + c of each hot key h of the bin
+  for (int i = tid; i < nh * D; i += kHotThreads) {
+    const int h = i / D, d = i - h * D;
+    a.hot_partials[((long long)(hb + h) * a.hot_nc + c) * D + d] = s_acc[i];
+  }
 }
 
 template <int D, typename TP, int OPT>
@@ -1122,6 +1542,10 @@ void bwd_dispatch(BwdArgs a, long long n, hipStream_t s) {
   long long lb = (n / kChunk + 4) / 4;
   lb = lb > 2048 ? 2048 : (lb < 1 ? 1 : lb);
   RECIS_LAUNCH("k_bwd_long_partial", (k_bwd_long_partial<D, TP>), dim3((unsigned)lb), dim3(256), s, a);
+  if constexpr (D == 64 || D == 128) {
+    if (a.hot)
+      RECIS_LAUNCH("k_bwd_hot", k_bwd_hot<D>, dim3((unsigned)a.hot_nc, (unsigned)a.F), dim3(kHotThreads), s, a);
+  }
   long long fb = (n / (kShortMax + 1) + 4) / 4;  // long keys <= n / (kShortMax + 1), four per block
   fb = fb > 2048 ? 2048 : (fb < 1 ? 1 : fb);
   RECIS_LAUNCH("k_bwd_long_final", (k_bwd_long_final<D, TP, OPT>), dim3((unsigned)fb), dim3(256), s, a);
@@ -1180,8 +1604,9 @@ void launch_forward(const recis_lookup_result& res, const TableDev& t, int pool,
 
 recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, int pool,
                              const void* grad, int grad_dtype, const OptConsts& oc,
-                             double* partials, int* reorder, long long reorder_ints, bool current,
-                             hipStream_t s) {
+                             double* partials, int* reorder, long long reorder_ints,
+                             double* hot_partials, long long hot_rows, int* hot_ws, long long hot_ws_len,
+                             bool current, hipStream_t s) {
   if (res.n == 0) return RECIS_OK;
   BwdArgs a;
   a.current = current ? 1 : 0;
@@ -1207,28 +1632,71 @@ recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, 
   a.long_base = res.plan + a.pl.o_long_base;
   a.long_nch = res.plan + a.pl.o_long_nch;
   a.owner = res.plan + a.pl.o_chunk_owner;
-  // pooled gradients larger than the memory-side cache: the long keys'
-  // chunks go feature by feature (see k_long_place)
+  a.nchunks = nullptr;
+  a.hot = 0;
+  a.hot_nc = (int)hot_blocks(res.batch);
+  a.hot_min = hot_min_count(a.hot_nc);
+  a.hot_partials = hot_partials;
+  // The long keys' plan is rebuilt feature by feature (see k_long_place) for
+  // pooled gradients larger than the memory-side cache, and whenever hot keys
+  // are summed bag-major (the hot pass needs room for every feature's hot
+  // keys, and the plan room for its hot indices).
+  const bool pooled = pool != RECIS_POOL_NONE;
+  const int kmax = hot_kmax(t.dim);
+  bool hot = pooled && kmax > 0 && hot_partials && hot_ws && res.num_feats <= kFeatBins &&
+             (long long)res.num_feats * kmax * a.hot_nc <= hot_rows &&
+             hot_ws_ints(res.n, res.num_feats, res.batch, t.dim) <= hot_ws_len;
+  a.hot_spf = (int)hot_stages(res.batch, t.dim);
+  a.n_occ = res.n;
   const double grad_bytes = (double)res.num_feats * res.batch * t.dim * (grad_dtype == RECIS_DTYPE_BF16 ? 2 : 4);
-  if (pool != RECIS_POOL_NONE && grad_bytes > kMemCacheBytes && reorder_ints > 0) {
-    const long long maxl = res.n / (kShortMax + 1) + 1, maxc = res.n / kChunk + maxl + 1;
-    const long long bins_at = (3 * maxl + maxc + 1) & ~1ll;  // 8-byte aligned (the scratch is)
-    if (bins_at + 2 * (long long)kFeatBins <= reorder_ints) {
-      int* ou = reorder;
-      int* ob = ou + maxl;
-      int* on = ob + maxl;
-      int* oo = on + maxl;
-      unsigned long long* bins = reinterpret_cast<unsigned long long*>(reorder + bins_at);
-      const unsigned kb = (unsigned)((maxl + 255) / 256);
-      RECIS_LAUNCH("k_long_zero", k_zero_u64, dim3(kFeatBins / 256), dim3(256), s, bins, (long long)kFeatBins);
-      RECIS_LAUNCH("k_long_hist", k_long_hist, dim3(kb), dim3(256), s, a, bins);
-      RECIS_LAUNCH("k_long_scan", k_long_scan, dim3(1), dim3(1024), s, bins);
-      RECIS_LAUNCH("k_long_place", k_long_place, dim3(kb), dim3(256), s, a, bins, ou, ob, on, oo);
-      a.long_u = ou;
-      a.long_base = ob;
-      a.long_nch = on;
-      a.owner = oo;
+  const long long maxl = res.n / (kShortMax + 1) + 1, maxc = res.n / kChunk + maxl + 1;
+  const long long bins_at = (3 * maxl + maxc + 1) & ~1ll;  // 8-byte aligned (the scratch is)
+  const long long plain_need = bins_at + 2 * (long long)kFeatBins + 2;
+  if (pooled && reorder_ints > 0 && (hot || grad_bytes > kMemCacheBytes) && plain_need <= reorder_ints) {
+    int* ou = reorder;
+    int* ob = ou + maxl;
+    int* on = ob + maxl;
+    int* oo = on + maxl;
+    unsigned long long* bins = reinterpret_cast<unsigned long long*>(reorder + bins_at);
+    int* ncold = reorder + bins_at + 2 * kFeatBins;
+    const unsigned kb = (unsigned)((maxl + 255) / 256);
+    RECIS_LAUNCH("k_long_zero", k_zero_u64, dim3(kFeatBins / 256), dim3(256), s, bins, (long long)kFeatBins);
+    if (hot) {
+      a.hot = 1;
+      a.hot_cls = reinterpret_cast<unsigned*>(hot_ws);  // 16-byte aligned: k_hot_plan reads it by 4
+      a.hot_thr = hot_ws + (long long)kFeatBins * kHotClasses;
+      a.hot_n = a.hot_thr + kFeatBins;
+      a.hot_base = a.hot_n + kFeatBins;
+      a.hot_cnt = a.hot_base + kFeatBins;
+      a.hot_ent = reinterpret_cast<unsigned*>(a.hot_cnt + kFeatBins);
+      a.hot_of = reinterpret_cast<unsigned char*>(a.hot_ent + res.n);
+      a.hot_scnt = reinterpret_cast<int*>(a.hot_of) + (res.n + 3) / 4;
+      const long long cls_u64 = (long long)kFeatBins * kHotClasses / 2;
+      RECIS_LAUNCH("k_long_zero", k_zero_u64, dim3((unsigned)((cls_u64 + 255) / 256)), dim3(256), s,
+                   reinterpret_cast<unsigned long long*>(a.hot_cls), cls_u64);
+      const long long fg = std::min<long long>(4096, res.n / 256 + 1);
+      RECIS_LAUNCH("k_hot_fill", k_hot_fill, dim3((unsigned)fg), dim3(256), s, a);
+      RECIS_LAUNCH("k_hot_hist", k_hot_hist, dim3(kb), dim3(256), s, a);
+      if (kmax == hot_kmax(64))
+        RECIS_LAUNCH("k_hot_plan", k_hot_plan<HotShape<64>::KMAX>, dim3(1), dim3(1024), s, a);
+      else
+        RECIS_LAUNCH("k_hot_plan", k_hot_plan<HotShape<128>::KMAX>, dim3(1), dim3(1024), s, a);
     }
+    RECIS_LAUNCH("k_long_hist", k_long_hist, dim3(kb), dim3(256), s, a, bins);
+    RECIS_LAUNCH("k_long_scan", k_long_scan, dim3(1), dim3(1024), s, bins, ncold);
+    RECIS_LAUNCH("k_long_place", k_long_place, dim3(kb), dim3(256), s, a, bins, ou, ob, on, oo);
+    if (hot) {
+      const unsigned sg = (unsigned)((long long)res.num_feats * a.hot_spf);
+      if (t.dim == 64)
+        RECIS_LAUNCH("k_hot_sort", k_hot_sort<64>, dim3(sg), dim3(kSortThreads), s, a, res.inverse);
+      else
+        RECIS_LAUNCH("k_hot_sort", k_hot_sort<128>, dim3(sg), dim3(kSortThreads), s, a, res.inverse);
+    }
+    a.long_u = ou;
+    a.long_base = ob;
+    a.long_nch = on;
+    a.owner = oo;
+    a.nchunks = ncold;
   }
   if (t.dtype == RECIS_DTYPE_BF16) {
     if (t.optim == RECIS_OPTIM_ADAGRAD) bwd_dim<bf16_t, RECIS_OPTIM_ADAGRAD>(a, t.dim, res.n, s);

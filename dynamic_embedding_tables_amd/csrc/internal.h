@@ -132,10 +132,18 @@ struct FeatDev {
 };
 
 // Backward work plan header (in recis_lookup_result.plan).
+// Feature bins: a key's bin is its feature slot modulo kFeatBins.  The
+// backward groups the long keys by bin, and picks the hot keys of each bin.
+constexpr int kFeatBins = 4096;
+
+// Plan words 0..3: long keys, chunks, whether the lookup's features have
+// distinct bins (kPlanHotOk, with at most kFeatBins features), unused.
+// Words o_fbin..: the bin of each feature.
+constexpr int kPlanHotOk = 2;
 struct PlanLayout {
   long long max_long, max_chunks;
   // word offsets
-  long long o_long_u, o_long_base, o_long_nch, o_chunk_owner, o_idslot, o_occref;
+  long long o_fbin, o_long_u, o_long_base, o_long_nch, o_chunk_owner, o_idslot, o_occref;
   long long words;
 };
 
@@ -143,7 +151,8 @@ __host__ __device__ inline PlanLayout plan_layout(long long cap) {
   PlanLayout p;
   p.max_long = cap / kShortMax + 1;
   p.max_chunks = cap / kChunk + p.max_long + 1;
-  p.o_long_u = 4;
+  p.o_fbin = 4;
+  p.o_long_u = p.o_fbin + kFeatBins;
   p.o_long_base = p.o_long_u + p.max_long;
   p.o_long_nch = p.o_long_base + p.max_long;
   p.o_chunk_owner = p.o_long_nch + p.max_long;
@@ -401,6 +410,10 @@ struct recis_table {
   unsigned* sketch = nullptr;    // [kSketchRows << cfg.admit_sketch_bits] when sketch admission is on
   long long* wb_keys = nullptr;
   double* partials = nullptr;
+  double* hot_partials = nullptr;  // the hot keys' partials: hot_rows rows of dim doubles
+  long long hot_rows = 0;
+  int* hot_ws = nullptr;  // the hot pass's workspace: hot_ws_len ints
+  long long hot_ws_len = 0;
 
   // pinned staging ring for per-call descriptors
   static constexpr int kRing = 4;
@@ -469,6 +482,7 @@ struct LookupLaunch {
   unsigned short* occ_local;  // N: each occurrence's index among its tile's distinct keys
   int* obase;                 // nbk + 1: occurrences per bucket, then the first grouped position
   int big_tab;                // buckets average more than kBucketOcc occurrences
+  int hot_ok;                 // at most kFeatBins features, in distinct feature bins
   int* hist;                  // [part_blocks][nbk]
   int* bbase;                 // nbk + 1: first position of each bucket
   int* ubase;                 // nbk + 1: distinct keys per bucket, then their first index
@@ -501,12 +515,43 @@ struct OptConsts {
   float lr, b1, omb1, b2, omb2, eps, step_size;  // omb = 1 - beta, formed in double
 };
 // reorder: device scratch of reorder_ints ints for the long keys' plan in
-// feature order (used when the pooled gradient exceeds kMemCacheBytes).
+// feature order (used when the pooled gradient exceeds kMemCacheBytes, or
+// with hot keys).
 constexpr double kMemCacheBytes = 256.0 * 1024 * 1024;  // the memory-side (Infinity) cache
+// Hot keys (pooled backward, dim 64 or 128): per feature at most
+// hot_kmax(dim) long keys with at least hot_min_count(blocks) occurrences
+// are summed bag-major, one partial per key and block of kHotBags bags.
+// hot_partials: hot_rows rows of dim doubles, at least
+// num_feats * hot_kmax(dim) * hot_blocks(batch) for the pass to run.
+constexpr int kHotBags = 2048;
+__host__ __device__ inline int hot_kmax(int dim) { return dim == 64 || dim == 128 ? 8192 / dim : 0; }
+__host__ __device__ inline long long hot_blocks(int batch) { return (batch + kHotBags - 1) / kHotBags; }
+// The pass takes a block's bags hot_stage(dim) at a time (kHotBags is a
+// multiple of it); per stage the hot occurrences are sorted by key first.
+__host__ __device__ inline int hot_stage(int dim) { return dim == 64 || dim == 128 ? 16384 / dim : 1; }
+__host__ __device__ inline long long hot_stages(int batch, int dim) {
+  return (batch + hot_stage(dim) - 1) / hot_stage(dim);
+}
+// Its workspace (ints): per bin the count classes, threshold, hot-key count,
+// first hot index and placement counter; per distinct key its hot index; per
+// occurrence slot a sorted hot entry; per distinct key its hot index (a
+// byte); per (feature, stage) the entry count.
+constexpr int kHotClasses = 32;
+__host__ __device__ inline long long hot_ws_ints(long long n, int num_feats, int batch, int dim) {
+  return (long long)kFeatBins * (kHotClasses + 4) + n + (n + 3) / 4 + (long long)num_feats * hot_stages(batch, dim) +
+         16;
+}
+// A hot key's partial rows cost about as much as 4 of its gradient rows
+// each; with 8 occurrences per partial the bag-major pass reads fewer bytes.
+__host__ __device__ inline int hot_min_count(long long blocks) {
+  const long long m = 8 * blocks;
+  return m > kShortMax + 1 ? (int)(m < (1 << 30) ? m : (1 << 30)) : kShortMax + 1;
+}
 recis_status launch_backward(const recis_lookup_result& res, const TableDev& t, int pool,
                              const void* grad, int grad_dtype, const OptConsts& oc,
-                             double* partials, int* reorder, long long reorder_ints, bool current,
-                             hipStream_t s);
+                             double* partials, int* reorder, long long reorder_ints,
+                             double* hot_partials, long long hot_rows, int* hot_ws, long long hot_ws_len,
+                             bool current, hipStream_t s);
 
 // The fixed device scratch of the allocation-free backward: the long keys'
 // chunk partials, kNoAllocScratchBytes on each GPU the library runs it on,

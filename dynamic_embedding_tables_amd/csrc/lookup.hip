@@ -157,10 +157,14 @@ __device__ __forceinline__ long long transform_value(long long v, const FeatDev&
 __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
   const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
   const long long nb = (long long)L.F * L.B;
+  if (L.hot_ok && idx < L.F) {  // F <= kFeatBins <= the grid here (B >= 1 when N > 0)
+    L.res.plan[plan_layout(L.res.capacity).o_fbin + idx] = (int)(L.feats[idx].slot & (kFeatBins - 1));
+  }
   if (idx == 0) {
     *L.res.num_unique = 0;
     L.res.plan[0] = 0;  // long keys
     L.res.plan[1] = 0;  // chunks
+    L.res.plan[kPlanHotOk] = L.hot_ok;
     L.hslice[0] = 0;    // heavy slices (listed by k_part_colscan)
   }
   if (idx > nb) return;

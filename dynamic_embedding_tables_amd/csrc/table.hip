@@ -510,6 +510,8 @@ recis_status recis_idmap_destroy(recis_table* t) {
   tab_free(t, t->last_use, (size_t)t->slot_cap * sizeof(unsigned), s);
   tab_free(t, t->sketch, (size_t)((long long)kSketchRows << t->cfg.admit_sketch_bits) * sizeof(unsigned), s);
   tab_free(t, t->ctr, sizeof(DevCounters), s);
+  tab_free(t, t->hot_partials, (size_t)t->hot_rows * (size_t)t->cfg.dim * 8, s);
+  tab_free(t, t->hot_ws, (size_t)t->hot_ws_len * 4, s);
   free_scratch(t, s);
   for (int k = 0; k < recis_table::kRing; ++k) {
     if (t->stage_host[k]) (void)hipHostFree(t->stage_host[k]);
@@ -617,6 +619,17 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.occ_local = t->occ_local;
   L.obase = t->bbase + 2 * (kMaxBuckets + 1);
   L.big_tab = g.big;
+  // the backward's hot-key pass needs each feature's own bin
+  L.hot_ok = 0;
+  if (!(flags & RECIS_GROUP_BY_OCCURRENCE) && num_feats <= kFeatBins && N > 0) {
+    std::vector<unsigned char> used(kFeatBins, 0);
+    L.hot_ok = 1;
+    for (int f = 0; f < num_feats && L.hot_ok; ++f) {
+      const unsigned bin = feats[f].slot & (kFeatBins - 1);
+      if (used[bin]) L.hot_ok = 0;
+      used[bin] = 1;
+    }
+  }
   L.hist = t->hist;
   L.bbase = t->bbase;
   L.ubase = t->ubase;
@@ -766,6 +779,40 @@ recis_status pool_bwd_update(recis_table* t, const recis_lookup_result* res, int
     reorder = reinterpret_cast<int*>(t->wb_keys);
     reorder_ints = 2 * t->scr_cap;
   }
+  // the hot keys' partials (not in the allocation-free call: its long keys
+  // keep the chunked plan)
+  double* hot_partials = nullptr;
+  long long hot_rows = 0;
+  int* hot_ws = nullptr;
+  long long hot_ws_len = 0;
+  if (!noalloc && pool != RECIS_POOL_NONE && hot_kmax(t->cfg.dim) > 0 && res->num_feats <= kFeatBins &&
+      res->n > 0) {
+    const long long rows = (long long)res->num_feats * hot_kmax(t->cfg.dim) * hot_blocks(res->batch);
+    const long long ws = hot_ws_ints(res->n, res->num_feats, res->batch, t->cfg.dim);
+    if (rows <= INT32_MAX / 2) {
+      if (rows > t->hot_rows || ws > t->hot_ws_len) {
+        HIP_TRY(hipStreamSynchronize(s));
+        if (rows > t->hot_rows) {
+          tab_free(t, t->hot_partials, (size_t)t->hot_rows * (size_t)t->cfg.dim * 8, s);
+          t->hot_rows = 0;
+          t->hot_partials = static_cast<double*>(tab_alloc(t, (size_t)rows * (size_t)t->cfg.dim * 8, s));
+          if (t->hot_partials) t->hot_rows = rows;
+        }
+        if (ws > t->hot_ws_len) {
+          tab_free(t, t->hot_ws, (size_t)t->hot_ws_len * 4, s);
+          t->hot_ws_len = 0;
+          t->hot_ws = static_cast<int*>(tab_alloc(t, (size_t)ws * 4, s));
+          if (t->hot_ws) t->hot_ws_len = ws;
+        }
+      }
+      if (t->hot_partials && t->hot_ws) {
+        hot_partials = t->hot_partials;
+        hot_rows = t->hot_rows;
+        hot_ws = t->hot_ws;
+        hot_ws_len = t->hot_ws_len;
+      }
+    }
+  }
   OptConsts oc;
   oc.lr = (float)opt->lr;
   oc.eps = (float)opt->eps;
@@ -784,7 +831,7 @@ recis_status pool_bwd_update(recis_table* t, const recis_lookup_result* res, int
   const bool current = !moved && res->epoch == t->update_epoch;
   t->update_epoch += 1;
   recis_status st = launch_backward(*res, t->dev(), pool, grad_out, grad_dtype, oc, partials, reorder, reorder_ints,
-                                    current, s);
+                                    hot_partials, hot_rows, hot_ws, hot_ws_len, current, s);
   if (st != RECIS_OK) return st;
   return check_launch();
 }
