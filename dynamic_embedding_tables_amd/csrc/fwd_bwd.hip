@@ -1167,6 +1167,7 @@ __global__ __launch_bounds__(1024) void k_hot_plan(BwdArgs a) {
     a.hot_base[tid * kPer + k] = base;
     base += n[k];
   }
+  if (tid == 1023) a.t.ctr->hot_keys += (unsigned long long)base;
 }
 
 __global__ __launch_bounds__(256) void k_long_hist(BwdArgs a, unsigned long long* bins) {

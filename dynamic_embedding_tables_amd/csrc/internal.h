@@ -115,6 +115,8 @@ struct DevCounters {
   // (key, tile) pairs: distinct keys of each tile of kTileOcc consecutive
   // occurrences, summed over the tiles of every insert_find since creation
   unsigned long long lookup_pairs;
+  // long keys the backward summed bag-major (hot keys), over every call
+  unsigned long long hot_keys;
 };
 
 // Device view of one feature of a call.

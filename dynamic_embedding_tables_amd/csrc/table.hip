@@ -956,6 +956,7 @@ recis_status recis_idmap_stats(recis_table* t, recis_table_stats* out, hipStream
   out->claim_attempts = (int64_t)c.claim_attempts;
   out->claim_failures = (int64_t)c.claim_failures;
   out->lookup_pairs = (int64_t)c.lookup_pairs;
+  out->hot_keys = (int64_t)c.hot_keys;
   return RECIS_OK;
 }
 

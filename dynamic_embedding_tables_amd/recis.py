@@ -94,7 +94,7 @@ class recis_table_stats(C.Structure):
                 ("blocks", C.c_int64), ("slot_capacity", C.c_int64), ("adam_step", C.c_int64),
                 ("bytes", C.c_int64), ("probationary_keys", C.c_int64), ("claim_attempts", C.c_int64),
                 ("claim_failures", C.c_int64), ("hbm_rows", C.c_int64),
-                ("lookup_pairs", C.c_int64)]
+                ("lookup_pairs", C.c_int64), ("hot_keys", C.c_int64)]
 
 
 class RecisError(RuntimeError):

@@ -238,6 +238,14 @@ typedef struct {
                              over the tiles of every call since creation.  The
                              later passes move one record per such pair, not one
                              per occurrence */
+  int64_t hot_keys;       /* long keys (more than 64 occurrences in a call) whose gradient
+                             sum the pooled backward took bag-major -- each bag's upstream
+                             gradient row read once for all of them -- instead of key by
+                             key, summed over every call since creation.  Per call and
+                             feature at most 8192 / dim of the keys with the most
+                             occurrences (dim 64 or 128; features in distinct feature
+                             slots modulo 4096), each with at least 8 occurrences per
+                             block of 2048 bags */
 } recis_table_stats;
 
 /* Creates a table.  Allocates the IDMap and `reserve_rows` worth of blocks

@@ -58,7 +58,8 @@ def check_tiers(table):
 
 
 def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopulate=None,
-               export_every=1, evict_decay=0.0, lru_max=None, find_only_steps=(), retier_every=0):
+               export_every=1, evict_decay=0.0, lru_max=None, find_only_steps=(), retier_every=0,
+               stats_out=None):
     import torch
     from dynamic_embedding_tables_amd import recis
     table = make_table(spec, **(table_kw or {}))
@@ -105,6 +106,8 @@ def run_parity(spec, batches, table_kw=None, evict_every=0, evict_min=2, prepopu
     st = table.stats()
     assert st.keys == otab.size()
     assert st.rows_in_use == otab.rows_in_use()
+    if stats_out is not None:
+        stats_out.append(st)
     table.close()
     return passes
 
@@ -887,6 +890,89 @@ def test_lookup_pairs_are_tile_distinct_keys(batch, num_feats):
     assert table.stats().lookup_pairs == 2 * want
     table.close()
     otab.close()
+
+
+def _hot_batch(seed, B, dim, key_space, num_feats, slots, alpha, long_bags=False):
+    """Power-law IDs that give each feature many keys with more than 64
+    occurrences (the backward's long keys), ragged bags with empty ones in
+    the middle and at the end, or long bags (a stage of the bag-major pass
+    then holds more occurrences than one sorted batch)."""
+    rng = W.rng_for(seed)
+    feats = []
+    for f in range(num_feats):
+        lens = rng.integers(40, 81, B) if long_bags else rng.poisson(8, B)
+        lens[::97] = 0
+        lens[-3:] = 0
+        off = W.offsets_from_lengths(lens)
+        # ranks 1..key_space with P(k) proportional to k**-alpha
+        pk = np.arange(1, key_space + 1, dtype=np.float64) ** -alpha
+        vals = rng.choice(key_space, int(off[-1]), p=pk / pk.sum()).astype(np.int64) + 1
+        feats.append(W.FeatureInput(values=vals, bag_offsets=off, slot=slots[f]))
+    return W.Batch(feats, B, rng.standard_normal((B, num_feats * dim), dtype=np.float32))
+
+
+def _expected_hot_keys(batch, dim):
+    """The keys the pooled backward sums bag-major, by the rule the stats
+    field documents: per feature (each in its own slot modulo 4096), of the
+    keys with more than 64 occurrences and at least 8 per block of 2048 bags,
+    whole count classes floor(log2(count)) from the top while at most
+    8192 / dim keys fit."""
+    bins = [f.slot % 4096 for f in batch.features]
+    if len(set(bins)) != len(bins):
+        return 0
+    blocks = -(-batch.batch // 2048)
+    kmax = 8192 // dim
+    total = 0
+    for f in batch.features:
+        _, counts = np.unique(f.values, return_counts=True)
+        c = counts[(counts > 64) & (counts >= 8 * blocks)]
+        cls = np.floor(np.log2(c)).astype(np.int64)
+        taken = 0
+        for k in range(31, -1, -1):
+            x = int((cls == k).sum())
+            if taken + x > kmax:
+                break
+            taken += x
+        total += taken
+    return total
+
+
+@pytest.mark.parametrize("case", ["sum64_threshold_split", "mean128_bf16_grad", "long_bags", "shared_slot",
+                                  "slots_alike_mod_4096"])
+def test_hot_keys_summed_bag_major(case):
+    """The pooled backward's bag-major pass for hot long keys, at parity with
+    the oracle over two steps: several 2048-bag blocks with a partial last
+    one; more eligible keys than a feature's limit (the count classes split);
+    mean pooling with bf16 gradients at dim 128; stages with more
+    occurrences than one sorted batch; and features whose slots coincide
+    modulo 4096 (the pass stays off).  The stats count exactly the keys the
+    documented rule selects."""
+    spec_kw = dict(dtype="f32", optim="adam", lr=1e-3, eps=1e-8)
+    if case == "sum64_threshold_split":
+        dim, pool, gdt = 64, "sum", "f32"
+        mk = lambda s: _hot_batch(s, 5000, dim, 400, 2, (1, 2), 0.8)
+    elif case == "mean128_bf16_grad":
+        dim, pool, gdt = 128, "mean", "bf16"
+        mk = lambda s: _hot_batch(s, 3000, dim, 300, 3, (4, 5, 6), 0.8)
+    elif case == "long_bags":
+        dim, pool, gdt = 64, "sum", "f32"
+        mk = lambda s: _hot_batch(s, 600, dim, 4000, 1, (7,), 1.2, long_bags=True)
+    elif case == "shared_slot":
+        dim, pool, gdt = 64, "mean", "f32"
+        mk = lambda s: _hot_batch(s, 2500, dim, 1500, 2, (8, 8), 1.1)
+    else:
+        dim, pool, gdt = 64, "mean", "f32"
+        mk = lambda s: _hot_batch(s, 2500, dim, 1500, 2, (3, 4099), 1.1)
+    spec = W.TableSpec(dim=dim, pool=pool, grad_dtype=gdt, **spec_kw)
+    batches = [mk(900 + s) for s in range(2)]
+    want = sum(_expected_hot_keys(b, dim) for b in batches)
+    if case in ("shared_slot", "slots_alike_mod_4096"):
+        assert want == 0
+    else:
+        assert want > 0
+    st = []
+    run_parity(spec, batches, stats_out=st)
+    assert st[0].hot_keys == want
 
 
 def test_torch_allocator_bridge():
