@@ -192,31 +192,65 @@ def copy_calibration(torch, dev):
     torch.cuda.synchronize()
 
 
-def step_shapes(results, U, resident0):
+def hot_mask(keys, counts, batch, dim):
+    """The long keys the pooled backward sums bag-major (the rule the
+    library's stats field hot_keys documents): per feature bin (key slot
+    modulo 4096), of the keys with more than SHORT_MAX occurrences and at
+    least 8 per block of 2048 bags, whole count classes floor(log2(count))
+    from the top while at most 8192 / dim keys fit."""
+    hot = np.zeros(keys.size, bool)
+    if dim not in (64, 128):
+        return hot
+    blocks = -(-batch // 2048)
+    kmax = 8192 // dim
+    elig = (counts > SHORT_MAX) & (counts >= 8 * blocks) & (keys >= 0)
+    bins = (keys >> 48) & 4095
+    cls = np.floor(np.log2(np.maximum(counts, 1))).astype(np.int64)
+    for b in np.unique(bins[elig]):
+        m = elig & (bins == b)
+        taken, thr = 0, 32
+        for k in range(31, -1, -1):
+            x = int((cls[m] == k).sum())
+            if taken + x > kmax:
+                break
+            taken += x
+            if x:
+                thr = k
+        hot |= m & (cls >= thr)
+    return hot
+
+
+def step_shapes(results, U, resident0, hot=None):
     """Per timed step: distinct keys with a row and count <= SHORT_MAX (short)
     or more (long), how many short ones got their row in that step, and the
-    occurrences of short keys; averaged over the steps."""
+    occurrences of short keys; of the long keys, those summed bag-major (hot,
+    when hot = (batch, dim) says the pass runs) and the chunks of the others;
+    averaged over the steps."""
     per = []
     for r, u in zip(results, U):
         counts = r.counts[:u].cpu().numpy().astype(np.int64)
         raw = r.unique_rows[:u].cpu().numpy()
-        per.append((counts, raw >= 0, raw & ((1 << 62) - 1)))
+        keys = r.unique_keys[:u].cpu().numpy()
+        hm = hot_mask(keys, counts, *hot) if hot else np.zeros(u, bool)
+        per.append((counts, raw >= 0, raw & ((1 << 62) - 1), hm))
     # a row allocated in the timed steps is new in the first step that uses it
-    cand = [np.nonzero(h & (rw >= resident0))[0] for (_, h, rw) in per]
+    cand = [np.nonzero(h & (rw >= resident0))[0] for (_, h, rw, _) in per]
     allrows = np.concatenate([per[k][2][c] for k, c in enumerate(cand)]) if cand else np.zeros(0, np.int64)
     _, first = np.unique(allrows, return_index=True)
     is_first = np.zeros(allrows.size, bool)
     is_first[first] = True
     out, pos = [], 0
-    for (counts, has, _), c in zip(per, cand):
+    for (counts, has, _, hm), c in zip(per, cand):
         new = np.zeros(counts.size, bool)
         new[c[is_first[pos:pos + c.size]]] = True
         pos += c.size
         short = counts <= SHORT_MAX
         lc = counts[~short & has]
+        cold = counts[~short & ~hm]  # the chunked plan takes every long key that is not hot
         out.append({"U_s": int((short & has).sum()), "U_s_new": int((short & new).sum()),
                     "E_s": int(counts[short & has].sum()), "U_l": int((~short & has).sum()),
-                    "E_l": int(lc.sum()), "chunks_l": int(long_chunks(lc).sum())})
+                    "E_l": int(lc.sum()), "U_hot": int(hm.sum()), "E_hot": int(counts[hm].sum()),
+                    "E_l_cold": int(cold.sum()), "chunks_l": int(long_chunks(cold).sum())})
     return {k: float(np.mean([o[k] for o in out])) for k in out[0]}
 
 
@@ -258,9 +292,14 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
       k_occ_tile: per occurrence its pair index 2 read, and its inverse index
         4, grouped entry 4 and forward reference 8 written; per pair its
         record's position 4 and resolved record 16 read; offsets 4 (Bg + 1).
-      k_bwd_long_partial: per long entry 4; per chunk a partial of D fp64
-        written; the gradient rows of the bags its entries touch, at most
-        min(E_l, Bg) pooled (one row per entry when not pooled).
+      k_bwd_long_partial: per entry of a long key that is not hot 4; per
+        chunk a partial of D fp64 written; the gradient rows of the bags its
+        entries touch, at most min(E_l_cold, Bg) pooled (one row per entry
+        when not pooled).
+      k_hot_sort: per occurrence its distinct-key index 4 and that key's hot
+        index 1 read; per hot entry 4 written.
+      k_bwd_hot: every bag's gradient row once, Bg D gs; per hot entry 4; per
+        hot key a partial of D fp64 per block of 2048 bags written.
       step: insert_find 12 N + 4 (Bg + 1) + 32 U + 16 U_new, forward
         4 N + 8 U + U_hit D s + output, backward 4 N + 8 U + U_hit 2P
         + U_new P + gradient; output and gradient Bg D 4 each when pooled,
@@ -277,16 +316,19 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
     count = 12 * Pp
     emit = 32 * Pp + 40 * Um + 16 * Unew
     occ = 18 * N + 20 * Pp + 4 * (Bg + 1)
-    El = shape["E_l"]
+    El = shape.get("E_l_cold", shape["E_l"])
     g_long = min(El, Bg) * D * gs if pooled else El * D * gs
     long_partial = 4 * El + shape["chunks_l"] * D * 8 + g_long
+    Eh, Uh = shape.get("E_hot", 0), shape.get("U_hot", 0)
+    hot_sort = 5 * N + 4 * Eh if Uh else 0
+    hot_pass = Bg * D * gs + 4 * Eh + Uh * shape.get("hot_nc", 1) * D * 8 if Uh else 0
     out_b, grad_b = (Bg * D * 4, Bg * D * 4) if pooled else (N * D * s, N * D * gs)
     ins = 12 * N + 4 * (Bg + 1) + 32 * Um + 16 * Unew
     fwd_call = 4 * N + 8 * Um + Uhit * D * s + out_b
     bwd_call = 4 * N + 8 * Um + Uhit * 2 * P + Unew * P + grad_b
     return {"k_bwd_short": bwd_short, "k_fwd_pool": fwd, "k_fwd_gather": gather,
             "k_tile": tile, "k_pair_scatter": scatter, "k_bucket_count": count, "k_bucket_emit": emit,
-            "k_occ_tile": occ,
+            "k_occ_tile": occ, "k_hot_sort": hot_sort, "k_bwd_hot": hot_pass,
             "k_bwd_long_partial": long_partial, "step": ins + fwd_call + bwd_call}
 
 
@@ -946,7 +988,11 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     Unew = new_rows / K
     Uhit = Um - Unew
     Bg = F * B
-    shape = step_shapes(timed_res, U, int(st0.rows_in_use))
+    # the hot keys by the documented rule, checked against the library's count
+    hot_lib = (st1.hot_keys - st0.hot_keys) / K
+    shape = step_shapes(timed_res, U, int(st0.rows_in_use), hot=(B, D) if pooled and hot_lib > 0 else None)
+    shape["hot_keys_counted_by_library"] = hot_lib
+    shape["hot_nc"] = -(-B // 2048)
     shape["pairs"] = (st1.lookup_pairs - st0.lookup_pairs) / K
     alg = algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s_bytes, S, gs, pooled)
     a_bytes = alg[dom] if dom in alg else None
