@@ -785,8 +785,11 @@ recis_status pool_bwd_update(recis_table* t, const recis_lookup_result* res, int
   long long hot_rows = 0;
   int* hot_ws = nullptr;
   long long hot_ws_len = 0;
+  const double grad_bytes =
+      (double)res->num_feats * res->batch * t->cfg.dim * (grad_dtype == RECIS_DTYPE_BF16 ? 2 : 4);
+  const double hot_from = t->cfg.hot_grad_bytes == 0 ? kMemCacheBytes : (double)t->cfg.hot_grad_bytes;
   if (!noalloc && pool != RECIS_POOL_NONE && hot_kmax(t->cfg.dim) > 0 && res->num_feats <= kFeatBins &&
-      res->n > 0) {
+      res->n > 0 && t->cfg.hot_grad_bytes >= 0 && grad_bytes >= hot_from) {
     const long long rows = (long long)res->num_feats * hot_kmax(t->cfg.dim) * hot_blocks(res->batch);
     const long long ws = hot_ws_ints(res->n, res->num_feats, res->batch, t->cfg.dim);
     if (rows <= INT32_MAX / 2) {

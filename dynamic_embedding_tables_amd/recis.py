@@ -63,7 +63,8 @@ class recis_table_config(C.Structure):
                 ("admit_threshold", C.c_uint32), ("seed", C.c_uint64), ("init_bound", C.c_float),
                 ("max_load", C.c_float), ("slot_capacity", C.c_int64), ("block_rows", C.c_int64),
                 ("max_rows", C.c_int64), ("reserve_rows", C.c_int64), ("block_memory", C.c_int32),
-                ("track_last_use", C.c_int32), ("admit_sketch_bits", C.c_int32), ("device_rows", C.c_int64)]
+                ("track_last_use", C.c_int32), ("admit_sketch_bits", C.c_int32), ("device_rows", C.c_int64),
+                ("hot_grad_bytes", C.c_int64)]
 
 
 class recis_allocator(C.Structure):
@@ -405,7 +406,8 @@ class Table:
                  init_bound: float = 0.05, admit_threshold: int = 1, slot_capacity: int = 1 << 20,
                  block_rows: int = 1 << 20, max_rows: int = (1 << 30) - 1, reserve_rows: int = 0,
                  max_load: float = 0.5, block_memory: str = "device", track_last_use: bool = False,
-                 admit_sketch_bits: int = 0, stream=None, allocator: str = "torch", device_rows: int = 0):
+                 admit_sketch_bits: int = 0, stream=None, allocator: str = "torch", device_rows: int = 0,
+                 hot_grad_bytes: int = 0):
         cfg = recis_table_config_default()
         cfg.dim, cfg.dtype, cfg.optim = dim, DTYPES[dtype], OPTIMS[optim]
         cfg.seed, cfg.init_bound, cfg.admit_threshold = seed, init_bound, admit_threshold
@@ -415,10 +417,12 @@ class Table:
         cfg.track_last_use = 1 if track_last_use else 0
         cfg.admit_sketch_bits = admit_sketch_bits
         cfg.device_rows = device_rows
+        cfg.hot_grad_bytes = hot_grad_bytes
         self.dim, self.dtype, self.optim = dim, dtype, optim
         self.config = {"seed": seed, "init_bound": init_bound, "admit_threshold": admit_threshold,
                        "block_memory": block_memory, "track_last_use": bool(track_last_use),
-                       "admit_sketch_bits": int(admit_sketch_bits), "device_rows": int(device_rows)}
+                       "admit_sketch_bits": int(admit_sketch_bits), "device_rows": int(device_rows),
+                       "hot_grad_bytes": int(hot_grad_bytes)}
         if allocator not in ("torch", "hip"):
             raise ValueError("allocator is 'torch' (torch's caching allocator) or 'hip' (hipMalloc)")
         self.allocator = allocator

@@ -128,11 +128,20 @@ typedef struct {
                                start, so they fill the HBM tier first, and recis_idmap_retier
                                moves the most frequent keys into it.  0: every block in host
                                memory.  Ignored for RECIS_MEM_DEVICE (every row in HBM). */
+  int64_t hot_grad_bytes;   /* the pooled backward sums the gradients of hot long keys
+                               bag-major (each bag's gradient row read once for all of them,
+                               see recis_table_stats.hot_keys) when the upstream gradient
+                               (num_feats * batch * dim elements) holds at least this many
+                               bytes: below that it stays in the memory-side cache and the
+                               key-by-key sums re-read it cheaply.  0: the library's default,
+                               256 MiB; negative: never.  Either way the results agree to
+                               the parity bar (the same terms, summed in another order). */
 } recis_table_config;
 
 /* Fills `cfg` with defaults (dim 64, f32, Adagrad, seed 20250925, bound 0.05,
  * max_load 0.5, 2^20 slots, 2^20 rows per block, max_rows 2^30-1, reserve 0,
- * blocks in device memory, no last-use stamps, exact admission, no HBM tier).
+ * blocks in device memory, no last-use stamps, exact admission, no HBM tier,
+ * the default gradient size for the bag-major pass).
  * Passage: page "RecIS (Recommendation Intelligence System)" README, section "Key optimisations > Distributed optimisation"
  * (a table's attributes: dimension, initializer). */
 void recis_table_config_default(recis_table_config* cfg);

@@ -938,14 +938,16 @@ def _expected_hot_keys(batch, dim):
 
 
 @pytest.mark.parametrize("case", ["sum64_threshold_split", "mean128_bf16_grad", "long_bags", "shared_slot",
-                                  "slots_alike_mod_4096"])
+                                  "slots_alike_mod_4096", "small_gradient_default"])
 def test_hot_keys_summed_bag_major(case):
-    """The pooled backward's bag-major pass for hot long keys, at parity with
-    the oracle over two steps: several 2048-bag blocks with a partial last
-    one; more eligible keys than a feature's limit (the count classes split);
-    mean pooling with bf16 gradients at dim 128; stages with more
-    occurrences than one sorted batch; and features whose slots coincide
-    modulo 4096 (the pass stays off).  The stats count exactly the keys the
+    """The pooled backward's bag-major pass for hot long keys (forced on for
+    these small gradients with hot_grad_bytes = 1), at parity with the oracle
+    over two steps: several 2048-bag blocks with a partial last one; more
+    eligible keys than a feature's limit (the count classes split); mean
+    pooling with bf16 gradients at dim 128; stages with more occurrences than
+    one sorted batch; features whose slots coincide modulo 4096 (the pass
+    stays off); and the default threshold, under which a gradient of a few
+    MB keeps the key-by-key sums.  The stats count exactly the keys the
     documented rule selects."""
     spec_kw = dict(dtype="f32", optim="adam", lr=1e-3, eps=1e-8)
     if case == "sum64_threshold_split":
@@ -960,9 +962,12 @@ def test_hot_keys_summed_bag_major(case):
     elif case == "shared_slot":
         dim, pool, gdt = 64, "mean", "f32"
         mk = lambda s: _hot_batch(s, 2500, dim, 1500, 2, (8, 8), 1.1)
-    else:
+    elif case == "slots_alike_mod_4096":
         dim, pool, gdt = 64, "mean", "f32"
         mk = lambda s: _hot_batch(s, 2500, dim, 1500, 2, (3, 4099), 1.1)
+    else:
+        dim, pool, gdt = 64, "sum", "f32"
+        mk = lambda s: _hot_batch(s, 5000, dim, 400, 2, (1, 2), 0.8)
     spec = W.TableSpec(dim=dim, pool=pool, grad_dtype=gdt, **spec_kw)
     batches = [mk(900 + s) for s in range(2)]
     want = sum(_expected_hot_keys(b, dim) for b in batches)
@@ -970,8 +975,12 @@ def test_hot_keys_summed_bag_major(case):
         assert want == 0
     else:
         assert want > 0
+    if case == "small_gradient_default":
+        want, table_kw = 0, {}
+    else:
+        table_kw = {"hot_grad_bytes": 1}
     st = []
-    run_parity(spec, batches, stats_out=st)
+    run_parity(spec, batches, stats_out=st, table_kw=table_kw)
     assert st[0].hot_keys == want
 
 
