@@ -982,6 +982,19 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
     s_claims = 0;
     s_err = 0;
   }
+  // EMIT: the bucket's first distinct-key index and grouped position, loaded
+  // now so that they arrive during the dedup
+  long long ub_pre = 0;
+  int ob_pre = 0;
+  if (EMIT) {
+    ub_pre = L.ubase[b];
+    ob_pre = L.obase[b];
+  }
+  // a bucket that one pass of the block covers keeps each pair's table slot
+  // and weight in registers for EMIT's last pass
+  const bool one_pass = m <= NT * kBucketPer;
+  unsigned hk[kBucketPer];
+  int wk[kBucketPer];
   __syncthreads();
   for (int i0 = 0; i0 < m; i0 += NT * kBucketPer) {
     long long key[kBucketPer];
@@ -1023,6 +1036,8 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
         counted = steps < TAB;
       }
       if (counted) atomicAdd(&s_cnt[h], w[k]);
+      hk[k] = h;
+      wk[k] = act ? w[k] : 0;
     }
   }
   __syncthreads();
@@ -1044,8 +1059,8 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
     return;
   }
   const int nd = s_nd;
-  const long long ub = L.ubase[b];
-  const int ob = L.obase[b];  // the bucket's first grouped position
+  const long long ub = ub_pre;
+  const int ob = ob_pre;  // the bucket's first grouped position
   const bool find_only = (L.flags & RECIS_FIND_ONLY) != 0;
   // an empty IDMap slot goes to the first thread that enters it in the set
   // (slot indices are below 2^32; the last index of a 2^32-slot table, equal
@@ -1095,6 +1110,15 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
     L.blk_long[b] = s_sum_long;
     L.blk_claim[b] = s_claims;
     if (s_err) atomicOr(&t.ctr->error, s_err);
+  }
+  if (one_pass) {  // the slots and weights kept from the dedup
+#pragma unroll
+    for (int k = 0; k < kBucketPer; ++k) {
+      const bool act = tid + k * NT < m;
+      const int pos = act ? atomicAdd(&s_cnt[hk[k]], wk[k]) : 0;
+      if (act) put_out(L, s + tid + k * NT, s_ref[hk[k]], s_u[hk[k]], ob + pos);
+    }
+    return;
   }
   for (int i0 = 0; i0 < m; i0 += NT * kBucketPer) {
     PartEntry e[kBucketPer];
