@@ -85,16 +85,15 @@ struct __align__(16) PartEntry {
   int w;
 };
 
-// What the bucket kernels leave in place of a pair's record once its key is
-// resolved: the forward reference, the distinct-key index, and where the
-// pair's occurrences start in the key's group.  The lookup's last kernel
-// reads them tile by tile.
+// What the bucket kernels write for a pair once its key is resolved, at the
+// pair's slot (tile * kTileOcc + its index in the tile): the forward
+// reference, the distinct-key index, and where the pair's occurrences start
+// in the key's group.  The lookup's last kernel reads a tile's contiguously.
 struct __align__(16) PartOut {
   long long ref;
   int u;
   int gpos;
 };
-static_assert(sizeof(PartOut) == sizeof(PartEntry), "written in place of the record");
 
 struct DevCounters {
   unsigned long long next_row;  // bump pointer over EmbeddingBlocks
@@ -401,7 +400,7 @@ struct recis_table {
   int* bbase = nullptr;
   int* ubase = nullptr;
   int* uslot = nullptr;
-  int* posmap = nullptr;
+  recis::PartOut* pout = nullptr;
   long long* tkey = nullptr;  // tile-distinct keys, their counts, per-tile sizes
   int* tcnt = nullptr;
   int* tile_n = nullptr;
@@ -489,7 +488,7 @@ struct LookupLaunch {
   int* bbase;                 // nbk + 1: first position of each bucket
   int* ubase;                 // nbk + 1: distinct keys per bucket, then their first index
   PartEntry* part;            // pairs (at most N)
-  int* posmap;                // [ntiles * kTileOcc]: position of each pair's record in part
+  PartOut* pout;              // [ntiles * kTileOcc]: each pair resolved (emit), at its pair slot
   unsigned long long* blk_sums;  // per key tile: rows to allocate << 32 | keys inserted
   unsigned long long* blk_long;  // per key tile: long keys << 32 | their chunks
   unsigned long long* blk_claim; // per key tile: IDMap slot claims << 32 | claims lost

@@ -25,7 +25,7 @@
 //               insert of every distinct key (count, admission decision,
 //               without global atomics: the block owns the bucket's IDMap
 //               regions), then for each pair its distinct-key index, forward
-//               reference and span of its key's group, in place of its record
+//               reference and span of its key's group, at the pair's slot
 //               (a bucket that overflows the LDS table, from colliding inputs,
 //               uses a global one; a heavy bucket is counted slice by slice
 //               and its pairs are resolved by k_key_scan's other blocks)
@@ -454,7 +454,7 @@ __device__ void scan_small(int* a, int n, long long* total_ll) {
 
 // Every pair of the block's tiles to its bucket's range (the same partition
 // block as in k_tile; the blocks of one XCD write neighbouring records of
-// every bucket), noting where each pair's record went.
+// every bucket).
 __global__ __launch_bounds__(kPartThreads) void k_pair_scatter(LookupLaunch L) {
   constexpr int kPer = kTileOcc / kPartThreads;
   __shared__ int s_h[kMaxBuckets];
@@ -486,7 +486,6 @@ __global__ __launch_bounds__(kPartThreads) void k_pair_scatter(LookupLaunch L) {
       e.pid = (int)(p0 + l);
       e.w = w[k];
       L.part[pos] = e;
-      L.posmap[p0 + l] = pos;
     }
   }
 }
@@ -640,15 +639,15 @@ __device__ __forceinline__ long long ref_of_row(const TableDev& t, long long v, 
   return (long long)row_ptr(t.rs, v);
 }
 
-// The resolved pair at partition position p (in place of its record, which
-// its thread has read): written in bucket order, so the stores of a wave are
-// contiguous; k_occ_tile reads them tile by tile.
-__device__ __forceinline__ void put_out(const LookupLaunch& L, long long p, long long ref, int u, int gpos) {
+// The resolved pair `pid` (tile * kTileOcc + its index among the tile's
+// distinct keys): written at its pair slot, so that k_occ_tile reads a
+// tile's resolved pairs contiguously.
+__device__ __forceinline__ void put_out(const LookupLaunch& L, int pid, long long ref, int u, int gpos) {
   PartOut o;
   o.ref = ref;
   o.u = u;
   o.gpos = gpos;
-  reinterpret_cast<PartOut*>(L.part)[p] = o;
+  L.pout[pid] = o;
 }
 
 template <bool EMIT, int NT>
@@ -746,7 +745,7 @@ __device__ void bucket_global(const LookupLaunch& L, const TableDev& t, int b, i
     const int pos = atomicSub(&R[h].count, e.w) - e.w;  // the group is filled from its end
     const long long v = (long long)__hip_atomic_load(reinterpret_cast<unsigned long long*>(&L.res.unique_rows[u]),
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    put_out(L, s + i, ref_of_row(t, v, e.key), u, ld_int(&L.res.unique_offsets[u]) + pos);
+    put_out(L, e.pid, ref_of_row(t, v, e.key), u, ld_int(&L.res.unique_offsets[u]) + pos);
   }
   __syncthreads();
   for (unsigned long long h = tid; h < cap; h += NT) {
@@ -834,7 +833,7 @@ constexpr int kBigBucketThreads = 512;
 // set instead of global atomics -- and writes its row and the bucket's sums
 // (rows to allocate, keys inserted, long keys, chunks); then every
 // occurrence's grouped-list entry, and its distinct-key index and forward
-// reference in place of its partition record.
+// reference at the pair's slot.
 // COUNT's grid has the heavy slices after the buckets; a heavy bucket's own
 // block skips COUNT and does EMIT's key pass (see above).
 template <int TAB, bool EMIT, int NT>
@@ -994,20 +993,22 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
   // and weight in registers for EMIT's last pass
   const bool one_pass = m <= NT * kBucketPer;
   unsigned hk[kBucketPer];
-  int wk[kBucketPer];
+  int wk[kBucketPer], pk[kBucketPer];
   __syncthreads();
   for (int i0 = 0; i0 < m; i0 += NT * kBucketPer) {
     long long key[kBucketPer];
-    int w[kBucketPer];
+    int w[kBucketPer], pid[kBucketPer];
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
       const int i = i0 + tid + k * NT;
       PartEntry e;
       e.key = 0;
+      e.pid = 0;
       e.w = 0;
       if (i < m) e = L.part[s + i];
       key[k] = e.key;
       w[k] = e.w;
+      pid[k] = e.pid;
     }
 #pragma unroll
     for (int k = 0; k < kBucketPer; ++k) {
@@ -1038,6 +1039,7 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
       if (counted) atomicAdd(&s_cnt[h], w[k]);
       hk[k] = h;
       wk[k] = act ? w[k] : 0;
+      pk[k] = pid[k];
     }
   }
   __syncthreads();
@@ -1116,7 +1118,7 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
     for (int k = 0; k < kBucketPer; ++k) {
       const bool act = tid + k * NT < m;
       const int pos = act ? atomicAdd(&s_cnt[hk[k]], wk[k]) : 0;
-      if (act) put_out(L, s + tid + k * NT, s_ref[hk[k]], s_u[hk[k]], ob + pos);
+      if (act) put_out(L, pk[k], s_ref[hk[k]], s_u[hk[k]], ob + pos);
     }
     return;
   }
@@ -1136,7 +1138,7 @@ __global__ __launch_bounds__(NT) void k_bucket(LookupLaunch L, TableDev t) {
         while (s_key[h] != e[k].key) h = (h + 1) & (TAB - 1);
       }
       const int pos = act ? atomicAdd(&s_cnt[h], e[k].w) : 0;
-      if (act) put_out(L, s + i0 + tid + k * NT, s_ref[h], s_u[h], ob + pos);
+      if (act) put_out(L, e[k].pid, s_ref[h], s_u[h], ob + pos);
     }
   }
 }
@@ -1203,7 +1205,7 @@ __device__ void heavy_occ(const LookupLaunch& L, const TableDev& t, int e0, int 
       while (s_key[h] != en.key) h = (h + 1) & (TAB - 1);
     }
     const int pos = act ? atomicAdd(&s_cnt[h], en.w) : 0;
-    if (act) put_out(L, i, s_ref[h], s_u[h], pos);
+    if (act) put_out(L, en.pid, s_ref[h], s_u[h], pos);
   }
   __syncthreads();  // the LDS table is reused by the next slice
   }
@@ -1410,7 +1412,7 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
 }
 
 // Each occurrence's outputs, one tile per block.  The tile's resolved pairs
-// (read through the positions the scatter noted, bucket order) go to LDS;
+// (contiguous at the tile's pair slots) go to LDS;
 // then every occurrence takes its pair's distinct-key index and forward
 // reference (stored contiguously, in occurrence order) and the next place in
 // its pair's span of the key's group, where its grouped entry goes: its bag
@@ -1420,23 +1422,19 @@ __global__ __launch_bounds__(kThreads) void k_key_finalize(LookupLaunch L, Table
 constexpr int kOccThreads = 1024;
 constexpr int kOccPer = kTileOcc / kOccThreads;
 constexpr int kOccBagWin = 3072;  // offsets kept in LDS: two blocks per CU fit
-// The tile's resolved pairs to LDS, K per thread: the record positions, then
-// the records, each batch of loads in flight together.
+// The tile's resolved pairs to LDS, K per thread, the loads in flight
+// together.
 template <int K>
 __device__ __forceinline__ void occ_pairs(const LookupLaunch& L, long long j0, int nd, long long* s_ref, int* s_u,
                                           int* s_g) {
   const int tid = threadIdx.x;
   const int lastl = nd > 0 ? nd - 1 : 0;
-  const PartOut* po = reinterpret_cast<const PartOut*>(L.part);
-  int p[K];
+  PartOut o[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int l = tid + k * kOccThreads;
-    p[k] = L.posmap[j0 + (l < nd ? l : lastl)];
+    o[k] = L.pout[j0 + (l < nd ? l : lastl)];
   }
-  PartOut o[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) o[k] = po[p[k]];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int l = tid + k * kOccThreads;

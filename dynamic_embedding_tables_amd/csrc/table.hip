@@ -263,7 +263,7 @@ PartGeom part_geom(long long n, int max_bits = kMaxBucketBits) {
 
 // Bytes of each per-step scratch array for cap occurrences.
 struct ScratchSizes {
-  size_t dd, part, hist, bbase, uslot, posmap, blk, wb, partials, tkey, tcnt, tile_n, occ_local;
+  size_t dd, part, hist, bbase, uslot, pout, blk, wb, partials, tkey, tcnt, tile_n, occ_local;
 };
 ScratchSizes scratch_sizes(long long cap, int dim) {
   ScratchSizes z;
@@ -276,7 +276,7 @@ ScratchSizes scratch_sizes(long long cap, int dim) {
   z.bbase = (size_t)(kMaxBuckets + 1) * 4 * 3;  // bbase, ubase, obase
   z.uslot = (size_t)cap * 4;
   const size_t tiled = (size_t)g.ntiles * kTileOcc;  // pair slots, whole tiles
-  z.posmap = tiled * 4;
+  z.pout = tiled * sizeof(PartOut);
   z.tkey = tiled * 8;
   z.tcnt = tiled * 4;
   z.tile_n = (size_t)(g.ntiles + 1) * 4 * 2;  // tile_n, then tile_bag
@@ -295,7 +295,7 @@ void free_scratch(recis_table* t, hipStream_t s) {
   tab_free(t, t->hist, z.hist, s);
   tab_free(t, t->bbase, z.bbase, s);
   tab_free(t, t->uslot, z.uslot, s);
-  tab_free(t, t->posmap, z.posmap, s);
+  tab_free(t, t->pout, z.pout, s);
   tab_free(t, t->blk_sums, z.blk, s);
   tab_free(t, t->wb_keys, z.wb, s);
   tab_free(t, t->partials, z.partials, s);
@@ -308,7 +308,8 @@ void free_scratch(recis_table* t, hipStream_t s) {
   t->occ_local = nullptr;
   t->dd = nullptr;
   t->part = nullptr;
-  t->hist = t->bbase = t->ubase = t->uslot = t->posmap = nullptr;
+  t->hist = t->bbase = t->ubase = t->uslot = nullptr;
+  t->pout = nullptr;
   t->blk_sums = nullptr;
   t->wb_keys = nullptr;
   t->partials = nullptr;
@@ -331,7 +332,7 @@ recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
   t->bbase = static_cast<int*>(tab_alloc(t, z.bbase, s));
   t->ubase = t->bbase ? t->bbase + (kMaxBuckets + 1) : nullptr;
   t->uslot = static_cast<int*>(tab_alloc(t, z.uslot, s));
-  t->posmap = static_cast<int*>(tab_alloc(t, z.posmap, s));
+  t->pout = static_cast<recis::PartOut*>(tab_alloc(t, z.pout, s));
   t->blk_sums = static_cast<unsigned long long*>(tab_alloc(t, z.blk, s));
   t->wb_keys = static_cast<long long*>(tab_alloc(t, z.wb, s));
   t->partials = static_cast<double*>(tab_alloc(t, z.partials, s));
@@ -339,7 +340,7 @@ recis_status ensure_scratch(recis_table* t, long long n, hipStream_t s) {
   t->tcnt = static_cast<int*>(tab_alloc(t, z.tcnt, s));
   t->tile_n = static_cast<int*>(tab_alloc(t, z.tile_n, s));
   t->occ_local = static_cast<unsigned short*>(tab_alloc(t, z.occ_local, s));
-  if (!t->dd || !t->part || !t->hist || !t->bbase || !t->uslot || !t->posmap || !t->blk_sums || !t->wb_keys ||
+  if (!t->dd || !t->part || !t->hist || !t->bbase || !t->uslot || !t->pout || !t->blk_sums || !t->wb_keys ||
       !t->partials || !t->tkey || !t->tcnt || !t->tile_n || !t->occ_local) {
     free_scratch(t, s);
     return RECIS_ERR_OUT_OF_MEMORY;
@@ -634,7 +635,7 @@ recis_status recis_idmap_insert_find(recis_table* t, const recis_feature_desc* f
   L.bbase = t->bbase;
   L.ubase = t->ubase;
   L.part = t->part;
-  L.posmap = t->posmap;
+  L.pout = t->pout;
   L.blk_sums = t->blk_sums;
   L.blk_long = t->blk_sums + (kMaxBuckets + 2);
   L.blk_claim = t->blk_sums + 2 * (kMaxBuckets + 2);
