@@ -382,11 +382,13 @@ __global__ __launch_bounds__(256) void k_fwd_pool(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = acc[e] / len;
       }
+      // non-temporal: the step does not read the output again
       const int f = (int)(bag / a.B), i = (int)(bag - (long long)f * a.B);
       float* o = static_cast<float*>(a.out) + ((long long)i * a.F + f) * D + lane * E;
 #pragma unroll
       for (int q = 0; q < E / 4; ++q)
-        reinterpret_cast<float4*>(o)[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        __builtin_nontemporal_store(f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]},
+                                    reinterpret_cast<f32x4*>(o) + q);
     }
   }
 }

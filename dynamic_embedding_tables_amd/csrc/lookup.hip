@@ -1525,8 +1525,10 @@ __global__ __launch_bounds__(kOccThreads) void k_occ_tile(LookupLaunch L) {
     const int l = loc[k];
     const int pos = atomicAdd(&s_g[l], 1);
     L.res.grouped[pos] = g;
-    L.res.inverse[j] = s_u[l];
-    occref[j] = s_ref[l];
+    // contiguous, and read back by later launches only: non-temporal
+    // (the scattered grouped entries are not -- they merge in the caches)
+    __builtin_nontemporal_store(s_u[l], L.res.inverse + j);
+    __builtin_nontemporal_store(s_ref[l], occref + j);
   }
 }
 
