@@ -283,15 +283,16 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
       k_tile: per occurrence its raw ID 8 read and its index among its
         tile's pairs 2 written; per pair its key and count 12 written.
       k_pair_scatter: per pair its key and count 12 read, and its partition
-        record (key, pair, count) 16 and the record's position 4 written.
+        record (key, pair, count) 16 written.
       k_bucket_count: per pair its record's key and count 12.
       k_bucket_emit: per pair its record 16 read and its resolved record
-        (forward reference, distinct-key index, group position) 16 written;
+        (forward reference, distinct-key index, group position) 16 written
+        at the pair's slot;
         per distinct key its key and count 12, group offset 4, IDMap slot read
         16 and slot index 8; per new key its IDMap slot written 16.
       k_occ_tile: per occurrence its pair index 2 read, and its inverse index
         4, grouped entry 4 and forward reference 8 written; per pair its
-        record's position 4 and resolved record 16 read; offsets 4 (Bg + 1).
+        resolved record 16 read; offsets 4 (Bg + 1).
       k_bwd_long_partial: per entry of a long key that is not hot 4; per
         chunk a partial of D fp64 written; the gradient rows of the bags its
         entries touch, at most min(E_l_cold, Bg) pooled (one row per entry
@@ -312,10 +313,10 @@ def algorithmic_bytes(shape, N, Um, Unew, Uhit, Bg, D, s=4, S=2, gs=4, pooled=Tr
     gather = 8 * N + Uhit * D * s + N * D * s
     Pp = shape.get("pairs", 0)
     tile = 10 * N + 12 * Pp
-    scatter = 32 * Pp
+    scatter = 28 * Pp
     count = 12 * Pp
     emit = 32 * Pp + 40 * Um + 16 * Unew
-    occ = 18 * N + 20 * Pp + 4 * (Bg + 1)
+    occ = 18 * N + 16 * Pp + 4 * (Bg + 1)
     El = shape.get("E_l_cold", shape["E_l"])
     g_long = min(El, Bg) * D * gs if pooled else El * D * gs
     long_partial = 4 * El + shape["chunks_l"] * D * 8 + g_long
