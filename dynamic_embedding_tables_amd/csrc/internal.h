@@ -452,7 +452,11 @@ __device__ __forceinline__ int xcd_block(int i, int G) {
 constexpr int kTileOcc = 4096;
 constexpr int kTileTab = 2 * kTileOcc;  // the tile's LDS table, at most half full
 constexpr int kPartThreads = 1024;   // partition kernels' block size
-constexpr int kMaxPartBlocks = 1024;
+// At most one partition block per CU: k_tile's LDS table allows one block
+// per CU anyway, and fewer, longer blocks give k_pair_scatter longer runs of
+// records per bucket (each block's records of a bucket are contiguous) and
+// the column scan a smaller histogram.
+constexpr int kMaxPartBlocks = 256;
 constexpr int kBucketOcc = 384;      // target occurrences per bucket
 constexpr int kMaxBucketBits = 13;
 constexpr int kMaxBuckets = 1 << kMaxBucketBits;
