@@ -457,7 +457,12 @@ constexpr int kPartThreads = 1024;   // partition kernels' block size
 // records per bucket (each block's records of a bucket are contiguous) and
 // the column scan a smaller histogram.
 constexpr int kMaxPartBlocks = 256;
-constexpr int kBucketOcc = 384;      // target occurrences per bucket
+// Target occurrences per bucket.  The bucket count is this share rounded up
+// to a power of two (then capped), so a call gets 512 to 1024 occurrences per
+// bucket until the cap: after the tile-level dedup that is a few hundred
+// pairs, enough to keep a bucket block's threads busy past its fixed costs
+// (table clear, bases, barriers).
+constexpr int kBucketOcc = 1024;
 constexpr int kMaxBucketBits = 13;
 constexpr int kMaxBuckets = 1 << kMaxBucketBits;
 constexpr int kBucketPer = 4;        // occurrences per thread per pass of k_bucket

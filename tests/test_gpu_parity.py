@@ -1176,10 +1176,10 @@ def _ids_in_first_hash_bucket(count, bits, rng):
 
 
 def test_bucket_overflow_path():
-    """2000 distinct keys that collide in the top bits of the partition hash:
-    3000 occurrences make 8 buckets (bits = 3), so all of them land in one
-    bucket and overflow its LDS table; the global-table path must give the
-    same lookup, forward and update as the oracle."""
+    """2000 distinct keys that collide in the top 3 bits of the partition
+    hash: 3000 occurrences make 4 buckets (bits = 2), so all of them land in
+    one bucket and overflow its LDS table; the global-table path must give
+    the same lookup, forward and update as the oracle."""
     spec = W.TableSpec(dim=16, dtype="f32", optim="adagrad", pool="sum", lr=0.05)
     rng = W.rng_for(91)
     ids = _ids_in_first_hash_bucket(2000, 3, rng)
@@ -1190,6 +1190,33 @@ def test_bucket_overflow_path():
     b = W.Batch([W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=0)], B,
                 rng.standard_normal((B, 16), dtype=np.float32))
     run_parity(spec, [b, b])
+
+
+@pytest.mark.parametrize("pool", ["sum", "none"])
+def test_heavy_bucket_sliced(pool):
+    """20,000 distinct keys that collide in the top 6 bits of the partition
+    hash, three occurrences each, shuffled, beside 4000 ordinary occurrences:
+    64,000 occurrences make 64 buckets (bits = 6), and the first one gets
+    about 56k (key, tile) pairs, past the 16,384 at which a bucket is cut
+    into slices that separate blocks deduplicate through the global table.
+    Two steps (inserts, then stored rows) at parity with the oracle.  The
+    keys also share their IDMap regions (the same top bits pick them), 1/64
+    of the slots: a 2^23-slot IDMap gives them room."""
+    spec = W.TableSpec(dim=16, dtype="f32", optim="adagrad", pool=pool, lr=0.05, eps=1e-10)
+    rng = W.rng_for(93)
+    ids = _ids_in_first_hash_bucket(20000, 6, rng)
+    assert ids.size == 20000
+    batches = []
+    for step in range(2):
+        r = W.rng_for(94, step)
+        vals = np.concatenate([np.repeat(ids, 3), r.integers(1, 1 << 40, 4000)])
+        r.shuffle(vals)
+        B = 1000
+        off = (np.arange(B + 1) * (vals.size // B)).astype(np.int32)
+        rows = vals.size if pool == "none" else B
+        batches.append(W.Batch([W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=0)], B,
+                               r.standard_normal((rows, 16), dtype=np.float32)))
+    run_parity(spec, batches, table_kw=dict(slot_capacity=1 << 23))
 
 
 @pytest.mark.parametrize("row_offset", [0, 1])
