@@ -895,12 +895,14 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     # ---- fill the table (untimed)
     i = 0
     if wl["fill"] == "keys":  # pre-populate: each feature's resident IDs, one per bag
-        for f, keys in resident_keys:
+        for j, (f, keys) in enumerate(resident_keys):
             kd = torch.from_numpy(keys).to(dev)
             od = torch.arange(keys.shape[0] + 1, dtype=torch.int32, device=dev)
             r = recis.LookupResult(keys.shape[0], keys.shape[0])
             table.insert_find([recis.DeviceFeature(kd, od, f)], keys.shape[0], r)
             del r, kd, od
+            if j % 25 == 24:
+                log(f"{name} fill: {j + 1} features' resident keys inserted")
         torch.cuda.synchronize()
         table.check()
     else:

@@ -463,6 +463,13 @@ constexpr int kMaxPartBlocks = 256;
 // pairs, enough to keep a bucket block's threads busy past its fixed costs
 // (table clear, bases, barriers).
 constexpr int kBucketOcc = 1024;
+constexpr int kMinBuckets = 256;  // one bucket block per CU for small calls (within the IDMap's regions)
+// The bucket blocks' smaller LDS table (1024 entries) holds at most 768
+// distinct keys.  A call with more than kSmallTabOcc occurrences per bucket
+// on average could give a bucket more than that when most of its keys are
+// distinct (a bulk insert of new keys), so it takes the 2048-entry table:
+// an overflowing bucket falls back to a global table, several times slower.
+constexpr int kSmallTabOcc = 640;
 constexpr int kMaxBucketBits = 13;
 constexpr int kMaxBuckets = 1 << kMaxBucketBits;
 constexpr int kBucketPer = 4;        // occurrences per thread per pass of k_bucket
@@ -491,7 +498,7 @@ struct LookupLaunch {
   int* tile_bag;              // [ntiles]: the bag of each tile's first occurrence
   unsigned short* occ_local;  // N: each occurrence's index among its tile's distinct keys
   int* obase;                 // nbk + 1: occurrences per bucket, then the first grouped position
-  int big_tab;                // buckets average more than kBucketOcc occurrences
+  int big_tab;                // buckets average more than kSmallTabOcc occurrences
   int hot_ok;                 // at most kFeatBins features, in distinct feature bins
   int* hist;                  // [part_blocks][nbk]
   int* bbase;                 // nbk + 1: first position of each bucket

@@ -189,11 +189,11 @@ __global__ __launch_bounds__(kThreads) void k_prep(LookupLaunch L, TableDev t) {
 }
 
 // ------------------------------------------------------ hash partition
-// The call's occurrences are partitioned by the top bits of their key's
-// Fibonacci hash into nbk buckets (about kBucketOcc occurrences each), like
-// one pass of a radix sort: k_part_hist counts per (partition block,
-// bucket), two scans turn the counts into positions, and k_part_scatter
-// writes every occurrence to its bucket's range.  Each bucket is then
+// The call's tile-distinct keys (pairs) are partitioned by the top bits of
+// their key's Fibonacci hash into nbk buckets (see part_geom), like one pass
+// of a radix sort: k_tile counts per (partition block, bucket), the column
+// scan and a small scan turn the counts into positions, and k_pair_scatter
+// writes every pair to its bucket's range.  Each bucket is then
 // deduplicated by one block entirely in LDS (k_bucket), so the dedup needs
 // no global atomics at all: on this GPU those are performed at the memory
 // side and would bound the step.
@@ -814,9 +814,8 @@ __device__ __forceinline__ void slice_dedup(const LookupLaunch& L, int s0, int s
   }
 }
 
-// Block size of the bucket kernels when the buckets are fuller than the
-// target (the call's occurrences outnumber kMaxBuckets * kBucketOcc: the
-// 2048-entry table).  More threads put more of a bucket's IDMap probes in
+// Block size of the bucket kernels when the buckets average more than
+// kSmallTabOcc occurrences (the 2048-entry table).  More threads put more of a bucket's IDMap probes in
 // flight at once; 512 measured faster than 256 and 1024 on the capacity
 // workload (1024: registers allow one block per CU).
 constexpr int kBigBucketThreads = 512;

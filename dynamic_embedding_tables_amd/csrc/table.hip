@@ -240,9 +240,10 @@ int region_bits_for(long long slot_cap) {
 }
 
 // Hash-partition geometry of a call with n occurrences: buckets of about
-// kBucketOcc occurrences (a power of two, at most kMaxBuckets), tiles of
-// kTileOcc occurrences, partition blocks of whole tiles (at most
-// kMaxPartBlocks of them).
+// kBucketOcc occurrences, but at least kMinBuckets of them (a small call's
+// bucket blocks then spread over the CUs instead of queueing a few long
+// chains), a power of two, at most kMaxBuckets; tiles of kTileOcc
+// occurrences, partition blocks of whole tiles (at most kMaxPartBlocks).
 struct PartGeom {
   int nbits, nbk, blocks, big;
   long long ntiles, tiles_per_block;
@@ -251,13 +252,13 @@ struct PartGeom {
 // bucket's block owns whole regions.
 PartGeom part_geom(long long n, int max_bits = kMaxBucketBits) {
   PartGeom g;
-  const long long want = std::max<long long>(1, (n + kBucketOcc - 1) / kBucketOcc);
+  const long long want = std::max<long long>(kMinBuckets, (n + kBucketOcc - 1) / kBucketOcc);
   g.nbk = (int)std::min<long long>(next_pow2(want), 1ll << max_bits);
   g.nbits = log2_exact(g.nbk);
   g.ntiles = std::max<long long>(1, (n + kTileOcc - 1) / kTileOcc);
   g.tiles_per_block = (g.ntiles + kMaxPartBlocks - 1) / kMaxPartBlocks;
   g.blocks = (int)((g.ntiles + g.tiles_per_block - 1) / g.tiles_per_block);
-  g.big = n > (long long)g.nbk * kBucketOcc ? 1 : 0;
+  g.big = n > (long long)g.nbk * kSmallTabOcc ? 1 : 0;
   return g;
 }
 

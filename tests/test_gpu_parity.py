@@ -1176,13 +1176,14 @@ def _ids_in_first_hash_bucket(count, bits, rng):
 
 
 def test_bucket_overflow_path():
-    """2000 distinct keys that collide in the top 3 bits of the partition
-    hash: 3000 occurrences make 4 buckets (bits = 2), so all of them land in
-    one bucket and overflow its LDS table; the global-table path must give
-    the same lookup, forward and update as the oracle."""
+    """2000 distinct keys that collide in the top 8 bits of the partition
+    hash: 3000 occurrences make 256 buckets (the floor for small calls, bits
+    = 8), so all of them land in one bucket and overflow its LDS table; the
+    global-table path must give the same lookup, forward and update as the
+    oracle.  In the IDMap (1024 regions of 1024 slots) they share 4 regions."""
     spec = W.TableSpec(dim=16, dtype="f32", optim="adagrad", pool="sum", lr=0.05)
     rng = W.rng_for(91)
-    ids = _ids_in_first_hash_bucket(2000, 3, rng)
+    ids = _ids_in_first_hash_bucket(2000, 8, rng)
     vals = np.concatenate([ids, rng.choice(ids, 1000)])
     rng.shuffle(vals)
     B = 300
@@ -1194,17 +1195,18 @@ def test_bucket_overflow_path():
 
 @pytest.mark.parametrize("pool", ["sum", "none"])
 def test_heavy_bucket_sliced(pool):
-    """20,000 distinct keys that collide in the top 6 bits of the partition
+    """20,000 distinct keys that collide in the top 8 bits of the partition
     hash, three occurrences each, shuffled, beside 4000 ordinary occurrences:
-    64,000 occurrences make 64 buckets (bits = 6), and the first one gets
-    about 56k (key, tile) pairs, past the 16,384 at which a bucket is cut
-    into slices that separate blocks deduplicate through the global table.
-    Two steps (inserts, then stored rows) at parity with the oracle.  The
-    keys also share their IDMap regions (the same top bits pick them), 1/64
-    of the slots: a 2^23-slot IDMap gives them room."""
+    64,000 occurrences make 256 buckets (the floor for small calls, bits =
+    8), and the first one gets about 56k (key, tile) pairs, past the 16,384
+    at which a bucket is cut into slices that separate blocks deduplicate
+    through the global table.  Two steps (inserts, then stored rows) at
+    parity with the oracle.  The keys also share their IDMap regions (the
+    same top bits pick them), 1/256 of the slots: a 2^24-slot IDMap gives
+    them 65,536."""
     spec = W.TableSpec(dim=16, dtype="f32", optim="adagrad", pool=pool, lr=0.05, eps=1e-10)
     rng = W.rng_for(93)
-    ids = _ids_in_first_hash_bucket(20000, 6, rng)
+    ids = _ids_in_first_hash_bucket(20000, 8, rng)
     assert ids.size == 20000
     batches = []
     for step in range(2):
@@ -1216,7 +1218,7 @@ def test_heavy_bucket_sliced(pool):
         rows = vals.size if pool == "none" else B
         batches.append(W.Batch([W.FeatureInput(values=vals.astype(np.int64), bag_offsets=off, slot=0)], B,
                                r.standard_normal((rows, 16), dtype=np.float32)))
-    run_parity(spec, batches, table_kw=dict(slot_capacity=1 << 23))
+    run_parity(spec, batches, table_kw=dict(slot_capacity=1 << 24))
 
 
 @pytest.mark.parametrize("row_offset", [0, 1])
