@@ -78,7 +78,11 @@ WORKLOADS = {
         "title": "Capacity stress: 200M pre-populated rows x dim 64 fp32 + Adam m/v, 100 features, batch 65536, "
                  "bag length Poisson(8), Zipf(1.2) IDs with 2% novel per step, sum pooling",
         "spec": W.spec_capacity, "F": 100, "B": 65536, "fill": "keys", "steps": 5, "warmup": 10,
-        "table": {"slot_capacity": 1 << 29, "block_rows": 1 << 20},
+        # max_load 0.6: before a call the IDMap's growth check counts each of its
+        # 52.4M occurrences as a possible new key, so at 0.5 the 2^29-slot map
+        # would double (a rehash inside the timed steps) once it held 216M keys,
+        # although the keys fill only about 0.42 of it
+        "table": {"slot_capacity": 1 << 29, "block_rows": 1 << 20, "max_load": 0.6},
         "candidates": ("k_bwd_short", "k_fwd_pool", "k_bwd_long_partial", "k_occ_tile", "k_bucket_emit"),
         # the oracle baseline: these features of the first timed step (21M IDs)
         "cpu_features": 40,
@@ -255,6 +259,8 @@ def step_shapes(results, U, resident0, hot=None):
 
 
 SHORT_MAX = 64   # occurrences up to which the backward treats a key as short
+GRAD_POOL = 8    # distinct upstream gradients staged for the warm-up and timed steps
+KEEP_RESULTS = 5  # timed steps whose lookup results are kept for the step shapes
 MAX_KEY_CHUNKS = 1024  # a long key is summed in at most this many chunks
 
 
@@ -835,8 +841,8 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     dev = torch.device("cuda", 0)
     cap = max(sum(v.shape[0] for (v, *_r) in b[0]) for b in batches)
     pre_rows = sum(k.shape[0] for _, k in resident_keys)
-    if wl["fill"] == "keys":  # a call may add up to its N rows; 2% of N are new per step
-        reserve = pre_rows + cap + (Wm + K + 1) * (cap // 30)
+    if wl["fill"] == "keys":  # a call may add up to its N rows; 2% of N are new per step (2.2% reserved)
+        reserve = pre_rows + cap + (Wm + K + 1) * (cap // 45)
     elif wl["fill"] == "resident":  # the fill stops within one step of the target
         reserve = args.resident + (Wm + K + 3) * wl["new_per_step"]
     elif wl["fill"] == "steps":
@@ -855,15 +861,23 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     gdt = torch.bfloat16 if spec.grad_dtype == "bf16" else torch.float32
     flags = 0 if pooled else recis.RECIS_GROUP_BY_OCCURRENCE
 
-    def upload(batch):
-        """The batch's IDs and offsets in HBM, and a fresh N(0,1) upstream
-        gradient for its step."""
+    grad_pool = []
+
+    def upload(batch, j=None):
+        """The batch's IDs and offsets in HBM, and its N(0,1) upstream
+        gradient: a fresh one for a fill step (j None), else gradient j of the
+        staged pool (one per timed step while they number at most GRAD_POOL,
+        then reused in turn; the warm-up steps reuse them too)."""
         feats, bsz = batch
         dfs = [recis.DeviceFeature(torch.from_numpy(v).to(dev), torch.from_numpy(o).to(dev), sl, ops, mod)
                for (v, o, sl, ops, mod) in feats]
         n = sum(f.n for f in dfs)
-        shape = (bsz, F * D) if pooled else (n, D)
-        grad = torch.randn(*shape, device=dev, generator=gen, dtype=torch.float32).to(gdt)
+        if j is None:
+            shape = (bsz, F * D) if pooled else (n, D)
+            grad = torch.randn(*shape, device=dev, generator=gen, dtype=torch.float32).to(gdt)
+        else:
+            grad = grad_pool[j % len(grad_pool)]
+            grad = grad if pooled else grad[:n]
         return dfs, recis.make_descs(dfs), n, grad
 
     out = torch.empty(B, F * D, device=dev, dtype=torch.float32) if pooled else \
@@ -915,10 +929,17 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     resident0 = table.stats().rows_in_use
     log(f"{name} fill: {i} steps, {resident0} resident rows")
 
-    # ---- stage warm-up + timed inputs in HBM
+    # ---- stage warm-up + timed inputs in HBM.  Device memory stays within
+    # bounds for any K: at most GRAD_POOL upstream gradients (1.7 GB each on the
+    # capacity workload), and full lookup results (2.3 GB each there) for the
+    # first KEEP_RESULTS timed steps only -- the measured step shapes come from
+    # those; later timed steps reuse the two fill buffers in turn.
     first_timed = i + Wm
-    staged = [upload(batches[j]) for j in range(i, i + Wm + K)]
-    timed_res = [recis.LookupResult(cap, F * B) for _ in range(K)]
+    for _ in range(min(GRAD_POOL, max(K, 1))):
+        shape = (B, F * D) if pooled else (cap, D)
+        grad_pool.append(torch.randn(*shape, device=dev, generator=gen, dtype=torch.float32).to(gdt))
+    staged = [upload(batches[i + w], w) for w in range(Wm)] + [upload(batches[i + Wm + k], k) for k in range(K)]
+    timed_res = [recis.LookupResult(cap, F * B) for _ in range(min(K, KEEP_RESULTS))]
     stream = torch.cuda.current_stream()
 
     def event_pair():
@@ -959,7 +980,7 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     t0 = time.perf_counter()
     for k in range(K):
         dfs, descs, n, grad = staged[Wm + k]
-        res = timed_res[k]
+        res = timed_res[k] if k < len(timed_res) else res_pool[k % 2]
         e = ev[k]
         if dom:
             table.profile_kernel(dom, *kev[k])
@@ -973,6 +994,9 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
         maybe_retier(Wm + k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    free_b, total_b = torch.cuda.mem_get_info()
+    log(f"{name}: {K} timed steps in {elapsed * 1e3:.1f} ms; device memory free {free_b / 1e9:.1f} of "
+        f"{total_b / 1e9:.1f} GB")
     table.profile_kernel(None)
     table.check()
     st1 = table.stats()
@@ -1029,6 +1053,9 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
             "global_batch": B, "num_features": F, "dim": D, "storage": spec.dtype,
             "ids_per_step": N, "unique_per_step": Um, "new_rows_per_step": Unew,
             "resident_rows_start": int(st0.rows_in_use), "resident_rows_end": int(st1.rows_in_use),
+            # timed steps with a gradient of their own (reused in turn past it), and the
+            # first timed steps whose lookup results give the measured step shape
+            "distinct_timed_gradients": len(grad_pool), "shape_from_first_steps": len(timed_res),
             "parallelism": "single GPU",
         },
         "step_breakdown_ms": {"insert_find": t_ins * 1e3, "lookup_pool_fwd": t_fwd * 1e3,
