@@ -1034,6 +1034,22 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
     traffic = read_traffic(dom, name) if dom else None
     claims = (st1.claim_attempts - st0.claim_attempts) / K
     lost = (st1.claim_failures - st0.claim_failures) / K
+    # rows in host blocks: the share of the timed lookups' rows past the HBM
+    # tier (all of them without one) scales the rows that cross the host link
+    host_keys, host_share = [], 1.0
+    if block_memory == "host":
+        H = int(st1.hbm_rows)
+        with_rows = []
+        for r, u in zip(timed_res, U):
+            rw = r.unique_rows[:u].cpu().numpy()
+            rw = rw[rw >= 0] & ((1 << 62) - 1)
+            host_keys.append(int(np.count_nonzero(rw >= H)))
+            with_rows.append(int(rw.size))
+        host_share = sum(host_keys) / max(sum(with_rows), 1)
+
+    def link(kernel):
+        rd, wr = link_bytes(kernel, shape, Uhit, D, s_bytes, S)
+        return rd * host_share, wr * host_share
 
     result = {
         "metric": "lookup+pool+update IDs/sec and achieved HBM GB/s vs peak, 1xMI355X",
@@ -1075,10 +1091,10 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
                      # rows in host memory: the dominant kernel against the host link, in
                      # the direction that carries more of its row bytes
                      {"bound": "host-link", "kernel": dom, "kernel_ms": t_dom * 1e3,
-                      "link_bytes_read_written": list(link_bytes(dom, shape, Uhit, D, s_bytes, S)),
-                      "achieved": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9,
+                      "link_bytes_read_written": list(link(dom)), "host_row_share": host_share,
+                      "achieved": max(link(dom)) / t_dom / 1e9,
                       "peak": LINK_PEAK_GBS, "unit": "GB/s",
-                      "frac": max(link_bytes(dom, shape, Uhit, D, s_bytes, S)) / t_dom / 1e9 / LINK_PEAK_GBS,
+                      "frac": max(link(dom)) / t_dom / 1e9 / LINK_PEAK_GBS,
                       "traffic": None}) if dom else None,
         "warmup_kernel_ms": {k: float(np.mean(v)) for k, v in probe_ms.items()},
         # every kernel timed in the warm-up, against the same algorithmic
@@ -1113,11 +1129,6 @@ def run_standard(name, args, K=None, Wm=None, cpu=True, extra=False):
             # timed lookups handed out: keys on host rows read their row in the
             # forward and read + write it with its state in the update
             P = D * s_bytes + S * D * 4
-            host_keys = []
-            for r, u in zip(timed_res, U):
-                rw = r.unique_rows[:u].cpu().numpy()
-                rw = rw[rw >= 0] & ((1 << 62) - 1)
-                host_keys.append(int(np.count_nonzero(rw >= H)))
             result["host_tier_keys_per_step"] = float(np.mean(host_keys))
             result["host_link_row_bytes_per_step"] = float(np.mean(host_keys)) * (D * s_bytes + 2 * P)
     cpu_src = None
