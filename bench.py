@@ -72,7 +72,7 @@ WORKLOADS = {
         "spec": W.spec_seq, "F": 1, "B": 2048, "fill": "steps", "fill_steps": 10, "steps": 20, "warmup": 5,
         "new_per_step": 250_000,
         "table": {"slot_capacity": 1 << 23, "block_rows": 1 << 20},
-        "candidates": ("k_bwd_short", "k_fwd_gather", "k_bwd_long_partial", "k_bucket_emit", "k_occ_tile"),
+        "candidates": ("k_fwd_gather", "k_bwd_short", "k_bwd_long_partial", "k_bucket_emit", "k_occ_tile"),
     },
     "capacity": {
         "title": "Capacity stress: 200M pre-populated rows x dim 64 fp32 + Adam m/v, 100 features, batch 65536, "
