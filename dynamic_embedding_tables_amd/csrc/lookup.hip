@@ -407,24 +407,37 @@ __global__ __launch_bounds__(kPartThreads) void k_part_colscan(LookupLaunch L) {
 // In-place exclusive scan of a[0..n) (n <= kMaxBuckets), a[n] = total, and
 // the total also to *total_ll when given.  Bucket positions (bbase), and the
 // distinct-key and occurrence bases of the buckets (ubase, obase: the second
-// array, scanned by the same launch).
-__device__ void scan_small(int* a, int n, long long* total_ll);
+// array, scanned by the same launch).  Both arrays' loads are issued before
+// either scan, so the launch waits for memory once.
+constexpr int kSmallPer = kMaxBuckets / kPartThreads;  // n <= kMaxBuckets
+__device__ void scan_small(int* a, const int (&v)[kSmallPer], int n, long long* total_ll);
 __global__ __launch_bounds__(kPartThreads) void k_scan_small(int* a, int* a2, int n, long long* total_ll) {
-  scan_small(a, n, total_ll);
+  const int b0 = threadIdx.x * kSmallPer;
+  const int* src2 = a2 ? a2 : a;  // without a second array: a second read of a, unused
+  int v[kSmallPer], v2[kSmallPer];
+#pragma unroll
+  for (int k = 0; k < kSmallPer; ++k) {  // from indices clamped into range: no load in a branch of its own
+    const int i = b0 + k < n ? b0 + k : 0;
+    v[k] = a[i];
+    v2[k] = src2[i];
+  }
+#pragma unroll
+  for (int k = 0; k < kSmallPer; ++k) {
+    v[k] = b0 + k < n ? v[k] : 0;
+    v2[k] = b0 + k < n ? v2[k] : 0;
+  }
+  scan_small(a, v, n, total_ll);
   if (a2) {
     __syncthreads();
-    scan_small(a2, n, nullptr);
+    scan_small(a2, v2, n, nullptr);
   }
 }
-__device__ void scan_small(int* a, int n, long long* total_ll) {
-  constexpr int kPer = kMaxBuckets / kPartThreads;  // n <= kMaxBuckets
+__device__ void scan_small(int* a, const int (&v)[kSmallPer], int n, long long* total_ll) {
+  constexpr int kPer = kSmallPer;
   __shared__ int s_w[kPartThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b0 = tid * kPer;
-  int v[kPer];
   int sum = 0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) v[k] = b0 + k < n ? a[b0 + k] : 0;  // all loads in flight
 #pragma unroll
   for (int k = 0; k < kPer; ++k) sum += v[k];
   int x = sum;
@@ -1276,32 +1289,64 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
     heavy_occ<1024, kScanThreads>(L, t, (int)blockIdx.x - 1, (int)gridDim.x - 1);
     return;
   }
-  const long long U = *L.res.num_unique;
+  const int tid = threadIdx.x;
   const long long nblk = L.N > 0 ? L.nbk : 0;  // per-bucket sums
+  // Loaded before the scan's own loads and kept in flight with them, so
+  // that the block waits for memory once: the buckets' IDMap slot claims
+  // (attempts << 32 | lost); the table's counters, a word per lane, and the
+  // call's distinct-key count in the next lane; the call's pair count.  Each
+  // value is a lane's own (a value every lane shared would be moved to a
+  // scalar register, which waits for its load at once), from an address
+  // clamped into range, outside any branch.  The scratch arrays exist for
+  // any call; the values of an empty call go unused.  Nothing else writes
+  // these counters during the launch: thread 0 writes them once at the end.
+  constexpr int kClaimPer = kMaxBuckets / kScanThreads;
+  constexpr int kCtrWords = (int)(sizeof(DevCounters) / 8);
+  static_assert(sizeof(DevCounters) % 8 == 0 && kCtrWords < kScanThreads, "the counters are whole words");
+  __shared__ DevCounters s_ctr;
+  __shared__ long long s_u;
+  __shared__ int s_pairs;
+  unsigned long long cl[kClaimPer];
+#pragma unroll
+  for (int j = 0; j < kClaimPer; ++j) {
+    const long long b = tid + (long long)j * kScanThreads;
+    cl[j] = L.blk_claim[b < nblk ? b : 0];
+  }
+  const unsigned long long* pre_src =
+      tid == kCtrWords ? reinterpret_cast<const unsigned long long*>(L.res.num_unique)
+                       : reinterpret_cast<const unsigned long long*>(t.ctr) + (tid < kCtrWords ? tid : 0);
+  const unsigned long long pre = *pre_src;
+  const int pairs = L.bbase[tid == 0 ? L.nbk : 0];
   unsigned long long all, all_long;
   scan_two(L.blk_sums, L.blk_long, nblk, &all, &all_long);
-  // IDMap slot claims of the call (attempts << 32 | lost), summed over the
-  // buckets; each bucket's figures fit 32 bits, the call's total 64
+  // the loads above are complete here: the scan waited for its own
+  if (tid < kCtrWords) reinterpret_cast<unsigned long long*>(&s_ctr)[tid] = pre;
+  if (tid == kCtrWords) s_u = (long long)pre;
+  if (tid == 0) s_pairs = pairs;
+  // the call's claims, summed over the buckets; each bucket's figures fit 32
+  // bits, the call's total 64
   __shared__ unsigned long long s_cl[2];
-  if (threadIdx.x == 0) s_cl[0] = s_cl[1] = 0;
+  if (tid == 0) s_cl[0] = s_cl[1] = 0;
   __syncthreads();
   unsigned long long ca = 0, cf = 0;
-  for (long long b = threadIdx.x; b < nblk; b += kScanThreads) {
-    const unsigned long long v = L.blk_claim[b];
-    ca += v >> 32;
-    cf += v & 0xFFFFFFFFull;
+#pragma unroll
+  for (int j = 0; j < kClaimPer; ++j) {
+    const bool in = tid + (long long)j * kScanThreads < nblk;
+    ca += in ? cl[j] >> 32 : 0ull;
+    cf += in ? cl[j] & 0xFFFFFFFFull : 0ull;
   }
   if (ca) atomicAdd(&s_cl[0], ca);
   if (cf) atomicAdd(&s_cl[1], cf);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    t.ctr->claim_attempts += s_cl[0];
-    t.ctr->claim_failures += s_cl[1];
-    if (L.N > 0) t.ctr->lookup_pairs += (unsigned long long)L.bbase[L.nbk];
+  if (tid == 0) {
+    const DevCounters c = s_ctr;
+    t.ctr->claim_attempts = c.claim_attempts + s_cl[0];
+    t.ctr->claim_failures = c.claim_failures + s_cl[1];
+    if (L.N > 0) t.ctr->lookup_pairs = c.lookup_pairs + (unsigned long long)s_pairs;
     const long long R = (long long)(all >> 32);
-    const long long Fr = t.ctr->free_top > 0 ? t.ctr->free_top : 0;
+    const long long Fr = c.free_top > 0 ? c.free_top : 0;
     const long long take = R < Fr ? R : Fr;
-    const long long base = (long long)t.ctr->next_row;
+    const long long base = (long long)c.next_row;
     long long next = base + (R - take);
     if (next > t.rows_limit) next = base > t.rows_limit ? base : t.rows_limit;
     t.ctr->take_free = take;
@@ -1309,8 +1354,8 @@ __global__ __launch_bounds__(kScanThreads) void k_key_scan(LookupLaunch L, Table
     t.ctr->bump_base = base;
     t.ctr->free_top = Fr - take;
     t.ctr->next_row = (unsigned long long)next;
-    t.ctr->num_keys += all & 0xFFFFFFFFull;
-    L.res.unique_offsets[U] = (int)L.N;
+    t.ctr->num_keys = c.num_keys + (all & 0xFFFFFFFFull);
+    L.res.unique_offsets[s_u] = (int)L.N;
     L.res.plan[0] = (int)(all_long >> 32);
     L.res.plan[1] = (int)(all_long & 0xFFFFFFFFull);
   }
